@@ -1,0 +1,162 @@
+"""fp64 CPU oracle for the selective scan (S6): test infrastructure only.
+
+Only the test suite, the smoke check and the benchmark's CPU-baseline leg may
+import this package.  The HIP library never loads it and shares no code with it.
+
+The arithmetic lives in ``ssm_oracle.c`` (plain nested loops in double
+precision, written from eq. (1)-(4), Algorithm 2 and sec. 4a of the paper
+summary page "Mamba: Linear-Time Sequence Modeling with Selective State
+Spaces", and sec. 3.1 of "14.1 SSM(State Space Models)과 Mamba 아키텍처의 부상"
+for the D skip term).  This module only compiles it with gcc (``-O2``, no
+fast-math) and marshals numpy arrays through ctypes.
+
+Every array is converted to contiguous float64 first, so bf16/fp32 inputs are
+widened exactly.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "ssm_oracle.c")
+_LIB = os.path.join(_HERE, "libssm_oracle.so")
+_lib = None
+
+
+def build(force: bool = False) -> str:
+    """Compile ssm_oracle.c into libssm_oracle.so (gcc -O2 -fopenmp)."""
+    stale = (not os.path.exists(_LIB)) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC)
+    if force or stale:
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp",
+               "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        build()
+        lib = ctypes.CDLL(_LIB)
+        P = ctypes.c_void_p
+        I64 = ctypes.c_int64
+        I = ctypes.c_int
+        lib.oracle_selective_scan_f64.argtypes = [I64, I64, I64, I64,
+                                                  P, P, P, P, P, P, P, P, I, P, P, I64,
+                                                  P, P, P, I]
+        lib.oracle_selective_scan_f64.restype = I
+        lib.oracle_causal_conv1d_silu_f64.argtypes = [I64, I64, I64, I64, P, P, P, P, I]
+        lib.oracle_causal_conv1d_silu_f64.restype = I
+        lib.oracle_state_update_f64.argtypes = [I64, I64, I64, P, P, P, P, P, P, P, P, P, I,
+                                                P, I]
+        lib.oracle_state_update_f64.restype = I
+        _lib = lib
+    return _lib
+
+
+def default_threads() -> int:
+    n = os.environ.get("OMP_NUM_THREADS")
+    if n and n.isdigit() and int(n) > 0:
+        return int(n)
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
+def _f64(a, shape=None):
+    if a is None:
+        return None
+    a = np.ascontiguousarray(np.asarray(a, dtype=np.float64))
+    if shape is not None and a.shape != tuple(shape):
+        raise ValueError("expected shape %s, got %s" % (tuple(shape), a.shape))
+    return a
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def selective_scan(x, delta, A, Bm, Cm, Dskip=None, z=None, delta_bias=None,
+                   delta_softplus: bool = False, conv_w=None, conv_b=None, h0=None,
+                   nthreads: Optional[int] = None):
+    """Return (y, h_final) in float64.
+
+    x, delta, z: (B, L, D); A: (D, N); Bm, Cm: (B, L, N); Dskip, delta_bias,
+    conv_b: (D,); conv_w: (D, K); h0: (B, D, N).
+    """
+    x = _f64(x)
+    Bsz, L, D = x.shape
+    A = _f64(A)
+    N = A.shape[1]
+    delta = _f64(delta, (Bsz, L, D))
+    A = _f64(A, (D, N))
+    Bm = _f64(Bm, (Bsz, L, N))
+    Cm = _f64(Cm, (Bsz, L, N))
+    Dskip = _f64(Dskip, (D,))
+    z = _f64(z, (Bsz, L, D))
+    delta_bias = _f64(delta_bias, (D,))
+    conv_w = _f64(conv_w)
+    K = 0 if conv_w is None else conv_w.shape[1]
+    if conv_w is not None:
+        conv_w = _f64(conv_w, (D, K))
+    conv_b = _f64(conv_b, (D,))
+    h0 = _f64(h0, (Bsz, D, N))
+    y = np.zeros((Bsz, L, D), np.float64)
+    hf = np.zeros((Bsz, D, N), np.float64)
+    rc = _load().oracle_selective_scan_f64(
+        Bsz, L, D, N, _ptr(x), _ptr(delta), _ptr(A), _ptr(Bm), _ptr(Cm), _ptr(Dskip),
+        _ptr(z), _ptr(delta_bias), int(bool(delta_softplus)), _ptr(conv_w), _ptr(conv_b), K,
+        _ptr(h0), _ptr(y), _ptr(hf), int(nthreads or default_threads()))
+    if rc != 0:
+        raise ValueError("oracle_selective_scan_f64 rejected the sizes")
+    return y, hf
+
+
+def causal_conv1d_silu(x, w, bias=None, nthreads: Optional[int] = None):
+    """u = silu(causal depthwise conv1d(x, w) + bias); x (B,L,D), w (D,K)."""
+    x = _f64(x)
+    Bsz, L, D = x.shape
+    w = _f64(w)
+    K = w.shape[1]
+    w = _f64(w, (D, K))
+    bias = _f64(bias, (D,))
+    u = np.zeros_like(x)
+    rc = _load().oracle_causal_conv1d_silu_f64(Bsz, L, D, K, _ptr(x), _ptr(w), _ptr(bias),
+                                               _ptr(u), int(nthreads or default_threads()))
+    if rc != 0:
+        raise ValueError("oracle_causal_conv1d_silu_f64 rejected the sizes")
+    return u
+
+
+def state_update(state, x, delta, A, Bm, Cm, Dskip=None, z=None, delta_bias=None,
+                 delta_softplus: bool = False, nthreads: Optional[int] = None):
+    """One decode step.  Returns (y, new_state); the input state is not modified.
+
+    state: (B, D, N); x, delta, z: (B, D); A: (D, N); Bm, Cm: (B, N).
+    """
+    st = _f64(state).copy()
+    Bsz, D, N = st.shape
+    x = _f64(x, (Bsz, D))
+    delta = _f64(delta, (Bsz, D))
+    A = _f64(A, (D, N))
+    Bm = _f64(Bm, (Bsz, N))
+    Cm = _f64(Cm, (Bsz, N))
+    Dskip = _f64(Dskip, (D,))
+    z = _f64(z, (Bsz, D))
+    delta_bias = _f64(delta_bias, (D,))
+    y = np.zeros((Bsz, D), np.float64)
+    rc = _load().oracle_state_update_f64(Bsz, D, N, _ptr(st), _ptr(x), _ptr(delta), _ptr(A),
+                                         _ptr(Bm), _ptr(Cm), _ptr(Dskip), _ptr(z),
+                                         _ptr(delta_bias), int(bool(delta_softplus)), _ptr(y),
+                                         int(nthreads or default_threads()))
+    if rc != 0:
+        raise ValueError("oracle_state_update_f64 rejected the sizes")
+    return y, st

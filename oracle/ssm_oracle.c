@@ -1,0 +1,192 @@
+/*
+ * ssm_oracle.c -- plain fp64 CPU reference of the Mamba-1 selective scan (S6).
+ *
+ * TEST INFRASTRUCTURE ONLY.  This file is the oracle that the HIP library is
+ * checked against.  Only the test suite, the smoke check and the CPU-baseline
+ * leg of the benchmark may load it; the library itself never does, and the two
+ * share no code, header, table or helper.
+ *
+ * It is written from the equations on these pages, as direct nested loops over
+ * batch, channel, time and state, in double precision, with libm's exp/expm1/
+ * log1p and no reordering beyond what the definitions state:
+ *
+ *   [P1] "Mamba: Linear-Time Sequence Modeling with Selective State Spaces"
+ *        (paper summary page): sec. 4a (block: Conv1d -> SiLU -> SSM -> x SiLU
+ *        gate), sec. 4b eq. (1a)/(1b) (continuous SSM), eq. (4) (ZOH rule),
+ *        eq. (2a)/(2b) (recurrence), Algorithm 2 (S6 shapes: A (D,N), B and C
+ *        (B,L,N), Delta (B,L,D)), the softplus tau_Delta parameterisation.
+ *   [P2] "2. Mamba 상세" (EulerStack mixer tutorial): the YAML example
+ *        (d_conv: 4, ssm_state kept for inference).
+ *   [P4] "14.1 SSM(State Space Models)과 Mamba 아키텍처의 부상": sec. 3.1
+ *        (y = C h + D x, the D skip term), sec. 3.2 (ZOH), sec. 4.1 (selection).
+ *
+ * Readings taken where the pages leave a step open (each one is listed in the
+ * design notes):
+ *   - B-bar is the exact ZOH form of eq. (4) for a diagonal A, element-wise
+ *     (Delta a)^-1 (exp(Delta a) - 1) Delta b; at Delta a == 0 the removable
+ *     singularity takes its limit, B-bar = Delta b.
+ *   - the D skip multiplies the SSM input u (after the conv prologue if any).
+ *   - the gate multiplies the whole output: y = (C h + D u) * silu(z).
+ *   - the initial state is zero unless h0 is given.
+ *   - the conv prologue is a causal cross-correlation with zero left padding:
+ *     u_t = silu(sum_k w[k] x_{t-(K-1)+k} + b), so w[K-1] weighs the current
+ *     token.
+ *
+ * All arrays are row-major with the last index fastest, host memory, double.
+ * Threads (OpenMP) split only independent (batch, channel) pairs.
+ */
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+#include <stdlib.h>
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* SiLU (swish), the activation named in [P1] sec. 4a / 4d: v * sigmoid(v). */
+static double silu(double v) { return v / (1.0 + exp(-v)); }
+
+/* softplus, the tau_Delta of [P1] Algorithm 2, in the overflow-free form
+ * max(v,0) + log(1 + exp(-|v|)). */
+static double softplus(double v) { return (v > 0 ? v : 0.0) + log1p(exp(-fabs(v))); }
+
+/* ZOH discretisation of one diagonal entry, [P1] eq. (4) / [P4] sec. 3.2:
+ *   Abar = exp(Delta a),  Bbar = (Delta a)^-1 (exp(Delta a) - 1) Delta b.
+ * expm1 keeps the bracket accurate for small Delta a; at Delta a == 0 the
+ * quotient takes its limit 1. */
+static void zoh(double dt, double a, double b, double *abar, double *bbar)
+{
+    double za = dt * a;
+    *abar = exp(za);
+    double phi = (za == 0.0) ? 1.0 : expm1(za) / za;
+    *bbar = phi * dt * b;
+}
+
+/* Causal depthwise conv1d(K) + SiLU on one channel's input at time t.
+ * x points at element (b, 0, d); consecutive times are `stride` apart. */
+static double conv_silu_at(const double *x, int64_t stride, int64_t t, int64_t K,
+                           const double *wd, double bias)
+{
+    double acc = bias;
+    for (int64_t k = 0; k < K; ++k) {
+        int64_t s = t - (K - 1) + k;
+        if (s >= 0) acc += wd[k] * x[s * stride];
+    }
+    return silu(acc);
+}
+
+int oracle_abi_version(void) { return 1; }
+
+/*
+ * Selective scan forward ([P1] Algorithm 2 with the block's gate and the
+ * [P4] sec. 3.1 skip term):
+ *   u_t   = x_t, or conv1d+SiLU of x when conv_w is given          ([P1] 4a)
+ *   dt    = delta_t, or softplus(delta_t + bias) when requested     ([P1] Alg. 2)
+ *   h_t,n = Abar h_{t-1},n + Bbar u_t         with eq. (4) per n    ([P1] eq. 2a)
+ *   y_t   = (sum_n C_t,n h_t,n + Dskip u_t) * silu(z_t)             ([P1] eq. 2b, 4a)
+ *
+ * Shapes: x, delta, z, y (B,L,D); A (D,N); Bm, Cm (B,L,N); Dskip, delta_bias,
+ * conv_b (D); conv_w (D,K); h0, h_final (B,D,N).  Optional inputs may be NULL.
+ * Returns 0, or -1 on a bad size.
+ */
+int oracle_selective_scan_f64(int64_t Bsz, int64_t L, int64_t D, int64_t N,
+                              const double *x, const double *delta, const double *A,
+                              const double *Bm, const double *Cm, const double *Dskip,
+                              const double *z, const double *delta_bias, int delta_softplus,
+                              const double *conv_w, const double *conv_b, int64_t conv_k,
+                              const double *h0, double *y, double *h_final, int nthreads)
+{
+    if (Bsz < 0 || L < 0 || D < 0 || N < 1 || (conv_w && conv_k < 1)) return -1;
+    if (nthreads < 1) nthreads = 1;
+    int64_t nch = Bsz * D;
+#pragma omp parallel for num_threads(nthreads) schedule(dynamic, 1)
+    for (int64_t ch = 0; ch < nch; ++ch) {
+        int64_t b = ch / D, d = ch % D;
+        double *h = (double *)malloc(sizeof(double) * (size_t)N);
+        for (int64_t n = 0; n < N; ++n) h[n] = h0 ? h0[(b * D + d) * N + n] : 0.0;
+        const double *xbd = x + b * L * D + d;
+        for (int64_t t = 0; t < L; ++t) {
+            int64_t i = (b * L + t) * D + d;
+            double u = conv_w ? conv_silu_at(xbd, D, t, conv_k, conv_w + d * conv_k,
+                                             conv_b ? conv_b[d] : 0.0)
+                              : x[i];
+            double dt = delta[i];
+            if (delta_softplus) dt = softplus(dt + (delta_bias ? delta_bias[d] : 0.0));
+            double acc = 0.0;
+            for (int64_t n = 0; n < N; ++n) {
+                double abar, bbar;
+                zoh(dt, A[d * N + n], Bm[(b * L + t) * N + n], &abar, &bbar);
+                h[n] = abar * h[n] + bbar * u;
+                acc += Cm[(b * L + t) * N + n] * h[n];
+            }
+            double yv = acc + (Dskip ? Dskip[d] * u : 0.0);
+            if (z) yv *= silu(z[i]);
+            y[i] = yv;
+        }
+        if (h_final)
+            for (int64_t n = 0; n < N; ++n) h_final[(b * D + d) * N + n] = h[n];
+        free(h);
+    }
+    return 0;
+}
+
+/*
+ * Depthwise causal conv1d(K) followed by SiLU ([P1] sec. 4a, [P2] d_conv: 4):
+ *   u[b,t,d] = silu(sum_k w[d,k] x[b,t-(K-1)+k,d] + bias[d]), x at t<0 is 0.
+ * x, u (B,L,D); w (D,K); bias (D) or NULL.
+ */
+int oracle_causal_conv1d_silu_f64(int64_t Bsz, int64_t L, int64_t D, int64_t K,
+                                  const double *x, const double *w, const double *bias,
+                                  double *u, int nthreads)
+{
+    if (Bsz < 0 || L < 0 || D < 0 || K < 1) return -1;
+    if (nthreads < 1) nthreads = 1;
+    int64_t nch = Bsz * D;
+#pragma omp parallel for num_threads(nthreads) schedule(static)
+    for (int64_t ch = 0; ch < nch; ++ch) {
+        int64_t b = ch / D, d = ch % D;
+        const double *xbd = x + b * L * D + d;
+        for (int64_t t = 0; t < L; ++t)
+            u[(b * L + t) * D + d] = conv_silu_at(xbd, D, t, K, w + d * K, bias ? bias[d] : 0.0);
+    }
+    return 0;
+}
+
+/*
+ * One recurrent (decode) step ([P1] eq. (2a)/(2b) used as a recurrence, one
+ * token at a time, with the state carried between calls as in [P2]'s
+ * ssm_state option):
+ *   state[b,d,n] <- Abar state[b,d,n] + Bbar x[b,d]     (eq. 4 per n)
+ *   y[b,d]        = (sum_n C[b,n] state[b,d,n] + Dskip[d] x[b,d]) * silu(z[b,d])
+ * state (B,D,N) is updated in place; x, delta, z, y (B,D); Bm, Cm (B,N).
+ */
+int oracle_state_update_f64(int64_t Bsz, int64_t D, int64_t N, double *state,
+                            const double *x, const double *delta, const double *A,
+                            const double *Bm, const double *Cm, const double *Dskip,
+                            const double *z, const double *delta_bias, int delta_softplus,
+                            double *y, int nthreads)
+{
+    if (Bsz < 0 || D < 0 || N < 1) return -1;
+    if (nthreads < 1) nthreads = 1;
+    int64_t nch = Bsz * D;
+#pragma omp parallel for num_threads(nthreads) schedule(static)
+    for (int64_t ch = 0; ch < nch; ++ch) {
+        int64_t b = ch / D, d = ch % D;
+        double u = x[ch];
+        double dt = delta[ch];
+        if (delta_softplus) dt = softplus(dt + (delta_bias ? delta_bias[d] : 0.0));
+        double *h = state + ch * N;
+        double acc = 0.0;
+        for (int64_t n = 0; n < N; ++n) {
+            double abar, bbar;
+            zoh(dt, A[d * N + n], Bm[b * N + n], &abar, &bbar);
+            h[n] = abar * h[n] + bbar * u;
+            acc += Cm[b * N + n] * h[n];
+        }
+        double yv = acc + (Dskip ? Dskip[d] * u : 0.0);
+        if (z) yv *= silu(z[ch]);
+        y[ch] = yv;
+    }
+    return 0;
+}

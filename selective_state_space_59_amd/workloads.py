@@ -1,0 +1,165 @@
+"""Seeded synthetic inputs for the selective scan and the decode step.
+
+This module holds only the input recipe (shapes, distributions, seeds).  It
+computes none of the scan's arithmetic, so the HIP path, the tests and the
+benchmark can all draw the same inputs from it while the oracle stays an
+independent implementation.
+
+Shapes follow Algorithm 2 and the block table of sec. 4a on the paper summary
+page "Mamba: Linear-Time Sequence Modeling with Selective State Spaces":
+x, delta, z: (B, L, D); B, C: (B, L, N); A: (D, N); plus the D skip (D,),
+conv1d weights (D, K) and states (B, D, N).  A uses the S4D-Real rule of that
+page's sec. 4d, A[d, n] = -(n + 1), for every channel.
+
+Recipe: every tensor is drawn in float32 from a torch.Generator seeded with
+the config's seed, in a fixed order (x, delta, B, C, z, Dskip, conv_w, h0),
+on the requested device, then rounded to the I/O dtype (round to nearest
+even).  delta = softplus(N(0,1) - shift) is formed in float32 before the
+rounding, so the kernels receive an already activated step size.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Dict, Optional
+
+import torch
+import torch.nn.functional as F
+
+
+@dataclasses.dataclass(frozen=True)
+class ScanConfig:
+    name: str
+    batch: int
+    seqlen: int
+    dim: int
+    dstate: int
+    io_dtype: torch.dtype
+    seed: int
+    delta_shift: float = 2.0
+    gate: bool = True
+    skip: bool = True
+    conv_k: int = 0
+    conv_std: float = 0.5
+    final_state: bool = True
+    h0: bool = False
+    description: str = ""
+
+    @property
+    def elems(self) -> int:
+        return self.batch * self.seqlen * self.dim
+
+
+@dataclasses.dataclass(frozen=True)
+class DecodeConfig:
+    name: str
+    batch: int
+    dim: int
+    dstate: int
+    steps: int
+    io_dtype: torch.dtype
+    seed: int
+    delta_shift: float = 2.0
+    gate: bool = True
+    skip: bool = True
+    description: str = ""
+
+
+# The five workloads.  The first is small enough for the oracle to finish in
+# well under a second; the others are full-size layer shapes.
+C1_TINY = ScanConfig("c1_tiny_f32", 1, 64, 16, 4, torch.float32, seed=0,
+                     description="tiny S6 scan, fp32 I/O, B=1 L=64 D=16 N=4")
+C2_130M = ScanConfig("c2_mamba130m_layer", 8, 2048, 1536, 16, torch.bfloat16, seed=1,
+                     description="Mamba-130M-like layer scan (d_model 768, expand 2), bf16 I/O")
+C3_2P8B_CONV = ScanConfig("c3_mamba2p8b_conv", 4, 4096, 5120, 16, torch.bfloat16, seed=2,
+                          conv_k=4, description="Mamba-2.8B-like layer, fused causal "
+                          "conv1d(k=4)+SiLU prologue, bf16 I/O")
+C4_DNA_1M = ScanConfig("c4_dna_1m", 1, 1 << 20, 1024, 16, torch.bfloat16, seed=3,
+                       delta_shift=3.0, description="1M-token DNA-like scan, bf16 I/O, "
+                       "final state")
+C5_DECODE = DecodeConfig("c5_decode", 256, 5120, 16, 64, torch.bfloat16, seed=4,
+                         description="decode state_update, fp32 state (256,5120,16), "
+                         "64 single-token steps")
+
+SCAN_CONFIGS = {c.name: c for c in (C1_TINY, C2_130M, C3_2P8B_CONV, C4_DNA_1M)}
+
+
+def _gen(device, seed: int) -> torch.Generator:
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    return g
+
+
+def _randn(shape, g, device, std: float = 1.0, shift: float = 0.0):
+    t = torch.randn(*shape, generator=g, device=device, dtype=torch.float32)
+    if std != 1.0:
+        t.mul_(std)
+    if shift != 0.0:
+        t.sub_(shift)
+    return t
+
+
+def s4d_real_A(dim: int, dstate: int, device="cpu") -> torch.Tensor:
+    """A[d, n] = -(n + 1) for every channel (sec. 4d, S4D-Real)."""
+    row = -torch.arange(1, dstate + 1, dtype=torch.float32, device=device)
+    return row.expand(dim, dstate).contiguous()
+
+
+def make_scan_inputs(batch: int, seqlen: int, dim: int, dstate: int,
+                     io_dtype: torch.dtype = torch.bfloat16, seed: int = 0,
+                     device="cpu", delta_shift: float = 2.0, gate: bool = True,
+                     skip: bool = True, conv_k: int = 0, conv_std: float = 0.5,
+                     h0: bool = False, A: Optional[torch.Tensor] = None
+                     ) -> Dict[str, Optional[torch.Tensor]]:
+    """Draw one scan input set.  Returns a dict keyed like the scan arguments."""
+    g = _gen(device, seed)
+    shp = (batch, seqlen, dim)
+    x = _randn(shp, g, device).to(io_dtype)
+    delta = F.softplus(_randn(shp, g, device, shift=delta_shift)).to(io_dtype)
+    Bm = _randn((batch, seqlen, dstate), g, device).to(io_dtype)
+    Cm = _randn((batch, seqlen, dstate), g, device).to(io_dtype)
+    z = _randn(shp, g, device).to(io_dtype) if gate else None
+    Dskip = _randn((dim,), g, device) if skip else None
+    conv_w = _randn((dim, conv_k), g, device, std=conv_std) if conv_k else None
+    hinit = _randn((batch, dim, dstate), g, device) if h0 else None
+    if A is None:
+        A = s4d_real_A(dim, dstate, device)
+    return dict(x=x, delta=delta, A=A, Bm=Bm, Cm=Cm, Dskip=Dskip, z=z,
+                conv_w=conv_w, conv_b=None, h0=hinit)
+
+
+def make_config_inputs(cfg: ScanConfig, device="cpu", **overrides):
+    kw = dict(batch=cfg.batch, seqlen=cfg.seqlen, dim=cfg.dim, dstate=cfg.dstate,
+              io_dtype=cfg.io_dtype, seed=cfg.seed, delta_shift=cfg.delta_shift,
+              gate=cfg.gate, skip=cfg.skip, conv_k=cfg.conv_k, conv_std=cfg.conv_std,
+              h0=cfg.h0)
+    kw.update(overrides)
+    return make_scan_inputs(device=device, **kw)
+
+
+def make_decode_inputs(batch: int, dim: int, dstate: int, steps: int,
+                       io_dtype: torch.dtype = torch.bfloat16, seed: int = 4,
+                       device="cpu", delta_shift: float = 2.0, gate: bool = True,
+                       skip: bool = True) -> Dict[str, Optional[torch.Tensor]]:
+    """Initial fp32 state ~ N(0,1) plus `steps` fresh single-token inputs.
+
+    x, delta, z: (steps, B, D); Bm, Cm: (steps, B, N); state0: (B, D, N).
+    """
+    g = _gen(device, seed)
+    state0 = _randn((batch, dim, dstate), g, device)
+    shp = (steps, batch, dim)
+    x = _randn(shp, g, device).to(io_dtype)
+    delta = F.softplus(_randn(shp, g, device, shift=delta_shift)).to(io_dtype)
+    Bm = _randn((steps, batch, dstate), g, device).to(io_dtype)
+    Cm = _randn((steps, batch, dstate), g, device).to(io_dtype)
+    z = _randn(shp, g, device).to(io_dtype) if gate else None
+    Dskip = _randn((dim,), g, device) if skip else None
+    A = s4d_real_A(dim, dstate, device)
+    return dict(state0=state0, x=x, delta=delta, A=A, Bm=Bm, Cm=Cm, z=z, Dskip=Dskip)
+
+
+def make_decode_config_inputs(cfg: DecodeConfig, device="cpu", **overrides):
+    kw = dict(batch=cfg.batch, dim=cfg.dim, dstate=cfg.dstate, steps=cfg.steps,
+              io_dtype=cfg.io_dtype, seed=cfg.seed, delta_shift=cfg.delta_shift,
+              gate=cfg.gate, skip=cfg.skip)
+    kw.update(overrides)
+    return make_decode_inputs(device=device, **kw)
