@@ -1,0 +1,267 @@
+"""Benchmark of the selective-scan hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extras] [--no-cpu-baseline]
+
+A step is one selective-scan forward over one batch of the Mamba-130M-like
+layer workload (B=8, L=2048, D=1536, N=16, bf16 I/O, fp32 state, SiLU gate,
+D skip).  Three independent input sets (3 x 202 MB) rotate between steps, so
+the 256 MB last-level cache cannot hold the next step's inputs.  Inputs are
+resident in HBM before the timed region starts.
+
+Prints ONE JSON line.  `value` is algorithmic HBM bytes per second (GB/s):
+the minimum bytes a scan must move (each of x, delta, z read once, y written
+once, the B/C rows read once, A and D once) divided by the time per step.
+`roofline` relates the kernel to the MI355X HBM peak and to the vector-ALU
+peak; `cpu_baseline` times the fp64 oracle on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+# Vector ALU: 256 CUs x 4 SIMDs x 16 fp32 lanes x 2.4 GHz (no packed-fp32 forms).
+VALU_PEAK_LANE_OPS = 256 * 4 * 16 * 2.4e9
+
+
+def scan_algorithmic_bytes(B, L, D, N, io_bytes, conv_k=0, final_state=False, h0=False,
+                           gate=True, skip=True):
+    """Minimum HBM bytes of one scan: x, delta, (z) read and y written once per element;
+    B and C once per (b, t); A, D skip and conv weights once; states once if used."""
+    elems = B * L * D
+    per_elem = (3 + (1 if gate else 0)) * io_bytes
+    total = elems * per_elem + 2 * B * L * N * io_bytes + 4 * D * N
+    if skip:
+        total += 4 * D
+    if conv_k:
+        total += 4 * D * conv_k
+    if final_state:
+        total += 4 * B * D * N
+    if h0:
+        total += 4 * B * D * N
+    return total
+
+
+def decode_algorithmic_bytes(B, D, N, io_bytes, gate=True, skip=True):
+    """One decode step: state read + written, x, delta, (z) read, y written, B/C rows, A, D."""
+    return (8 * B * D * N + (3 + (1 if gate else 0)) * io_bytes * B * D + 2 * B * N * io_bytes
+            + 4 * D * N + (4 * D if skip else 0))
+
+
+def _load_metric():
+    try:
+        with open(os.path.join(ROOT, "BASELINE.json")) as f:
+            return json.load(f).get("metric")
+    except Exception:
+        return "selective-scan HBM GB/s"
+
+
+def _counter_traffic(kernel_key):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were taken on
+    the current kernel source (matched by hash); else None."""
+    path = os.path.join(ROOT, "profiles", "hbm_counters.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except Exception:
+        return None
+    ent = rec.get(kernel_key)
+    if not ent:
+        return None
+    from selective_state_space_59_amd import build as B
+    if ent.get("source_hash") != B.source_hash():
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def time_launches(fn, steps, warmup):
+    import torch
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(steps):
+        fn(i)
+    stop.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(stop) / steps  # ms per launch
+
+
+def bench_scan(cfg, steps, warmup, nsets=3, final_state=False):
+    import torch
+    import selective_state_space_59_amd as ssm
+    from selective_state_space_59_amd import workloads as W
+    dev = "cuda:0"
+    sets = [W.make_config_inputs(cfg, device=dev, seed=cfg.seed + 100 * k) for k in range(nsets)]
+    ys = [torch.empty_like(s["x"]) for s in sets]
+    hfs = [torch.empty(cfg.batch, cfg.dim, cfg.dstate, device=dev) if final_state else None
+           for _ in sets]
+
+    def run(i):
+        s = sets[i % nsets]
+        ssm.selective_scan_fwd(s["x"], s["delta"], s["A"], s["Bm"], s["Cm"], Dskip=s["Dskip"],
+                               z=s["z"], conv_w=s["conv_w"], y=ys[i % nsets],
+                               h_final=hfs[i % nsets])
+
+    ms = time_launches(run, steps, warmup)
+    nbytes = scan_algorithmic_bytes(cfg.batch, cfg.seqlen, cfg.dim, cfg.dstate,
+                                    2 if cfg.io_dtype == torch.bfloat16 else 4, cfg.conv_k,
+                                    final_state, gate=cfg.gate, skip=cfg.skip)
+    first = sets[0]
+    del sets, ys, hfs
+    torch.cuda.empty_cache()
+    return ms, nbytes, first
+
+
+def bench_decode(cfg, reps=3):
+    import torch
+    import selective_state_space_59_amd as ssm
+    from selective_state_space_59_amd import workloads as W
+    dev = "cuda:0"
+    inp = W.make_decode_config_inputs(cfg, device=dev)
+    st = inp["state0"].clone()
+    ys = torch.empty(cfg.steps, cfg.batch, cfg.dim, dtype=cfg.io_dtype, device=dev)
+
+    def run_all(_):
+        for t in range(cfg.steps):
+            ssm.state_update(st, inp["x"][t], inp["delta"][t], inp["A"], inp["Bm"][t],
+                             inp["Cm"][t], Dskip=inp["Dskip"], z=inp["z"][t], y=ys[t])
+
+    hot_ms = time_launches(run_all, reps, 1) / cfg.steps
+    # Cold: evict the last-level cache (write 1 GiB) before each timed step.
+    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    cold = []
+    for t in range(cfg.steps):
+        flush.fill_(float(t))
+        start.record()
+        ssm.state_update(st, inp["x"][t], inp["delta"][t], inp["A"], inp["Bm"][t],
+                         inp["Cm"][t], Dskip=inp["Dskip"], z=inp["z"][t], y=ys[t])
+        stop.record()
+        torch.cuda.synchronize()
+        cold.append(start.elapsed_time(stop))
+    cold.sort()
+    cold_ms = cold[len(cold) // 2]
+    nbytes = decode_algorithmic_bytes(cfg.batch, cfg.dim, cfg.dstate,
+                                      2 if cfg.io_dtype == torch.bfloat16 else 4)
+    del inp, st, ys, flush
+    torch.cuda.empty_cache()
+    return hot_ms, cold_ms, nbytes
+
+
+def cpu_baseline(inp, cfg):
+    """The fp64 oracle as it stands, on the host cores, over the first `Lb` steps of every
+    channel of one input set (the whole workload when that fits the time budget)."""
+    import numpy as np
+    import oracle
+    nthreads = oracle.default_threads()
+    Lb = cfg.seqlen
+    f = lambda t: None if t is None else t[:, :Lb].double().cpu().numpy()
+    g = lambda t: None if t is None else t.double().cpu().numpy()
+    args = (f(inp["x"]), f(inp["delta"]), g(inp["A"]), f(inp["Bm"]), f(inp["Cm"]))
+    t0 = time.perf_counter()
+    oracle.selective_scan(*args, Dskip=g(inp["Dskip"]), z=f(inp["z"]), conv_w=g(inp["conv_w"]),
+                          nthreads=nthreads)
+    dt = time.perf_counter() - t0
+    elems = cfg.batch * Lb * cfg.dim
+    nbytes = scan_algorithmic_bytes(cfg.batch, Lb, cfg.dim, cfg.dstate,
+                                    2 if str(inp["x"].dtype).endswith("bfloat16") else 4,
+                                    cfg.conv_k, gate=cfg.gate, skip=cfg.skip)
+    return dict(value=round(nbytes / dt / 1e9, 4), unit="GB/s", cores=nthreads, kind="oracle",
+                elems_per_s=round(elems / dt, 1), seconds=round(dt, 3),
+                sample="one full pass of the workload (B=%d, L=%d, D=%d, N=%d), fp64, "
+                       "%d threads over independent channels" % (cfg.batch, Lb, cfg.dim,
+                                                                  cfg.dstate, nthreads))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-extras", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: the selective scan is benchmarked on a single "
+              "MI355X (got --gpus %d)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from selective_state_space_59_amd import workloads as W
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+
+    cfg = W.C2_130M
+    print("bench: %s, %d warmup + %d timed steps" % (cfg.name, args.warmup, args.steps),
+          file=sys.stderr, flush=True)
+    ms, nbytes, first = bench_scan(cfg, args.steps, args.warmup)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    elems = cfg.elems
+    upd = elems * cfg.dstate
+    traffic = _counter_traffic("scan_" + cfg.name)
+    roof = dict(bound="hbm", achieved=round(gbs, 2), peak=HBM_PEAK_GBS, unit="GB/s",
+                frac=round(gbs / HBM_PEAK_GBS, 4), traffic=traffic,
+                algorithmic_bytes_per_launch=nbytes, launch_ms=round(ms, 5),
+                state_updates_per_s=round(upd / (ms * 1e-3), 1))
+
+    out = {
+        "metric": _load_metric(),
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "batch": cfg.batch, "seq_len": cfg.seqlen,
+                   "dim": cfg.dim, "dstate": cfg.dstate, "io_dtype": "bf16",
+                   "gate": cfg.gate, "skip": cfg.skip, "input_sets_rotated": 3,
+                   "parallelism": "single GPU"},
+        "elems_per_s": round(elems / (ms * 1e-3), 1),
+        "roofline": roof,
+    }
+
+    if not args.no_extras:
+        extra = {}
+        for c in (W.C3_2P8B_CONV, W.C4_DNA_1M):
+            print("bench extra: %s" % c.name, file=sys.stderr, flush=True)
+            reps = 3 if c.seqlen > 100000 else 5
+            cms, cb, _ = bench_scan(c, reps, 1, nsets=1, final_state=c.final_state)
+            extra[c.name] = dict(ms=round(cms, 4), gbs=round(cb / (cms * 1e-3) / 1e9, 2),
+                                 frac_hbm=round(cb / (cms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                                 elems_per_s=round(c.elems / (cms * 1e-3), 1),
+                                 algorithmic_bytes=cb)
+        print("bench extra: %s" % W.C5_DECODE.name, file=sys.stderr, flush=True)
+        hot, cold, db = bench_decode(W.C5_DECODE)
+        extra[W.C5_DECODE.name] = dict(
+            hot_ms_per_step=round(hot, 5), cold_ms_per_step=round(cold, 5),
+            hot_steps_per_s=round(1e3 / hot, 1), cold_steps_per_s=round(1e3 / cold, 1),
+            cold_gbs=round(db / (cold * 1e-3) / 1e9, 2),
+            cold_frac_hbm=round(db / (cold * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            hot_gbs=round(db / (hot * 1e-3) / 1e9, 2), algorithmic_bytes_per_step=db)
+        out["extra"] = extra
+
+    if not args.no_cpu_baseline:
+        print("bench: cpu baseline (oracle)", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(first, cfg)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,194 @@
+/*
+ * ssm.h -- C ABI of the MI355X (gfx950) selective-scan library.
+ *
+ * The library computes the Mamba-1 selective state-space layer (S6) on one
+ * GPU with hand-written HIP kernels:
+ *   - ssm_selective_scan_fwd: the whole-sequence scan (prefill), optionally
+ *     with a fused depthwise causal conv1d + SiLU prologue and a final-state
+ *     output;
+ *   - ssm_state_update: one recurrent (decode) step on a resident state;
+ *   - ssm_causal_conv1d_silu: the conv prologue on its own.
+ *
+ * The operations are defined on these pages (cited by title and section):
+ *   [P1] "Mamba: Linear-Time Sequence Modeling with Selective State Spaces"
+ *        (paper summary page): sec. 4a (Mamba block: Conv1d -> SiLU -> SSM,
+ *        output x SiLU(gate)), sec. 4b eq. (1a)/(1b), eq. (4) (ZOH),
+ *        eq. (2a)/(2b) (recurrence), Algorithm 2 (S6 shapes), sec. 4d (A
+ *        diagonal and real, N = 16, E = 2).
+ *   [P2] "2. Mamba 상세" (EulerStack mixer tutorial): d_conv: 4 and the
+ *        ssm_state kept between inference steps.
+ *   [P4] "14.1 SSM(State Space Models)과 Mamba 아키텍처의 부상": sec. 3.1
+ *        (y = C h + D x, the D skip), sec. 3.2 (ZOH), sec. 4.1 (Delta =
+ *        softplus(parameter + projection)).
+ *
+ * Conventions common to every entry point
+ *   - Every tensor pointer is a DEVICE pointer into memory the caller owns
+ *     (e.g. a torch tensor's data_ptr()).  The library allocates nothing,
+ *     keeps no state between calls and never frees caller memory.
+ *   - Tensors are dense and row-major with the last index fastest; element
+ *     strides are implied by the shapes.  Pointers must be aligned to their
+ *     element size (2 bytes for bf16, 4 for fp32).
+ *   - `stream` is a hipStream_t passed as void*; NULL means the default
+ *     stream.  Calls are asynchronous with respect to the host: they enqueue
+ *     kernels on `stream` and return.  Faults inside a kernel surface at the
+ *     caller's next synchronisation on that stream.
+ *   - Argument checking is complete before any HIP call: on an error the
+ *     function returns a status other than SSM_OK, enqueues nothing and
+ *     writes nothing.  ssm_last_error_message() then describes the failure
+ *     (per calling thread).  After launching, a launch failure reported by
+ *     the runtime returns SSM_ERR_HIP.
+ *   - No C++ exception crosses this interface.  All entry points are
+ *     re-entrant and thread-safe; calls that write the same output memory
+ *     concurrently race, as with any kernel.
+ *   - Sizes: a batch or sequence length of 0 is a valid empty call and
+ *     returns SSM_OK without launching (the final state, if requested, is
+ *     then a copy of h0, or zeros).  Negative sizes give SSM_ERR_BAD_SHAPE.
+ *   - Arithmetic is fp32 throughout, on fp32 or bf16 inputs; bf16 results
+ *     are rounded to nearest even.  State, A, D, bias and conv weights are
+ *     always fp32.
+ */
+#ifndef SSM_MI355X_H
+#define SSM_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SSM_ABI_VERSION 1
+#define SSM_MAX_DSTATE 16 /* largest N the kernels hold in registers */
+#define SSM_MAX_CONV_K 4  /* largest conv1d kernel width */
+
+typedef enum ssm_status {
+    SSM_OK = 0,
+    SSM_ERR_NULL_ARG = 1,    /* a required pointer is NULL                   */
+    SSM_ERR_BAD_SHAPE = 2,   /* a negative or inconsistent size              */
+    SSM_ERR_BAD_DTYPE = 3,   /* io_dtype is not one of ssm_dtype_t           */
+    SSM_ERR_UNSUPPORTED = 4, /* N or K above the compiled maximum, bad flags */
+    SSM_ERR_ALIAS = 5,       /* an output overlaps an input or another output*/
+    SSM_ERR_WORKSPACE = 6,   /* workspace missing, too small or misaligned  */
+    SSM_ERR_HIP = 7,         /* the HIP runtime reported an error            */
+    SSM_ERR_ALIGN = 8        /* a pointer is not aligned to its element size */
+} ssm_status_t;
+
+typedef enum ssm_dtype {
+    SSM_F32 = 0, /* IEEE binary32 */
+    SSM_BF16 = 1 /* bfloat16 (upper half of a binary32) */
+} ssm_dtype_t;
+
+/*
+ * Arguments of the selective scan, [P1] Algorithm 2 with the gate of sec. 4a
+ * and the skip of [P4] sec. 3.1.  Per batch b, channel d and state index n:
+ *
+ *   u[b,t,d]   = x[b,t,d], or, when conv_w != NULL, the fused prologue
+ *                silu(sum_{k<K} conv_w[d,k] x[b,t-(K-1)+k,d] + conv_b[d])
+ *                with x at negative times taken as 0 ([P1] sec. 4a, [P2]).
+ *   dt[b,t,d]  = delta[b,t,d], or softplus(delta[b,t,d] + delta_bias[d])
+ *                when delta_softplus != 0 ([P1] Algorithm 2).
+ *   Abar       = exp(dt A[d,n])                                 (eq. 4)
+ *   Bbar       = (dt A[d,n])^-1 (exp(dt A[d,n]) - 1) dt Bm[b,t,n]  (eq. 4),
+ *                = dt Bm[b,t,n] where A[d,n] == 0 (the limit)
+ *   h[b,d,n]   = Abar h[b,d,n] + Bbar u[b,t,d], from h0 (or 0)  (eq. 2a)
+ *   y[b,t,d]   = (sum_n Cm[b,t,n] h[b,d,n] + Dskip[d] u[b,t,d])
+ *                * silu(z[b,t,d])                               (eq. 2b, 4a)
+ *   h_final    = h after the last time step.
+ */
+typedef struct ssm_scan_args {
+    int64_t batch;          /* B >= 0                                         */
+    int64_t seqlen;         /* L >= 0                                         */
+    int64_t dim;            /* D >= 1 (channels, E*d_model in the block)      */
+    int64_t dstate;         /* N, 1 <= N <= SSM_MAX_DSTATE                    */
+    int32_t io_dtype;       /* ssm_dtype_t of x, delta, Bm, Cm, z and y       */
+    int32_t delta_softplus; /* 0: delta is the step; 1: softplus(delta+bias) */
+    int64_t conv_k;         /* 0: no prologue; 1..SSM_MAX_CONV_K: fused conv  */
+    const void *x;          /* (B,L,D) io_dtype, required                     */
+    const void *delta;      /* (B,L,D) io_dtype, required                     */
+    const void *Bm;         /* (B,L,N) io_dtype, required; shared by channels */
+    const void *Cm;         /* (B,L,N) io_dtype, required; shared by channels */
+    const void *z;          /* (B,L,D) io_dtype gate, or NULL (no gate)       */
+    const float *A;         /* (D,N) fp32, required; any finite value         */
+    const float *Dskip;     /* (D) fp32, or NULL (no skip term)               */
+    const float *delta_bias;/* (D) fp32, or NULL (= 0); used with softplus    */
+    const float *conv_w;    /* (D,conv_k) fp32; required iff conv_k > 0       */
+    const float *conv_b;    /* (D) fp32, or NULL (= 0)                        */
+    const float *h0;        /* (B,D,N) fp32 initial state, or NULL (= 0)      */
+    void *y;                /* (B,L,D) io_dtype output; required              */
+    float *h_final;         /* (B,D,N) fp32 output, or NULL (not written)     */
+    void *workspace;        /* device scratch of workspace_bytes, 256-aligned */
+    size_t workspace_bytes; /* >= ssm_selective_scan_workspace_size(args)     */
+} ssm_scan_args_t;
+
+/*
+ * Bytes of device workspace ssm_selective_scan_fwd needs for these sizes and
+ * options (0 when none is needed; only the size fields, io_dtype and the
+ * optional-output flags are read, pointers may be NULL).  The workspace holds
+ * per-chunk carries of the split sequence; its contents on entry do not
+ * matter and on return are unspecified.  Two calls in flight at once need
+ * two workspaces.  Returns (size_t)-1 for invalid sizes.
+ */
+size_t ssm_selective_scan_workspace_size(const ssm_scan_args_t *args);
+
+/*
+ * Enqueue the selective scan described above on `stream`.
+ * y must not overlap any input; h_final must not overlap any input or y.
+ * h0 may be NULL; when given it may not overlap h_final (copy first to scan
+ * in place).  Returns SSM_OK or an error status (see the conventions).
+ */
+ssm_status_t ssm_selective_scan_fwd(const ssm_scan_args_t *args, void *stream);
+
+/*
+ * Depthwise causal conv1d + SiLU, the prologue of [P1] sec. 4a with the
+ * width of [P2] (d_conv: 4):
+ *   u[b,t,d] = silu(sum_{k<K} w[d,k] x[b,t-(K-1)+k,d] + bias[d]),
+ * x at negative times taken as 0 (zero left padding; w[d,K-1] weighs the
+ * current token).  x and u: (B,L,D) of io_dtype; w: (D,K) fp32; bias: (D)
+ * fp32 or NULL.  1 <= K <= SSM_MAX_CONV_K.  u must not overlap x.
+ */
+ssm_status_t ssm_causal_conv1d_silu(int64_t batch, int64_t seqlen, int64_t dim, int64_t k,
+                                    int32_t io_dtype, const void *x, const float *w,
+                                    const float *bias, void *u, void *stream);
+
+/*
+ * One decode step, [P1] eq. (2a)/(2b) in recurrent mode on a state kept
+ * between calls ([P2] ssm_state), for every batch row b and channel d:
+ *   dt          = delta[b,d] or softplus(delta[b,d] + delta_bias[d])
+ *   state[b,d,n] <- exp(dt A[d,n]) state[b,d,n] + Bbar(dt, A[d,n], Bm[b,n]) x[b,d]
+ *   y[b,d]      = (sum_n Cm[b,n] state[b,d,n] + Dskip[d] x[b,d]) * silu(z[b,d])
+ * with Bbar as in the scan.  The state is read and written IN PLACE.
+ */
+typedef struct ssm_state_update_args {
+    int64_t batch;          /* B >= 0                                     */
+    int64_t dim;            /* D >= 1                                     */
+    int64_t dstate;         /* N, 1 <= N <= SSM_MAX_DSTATE                */
+    int32_t io_dtype;       /* ssm_dtype_t of x, delta, z, Bm, Cm, y      */
+    int32_t delta_softplus; /* as in ssm_scan_args                        */
+    float *state;           /* (B,D,N) fp32, updated in place; required   */
+    const void *x;          /* (B,D) io_dtype, required                   */
+    const void *delta;      /* (B,D) io_dtype, required                   */
+    const void *z;          /* (B,D) io_dtype, or NULL (no gate)          */
+    const void *Bm;         /* (B,N) io_dtype, required                   */
+    const void *Cm;         /* (B,N) io_dtype, required                   */
+    const float *A;         /* (D,N) fp32, required                       */
+    const float *Dskip;     /* (D) fp32, or NULL                          */
+    const float *delta_bias;/* (D) fp32, or NULL                          */
+    void *y;                /* (B,D) io_dtype output; must not overlap any input or the state */
+} ssm_state_update_args_t;
+
+ssm_status_t ssm_state_update(const ssm_state_update_args_t *args, void *stream);
+
+/* Static description of a status code (never NULL). */
+const char *ssm_status_string(ssm_status_t status);
+
+/* Description of the last failure returned on the calling thread ("" if none). */
+const char *ssm_last_error_message(void);
+
+/* SSM_ABI_VERSION of the built library. */
+int ssm_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SSM_MI355X_H */

@@ -1,0 +1,19 @@
+"""MI355X-native selective-scan (Mamba-1 S6) library.
+
+The compute path is the C-ABI HIP library libssm_hip.so (include/ssm.h); the
+`ssm` module is its thin Python binding.  The library is loaded on first use
+and its absence raises an error; nothing here computes on the CPU.
+"""
+from .ssm import (  # noqa: F401
+    SSMError,
+    abi_version,
+    causal_conv1d_silu,
+    lib,
+    selective_scan_fwd,
+    selective_scan_workspace_size,
+    state_update,
+    status_string,
+)
+
+__all__ = ["SSMError", "abi_version", "causal_conv1d_silu", "lib", "selective_scan_fwd",
+           "selective_scan_workspace_size", "state_update", "status_string"]

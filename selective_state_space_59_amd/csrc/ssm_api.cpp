@@ -1,0 +1,248 @@
+// ssm_api.cpp -- the C ABI declared in include/ssm.h: argument checking,
+// dispatch to the kernel launchers, status strings.  Nothing here allocates
+// device memory or keeps state between calls (apart from the per-thread text
+// of the last error).
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstdint>
+
+#include "ssm_internal.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+ssm_status_t fail(ssm_status_t s, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+ssm_status_t ok() {
+    g_last_error[0] = '\0';
+    return SSM_OK;
+}
+
+struct Range {
+    uintptr_t lo, hi;  // [lo, hi)
+    const char *name;
+};
+
+Range range(const void *p, int64_t count, int64_t elem, const char *name) {
+    const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+    return Range{lo, p ? lo + (uintptr_t)(count * elem) : lo, name};
+}
+
+bool overlaps(const Range &a, const Range &b) {
+    if (a.lo == a.hi || b.lo == b.hi) return false;  // empty or absent
+    return a.lo < b.hi && b.lo < a.hi;
+}
+
+int64_t io_bytes(int32_t dt) { return dt == SSM_BF16 ? 2 : 4; }
+
+bool aligned(const void *p, int64_t a) { return (reinterpret_cast<uintptr_t>(p) % (uintptr_t)a) == 0; }
+
+// Products of non-negative sizes that must stay far from int64 overflow.
+bool mul_ok(int64_t a, int64_t b, int64_t c = 1) {
+    const int64_t lim = (int64_t)1 << 60;
+    if (a == 0 || b == 0 || c == 0) return true;
+    if (a > lim / b) return false;
+    const int64_t ab = a * b;
+    return ab <= lim / c;
+}
+
+ssm_status_t check_scan_sizes(const ssm_scan_args_t *a) {
+    if (!a) return fail(SSM_ERR_NULL_ARG, "args is NULL");
+    if (a->io_dtype != SSM_F32 && a->io_dtype != SSM_BF16)
+        return fail(SSM_ERR_BAD_DTYPE, "io_dtype %d is not SSM_F32 or SSM_BF16", a->io_dtype);
+    if (a->batch < 0 || a->seqlen < 0)
+        return fail(SSM_ERR_BAD_SHAPE, "negative batch (%lld) or seqlen (%lld)",
+                    (long long)a->batch, (long long)a->seqlen);
+    if (a->dim < 1) return fail(SSM_ERR_BAD_SHAPE, "dim must be >= 1 (got %lld)", (long long)a->dim);
+    if (a->dstate < 1) return fail(SSM_ERR_BAD_SHAPE, "dstate must be >= 1 (got %lld)", (long long)a->dstate);
+    if (a->dstate > SSM_MAX_DSTATE)
+        return fail(SSM_ERR_UNSUPPORTED, "dstate %lld exceeds SSM_MAX_DSTATE (%d)",
+                    (long long)a->dstate, SSM_MAX_DSTATE);
+    if (a->conv_k < 0) return fail(SSM_ERR_BAD_SHAPE, "conv_k must be >= 0");
+    if (a->conv_k > SSM_MAX_CONV_K)
+        return fail(SSM_ERR_UNSUPPORTED, "conv_k %lld exceeds SSM_MAX_CONV_K (%d)",
+                    (long long)a->conv_k, SSM_MAX_CONV_K);
+    if (a->delta_softplus != 0 && a->delta_softplus != 1)
+        return fail(SSM_ERR_UNSUPPORTED, "delta_softplus must be 0 or 1");
+    if (!mul_ok(a->batch, a->seqlen, a->dim) || !mul_ok(a->batch, a->seqlen, a->dstate) ||
+        !mul_ok(a->batch, a->dim, a->dstate))
+        return fail(SSM_ERR_BAD_SHAPE, "sizes overflow");
+    return SSM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ssm_abi_version(void) { return SSM_ABI_VERSION; }
+
+const char *ssm_last_error_message(void) { return g_last_error; }
+
+const char *ssm_status_string(ssm_status_t s) {
+    switch (s) {
+        case SSM_OK: return "SSM_OK: success";
+        case SSM_ERR_NULL_ARG: return "SSM_ERR_NULL_ARG: a required pointer is NULL";
+        case SSM_ERR_BAD_SHAPE: return "SSM_ERR_BAD_SHAPE: a size is negative or inconsistent";
+        case SSM_ERR_BAD_DTYPE: return "SSM_ERR_BAD_DTYPE: unknown io_dtype";
+        case SSM_ERR_UNSUPPORTED: return "SSM_ERR_UNSUPPORTED: size or option beyond what the kernels support";
+        case SSM_ERR_ALIAS: return "SSM_ERR_ALIAS: an output overlaps another argument";
+        case SSM_ERR_WORKSPACE: return "SSM_ERR_WORKSPACE: workspace missing, too small or misaligned";
+        case SSM_ERR_HIP: return "SSM_ERR_HIP: the HIP runtime reported an error";
+        case SSM_ERR_ALIGN: return "SSM_ERR_ALIGN: a pointer is not aligned to its element size";
+    }
+    return "unknown ssm_status_t";
+}
+
+size_t ssm_selective_scan_workspace_size(const ssm_scan_args_t *a) {
+    if (check_scan_sizes(a) != SSM_OK) return (size_t)-1;
+    if (a->batch == 0 || a->seqlen == 0) return 0;
+    return ssm::scan_workspace_bytes(*a);
+}
+
+ssm_status_t ssm_selective_scan_fwd(const ssm_scan_args_t *a, void *stream) {
+    ssm_status_t s = check_scan_sizes(a);
+    if (s != SSM_OK) return s;
+    const int64_t B = a->batch, L = a->seqlen, D = a->dim, N = a->dstate, K = a->conv_k;
+    const int64_t es = io_bytes(a->io_dtype);
+    const bool work = B > 0 && L > 0;
+    if (work) {
+        if (!a->x) return fail(SSM_ERR_NULL_ARG, "x is NULL");
+        if (!a->delta) return fail(SSM_ERR_NULL_ARG, "delta is NULL");
+        if (!a->Bm) return fail(SSM_ERR_NULL_ARG, "Bm is NULL");
+        if (!a->Cm) return fail(SSM_ERR_NULL_ARG, "Cm is NULL");
+        if (!a->A) return fail(SSM_ERR_NULL_ARG, "A is NULL");
+        if (!a->y) return fail(SSM_ERR_NULL_ARG, "y is NULL");
+        if (K > 0 && !a->conv_w) return fail(SSM_ERR_NULL_ARG, "conv_w is NULL but conv_k > 0");
+    }
+    if (K == 0 && (a->conv_w || a->conv_b))
+        return fail(SSM_ERR_BAD_SHAPE, "conv_w/conv_b given but conv_k == 0");
+    const void *io_ptrs[] = {a->x, a->delta, a->Bm, a->Cm, a->z, a->y};
+    for (const void *p : io_ptrs)
+        if (!aligned(p, es)) return fail(SSM_ERR_ALIGN, "an io_dtype pointer is not %lld-byte aligned", (long long)es);
+    const void *f_ptrs[] = {a->A, a->Dskip, a->delta_bias, a->conv_w, a->conv_b, a->h0, a->h_final};
+    for (const void *p : f_ptrs)
+        if (!aligned(p, 4)) return fail(SSM_ERR_ALIGN, "an fp32 pointer is not 4-byte aligned");
+
+    const Range inputs[] = {
+        range(a->x, B * L * D, es, "x"),          range(a->delta, B * L * D, es, "delta"),
+        range(a->Bm, B * L * N, es, "Bm"),        range(a->Cm, B * L * N, es, "Cm"),
+        range(a->z, B * L * D, es, "z"),          range(a->A, D * N, 4, "A"),
+        range(a->Dskip, D, 4, "Dskip"),           range(a->delta_bias, D, 4, "delta_bias"),
+        range(a->conv_w, D * K, 4, "conv_w"),     range(a->conv_b, D, 4, "conv_b"),
+        range(a->h0, B * D * N, 4, "h0"),
+    };
+    const Range y = range(a->y, B * L * D, es, "y");
+    const Range hf = range(a->h_final, B * D * N, 4, "h_final");
+    for (const Range &r : inputs) {
+        if (overlaps(y, r)) return fail(SSM_ERR_ALIAS, "y overlaps %s", r.name);
+        if (overlaps(hf, r)) return fail(SSM_ERR_ALIAS, "h_final overlaps %s", r.name);
+    }
+    if (overlaps(y, hf)) return fail(SSM_ERR_ALIAS, "y overlaps h_final");
+
+    const size_t need = work ? ssm::scan_workspace_bytes(*a) : 0;
+    if (need > 0) {
+        if (!a->workspace) return fail(SSM_ERR_WORKSPACE, "workspace of %zu bytes required", need);
+        if (a->workspace_bytes < need)
+            return fail(SSM_ERR_WORKSPACE, "workspace has %zu bytes, %zu required", a->workspace_bytes, need);
+        if (!aligned(a->workspace, 256)) return fail(SSM_ERR_WORKSPACE, "workspace is not 256-byte aligned");
+        const Range ws = range(a->workspace, (int64_t)need, 1, "workspace");
+        for (const Range &r : inputs)
+            if (overlaps(ws, r)) return fail(SSM_ERR_ALIAS, "workspace overlaps %s", r.name);
+        if (overlaps(ws, y) || overlaps(ws, hf)) return fail(SSM_ERR_ALIAS, "workspace overlaps an output");
+    }
+
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    hipError_t e = hipSuccess;
+    if (B == 0) return ok();
+    if (L == 0) {
+        e = ssm::launch_empty_scan_state(*a, st);
+    } else {
+        e = ssm::launch_scan_fwd(*a, st);
+    }
+    if (e != hipSuccess) return fail(SSM_ERR_HIP, "HIP error: %s", hipGetErrorString(e));
+    return ok();
+}
+
+ssm_status_t ssm_causal_conv1d_silu(int64_t B, int64_t L, int64_t D, int64_t K, int32_t io_dtype,
+                                    const void *x, const float *w, const float *bias, void *u,
+                                    void *stream) {
+    if (io_dtype != SSM_F32 && io_dtype != SSM_BF16)
+        return fail(SSM_ERR_BAD_DTYPE, "io_dtype %d is not SSM_F32 or SSM_BF16", io_dtype);
+    if (B < 0 || L < 0) return fail(SSM_ERR_BAD_SHAPE, "negative batch or seqlen");
+    if (D < 1) return fail(SSM_ERR_BAD_SHAPE, "dim must be >= 1");
+    if (K < 1) return fail(SSM_ERR_BAD_SHAPE, "k must be >= 1");
+    if (K > SSM_MAX_CONV_K) return fail(SSM_ERR_UNSUPPORTED, "k %lld exceeds SSM_MAX_CONV_K (%d)", (long long)K, SSM_MAX_CONV_K);
+    if (!mul_ok(B, L, D)) return fail(SSM_ERR_BAD_SHAPE, "sizes overflow");
+    const int64_t es = io_bytes(io_dtype);
+    if (B == 0 || L == 0) return ok();
+    if (!x) return fail(SSM_ERR_NULL_ARG, "x is NULL");
+    if (!w) return fail(SSM_ERR_NULL_ARG, "w is NULL");
+    if (!u) return fail(SSM_ERR_NULL_ARG, "u is NULL");
+    if (!aligned(x, es) || !aligned(u, es) || !aligned(w, 4) || !aligned(bias, 4))
+        return fail(SSM_ERR_ALIGN, "a pointer is not aligned to its element size");
+    const Range ur = range(u, B * L * D, es, "u");
+    if (overlaps(ur, range(x, B * L * D, es, "x")) || overlaps(ur, range(w, D * K, 4, "w")) ||
+        overlaps(ur, range(bias, D, 4, "bias")))
+        return fail(SSM_ERR_ALIAS, "u overlaps an input");
+    hipError_t e = ssm::launch_conv1d_silu(B, L, D, (int)K, io_dtype, x, w, bias, u,
+                                           static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(SSM_ERR_HIP, "HIP error: %s", hipGetErrorString(e));
+    return ok();
+}
+
+ssm_status_t ssm_state_update(const ssm_state_update_args_t *a, void *stream) {
+    if (!a) return fail(SSM_ERR_NULL_ARG, "args is NULL");
+    if (a->io_dtype != SSM_F32 && a->io_dtype != SSM_BF16)
+        return fail(SSM_ERR_BAD_DTYPE, "io_dtype %d is not SSM_F32 or SSM_BF16", a->io_dtype);
+    if (a->batch < 0) return fail(SSM_ERR_BAD_SHAPE, "negative batch");
+    if (a->dim < 1) return fail(SSM_ERR_BAD_SHAPE, "dim must be >= 1");
+    if (a->dstate < 1) return fail(SSM_ERR_BAD_SHAPE, "dstate must be >= 1");
+    if (a->dstate > SSM_MAX_DSTATE)
+        return fail(SSM_ERR_UNSUPPORTED, "dstate %lld exceeds SSM_MAX_DSTATE (%d)", (long long)a->dstate, SSM_MAX_DSTATE);
+    if (a->delta_softplus != 0 && a->delta_softplus != 1)
+        return fail(SSM_ERR_UNSUPPORTED, "delta_softplus must be 0 or 1");
+    if (!mul_ok(a->batch, a->dim, a->dstate)) return fail(SSM_ERR_BAD_SHAPE, "sizes overflow");
+    const int64_t B = a->batch, D = a->dim, N = a->dstate;
+    const int64_t es = io_bytes(a->io_dtype);
+    if (B == 0) return ok();
+    if (!a->state) return fail(SSM_ERR_NULL_ARG, "state is NULL");
+    if (!a->x) return fail(SSM_ERR_NULL_ARG, "x is NULL");
+    if (!a->delta) return fail(SSM_ERR_NULL_ARG, "delta is NULL");
+    if (!a->Bm) return fail(SSM_ERR_NULL_ARG, "Bm is NULL");
+    if (!a->Cm) return fail(SSM_ERR_NULL_ARG, "Cm is NULL");
+    if (!a->A) return fail(SSM_ERR_NULL_ARG, "A is NULL");
+    if (!a->y) return fail(SSM_ERR_NULL_ARG, "y is NULL");
+    const void *io_ptrs[] = {a->x, a->delta, a->z, a->Bm, a->Cm, a->y};
+    for (const void *p : io_ptrs)
+        if (!aligned(p, es)) return fail(SSM_ERR_ALIGN, "an io_dtype pointer is not %lld-byte aligned", (long long)es);
+    const void *f_ptrs[] = {a->state, a->A, a->Dskip, a->delta_bias};
+    for (const void *p : f_ptrs)
+        if (!aligned(p, 4)) return fail(SSM_ERR_ALIGN, "an fp32 pointer is not 4-byte aligned");
+    const Range st = range(a->state, B * D * N, 4, "state");
+    const Range y = range(a->y, B * D, es, "y");
+    const Range inputs[] = {
+        range(a->x, B * D, es, "x"),   range(a->delta, B * D, es, "delta"),
+        range(a->z, B * D, es, "z"),   range(a->Bm, B * N, es, "Bm"),
+        range(a->Cm, B * N, es, "Cm"), range(a->A, D * N, 4, "A"),
+        range(a->Dskip, D, 4, "Dskip"), range(a->delta_bias, D, 4, "delta_bias"),
+    };
+    for (const Range &r : inputs) {
+        if (overlaps(y, r)) return fail(SSM_ERR_ALIAS, "y overlaps %s", r.name);
+        if (overlaps(st, r)) return fail(SSM_ERR_ALIAS, "state overlaps %s", r.name);
+    }
+    if (overlaps(y, st)) return fail(SSM_ERR_ALIAS, "y overlaps state");
+    hipError_t e = ssm::launch_state_update(*a, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(SSM_ERR_HIP, "HIP error: %s", hipGetErrorString(e));
+    return ok();
+}
+
+}  // extern "C"

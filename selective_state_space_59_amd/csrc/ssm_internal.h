@@ -1,0 +1,31 @@
+// ssm_internal.h -- host-side interface between the argument-checking C ABI
+// (ssm_api.cpp) and the kernel launchers (*.hip).  Launchers assume their
+// arguments were validated: sizes in range, required pointers non-NULL,
+// outputs not aliasing inputs, workspace large enough.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/ssm.h"
+
+namespace ssm {
+
+// Scan: bytes of workspace the chosen launch plan needs (0 if none).
+size_t scan_workspace_bytes(const ssm_scan_args_t &a);
+// Scan: enqueue the kernels.  a.batch, a.seqlen > 0.
+hipError_t launch_scan_fwd(const ssm_scan_args_t &a, hipStream_t stream);
+
+// Standalone conv1d + SiLU.  B, L > 0.
+hipError_t launch_conv1d_silu(int64_t B, int64_t L, int64_t D, int K, int io_dtype,
+                              const void *x, const float *w, const float *bias, void *u,
+                              hipStream_t stream);
+
+// Decode step.  a.batch > 0.
+hipError_t launch_state_update(const ssm_state_update_args_t &a, hipStream_t stream);
+
+// Copy or zero-fill the final state for an empty (L == 0) scan.
+hipError_t launch_empty_scan_state(const ssm_scan_args_t &a, hipStream_t stream);
+
+}  // namespace ssm

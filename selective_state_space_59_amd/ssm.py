@@ -1,0 +1,298 @@
+"""Python binding of the C-ABI library libssm_hip.so (argument marshalling only).
+
+Every function here checks tensor devices, dtypes, shapes and contiguity,
+allocates the outputs it is not given, and passes raw device pointers plus
+torch's current HIP stream to the library.  All arithmetic runs in the HIP
+kernels; if the library is missing this module raises instead of computing
+anything itself.
+
+Names and semantics mirror include/ssm.h.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libssm_hip.so")
+
+SSM_OK = 0
+SSM_ERR_NULL_ARG = 1
+SSM_ERR_BAD_SHAPE = 2
+SSM_ERR_BAD_DTYPE = 3
+SSM_ERR_UNSUPPORTED = 4
+SSM_ERR_ALIAS = 5
+SSM_ERR_WORKSPACE = 6
+SSM_ERR_HIP = 7
+SSM_ERR_ALIGN = 8
+SSM_F32 = 0
+SSM_BF16 = 1
+MAX_DSTATE = 16
+MAX_CONV_K = 4
+
+EXPORTED_SYMBOLS = ("ssm_selective_scan_workspace_size", "ssm_selective_scan_fwd",
+                    "ssm_causal_conv1d_silu", "ssm_state_update", "ssm_status_string",
+                    "ssm_last_error_message", "ssm_abi_version")
+
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_I32 = ctypes.c_int32
+
+
+class ScanArgs(ctypes.Structure):
+    """Mirror of ssm_scan_args_t."""
+    _fields_ = [("batch", _I64), ("seqlen", _I64), ("dim", _I64), ("dstate", _I64),
+                ("io_dtype", _I32), ("delta_softplus", _I32), ("conv_k", _I64),
+                ("x", _P), ("delta", _P), ("Bm", _P), ("Cm", _P), ("z", _P),
+                ("A", _P), ("Dskip", _P), ("delta_bias", _P), ("conv_w", _P), ("conv_b", _P),
+                ("h0", _P), ("y", _P), ("h_final", _P),
+                ("workspace", _P), ("workspace_bytes", ctypes.c_size_t)]
+
+
+class StateUpdateArgs(ctypes.Structure):
+    """Mirror of ssm_state_update_args_t."""
+    _fields_ = [("batch", _I64), ("dim", _I64), ("dstate", _I64),
+                ("io_dtype", _I32), ("delta_softplus", _I32),
+                ("state", _P), ("x", _P), ("delta", _P), ("z", _P), ("Bm", _P), ("Cm", _P),
+                ("A", _P), ("Dskip", _P), ("delta_bias", _P), ("y", _P)]
+
+
+class SSMError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(message)
+        self.status = status
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libssm_hip.so (built by selective_state_space_59_amd.build)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libssm_hip.so is not built; run "
+                               "`python -m selective_state_space_59_amd.build` first")
+        L = ctypes.CDLL(LIB_PATH)
+        L.ssm_selective_scan_workspace_size.argtypes = [ctypes.POINTER(ScanArgs)]
+        L.ssm_selective_scan_workspace_size.restype = ctypes.c_size_t
+        L.ssm_selective_scan_fwd.argtypes = [ctypes.POINTER(ScanArgs), _P]
+        L.ssm_selective_scan_fwd.restype = ctypes.c_int
+        L.ssm_causal_conv1d_silu.argtypes = [_I64, _I64, _I64, _I64, _I32, _P, _P, _P, _P, _P]
+        L.ssm_causal_conv1d_silu.restype = ctypes.c_int
+        L.ssm_state_update.argtypes = [ctypes.POINTER(StateUpdateArgs), _P]
+        L.ssm_state_update.restype = ctypes.c_int
+        L.ssm_status_string.argtypes = [ctypes.c_int]
+        L.ssm_status_string.restype = ctypes.c_char_p
+        L.ssm_last_error_message.argtypes = []
+        L.ssm_last_error_message.restype = ctypes.c_char_p
+        L.ssm_abi_version.argtypes = []
+        L.ssm_abi_version.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def abi_version() -> int:
+    return lib().ssm_abi_version()
+
+
+def status_string(status: int) -> str:
+    return lib().ssm_status_string(int(status)).decode()
+
+
+def _check(status: int, what: str):
+    if status != SSM_OK:
+        msg = lib().ssm_last_error_message().decode()
+        raise SSMError(status, "%s failed: %s (%s)" % (what, status_string(status), msg))
+
+
+def _io_code(dtype: torch.dtype) -> int:
+    if dtype == torch.bfloat16:
+        return SSM_BF16
+    if dtype == torch.float32:
+        return SSM_F32
+    raise TypeError("I/O tensors must be bfloat16 or float32, got %s" % dtype)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _req(t, name, shape, dtype, device):
+    if t is None:
+        raise ValueError("%s is required" % name)
+    return _opt(t, name, shape, dtype, device)
+
+
+def _opt(t, name, shape, dtype, device):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.device != device:
+        raise ValueError("%s is on %s, expected %s" % (name, t.device, device))
+    if t.dtype != dtype:
+        raise TypeError("%s has dtype %s, expected %s" % (name, t.dtype, dtype))
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    return t
+
+
+def _stream(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _scan_args(x, delta, A, Bm, Cm, Dskip, z, delta_bias, delta_softplus, conv_w, conv_b, h0,
+               y, h_final):
+    if not isinstance(x, torch.Tensor) or x.dim() != 3:
+        raise ValueError("x must be a (B, L, D) tensor")
+    if x.device.type != "cuda":
+        raise ValueError("x must be on a GPU")
+    dev = x.device
+    Bsz, L, D = x.shape
+    if not isinstance(A, torch.Tensor) or A.dim() != 2:
+        raise ValueError("A must be a (D, N) float32 tensor")
+    N = A.shape[1]
+    io = x.dtype
+    _req(x, "x", (Bsz, L, D), io, dev)
+    _req(delta, "delta", (Bsz, L, D), io, dev)
+    _req(A, "A", (D, N), torch.float32, dev)
+    _req(Bm, "Bm", (Bsz, L, N), io, dev)
+    _req(Cm, "Cm", (Bsz, L, N), io, dev)
+    _opt(z, "z", (Bsz, L, D), io, dev)
+    _opt(Dskip, "Dskip", (D,), torch.float32, dev)
+    _opt(delta_bias, "delta_bias", (D,), torch.float32, dev)
+    K = 0
+    if conv_w is not None:
+        if conv_w.dim() != 2:
+            raise ValueError("conv_w must be (D, K)")
+        K = conv_w.shape[1]
+        _req(conv_w, "conv_w", (D, K), torch.float32, dev)
+    _opt(conv_b, "conv_b", (D,), torch.float32, dev)
+    _opt(h0, "h0", (Bsz, D, N), torch.float32, dev)
+    _req(y, "y", (Bsz, L, D), io, dev)
+    _opt(h_final, "h_final", (Bsz, D, N), torch.float32, dev)
+    a = ScanArgs(batch=Bsz, seqlen=L, dim=D, dstate=N, io_dtype=_io_code(io),
+                 delta_softplus=int(bool(delta_softplus)), conv_k=K,
+                 x=_ptr(x), delta=_ptr(delta), Bm=_ptr(Bm), Cm=_ptr(Cm), z=_ptr(z), A=_ptr(A),
+                 Dskip=_ptr(Dskip), delta_bias=_ptr(delta_bias), conv_w=_ptr(conv_w),
+                 conv_b=_ptr(conv_b), h0=_ptr(h0), y=_ptr(y), h_final=_ptr(h_final),
+                 workspace=None, workspace_bytes=0)
+    return a, dev
+
+
+_ws_cache = {}
+
+
+def _workspace(dev: torch.device, nbytes: int) -> torch.Tensor:
+    """Per-device cached scratch tensor (grown on demand; calls on one stream reuse it)."""
+    key = (dev.type, dev.index)
+    buf = _ws_cache.get(key)
+    if buf is None or buf.numel() < nbytes:
+        buf = torch.empty(max(nbytes, 1 << 20), dtype=torch.uint8, device=dev)
+        _ws_cache[key] = buf
+    return buf
+
+
+def selective_scan_workspace_size(x, delta, A, Bm, Cm, Dskip=None, z=None, delta_bias=None,
+                                  delta_softplus=False, conv_w=None, conv_b=None, h0=None,
+                                  return_final_state=False) -> int:
+    y = torch.empty_like(x)
+    hf = (torch.empty(x.shape[0], x.shape[2], A.shape[1], device=x.device, dtype=torch.float32)
+          if return_final_state else None)
+    a, _ = _scan_args(x, delta, A, Bm, Cm, Dskip, z, delta_bias, delta_softplus, conv_w, conv_b,
+                      h0, y, hf)
+    n = lib().ssm_selective_scan_workspace_size(ctypes.byref(a))
+    if n == ctypes.c_size_t(-1).value:
+        raise SSMError(SSM_ERR_BAD_SHAPE, "invalid sizes")
+    return int(n)
+
+
+def selective_scan_fwd(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, Bm: torch.Tensor,
+                       Cm: torch.Tensor, Dskip: Optional[torch.Tensor] = None,
+                       z: Optional[torch.Tensor] = None,
+                       delta_bias: Optional[torch.Tensor] = None, delta_softplus: bool = False,
+                       conv_w: Optional[torch.Tensor] = None,
+                       conv_b: Optional[torch.Tensor] = None,
+                       h0: Optional[torch.Tensor] = None, return_final_state: bool = False,
+                       y: Optional[torch.Tensor] = None,
+                       h_final: Optional[torch.Tensor] = None,
+                       workspace: Optional[torch.Tensor] = None
+                       ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """ssm_selective_scan_fwd.  Returns (y, h_final or None)."""
+    if y is None:
+        y = torch.empty_like(x)
+    if return_final_state and h_final is None:
+        h_final = torch.empty(x.shape[0], x.shape[2], A.shape[1], device=x.device,
+                              dtype=torch.float32)
+    a, dev = _scan_args(x, delta, A, Bm, Cm, Dskip, z, delta_bias, delta_softplus, conv_w,
+                        conv_b, h0, y, h_final)
+    need = lib().ssm_selective_scan_workspace_size(ctypes.byref(a))
+    if need == ctypes.c_size_t(-1).value:
+        _check(lib().ssm_selective_scan_fwd(ctypes.byref(a), None), "ssm_selective_scan_fwd")
+    if need > 0:
+        ws = workspace if workspace is not None else _workspace(dev, need)
+        if ws.device != dev or ws.numel() * ws.element_size() < need:
+            raise ValueError("workspace must be a device tensor of >= %d bytes" % need)
+        a.workspace = ws.data_ptr()
+        a.workspace_bytes = ws.numel() * ws.element_size()
+    _check(lib().ssm_selective_scan_fwd(ctypes.byref(a), _stream(dev)), "ssm_selective_scan_fwd")
+    return y, h_final
+
+
+def causal_conv1d_silu(x: torch.Tensor, w: torch.Tensor, bias: Optional[torch.Tensor] = None,
+                       out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """ssm_causal_conv1d_silu on x (B, L, D) with weights w (D, K)."""
+    if not isinstance(x, torch.Tensor) or x.dim() != 3 or x.device.type != "cuda":
+        raise ValueError("x must be a (B, L, D) GPU tensor")
+    dev = x.device
+    Bsz, L, D = x.shape
+    if w.dim() != 2:
+        raise ValueError("w must be (D, K)")
+    K = w.shape[1]
+    _req(x, "x", (Bsz, L, D), x.dtype, dev)
+    _req(w, "w", (D, K), torch.float32, dev)
+    _opt(bias, "bias", (D,), torch.float32, dev)
+    if out is None:
+        out = torch.empty_like(x)
+    _req(out, "out", (Bsz, L, D), x.dtype, dev)
+    _check(lib().ssm_causal_conv1d_silu(Bsz, L, D, K, _io_code(x.dtype), _ptr(x), _ptr(w),
+                                        _ptr(bias), _ptr(out), _stream(dev)),
+           "ssm_causal_conv1d_silu")
+    return out
+
+
+def state_update(state: torch.Tensor, x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor,
+                 Bm: torch.Tensor, Cm: torch.Tensor, Dskip: Optional[torch.Tensor] = None,
+                 z: Optional[torch.Tensor] = None, delta_bias: Optional[torch.Tensor] = None,
+                 delta_softplus: bool = False, y: Optional[torch.Tensor] = None
+                 ) -> torch.Tensor:
+    """ssm_state_update: advances `state` (B, D, N) in place and returns y (B, D)."""
+    if not isinstance(state, torch.Tensor) or state.dim() != 3 or state.device.type != "cuda":
+        raise ValueError("state must be a (B, D, N) float32 GPU tensor")
+    dev = state.device
+    Bsz, D, N = state.shape
+    io = x.dtype
+    _req(state, "state", (Bsz, D, N), torch.float32, dev)
+    _req(x, "x", (Bsz, D), io, dev)
+    _req(delta, "delta", (Bsz, D), io, dev)
+    _opt(z, "z", (Bsz, D), io, dev)
+    _req(Bm, "Bm", (Bsz, N), io, dev)
+    _req(Cm, "Cm", (Bsz, N), io, dev)
+    _req(A, "A", (D, N), torch.float32, dev)
+    _opt(Dskip, "Dskip", (D,), torch.float32, dev)
+    _opt(delta_bias, "delta_bias", (D,), torch.float32, dev)
+    if y is None:
+        y = torch.empty_like(x)
+    _req(y, "y", (Bsz, D), io, dev)
+    a = StateUpdateArgs(batch=Bsz, dim=D, dstate=N, io_dtype=_io_code(io),
+                        delta_softplus=int(bool(delta_softplus)), state=_ptr(state), x=_ptr(x),
+                        delta=_ptr(delta), z=_ptr(z), Bm=_ptr(Bm), Cm=_ptr(Cm), A=_ptr(A),
+                        Dskip=_ptr(Dskip), delta_bias=_ptr(delta_bias), y=_ptr(y))
+    _check(lib().ssm_state_update(ctypes.byref(a), _stream(dev)), "ssm_state_update")
+    return y

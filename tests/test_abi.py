@@ -1,0 +1,254 @@
+"""Host-side tests of the C ABI (no GPU needed).
+
+Argument checking in libssm_hip.so finishes before any HIP call, so every
+error path can be driven from the CPU with placeholder device addresses that
+are never dereferenced.  Also checks that the library exports every function
+include/ssm.h declares and that the ctypes mirrors match the C layouts.
+"""
+import ctypes
+import os
+import re
+import subprocess
+import tempfile
+
+import pytest
+
+from selective_state_space_59_amd import ssm
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ssm.h")
+
+# Placeholder device addresses (256-aligned, far apart, never dereferenced).
+BASE = 0x7F0000000000
+STEP = 1 << 32
+
+
+def addr(i, off=0):
+    return BASE + i * STEP + off
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(ssm_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_function():
+    names = declared_functions()
+    assert set(names) == set(ssm.EXPORTED_SYMBOLS)
+    L = ssm.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", ssm.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    for n in names:
+        assert re.search(r"\bT %s\b" % n, out), n
+
+
+def test_abi_version_and_status_strings():
+    ver = int(re.search(r"#define SSM_ABI_VERSION (\d+)", open(HEADER).read()).group(1))
+    assert ssm.abi_version() == ver
+    for code in range(0, 9):
+        s = ssm.status_string(code)
+        assert s.startswith("SSM_")
+    assert "unknown" in ssm.status_string(99)
+
+
+C_LAYOUT = r"""
+#include <stdio.h>
+#include <stddef.h>
+#include "ssm.h"
+#define F(T, f) printf(#T " " #f " %zu\n", offsetof(T, f));
+int main(void) {
+  printf("ssm_scan_args_t size %zu\n", sizeof(ssm_scan_args_t));
+  printf("ssm_state_update_args_t size %zu\n", sizeof(ssm_state_update_args_t));
+  %FIELDS%
+  return 0;
+}
+"""
+
+
+def test_ctypes_structs_match_c_layout():
+    lines = []
+    for cname, cls in (("ssm_scan_args_t", ssm.ScanArgs),
+                       ("ssm_state_update_args_t", ssm.StateUpdateArgs)):
+        for f, _ in cls._fields_:
+            lines.append("F(%s, %s)" % (cname, f))
+    with tempfile.TemporaryDirectory() as d:
+        c = os.path.join(d, "layout.c")
+        open(c, "w").write(C_LAYOUT.replace("%FIELDS%", "\n  ".join(lines)))
+        exe = os.path.join(d, "layout")
+        subprocess.run(["gcc", "-std=c11", "-I", os.path.join(ROOT, "include"), c, "-o", exe],
+                       check=True)
+        out = subprocess.run([exe], capture_output=True, text=True, check=True).stdout.split("\n")
+    got = {}
+    for line in out:
+        if line:
+            t, f, v = line.split()
+            got[(t, f)] = int(v)
+    assert got[("ssm_scan_args_t", "size")] == ctypes.sizeof(ssm.ScanArgs)
+    assert got[("ssm_state_update_args_t", "size")] == ctypes.sizeof(ssm.StateUpdateArgs)
+    for cname, cls in (("ssm_scan_args_t", ssm.ScanArgs),
+                       ("ssm_state_update_args_t", ssm.StateUpdateArgs)):
+        for f, _ in cls._fields_:
+            assert got[(cname, f)] == getattr(cls, f).offset, (cname, f)
+
+
+# ----------------------------------------------------------------- scan checks
+def scan_args(**kw):
+    a = ssm.ScanArgs(batch=2, seqlen=8, dim=64, dstate=16, io_dtype=ssm.SSM_BF16,
+                     delta_softplus=0, conv_k=0, x=addr(0), delta=addr(1), Bm=addr(2),
+                     Cm=addr(3), z=addr(4), A=addr(5), Dskip=addr(6), delta_bias=None,
+                     conv_w=None, conv_b=None, h0=None, y=addr(7), h_final=addr(8),
+                     workspace=addr(9), workspace_bytes=1 << 30)
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def run_scan(a):
+    return ssm.lib().ssm_selective_scan_fwd(ctypes.byref(a), None)
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("io_dtype", 7, ssm.SSM_ERR_BAD_DTYPE),
+    ("batch", -1, ssm.SSM_ERR_BAD_SHAPE),
+    ("seqlen", -5, ssm.SSM_ERR_BAD_SHAPE),
+    ("dim", 0, ssm.SSM_ERR_BAD_SHAPE),
+    ("dstate", 0, ssm.SSM_ERR_BAD_SHAPE),
+    ("dstate", 17, ssm.SSM_ERR_UNSUPPORTED),
+    ("conv_k", -1, ssm.SSM_ERR_BAD_SHAPE),
+    ("conv_k", 5, ssm.SSM_ERR_UNSUPPORTED),
+    ("conv_k", 4, ssm.SSM_ERR_NULL_ARG),          # conv_k without conv_w
+    ("delta_softplus", 2, ssm.SSM_ERR_UNSUPPORTED),
+    ("x", None, ssm.SSM_ERR_NULL_ARG),
+    ("delta", None, ssm.SSM_ERR_NULL_ARG),
+    ("Bm", None, ssm.SSM_ERR_NULL_ARG),
+    ("Cm", None, ssm.SSM_ERR_NULL_ARG),
+    ("A", None, ssm.SSM_ERR_NULL_ARG),
+    ("y", None, ssm.SSM_ERR_NULL_ARG),
+    ("x", addr(0, 1), ssm.SSM_ERR_ALIGN),        # odd address for bf16
+    ("A", addr(5, 2), ssm.SSM_ERR_ALIGN),        # fp32 not 4-aligned
+    ("y", addr(0, 64), ssm.SSM_ERR_ALIAS),       # y inside x
+    ("h_final", addr(7, 16), ssm.SSM_ERR_ALIAS), # h_final inside y
+    ("h0", addr(8), ssm.SSM_ERR_ALIAS),          # h0 == h_final
+    ("conv_b", addr(10), ssm.SSM_ERR_BAD_SHAPE), # conv bias without conv
+    ("batch", 1 << 56, ssm.SSM_ERR_BAD_SHAPE),   # overflow of B*L*D
+])
+def test_scan_rejects_bad_arguments(field, value, status):
+    a = scan_args(**{field: value})
+    assert run_scan(a) == status
+    assert ssm.lib().ssm_last_error_message().decode() != ""
+
+
+def test_scan_null_args_pointer():
+    assert ssm.lib().ssm_selective_scan_fwd(None, None) == ssm.SSM_ERR_NULL_ARG
+
+
+def test_scan_empty_batch_is_a_noop():
+    # B == 0 returns before any HIP call, so it succeeds even without a GPU.
+    a = scan_args(batch=0)
+    assert run_scan(a) == ssm.SSM_OK
+    assert ssm.lib().ssm_last_error_message().decode() == ""
+
+
+def test_scan_empty_sequence_without_final_state_is_a_noop():
+    a = scan_args(seqlen=0, h_final=None)
+    assert run_scan(a) == ssm.SSM_OK
+
+
+def test_workspace_size_queries():
+    L = ssm.lib()
+    assert L.ssm_selective_scan_workspace_size(ctypes.byref(scan_args(dstate=99))) == \
+        ctypes.c_size_t(-1).value
+    assert L.ssm_selective_scan_workspace_size(ctypes.byref(scan_args(batch=0))) == 0
+    assert L.ssm_selective_scan_workspace_size(None) == ctypes.c_size_t(-1).value
+    # Valid sizes give a finite answer that only depends on sizes and flags.
+    n1 = L.ssm_selective_scan_workspace_size(ctypes.byref(scan_args()))
+    n2 = L.ssm_selective_scan_workspace_size(ctypes.byref(scan_args(x=addr(11))))
+    assert n1 == n2 and n1 < (1 << 40)
+
+
+def test_scan_workspace_checks():
+    L = ssm.lib()
+    a = scan_args(batch=1, seqlen=1 << 20, dim=1024)
+    need = L.ssm_selective_scan_workspace_size(ctypes.byref(a))
+    if need == 0:
+        pytest.skip("this launch plan needs no workspace")
+    a.workspace = None
+    assert run_scan(a) == ssm.SSM_ERR_WORKSPACE
+    a.workspace = addr(9)
+    a.workspace_bytes = need - 1
+    assert run_scan(a) == ssm.SSM_ERR_WORKSPACE
+    a.workspace_bytes = need
+    a.workspace = addr(9, 8)
+    assert run_scan(a) == ssm.SSM_ERR_WORKSPACE
+
+
+# ----------------------------------------------------------------- conv checks
+def run_conv(B=2, L=8, D=64, K=4, dt=ssm.SSM_BF16, x=addr(0), w=addr(1), b=addr(2), u=addr(3)):
+    return ssm.lib().ssm_causal_conv1d_silu(B, L, D, K, dt, x, w, b, u, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dt=5), ssm.SSM_ERR_BAD_DTYPE),
+    (dict(B=-1), ssm.SSM_ERR_BAD_SHAPE),
+    (dict(D=0), ssm.SSM_ERR_BAD_SHAPE),
+    (dict(K=0), ssm.SSM_ERR_BAD_SHAPE),
+    (dict(K=5), ssm.SSM_ERR_UNSUPPORTED),
+    (dict(x=None), ssm.SSM_ERR_NULL_ARG),
+    (dict(w=None), ssm.SSM_ERR_NULL_ARG),
+    (dict(u=None), ssm.SSM_ERR_NULL_ARG),
+    (dict(u=addr(0, 2)), ssm.SSM_ERR_ALIAS),
+    (dict(x=addr(0, 1)), ssm.SSM_ERR_ALIGN),
+])
+def test_conv_rejects_bad_arguments(kw, status):
+    assert run_conv(**kw) == status
+
+
+def test_conv_empty_is_a_noop():
+    assert run_conv(B=0) == ssm.SSM_OK
+    assert run_conv(L=0, x=None, u=None) == ssm.SSM_OK
+
+
+# --------------------------------------------------------- state-update checks
+def upd_args(**kw):
+    a = ssm.StateUpdateArgs(batch=4, dim=64, dstate=16, io_dtype=ssm.SSM_BF16, delta_softplus=0,
+                            state=addr(0), x=addr(1), delta=addr(2), z=addr(3), Bm=addr(4),
+                            Cm=addr(5), A=addr(6), Dskip=addr(7), delta_bias=None, y=addr(8))
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("io_dtype", -1, ssm.SSM_ERR_BAD_DTYPE),
+    ("batch", -2, ssm.SSM_ERR_BAD_SHAPE),
+    ("dim", 0, ssm.SSM_ERR_BAD_SHAPE),
+    ("dstate", 0, ssm.SSM_ERR_BAD_SHAPE),
+    ("dstate", 32, ssm.SSM_ERR_UNSUPPORTED),
+    ("delta_softplus", 3, ssm.SSM_ERR_UNSUPPORTED),
+    ("state", None, ssm.SSM_ERR_NULL_ARG),
+    ("x", None, ssm.SSM_ERR_NULL_ARG),
+    ("Bm", None, ssm.SSM_ERR_NULL_ARG),
+    ("y", None, ssm.SSM_ERR_NULL_ARG),
+    ("y", addr(1), ssm.SSM_ERR_ALIAS),
+    ("y", addr(0, 128), ssm.SSM_ERR_ALIAS),
+    ("x", addr(0, 64), ssm.SSM_ERR_ALIAS),       # input inside the state
+    ("state", addr(0, 2), ssm.SSM_ERR_ALIGN),
+])
+def test_state_update_rejects_bad_arguments(field, value, status):
+    a = upd_args(**{field: value})
+    assert ssm.lib().ssm_state_update(ctypes.byref(a), None) == status
+
+
+def test_state_update_empty_batch_is_a_noop():
+    a = upd_args(batch=0)
+    assert ssm.lib().ssm_state_update(ctypes.byref(a), None) == ssm.SSM_OK
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    x = torch.zeros(1, 4, 8)
+    with pytest.raises(ValueError):
+        ssm.selective_scan_fwd(x, x, torch.zeros(8, 4), torch.zeros(1, 4, 4), torch.zeros(1, 4, 4))
