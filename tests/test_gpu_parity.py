@@ -54,6 +54,12 @@ CASES = [
     ("conv_k1_f32", 1, 20, 10, 4, torch.float32, dict(conv_k=1)),
     ("conv_k3_bf16", 2, 33, 64, 16, torch.bfloat16, dict(conv_k=3)),
     ("L4097_bf16", 1, 4097, 64, 16, torch.bfloat16, {}),
+    # shapes whose launch uses wide workgroups (several waves per tile)
+    ("wide16_partial_bf16", 16, 33, 3000, 16, torch.bfloat16, {}),
+    ("wide9_generic_bf16", 8, 40, 2050, 16, torch.bfloat16, dict(conv_k=4)),
+    ("wide13_generic_f32", 6, 21, 4099, 16, torch.float32, dict(h0=True)),
+    ("wide16_f32_conv", 24, 18, 2000, 16, torch.float32, dict(conv_k=4)),
+    ("wide_n5_bf16", 32, 19, 1536, 5, torch.bfloat16, dict(h0=True)),
 ]
 
 
