@@ -237,11 +237,14 @@ struct Geo {
 //     4 (t % W) .. +3) of each of x, delta, z;
 //   own tiles, element path: thread t holds element t (row t / CH, channel
 //     t % CH) of each of x, delta, z;
-//   B/C rows, 8-byte path (bf16, N = 16): threads t < 64 hold chunk t of B
-//     and of C; element path: elements t + i * threads (< 256) of B and C.
+//   B/C rows, wide path (N = 16): threads t < 64 hold chunk t (4 elements)
+//     of B and of C; element path: elements t + i * threads (< 256) of B, C.
+// Which path runs is fixed at compile time: a run-time choice would merge
+// the two register sets at the loop back-edge with copies that must wait
+// for every load in flight.
 struct Fetch {
     uint4 own[3];
-    uint2 bcv[2];
+    uint4 bcv[2];
     uint32_t bce[8];
 };
 
@@ -272,10 +275,17 @@ __device__ __forceinline__ void fetch_block(const Geo &g, uint32_t blk_off, uint
 #pragma unroll
         for (int i = 0; i < 3; ++i) f.own[i].x = buf_ld<IO>(rs[i], off);
     }
-    if (es == 2 && g.N == kRow) {
-        const uint32_t off = tid < 64 ? bc_off + (uint32_t)(tid * 8) : kOOB;
-        f.bcv[0] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(g.rb, off, 0, 0));
-        f.bcv[1] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(g.rc, off, 0, 0));
+    if (VEC) {
+        const uint32_t off = tid < 64 ? bc_off + (uint32_t)(tid * 4 * es) : kOOB;
+        if constexpr (es == 2) {
+            const uint2 b = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(g.rb, off, 0, 0));
+            const uint2 c = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(g.rc, off, 0, 0));
+            f.bcv[0] = make_uint4(b.x, b.y, 0u, 0u);
+            f.bcv[1] = make_uint4(c.x, c.y, 0u, 0u);
+        } else {
+            f.bcv[0] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(g.rb, off, 0, 0));
+            f.bcv[1] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(g.rc, off, 0, 0));
+        }
     } else {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -317,10 +327,15 @@ __device__ __forceinline__ void stage_block(const Geo &g, const Tiles &T, char *
     }
     char *bc = lds + T.bc + slot * T.bc_slot;
     char *cc = bc + kTB * kRow * es;
-    if (es == 2 && g.N == kRow) {
+    if (VEC) {
         if (tid < 64) {
-            *reinterpret_cast<uint2 *>(bc + tid * 8) = f.bcv[0];
-            *reinterpret_cast<uint2 *>(cc + tid * 8) = f.bcv[1];
+            if constexpr (es == 2) {
+                *reinterpret_cast<uint2 *>(bc + tid * 8) = make_uint2(f.bcv[0].x, f.bcv[0].y);
+                *reinterpret_cast<uint2 *>(cc + tid * 8) = make_uint2(f.bcv[1].x, f.bcv[1].y);
+            } else {
+                *reinterpret_cast<uint4 *>(bc + tid * 16) = f.bcv[0];
+                *reinterpret_cast<uint4 *>(cc + tid * 16) = f.bcv[1];
+            }
         }
     } else {
 #pragma unroll
@@ -495,7 +510,12 @@ __device__ __forceinline__ void scan_tiles_body(const ScanKernelParams &p, const
     // Tile j is requested three blocks before it is computed (two blocks of
     // latency budget), copied into LDS slot j % 2 one block before, and its
     // outputs leave LDS one block after.  Unrolled by two so the two fetch
-    // register sets alternate without copies.
+    // register sets alternate without copies.  The loop has a single exit
+    // at its bottom (the last one or two blocks run after it): an exit in
+    // the middle would route through the back-edge once the control flow is
+    // structured, and the load counters merged there would force a wait for
+    // every prefetch in flight.  Prefetches past the last block read zeros
+    // or unused rows and are never consumed.
     Fetch f0, f1;
     fetch_block<IO, VEC>(geo, 0, 0, tid, nthreads, f0);
     fetch_block<IO, VEC>(geo, geo.row_step, geo.bc_step, tid, nthreads, f1);
@@ -503,34 +523,44 @@ __device__ __forceinline__ void scan_tiles_body(const ScanKernelParams &p, const
     fetch_block<IO, VEC>(geo, 2 * geo.row_step, 2 * geo.bc_step, tid, nthreads, f0);
     uint32_t ro = 0, bo = 0;  // offsets of block j
     int64_t j = 0;
-    for (;;) {
+    for (; j + 2 < nblocks; j += 2) {
         // -- block j (slot 0); f1 holds block j+1, f0 block j+2 --------------
         __syncthreads();
         if (j > 0) store_block<IO, VEC>(geo, T, lds, 1, ro - geo.row_step, tid, nthreads);
         compute_block<IO, CONV, FAST>(p, T, lds, 0, p.t_begin + j * kTB, wave, c, n, lane, sel, k,
                                       x_prev, h);
-        if (j + 1 >= nblocks) {
-            __syncthreads();
-            store_block<IO, VEC>(geo, T, lds, 0, ro, tid, nthreads);
-            break;
-        }
         stage_block<IO, VEC>(geo, T, lds, 1, tid, nthreads, f1);
+        // Keep the refill of f1 after its copy into LDS, so the new data can
+        // land in the same registers.
+        __builtin_amdgcn_sched_barrier(0);
         fetch_block<IO, VEC>(geo, ro + 3 * geo.row_step, bo + 3 * geo.bc_step, tid, nthreads, f1);
         // -- block j+1 (slot 1); f0 holds block j+2, f1 block j+3 ------------
         __syncthreads();
         store_block<IO, VEC>(geo, T, lds, 0, ro, tid, nthreads);
         compute_block<IO, CONV, FAST>(p, T, lds, 1, p.t_begin + (j + 1) * kTB, wave, c, n, lane,
                                       sel, k, x_prev, h);
-        if (j + 2 >= nblocks) {
-            __syncthreads();
-            store_block<IO, VEC>(geo, T, lds, 1, ro + geo.row_step, tid, nthreads);
-            break;
-        }
         stage_block<IO, VEC>(geo, T, lds, 0, tid, nthreads, f0);
+        __builtin_amdgcn_sched_barrier(0);
         fetch_block<IO, VEC>(geo, ro + 4 * geo.row_step, bo + 4 * geo.bc_step, tid, nthreads, f0);
         ro += 2 * geo.row_step;
         bo += 2 * geo.bc_step;
-        j += 2;
+    }
+    // One or two blocks remain; block j sits in slot 0 and f1 holds j+1.
+    __syncthreads();
+    if (j > 0) store_block<IO, VEC>(geo, T, lds, 1, ro - geo.row_step, tid, nthreads);
+    compute_block<IO, CONV, FAST>(p, T, lds, 0, p.t_begin + j * kTB, wave, c, n, lane, sel, k,
+                                  x_prev, h);
+    if (j + 1 < nblocks) {
+        stage_block<IO, VEC>(geo, T, lds, 1, tid, nthreads, f1);
+        __syncthreads();
+        store_block<IO, VEC>(geo, T, lds, 0, ro, tid, nthreads);
+        compute_block<IO, CONV, FAST>(p, T, lds, 1, p.t_begin + (j + 1) * kTB, wave, c, n, lane,
+                                      sel, k, x_prev, h);
+        __syncthreads();
+        store_block<IO, VEC>(geo, T, lds, 1, ro + geo.row_step, tid, nthreads);
+    } else {
+        __syncthreads();
+        store_block<IO, VEC>(geo, T, lds, 0, ro, tid, nthreads);
     }
 }
 
@@ -691,10 +721,10 @@ hipError_t launch_scan_fwd(const ssm_scan_args_t &a, hipStream_t stream) {
     const int64_t es = a.io_dtype == SSM_BF16 ? 2 : 4;
     const int64_t chunk = rows_per_launch(a);
     if (chunk < 2 * kTB || a.dim * es > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    // Wide (4-element) tile chunks need D % 4 == 0 and aligned tensors.
+    // Wide (4-element) chunks need D % 4 == 0, N = 16 and aligned tensors.
     auto al = [&](const void *q) { return ((uintptr_t)q % (4 * es)) == 0; };
-    const bool vec = (a.dim % 4 == 0) && al(a.x) && al(a.delta) && al(a.y) && (!a.z || al(a.z)) &&
-                     ((uintptr_t)a.Bm % 8 == 0) && ((uintptr_t)a.Cm % 8 == 0);
+    const bool vec = (a.dim % 4 == 0) && a.dstate == kRow && al(a.x) && al(a.delta) && al(a.y) &&
+                     (!a.z || al(a.z)) && al(a.Bm) && al(a.Cm);
     float *carry = static_cast<float *>(a.workspace);
     hipError_t e = hipSuccess;
     for (int64_t t = 0; t < a.seqlen && e == hipSuccess; t += chunk) {
