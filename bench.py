@@ -191,6 +191,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-extras", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (fp32) five times; its "
+                         "FETCH_SIZE / WRITE_SIZE counters scale the scan's traffic counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: the selective scan is benchmarked on a single "
@@ -202,6 +205,16 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+
+    if args.copy_calibration:
+        n = args.copy_calibration << 18
+        src = torch.randn(n, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": 4 * n, "copy_bytes_written": 4 * n, "launches": 5}))
+        return
 
     cfg = W.C2_130M
     print("bench: %s, %d warmup + %d timed steps" % (cfg.name, args.warmup, args.steps),

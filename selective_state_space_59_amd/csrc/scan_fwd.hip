@@ -412,11 +412,12 @@ __device__ __forceinline__ void wave_sync() {
 
 struct LaneConst {
     float a, a2, ia, dsk, dbias, cb, wp0, wp1, wp2, wp3;
+    float iar[kRow];  // 1 / A of every state entry of the lane's channel (0 where A == 0)
 };
 
 // One block of one wave: decode the lane's own step from the staged tile,
 // run 16 recurrence steps, transpose the partial read-outs, write y to LDS.
-template <typename IO, bool CONV, bool FAST>
+template <typename IO, bool CONV, bool FAST, bool TAIL>
 __device__ __forceinline__ void compute_block(const ScanKernelParams &p, const Tiles &T,
                                               char *lds, int slot, int64_t t0, int wave, int c,
                                               int n, int lane, const BcastSel &sel,
@@ -443,7 +444,7 @@ __device__ __forceinline__ void compute_block(const ScanKernelParams &p, const T
         x_prev = xv;
     }
     if (p.softplus) dt = softplus_fast(dt + k.dbias);
-    if (t0 + n >= p.t_end) {  // past the end: the state must not move
+    if (TAIL && t0 + n >= p.t_end) {  // past the end: the state must not move
         dt = 0.0f;
         u = 0.0f;
     }
@@ -468,8 +469,7 @@ __device__ __forceinline__ void compute_block(const ScanKernelParams &p, const T
             const float bu = uk * Bk[kk];
             float bx;
             if (FAST) {
-                const float q = bu * k.ia;
-                bx = __builtin_fmaf(e, q, -q);
+                bx = __builtin_fmaf(e, bu, -bu);  // h holds A h here
             } else {
                 bx = (dtk * phi_of(dtk * k.a, e)) * bu;
             }
@@ -482,11 +482,24 @@ __device__ __forceinline__ void compute_block(const ScanKernelParams &p, const T
     float part[kRow];
 #pragma unroll
     for (int j = 0; j < kRow; ++j) part[j] = prow[j * kPStride + n];
+    float acc;
+    if (FAST) {
+        // The fast form keeps g = A h, so C h = (C g) / A per entry.
+        float s0 = part[0] * k.iar[0], s1 = part[1] * k.iar[1];
 #pragma unroll
-    for (int w = kRow / 2; w >= 1; w /= 2)
+        for (int j = 2; j < kRow; j += 2) {
+            s0 = __builtin_fmaf(part[j], k.iar[j], s0);
+            s1 = __builtin_fmaf(part[j + 1], k.iar[j + 1], s1);
+        }
+        acc = s0 + s1;
+    } else {
 #pragma unroll
-        for (int j = 0; j < w; ++j) part[j] += part[j + w];
-    float yv = part[0] + k.dsk * u;
+        for (int w = kRow / 2; w >= 1; w /= 2)
+#pragma unroll
+            for (int j = 0; j < w; ++j) part[j] += part[j + w];
+        acc = part[0];
+    }
+    float yv = acc + k.dsk * u;
     if (p.z) yv *= silu(zv);
     char *ydst = lds + T.ybuf + slot * T.ybuf_slot + (n * T.CH + ci) * es;
     if constexpr (es == 2)
@@ -527,7 +540,7 @@ __device__ __forceinline__ void scan_tiles_body(const ScanKernelParams &p, const
         // -- block j (slot 0); f1 holds block j+1, f0 block j+2 --------------
         __syncthreads();
         if (j > 0) store_block<IO, VEC>(geo, T, lds, 1, ro - geo.row_step, tid, nthreads);
-        compute_block<IO, CONV, FAST>(p, T, lds, 0, p.t_begin + j * kTB, wave, c, n, lane, sel, k,
+        compute_block<IO, CONV, FAST, false>(p, T, lds, 0, p.t_begin + j * kTB, wave, c, n, lane, sel, k,
                                       x_prev, h);
         stage_block<IO, VEC>(geo, T, lds, 1, tid, nthreads, f1);
         // Keep the refill of f1 after its copy into LDS, so the new data can
@@ -537,7 +550,7 @@ __device__ __forceinline__ void scan_tiles_body(const ScanKernelParams &p, const
         // -- block j+1 (slot 1); f0 holds block j+2, f1 block j+3 ------------
         __syncthreads();
         store_block<IO, VEC>(geo, T, lds, 0, ro, tid, nthreads);
-        compute_block<IO, CONV, FAST>(p, T, lds, 1, p.t_begin + (j + 1) * kTB, wave, c, n, lane,
+        compute_block<IO, CONV, FAST, false>(p, T, lds, 1, p.t_begin + (j + 1) * kTB, wave, c, n, lane,
                                       sel, k, x_prev, h);
         stage_block<IO, VEC>(geo, T, lds, 0, tid, nthreads, f0);
         __builtin_amdgcn_sched_barrier(0);
@@ -548,13 +561,13 @@ __device__ __forceinline__ void scan_tiles_body(const ScanKernelParams &p, const
     // One or two blocks remain; block j sits in slot 0 and f1 holds j+1.
     __syncthreads();
     if (j > 0) store_block<IO, VEC>(geo, T, lds, 1, ro - geo.row_step, tid, nthreads);
-    compute_block<IO, CONV, FAST>(p, T, lds, 0, p.t_begin + j * kTB, wave, c, n, lane, sel, k,
+    compute_block<IO, CONV, FAST, true>(p, T, lds, 0, p.t_begin + j * kTB, wave, c, n, lane, sel, k,
                                   x_prev, h);
     if (j + 1 < nblocks) {
         stage_block<IO, VEC>(geo, T, lds, 1, tid, nthreads, f1);
         __syncthreads();
         store_block<IO, VEC>(geo, T, lds, 0, ro, tid, nthreads);
-        compute_block<IO, CONV, FAST>(p, T, lds, 1, p.t_begin + (j + 1) * kTB, wave, c, n, lane,
+        compute_block<IO, CONV, FAST, true>(p, T, lds, 1, p.t_begin + (j + 1) * kTB, wave, c, n, lane,
                                       sel, k, x_prev, h);
         __syncthreads();
         store_block<IO, VEC>(geo, T, lds, 1, ro + geo.row_step, tid, nthreads);
@@ -566,8 +579,14 @@ __device__ __forceinline__ void scan_tiles_body(const ScanKernelParams &p, const
 
 // blockDim.x = 64 W; workgroup g covers channels [4 W q, 4 W q + 4 W) of
 // batch row g / groups_per_b, with q = g % groups_per_b.
+// Register budget: the bf16 wide-tile variants (the 130M- and 2.8B-like
+// layers) must fit 5 waves per SIMD (<= 96 VGPRs) so a 2.8B-like layer
+// (5120 waves) is resident at once; the others may use up to 128.
+template <typename IO, bool VEC>
+constexpr int kMinWavesPerEU = (VEC && std::is_same<IO, io_bf16>::value) ? 5 : 4;
+
 template <typename IO, bool CONV, bool VEC>
-__global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4, 8)))
+__global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(kMinWavesPerEU<IO, VEC>, 8)))
 void scan_tiles_kernel(ScanKernelParams p) {
     extern __shared__ __attribute__((aligned(16))) char lds[];
     constexpr int es = sizeof(typename IO::storage);
@@ -607,6 +626,7 @@ void scan_tiles_kernel(ScanKernelParams p) {
     k.a = live ? p.A[d * N + n] : 0.0f;
     k.a2 = k.a * kLog2e;
     k.ia = (k.a != 0.0f) ? 1.0f / k.a : 0.0f;
+    static_for<kRow>([&](auto J) { k.iar[decltype(J)::value] = row_bcast<decltype(J)::value>(k.ia); });
     k.dsk = (p.Dskip && dvalid) ? p.Dskip[d] : 0.0f;
     k.dbias = (p.dbias && dvalid) ? p.dbias[d] : 0.0f;
     k.wp0 = k.wp1 = k.wp2 = k.wp3 = k.cb = 0.0f;
@@ -630,10 +650,14 @@ void scan_tiles_kernel(ScanKernelParams p) {
     }
     // Wave-uniform choice of the update form (see the file comment).
     const bool fast = __all(!live || fabsf(k.a) >= kFastMinAbsA);
-    if (fast)
+    if (fast) {
+        // The fast form carries g = A h (the 1/A moves to the read-out).
+        h *= k.a;
         scan_tiles_body<IO, CONV, VEC, true>(p, geo, T, lds, wave, c, n, k, h, x_prev);
-    else
+        h *= k.ia;
+    } else {
         scan_tiles_body<IO, CONV, VEC, false>(p, geo, T, lds, wave, c, n, k, h, x_prev);
+    }
     if (p.h_out && live) p.h_out[(b * D + d) * N + n] = h;
 }
 

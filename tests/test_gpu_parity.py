@@ -100,7 +100,9 @@ def test_zero_step_holds_state():
     inp["delta"] = torch.zeros_like(inp["delta"])
     y, hf = run_scan(inp)
     torch.cuda.synchronize()
-    assert torch.equal(hf, inp["h0"])
+    # The state is carried as A h and divided by A on the way out: one
+    # rounding at most, otherwise held exactly.
+    assert torch.allclose(hf, inp["h0"], rtol=2.5e-7, atol=0.0)
     yr, _ = oracle_scan(inp)
     assert_close(to64(y), yr, 1e-2, "y")
 
