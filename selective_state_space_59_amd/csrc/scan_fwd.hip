@@ -188,15 +188,34 @@ __device__ __forceinline__ BcastSel make_sel(int lane) {
 // Workgroup tiles.  A workgroup of W waves covers CH = 4W consecutive
 // channels of one batch row.  Per 16-step block it stages in LDS, with wide
 // coalesced loads shared by all its waves:
-//   own [slot][x|delta|z][16 rows][CH]   raw I/O elements
-//   ybuf[slot][16 rows][CH]              raw outputs, stored coalesced
-//   bc  [slot][B|C][16 rows][16]         raw B and C rows (zero past N)
-// and per wave a partial-sum transpose area.  Slots alternate per block.
+//   own [3 slots][x|delta|z][16 rows][CH + pad]  raw I/O elements
+//   bc  [3 slots][B|C][16 rows][16]               raw B and C rows (zero past N)
+//   ybuf[2][16 rows][CH + pad]                    raw outputs, stored coalesced
+// and per wave a partial-sum transpose area.  The row pad puts the 16 time
+// steps that the 16 lanes of a wave row read (or write) on distinct banks;
+// the planes of one slot are a fixed distance apart (sized for W = 16), so
+// a lane reaches its x, delta and z with one address.
 // ---------------------------------------------------------------------------
+constexpr int kSlots = 3;
+constexpr int kMaxW = 16;
+
+// Row stride in dwords: a multiple of 4 (16-byte chunks) that is 4 mod 8,
+// so the 16 time steps a wave row reads fall on two-way-shared banks at
+// worst.
+template <typename IO>
+__device__ __host__ constexpr int row_dwords(int W) {
+    const int data = (4 * W * (int)sizeof(typename IO::storage) + 3) / 4;
+    const int s = (data + 3) / 4 * 4;
+    return s % 8 == 0 ? s + 4 : s;
+}
+template <typename IO>
+constexpr uint32_t kPlane = (uint32_t)kTB * 4u * row_dwords<IO>(kMaxW);
+
 struct Tiles {
     int CH;
-    uint32_t own, ybuf, bc, part;    // byte offsets in the dynamic LDS block
-    uint32_t own_slot, ybuf_slot, bc_slot, own_tensor;
+    uint32_t rs;                   // bytes per staged row
+    uint32_t own, bc, ybuf, part;  // byte offsets in the dynamic LDS block
+    uint32_t own_slot, bc_slot, ybuf_slot;
 };
 
 template <typename IO>
@@ -204,14 +223,14 @@ __device__ __host__ __forceinline__ Tiles tile_layout(int W) {
     constexpr int es = sizeof(typename IO::storage);
     Tiles t;
     t.CH = 4 * W;
-    t.own_tensor = (uint32_t)(kTB * t.CH * es);
-    t.own_slot = 3 * t.own_tensor;
-    t.ybuf_slot = (uint32_t)(kTB * t.CH * es);
+    t.rs = 4u * (uint32_t)row_dwords<IO>(W);
+    t.own_slot = 3 * kPlane<IO>;
     t.bc_slot = (uint32_t)(2 * kTB * kRow * es);
+    t.ybuf_slot = kTB * t.rs;
     t.own = 0;
-    t.ybuf = t.own + 2 * t.own_slot;
-    t.bc = t.ybuf + 2 * t.ybuf_slot;
-    t.part = (t.bc + 2 * t.bc_slot + 15u) & ~15u;
+    t.bc = t.own + kSlots * t.own_slot;
+    t.ybuf = t.bc + kSlots * t.bc_slot;
+    t.part = (t.ybuf + 2 * t.ybuf_slot + 15u) & ~15u;
     return t;
 }
 template <typename IO>
@@ -222,122 +241,159 @@ __host__ __forceinline__ size_t tile_lds_bytes(int W) {
 
 // Launch-wide addressing of one workgroup.
 struct Geo {
-    __amdgpu_buffer_rsrc_t rx, rdt, rz, ry, rb, rc;
+    __amdgpu_buffer_rsrc_t rx, rdt, rz, ry, rb, rc;  // element path
     uint32_t row_step;   // bytes per block in x/delta/z/y
     uint32_t bc_step;    // bytes per block in B/C
     int64_t D;
     int N, W, d0;
 };
 
+// Wide path: how the block moves between global memory and LDS.  Each wave
+// has one duty, so every load instruction reads one tensor through a
+// wave-uniform descriptor and each thread holds one 16-byte chunk:
+//   waves [0, a), [a, 2a), [2a, 3a): chunk q of x, delta, z, with
+//     q = (wave - role a) * 64 + lane < 16 CH / cw  (row q / (CH / cw),
+//     channels cw (q % (CH / cw)) .. +cw-1; cw = 16 / element size);
+//   wave 3a: chunk lane of the 16 B rows; wave 3a + 1: of the C rows;
+//   the x waves also carry the matching chunks of y from LDS to memory.
+// a = ceil(16 CH / cw / 64).  The launch picks W so that 3a + 2 <= W.
+struct Duty {
+    const char *gbase;  // tensor of the duty at the launch's first row (uniform)
+    int64_t grec;       // its bytes in this launch (uniform)
+    uint32_t step;      // its bytes per block (uniform)
+    uint32_t goff;      // the thread's chunk within a block, or kOOB
+    uint32_t lds;       // LDS offset of the chunk within a slot of the own or bc area
+    bool to_bc;         // the duty fills the bc area (uniform)
+    bool ystore;        // the wave stores y chunks (uniform)
+    uint32_t ylds;      // ybuf offset of the thread's y chunk
+};
+
+template <typename IO>
+__device__ __forceinline__ constexpr int chunk_ch() {
+    return 16 / (int)sizeof(typename IO::storage);
+}
+template <typename IO>
+__device__ __forceinline__ int duty_waves(int W) {  // a
+    return (kTB * 4 * W / chunk_ch<IO>() + 63) / 64;
+}
+
+template <typename IO>
+__device__ __forceinline__ Duty make_duty(const ScanKernelParams &p, const Tiles &T, int64_t b,
+                                          int d0, int wave, int lane) {
+    constexpr int es = sizeof(typename IO::storage);
+    constexpr int cw = chunk_ch<IO>();
+    const int W = T.CH / 4;
+    const int a = duty_waves<IO>(W);
+    const int per_row = T.CH / cw;  // chunks per staged row
+    const int64_t D = p.D, N = p.N, rows = p.t_end - p.t_begin;
+    const int role = wave < 3 * a ? wave / a : 3 + (wave - 3 * a);  // uniform
+    Duty d;
+    d.to_bc = role == 3 || role == 4;
+    d.ystore = role == 0;
+    d.goff = kOOB;
+    d.lds = 0;
+    d.ylds = 0;
+    if (role < 3) {
+        const void *src = role == 0 ? p.x : role == 1 ? p.delta : p.z;
+        const int64_t base = (b * p.L + p.t_begin) * D * es;
+        d.gbase = static_cast<const char *>(src ? src : p.x) + base;
+        d.grec = src ? rows * D * es : 0;  // no gate: every z read gives 0
+        d.step = (uint32_t)(kTB * D * es);
+        const int q = (wave - role * a) * 64 + lane;
+        const int row = q / per_row, ck = q % per_row;
+        const int64_t ch = d0 + (int64_t)ck * cw;
+        if (q < kTB * per_row && ch < D) d.goff = (uint32_t)((row * D + ch) * es);
+        if (q < kTB * per_row) {
+            d.lds = (uint32_t)role * kPlane<IO> + (uint32_t)(row * T.rs + ck * 16);
+            d.ylds = (uint32_t)(row * T.rs + ck * 16);
+        }
+    } else {
+        const void *src = role == 3 ? p.Bm : p.Cm;
+        const int64_t base = (b * p.L + p.t_begin) * N * es;
+        d.gbase = static_cast<const char *>(src) + base;
+        d.grec = role <= 4 ? rows * N * es : 0;
+        d.step = (uint32_t)(kTB * N * es);
+        if (role <= 4 && lane * 16 < kTB * kRow * es) {
+            d.goff = (uint32_t)(lane * 16);
+            d.lds = (uint32_t)((role - 3) * kTB * kRow * es + lane * 16);
+        }
+    }
+    return d;
+}
+
+// Buffer descriptor of the duty's tensor for block jb (rebased on the
+// block, so the per-lane offsets stay fixed; scalar arithmetic only).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t duty_rsrc(const Duty &d, int64_t jb) {
+    const int64_t off = jb * (int64_t)d.step;
+    return rsrc(d.gbase, off, d.grec - off);
+}
+
 // Raw global data of one block held by one thread between its load and its
-// copy into LDS.  Every load instruction reads a single tensor, so its
-// buffer descriptor is wave-uniform (a per-lane descriptor would turn each
-// load into a loop over lanes).
-//   own tiles, wide path: thread t < 16 W holds chunk t (row t / W, channels
-//     4 (t % W) .. +3) of each of x, delta, z;
-//   own tiles, element path: thread t holds element t (row t / CH, channel
-//     t % CH) of each of x, delta, z;
-//   B/C rows, wide path (N = 16): threads t < 64 hold chunk t (4 elements)
-//     of B and of C; element path: elements t + i * threads (< 256) of B, C.
-// Which path runs is fixed at compile time: a run-time choice would merge
-// the two register sets at the loop back-edge with copies that must wait
-// for every load in flight.
-struct Fetch {
-    uint4 own[3];
-    uint4 bcv[2];
+// copy into LDS.  Which layout is used is fixed at compile time: a run-time
+// choice would merge two register sets at the loop back-edge with copies
+// that must wait for every load in flight.
+//   wide path: the thread's 16-byte chunk of its duty;
+//   element path: element t (row t / CH, channel t % CH) of each of x,
+//     delta, z, and elements t + i * threads (< 256) of the B and C rows.
+template <bool VEC>
+struct Fetch;
+template <>
+struct Fetch<true> {
+    uint4 v;
+};
+template <>
+struct Fetch<false> {
+    uint32_t own[3];
     uint32_t bce[8];
 };
 
 template <typename IO, bool VEC>
-__device__ __forceinline__ void fetch_block(const Geo &g, uint32_t blk_off, uint32_t bc_off,
-                                            int tid, int nthreads, Fetch &f) {
+__device__ __forceinline__ void fetch_block(const Geo &g, const Duty &d, int64_t jb, int tid,
+                                            int nthreads, Fetch<VEC> &f) {
     constexpr int es = sizeof(typename IO::storage);
-    const int CH = 4 * g.W;
-    const __amdgpu_buffer_rsrc_t rs[3] = {g.rx, g.rdt, g.rz};
-    if (VEC) {
-        const int row = tid / g.W, cc = tid % g.W;
-        const int ch = g.d0 + 4 * cc;
-        const uint32_t off = (tid < kTB * g.W && ch < g.D)
-                                 ? blk_off + (uint32_t)((row * g.D + ch) * es) : kOOB;
-#pragma unroll
-        for (int i = 0; i < 3; ++i) {
-            if constexpr (es == 2) {
-                const uint2 v = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rs[i], off, 0, 0));
-                f.own[i] = make_uint4(v.x, v.y, 0u, 0u);
-            } else {
-                f.own[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs[i], off, 0, 0));
-            }
-        }
+    if constexpr (VEC) {
+        f.v = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(duty_rsrc(d, jb), d.goff, 0, 0));
     } else {
+        const uint32_t blk_off = (uint32_t)(jb * g.row_step), bc_off = (uint32_t)(jb * g.bc_step);
+        const int CH = 4 * g.W;
+        const __amdgpu_buffer_rsrc_t rs[3] = {g.rx, g.rdt, g.rz};
         const int row = tid / CH, ci = tid % CH;
         const int ch = g.d0 + ci;
         const uint32_t off = ch < g.D ? blk_off + (uint32_t)((row * g.D + ch) * es) : kOOB;
 #pragma unroll
-        for (int i = 0; i < 3; ++i) f.own[i].x = buf_ld<IO>(rs[i], off);
-    }
-    if (VEC) {
-        const uint32_t off = tid < 64 ? bc_off + (uint32_t)(tid * 4 * es) : kOOB;
-        if constexpr (es == 2) {
-            const uint2 b = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(g.rb, off, 0, 0));
-            const uint2 c = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(g.rc, off, 0, 0));
-            f.bcv[0] = make_uint4(b.x, b.y, 0u, 0u);
-            f.bcv[1] = make_uint4(c.x, c.y, 0u, 0u);
-        } else {
-            f.bcv[0] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(g.rb, off, 0, 0));
-            f.bcv[1] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(g.rc, off, 0, 0));
-        }
-    } else {
+        for (int i = 0; i < 3; ++i) f.own[i] = buf_ld<IO>(rs[i], off);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int e = tid + i * nthreads;
-            const int row = e / kRow, nn = e % kRow;
-            const uint32_t off = (e < kTB * kRow && nn < g.N)
-                                     ? bc_off + (uint32_t)((row * g.N + nn) * es) : kOOB;
-            f.bce[i] = buf_ld<IO>(g.rb, off);
-            f.bce[4 + i] = buf_ld<IO>(g.rc, off);
+            const int brow = e / kRow, nn = e % kRow;
+            const uint32_t boff = (e < kTB * kRow && nn < g.N)
+                                      ? bc_off + (uint32_t)((brow * g.N + nn) * es) : kOOB;
+            f.bce[i] = buf_ld<IO>(g.rb, boff);
+            f.bce[4 + i] = buf_ld<IO>(g.rc, boff);
         }
     }
 }
 
 template <typename IO, bool VEC>
-__device__ __forceinline__ void stage_block(const Geo &g, const Tiles &T, char *lds, int slot,
-                                            int tid, int nthreads, const Fetch &f) {
+__device__ __forceinline__ void stage_block(const Geo &g, const Duty &d, const Tiles &T, char *lds,
+                                            int slot, int tid, int nthreads, const Fetch<VEC> &f) {
     constexpr int es = sizeof(typename IO::storage);
-    const int CH = T.CH;
-    char *own = lds + T.own + slot * T.own_slot;
-    if (VEC) {
-        if (tid < kTB * g.W) {
-            const int row = tid / g.W, cc = tid % g.W;
-            char *dst = own + (row * CH + 4 * cc) * es;
-#pragma unroll
-            for (int i = 0; i < 3; ++i) {
-                if constexpr (es == 2)
-                    *reinterpret_cast<uint2 *>(dst + i * T.own_tensor) = make_uint2(f.own[i].x, f.own[i].y);
-                else
-                    *reinterpret_cast<uint4 *>(dst + i * T.own_tensor) = f.own[i];
-            }
-        }
+    if constexpr (VEC) {
+        // Lanes without a chunk (or past the channel range) write nothing:
+        // channels past D are never stored, so their staged values do not matter.
+        char *base = lds + (d.to_bc ? T.bc + slot * T.bc_slot : T.own + slot * T.own_slot);
+        if (d.goff != kOOB) *reinterpret_cast<uint4 *>(base + d.lds) = f.v;
     } else {
-        char *dst = own + tid * es;  // element tid = (row, channel) of each tensor
+        char *own = lds + T.own + slot * T.own_slot;
+        char *bc = lds + T.bc + slot * T.bc_slot;
+        char *cc = bc + kTB * kRow * es;
+        const int row = tid / T.CH, ci = tid % T.CH;
+        char *dst = own + row * T.rs + ci * es;
 #pragma unroll
         for (int i = 0; i < 3; ++i) {
-            if constexpr (es == 2) *reinterpret_cast<uint16_t *>(dst + i * T.own_tensor) = (uint16_t)f.own[i].x;
-            else *reinterpret_cast<uint32_t *>(dst + i * T.own_tensor) = f.own[i].x;
+            if constexpr (es == 2) *reinterpret_cast<uint16_t *>(dst + i * kPlane<IO>) = (uint16_t)f.own[i];
+            else *reinterpret_cast<uint32_t *>(dst + i * kPlane<IO>) = f.own[i];
         }
-    }
-    char *bc = lds + T.bc + slot * T.bc_slot;
-    char *cc = bc + kTB * kRow * es;
-    if (VEC) {
-        if (tid < 64) {
-            if constexpr (es == 2) {
-                *reinterpret_cast<uint2 *>(bc + tid * 8) = make_uint2(f.bcv[0].x, f.bcv[0].y);
-                *reinterpret_cast<uint2 *>(cc + tid * 8) = make_uint2(f.bcv[1].x, f.bcv[1].y);
-            } else {
-                *reinterpret_cast<uint4 *>(bc + tid * 16) = f.bcv[0];
-                *reinterpret_cast<uint4 *>(cc + tid * 16) = f.bcv[1];
-            }
-        }
-    } else {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int e = tid + i * nthreads;
@@ -354,35 +410,53 @@ __device__ __forceinline__ void stage_block(const Geo &g, const Tiles &T, char *
     }
 }
 
-// Coalesced store of one block of outputs from LDS.
+// Outputs of block jb from ybuf half `par` to global memory.  The LDS read
+// is issued by read_ybuf early and the store made later by store_y, so the
+// read latency is hidden.
+template <bool VEC>
+struct YChunk;
+template <>
+struct YChunk<true> {
+    uint4 v;
+};
+template <>
+struct YChunk<false> {
+    uint32_t v;
+};
 template <typename IO, bool VEC>
-__device__ __forceinline__ void store_block(const Geo &g, const Tiles &T, const char *lds,
-                                            int slot, uint32_t blk_off, int tid, int nthreads) {
+__device__ __forceinline__ YChunk<VEC> read_ybuf(const Duty &d, const Tiles &T, const char *lds,
+                                                 int par, int tid) {
     constexpr int es = sizeof(typename IO::storage);
-    const int CH = T.CH;
-    const char *yb = lds + T.ybuf + slot * T.ybuf_slot;
-    if (VEC) {
-        if (tid < kTB * g.W) {
-            const int row = tid / g.W, cc = tid % g.W;
-            const int ch = g.d0 + 4 * cc;
-            const uint32_t off = ch < g.D ? blk_off + (uint32_t)((row * g.D + ch) * es) : kOOB;
-            const char *src = yb + (row * CH + 4 * cc) * es;
-            if constexpr (es == 2) {
-                const uint2 v = *reinterpret_cast<const uint2 *>(src);
-                __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(v2i_t, v), g.ry, off, 0, 0);
-            } else {
-                const uint4 v = *reinterpret_cast<const uint4 *>(src);
-                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4i_t, v), g.ry, off, 0, 0);
-            }
-        }
+    const char *yb = lds + T.ybuf + par * T.ybuf_slot;
+    YChunk<VEC> y;
+    if constexpr (VEC) {
+        y.v = *reinterpret_cast<const uint4 *>(yb + d.ylds);
     } else {
+        const char *src = yb + (tid / T.CH) * T.rs + (tid % T.CH) * es;
+        if constexpr (es == 2) y.v = *reinterpret_cast<const uint16_t *>(src);
+        else y.v = *reinterpret_cast<const uint32_t *>(src);
+    }
+    return y;
+}
+template <typename IO, bool VEC>
+__device__ __forceinline__ void store_y(const ScanKernelParams &p, const Geo &g, const Duty &d,
+                                        const YChunk<VEC> &y, int64_t jb, int tid) {
+    constexpr int es = sizeof(typename IO::storage);
+    if constexpr (VEC) {
+        const int64_t off = jb * (int64_t)d.step;
+        const __amdgpu_buffer_rsrc_t r =
+            rsrc(static_cast<const char *>(p.y) + (d.gbase - static_cast<const char *>(p.x)), off,
+                 d.grec - off);
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4i_t, y.v), r, d.goff, 0, 0);
+    } else {
+        const int CH = 4 * g.W;
         const int row = tid / CH, ci = tid % CH;
         const int ch = g.d0 + ci;
-        const uint32_t off = ch < g.D ? blk_off + (uint32_t)((row * g.D + ch) * es) : kOOB;
+        const uint32_t off = ch < g.D ? (uint32_t)(jb * g.row_step) + (uint32_t)((row * g.D + ch) * es) : kOOB;
         if constexpr (es == 2)
-            __builtin_amdgcn_raw_buffer_store_b16(*reinterpret_cast<const uint16_t *>(yb + tid * es), g.ry, off, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b16((unsigned short)y.v, g.ry, off, 0, 0);
         else
-            __builtin_amdgcn_raw_buffer_store_b32(*reinterpret_cast<const uint32_t *>(yb + tid * es), g.ry, off, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b32(y.v, g.ry, off, 0, 0);
     }
 }
 
@@ -390,75 +464,172 @@ __device__ __forceinline__ void store_block(const Geo &g, const Tiles &T, const 
 //  bf16: row 4g + lane%4, entries 4*(lane/16) .. +3   (A operand, 16x16x16)
 //  fp32: row 4g + lane/16, entry lane%16                (B operand, 16x16x4)
 template <typename IO>
-__device__ __forceinline__ mfma_f32x4 bcast_group(const char *rows, int g, int lane,
-                                                  const BcastSel &sel) {
+struct BcOperand {
+    using type = typename std::conditional<std::is_same<IO, io_bf16>::value, uint2, float>::type;
+};
+template <typename IO>
+__device__ __forceinline__ typename BcOperand<IO>::type load_bc_operand(const char *rows, int g,
+                                                                       int lane) {
+    if constexpr (std::is_same<IO, io_bf16>::value)
+        return *reinterpret_cast<const uint2 *>(rows + ((4 * g + (lane & 3)) * kRow + 4 * (lane >> 4)) * 2);
+    else
+        return *reinterpret_cast<const float *>(rows + ((4 * g + (lane >> 4)) * kRow + (lane & 15)) * 4);
+}
+// Broadcast of rows 4g..4g+3 to every wave row: register r of lane l gets
+// entry l%16 of row 4g + r (0/1 selector, exact).
+template <typename IO>
+__device__ __forceinline__ mfma_f32x4 bcast(typename BcOperand<IO>::type op, const BcastSel &sel) {
     const mfma_f32x4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
-    if constexpr (std::is_same<IO, io_bf16>::value) {
-        const uint2 op = *reinterpret_cast<const uint2 *>(
-            rows + ((4 * g + (lane & 3)) * kRow + 4 * (lane >> 4)) * 2);
+    if constexpr (std::is_same<IO, io_bf16>::value)
         return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(mfma_bf16x4, op), sel.bf,
                                                          zero, 0, 0, 0);
-    } else {
-        const float op = *reinterpret_cast<const float *>(
-            rows + ((4 * g + (lane >> 4)) * kRow + (lane & 15)) * 4);
+    else
         return __builtin_amdgcn_mfma_f32_16x16x4f32(sel.f, op, zero, 0, 0, 0);
-    }
-}
-
-__device__ __forceinline__ void wave_sync() {
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-    __builtin_amdgcn_wave_barrier();
 }
 
 struct LaneConst {
     float a, a2, ia, dsk, dbias, cb, wp0, wp1, wp2, wp3;
-    float iar[kRow];  // 1 / A of every state entry of the lane's channel (0 where A == 0)
 };
 
-// One block of one wave: decode the lane's own step from the staged tile,
-// run 16 recurrence steps, transpose the partial read-outs, write y to LDS.
-template <typename IO, bool CONV, bool FAST, bool TAIL>
-__device__ __forceinline__ void compute_block(const ScanKernelParams &p, const Tiles &T,
-                                              char *lds, int slot, int64_t t0, int wave, int c,
-                                              int n, int lane, const BcastSel &sel,
-                                              const LaneConst &k, float &x_prev, float &h) {
-    constexpr int es = sizeof(typename IO::storage);
-    const int ci = 4 * wave + c;
-    const char *own = lds + T.own + slot * T.own_slot + (n * T.CH + ci) * es;
-    float xv, dt, zv;
-    if constexpr (es == 2) {
-        xv = __uint_as_float((uint32_t)*reinterpret_cast<const uint16_t *>(own) << 16);
-        dt = __uint_as_float((uint32_t)*reinterpret_cast<const uint16_t *>(own + T.own_tensor) << 16);
-        zv = __uint_as_float((uint32_t)*reinterpret_cast<const uint16_t *>(own + 2 * T.own_tensor) << 16);
+// Read-out of one step: the sum over the 16 state entries of the partials
+// C g that the lanes of this row transposed into prow.  The fast form keeps
+// g = A h, so each partial is first multiplied by 1/A of its entry, which
+// lane i of the row holds (a DPP row broadcast folded into the FMA).
+template <bool FAST>
+__device__ __forceinline__ float readout(const float *prow, const float *iat, int n) {
+    float part[kRow];
+#pragma unroll
+    for (int i = 0; i < kRow; ++i) part[i] = prow[i * kPStride + n];
+    if (FAST) {
+        float ia[kRow];
+#pragma unroll
+        for (int i = 0; i < kRow; i += 4) {
+            const float4 v = *reinterpret_cast<const float4 *>(iat + i);
+            ia[i] = v.x;
+            ia[i + 1] = v.y;
+            ia[i + 2] = v.z;
+            ia[i + 3] = v.w;
+        }
+        float s0 = part[0] * ia[0], s1 = part[1] * ia[1];
+#pragma unroll
+        for (int i = 2; i < kRow; i += 2) {
+            s0 = __builtin_fmaf(part[i], ia[i], s0);
+            s1 = __builtin_fmaf(part[i + 1], ia[i + 1], s1);
+        }
+        return s0 + s1;
     } else {
-        xv = *reinterpret_cast<const float *>(own);
-        dt = *reinterpret_cast<const float *>(own + T.own_tensor);
-        zv = *reinterpret_cast<const float *>(own + 2 * T.own_tensor);
+#pragma unroll
+        for (int w = kRow / 2; w >= 1; w /= 2)
+#pragma unroll
+            for (int i = 0; i < w; ++i) part[i] += part[i + w];
+        return part[0];
     }
+}
+
+// Per-lane values carried from one block to the next.
+struct Carry {
+    uint32_t own[3];       // raw x, delta, z of this lane's step in the current block
+    float u_prev, z_prev;  // u and z of this lane's step in the previous block
+    float x_prev;          // conv history: x of the previous block (lanes 13..15 used)
+    float h;               // state (A h in the fast form)
+};
+
+template <typename IO>
+__device__ __forceinline__ void read_own(const Tiles &T, const char *lds, int slot, int n, int ci,
+                                         uint32_t (&raw)[3]) {
+    constexpr int es = sizeof(typename IO::storage);
+    const char *src = lds + T.own + slot * T.own_slot + n * T.rs + ci * es;
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+        if constexpr (es == 2) raw[i] = *reinterpret_cast<const uint16_t *>(src + i * kPlane<IO>);
+        else raw[i] = *reinterpret_cast<const uint32_t *>(src + i * kPlane<IO>);
+    }
+}
+
+// One 16-step block of one wave, software-pipelined across blocks:
+//   * the LDS reads whose results this block needs later (its partial
+//     read-outs of the previous block, the next block's own inputs, the
+//     outputs two blocks back) are issued first;
+//   * the previous block's outputs are finished while those reads and the
+//     B/C broadcasts are in flight;
+//   * then the 16 recurrence steps, whose partial read-outs are transposed
+//     through LDS and summed one block later;
+//   * finally block j+2 is copied from registers into LDS and block j+4 is
+//     requested from global memory.
+// PAR = j % 2 selects the ybuf halves; TAIL masks steps past the sequence
+// end; STAGE is off in the last block.
+template <typename IO, bool CONV, bool VEC, bool FAST, bool TAIL, int PAR, bool STAGE>
+__device__ __forceinline__ void block_iter(const ScanKernelParams &p, const Geo &geo,
+                                           const Tiles &T, char *lds, int wave, int c, int n,
+                                           int lane, const BcastSel &sel, const LaneConst &k,
+                                           const Duty &du, int64_t j, int s_cur, Fetch<VEC> &f,
+                                           Carry &cy) {
+    constexpr int es = sizeof(typename IO::storage);
+    const int tid = threadIdx.x, nthreads = blockDim.x;
+    const int ci = 4 * wave + c;
+    const int s_next = s_cur == kSlots - 1 ? 0 : s_cur + 1;
+    const int s_stage = s_next == kSlots - 1 ? 0 : s_next + 1;
+    float *prow = reinterpret_cast<float *>(lds + T.part) + (wave * kChPerWave + c) * kPRow;
+    const char *brows = lds + T.bc + s_cur * T.bc_slot;
+    const char *crows = brows + kTB * kRow * es;
+
+    __syncthreads();
+    // -- LDS reads first ------------------------------------------------------
+    const float acc = readout<FAST>(prow, prow + kRow * kPStride, n);
+    uint32_t own_next[3];
+    read_own<IO>(T, lds, s_next, n, ci, own_next);
+    const YChunk<VEC> yst = read_ybuf<IO, VEC>(du, T, lds, PAR, tid);
+    typename BcOperand<IO>::type bop[4], cop[4];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+        bop[g] = load_bc_operand<IO>(brows, g, lane);
+        cop[g] = load_bc_operand<IO>(crows, g, lane);
+    }
+
+    // -- this block's inputs ---------------------------------------------------
+    const float xv = widen<IO>(cy.own[0]);
+    float dt = widen<IO>(cy.own[1]);
+    const float zv = widen<IO>(cy.own[2]);
     float u = xv;
     if (CONV) {
-        const float xm1 = row_shift_in<1>(xv, x_prev);
-        const float xm2 = row_shift_in<2>(xv, x_prev);
-        const float xm3 = row_shift_in<3>(xv, x_prev);
+        const float xm1 = row_shift_in<1>(xv, cy.x_prev);
+        const float xm2 = row_shift_in<2>(xv, cy.x_prev);
+        const float xm3 = row_shift_in<3>(xv, cy.x_prev);
         u = silu(k.cb + k.wp0 * xm3 + k.wp1 * xm2 + k.wp2 * xm1 + k.wp3 * xv);
-        x_prev = xv;
+        cy.x_prev = xv;
     }
     if (p.softplus) dt = softplus_fast(dt + k.dbias);
-    if (TAIL && t0 + n >= p.t_end) {  // past the end: the state must not move
+    if (TAIL && p.t_begin + j * kTB + n >= p.t_end) {  // past the end: the state must not move
         dt = 0.0f;
         u = 0.0f;
     }
-    const char *brows = lds + T.bc + slot * T.bc_slot;
-    const char *crows = brows + kTB * kRow * es;
-    float *prow = reinterpret_cast<float *>(lds + T.part) + (wave * kChPerWave + c) * kPRow;
 
+    // -- outputs of block j-1 (lane (c, n) finishes its step n) ---------------
+    {
+        float yv = acc + k.dsk * cy.u_prev;
+        if (p.z) yv *= silu(cy.z_prev);
+        char *ydst = lds + T.ybuf + (1 - PAR) * T.ybuf_slot + n * T.rs + ci * es;
+        if constexpr (es == 2)
+            *reinterpret_cast<uint16_t *>(ydst) = __builtin_bit_cast(uint16_t, (__bf16)yv);
+        else
+            *reinterpret_cast<float *>(ydst) = yv;
+    }
+    // -- outputs of block j-2 leave ----------------------------------------------
+    if (j >= 2 && (!VEC || du.ystore)) store_y<IO, VEC>(p, geo, du, yst, j - 2, tid);
+
+    // -- the 16 steps ----------------------------------------------------------
     // Steps in groups of four: one broadcast MFMA each for B and C per
-    // group, one 128-bit LDS write of the group's four partial read-outs.
+    // group, issued one group ahead so the matrix cores' latency is hidden,
+    // and one 128-bit LDS write of the group's four partial read-outs.
+    mfma_f32x4 Bn = bcast<IO>(bop[0], sel), Cn = bcast<IO>(cop[0], sel);
     static_for<kTB / 4>([&](auto G) {
         constexpr int gi = decltype(G)::value;
         constexpr int g4 = 4 * gi;
-        const mfma_f32x4 Bk = bcast_group<IO>(brows, gi, lane, sel);
-        const mfma_f32x4 Ck = bcast_group<IO>(crows, gi, lane, sel);
+        const mfma_f32x4 Bk = Bn, Ck = Cn;
+        if constexpr (gi + 1 < kTB / 4) {
+            Bn = bcast<IO>(bop[gi + 1], sel);
+            Cn = bcast<IO>(cop[gi + 1], sel);
+        }
         float pk[4];
         static_for<4>([&](auto K) {
             constexpr int kk = decltype(K)::value;
@@ -473,107 +644,103 @@ __device__ __forceinline__ void compute_block(const ScanKernelParams &p, const T
             } else {
                 bx = (dtk * phi_of(dtk * k.a, e)) * bu;
             }
-            h = __builtin_fmaf(e, h, bx);
-            pk[kk] = Ck[kk] * h;
+            cy.h = __builtin_fmaf(e, cy.h, bx);
+            pk[kk] = Ck[kk] * cy.h;
         });
         *reinterpret_cast<float4 *>(&prow[n * kPStride + g4]) = make_float4(pk[0], pk[1], pk[2], pk[3]);
     });
-    wave_sync();
-    float part[kRow];
+
+    cy.u_prev = u;
+    cy.z_prev = zv;
 #pragma unroll
-    for (int j = 0; j < kRow; ++j) part[j] = prow[j * kPStride + n];
-    float acc;
-    if (FAST) {
-        // The fast form keeps g = A h, so C h = (C g) / A per entry.
-        float s0 = part[0] * k.iar[0], s1 = part[1] * k.iar[1];
-#pragma unroll
-        for (int j = 2; j < kRow; j += 2) {
-            s0 = __builtin_fmaf(part[j], k.iar[j], s0);
-            s1 = __builtin_fmaf(part[j + 1], k.iar[j + 1], s1);
-        }
-        acc = s0 + s1;
-    } else {
-#pragma unroll
-        for (int w = kRow / 2; w >= 1; w /= 2)
-#pragma unroll
-            for (int j = 0; j < w; ++j) part[j] += part[j + w];
-        acc = part[0];
+    for (int i = 0; i < 3; ++i) cy.own[i] = own_next[i];
+
+    if (STAGE) {
+        stage_block<IO, VEC>(geo, du, T, lds, s_stage, tid, nthreads, f);
+        // Keep the refill after the copy, so the new data can land in the
+        // same registers.
+        __builtin_amdgcn_sched_barrier(0);
+        fetch_block<IO, VEC>(geo, du, j + 4, tid, nthreads, f);
     }
-    float yv = acc + k.dsk * u;
-    if (p.z) yv *= silu(zv);
-    char *ydst = lds + T.ybuf + slot * T.ybuf_slot + (n * T.CH + ci) * es;
-    if constexpr (es == 2)
-        *reinterpret_cast<uint16_t *>(ydst) = __builtin_bit_cast(uint16_t, (__bf16)yv);
-    else
-        *reinterpret_cast<float *>(ydst) = yv;
-    wave_sync();  // the next block rewrites the partials
 }
 
 template <typename IO, bool CONV, bool VEC, bool FAST>
 __device__ __forceinline__ void scan_tiles_body(const ScanKernelParams &p, const Geo &geo,
-                                                const Tiles &T, char *lds, int wave, int c,
-                                                int n, const LaneConst &k, float &h,
-                                                float x_prev) {
+                                                const Tiles &T, char *lds, int64_t b, int wave,
+                                                int c, int n, const LaneConst &k, Carry &cy) {
     const int tid = threadIdx.x, nthreads = blockDim.x;
     const int lane = tid & 63;
+    const int ci = 4 * wave + c;
     const BcastSel sel = make_sel(lane);
     const int64_t rows = p.t_end - p.t_begin;
     const int64_t nblocks = (rows + kTB - 1) / kTB;
 
-    // Tile j is requested three blocks before it is computed (two blocks of
-    // latency budget), copied into LDS slot j % 2 one block before, and its
-    // outputs leave LDS one block after.  Unrolled by two so the two fetch
-    // register sets alternate without copies.  The loop has a single exit
-    // at its bottom (the last one or two blocks run after it): an exit in
-    // the middle would route through the back-edge once the control flow is
-    // structured, and the load counters merged there would force a wait for
-    // every prefetch in flight.  Prefetches past the last block read zeros
-    // or unused rows and are never consumed.
-    Fetch f0, f1;
-    fetch_block<IO, VEC>(geo, 0, 0, tid, nthreads, f0);
-    fetch_block<IO, VEC>(geo, geo.row_step, geo.bc_step, tid, nthreads, f1);
-    stage_block<IO, VEC>(geo, T, lds, 0, tid, nthreads, f0);
-    fetch_block<IO, VEC>(geo, 2 * geo.row_step, 2 * geo.bc_step, tid, nthreads, f0);
-    uint32_t ro = 0, bo = 0;  // offsets of block j
-    int64_t j = 0;
-    for (; j + 2 < nblocks; j += 2) {
-        // -- block j (slot 0); f1 holds block j+1, f0 block j+2 --------------
-        __syncthreads();
-        if (j > 0) store_block<IO, VEC>(geo, T, lds, 1, ro - geo.row_step, tid, nthreads);
-        compute_block<IO, CONV, FAST, false>(p, T, lds, 0, p.t_begin + j * kTB, wave, c, n, lane, sel, k,
-                                      x_prev, h);
-        stage_block<IO, VEC>(geo, T, lds, 1, tid, nthreads, f1);
-        // Keep the refill of f1 after its copy into LDS, so the new data can
-        // land in the same registers.
-        __builtin_amdgcn_sched_barrier(0);
-        fetch_block<IO, VEC>(geo, ro + 3 * geo.row_step, bo + 3 * geo.bc_step, tid, nthreads, f1);
-        // -- block j+1 (slot 1); f0 holds block j+2, f1 block j+3 ------------
-        __syncthreads();
-        store_block<IO, VEC>(geo, T, lds, 0, ro, tid, nthreads);
-        compute_block<IO, CONV, FAST, false>(p, T, lds, 1, p.t_begin + (j + 1) * kTB, wave, c, n, lane,
-                                      sel, k, x_prev, h);
-        stage_block<IO, VEC>(geo, T, lds, 0, tid, nthreads, f0);
-        __builtin_amdgcn_sched_barrier(0);
-        fetch_block<IO, VEC>(geo, ro + 4 * geo.row_step, bo + 4 * geo.bc_step, tid, nthreads, f0);
-        ro += 2 * geo.row_step;
-        bo += 2 * geo.bc_step;
-    }
-    // One or two blocks remain; block j sits in slot 0 and f1 holds j+1.
+    // Block j is requested four blocks ahead, copied into LDS slot j % 3
+    // two blocks ahead, and its outputs leave LDS two blocks later.  Two
+    // fetch register sets alternate (the loop is unrolled by two).  The loop
+    // has a single exit at its bottom: an exit in the middle would route
+    // through the back-edge once the control flow is structured, and the
+    // load counters merged there would force a wait for every prefetch in
+    // flight.  Prefetches past the last block read zeros or unused rows and
+    // are never consumed.
+    const Duty du = make_duty<IO>(p, T, b, geo.d0, __builtin_amdgcn_readfirstlane(wave), lane);
+    Fetch<VEC> fa, fb;
+    fetch_block<IO, VEC>(geo, du, 0, tid, nthreads, fa);
+    fetch_block<IO, VEC>(geo, du, 1, tid, nthreads, fb);
+    stage_block<IO, VEC>(geo, du, T, lds, 0, tid, nthreads, fa);
+    fetch_block<IO, VEC>(geo, du, 2, tid, nthreads, fa);
+    stage_block<IO, VEC>(geo, du, T, lds, 1, tid, nthreads, fb);
+    fetch_block<IO, VEC>(geo, du, 3, tid, nthreads, fb);
     __syncthreads();
-    if (j > 0) store_block<IO, VEC>(geo, T, lds, 1, ro - geo.row_step, tid, nthreads);
-    compute_block<IO, CONV, FAST, true>(p, T, lds, 0, p.t_begin + j * kTB, wave, c, n, lane, sel, k,
-                                  x_prev, h);
+    read_own<IO>(T, lds, 0, n, ci, cy.own);
+    cy.u_prev = 0.0f;
+    cy.z_prev = 0.0f;
+
+    int s = 0;  // LDS slot of block j
+    int64_t j = 0;
+    auto advance = [&]() { s = s == kSlots - 1 ? 0 : s + 1; };
+    for (; j + 2 < nblocks; j += 2) {
+        block_iter<IO, CONV, VEC, FAST, false, 0, true>(p, geo, T, lds, wave, c, n, lane, sel, k,
+                                                        du, j, s, fa, cy);
+        advance();
+        block_iter<IO, CONV, VEC, FAST, false, 1, true>(p, geo, T, lds, wave, c, n, lane, sel, k,
+                                                        du, j + 1, s, fb, cy);
+        advance();
+    }
+    // One or two blocks remain (j is even).
+    int last_par;
     if (j + 1 < nblocks) {
-        stage_block<IO, VEC>(geo, T, lds, 1, tid, nthreads, f1);
-        __syncthreads();
-        store_block<IO, VEC>(geo, T, lds, 0, ro, tid, nthreads);
-        compute_block<IO, CONV, FAST, true>(p, T, lds, 1, p.t_begin + (j + 1) * kTB, wave, c, n, lane,
-                                      sel, k, x_prev, h);
-        __syncthreads();
-        store_block<IO, VEC>(geo, T, lds, 1, ro + geo.row_step, tid, nthreads);
+        block_iter<IO, CONV, VEC, FAST, false, 0, true>(p, geo, T, lds, wave, c, n, lane, sel, k,
+                                                        du, j, s, fa, cy);
+        advance();
+        block_iter<IO, CONV, VEC, FAST, true, 1, false>(p, geo, T, lds, wave, c, n, lane, sel, k,
+                                                        du, j + 1, s, fb, cy);
+        last_par = 1;
     } else {
-        __syncthreads();
-        store_block<IO, VEC>(geo, T, lds, 0, ro, tid, nthreads);
+        block_iter<IO, CONV, VEC, FAST, true, 0, false>(p, geo, T, lds, wave, c, n, lane, sel, k,
+                                                        du, j, s, fa, cy);
+        last_par = 0;
+    }
+    // Outputs of the last block and of the one before it.
+    constexpr int es = sizeof(typename IO::storage);
+    const int64_t jl = nblocks - 1;
+    __syncthreads();  // every wave has read ybuf[last_par] for its store
+    {
+        const float *prow = reinterpret_cast<const float *>(lds + T.part) + (wave * kChPerWave + c) * kPRow;
+        float yv = readout<FAST>(prow, prow + kRow * kPStride, n) + k.dsk * cy.u_prev;
+        if (p.z) yv *= silu(cy.z_prev);
+        char *ydst = lds + T.ybuf + last_par * T.ybuf_slot + n * T.rs + ci * es;
+        if constexpr (es == 2)
+            *reinterpret_cast<uint16_t *>(ydst) = __builtin_bit_cast(uint16_t, (__bf16)yv);
+        else
+            *reinterpret_cast<float *>(ydst) = yv;
+    }
+    __syncthreads();
+    if (!VEC || du.ystore) {
+        const YChunk<VEC> y1 = read_ybuf<IO, VEC>(du, T, lds, 1 - last_par, tid);
+        const YChunk<VEC> y0 = read_ybuf<IO, VEC>(du, T, lds, last_par, tid);
+        if (jl >= 1) store_y<IO, VEC>(p, geo, du, y1, jl - 1, tid);
+        store_y<IO, VEC>(p, geo, du, y0, jl, tid);
     }
 }
 
@@ -583,7 +750,7 @@ __device__ __forceinline__ void scan_tiles_body(const ScanKernelParams &p, const
 // layers) must fit 5 waves per SIMD (<= 96 VGPRs) so a 2.8B-like layer
 // (5120 waves) is resident at once; the others may use up to 128.
 template <typename IO, bool VEC>
-constexpr int kMinWavesPerEU = (VEC && std::is_same<IO, io_bf16>::value) ? 5 : 4;
+constexpr int kMinWavesPerEU = 4;
 
 template <typename IO, bool CONV, bool VEC>
 __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(kMinWavesPerEU<IO, VEC>, 8)))
@@ -626,7 +793,6 @@ void scan_tiles_kernel(ScanKernelParams p) {
     k.a = live ? p.A[d * N + n] : 0.0f;
     k.a2 = k.a * kLog2e;
     k.ia = (k.a != 0.0f) ? 1.0f / k.a : 0.0f;
-    static_for<kRow>([&](auto J) { k.iar[decltype(J)::value] = row_bcast<decltype(J)::value>(k.ia); });
     k.dsk = (p.Dskip && dvalid) ? p.Dskip[d] : 0.0f;
     k.dbias = (p.dbias && dvalid) ? p.dbias[d] : 0.0f;
     k.wp0 = k.wp1 = k.wp2 = k.wp3 = k.cb = 0.0f;
@@ -640,25 +806,30 @@ void scan_tiles_kernel(ScanKernelParams p) {
         if (K >= 4) k.wp0 = w[K - 4];
         if (p.conv_b) k.cb = p.conv_b[d];
     }
-    float h = (live && p.h_in) ? p.h_in[(b * D + d) * N + n] : 0.0f;
+    {
+        float *prow = reinterpret_cast<float *>(lds + T.part) + (wave * kChPerWave + c) * kPRow;
+        prow[kRow * kPStride + n] = k.ia;
+    }
+    Carry cy;
+    cy.h = (live && p.h_in) ? p.h_in[(b * D + d) * N + n] : 0.0f;
     // Conv history entering the launch: x at rows t_begin - 16 + n (only the
     // last three lanes of a row are used).
-    float x_prev = 0.0f;
+    cy.x_prev = 0.0f;
     if (CONV && p.t_begin > 0 && dvalid && n >= kRow - 3) {
         const int64_t t = p.t_begin - kRow + n;
-        x_prev = t >= 0 ? load_io<IO>(p.x, (b * p.L + t) * D + d) : 0.0f;
+        cy.x_prev = t >= 0 ? load_io<IO>(p.x, (b * p.L + t) * D + d) : 0.0f;
     }
     // Wave-uniform choice of the update form (see the file comment).
     const bool fast = __all(!live || fabsf(k.a) >= kFastMinAbsA);
     if (fast) {
         // The fast form carries g = A h (the 1/A moves to the read-out).
-        h *= k.a;
-        scan_tiles_body<IO, CONV, VEC, true>(p, geo, T, lds, wave, c, n, k, h, x_prev);
-        h *= k.ia;
+        cy.h *= k.a;
+        scan_tiles_body<IO, CONV, VEC, true>(p, geo, T, lds, b, wave, c, n, k, cy);
+        cy.h *= k.ia;
     } else {
-        scan_tiles_body<IO, CONV, VEC, false>(p, geo, T, lds, wave, c, n, k, h, x_prev);
+        scan_tiles_body<IO, CONV, VEC, false>(p, geo, T, lds, b, wave, c, n, k, cy);
     }
-    if (p.h_out && live) p.h_out[(b * D + d) * N + n] = h;
+    if (p.h_out && live) p.h_out[(b * D + d) * N + n] = cy.h;
 }
 
 __global__ void copy_or_zero_kernel(const float *src, float *dst, int64_t n) {
@@ -667,13 +838,23 @@ __global__ void copy_or_zero_kernel(const float *src, float *dst, int64_t n) {
 }
 
 // Waves per workgroup: the workgroups should spread evenly over the 256 CUs
-// (each CU holds up to 20 waves of this kernel).  Among W = 1..16 pick the
-// one whose busiest CU carries the least work, preferring wider tiles.
-int choose_waves(int64_t batch, int64_t dim) {
+// (each CU holds up to 20 waves of this kernel).  Among the allowed W pick
+// the one whose busiest CU carries the least work, preferring wider tiles.
+// The wide path needs 3 ceil(W / cw) + 2 <= W waves for its load duties
+// (cw = channels per 16-byte chunk) and, for bf16, an even W so that every
+// workgroup's channel range starts on a 16-byte boundary.
+bool wide_w_ok(int W, int64_t es) {
+    const int cw = (int)(16 / es);
+    if (es == 2 && W % 2 != 0) return false;
+    return 3 * ((W + cw - 1) / cw) + 2 <= W;
+}
+
+int choose_waves(int64_t batch, int64_t dim, bool wide, int64_t es) {
     constexpr int64_t kCUs = 256, kMaxWavesPerCU = 20;
-    int best = 1;
+    int best = 0;
     double best_cost = 1e300;
-    for (int W = 1; W <= 16; ++W) {
+    for (int W = 1; W <= kMaxW; ++W) {
+        if (wide && !wide_w_ok(W, es)) continue;
         const int64_t per_row = (dim + 4 * W - 1) / (4 * W);
         const int64_t groups = per_row * batch;
         const int64_t per_cu = (groups + kCUs - 1) / kCUs;            // workgroups on the busiest CU
@@ -727,7 +908,13 @@ hipError_t launch_scan_fwd(const ssm_scan_args_t &a, hipStream_t stream) {
     p.N = (int)a.dstate;
     p.K = (int)a.conv_k;
     p.softplus = a.delta_softplus;
-    const int W = choose_waves(a.batch, a.dim);
+    const int64_t es = a.io_dtype == SSM_BF16 ? 2 : 4;
+    // Wide (16-byte chunk) staging needs whole chunks per row, N = 16 and
+    // 16-byte aligned tensors; otherwise elements are staged one by one.
+    auto al = [](const void *q) { return ((uintptr_t)q % 16) == 0; };
+    const bool vec = (a.dim % (16 / es) == 0) && a.dstate == kRow && al(a.x) && al(a.delta) &&
+                     al(a.y) && (!a.z || al(a.z)) && al(a.Bm) && al(a.Cm);
+    const int W = choose_waves(a.batch, a.dim, vec, es);
     p.groups_per_b = (a.dim + 4 * W - 1) / (4 * W);
     p.ngroups = p.groups_per_b * a.batch;
     p.x = a.x;
@@ -741,14 +928,9 @@ hipError_t launch_scan_fwd(const ssm_scan_args_t &a, hipStream_t stream) {
     p.conv_w = a.conv_w;
     p.conv_b = a.conv_b;
     p.y = a.y;
-    if (p.ngroups > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    const int64_t es = a.io_dtype == SSM_BF16 ? 2 : 4;
+    if (p.ngroups > 0x7fffffffLL || W == 0) return hipErrorInvalidConfiguration;
     const int64_t chunk = rows_per_launch(a);
     if (chunk < 2 * kTB || a.dim * es > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    // Wide (4-element) chunks need D % 4 == 0, N = 16 and aligned tensors.
-    auto al = [&](const void *q) { return ((uintptr_t)q % (4 * es)) == 0; };
-    const bool vec = (a.dim % 4 == 0) && a.dstate == kRow && al(a.x) && al(a.delta) && al(a.y) &&
-                     (!a.z || al(a.z)) && al(a.Bm) && al(a.Cm);
     float *carry = static_cast<float *>(a.workspace);
     hipError_t e = hipSuccess;
     for (int64_t t = 0; t < a.seqlen && e == hipSuccess; t += chunk) {
