@@ -80,6 +80,22 @@ struct ScanKernelParams {
     const float *h_in;  // state entering row t_begin, or NULL (= 0)
     void *y;
     float *h_out;       // state after row t_end - 1, or NULL
+    // Sequence segments (see launch_segmented): mode 0 scans [t_begin, t_end)
+    // as one piece; mode 1 scans every segment of seg_len rows from a zero
+    // state (the first from h_in) and records its end state, its sum of dt
+    // and its head length; mode 2 re-scans the heads of segments 1.. from
+    // their true entering states.
+    int mode, nseg;
+    int64_t seg_len;
+    float *ws_hend;        // [nseg][B][D][N]  end state of each segment (mode 1)
+    float *ws_stot;        // [nseg][B][D]     sum of dt over each segment (mode 1)
+    int *ws_head;          // [nseg][ngroups]  head blocks of each segment (mode 1 -> 2)
+    const float *ws_hin;   // [nseg][B][D][N]  state entering each segment (mode 2)
+};
+
+// Rows [t0, t1) a workgroup scans (its segment of the launch's rows).
+struct Span {
+    int64_t t0, t1;
 };
 
 template <int I>
@@ -236,7 +252,8 @@ __device__ __host__ __forceinline__ Tiles tile_layout(int W) {
 template <typename IO>
 __host__ __forceinline__ size_t tile_lds_bytes(int W) {
     const Tiles t = tile_layout<IO>(W);
-    return t.part + (size_t)W * kChPerWave * kPRow * sizeof(float);
+    // partials, then one int per wave for the head-length reduction
+    return t.part + (size_t)W * kChPerWave * kPRow * sizeof(float) + kMaxW * sizeof(int);
 }
 
 // Launch-wide addressing of one workgroup.
@@ -278,14 +295,14 @@ __device__ __forceinline__ int duty_waves(int W) {  // a
 }
 
 template <typename IO>
-__device__ __forceinline__ Duty make_duty(const ScanKernelParams &p, const Tiles &T, int64_t b,
-                                          int d0, int wave, int lane) {
+__device__ __forceinline__ Duty make_duty(const ScanKernelParams &p, const Span &sp,
+                                          const Tiles &T, int64_t b, int d0, int wave, int lane) {
     constexpr int es = sizeof(typename IO::storage);
     constexpr int cw = chunk_ch<IO>();
     const int W = T.CH / 4;
     const int a = duty_waves<IO>(W);
     const int per_row = T.CH / cw;  // chunks per staged row
-    const int64_t D = p.D, N = p.N, rows = p.t_end - p.t_begin;
+    const int64_t D = p.D, N = p.N, rows = sp.t1 - sp.t0;
     const int role = wave < 3 * a ? wave / a : 3 + (wave - 3 * a);  // uniform
     Duty d;
     d.to_bc = role == 3 || role == 4;
@@ -295,7 +312,7 @@ __device__ __forceinline__ Duty make_duty(const ScanKernelParams &p, const Tiles
     d.ylds = 0;
     if (role < 3) {
         const void *src = role == 0 ? p.x : role == 1 ? p.delta : p.z;
-        const int64_t base = (b * p.L + p.t_begin) * D * es;
+        const int64_t base = (b * p.L + sp.t0) * D * es;
         d.gbase = static_cast<const char *>(src ? src : p.x) + base;
         d.grec = src ? rows * D * es : 0;  // no gate: every z read gives 0
         d.step = (uint32_t)(kTB * D * es);
@@ -309,7 +326,7 @@ __device__ __forceinline__ Duty make_duty(const ScanKernelParams &p, const Tiles
         }
     } else {
         const void *src = role == 3 ? p.Bm : p.Cm;
-        const int64_t base = (b * p.L + p.t_begin) * N * es;
+        const int64_t base = (b * p.L + sp.t0) * N * es;
         d.gbase = static_cast<const char *>(src) + base;
         d.grec = role <= 4 ? rows * N * es : 0;
         d.step = (uint32_t)(kTB * N * es);
@@ -489,6 +506,7 @@ __device__ __forceinline__ mfma_f32x4 bcast(typename BcOperand<IO>::type op, con
 
 struct LaneConst {
     float a, a2, ia, dsk, dbias, cb, wp0, wp1, wp2, wp3;
+    bool live;  // the lane holds a real (channel, entry)
 };
 
 // Read-out of one step: the sum over the 16 state entries of the partials
@@ -532,7 +550,23 @@ struct Carry {
     float u_prev, z_prev;  // u and z of this lane's step in the previous block
     float x_prev;          // conv history: x of the previous block (lanes 13..15 used)
     float h;               // state (A h in the fast form)
+    float scum;            // segment pass: sum of dt of the channel so far
+    int head;              // segment pass: blocks until the entering state is forgotten, or -1
 };
+
+// Sum over the 16 lanes of a row (every lane gets it): four rotations.
+__device__ __forceinline__ float row_sum(float v) {
+    v += __builtin_amdgcn_update_dpp(0.0f, v, 0x128, 0xf, 0xf, false);  // row_ror:8
+    v += __builtin_amdgcn_update_dpp(0.0f, v, 0x124, 0xf, 0xf, false);  // row_ror:4
+    v += __builtin_amdgcn_update_dpp(0.0f, v, 0x122, 0xf, 0xf, false);  // row_ror:2
+    v += __builtin_amdgcn_update_dpp(0.0f, v, 0x121, 0xf, 0xf, false);  // row_ror:1
+    return v;
+}
+
+// exp2 of anything below this is exactly 0 in fp32: once A log2(e) sum(dt)
+// is below it for every state entry, the state a segment started from no
+// longer reaches its outputs.
+constexpr float kForgetExp2 = -160.0f;
 
 template <typename IO>
 __device__ __forceinline__ void read_own(const Tiles &T, const char *lds, int slot, int n, int ci,
@@ -558,8 +592,8 @@ __device__ __forceinline__ void read_own(const Tiles &T, const char *lds, int sl
 //     requested from global memory.
 // PAR = j % 2 selects the ybuf halves; TAIL masks steps past the sequence
 // end; STAGE is off in the last block.
-template <typename IO, bool CONV, bool VEC, bool FAST, bool TAIL, int PAR, bool STAGE>
-__device__ __forceinline__ void block_iter(const ScanKernelParams &p, const Geo &geo,
+template <typename IO, bool CONV, bool VEC, bool FAST, bool STATS, bool TAIL, int PAR, bool STAGE>
+__device__ __forceinline__ void block_iter(const ScanKernelParams &p, const Span &sp, const Geo &geo,
                                            const Tiles &T, char *lds, int wave, int c, int n,
                                            int lane, const BcastSel &sel, const LaneConst &k,
                                            const Duty &du, int64_t j, int s_cur, Fetch<VEC> &f,
@@ -599,9 +633,14 @@ __device__ __forceinline__ void block_iter(const ScanKernelParams &p, const Geo 
         cy.x_prev = xv;
     }
     if (p.softplus) dt = softplus_fast(dt + k.dbias);
-    if (TAIL && p.t_begin + j * kTB + n >= p.t_end) {  // past the end: the state must not move
+    if (TAIL && sp.t0 + j * kTB + n >= sp.t1) {  // past the end: the state must not move
         dt = 0.0f;
         u = 0.0f;
+    }
+    if constexpr (STATS) {
+        // Decay of the entering state through this block: exp(A sum(dt)).
+        cy.scum += row_sum(dt);
+        if (cy.head < 0 && __all(!k.live || k.a2 * cy.scum < kForgetExp2)) cy.head = (int)j + 1;
     }
 
     // -- outputs of block j-1 (lane (c, n) finishes its step n) ---------------
@@ -664,15 +703,15 @@ __device__ __forceinline__ void block_iter(const ScanKernelParams &p, const Geo 
     }
 }
 
-template <typename IO, bool CONV, bool VEC, bool FAST>
-__device__ __forceinline__ void scan_tiles_body(const ScanKernelParams &p, const Geo &geo,
+template <typename IO, bool CONV, bool VEC, bool FAST, bool STATS>
+__device__ __forceinline__ void scan_tiles_body(const ScanKernelParams &p, const Span &sp, const Geo &geo,
                                                 const Tiles &T, char *lds, int64_t b, int wave,
                                                 int c, int n, const LaneConst &k, Carry &cy) {
     const int tid = threadIdx.x, nthreads = blockDim.x;
     const int lane = tid & 63;
     const int ci = 4 * wave + c;
     const BcastSel sel = make_sel(lane);
-    const int64_t rows = p.t_end - p.t_begin;
+    const int64_t rows = sp.t1 - sp.t0;
     const int64_t nblocks = (rows + kTB - 1) / kTB;
 
     // Block j is requested four blocks ahead, copied into LDS slot j % 3
@@ -683,7 +722,7 @@ __device__ __forceinline__ void scan_tiles_body(const ScanKernelParams &p, const
     // load counters merged there would force a wait for every prefetch in
     // flight.  Prefetches past the last block read zeros or unused rows and
     // are never consumed.
-    const Duty du = make_duty<IO>(p, T, b, geo.d0, __builtin_amdgcn_readfirstlane(wave), lane);
+    const Duty du = make_duty<IO>(p, sp, T, b, geo.d0, __builtin_amdgcn_readfirstlane(wave), lane);
     Fetch<VEC> fa, fb;
     fetch_block<IO, VEC>(geo, du, 0, tid, nthreads, fa);
     fetch_block<IO, VEC>(geo, du, 1, tid, nthreads, fb);
@@ -700,24 +739,24 @@ __device__ __forceinline__ void scan_tiles_body(const ScanKernelParams &p, const
     int64_t j = 0;
     auto advance = [&]() { s = s == kSlots - 1 ? 0 : s + 1; };
     for (; j + 2 < nblocks; j += 2) {
-        block_iter<IO, CONV, VEC, FAST, false, 0, true>(p, geo, T, lds, wave, c, n, lane, sel, k,
+        block_iter<IO, CONV, VEC, FAST, STATS, false, 0, true>(p, sp, geo, T, lds, wave, c, n, lane, sel, k,
                                                         du, j, s, fa, cy);
         advance();
-        block_iter<IO, CONV, VEC, FAST, false, 1, true>(p, geo, T, lds, wave, c, n, lane, sel, k,
+        block_iter<IO, CONV, VEC, FAST, STATS, false, 1, true>(p, sp, geo, T, lds, wave, c, n, lane, sel, k,
                                                         du, j + 1, s, fb, cy);
         advance();
     }
     // One or two blocks remain (j is even).
     int last_par;
     if (j + 1 < nblocks) {
-        block_iter<IO, CONV, VEC, FAST, false, 0, true>(p, geo, T, lds, wave, c, n, lane, sel, k,
+        block_iter<IO, CONV, VEC, FAST, STATS, false, 0, true>(p, sp, geo, T, lds, wave, c, n, lane, sel, k,
                                                         du, j, s, fa, cy);
         advance();
-        block_iter<IO, CONV, VEC, FAST, true, 1, false>(p, geo, T, lds, wave, c, n, lane, sel, k,
+        block_iter<IO, CONV, VEC, FAST, STATS, true, 1, false>(p, sp, geo, T, lds, wave, c, n, lane, sel, k,
                                                         du, j + 1, s, fb, cy);
         last_par = 1;
     } else {
-        block_iter<IO, CONV, VEC, FAST, true, 0, false>(p, geo, T, lds, wave, c, n, lane, sel, k,
+        block_iter<IO, CONV, VEC, FAST, STATS, true, 0, false>(p, sp, geo, T, lds, wave, c, n, lane, sel, k,
                                                         du, j, s, fa, cy);
         last_par = 0;
     }
@@ -752,7 +791,7 @@ __device__ __forceinline__ void scan_tiles_body(const ScanKernelParams &p, const
 template <typename IO, bool VEC>
 constexpr int kMinWavesPerEU = 4;
 
-template <typename IO, bool CONV, bool VEC>
+template <typename IO, bool CONV, bool VEC, bool STATS>
 __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(kMinWavesPerEU<IO, VEC>, 8)))
 void scan_tiles_kernel(ScanKernelParams p) {
     extern __shared__ __attribute__((aligned(16))) char lds[];
@@ -761,25 +800,47 @@ void scan_tiles_kernel(ScanKernelParams p) {
     const int wave = threadIdx.x / 64;
     const int lane = threadIdx.x & 63;
     const int c = lane / kRow, n = lane % kRow;
-    const int64_t grp = xcd_group(blockIdx.x, gridDim.x);
+    const int64_t gid = xcd_group(blockIdx.x, gridDim.x);
+    const int64_t grp = gid % p.ngroups;
     const int64_t b = grp / p.groups_per_b;
     const int d0 = (int)((grp % p.groups_per_b) * 4 * W);
     const int64_t d = d0 + 4 * wave + c;
     const bool dvalid = d < p.D;
     const bool live = dvalid && n < p.N;
     const int64_t D = p.D, N = p.N;
-    const int64_t rows = p.t_end - p.t_begin;
+    const int64_t BDN = p.B * D * N;
+
+    // This workgroup's rows and states (segments shift them; all uniform).
+    Span sp{p.t_begin, p.t_end};
+    const float *h_in = p.h_in;
+    float *h_out = p.h_out;
+    int64_t seg = 0;
+    if (p.mode != 0) {
+        seg = gid / p.ngroups + (p.mode == 2 ? 1 : 0);
+        sp.t0 = p.t_begin + seg * p.seg_len;
+        sp.t1 = std::min(p.t_end, sp.t0 + p.seg_len);
+        if (p.mode == 1) {
+            h_in = seg == 0 ? p.h_in : nullptr;
+            h_out = p.ws_hend + seg * BDN;
+        } else {
+            const int head = p.ws_head[seg * p.ngroups + grp];
+            sp.t1 = std::min(sp.t1, sp.t0 + (int64_t)head * kTB);
+            h_in = p.ws_hin + seg * BDN;
+            h_out = nullptr;
+        }
+    }
+    const int64_t rows = sp.t1 - sp.t0;
     const Tiles T = tile_layout<IO>(W);
 
     Geo geo;
-    const int64_t xbase = (b * p.L + p.t_begin) * D * es;
+    const int64_t xbase = (b * p.L + sp.t0) * D * es;
     const int64_t xrec = rows * D * es;
     geo.rx = rsrc(p.x, xbase, xrec);
     geo.rdt = rsrc(p.delta, xbase, xrec);
     // Without a gate the descriptor has no records: loads return 0.
     geo.rz = p.z ? rsrc(p.z, xbase, xrec) : rsrc(p.x, 0, 0);
     geo.ry = rsrc(p.y, xbase, xrec);
-    const int64_t bbase = (b * p.L + p.t_begin) * N * es;
+    const int64_t bbase = (b * p.L + sp.t0) * N * es;
     geo.rb = rsrc(p.Bm, bbase, rows * N * es);
     geo.rc = rsrc(p.Cm, bbase, rows * N * es);
     geo.row_step = (uint32_t)(kTB * D * es);
@@ -790,6 +851,7 @@ void scan_tiles_kernel(ScanKernelParams p) {
     geo.d0 = d0;
 
     LaneConst k;
+    k.live = live;
     k.a = live ? p.A[d * N + n] : 0.0f;
     k.a2 = k.a * kLog2e;
     k.ia = (k.a != 0.0f) ? 1.0f / k.a : 0.0f;
@@ -811,25 +873,64 @@ void scan_tiles_kernel(ScanKernelParams p) {
         prow[kRow * kPStride + n] = k.ia;
     }
     Carry cy;
-    cy.h = (live && p.h_in) ? p.h_in[(b * D + d) * N + n] : 0.0f;
-    // Conv history entering the launch: x at rows t_begin - 16 + n (only the
+    cy.h = (live && h_in) ? h_in[(b * D + d) * N + n] : 0.0f;
+    cy.scum = 0.0f;
+    cy.head = -1;
+    // Conv history entering the rows: x at rows t_begin - 16 + n (only the
     // last three lanes of a row are used).
     cy.x_prev = 0.0f;
-    if (CONV && p.t_begin > 0 && dvalid && n >= kRow - 3) {
-        const int64_t t = p.t_begin - kRow + n;
+    if (CONV && sp.t0 > 0 && dvalid && n >= kRow - 3) {
+        const int64_t t = sp.t0 - kRow + n;
         cy.x_prev = t >= 0 ? load_io<IO>(p.x, (b * p.L + t) * D + d) : 0.0f;
     }
     // Wave-uniform choice of the update form (see the file comment).
     const bool fast = __all(!live || fabsf(k.a) >= kFastMinAbsA);
-    if (fast) {
-        // The fast form carries g = A h (the 1/A moves to the read-out).
-        cy.h *= k.a;
-        scan_tiles_body<IO, CONV, VEC, true>(p, geo, T, lds, b, wave, c, n, k, cy);
-        cy.h *= k.ia;
-    } else {
-        scan_tiles_body<IO, CONV, VEC, false>(p, geo, T, lds, b, wave, c, n, k, cy);
+    if (rows > 0) {
+        if (fast) {
+            // The fast form carries g = A h (the 1/A moves to the read-out).
+            cy.h *= k.a;
+            scan_tiles_body<IO, CONV, VEC, true, STATS>(p, sp, geo, T, lds, b, wave, c, n, k, cy);
+            cy.h *= k.ia;
+        } else {
+            scan_tiles_body<IO, CONV, VEC, false, STATS>(p, sp, geo, T, lds, b, wave, c, n, k, cy);
+        }
     }
-    if (p.h_out && live) p.h_out[(b * D + d) * N + n] = cy.h;
+    if (h_out && live) h_out[(b * D + d) * N + n] = cy.h;
+    if constexpr (STATS) {
+        // Sum of dt per channel, and the workgroup's head length: the most
+        // blocks any of its waves needs before the entering state is gone.
+        if (dvalid && n == 0) p.ws_stot[(seg * p.B + b) * D + d] = cy.scum;
+        const int nblk = (int)((rows + kTB - 1) / kTB);
+        int *kred = reinterpret_cast<int *>(lds + T.part + (size_t)W * kChPerWave * kPRow * sizeof(float));
+        __syncthreads();
+        if (lane == 0) kred[wave] = cy.head < 0 ? nblk : cy.head;
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            int m = 0;
+            for (int w = 0; w < W; ++w) m = std::max(m, kred[w]);
+            p.ws_head[seg * p.ngroups + grp] = m;
+        }
+    }
+}
+
+// State entering every segment and after the last one: segment 0 ran from
+// the true state; segment s > 0 from zero, so its true end state is
+// exp(A sum(dt)) times its entering state plus its local end state.
+__global__ void seg_combine_kernel(const float *A, const float *hend, const float *stot,
+                                   float *hin, float *h_final, int64_t B, int64_t D, int N,
+                                   int nseg) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t BDN = B * D * N;
+    if (i >= BDN) return;
+    const int64_t bd = i / N;
+    const int64_t d = bd % D;
+    const float a2 = A[d * N + i % N] * kLog2e;
+    float h = hend[i];
+    for (int s = 1; s < nseg; ++s) {
+        hin[s * BDN + i] = h;
+        h = __builtin_amdgcn_exp2f(a2 * stot[s * B * D + bd]) * h + hend[s * BDN + i];
+    }
+    if (h_final) h_final[i] = h;
 }
 
 __global__ void copy_or_zero_kernel(const float *src, float *dst, int64_t n) {
@@ -872,12 +973,20 @@ int choose_waves(int64_t batch, int64_t dim, bool wide, int64_t es) {
 
 template <typename IO, bool VEC>
 hipError_t launch_typed(const ScanKernelParams &p, int W, hipStream_t stream) {
-    const unsigned grid = (unsigned)p.ngroups;
+    const int64_t copies = p.mode == 0 ? 1 : p.mode == 1 ? p.nseg : p.nseg - 1;
+    const unsigned grid = (unsigned)(p.ngroups * copies);
     const size_t lds = tile_lds_bytes<IO>(W);
-    if (p.K > 0)
-        scan_tiles_kernel<IO, true, VEC><<<grid, 64 * W, lds, stream>>>(p);
-    else
-        scan_tiles_kernel<IO, false, VEC><<<grid, 64 * W, lds, stream>>>(p);
+    if (p.mode == 1) {
+        if (p.K > 0)
+            scan_tiles_kernel<IO, true, VEC, true><<<grid, 64 * W, lds, stream>>>(p);
+        else
+            scan_tiles_kernel<IO, false, VEC, true><<<grid, 64 * W, lds, stream>>>(p);
+    } else {
+        if (p.K > 0)
+            scan_tiles_kernel<IO, true, VEC, false><<<grid, 64 * W, lds, stream>>>(p);
+        else
+            scan_tiles_kernel<IO, false, VEC, false><<<grid, 64 * W, lds, stream>>>(p);
+    }
     return hipGetLastError();
 }
 
@@ -891,16 +1000,83 @@ int64_t rows_per_launch(const ssm_scan_args_t &a) {
     return r;
 }
 
+// Sequence segments.  With few (batch, channel) pairs the scan alone cannot
+// fill the GPU (one wave per 4 channels); a long sequence is then cut into
+// S segments scanned at the same time:
+//   1. every segment is scanned from a zero state (the first from the true
+//      one), writing y, its end state, its sum of dt and the number of
+//      blocks after which exp(A sum(dt)) is exactly 0 in fp32 for all its
+//      state entries (its "head");
+//   2. the true entering states follow in one pass over the segments:
+//      h_in(s+1) = exp(A sum_s(dt)) h_in(s) + h_end(s);
+//   3. the heads of segments 1.. are scanned again from their true entering
+//      states, overwriting y there.  Past the head the zero-start outputs
+//      already are the true ones: the entering state's share has decayed to 0.
+// The extra work is the heads (short when A dt is not tiny; a whole segment
+// when some A is 0).
+constexpr int64_t kMinSegRows = 2048;
+constexpr int64_t kMaxSegs = 64;
+constexpr int64_t kWaveTarget = 4096;  // about 4 waves per SIMD
+
+struct Plan {
+    int W, nseg;
+    int64_t chunk, seg_len, groups_per_b, ngroups;
+    bool vec;
+    size_t ws_carry, ws_hend, ws_hin, ws_stot, ws_head, total;
+};
+
+size_t round256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+Plan make_plan(const ssm_scan_args_t &a) {
+    Plan q;
+    const int64_t es = a.io_dtype == SSM_BF16 ? 2 : 4;
+    // Wide (16-byte chunk) staging needs whole chunks per row, N = 16 and
+    // 16-byte aligned tensors; otherwise elements are staged one by one.
+    auto al = [](const void *v) { return ((uintptr_t)v % 16) == 0; };
+    q.vec = (a.dim % (16 / es) == 0) && a.dstate == kRow && al(a.x) && al(a.delta) &&
+            al(a.y) && (!a.z || al(a.z)) && al(a.Bm) && al(a.Cm);
+    q.chunk = rows_per_launch(a);
+    const int64_t rows = std::min(a.seqlen, q.chunk);  // rows of the longest launch
+    const int64_t waves = a.batch * ((a.dim + 3) / 4);
+    int64_t S = 1;
+    if (waves * 2 < kWaveTarget)
+        S = std::max<int64_t>(1, std::min({kMaxSegs, kWaveTarget / std::max<int64_t>(waves, 1),
+                                           rows / kMinSegRows}));
+    q.nseg = (int)S;
+    q.seg_len = S > 1 ? ((rows + S - 1) / S + kTB - 1) / kTB * kTB : rows;
+    q.W = choose_waves(a.batch * S, a.dim, q.vec, es);
+    q.groups_per_b = q.W ? (a.dim + 4 * q.W - 1) / (4 * q.W) : 0;
+    q.ngroups = q.groups_per_b * a.batch;
+    const size_t bdn = (size_t)(a.batch * a.dim * a.dstate) * sizeof(float);
+    q.ws_carry = a.seqlen > q.chunk ? round256(bdn) : 0;
+    q.ws_hend = S > 1 ? round256(bdn * S) : 0;
+    q.ws_hin = S > 1 ? round256(bdn * S) : 0;
+    q.ws_stot = S > 1 ? round256((size_t)(a.batch * a.dim) * sizeof(float) * S) : 0;
+    q.ws_head = S > 1 ? round256((size_t)q.ngroups * sizeof(int) * S) : 0;
+    q.total = q.ws_carry + q.ws_hend + q.ws_hin + q.ws_stot + q.ws_head;
+    return q;
+}
+
+hipError_t launch_pass(const ssm_scan_args_t &a, const ScanKernelParams &p, const Plan &q,
+                       hipStream_t stream) {
+    if (a.io_dtype == SSM_BF16)
+        return q.vec ? launch_typed<io_bf16, true>(p, q.W, stream) : launch_typed<io_bf16, false>(p, q.W, stream);
+    return q.vec ? launch_typed<io_f32, true>(p, q.W, stream) : launch_typed<io_f32, false>(p, q.W, stream);
+}
+
 }  // namespace
 
 size_t scan_workspace_bytes(const ssm_scan_args_t &a) {
     // A sequence too long for one launch is split; the state between the
-    // launches lives in the workspace.
-    if (a.seqlen <= rows_per_launch(a)) return 0;
-    return (size_t)(a.batch * a.dim * a.dstate) * sizeof(float);
+    // launches lives in the workspace, and so do the segment records.
+    return make_plan(a).total;
 }
 
 hipError_t launch_scan_fwd(const ssm_scan_args_t &a, hipStream_t stream) {
+    const Plan q = make_plan(a);
+    const int64_t es = a.io_dtype == SSM_BF16 ? 2 : 4;
+    if (q.W == 0 || q.ngroups * q.nseg > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    if (q.chunk < 2 * kTB || a.dim * es > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     ScanKernelParams p;
     p.B = a.batch;
     p.L = a.seqlen;
@@ -908,15 +1084,8 @@ hipError_t launch_scan_fwd(const ssm_scan_args_t &a, hipStream_t stream) {
     p.N = (int)a.dstate;
     p.K = (int)a.conv_k;
     p.softplus = a.delta_softplus;
-    const int64_t es = a.io_dtype == SSM_BF16 ? 2 : 4;
-    // Wide (16-byte chunk) staging needs whole chunks per row, N = 16 and
-    // 16-byte aligned tensors; otherwise elements are staged one by one.
-    auto al = [](const void *q) { return ((uintptr_t)q % 16) == 0; };
-    const bool vec = (a.dim % (16 / es) == 0) && a.dstate == kRow && al(a.x) && al(a.delta) &&
-                     al(a.y) && (!a.z || al(a.z)) && al(a.Bm) && al(a.Cm);
-    const int W = choose_waves(a.batch, a.dim, vec, es);
-    p.groups_per_b = (a.dim + 4 * W - 1) / (4 * W);
-    p.ngroups = p.groups_per_b * a.batch;
+    p.groups_per_b = q.groups_per_b;
+    p.ngroups = q.ngroups;
     p.x = a.x;
     p.delta = a.delta;
     p.Bm = a.Bm;
@@ -928,21 +1097,41 @@ hipError_t launch_scan_fwd(const ssm_scan_args_t &a, hipStream_t stream) {
     p.conv_w = a.conv_w;
     p.conv_b = a.conv_b;
     p.y = a.y;
-    if (p.ngroups > 0x7fffffffLL || W == 0) return hipErrorInvalidConfiguration;
-    const int64_t chunk = rows_per_launch(a);
-    if (chunk < 2 * kTB || a.dim * es > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    float *carry = static_cast<float *>(a.workspace);
+    p.mode = 0;
+    p.nseg = 1;
+    p.seg_len = q.seg_len;
+    char *ws = static_cast<char *>(a.workspace);
+    float *carry = reinterpret_cast<float *>(ws);
+    p.ws_hend = reinterpret_cast<float *>(ws + q.ws_carry);
+    float *hin = reinterpret_cast<float *>(ws + q.ws_carry + q.ws_hend);
+    p.ws_hin = hin;
+    p.ws_stot = reinterpret_cast<float *>(ws + q.ws_carry + q.ws_hend + q.ws_hin);
+    p.ws_head = reinterpret_cast<int *>(ws + q.ws_carry + q.ws_hend + q.ws_hin + q.ws_stot);
     hipError_t e = hipSuccess;
-    for (int64_t t = 0; t < a.seqlen && e == hipSuccess; t += chunk) {
-        const bool first = t == 0, last = t + chunk >= a.seqlen;
+    for (int64_t t = 0; t < a.seqlen && e == hipSuccess; t += q.chunk) {
+        const bool first = t == 0, last = t + q.chunk >= a.seqlen;
         p.t_begin = t;
-        p.t_end = last ? a.seqlen : t + chunk;
+        p.t_end = last ? a.seqlen : t + q.chunk;
         p.h_in = first ? a.h0 : carry;
         p.h_out = last ? a.h_final : carry;
-        if (a.io_dtype == SSM_BF16)
-            e = vec ? launch_typed<io_bf16, true>(p, W, stream) : launch_typed<io_bf16, false>(p, W, stream);
-        else
-            e = vec ? launch_typed<io_f32, true>(p, W, stream) : launch_typed<io_f32, false>(p, W, stream);
+        const int64_t nseg = q.nseg > 1 ? (p.t_end - p.t_begin + q.seg_len - 1) / q.seg_len : 1;
+        if (nseg <= 1) {
+            p.mode = 0;
+            p.nseg = 1;
+            e = launch_pass(a, p, q, stream);
+            continue;
+        }
+        p.nseg = (int)nseg;
+        p.mode = 1;
+        e = launch_pass(a, p, q, stream);
+        if (e != hipSuccess) break;
+        const int64_t bdn = a.batch * a.dim * a.dstate;
+        seg_combine_kernel<<<(unsigned)((bdn + 255) / 256), 256, 0, stream>>>(
+            a.A, p.ws_hend, p.ws_stot, hin, p.h_out, a.batch, a.dim, (int)a.dstate, p.nseg);
+        e = hipGetLastError();
+        if (e != hipSuccess) break;
+        p.mode = 2;
+        e = launch_pass(a, p, q, stream);
     }
     return e;
 }

@@ -7,10 +7,18 @@
 // between tokens ("2. Mamba 상세": ssm_state):
 //   state[b,d,n] <- exp(dt A) state + Bbar x;   y = (sum_n C state + D x) silu(z)
 //
-// HBM-bound: the fp32 state is read and written once.  Four lanes share one
-// channel, each holding four consecutive state entries, so a wave streams 16
-// channels x 64 bytes of state contiguously; the four partial read-outs are
-// summed with two cross-lane butterflies.
+// HBM-bound: the fp32 state is read and written once; everything else is
+// small (x, delta, z, y per channel; B, C per batch row; A and D per channel,
+// shared by all batch rows and so served from the caches).  Four lanes share
+// one channel, each holding four consecutive state entries, so a wave moves
+// 16 channels x 64 bytes of state with one 16-byte access per lane.  Each
+// thread handles four such quarters (a grid-size stride apart) and issues all
+// their loads before any arithmetic, to keep enough bytes in flight.  The
+// four partial read-outs of a channel are summed with two DPP quad swaps.
+//
+// Bbar x = dt phi(dt A) B x with phi(z) = (e^z - 1) / z, evaluated as a
+// degree-6 series for |z| < 1/4 (no cancellation, and phi(0) = 1 covers
+// A = 0) and as (e^z - 1) / z otherwise.
 #include "ssm_device.h"
 #include "ssm_internal.h"
 
@@ -19,6 +27,7 @@ namespace {
 
 constexpr int kLanesPerChannel = 4;
 constexpr int kPerLane = SSM_MAX_DSTATE / kLanesPerChannel;  // 4 state entries per lane
+constexpr int kQuartersPerThread = 4;
 
 struct UpdateParams {
     int64_t B, D;
@@ -29,7 +38,93 @@ struct UpdateParams {
     void *y;
 };
 
-template <typename IO, bool VEC>
+// phi(z) = (e^z - 1) / z given e = e^z.
+__device__ __forceinline__ float phi_of(float z, float e) {
+    const float s = 1.0f + z * (0.5f + z * (1.0f / 6.0f + z * (1.0f / 24.0f +
+                    z * (1.0f / 120.0f + z * (1.0f / 720.0f + z * (1.0f / 5040.0f))))));
+    const float big = (e - 1.0f) * hw_rcp(z);
+    return fabsf(z) < 0.25f ? s : big;
+}
+
+// Four consecutive I/O elements as fp32.
+template <typename IO>
+__device__ __forceinline__ float4 load4_io(const void *p, int64_t i);
+template <>
+__device__ __forceinline__ float4 load4_io<io_f32>(const void *p, int64_t i) {
+    return *reinterpret_cast<const float4 *>(static_cast<const float *>(p) + i);
+}
+template <>
+__device__ __forceinline__ float4 load4_io<io_bf16>(const void *p, int64_t i) {
+    const uint2 v = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(p) + i);
+    return make_float4(__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xFFFF0000u),
+                       __uint_as_float(v.y << 16), __uint_as_float(v.y & 0xFFFF0000u));
+}
+
+__device__ __forceinline__ float quad_sum(float v) {
+    v += __builtin_amdgcn_update_dpp(0.0f, v, 0xB1, 0xf, 0xf, false);  // quad_perm [1,0,3,2]
+    v += __builtin_amdgcn_update_dpp(0.0f, v, 0x4E, 0xf, 0xf, false);  // quad_perm [2,3,0,1]
+    return v;
+}
+
+// N = 16 with 16-byte aligned state, A, B and C: quarter q of the
+// (B*D*4) quarters is entries 4(q%4)..+3 of channel q/4.
+template <typename IO>
+__global__ __launch_bounds__(256) void state_update_vec_kernel(UpdateParams p, int64_t nq) {
+    constexpr int K = kQuartersPerThread;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    const int64_t q0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    float4 st[K], av[K], bv[K], cv[K];
+    float xv[K], dv[K], zv[K], dsk[K];
+    // All loads first.
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        const int64_t q = q0 + k * stride;
+        const int64_t qc = q < nq ? q : 0;
+        const int64_t ch = qc >> 2;
+        const int j = (int)(qc & 3);
+        // 32-bit division when the channel count allows it (always in practice).
+        const int64_t b = p.B * p.D <= 0xFFFFFFFFLL ? (int64_t)((uint32_t)ch / (uint32_t)p.D) : ch / p.D;
+        const int64_t d = ch - b * p.D;
+        st[k] = *reinterpret_cast<const float4 *>(p.state + ch * SSM_MAX_DSTATE + 4 * j);
+        av[k] = *reinterpret_cast<const float4 *>(p.A + d * SSM_MAX_DSTATE + 4 * j);
+        bv[k] = load4_io<IO>(p.Bm, b * SSM_MAX_DSTATE + 4 * j);
+        cv[k] = load4_io<IO>(p.Cm, b * SSM_MAX_DSTATE + 4 * j);
+        xv[k] = load_io<IO>(p.x, ch);
+        dv[k] = load_io<IO>(p.delta, ch);
+        zv[k] = p.z ? load_io<IO>(p.z, ch) : 0.0f;
+        dsk[k] = p.Dskip ? p.Dskip[d] : 0.0f;
+        if (p.softplus) dv[k] = softplus(dv[k] + (p.dbias ? p.dbias[d] : 0.0f));
+    }
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        const int64_t q = q0 + k * stride;
+        const float dt = dv[k], u = xv[k];
+        const float a[4] = {av[k].x, av[k].y, av[k].z, av[k].w};
+        const float bb[4] = {bv[k].x, bv[k].y, bv[k].z, bv[k].w};
+        const float cc[4] = {cv[k].x, cv[k].y, cv[k].z, cv[k].w};
+        float h[4] = {st[k].x, st[k].y, st[k].z, st[k].w};
+        float acc = 0.0f;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const float zz = dt * a[r];
+            const float e = hw_exp2(zz * kLog2e);
+            h[r] = e * h[r] + (dt * phi_of(zz, e)) * (bb[r] * u);
+            acc += cc[r] * h[r];
+        }
+        if (q < nq)
+            *reinterpret_cast<float4 *>(p.state + (q >> 2) * SSM_MAX_DSTATE + 4 * (q & 3)) =
+                make_float4(h[0], h[1], h[2], h[3]);
+        acc = quad_sum(acc);
+        if (q < nq && (q & 3) == 0) {
+            float yv = acc + dsk[k] * u;
+            if (p.z) yv *= silu(zv[k]);
+            store_io<IO>(p.y, q >> 2, yv);
+        }
+    }
+}
+
+// Any N <= 16 and any alignment: one quarter per thread, element loads.
+template <typename IO>
 __global__ __launch_bounds__(256) void state_update_kernel(UpdateParams p) {
     const int64_t gtid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int64_t ch = gtid / kLanesPerChannel;  // b * D + d
@@ -45,40 +140,29 @@ __global__ __launch_bounds__(256) void state_update_kernel(UpdateParams p) {
     const float u = load_io<IO>(p.x, chc);
 
     float hs[kPerLane];
-    float* sp = p.state + chc * N + n0;
-    if (VEC) {
-        const float4 v = *reinterpret_cast<const float4 *>(sp);
-        hs[0] = v.x; hs[1] = v.y; hs[2] = v.z; hs[3] = v.w;
-    } else {
+    float *sp = p.state + chc * N + n0;
 #pragma unroll
-        for (int k = 0; k < kPerLane; ++k) hs[k] = (n0 + k < N) ? sp[k] : 0.0f;
-    }
+    for (int k = 0; k < kPerLane; ++k) hs[k] = (n0 + k < N) ? sp[k] : 0.0f;
     float acc = 0.0f;
 #pragma unroll
     for (int k = 0; k < kPerLane; ++k) {
         const int n = n0 + k;
-        if (VEC || n < N) {
+        if (n < N) {
             const float a = p.A[d * N + n];
             const float bn = load_io<IO>(p.Bm, b * N + n);
             const float cn = load_io<IO>(p.Cm, b * N + n);
-            const float e = hw_exp2(dt * a * kLog2e);
-            const float coef = (a == 0.0f) ? dt : (e - 1.0f) / a;
-            hs[k] = e * hs[k] + coef * (bn * u);
+            const float zz = dt * a;
+            const float e = hw_exp2(zz * kLog2e);
+            hs[k] = e * hs[k] + (dt * phi_of(zz, e)) * (bn * u);
             acc += cn * hs[k];
         }
     }
     if (live) {
-        if (VEC) {
-            *reinterpret_cast<float4 *>(sp) = make_float4(hs[0], hs[1], hs[2], hs[3]);
-        } else {
 #pragma unroll
-            for (int k = 0; k < kPerLane; ++k)
-                if (n0 + k < N) sp[k] = hs[k];
-        }
+        for (int k = 0; k < kPerLane; ++k)
+            if (n0 + k < N) sp[k] = hs[k];
     }
-    // Sum the four partial read-outs of the channel (lanes 4c..4c+3).
-    acc += __shfl_xor(acc, 1, 64);
-    acc += __shfl_xor(acc, 2, 64);
+    acc = quad_sum(acc);
     if (live && j == 0) {
         float yv = acc + (p.Dskip ? p.Dskip[d] * u : 0.0f);
         if (p.z) yv *= silu(load_io<IO>(p.z, chc));
@@ -88,12 +172,15 @@ __global__ __launch_bounds__(256) void state_update_kernel(UpdateParams p) {
 
 template <typename IO>
 hipError_t launch_typed(const UpdateParams &p, bool vec, hipStream_t stream) {
-    const int64_t threads = p.B * p.D * kLanesPerChannel;
-    const unsigned blocks = (unsigned)((threads + 255) / 256);
-    if (vec)
-        state_update_kernel<IO, true><<<blocks, 256, 0, stream>>>(p);
-    else
-        state_update_kernel<IO, false><<<blocks, 256, 0, stream>>>(p);
+    const int64_t nq = p.B * p.D * kLanesPerChannel;
+    if (vec) {
+        const int64_t threads = (nq + kQuartersPerThread - 1) / kQuartersPerThread;
+        const unsigned blocks = (unsigned)((threads + 255) / 256);
+        state_update_vec_kernel<IO><<<blocks, 256, 0, stream>>>(p, nq);
+    } else {
+        const unsigned blocks = (unsigned)((nq + 255) / 256);
+        state_update_kernel<IO><<<blocks, 256, 0, stream>>>(p);
+    }
     return hipGetLastError();
 }
 
@@ -115,8 +202,12 @@ hipError_t launch_state_update(const ssm_state_update_args_t &a, hipStream_t str
     p.Dskip = a.Dskip;
     p.dbias = a.delta_bias;
     p.y = a.y;
-    // Whole float4 rows need N == 16 and a 16-byte aligned state.
-    const bool vec = (a.dstate == SSM_MAX_DSTATE) && ((uintptr_t)a.state % 16 == 0);
+    // Whole 16-byte quarters need N == 16 and aligned state, A, B and C
+    // (B and C rows are 8 bytes per quarter in bf16, 16 in fp32).
+    const size_t bc_align = a.io_dtype == SSM_BF16 ? 8 : 16;
+    const bool vec = a.dstate == SSM_MAX_DSTATE && (uintptr_t)a.state % 16 == 0 &&
+                     (uintptr_t)a.A % 16 == 0 && (uintptr_t)a.Bm % bc_align == 0 &&
+                     (uintptr_t)a.Cm % bc_align == 0;
     if (a.io_dtype == SSM_BF16) return launch_typed<io_bf16>(p, vec, stream);
     return launch_typed<io_f32>(p, vec, stream);
 }

@@ -60,6 +60,11 @@ CASES = [
     ("wide13_generic_f32", 6, 21, 4099, 16, torch.float32, dict(h0=True)),
     ("wide16_f32_conv", 24, 18, 2000, 16, torch.float32, dict(conv_k=4)),
     ("wide_n5_bf16", 32, 19, 1536, 5, torch.bfloat16, dict(h0=True)),
+    # few channels and long sequences: scanned as concurrent segments
+    ("seg4_bf16", 1, 8192, 64, 16, torch.bfloat16, dict(delta_shift=3.0)),
+    ("seg2_f32_h0", 1, 6000, 40, 16, torch.float32, dict(h0=True)),
+    ("seg2_conv_bf16", 2, 5000, 24, 16, torch.bfloat16, dict(conv_k=4)),
+    ("seg2_n5_f32", 1, 4500, 30, 5, torch.float32, dict(h0=True)),
 ]
 
 
@@ -90,6 +95,17 @@ def test_zero_and_positive_A():
     A[:, 0] = 0.0          # integrator channels: Bbar = dt * B
     A[5, :] = 0.0
     A[7, 3] = 0.05         # mildly unstable mode
+    inp["A"] = A
+    check_full(inp, 1e-4)
+
+
+def test_segments_with_undecaying_entries():
+    # A = 0 (and A > 0) entries never forget the entering state, so every
+    # later segment is rescanned whole from its true entering state.
+    inp = W.make_scan_inputs(1, 5000, 32, 16, io_dtype=torch.float32, seed=14, device=DEV, h0=True)
+    A = inp["A"].clone()
+    A[:, 0] = 0.0
+    A[3, 5] = 1e-3
     inp["A"] = A
     check_full(inp, 1e-4)
 
