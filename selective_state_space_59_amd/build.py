@@ -29,16 +29,26 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=" + ARCH, "-x", "hip",
           "-Wall", "-Wno-unused-function", "-I", os.path.join(PKG, "..", "include")]
 
 
+def _code_only(text: bytes) -> bytes:
+    """Source text without comments and blank space (comments do not change a build)."""
+    import re
+    t = text.decode("utf-8")
+    t = re.sub(r"/\*.*?\*/", " ", t, flags=re.S)
+    t = re.sub(r"//[^\n]*", " ", t)
+    return " ".join(t.split()).encode()
+
+
 def source_hash() -> str:
-    """sha256 over the library's sources and public header (identifies a kernel build)."""
+    """sha256 over the code of the library's sources and public header (comments
+    excluded), identifying a kernel build for measurements taken on it."""
     import hashlib
     h = hashlib.sha256()
     names = sorted(os.listdir(CSRC))
     for n in names:
         with open(os.path.join(CSRC, n), "rb") as f:
-            h.update(n.encode() + b"\0" + f.read())
+            h.update(n.encode() + b"\0" + _code_only(f.read()))
     with open(os.path.join(PKG, "..", "include", "ssm.h"), "rb") as f:
-        h.update(f.read())
+        h.update(_code_only(f.read()))
     return h.hexdigest()[:16]
 
 

@@ -8,42 +8,49 @@
 //   Abar = exp(dt A),  Bbar u = (exp(dt A) - 1) / A * B u   (dt B u if A == 0)
 //   h    = Abar h + Bbar u,   y = (sum_n C h + D u) * silu(z)
 //
-// Work decomposition ("row" layout).  One lane owns one (channel, state
-// index) chain; a 16-lane row of the wave holds the 16 state entries of one
-// channel, so a wave covers 4 channels and every workgroup is one wave.
-// With N = 16 the 130M-like layer (B=8, D=1536) becomes 3072 waves and the
-// 2.8B-like layer 5120 waves: 3 and 5 per SIMD, evenly spread.
+// Work decomposition.  One lane owns one (channel, state index) chain; a
+// 16-lane row of the wave holds the 16 state entries of one channel, so a
+// wave covers 4 channels and the (B, L, D, N) state never leaves registers.
+// A workgroup of W waves covers 4W consecutive channels of one batch row;
+// with N = 16 the 130M-like layer (B=8, D=1536) is 3072 waves and the
+// 2.8B-like layer 5120.  Few-channel long sequences are cut into segments
+// scanned at once (see launch_scan_fwd).
 //
-// Time advances in blocks of 16 steps.  Within a block:
-//   * each lane loads x/delta/z of ITS OWN step (t0 + n) for its channel and
-//     computes u (conv prologue) and dt there, once per (t, channel); the
-//     conv's 3-step history comes from the neighbouring lanes of the row
-//     (and the previous block's lanes 13..15) through DPP shifts;
+// Time advances in blocks of 16 steps.  Per block:
+//   * x, delta, z ([16 rows][4W channels]) and the B, C rows ([16][16]) are
+//     staged in LDS with 16-byte loads, each wave holding one load duty so
+//     every load reads one tensor through a wave-uniform buffer descriptor;
+//     reads past the data return 0 and such writes are dropped, so ragged
+//     edges need no branches;
+//   * each lane decodes x, delta, z of ITS OWN step (t0 + n) for its
+//     channel and computes u (conv prologue, its 3-step history from the
+//     neighbouring lanes through DPP shifts) and dt there, once per
+//     (t, channel);
 //   * the recurrence of step k reads dt and u of step k from lane k of the
-//     row through a DPP row broadcast folded into the multiply (no memory);
+//     row through a DPP row broadcast folded into the multiply;
 //   * the B and C rows (shared by all channels) reach every row of the wave
 //     through the matrix cores: one MFMA with a 0/1 selector matrix copies
-//     4 steps x 16 entries of B (or C), loaded from memory as an MFMA
-//     operand, into 4 registers of every lane, exactly (bf16 -> fp32 for
-//     free), keeping the broadcast off the LDS and the vector ALU;
-//   * each lane keeps its 16 partial read-outs C_{t,n} h_{t,n}; they are
-//     transposed through LDS so lane (c, j) sums the 16 partials of step
-//     t0 + j and applies the skip, the gate and the store.
-// Global memory goes through buffer descriptors built once per launch;
-// each lane advances a 32-bit offset per block.  Reads past the end of the
-// sequence (or of the channel range) return 0 and such writes are dropped,
-// so the ragged tail needs no branches.  Inputs are requested two blocks
-// ahead.  The (B, L, D, N) state never leaves registers.
+//     4 steps x 16 entries of B (or C) into 4 registers of every lane,
+//     exactly (bf16 -> fp32 for free), keeping the broadcast off the vector
+//     ALU;
+//   * each lane's 16 partial read-outs C_{t,n} h_{t,n} are transposed
+//     through LDS, so lane (c, j) sums the 16 partials of step t0 + j and
+//     applies the skip and the gate; y goes out through LDS with coalesced
+//     16-byte stores.
+// The block loop is software-pipelined: loads run four blocks ahead through
+// a three-slot LDS ring, a block's read-outs are summed and its y stored
+// during the next block, and the B/C broadcasts run one step group ahead.
 //
 // Vector-ALU cost per state update (the binding resource): one exp (two
-// issue slots on gfx950) and six fp32 ops:
-//   zz = dt*A*log2e; e = 2^zz; bu = B*u; q = bu/A; bx = e*q - q (fused);
-//   h = e*h + bx (fused); p = C*h.
-// bx = fma(e, q, -q) makes dt = 0 hold the state exactly (e = 1 gives 0).
+// issue slots on gfx950) and five fp32 ops in the fast form, which carries
+// g = A h:
+//   zz = dt*A*log2e; e = 2^zz; bu = B*u; bx = e*bu - bu (fused);
+//   g = e*g + bx (fused); p = C*g   (and C h = p / A in the read-out).
+// bx = fma(e, bu, -bu) makes dt = 0 hold the state exactly (e = 1 gives 0).
 //
 // Accuracy: e - 1 inherits the absolute rounding error of e (~1e-7), so the
-// fast form above errs by ~1e-7 |B u / A| per step.  Waves in which some
-// |A| < 1/16 (including A == 0) instead take the "precise" form
+// fast form errs by ~1e-7 |B u / A| per step.  Waves in which some
+// |A| < 1/16 (including A == 0) instead carry h and take the "precise" form
 //   Bbar u = dt * phi(dt A) * B u,  phi(z) = (e^z - 1) / z,
 // with a degree-6 series for |z| < 1/4 and (e - 1)/z otherwise.
 // B and C are broadcast through multiplications by 0 and 1, so they must be

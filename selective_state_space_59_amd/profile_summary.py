@@ -102,7 +102,7 @@ def cmd_counters(a):
              "| HBM bytes per launch | %.0f |" % total,
              "| algorithmic bytes per launch | %d |" % a.algorithmic_bytes,
              "| traffic / algorithmic | %.4f |" % (total / a.algorithmic_bytes),
-             "| library source hash | %s |" % entry["source_hash"]]
+             "| library source hash (code, comments excluded) | %s |" % entry["source_hash"]]
     _write(a.out, "\n".join(lines) + "\n")
 
 
