@@ -265,8 +265,8 @@ def main():
         extra = {}
         for c in (W.C3_2P8B_CONV, W.C4_DNA_1M):
             print("bench extra: %s" % c.name, file=sys.stderr, flush=True)
-            reps = 3 if c.seqlen > 100000 else 5
-            cms, cb, _ = bench_scan(c, reps, 1, nsets=1, final_state=c.final_state)
+            reps, warm = (5, 2) if c.seqlen > 100000 else (30, 5)
+            cms, cb, _ = bench_scan(c, reps, warm, nsets=1, final_state=c.final_state)
             extra[c.name] = dict(ms=round(cms, 4), gbs=round(cb / (cms * 1e-3) / 1e9, 2),
                                  frac_hbm=round(cb / (cms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                                  elems_per_s=round(c.elems / (cms * 1e-3), 1),

@@ -12,13 +12,15 @@
 // shared by all batch rows and so served from the caches).  Four lanes share
 // one channel, each holding four consecutive state entries, so a wave moves
 // 16 channels x 64 bytes of state with one 16-byte access per lane.  Each
-// thread handles four such quarters (a grid-size stride apart) and issues all
-// their loads before any arithmetic, to keep enough bytes in flight.  The
-// four partial read-outs of a channel are summed with two DPP quad swaps.
+// thread handles two such quarters (a grid-size stride apart) and issues all
+// their loads before any arithmetic.  The state is streamed with
+// non-temporal loads and stores (it is touched once per step).  The four
+// partial read-outs of a channel are summed with two DPP quad swaps.
 //
-// Bbar x = dt phi(dt A) B x with phi(z) = (e^z - 1) / z, evaluated as a
-// degree-6 series for |z| < 1/4 (no cancellation, and phi(0) = 1 covers
-// A = 0) and as (e^z - 1) / z otherwise.
+// Bbar x: in waves where every |A| >= 1/16, (e^{dt A} - 1) (B x) / A with an
+// approximate reciprocal; otherwise dt phi(dt A) B x with
+// phi(z) = (e^z - 1) / z, evaluated as a degree-6 series for |z| < 1/4 (no
+// cancellation, and phi(0) = 1 covers A = 0) and as (e^z - 1) / z beyond.
 #include "ssm_device.h"
 #include "ssm_internal.h"
 
@@ -27,7 +29,7 @@ namespace {
 
 constexpr int kLanesPerChannel = 4;
 constexpr int kPerLane = SSM_MAX_DSTATE / kLanesPerChannel;  // 4 state entries per lane
-constexpr int kQuartersPerThread = 4;
+constexpr int kQuartersPerThread = 2;
 
 struct UpdateParams {
     int64_t B, D;
@@ -85,7 +87,11 @@ __global__ __launch_bounds__(256) void state_update_vec_kernel(UpdateParams p, i
         // 32-bit division when the channel count allows it (always in practice).
         const int64_t b = p.B * p.D <= 0xFFFFFFFFLL ? (int64_t)((uint32_t)ch / (uint32_t)p.D) : ch / p.D;
         const int64_t d = ch - b * p.D;
-        st[k] = *reinterpret_cast<const float4 *>(p.state + ch * SSM_MAX_DSTATE + 4 * j);
+        {
+            typedef float f4v __attribute__((ext_vector_type(4)));
+            const f4v v = __builtin_nontemporal_load(reinterpret_cast<const f4v *>(p.state + ch * SSM_MAX_DSTATE + 4 * j));
+            st[k] = make_float4(v.x, v.y, v.z, v.w);
+        }
         av[k] = *reinterpret_cast<const float4 *>(p.A + d * SSM_MAX_DSTATE + 4 * j);
         bv[k] = load4_io<IO>(p.Bm, b * SSM_MAX_DSTATE + 4 * j);
         cv[k] = load4_io<IO>(p.Cm, b * SSM_MAX_DSTATE + 4 * j);
@@ -95,6 +101,12 @@ __global__ __launch_bounds__(256) void state_update_vec_kernel(UpdateParams p, i
         dsk[k] = p.Dskip ? p.Dskip[d] : 0.0f;
         if (p.softplus) dv[k] = softplus(dv[k] + (p.dbias ? p.dbias[d] : 0.0f));
     }
+    bool big = true;
+#pragma unroll
+    for (int k = 0; k < K; ++k)
+        big = big && fabsf(av[k].x) >= 0.0625f && fabsf(av[k].y) >= 0.0625f &&
+              fabsf(av[k].z) >= 0.0625f && fabsf(av[k].w) >= 0.0625f;
+    const bool fast = __all(big);
 #pragma unroll
     for (int k = 0; k < K; ++k) {
         const int64_t q = q0 + k * stride;
@@ -108,12 +120,20 @@ __global__ __launch_bounds__(256) void state_update_vec_kernel(UpdateParams p, i
         for (int r = 0; r < 4; ++r) {
             const float zz = dt * a[r];
             const float e = hw_exp2(zz * kLog2e);
-            h[r] = e * h[r] + (dt * phi_of(zz, e)) * (bb[r] * u);
+            if (fast) {
+                const float qq = (bb[r] * u) * hw_rcp(a[r]);
+                h[r] = __builtin_fmaf(e, h[r], __builtin_fmaf(e, qq, -qq));
+            } else {
+                h[r] = e * h[r] + (dt * phi_of(zz, e)) * (bb[r] * u);
+            }
             acc += cc[r] * h[r];
         }
         if (q < nq)
-            *reinterpret_cast<float4 *>(p.state + (q >> 2) * SSM_MAX_DSTATE + 4 * (q & 3)) =
-                make_float4(h[0], h[1], h[2], h[3]);
+        {
+            typedef float f4v __attribute__((ext_vector_type(4)));
+            const f4v v = {h[0], h[1], h[2], h[3]};
+            __builtin_nontemporal_store(v, reinterpret_cast<f4v *>(p.state + (q >> 2) * SSM_MAX_DSTATE + 4 * (q & 3)));
+        }
         acc = quad_sum(acc);
         if (q < nq && (q & 3) == 0) {
             float yv = acc + dsk[k] * u;

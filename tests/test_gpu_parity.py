@@ -211,6 +211,24 @@ def test_state_update_matches_oracle(B, D, N, dt):
     assert_close(to64(st), ref, TOL[dt], "state")
 
 
+def test_state_update_small_and_zero_A():
+    # |A| < 1/16 anywhere in a wave switches it to the phi form (A = 0 included).
+    inp = W.make_decode_inputs(3, 48, 16, 4, io_dtype=torch.float32, seed=21, device=DEV)
+    A = inp["A"].clone()
+    A[:, 0] = 0.0
+    A[7, 3] = 0.01
+    A[20, 9] = -0.03
+    inp["A"] = A
+    ys, st = _decode(inp, 4, torch.float32)
+    ref = inp["state0"].double().cpu().numpy()
+    for t in range(4):
+        yr, ref = oracle.state_update(ref, to64(inp["x"][t]), to64(inp["delta"][t]), to64(A),
+                                      to64(inp["Bm"][t]), to64(inp["Cm"][t]),
+                                      Dskip=to64(inp["Dskip"]), z=to64(inp["z"][t]))
+        assert_close(to64(ys[t]), yr, 1e-4, "y step %d" % t)
+    assert_close(to64(st), ref, 1e-4, "state")
+
+
 def test_decode_config_sampled_rows():
     cfg = W.C5_DECODE
     inp = W.make_decode_config_inputs(cfg, device=DEV)
