@@ -283,12 +283,12 @@ struct Geo {
 // a = ceil(16 CH / cw / 64).  The launch picks W so that 3a + 2 <= W.
 struct Duty {
     const char *gbase;  // tensor of the duty at the launch's first row (uniform)
-    int64_t grec;       // its bytes in this launch (uniform)
+    uint32_t grec;      // its bytes in this launch (uniform; < 4 GiB per launch)
     uint32_t step;      // its bytes per block (uniform)
     uint32_t goff;      // the thread's chunk within a block, or kOOB
     uint32_t lds;       // LDS offset of the chunk within a slot of the own or bc area
-    bool to_bc;         // the duty fills the bc area (uniform)
-    bool ystore;        // the wave stores y chunks (uniform)
+    int to_bc;          // the duty fills the bc area (uniform)
+    int ystore;         // the wave stores y chunks (uniform)
     uint32_t ylds;      // ybuf offset of the thread's y chunk
 };
 
@@ -312,8 +312,8 @@ __device__ __forceinline__ Duty make_duty(const ScanKernelParams &p, const Span 
     const int64_t D = p.D, N = p.N, rows = sp.t1 - sp.t0;
     const int role = wave < 3 * a ? wave / a : 3 + (wave - 3 * a);  // uniform
     Duty d;
-    d.to_bc = role == 3 || role == 4;
-    d.ystore = role == 0;
+    d.to_bc = __builtin_amdgcn_readfirstlane(role == 3 || role == 4 ? 1 : 0);
+    d.ystore = __builtin_amdgcn_readfirstlane(role == 0 ? 1 : 0);
     d.goff = kOOB;
     d.lds = 0;
     d.ylds = 0;
@@ -321,7 +321,7 @@ __device__ __forceinline__ Duty make_duty(const ScanKernelParams &p, const Span 
         const void *src = role == 0 ? p.x : role == 1 ? p.delta : p.z;
         const int64_t base = (b * p.L + sp.t0) * D * es;
         d.gbase = static_cast<const char *>(src ? src : p.x) + base;
-        d.grec = src ? rows * D * es : 0;  // no gate: every z read gives 0
+        d.grec = src ? (uint32_t)(rows * D * es) : 0u;  // no gate: every z read gives 0
         d.step = (uint32_t)(kTB * D * es);
         const int q = (wave - role * a) * 64 + lane;
         const int row = q / per_row, ck = q % per_row;
@@ -335,21 +335,35 @@ __device__ __forceinline__ Duty make_duty(const ScanKernelParams &p, const Span 
         const void *src = role == 3 ? p.Bm : p.Cm;
         const int64_t base = (b * p.L + sp.t0) * N * es;
         d.gbase = static_cast<const char *>(src) + base;
-        d.grec = role <= 4 ? rows * N * es : 0;
+        d.grec = role <= 4 ? (uint32_t)(rows * N * es) : 0u;
         d.step = (uint32_t)(kTB * N * es);
         if (role <= 4 && lane * 16 < kTB * kRow * es) {
             d.goff = (uint32_t)(lane * 16);
             d.lds = (uint32_t)((role - 3) * kTB * kRow * es + lane * 16);
         }
     }
+    d.grec = __builtin_amdgcn_readfirstlane(d.grec);
+    d.step = __builtin_amdgcn_readfirstlane(d.step);
     return d;
+}
+
+// max(a - b, 0) on the scalar unit (the compiler forms this saturating
+// difference on the vector ALU otherwise, one more vector op per use).
+__device__ __forceinline__ uint32_t scalar_sat_sub(uint32_t a, uint32_t b) {
+    uint32_t r;
+    asm("s_sub_u32 %0, %1, %2\n\ts_cselect_b32 %0, 0, %0" : "=s"(r) : "s"(a), "s"(b) : "scc");
+    return r;
 }
 
 // Buffer descriptor of the duty's tensor for block jb (rebased on the
 // block, so the per-lane offsets stay fixed; scalar arithmetic only).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t duty_rsrc(const Duty &d, int64_t jb) {
-    const int64_t off = jb * (int64_t)d.step;
-    return rsrc(d.gbase, off, d.grec - off);
+// 32-bit scalar arithmetic: a launch spans less than 4 GiB per tensor, and a
+// prefetch past the end gets no records.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t duty_rsrc(const Duty &d, uint32_t jb) {
+    const uint32_t off = jb * d.step;
+    const uint32_t rem = scalar_sat_sub(d.grec, off);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(d.gbase + off), (short)0, (int)rem,
+                                             kRsrcWord3);
 }
 
 // Raw global data of one block held by one thread between its load and its
@@ -372,7 +386,7 @@ struct Fetch<false> {
 };
 
 template <typename IO, bool VEC>
-__device__ __forceinline__ void fetch_block(const Geo &g, const Duty &d, int64_t jb, int tid,
+__device__ __forceinline__ void fetch_block(const Geo &g, const Duty &d, uint32_t jb, int tid,
                                             int nthreads, Fetch<VEC> &f) {
     constexpr int es = sizeof(typename IO::storage);
     if constexpr (VEC) {
@@ -464,13 +478,14 @@ __device__ __forceinline__ YChunk<VEC> read_ybuf(const Duty &d, const Tiles &T, 
 }
 template <typename IO, bool VEC>
 __device__ __forceinline__ void store_y(const ScanKernelParams &p, const Geo &g, const Duty &d,
-                                        const YChunk<VEC> &y, int64_t jb, int tid) {
+                                        const YChunk<VEC> &y, uint32_t jb, int tid) {
     constexpr int es = sizeof(typename IO::storage);
     if constexpr (VEC) {
-        const int64_t off = jb * (int64_t)d.step;
-        const __amdgpu_buffer_rsrc_t r =
-            rsrc(static_cast<const char *>(p.y) + (d.gbase - static_cast<const char *>(p.x)), off,
-                 d.grec - off);
+        const uint32_t off = jb * d.step;
+        const uint32_t rem = scalar_sat_sub(d.grec, off);
+        const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+            static_cast<char *>(p.y) + (d.gbase - static_cast<const char *>(p.x)) + off, (short)0,
+            (int)rem, kRsrcWord3);
         __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4i_t, y.v), r, d.goff, 0, 0);
     } else {
         const int CH = 4 * g.W;
@@ -553,7 +568,7 @@ __device__ __forceinline__ float readout(const float *prow, const float *iat, in
 
 // Per-lane values carried from one block to the next.
 struct Carry {
-    uint32_t own[3];       // raw x, delta, z of this lane's step in the current block
+    float own[3];          // x, delta, z of this lane's step in the current block
     float u_prev, z_prev;  // u and z of this lane's step in the previous block
     float x_prev;          // conv history: x of the previous block (lanes 13..15 used)
     float h;               // state (A h in the fast form)
@@ -577,13 +592,13 @@ constexpr float kForgetExp2 = -160.0f;
 
 template <typename IO>
 __device__ __forceinline__ void read_own(const Tiles &T, const char *lds, int slot, int n, int ci,
-                                         uint32_t (&raw)[3]) {
+                                         float (&v)[3]) {
     constexpr int es = sizeof(typename IO::storage);
     const char *src = lds + T.own + slot * T.own_slot + n * T.rs + ci * es;
 #pragma unroll
     for (int i = 0; i < 3; ++i) {
-        if constexpr (es == 2) raw[i] = *reinterpret_cast<const uint16_t *>(src + i * kPlane<IO>);
-        else raw[i] = *reinterpret_cast<const uint32_t *>(src + i * kPlane<IO>);
+        if constexpr (es == 2) v[i] = widen<IO>(*reinterpret_cast<const uint16_t *>(src + i * kPlane<IO>));
+        else v[i] = *reinterpret_cast<const float *>(src + i * kPlane<IO>);
     }
 }
 
@@ -603,7 +618,7 @@ template <typename IO, bool CONV, bool VEC, bool FAST, bool STATS, bool TAIL, in
 __device__ __forceinline__ void block_iter(const ScanKernelParams &p, const Span &sp, const Geo &geo,
                                            const Tiles &T, char *lds, int wave, int c, int n,
                                            int lane, const BcastSel &sel, const LaneConst &k,
-                                           const Duty &du, int64_t j, int s_cur, Fetch<VEC> &f,
+                                           const Duty &du, int j, int s_cur, Fetch<VEC> &f,
                                            Carry &cy) {
     constexpr int es = sizeof(typename IO::storage);
     const int tid = threadIdx.x, nthreads = blockDim.x;
@@ -617,7 +632,7 @@ __device__ __forceinline__ void block_iter(const ScanKernelParams &p, const Span
     __syncthreads();
     // -- LDS reads first ------------------------------------------------------
     const float acc = readout<FAST>(prow, prow + kRow * kPStride, n);
-    uint32_t own_next[3];
+    float own_next[3];
     read_own<IO>(T, lds, s_next, n, ci, own_next);
     const YChunk<VEC> yst = read_ybuf<IO, VEC>(du, T, lds, PAR, tid);
     typename BcOperand<IO>::type bop[4], cop[4];
@@ -628,9 +643,9 @@ __device__ __forceinline__ void block_iter(const ScanKernelParams &p, const Span
     }
 
     // -- this block's inputs ---------------------------------------------------
-    const float xv = widen<IO>(cy.own[0]);
-    float dt = widen<IO>(cy.own[1]);
-    const float zv = widen<IO>(cy.own[2]);
+    const float xv = cy.own[0];
+    float dt = cy.own[1];
+    const float zv = cy.own[2];
     float u = xv;
     if (CONV) {
         const float xm1 = row_shift_in<1>(xv, cy.x_prev);
@@ -719,7 +734,7 @@ __device__ __forceinline__ void scan_tiles_body(const ScanKernelParams &p, const
     const int ci = 4 * wave + c;
     const BcastSel sel = make_sel(lane);
     const int64_t rows = sp.t1 - sp.t0;
-    const int64_t nblocks = (rows + kTB - 1) / kTB;
+    const int nblocks = (int)((rows + kTB - 1) / kTB);
 
     // Block j is requested four blocks ahead, copied into LDS slot j % 3
     // two blocks ahead, and its outputs leave LDS two blocks later.  Two
@@ -743,8 +758,9 @@ __device__ __forceinline__ void scan_tiles_body(const ScanKernelParams &p, const
     cy.z_prev = 0.0f;
 
     int s = 0;  // LDS slot of block j
-    int64_t j = 0;
-    auto advance = [&]() { s = s == kSlots - 1 ? 0 : s + 1; };
+    int j = 0;
+    // The slot index is kept scalar (it is the same for the whole workgroup).
+    auto advance = [&]() { s = __builtin_amdgcn_readfirstlane(s == kSlots - 1 ? 0 : s + 1); };
     for (; j + 2 < nblocks; j += 2) {
         block_iter<IO, CONV, VEC, FAST, STATS, false, 0, true>(p, sp, geo, T, lds, wave, c, n, lane, sel, k,
                                                         du, j, s, fa, cy);
@@ -769,7 +785,7 @@ __device__ __forceinline__ void scan_tiles_body(const ScanKernelParams &p, const
     }
     // Outputs of the last block and of the one before it.
     constexpr int es = sizeof(typename IO::storage);
-    const int64_t jl = nblocks - 1;
+    const int jl = nblocks - 1;
     __syncthreads();  // every wave has read ybuf[last_par] for its store
     {
         const float *prow = reinterpret_cast<const float *>(lds + T.part) + (wave * kChPerWave + c) * kPRow;
