@@ -193,16 +193,22 @@ typedef int v4i_t __attribute__((ext_vector_type(4)));
 typedef short mfma_bf16x4 __attribute__((ext_vector_type(4)));
 typedef float mfma_f32x4 __attribute__((ext_vector_type(4)));
 
-// Selector operand of the broadcast MFMA (constant per lane).
+// Selector operands of the broadcast MFMA (constant per lane).
+//  bf16 (16x16x16): the selector of step group g is the A operand
+//    A[i][k] = (k == 4g + i % 4): lane l holds the one-hot of l % 4 when
+//    l / 16 == g, zeros otherwise;
+//  fp32 (16x16x4): A[i][k] = (k == i % 4).
 struct BcastSel {
-    mfma_bf16x4 bf;  // bf16: identity 16x16 as the B operand
-    float f;         // fp32: A[i][k] = (k == i % 4) as the A operand
+    mfma_bf16x4 bf[4];
+    float f;
 };
 __device__ __forceinline__ BcastSel make_sel(int lane) {
     BcastSel s;
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
-        s.bf[r] = (4 * (lane >> 4) + r == (lane & 15)) ? (short)0x3F80 : (short)0;
+    for (int g = 0; g < 4; ++g)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            s.bf[g][r] = ((lane >> 4) == g && r == (lane & 3)) ? (short)0x3F80 : (short)0;
     s.f = ((lane >> 4) == ((lane & 15) & 3)) ? 1.0f : 0.0f;
     return s;
 }
@@ -212,7 +218,8 @@ __device__ __forceinline__ BcastSel make_sel(int lane) {
 // channels of one batch row.  Per 16-step block it stages in LDS, with wide
 // coalesced loads shared by all its waves:
 //   own [3 slots][x|delta|z][16 rows][CH + pad]  raw I/O elements
-//   bc  [3 slots][B|C][16 rows][16]               raw B and C rows (zero past N)
+//   bc  [3 slots][B|C][16 rows][16]               raw B and C rows (zero past N);
+//                                                 bf16 entry-major, [16 entries][16 steps]
 //   ybuf[2][16 rows][CH + pad]                    raw outputs, stored coalesced
 // and per wave a partial-sum transpose area.  The row pad puts the 16 time
 // steps that the 16 lanes of a wave row read (or write) on distinct banks;
@@ -339,7 +346,10 @@ __device__ __forceinline__ Duty make_duty(const ScanKernelParams &p, const Span 
         d.step = (uint32_t)(kTB * N * es);
         if (role <= 4 && lane * 16 < kTB * kRow * es) {
             d.goff = (uint32_t)(lane * 16);
-            d.lds = (uint32_t)((role - 3) * kTB * kRow * es + lane * 16);
+            // bf16: the chunk is entries 8 (lane % 2) .. +7 of step lane / 2,
+            // stored entry-major (see stage_block)
+            d.lds = es == 2 ? (uint32_t)((role - 3) * kTB * kRow * es + (8 * (lane % 2) * kTB + lane / 2) * es)
+                            : (uint32_t)((role - 3) * kTB * kRow * es + lane * 16);
         }
     }
     d.grec = __builtin_amdgcn_readfirstlane(d.grec);
@@ -420,7 +430,19 @@ __device__ __forceinline__ void stage_block(const Geo &g, const Duty &d, const T
         // Lanes without a chunk (or past the channel range) write nothing:
         // channels past D are never stored, so their staged values do not matter.
         char *base = lds + (d.to_bc ? T.bc + slot * T.bc_slot : T.own + slot * T.own_slot);
-        if (d.goff != kOOB) *reinterpret_cast<uint4 *>(base + d.lds) = f.v;
+        if (d.goff != kOOB) {
+            if (es == 2 && d.to_bc) {
+                // bf16 B/C rows go in entry-major: 8 entries of one step, a
+                // column of the [n][t] tile.
+                char *dst = base + d.lds;
+                const uint32_t w[4] = {f.v.x, f.v.y, f.v.z, f.v.w};
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    *reinterpret_cast<uint16_t *>(dst + e * kTB * 2) = (uint16_t)(w[e / 2] >> (16 * (e % 2)));
+            } else {
+                *reinterpret_cast<uint4 *>(base + d.lds) = f.v;
+            }
+        }
     } else {
         char *own = lds + T.own + slot * T.own_slot;
         char *bc = lds + T.bc + slot * T.bc_slot;
@@ -437,8 +459,9 @@ __device__ __forceinline__ void stage_block(const Geo &g, const Duty &d, const T
             const int e = tid + i * nthreads;
             if (e < kTB * kRow) {
                 if constexpr (es == 2) {
-                    *reinterpret_cast<uint16_t *>(bc + e * es) = (uint16_t)f.bce[i];
-                    *reinterpret_cast<uint16_t *>(cc + e * es) = (uint16_t)f.bce[4 + i];
+                    const int te = (e % kRow) * kTB + e / kRow;  // entry-major
+                    *reinterpret_cast<uint16_t *>(bc + te * es) = (uint16_t)f.bce[i];
+                    *reinterpret_cast<uint16_t *>(cc + te * es) = (uint16_t)f.bce[4 + i];
                 } else {
                     *reinterpret_cast<uint32_t *>(bc + e * es) = f.bce[i];
                     *reinterpret_cast<uint32_t *>(cc + e * es) = f.bce[4 + i];
@@ -499,31 +522,42 @@ __device__ __forceinline__ void store_y(const ScanKernelParams &p, const Geo &g,
     }
 }
 
-// MFMA operand of step group g for this lane, from the staged B or C rows.
-//  bf16: row 4g + lane%4, entries 4*(lane/16) .. +3   (A operand, 16x16x16)
-//  fp32: row 4g + lane/16, entry lane%16                (B operand, 16x16x4)
+// MFMA data operands of one block's B (or C) rows held by a lane.
+//  bf16: the B operand of the whole block, staged entry-major ([n][t]):
+//        steps 4*(lane/16) .. +3 of entry lane%16 (each value read once);
+//  fp32: per step group g, row 4g + lane/16, entry lane%16 (B operand).
 template <typename IO>
-struct BcOperand {
-    using type = typename std::conditional<std::is_same<IO, io_bf16>::value, uint2, float>::type;
+struct BcBlock;
+template <>
+struct BcBlock<io_bf16> {
+    uint2 v;
+};
+template <>
+struct BcBlock<io_f32> {
+    float v[4];
 };
 template <typename IO>
-__device__ __forceinline__ typename BcOperand<IO>::type load_bc_operand(const char *rows, int g,
-                                                                       int lane) {
-    if constexpr (std::is_same<IO, io_bf16>::value)
-        return *reinterpret_cast<const uint2 *>(rows + ((4 * g + (lane & 3)) * kRow + 4 * (lane >> 4)) * 2);
-    else
-        return *reinterpret_cast<const float *>(rows + ((4 * g + (lane >> 4)) * kRow + (lane & 15)) * 4);
+__device__ __forceinline__ BcBlock<IO> load_bc_block(const char *rows, int lane) {
+    BcBlock<IO> o;
+    if constexpr (std::is_same<IO, io_bf16>::value) {
+        o.v = *reinterpret_cast<const uint2 *>(rows + ((lane & 15) * kTB + 4 * (lane >> 4)) * 2);
+    } else {
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+            o.v[g] = *reinterpret_cast<const float *>(rows + ((4 * g + (lane >> 4)) * kRow + (lane & 15)) * 4);
+    }
+    return o;
 }
 // Broadcast of rows 4g..4g+3 to every wave row: register r of lane l gets
 // entry l%16 of row 4g + r (0/1 selector, exact).
 template <typename IO>
-__device__ __forceinline__ mfma_f32x4 bcast(typename BcOperand<IO>::type op, const BcastSel &sel) {
+__device__ __forceinline__ mfma_f32x4 bcast(const BcBlock<IO> &op, const BcastSel &sel, int g) {
     const mfma_f32x4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
     if constexpr (std::is_same<IO, io_bf16>::value)
-        return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(mfma_bf16x4, op), sel.bf,
+        return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(sel.bf[g], __builtin_bit_cast(mfma_bf16x4, op.v),
                                                          zero, 0, 0, 0);
     else
-        return __builtin_amdgcn_mfma_f32_16x16x4f32(sel.f, op, zero, 0, 0, 0);
+        return __builtin_amdgcn_mfma_f32_16x16x4f32(sel.f, op.v[g], zero, 0, 0, 0);
 }
 
 struct LaneConst {
@@ -533,23 +567,14 @@ struct LaneConst {
 
 // Read-out of one step: the sum over the 16 state entries of the partials
 // C g that the lanes of this row transposed into prow.  The fast form keeps
-// g = A h, so each partial is first multiplied by 1/A of its entry, which
-// lane i of the row holds (a DPP row broadcast folded into the FMA).
+// g = A h, so each partial is first multiplied by 1/A of its entry (ia, the
+// channel's 16 values, held in registers by every lane of the row).
 template <bool FAST>
-__device__ __forceinline__ float readout(const float *prow, const float *iat, int n) {
+__device__ __forceinline__ float readout(const float *prow, const float (&ia)[kRow], int n) {
     float part[kRow];
 #pragma unroll
     for (int i = 0; i < kRow; ++i) part[i] = prow[i * kPStride + n];
     if (FAST) {
-        float ia[kRow];
-#pragma unroll
-        for (int i = 0; i < kRow; i += 4) {
-            const float4 v = *reinterpret_cast<const float4 *>(iat + i);
-            ia[i] = v.x;
-            ia[i + 1] = v.y;
-            ia[i + 2] = v.z;
-            ia[i + 3] = v.w;
-        }
         float s0 = part[0] * ia[0], s1 = part[1] * ia[1];
 #pragma unroll
         for (int i = 2; i < kRow; i += 2) {
@@ -618,7 +643,8 @@ template <typename IO, bool CONV, bool VEC, bool FAST, bool STATS, bool TAIL, in
 __device__ __forceinline__ void block_iter(const ScanKernelParams &p, const Span &sp, const Geo &geo,
                                            const Tiles &T, char *lds, int wave, int c, int n,
                                            int lane, const BcastSel &sel, const LaneConst &k,
-                                           const Duty &du, int j, int s_cur, Fetch<VEC> &f,
+                                           const float (&iat)[kRow], const Duty &du, int j, int s_cur,
+                                           Fetch<VEC> &f,
                                            Carry &cy) {
     constexpr int es = sizeof(typename IO::storage);
     const int tid = threadIdx.x, nthreads = blockDim.x;
@@ -631,16 +657,11 @@ __device__ __forceinline__ void block_iter(const ScanKernelParams &p, const Span
 
     __syncthreads();
     // -- LDS reads first ------------------------------------------------------
-    const float acc = readout<FAST>(prow, prow + kRow * kPStride, n);
+    const float acc = readout<FAST>(prow, iat, n);
     float own_next[3];
     read_own<IO>(T, lds, s_next, n, ci, own_next);
     const YChunk<VEC> yst = read_ybuf<IO, VEC>(du, T, lds, PAR, tid);
-    typename BcOperand<IO>::type bop[4], cop[4];
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-        bop[g] = load_bc_operand<IO>(brows, g, lane);
-        cop[g] = load_bc_operand<IO>(crows, g, lane);
-    }
+    const BcBlock<IO> bop = load_bc_block<IO>(brows, lane), cop = load_bc_block<IO>(crows, lane);
 
     // -- this block's inputs ---------------------------------------------------
     const float xv = cy.own[0];
@@ -682,14 +703,14 @@ __device__ __forceinline__ void block_iter(const ScanKernelParams &p, const Span
     // Steps in groups of four: one broadcast MFMA each for B and C per
     // group, issued one group ahead so the matrix cores' latency is hidden,
     // and one 128-bit LDS write of the group's four partial read-outs.
-    mfma_f32x4 Bn = bcast<IO>(bop[0], sel), Cn = bcast<IO>(cop[0], sel);
+    mfma_f32x4 Bn = bcast<IO>(bop, sel, 0), Cn = bcast<IO>(cop, sel, 0);
     static_for<kTB / 4>([&](auto G) {
         constexpr int gi = decltype(G)::value;
         constexpr int g4 = 4 * gi;
         const mfma_f32x4 Bk = Bn, Ck = Cn;
         if constexpr (gi + 1 < kTB / 4) {
-            Bn = bcast<IO>(bop[gi + 1], sel);
-            Cn = bcast<IO>(cop[gi + 1], sel);
+            Bn = bcast<IO>(bop, sel, gi + 1);
+            Cn = bcast<IO>(cop, sel, gi + 1);
         }
         float pk[4];
         static_for<4>([&](auto K) {
@@ -754,6 +775,19 @@ __device__ __forceinline__ void scan_tiles_body(const ScanKernelParams &p, const
     fetch_block<IO, VEC>(geo, du, 3, tid, nthreads, fb);
     __syncthreads();
     read_own<IO>(T, lds, 0, n, ci, cy.own);
+    // 1/A of the channel's 16 entries (the fast form's read-out weights).
+    float iat[kRow];
+    {
+        const float *src = reinterpret_cast<const float *>(lds + T.part) + (wave * kChPerWave + c) * kPRow + kRow * kPStride;
+#pragma unroll
+        for (int i = 0; i < kRow; i += 4) {
+            const float4 v = FAST ? *reinterpret_cast<const float4 *>(src + i) : make_float4(0.f, 0.f, 0.f, 0.f);
+            iat[i] = v.x;
+            iat[i + 1] = v.y;
+            iat[i + 2] = v.z;
+            iat[i + 3] = v.w;
+        }
+    }
     cy.u_prev = 0.0f;
     cy.z_prev = 0.0f;
 
@@ -763,24 +797,24 @@ __device__ __forceinline__ void scan_tiles_body(const ScanKernelParams &p, const
     auto advance = [&]() { s = __builtin_amdgcn_readfirstlane(s == kSlots - 1 ? 0 : s + 1); };
     for (; j + 2 < nblocks; j += 2) {
         block_iter<IO, CONV, VEC, FAST, STATS, false, 0, true>(p, sp, geo, T, lds, wave, c, n, lane, sel, k,
-                                                        du, j, s, fa, cy);
+                                                        iat, du, j, s, fa, cy);
         advance();
         block_iter<IO, CONV, VEC, FAST, STATS, false, 1, true>(p, sp, geo, T, lds, wave, c, n, lane, sel, k,
-                                                        du, j + 1, s, fb, cy);
+                                                        iat, du, j + 1, s, fb, cy);
         advance();
     }
     // One or two blocks remain (j is even).
     int last_par;
     if (j + 1 < nblocks) {
         block_iter<IO, CONV, VEC, FAST, STATS, false, 0, true>(p, sp, geo, T, lds, wave, c, n, lane, sel, k,
-                                                        du, j, s, fa, cy);
+                                                        iat, du, j, s, fa, cy);
         advance();
         block_iter<IO, CONV, VEC, FAST, STATS, true, 1, false>(p, sp, geo, T, lds, wave, c, n, lane, sel, k,
-                                                        du, j + 1, s, fb, cy);
+                                                        iat, du, j + 1, s, fb, cy);
         last_par = 1;
     } else {
         block_iter<IO, CONV, VEC, FAST, STATS, true, 0, false>(p, sp, geo, T, lds, wave, c, n, lane, sel, k,
-                                                        du, j, s, fa, cy);
+                                                        iat, du, j, s, fa, cy);
         last_par = 0;
     }
     // Outputs of the last block and of the one before it.
@@ -789,7 +823,7 @@ __device__ __forceinline__ void scan_tiles_body(const ScanKernelParams &p, const
     __syncthreads();  // every wave has read ybuf[last_par] for its store
     {
         const float *prow = reinterpret_cast<const float *>(lds + T.part) + (wave * kChPerWave + c) * kPRow;
-        float yv = readout<FAST>(prow, prow + kRow * kPStride, n) + k.dsk * cy.u_prev;
+        float yv = readout<FAST>(prow, iat, n) + k.dsk * cy.u_prev;
         if (p.z) yv *= silu(cy.z_prev);
         char *ydst = lds + T.ybuf + last_par * T.ybuf_slot + n * T.rs + ci * es;
         if constexpr (es == 2)
