@@ -219,7 +219,7 @@ __device__ __forceinline__ BcastSel make_sel(int lane) {
 // coalesced loads shared by all its waves:
 //   own [3 slots][x|delta|z][16 rows][CH + pad]  raw I/O elements
 //   bc  [3 slots][B|C][16 rows][16]               raw B and C rows (zero past N);
-//                                                 bf16 entry-major, [16 entries][16 steps]
+//                                                 bf16 entry-major, [16 entries][20] (16 steps used)
 //   ybuf[2][16 rows][CH + pad]                    raw outputs, stored coalesced
 // and per wave a partial-sum transpose area.  The row pad puts the 16 time
 // steps that the 16 lanes of a wave row read (or write) on distinct banks;
@@ -240,6 +240,13 @@ __device__ __host__ constexpr int row_dwords(int W) {
 }
 template <typename IO>
 constexpr uint32_t kPlane = (uint32_t)kTB * 4u * row_dwords<IO>(kMaxW);
+// Staged B (or C) tile of one block.  bf16 is entry-major with rows of 20
+// elements (40 bytes = 10 dwords): the 16 lanes that read one 8-byte piece
+// each (the same steps of the 16 entries) then hit 16 distinct bank pairs.
+// fp32 is step-major ([16 steps][16 entries]).
+constexpr uint32_t kBcRowBytes = 40;
+template <typename IO>
+constexpr uint32_t kBcTile = sizeof(typename IO::storage) == 2 ? kRow * kBcRowBytes : kTB * kRow * 4;
 
 struct Tiles {
     int CH;
@@ -255,7 +262,7 @@ __device__ __host__ __forceinline__ Tiles tile_layout(int W) {
     t.CH = 4 * W;
     t.rs = 4u * (uint32_t)row_dwords<IO>(W);
     t.own_slot = 3 * kPlane<IO>;
-    t.bc_slot = (uint32_t)(2 * kTB * kRow * es);
+    t.bc_slot = 2 * kBcTile<IO>;
     t.ybuf_slot = kTB * t.rs;
     t.own = 0;
     t.bc = t.own + kSlots * t.own_slot;
@@ -348,8 +355,8 @@ __device__ __forceinline__ Duty make_duty(const ScanKernelParams &p, const Span 
             d.goff = (uint32_t)(lane * 16);
             // bf16: the chunk is entries 8 (lane % 2) .. +7 of step lane / 2,
             // stored entry-major (see stage_block)
-            d.lds = es == 2 ? (uint32_t)((role - 3) * kTB * kRow * es + (8 * (lane % 2) * kTB + lane / 2) * es)
-                            : (uint32_t)((role - 3) * kTB * kRow * es + lane * 16);
+            d.lds = (uint32_t)(role - 3) * kBcTile<IO> +
+                    (es == 2 ? (uint32_t)(8 * (lane % 2) * kBcRowBytes + (lane / 2) * es) : (uint32_t)(lane * 16));
         }
     }
     d.grec = __builtin_amdgcn_readfirstlane(d.grec);
@@ -438,7 +445,7 @@ __device__ __forceinline__ void stage_block(const Geo &g, const Duty &d, const T
                 const uint32_t w[4] = {f.v.x, f.v.y, f.v.z, f.v.w};
 #pragma unroll
                 for (int e = 0; e < 8; ++e)
-                    *reinterpret_cast<uint16_t *>(dst + e * kTB * 2) = (uint16_t)(w[e / 2] >> (16 * (e % 2)));
+                    *reinterpret_cast<uint16_t *>(dst + e * kBcRowBytes) = (uint16_t)(w[e / 2] >> (16 * (e % 2)));
             } else {
                 *reinterpret_cast<uint4 *>(base + d.lds) = f.v;
             }
@@ -446,7 +453,7 @@ __device__ __forceinline__ void stage_block(const Geo &g, const Duty &d, const T
     } else {
         char *own = lds + T.own + slot * T.own_slot;
         char *bc = lds + T.bc + slot * T.bc_slot;
-        char *cc = bc + kTB * kRow * es;
+        char *cc = bc + kBcTile<IO>;
         const int row = tid / T.CH, ci = tid % T.CH;
         char *dst = own + row * T.rs + ci * es;
 #pragma unroll
@@ -459,9 +466,9 @@ __device__ __forceinline__ void stage_block(const Geo &g, const Duty &d, const T
             const int e = tid + i * nthreads;
             if (e < kTB * kRow) {
                 if constexpr (es == 2) {
-                    const int te = (e % kRow) * kTB + e / kRow;  // entry-major
-                    *reinterpret_cast<uint16_t *>(bc + te * es) = (uint16_t)f.bce[i];
-                    *reinterpret_cast<uint16_t *>(cc + te * es) = (uint16_t)f.bce[4 + i];
+                    const int te = (e % kRow) * kBcRowBytes + (e / kRow) * es;  // entry-major
+                    *reinterpret_cast<uint16_t *>(bc + te) = (uint16_t)f.bce[i];
+                    *reinterpret_cast<uint16_t *>(cc + te) = (uint16_t)f.bce[4 + i];
                 } else {
                     *reinterpret_cast<uint32_t *>(bc + e * es) = f.bce[i];
                     *reinterpret_cast<uint32_t *>(cc + e * es) = f.bce[4 + i];
@@ -540,7 +547,7 @@ template <typename IO>
 __device__ __forceinline__ BcBlock<IO> load_bc_block(const char *rows, int lane) {
     BcBlock<IO> o;
     if constexpr (std::is_same<IO, io_bf16>::value) {
-        o.v = *reinterpret_cast<const uint2 *>(rows + ((lane & 15) * kTB + 4 * (lane >> 4)) * 2);
+        o.v = *reinterpret_cast<const uint2 *>(rows + (lane & 15) * kBcRowBytes + 8 * (lane >> 4));
     } else {
 #pragma unroll
         for (int g = 0; g < 4; ++g)
@@ -653,7 +660,7 @@ __device__ __forceinline__ void block_iter(const ScanKernelParams &p, const Span
     const int s_stage = s_next == kSlots - 1 ? 0 : s_next + 1;
     float *prow = reinterpret_cast<float *>(lds + T.part) + (wave * kChPerWave + c) * kPRow;
     const char *brows = lds + T.bc + s_cur * T.bc_slot;
-    const char *crows = brows + kTB * kRow * es;
+    const char *crows = brows + kBcTile<IO>;
 
     __syncthreads();
     // -- LDS reads first ------------------------------------------------------
@@ -842,14 +849,15 @@ __device__ __forceinline__ void scan_tiles_body(const ScanKernelParams &p, const
 
 // blockDim.x = 64 W; workgroup g covers channels [4 W q, 4 W q + 4 W) of
 // batch row g / groups_per_b, with q = g % groups_per_b.
-// Register budget: the bf16 wide-tile variants (the 130M- and 2.8B-like
-// layers) must fit 5 waves per SIMD (<= 96 VGPRs) so a 2.8B-like layer
-// (5120 waves) is resident at once; the others may use up to 128.
-template <typename IO, bool VEC>
-constexpr int kMinWavesPerEU = 4;
+// Register budget: the wide-tile variants fit 5 waves per SIMD (<= 96
+// VGPRs; their block loops keep everything in registers), so two 10-wave
+// workgroups share a CU and a 2.8B-like layer (5120 waves) is resident at
+// once; the element path may use 128 (4 waves).
+template <bool VEC>
+constexpr int kWavesPerSimd = VEC ? 5 : 4;
 
 template <typename IO, bool CONV, bool VEC, bool STATS>
-__global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(kMinWavesPerEU<IO, VEC>, 8)))
+__global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(kWavesPerSimd<VEC>, 8)))
 void scan_tiles_kernel(ScanKernelParams p) {
     extern __shared__ __attribute__((aligned(16))) char lds[];
     constexpr int es = sizeof(typename IO::storage);
@@ -995,12 +1003,13 @@ __global__ void copy_or_zero_kernel(const float *src, float *dst, int64_t n) {
     if (i < n) dst[i] = src ? src[i] : 0.0f;
 }
 
-// Waves per workgroup: the workgroups should spread evenly over the 256 CUs
-// (each CU holds up to 20 waves of this kernel).  Among the allowed W pick
-// the one whose busiest CU carries the least work, preferring wider tiles.
-// The wide path needs 3 ceil(W / cw) + 2 <= W waves for its load duties
-// (cw = channels per 16-byte chunk) and, for bf16, an even W so that every
-// workgroup's channel range starts on a 16-byte boundary.
+// Waves per workgroup: the workgroups should spread evenly over the 256 CUs.
+// A CU holds 4 x kWavesPerSimd waves of this kernel and 160 KiB of LDS.
+// Among the allowed W pick the one whose busiest CU carries the least work,
+// preferring wider tiles.  The wide path needs 3 ceil(W / cw) + 2 <= W waves
+// for its load duties (cw = channels per 16-byte chunk) and, for bf16, an
+// even W so that every workgroup's channel range starts on a 16-byte
+// boundary.
 bool wide_w_ok(int W, int64_t es) {
     const int cw = (int)(16 / es);
     if (es == 2 && W % 2 != 0) return false;
@@ -1008,15 +1017,17 @@ bool wide_w_ok(int W, int64_t es) {
 }
 
 int choose_waves(int64_t batch, int64_t dim, bool wide, int64_t es) {
-    constexpr int64_t kCUs = 256, kMaxWavesPerCU = 20;
+    constexpr int64_t kCUs = 256, kLdsPerCU = 160 * 1024;
+    const int64_t waves_per_cu = 4 * (wide ? kWavesPerSimd<true> : kWavesPerSimd<false>);
     int best = 0;
     double best_cost = 1e300;
     for (int W = 1; W <= kMaxW; ++W) {
         if (wide && !wide_w_ok(W, es)) continue;
+        const int64_t lds = (int64_t)(es == 2 ? tile_lds_bytes<io_bf16>(W) : tile_lds_bytes<io_f32>(W));
         const int64_t per_row = (dim + 4 * W - 1) / (4 * W);
         const int64_t groups = per_row * batch;
-        const int64_t per_cu = (groups + kCUs - 1) / kCUs;            // workgroups on the busiest CU
-        const int64_t fit = std::max<int64_t>(1, kMaxWavesPerCU / W); // resident at once
+        const int64_t per_cu = (groups + kCUs - 1) / kCUs;  // workgroups on the busiest CU
+        const int64_t fit = std::max<int64_t>(1, std::min(waves_per_cu / W, kLdsPerCU / lds));  // resident at once
         const int64_t rounds = (per_cu + fit - 1) / fit;
         // busiest-CU work in wave-blocks, plus a small penalty for narrow tiles
         const double cost = (double)(rounds * std::min(per_cu, fit) * W) * (1.0 + 0.02 * (16 - W));
