@@ -50,12 +50,12 @@ def _load():
         I = ctypes.c_int
         lib.oracle_selective_scan_f64.argtypes = [I64, I64, I64, I64,
                                                   P, P, P, P, P, P, P, P, I, P, P, I64,
-                                                  P, P, P, I]
+                                                  P, P, P, P, P, I]
         lib.oracle_selective_scan_f64.restype = I
         lib.oracle_causal_conv1d_silu_f64.argtypes = [I64, I64, I64, I64, P, P, P, P, I]
         lib.oracle_causal_conv1d_silu_f64.restype = I
         lib.oracle_state_update_f64.argtypes = [I64, I64, I64, P, P, P, P, P, P, P, P, P, I,
-                                                P, I]
+                                                P, P, I64, P, P, I]
         lib.oracle_state_update_f64.restype = I
         _lib = lib
     return _lib
@@ -86,11 +86,14 @@ def _ptr(a):
 
 def selective_scan(x, delta, A, Bm, Cm, Dskip=None, z=None, delta_bias=None,
                    delta_softplus: bool = False, conv_w=None, conv_b=None, h0=None,
+                   conv_state_in=None, return_conv_state: bool = False,
                    nthreads: Optional[int] = None):
-    """Return (y, h_final) in float64.
+    """Return (y, h_final), or (y, h_final, conv_state_out), in float64.
 
     x, delta, z: (B, L, D); A: (D, N); Bm, Cm: (B, L, N); Dskip, delta_bias,
-    conv_b: (D,); conv_w: (D, K); h0: (B, D, N).
+    conv_b: (D,); conv_w: (D, K); h0: (B, D, N); conv_state_in and the
+    returned conv state: (B, K-1, D), the inputs before t = 0 (zeros when
+    None) and the last K-1 inputs.
     """
     x = _f64(x)
     Bsz, L, D = x.shape
@@ -109,15 +112,19 @@ def selective_scan(x, delta, A, Bm, Cm, Dskip=None, z=None, delta_bias=None,
         conv_w = _f64(conv_w, (D, K))
     conv_b = _f64(conv_b, (D,))
     h0 = _f64(h0, (Bsz, D, N))
+    if (conv_state_in is not None or return_conv_state) and conv_w is None:
+        raise ValueError("a conv state needs conv_w")
+    cs_in = _f64(conv_state_in, (Bsz, K - 1, D))
+    cs_out = np.zeros((Bsz, max(K - 1, 0), D), np.float64) if return_conv_state else None
     y = np.zeros((Bsz, L, D), np.float64)
     hf = np.zeros((Bsz, D, N), np.float64)
     rc = _load().oracle_selective_scan_f64(
         Bsz, L, D, N, _ptr(x), _ptr(delta), _ptr(A), _ptr(Bm), _ptr(Cm), _ptr(Dskip),
         _ptr(z), _ptr(delta_bias), int(bool(delta_softplus)), _ptr(conv_w), _ptr(conv_b), K,
-        _ptr(h0), _ptr(y), _ptr(hf), int(nthreads or default_threads()))
+        _ptr(cs_in), _ptr(cs_out), _ptr(h0), _ptr(y), _ptr(hf), int(nthreads or default_threads()))
     if rc != 0:
         raise ValueError("oracle_selective_scan_f64 rejected the sizes")
-    return y, hf
+    return (y, hf, cs_out) if return_conv_state else (y, hf)
 
 
 def causal_conv1d_silu(x, w, bias=None, nthreads: Optional[int] = None):
@@ -137,10 +144,14 @@ def causal_conv1d_silu(x, w, bias=None, nthreads: Optional[int] = None):
 
 
 def state_update(state, x, delta, A, Bm, Cm, Dskip=None, z=None, delta_bias=None,
-                 delta_softplus: bool = False, nthreads: Optional[int] = None):
-    """One decode step.  Returns (y, new_state); the input state is not modified.
+                 delta_softplus: bool = False, conv_w=None, conv_b=None, conv_state=None,
+                 nthreads: Optional[int] = None):
+    """One decode step.  Returns (y, new_state), or with conv_w given
+    (y, new_state, new_conv_state); the inputs are not modified.
 
-    state: (B, D, N); x, delta, z: (B, D); A: (D, N); Bm, Cm: (B, N).
+    state: (B, D, N); x, delta, z: (B, D); A: (D, N); Bm, Cm: (B, N);
+    conv_w: (D, K); conv_b: (D,); conv_state: (B, K-1, D), the previous K-1
+    inputs, oldest first.
     """
     st = _f64(state).copy()
     Bsz, D, N = st.shape
@@ -152,11 +163,23 @@ def state_update(state, x, delta, A, Bm, Cm, Dskip=None, z=None, delta_bias=None
     Dskip = _f64(Dskip, (D,))
     z = _f64(z, (Bsz, D))
     delta_bias = _f64(delta_bias, (D,))
+    K = 0
+    cs = None
+    if conv_w is not None:
+        conv_w = _f64(conv_w)
+        K = conv_w.shape[1]
+        conv_w = _f64(conv_w, (D, K))
+        cs = (_f64(conv_state, (Bsz, K - 1, D)).copy() if conv_state is not None
+              else np.zeros((Bsz, K - 1, D), np.float64))
+    elif conv_state is not None or conv_b is not None:
+        raise ValueError("conv_state/conv_b need conv_w")
+    conv_b = _f64(conv_b, (D,))
     y = np.zeros((Bsz, D), np.float64)
     rc = _load().oracle_state_update_f64(Bsz, D, N, _ptr(st), _ptr(x), _ptr(delta), _ptr(A),
                                          _ptr(Bm), _ptr(Cm), _ptr(Dskip), _ptr(z),
-                                         _ptr(delta_bias), int(bool(delta_softplus)), _ptr(y),
+                                         _ptr(delta_bias), int(bool(delta_softplus)),
+                                         _ptr(conv_w), _ptr(conv_b), K, _ptr(cs), _ptr(y),
                                          int(nthreads or default_threads()))
     if rc != 0:
         raise ValueError("oracle_state_update_f64 rejected the sizes")
-    return y, st
+    return (y, st, cs) if conv_w is not None else (y, st)

@@ -31,6 +31,10 @@
  *   - the conv prologue is a causal cross-correlation with zero left padding:
  *     u_t = silu(sum_k w[k] x_{t-(K-1)+k} + b), so w[K-1] weighs the current
  *     token.
+ *   - the conv state carried between calls ([P2] keeps a state for inference)
+ *     is the last K-1 inputs x, oldest first, laid out (B, K-1, D); a scan
+ *     may start from one (the inputs before t = 0) and return the one after
+ *     its last step, and a decode step shifts it by one input.
  *
  * All arrays are row-major with the last index fastest, host memory, double.
  * Threads (OpenMP) split only independent (batch, channel) pairs.
@@ -63,20 +67,26 @@ static void zoh(double dt, double a, double b, double *abar, double *bbar)
     *bbar = phi * dt * b;
 }
 
-/* Causal depthwise conv1d(K) + SiLU on one channel's input at time t.
- * x points at element (b, 0, d); consecutive times are `stride` apart. */
-static double conv_silu_at(const double *x, int64_t stride, int64_t t, int64_t K,
-                           const double *wd, double bias)
+/* One channel's input at time s.  x points at element (b, 0, d), times are
+ * `stride` apart.  Times before 0 come from hist, the K-1 inputs before the
+ * sequence (oldest first, also `stride` apart), or are 0 without it. */
+static double x_at(const double *x, const double *hist, int64_t stride, int64_t s, int64_t K)
+{
+    if (s >= 0) return x[s * stride];
+    if (hist && s >= -(K - 1)) return hist[(K - 1 + s) * stride];
+    return 0.0;
+}
+
+/* Causal depthwise conv1d(K) + SiLU on one channel's input at time t. */
+static double conv_silu_at(const double *x, const double *hist, int64_t stride, int64_t t,
+                           int64_t K, const double *wd, double bias)
 {
     double acc = bias;
-    for (int64_t k = 0; k < K; ++k) {
-        int64_t s = t - (K - 1) + k;
-        if (s >= 0) acc += wd[k] * x[s * stride];
-    }
+    for (int64_t k = 0; k < K; ++k) acc += wd[k] * x_at(x, hist, stride, t - (K - 1) + k, K);
     return silu(acc);
 }
 
-int oracle_abi_version(void) { return 1; }
+int oracle_abi_version(void) { return 2; }
 
 /*
  * Selective scan forward ([P1] Algorithm 2 with the block's gate and the
@@ -87,7 +97,9 @@ int oracle_abi_version(void) { return 1; }
  *   y_t   = (sum_n C_t,n h_t,n + Dskip u_t) * silu(z_t)             ([P1] eq. 2b, 4a)
  *
  * Shapes: x, delta, z, y (B,L,D); A (D,N); Bm, Cm (B,L,N); Dskip, delta_bias,
- * conv_b (D); conv_w (D,K); h0, h_final (B,D,N).  Optional inputs may be NULL.
+ * conv_b (D); conv_w (D,K); h0, h_final (B,D,N); conv_state_in and
+ * conv_state_out (B,K-1,D): the inputs before t = 0 and the last K-1 inputs
+ * (earlier than t = 0 where L < K-1).  Optional arguments may be NULL.
  * Returns 0, or -1 on a bad size.
  */
 int oracle_selective_scan_f64(int64_t Bsz, int64_t L, int64_t D, int64_t N,
@@ -95,6 +107,7 @@ int oracle_selective_scan_f64(int64_t Bsz, int64_t L, int64_t D, int64_t N,
                               const double *Bm, const double *Cm, const double *Dskip,
                               const double *z, const double *delta_bias, int delta_softplus,
                               const double *conv_w, const double *conv_b, int64_t conv_k,
+                              const double *conv_state_in, double *conv_state_out,
                               const double *h0, double *y, double *h_final, int nthreads)
 {
     if (Bsz < 0 || L < 0 || D < 0 || N < 1 || (conv_w && conv_k < 1)) return -1;
@@ -106,9 +119,10 @@ int oracle_selective_scan_f64(int64_t Bsz, int64_t L, int64_t D, int64_t N,
         double *h = (double *)malloc(sizeof(double) * (size_t)N);
         for (int64_t n = 0; n < N; ++n) h[n] = h0 ? h0[(b * D + d) * N + n] : 0.0;
         const double *xbd = x + b * L * D + d;
+        const double *hist = conv_state_in ? conv_state_in + b * (conv_k - 1) * D + d : NULL;
         for (int64_t t = 0; t < L; ++t) {
             int64_t i = (b * L + t) * D + d;
-            double u = conv_w ? conv_silu_at(xbd, D, t, conv_k, conv_w + d * conv_k,
+            double u = conv_w ? conv_silu_at(xbd, hist, D, t, conv_k, conv_w + d * conv_k,
                                              conv_b ? conv_b[d] : 0.0)
                               : x[i];
             double dt = delta[i];
@@ -126,6 +140,10 @@ int oracle_selective_scan_f64(int64_t Bsz, int64_t L, int64_t D, int64_t N,
         }
         if (h_final)
             for (int64_t n = 0; n < N; ++n) h_final[(b * D + d) * N + n] = h[n];
+        if (conv_state_out)
+            for (int64_t k = 0; k < conv_k - 1; ++k)
+                conv_state_out[(b * (conv_k - 1) + k) * D + d] =
+                    x_at(xbd, hist, D, L - (conv_k - 1) + k, conv_k);
         free(h);
     }
     return 0;
@@ -148,7 +166,7 @@ int oracle_causal_conv1d_silu_f64(int64_t Bsz, int64_t L, int64_t D, int64_t K,
         int64_t b = ch / D, d = ch % D;
         const double *xbd = x + b * L * D + d;
         for (int64_t t = 0; t < L; ++t)
-            u[(b * L + t) * D + d] = conv_silu_at(xbd, D, t, K, w + d * K, bias ? bias[d] : 0.0);
+            u[(b * L + t) * D + d] = conv_silu_at(xbd, NULL, D, t, K, w + d * K, bias ? bias[d] : 0.0);
     }
     return 0;
 }
@@ -157,23 +175,39 @@ int oracle_causal_conv1d_silu_f64(int64_t Bsz, int64_t L, int64_t D, int64_t K,
  * One recurrent (decode) step ([P1] eq. (2a)/(2b) used as a recurrence, one
  * token at a time, with the state carried between calls as in [P2]'s
  * ssm_state option):
- *   state[b,d,n] <- Abar state[b,d,n] + Bbar x[b,d]     (eq. 4 per n)
- *   y[b,d]        = (sum_n C[b,n] state[b,d,n] + Dskip[d] x[b,d]) * silu(z[b,d])
- * state (B,D,N) is updated in place; x, delta, z, y (B,D); Bm, Cm (B,N).
+ *   u             = x[b,d], or with conv_w the prologue of [P1] sec. 4a on the
+ *                   window (conv_state[b,0..K-2,d], x[b,d]), after which the
+ *                   window drops its oldest input and appends x[b,d]
+ *   state[b,d,n] <- Abar state[b,d,n] + Bbar u           (eq. 4 per n)
+ *   y[b,d]        = (sum_n C[b,n] state[b,d,n] + Dskip[d] u) * silu(z[b,d])
+ * state (B,D,N) and conv_state (B,K-1,D) are updated in place; x, delta, z,
+ * y (B,D); Bm, Cm (B,N); conv_w (D,K); conv_b (D).
  */
 int oracle_state_update_f64(int64_t Bsz, int64_t D, int64_t N, double *state,
                             const double *x, const double *delta, const double *A,
                             const double *Bm, const double *Cm, const double *Dskip,
                             const double *z, const double *delta_bias, int delta_softplus,
-                            double *y, int nthreads)
+                            const double *conv_w, const double *conv_b, int64_t conv_k,
+                            double *conv_state, double *y, int nthreads)
 {
-    if (Bsz < 0 || D < 0 || N < 1) return -1;
+    if (Bsz < 0 || D < 0 || N < 1 || (conv_w && conv_k < 1) || (conv_w && conv_k > 1 && !conv_state))
+        return -1;
     if (nthreads < 1) nthreads = 1;
     int64_t nch = Bsz * D;
 #pragma omp parallel for num_threads(nthreads) schedule(static)
     for (int64_t ch = 0; ch < nch; ++ch) {
         int64_t b = ch / D, d = ch % D;
         double u = x[ch];
+        if (conv_w) {
+            const double *wd = conv_w + d * conv_k;
+            double *win = conv_w && conv_k > 1 ? conv_state + b * (conv_k - 1) * D + d : NULL;
+            double acc = conv_b ? conv_b[d] : 0.0;
+            for (int64_t k = 0; k < conv_k - 1; ++k) acc += wd[k] * win[k * D];
+            acc += wd[conv_k - 1] * x[ch];
+            u = silu(acc);
+            for (int64_t k = 0; k + 1 < conv_k - 1; ++k) win[k * D] = win[(k + 1) * D];
+            if (conv_k > 1) win[(conv_k - 2) * D] = x[ch];
+        }
         double dt = delta[ch];
         if (delta_softplus) dt = softplus(dt + (delta_bias ? delta_bias[d] : 0.0));
         double *h = state + ch * N;

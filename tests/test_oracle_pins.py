@@ -367,6 +367,93 @@ def test_fused_conv_equals_conv_then_scan():
     np.testing.assert_allclose(h1, h2, rtol=1e-15, atol=1e-15)
 
 
+# ------------------------------- conv state carried between calls (f1)
+def _with_history(rng, K, B=2, L=13, D=3, N=4):
+    p = _rand_problem(rng, B=B, L=L, D=D, N=N)
+    w = 0.5 * rng.standard_normal((D, K))
+    cb = rng.standard_normal(D)
+    hist = rng.standard_normal((B, K - 1, D))
+    return p, w, cb, hist
+
+
+@pytest.mark.parametrize("K", [2, 3, 4])
+def test_conv_history_matches_torch_conv1d_on_concatenation(K):
+    """A scan entering with a conv state: the K-1 inputs before t = 0 take the place
+    of the zero padding of [P1] sec. 4a's causal conv.  Checked against torch conv1d
+    on the concatenated sequence (history, then x), whose last L outputs feed a scan
+    without prologue."""
+    rng = RNG(40 + K)
+    p, w, cb, hist = _with_history(rng, K)
+    y1, h1 = oracle.selective_scan(**p, conv_w=w, conv_b=cb, conv_state_in=hist)
+    xx = np.concatenate([hist, p["x"]], axis=1)
+    xt = torch.tensor(xx).transpose(1, 2)
+    u = torch.nn.functional.conv1d(xt, torch.tensor(w)[:, None, :], torch.tensor(cb),
+                                   padding=K - 1, groups=3)[..., K - 1:K - 1 + 13]
+    u = torch.nn.functional.silu(u).transpose(1, 2).numpy()
+    q = dict(p)
+    q["x"] = u
+    y2, h2 = oracle.selective_scan(**q)
+    np.testing.assert_allclose(y1, y2, rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(h1, h2, rtol=1e-13, atol=1e-13)
+
+
+@pytest.mark.parametrize("K,L", [(1, 5), (2, 0), (2, 7), (4, 0), (4, 1), (4, 2), (4, 3), (4, 17)])
+def test_conv_state_out_is_the_last_inputs(K, L):
+    """The conv state after a scan is its last K-1 inputs, reaching back into the
+    entering state when L < K-1 (numpy slicing of the concatenated inputs)."""
+    rng = RNG(50 + 10 * K + L)
+    p, w, cb, hist = _with_history(rng, K, L=L)
+    for h in (hist, None):
+        _, _, cs = oracle.selective_scan(**p, conv_w=w, conv_b=cb, conv_state_in=h,
+                                         return_conv_state=True)
+        prev = h if h is not None else np.zeros_like(hist)
+        ref = np.concatenate([prev, p["x"]], axis=1)[:, prev.shape[1] + L - (K - 1):]
+        assert cs.shape == (2, K - 1, 3)
+        assert np.array_equal(cs, ref)
+
+
+@pytest.mark.parametrize("K", [1, 2, 4])
+def test_decode_with_conv_state_equals_scan(K):
+    """Decode with the conv state of [P2] (a rolling window of the last K-1 inputs):
+    40 steps reproduce a scan over the same 40 tokens that enters with the same conv
+    state and h0 -- every y, the final h and the final window."""
+    rng = RNG(60 + K)
+    p, w, cb, hist = _with_history(rng, K, B=3, L=40, D=5, N=4)
+    y, hf, cs_ref = oracle.selective_scan(**p, conv_w=w, conv_b=cb, conv_state_in=hist,
+                                          return_conv_state=True)
+    st, cs = p["h0"].copy(), hist.copy()
+    for t in range(40):
+        yt, st, cs = oracle.state_update(st, p["x"][:, t], p["delta"][:, t], p["A"],
+                                         p["Bm"][:, t], p["Cm"][:, t], Dskip=p["Dskip"],
+                                         z=p["z"][:, t], conv_w=w, conv_b=cb, conv_state=cs)
+        np.testing.assert_allclose(yt, y[:, t], rtol=1e-14, atol=1e-14)
+    np.testing.assert_allclose(st, hf, rtol=1e-14, atol=1e-14)
+    assert np.array_equal(cs, cs_ref)
+
+
+@pytest.mark.parametrize("split", [1, 2, 3, 9])
+def test_chunked_prefill_hands_over_conv_state(split):
+    """Chunked prefill: a scan over [0, s) returning (h, conv state), then a scan over
+    [s, L) entering with both, equals one scan over [0, L) -- bit for bit, since the
+    second chunk's conv reads the same inputs from the handed-over state."""
+    rng = RNG(70 + split)
+    K = 4
+    p, w, cb, hist = _with_history(rng, K, L=14)
+    seq = ("x", "delta", "Bm", "Cm", "z")
+    y, hf, cs = oracle.selective_scan(**p, conv_w=w, conv_b=cb, conv_state_in=hist,
+                                      return_conv_state=True)
+    a = {k: (v[:, :split] if k in seq else v) for k, v in p.items()}
+    ya, ha, csa = oracle.selective_scan(**a, conv_w=w, conv_b=cb, conv_state_in=hist,
+                                        return_conv_state=True)
+    b = {k: (v[:, split:] if k in seq else v) for k, v in p.items()}
+    b["h0"] = ha
+    yb, hb, csb = oracle.selective_scan(**b, conv_w=w, conv_b=cb, conv_state_in=csa,
+                                        return_conv_state=True)
+    assert np.array_equal(np.concatenate([ya, yb], axis=1), y)
+    assert np.array_equal(hb, hf)
+    assert np.array_equal(csb, cs)
+
+
 def test_gate_is_silu_of_z():
     """[P1] sec. 4a: the SSM output is multiplied by SiLU(gate); torch silu in float64."""
     rng = RNG(16)
