@@ -54,10 +54,12 @@ def scan_algorithmic_bytes(B, L, D, N, io_bytes, conv_k=0, final_state=False, h0
     return total
 
 
-def decode_algorithmic_bytes(B, D, N, io_bytes, gate=True, skip=True):
-    """One decode step: state read + written, x, delta, (z) read, y written, B/C rows, A, D."""
+def decode_algorithmic_bytes(B, D, N, io_bytes, gate=True, skip=True, conv_k=0):
+    """One decode step: state read + written, x, delta, (z) read, y written, B/C rows, A, D;
+    with a conv window also the window read + written and the conv weights and bias."""
+    conv = (2 * (conv_k - 1) * io_bytes * B * D + 4 * D * conv_k + 4 * D) if conv_k else 0
     return (8 * B * D * N + (3 + (1 if gate else 0)) * io_bytes * B * D + 2 * B * N * io_bytes
-            + 4 * D * N + (4 * D if skip else 0))
+            + 4 * D * N + (4 * D if skip else 0) + conv)
 
 
 def _load_metric():
@@ -127,7 +129,9 @@ def bench_scan(cfg, steps, warmup, nsets=3, final_state=False):
     return ms, nbytes, first
 
 
-def bench_decode(cfg, reps=3):
+def bench_decode(cfg, reps=3, conv_k=0):
+    """Decode steps of `cfg`; with conv_k, each step also runs the conv prologue on
+    its (B, conv_k-1, D) window and shifts it (weights N(0, 0.5), seeded)."""
     import torch
     import selective_state_space_59_amd as ssm
     from selective_state_space_59_amd import workloads as W
@@ -135,11 +139,18 @@ def bench_decode(cfg, reps=3):
     inp = W.make_decode_config_inputs(cfg, device=dev)
     st = inp["state0"].clone()
     ys = torch.empty(cfg.steps, cfg.batch, cfg.dim, dtype=cfg.io_dtype, device=dev)
+    conv = {}
+    if conv_k:
+        g = torch.Generator(dev).manual_seed(cfg.seed + 50)
+        conv = dict(conv_w=0.5 * torch.randn(cfg.dim, conv_k, device=dev, generator=g),
+                    conv_b=torch.randn(cfg.dim, device=dev, generator=g),
+                    conv_state=torch.randn(cfg.batch, conv_k - 1, cfg.dim, device=dev,
+                                           generator=g).to(cfg.io_dtype))
 
     def run_all(_):
         for t in range(cfg.steps):
             ssm.state_update(st, inp["x"][t], inp["delta"][t], inp["A"], inp["Bm"][t],
-                             inp["Cm"][t], Dskip=inp["Dskip"], z=inp["z"][t], y=ys[t])
+                             inp["Cm"][t], Dskip=inp["Dskip"], z=inp["z"][t], y=ys[t], **conv)
 
     hot_ms = time_launches(run_all, reps, 1) / cfg.steps
     # Cold: evict the last-level cache (write 1 GiB) before each timed step.
@@ -151,15 +162,15 @@ def bench_decode(cfg, reps=3):
         flush.fill_(float(t))
         start.record()
         ssm.state_update(st, inp["x"][t], inp["delta"][t], inp["A"], inp["Bm"][t],
-                         inp["Cm"][t], Dskip=inp["Dskip"], z=inp["z"][t], y=ys[t])
+                         inp["Cm"][t], Dskip=inp["Dskip"], z=inp["z"][t], y=ys[t], **conv)
         stop.record()
         torch.cuda.synchronize()
         cold.append(start.elapsed_time(stop))
     cold.sort()
     cold_ms = cold[len(cold) // 2]
     nbytes = decode_algorithmic_bytes(cfg.batch, cfg.dim, cfg.dstate,
-                                      2 if cfg.io_dtype == torch.bfloat16 else 4)
-    del inp, st, ys, flush
+                                      2 if cfg.io_dtype == torch.bfloat16 else 4, conv_k=conv_k)
+    del inp, st, ys, flush, conv
     torch.cuda.empty_cache()
     return hot_ms, cold_ms, nbytes
 
@@ -271,14 +282,17 @@ def main():
                                  frac_hbm=round(cb / (cms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                                  elems_per_s=round(c.elems / (cms * 1e-3), 1),
                                  algorithmic_bytes=cb)
-        print("bench extra: %s" % W.C5_DECODE.name, file=sys.stderr, flush=True)
-        hot, cold, db = bench_decode(W.C5_DECODE)
-        extra[W.C5_DECODE.name] = dict(
-            hot_ms_per_step=round(hot, 5), cold_ms_per_step=round(cold, 5),
-            hot_steps_per_s=round(1e3 / hot, 1), cold_steps_per_s=round(1e3 / cold, 1),
-            cold_gbs=round(db / (cold * 1e-3) / 1e9, 2),
-            cold_frac_hbm=round(db / (cold * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-            hot_gbs=round(db / (hot * 1e-3) / 1e9, 2), algorithmic_bytes_per_step=db)
+        # the decode config, and the same with the d_conv = 4 window of the
+        # prefill -> decode handoff
+        for name, k in ((W.C5_DECODE.name, 0), (W.C5_DECODE.name + "_conv4_window", 4)):
+            print("bench extra: %s" % name, file=sys.stderr, flush=True)
+            hot, cold, db = bench_decode(W.C5_DECODE, conv_k=k)
+            extra[name] = dict(
+                hot_ms_per_step=round(hot, 5), cold_ms_per_step=round(cold, 5),
+                hot_steps_per_s=round(1e3 / hot, 1), cold_steps_per_s=round(1e3 / cold, 1),
+                cold_gbs=round(db / (cold * 1e-3) / 1e9, 2),
+                cold_frac_hbm=round(db / (cold * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                hot_gbs=round(db / (hot * 1e-3) / 1e9, 2), algorithmic_bytes_per_step=db)
         out["extra"] = extra
 
     if not args.no_cpu_baseline:

@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define SSM_ABI_VERSION 1
+#define SSM_ABI_VERSION 2
 #define SSM_MAX_DSTATE 16 /* largest N the kernels hold in registers */
 #define SSM_MAX_CONV_K 4  /* largest conv1d kernel width */
 
@@ -84,7 +84,8 @@ typedef enum ssm_dtype {
  *
  *   u[b,t,d]   = x[b,t,d], or, when conv_w != NULL, the fused prologue
  *                silu(sum_{k<K} conv_w[d,k] x[b,t-(K-1)+k,d] + conv_b[d])
- *                with x at negative times taken as 0 ([P1] sec. 4a, [P2]).
+ *                ([P1] sec. 4a, [P2] d_conv), where x at negative times
+ *                comes from conv_state_in, or is 0 without it.
  *   dt[b,t,d]  = delta[b,t,d], or softplus(delta[b,t,d] + delta_bias[d])
  *                when delta_softplus != 0 ([P1] Algorithm 2).
  *   Abar       = exp(dt A[d,n])                                 (eq. 4)
@@ -94,6 +95,15 @@ typedef enum ssm_dtype {
  *   y[b,t,d]   = (sum_n Cm[b,t,n] h[b,d,n] + Dskip[d] u[b,t,d])
  *                * silu(z[b,t,d])                               (eq. 2b, 4a)
  *   h_final    = h after the last time step.
+ *
+ * Conv state (the prefill -> decode handoff of the conv window, kept between
+ * inference calls like the SSM state of [P2]): a (B, K-1, D) io_dtype tensor
+ * holding, for every batch row and channel, the K-1 most recent inputs x,
+ * oldest first (row k is time -(K-1)+k relative to the next token).
+ * conv_state_in gives x at times -(K-1)..-1 of this call; conv_state_out
+ * receives x at times L-(K-1)..L-1 (from conv_state_in, or 0, where that time
+ * is negative), which is the window ssm_state_update expects for the next
+ * token.  Both are raw copies of the inputs, bit for bit.
  */
 typedef struct ssm_scan_args {
     int64_t batch;          /* B >= 0                                         */
@@ -118,6 +128,9 @@ typedef struct ssm_scan_args {
     float *h_final;         /* (B,D,N) fp32 output, or NULL (not written)     */
     void *workspace;        /* device scratch of workspace_bytes, 256-aligned */
     size_t workspace_bytes; /* >= ssm_selective_scan_workspace_size(args)     */
+    const void *conv_state_in; /* (B,K-1,D) io_dtype, or NULL (= 0); only with conv_k > 0 */
+    void *conv_state_out;   /* (B,K-1,D) io_dtype output, or NULL; only with conv_k > 0;
+                               may be exactly conv_state_in (updated in place)    */
 } ssm_scan_args_t;
 
 /*
@@ -134,7 +147,9 @@ size_t ssm_selective_scan_workspace_size(const ssm_scan_args_t *args);
  * Enqueue the selective scan described above on `stream`.
  * y must not overlap any input; h_final must not overlap any input or y.
  * h0 may be NULL; when given it may not overlap h_final (copy first to scan
- * in place).  Returns SSM_OK or an error status (see the conventions).
+ * in place).  conv_state_out must not overlap any other argument except that
+ * it may be the same tensor as conv_state_in.  Returns SSM_OK or an error
+ * status (see the conventions).
  */
 ssm_status_t ssm_selective_scan_fwd(const ssm_scan_args_t *args, void *stream);
 
@@ -153,10 +168,17 @@ ssm_status_t ssm_causal_conv1d_silu(int64_t batch, int64_t seqlen, int64_t dim, 
 /*
  * One decode step, [P1] eq. (2a)/(2b) in recurrent mode on a state kept
  * between calls ([P2] ssm_state), for every batch row b and channel d:
+ *   u           = x[b,d], or with conv_k > 0 the prologue of [P1] sec. 4a on
+ *                 the window (conv_state[b,0..K-2,d], x[b,d]):
+ *                 silu(sum_{k<K-1} conv_w[d,k] conv_state[b,k,d]
+ *                      + conv_w[d,K-1] x[b,d] + conv_b[d]);
+ *                 the window then drops its oldest row and appends x[b,d]
  *   dt          = delta[b,d] or softplus(delta[b,d] + delta_bias[d])
- *   state[b,d,n] <- exp(dt A[d,n]) state[b,d,n] + Bbar(dt, A[d,n], Bm[b,n]) x[b,d]
- *   y[b,d]      = (sum_n Cm[b,n] state[b,d,n] + Dskip[d] x[b,d]) * silu(z[b,d])
- * with Bbar as in the scan.  The state is read and written IN PLACE.
+ *   state[b,d,n] <- exp(dt A[d,n]) state[b,d,n] + Bbar(dt, A[d,n], Bm[b,n]) u
+ *   y[b,d]      = (sum_n Cm[b,n] state[b,d,n] + Dskip[d] u) * silu(z[b,d])
+ * with Bbar as in the scan.  The state and the conv state are read and
+ * written IN PLACE; the conv state has the layout of the scan's
+ * conv_state_out, so a prefill hands over to decode directly.
  */
 typedef struct ssm_state_update_args {
     int64_t batch;          /* B >= 0                                     */
@@ -174,6 +196,11 @@ typedef struct ssm_state_update_args {
     const float *Dskip;     /* (D) fp32, or NULL                          */
     const float *delta_bias;/* (D) fp32, or NULL                          */
     void *y;                /* (B,D) io_dtype output; must not overlap any input or the state */
+    int64_t conv_k;         /* 0: no prologue; 1..SSM_MAX_CONV_K: causal conv1d + SiLU on x */
+    const float *conv_w;    /* (D,conv_k) fp32; required iff conv_k > 0   */
+    const float *conv_b;    /* (D) fp32, or NULL (= 0)                    */
+    void *conv_state;       /* (B,conv_k-1,D) io_dtype, updated in place; required iff
+                               conv_k > 1; must not overlap any other argument */
 } ssm_state_update_args_t;
 
 ssm_status_t ssm_state_update(const ssm_state_update_args_t *args, void *stream);

@@ -85,6 +85,7 @@ struct ScanKernelParams {
     const void *x, *delta, *Bm, *Cm, *z;
     const float *A, *Dskip, *dbias, *conv_w, *conv_b;
     const float *h_in;  // state entering row t_begin, or NULL (= 0)
+    const void *cs_in;  // conv state (B, K-1, D): x before row 0, or NULL (= 0)
     void *y;
     float *h_out;       // state after row t_end - 1, or NULL
     // Sequence segments (see launch_segmented): mode 0 scans [t_begin, t_end)
@@ -941,12 +942,16 @@ void scan_tiles_kernel(ScanKernelParams p) {
     cy.h = (live && h_in) ? h_in[(b * D + d) * N + n] : 0.0f;
     cy.scum = 0.0f;
     cy.head = -1;
-    // Conv history entering the rows: x at rows t_begin - 16 + n (only the
-    // last three lanes of a row are used).
+    // Conv history entering the rows: x at rows t0 - 16 + n (only the last
+    // three lanes of a row are used); before row 0 it comes from the
+    // entering conv state, or is 0.
     cy.x_prev = 0.0f;
-    if (CONV && sp.t0 > 0 && dvalid && n >= kRow - 3) {
+    if (CONV && dvalid && n >= kRow - 3) {
         const int64_t t = sp.t0 - kRow + n;
-        cy.x_prev = t >= 0 ? load_io<IO>(p.x, (b * p.L + t) * D + d) : 0.0f;
+        if (t >= 0)
+            cy.x_prev = load_io<IO>(p.x, (b * p.L + t) * D + d);
+        else if (p.cs_in && t >= -(int64_t)(p.K - 1))
+            cy.x_prev = load_io<IO>(p.cs_in, (b * (p.K - 1) + (p.K - 1) + t) * D + d);
     }
     // Wave-uniform choice of the update form (see the file comment).
     const bool fast = __all(!live || fabsf(k.a) >= kFastMinAbsA);
@@ -996,6 +1001,45 @@ __global__ void seg_combine_kernel(const float *A, const float *hend, const floa
         h = __builtin_amdgcn_exp2f(a2 * stot[s * B * D + bd]) * h + hend[s * BDN + i];
     }
     if (h_final) h_final[i] = h;
+}
+
+// Conv state after the scan, per (batch, channel): x at rows L-(K-1)..L-1,
+// from the entering conv state (or 0) where the row is negative.  Raw bit
+// copies; each thread reads its whole window before writing, so the state
+// may be updated in place.
+template <typename T>
+__global__ void conv_state_out_kernel(const T *x, const T *cs_in, T *cs_out, int64_t B, int64_t L,
+                                      int64_t D, int K) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // b * D + d
+    if (i >= B * D) return;
+    const int64_t b = i / D, d = i % D;
+    T v[SSM_MAX_CONV_K - 1];
+#pragma unroll
+    for (int k = 0; k < SSM_MAX_CONV_K - 1; ++k) {
+        if (k >= K - 1) break;
+        const int64_t t = L - (K - 1) + k;
+        v[k] = t >= 0 ? x[(b * L + t) * D + d] : cs_in ? cs_in[(b * (K - 1) + (K - 1) + t) * D + d] : T(0);
+    }
+#pragma unroll
+    for (int k = 0; k < SSM_MAX_CONV_K - 1; ++k) {
+        if (k >= K - 1) break;
+        cs_out[(b * (K - 1) + k) * D + d] = v[k];
+    }
+}
+
+hipError_t launch_conv_state_out(const ssm_scan_args_t &a, hipStream_t stream) {
+    if (!a.conv_state_out || a.conv_k < 2 || a.batch == 0) return hipSuccess;
+    const int64_t n = a.batch * a.dim;
+    const unsigned blocks = (unsigned)((n + 255) / 256);
+    if (a.io_dtype == SSM_BF16)
+        conv_state_out_kernel<uint16_t><<<blocks, 256, 0, stream>>>(
+            static_cast<const uint16_t *>(a.x), static_cast<const uint16_t *>(a.conv_state_in),
+            static_cast<uint16_t *>(a.conv_state_out), a.batch, a.seqlen, a.dim, (int)a.conv_k);
+    else
+        conv_state_out_kernel<uint32_t><<<blocks, 256, 0, stream>>>(
+            static_cast<const uint32_t *>(a.x), static_cast<const uint32_t *>(a.conv_state_in),
+            static_cast<uint32_t *>(a.conv_state_out), a.batch, a.seqlen, a.dim, (int)a.conv_k);
+    return hipGetLastError();
 }
 
 __global__ void copy_or_zero_kernel(const float *src, float *dst, int64_t n) {
@@ -1164,6 +1208,7 @@ hipError_t launch_scan_fwd(const ssm_scan_args_t &a, hipStream_t stream) {
     p.dbias = a.delta_bias;
     p.conv_w = a.conv_w;
     p.conv_b = a.conv_b;
+    p.cs_in = a.conv_k > 0 ? a.conv_state_in : nullptr;
     p.y = a.y;
     p.mode = 0;
     p.nseg = 1;
@@ -1201,15 +1246,20 @@ hipError_t launch_scan_fwd(const ssm_scan_args_t &a, hipStream_t stream) {
         p.mode = 2;
         e = launch_pass(a, p, q, stream);
     }
+    // The conv state is written after every pass has read the entering one
+    // (it may be the same tensor).
+    if (e == hipSuccess) e = launch_conv_state_out(a, stream);
     return e;
 }
 
 hipError_t launch_empty_scan_state(const ssm_scan_args_t &a, hipStream_t stream) {
-    if (!a.h_final) return hipSuccess;
     const int64_t n = a.batch * a.dim * a.dstate;
-    if (n == 0) return hipSuccess;
-    copy_or_zero_kernel<<<(unsigned)((n + 255) / 256), 256, 0, stream>>>(a.h0, a.h_final, n);
-    return hipGetLastError();
+    if (a.h_final && n > 0) {
+        copy_or_zero_kernel<<<(unsigned)((n + 255) / 256), 256, 0, stream>>>(a.h0, a.h_final, n);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return launch_conv_state_out(a, stream);
 }
 
 }  // namespace ssm

@@ -123,15 +123,18 @@ ssm_status_t ssm_selective_scan_fwd(const ssm_scan_args_t *a, void *stream) {
         if (!a->y) return fail(SSM_ERR_NULL_ARG, "y is NULL");
         if (K > 0 && !a->conv_w) return fail(SSM_ERR_NULL_ARG, "conv_w is NULL but conv_k > 0");
     }
-    if (K == 0 && (a->conv_w || a->conv_b))
-        return fail(SSM_ERR_BAD_SHAPE, "conv_w/conv_b given but conv_k == 0");
-    const void *io_ptrs[] = {a->x, a->delta, a->Bm, a->Cm, a->z, a->y};
+    if (K == 0 && (a->conv_w || a->conv_b || a->conv_state_in || a->conv_state_out))
+        return fail(SSM_ERR_BAD_SHAPE, "conv_w/conv_b/conv state given but conv_k == 0");
+    const void *io_ptrs[] = {a->x, a->delta, a->Bm, a->Cm, a->z, a->y, a->conv_state_in,
+                             a->conv_state_out};
     for (const void *p : io_ptrs)
         if (!aligned(p, es)) return fail(SSM_ERR_ALIGN, "an io_dtype pointer is not %lld-byte aligned", (long long)es);
     const void *f_ptrs[] = {a->A, a->Dskip, a->delta_bias, a->conv_w, a->conv_b, a->h0, a->h_final};
     for (const void *p : f_ptrs)
         if (!aligned(p, 4)) return fail(SSM_ERR_ALIGN, "an fp32 pointer is not 4-byte aligned");
 
+    const int64_t csn = B * (K > 0 ? K - 1 : 0) * D;  // elements of a conv state
+    const Range csi = range(a->conv_state_in, csn, es, "conv_state_in");
     const Range inputs[] = {
         range(a->x, B * L * D, es, "x"),          range(a->delta, B * L * D, es, "delta"),
         range(a->Bm, B * L * N, es, "Bm"),        range(a->Cm, B * L * N, es, "Cm"),
@@ -139,14 +142,21 @@ ssm_status_t ssm_selective_scan_fwd(const ssm_scan_args_t *a, void *stream) {
         range(a->Dskip, D, 4, "Dskip"),           range(a->delta_bias, D, 4, "delta_bias"),
         range(a->conv_w, D * K, 4, "conv_w"),     range(a->conv_b, D, 4, "conv_b"),
         range(a->h0, B * D * N, 4, "h0"),
+        csi,
     };
     const Range y = range(a->y, B * L * D, es, "y");
     const Range hf = range(a->h_final, B * D * N, 4, "h_final");
+    const Range cso = range(a->conv_state_out, csn, es, "conv_state_out");
+    // The conv state may be updated in place (the same tensor in and out).
+    const bool cs_in_place = a->conv_state_out != nullptr && a->conv_state_out == a->conv_state_in;
     for (const Range &r : inputs) {
         if (overlaps(y, r)) return fail(SSM_ERR_ALIAS, "y overlaps %s", r.name);
         if (overlaps(hf, r)) return fail(SSM_ERR_ALIAS, "h_final overlaps %s", r.name);
+        if (!(cs_in_place && &r == &inputs[sizeof(inputs) / sizeof(inputs[0]) - 1]) && overlaps(cso, r))
+            return fail(SSM_ERR_ALIAS, "conv_state_out overlaps %s", r.name);
     }
     if (overlaps(y, hf)) return fail(SSM_ERR_ALIAS, "y overlaps h_final");
+    if (overlaps(cso, y) || overlaps(cso, hf)) return fail(SSM_ERR_ALIAS, "conv_state_out overlaps an output");
 
     const size_t need = work ? ssm::scan_workspace_bytes(*a) : 0;
     if (need > 0) {
@@ -157,7 +167,8 @@ ssm_status_t ssm_selective_scan_fwd(const ssm_scan_args_t *a, void *stream) {
         const Range ws = range(a->workspace, (int64_t)need, 1, "workspace");
         for (const Range &r : inputs)
             if (overlaps(ws, r)) return fail(SSM_ERR_ALIAS, "workspace overlaps %s", r.name);
-        if (overlaps(ws, y) || overlaps(ws, hf)) return fail(SSM_ERR_ALIAS, "workspace overlaps an output");
+        if (overlaps(ws, y) || overlaps(ws, hf) || overlaps(ws, cso))
+            return fail(SSM_ERR_ALIAS, "workspace overlaps an output");
     }
 
     hipStream_t st = static_cast<hipStream_t>(stream);
@@ -211,7 +222,12 @@ ssm_status_t ssm_state_update(const ssm_state_update_args_t *a, void *stream) {
     if (a->delta_softplus != 0 && a->delta_softplus != 1)
         return fail(SSM_ERR_UNSUPPORTED, "delta_softplus must be 0 or 1");
     if (!mul_ok(a->batch, a->dim, a->dstate)) return fail(SSM_ERR_BAD_SHAPE, "sizes overflow");
-    const int64_t B = a->batch, D = a->dim, N = a->dstate;
+    if (a->conv_k < 0) return fail(SSM_ERR_BAD_SHAPE, "conv_k must be >= 0");
+    if (a->conv_k > SSM_MAX_CONV_K)
+        return fail(SSM_ERR_UNSUPPORTED, "conv_k %lld exceeds SSM_MAX_CONV_K (%d)", (long long)a->conv_k, SSM_MAX_CONV_K);
+    if (a->conv_k == 0 && (a->conv_w || a->conv_b || a->conv_state))
+        return fail(SSM_ERR_BAD_SHAPE, "conv_w/conv_b/conv_state given but conv_k == 0");
+    const int64_t B = a->batch, D = a->dim, N = a->dstate, K = a->conv_k;
     const int64_t es = io_bytes(a->io_dtype);
     if (B == 0) return ok();
     if (!a->state) return fail(SSM_ERR_NULL_ARG, "state is NULL");
@@ -221,10 +237,12 @@ ssm_status_t ssm_state_update(const ssm_state_update_args_t *a, void *stream) {
     if (!a->Cm) return fail(SSM_ERR_NULL_ARG, "Cm is NULL");
     if (!a->A) return fail(SSM_ERR_NULL_ARG, "A is NULL");
     if (!a->y) return fail(SSM_ERR_NULL_ARG, "y is NULL");
-    const void *io_ptrs[] = {a->x, a->delta, a->z, a->Bm, a->Cm, a->y};
+    if (K > 0 && !a->conv_w) return fail(SSM_ERR_NULL_ARG, "conv_w is NULL but conv_k > 0");
+    if (K > 1 && !a->conv_state) return fail(SSM_ERR_NULL_ARG, "conv_state is NULL but conv_k > 1");
+    const void *io_ptrs[] = {a->x, a->delta, a->z, a->Bm, a->Cm, a->y, a->conv_state};
     for (const void *p : io_ptrs)
         if (!aligned(p, es)) return fail(SSM_ERR_ALIGN, "an io_dtype pointer is not %lld-byte aligned", (long long)es);
-    const void *f_ptrs[] = {a->state, a->A, a->Dskip, a->delta_bias};
+    const void *f_ptrs[] = {a->state, a->A, a->Dskip, a->delta_bias, a->conv_w, a->conv_b};
     for (const void *p : f_ptrs)
         if (!aligned(p, 4)) return fail(SSM_ERR_ALIGN, "an fp32 pointer is not 4-byte aligned");
     const Range st = range(a->state, B * D * N, 4, "state");
@@ -234,12 +252,16 @@ ssm_status_t ssm_state_update(const ssm_state_update_args_t *a, void *stream) {
         range(a->z, B * D, es, "z"),   range(a->Bm, B * N, es, "Bm"),
         range(a->Cm, B * N, es, "Cm"), range(a->A, D * N, 4, "A"),
         range(a->Dskip, D, 4, "Dskip"), range(a->delta_bias, D, 4, "delta_bias"),
+        range(a->conv_w, D * K, 4, "conv_w"), range(a->conv_b, D, 4, "conv_b"),
     };
+    const Range cs = range(K > 1 ? a->conv_state : nullptr, B * (K > 0 ? K - 1 : 0) * D, es, "conv_state");
     for (const Range &r : inputs) {
         if (overlaps(y, r)) return fail(SSM_ERR_ALIAS, "y overlaps %s", r.name);
         if (overlaps(st, r)) return fail(SSM_ERR_ALIAS, "state overlaps %s", r.name);
+        if (overlaps(cs, r)) return fail(SSM_ERR_ALIAS, "conv_state overlaps %s", r.name);
     }
     if (overlaps(y, st)) return fail(SSM_ERR_ALIAS, "y overlaps state");
+    if (overlaps(cs, y) || overlaps(cs, st)) return fail(SSM_ERR_ALIAS, "conv_state overlaps an output");
     hipError_t e = ssm::launch_state_update(*a, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(SSM_ERR_HIP, "HIP error: %s", hipGetErrorString(e));
     return ok();

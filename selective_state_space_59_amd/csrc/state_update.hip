@@ -5,7 +5,10 @@
 // the ZOH of eq. (4), the skip of "14.1 SSM(State Space Models)과 Mamba
 // 아키텍처의 부상" sec. 3.1 and the SiLU gate of sec. 4a, on a state kept
 // between tokens ("2. Mamba 상세": ssm_state):
-//   state[b,d,n] <- exp(dt A) state + Bbar x;   y = (sum_n C state + D x) silu(z)
+//   state[b,d,n] <- exp(dt A) state + Bbar u;   y = (sum_n C state + D u) silu(z)
+// with u = x, or, with a conv state (the last K-1 inputs of each channel),
+// the causal conv1d + SiLU prologue of sec. 4a on (window, x); the window
+// then drops its oldest input and appends x.
 //
 // HBM-bound: the fp32 state is read and written once; everything else is
 // small (x, delta, z, y per channel; B, C per batch row; A and D per channel,
@@ -33,12 +36,49 @@ constexpr int kQuartersPerThread = 2;
 
 struct UpdateParams {
     int64_t B, D;
-    int N, softplus;
+    int N, softplus, K;
     float *state;
     const void *x, *delta, *z, *Bm, *Cm;
-    const float *A, *Dskip, *dbias;
+    const float *A, *Dskip, *dbias, *conv_w, *conv_b;
+    void *cs;  // conv state (B, K-1, D), io type
     void *y;
 };
+
+// Conv prologue of channel (b, d), spread over the 4 lanes of its quad
+// (lane j = quarter index): with the taps right-aligned to width 4, lane j
+// holds tap j and input j, where input 3 is the current x and input j < 3
+// the one 3-j steps back (window row K-4+j; taps and rows below 0 are 0).
+// A quad sum gives every lane the conv output; the window shifts by one
+// with a quad permute (lane j takes lane j+1's input) and lanes 0..2 store
+// their rows.
+struct ConvLane {
+    float tap, win, bias;
+};
+template <typename IO>
+__device__ __forceinline__ ConvLane load_conv(const UpdateParams &p, int64_t b, int64_t d, int j) {
+    const int r = p.K - 4 + j;  // tap index = window row of this lane
+    ConvLane c;
+    c.tap = r >= 0 ? p.conv_w[d * p.K + r] : 0.0f;
+    c.win = (j < 3 && r >= 0) ? load_io<IO>(p.cs, (b * (p.K - 1) + r) * p.D + d) : 0.0f;
+    c.bias = (j == 3 && p.conv_b) ? p.conv_b[d] : 0.0f;
+    return c;
+}
+// Lane j's input: the window entry, or x on lane 3.
+__device__ __forceinline__ float conv_in(const ConvLane &c, int j, float x) { return j == 3 ? x : c.win; }
+__device__ __forceinline__ float quad_sum(float v);
+__device__ __forceinline__ float conv_u(const ConvLane &c, float v) {
+    return silu(quad_sum(__builtin_fmaf(c.tap, v, c.bias)));
+}
+// New window row of lane j (j < 3): lane j+1's input (exact: the values came
+// from I/O elements).  Every lane of the quad must call this.
+__device__ __forceinline__ float conv_shift(float v) {
+    return __builtin_amdgcn_update_dpp(0.0f, v, 0xF9, 0xf, 0xf, false);  // quad_perm [1,2,3,3]
+}
+template <typename IO>
+__device__ __forceinline__ void store_window(const UpdateParams &p, int64_t b, int64_t d, int j, float nv) {
+    const int r = p.K - 4 + j;
+    if (j < 3 && r >= 0) store_io<IO>(p.cs, (b * (p.K - 1) + r) * p.D + d, nv);
+}
 
 // phi(z) = (e^z - 1) / z given e = e^z.
 __device__ __forceinline__ float phi_of(float z, float e) {
@@ -77,6 +117,9 @@ __global__ __launch_bounds__(256) void state_update_vec_kernel(UpdateParams p, i
     const int64_t q0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     float4 st[K], av[K], bv[K], cv[K];
     float xv[K], dv[K], zv[K], dsk[K];
+    ConvLane cin[K];
+    int64_t bb_[K], dd_[K];
+    const int jq = (int)(threadIdx.x & 3);  // quarter of the channel (the stride keeps it)
     // All loads first.
 #pragma unroll
     for (int k = 0; k < K; ++k) {
@@ -100,6 +143,9 @@ __global__ __launch_bounds__(256) void state_update_vec_kernel(UpdateParams p, i
         zv[k] = p.z ? load_io<IO>(p.z, ch) : 0.0f;
         dsk[k] = p.Dskip ? p.Dskip[d] : 0.0f;
         if (p.softplus) dv[k] = softplus(dv[k] + (p.dbias ? p.dbias[d] : 0.0f));
+        bb_[k] = b;
+        dd_[k] = d;
+        if (p.K > 0) cin[k] = load_conv<IO>(p, b, d, jq);
     }
     bool big = true;
 #pragma unroll
@@ -110,7 +156,10 @@ __global__ __launch_bounds__(256) void state_update_vec_kernel(UpdateParams p, i
 #pragma unroll
     for (int k = 0; k < K; ++k) {
         const int64_t q = q0 + k * stride;
-        const float dt = dv[k], u = xv[k];
+        const float dt = dv[k];
+        const float vin = p.K > 0 ? conv_in(cin[k], jq, xv[k]) : 0.0f;
+        const float u = p.K > 0 ? conv_u(cin[k], vin) : xv[k];
+        const float nwin = p.K > 1 ? conv_shift(vin) : 0.0f;
         const float a[4] = {av[k].x, av[k].y, av[k].z, av[k].w};
         const float bb[4] = {bv[k].x, bv[k].y, bv[k].z, bv[k].w};
         const float cc[4] = {cv[k].x, cv[k].y, cv[k].z, cv[k].w};
@@ -135,6 +184,8 @@ __global__ __launch_bounds__(256) void state_update_vec_kernel(UpdateParams p, i
             __builtin_nontemporal_store(v, reinterpret_cast<f4v *>(p.state + (q >> 2) * SSM_MAX_DSTATE + 4 * (q & 3)));
         }
         acc = quad_sum(acc);
+        // The window was read above by every lane of the quad (loads first).
+        if (q < nq && p.K > 1) store_window<IO>(p, bb_[k], dd_[k], jq, nwin);
         if (q < nq && (q & 3) == 0) {
             float yv = acc + dsk[k] * u;
             if (p.z) yv *= silu(zv[k]);
@@ -157,7 +208,12 @@ __global__ __launch_bounds__(256) void state_update_kernel(UpdateParams p) {
 
     float dt = load_io<IO>(p.delta, chc);
     if (p.softplus) dt = softplus(dt + (p.dbias ? p.dbias[d] : 0.0f));
-    const float u = load_io<IO>(p.x, chc);
+    const float xin = load_io<IO>(p.x, chc);
+    ConvLane cin{0.0f, 0.0f, 0.0f};
+    if (p.K > 0) cin = load_conv<IO>(p, b, d, j);
+    const float vin = p.K > 0 ? conv_in(cin, j, xin) : 0.0f;
+    const float u = p.K > 0 ? conv_u(cin, vin) : xin;
+    const float nwin = p.K > 1 ? conv_shift(vin) : 0.0f;
 
     float hs[kPerLane];
     float *sp = p.state + chc * N + n0;
@@ -183,6 +239,7 @@ __global__ __launch_bounds__(256) void state_update_kernel(UpdateParams p) {
             if (n0 + k < N) sp[k] = hs[k];
     }
     acc = quad_sum(acc);
+    if (live && p.K > 1) store_window<IO>(p, b, d, j, nwin);
     if (live && j == 0) {
         float yv = acc + (p.Dskip ? p.Dskip[d] * u : 0.0f);
         if (p.z) yv *= silu(load_io<IO>(p.z, chc));
@@ -212,6 +269,10 @@ hipError_t launch_state_update(const ssm_state_update_args_t &a, hipStream_t str
     p.D = a.dim;
     p.N = (int)a.dstate;
     p.softplus = a.delta_softplus;
+    p.K = (int)a.conv_k;
+    p.conv_w = a.conv_w;
+    p.conv_b = a.conv_b;
+    p.cs = a.conv_state;
     p.state = a.state;
     p.x = a.x;
     p.delta = a.delta;

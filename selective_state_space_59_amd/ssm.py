@@ -49,7 +49,8 @@ class ScanArgs(ctypes.Structure):
                 ("x", _P), ("delta", _P), ("Bm", _P), ("Cm", _P), ("z", _P),
                 ("A", _P), ("Dskip", _P), ("delta_bias", _P), ("conv_w", _P), ("conv_b", _P),
                 ("h0", _P), ("y", _P), ("h_final", _P),
-                ("workspace", _P), ("workspace_bytes", ctypes.c_size_t)]
+                ("workspace", _P), ("workspace_bytes", ctypes.c_size_t),
+                ("conv_state_in", _P), ("conv_state_out", _P)]
 
 
 class StateUpdateArgs(ctypes.Structure):
@@ -57,7 +58,8 @@ class StateUpdateArgs(ctypes.Structure):
     _fields_ = [("batch", _I64), ("dim", _I64), ("dstate", _I64),
                 ("io_dtype", _I32), ("delta_softplus", _I32),
                 ("state", _P), ("x", _P), ("delta", _P), ("z", _P), ("Bm", _P), ("Cm", _P),
-                ("A", _P), ("Dskip", _P), ("delta_bias", _P), ("y", _P)]
+                ("A", _P), ("Dskip", _P), ("delta_bias", _P), ("y", _P),
+                ("conv_k", _I64), ("conv_w", _P), ("conv_b", _P), ("conv_state", _P)]
 
 
 class SSMError(RuntimeError):
@@ -148,7 +150,7 @@ def _stream(device: torch.device) -> int:
 
 
 def _scan_args(x, delta, A, Bm, Cm, Dskip, z, delta_bias, delta_softplus, conv_w, conv_b, h0,
-               y, h_final):
+               y, h_final, conv_state_in=None, conv_state_out=None):
     if not isinstance(x, torch.Tensor) or x.dim() != 3:
         raise ValueError("x must be a (B, L, D) tensor")
     if x.device.type != "cuda":
@@ -177,12 +179,17 @@ def _scan_args(x, delta, A, Bm, Cm, Dskip, z, delta_bias, delta_softplus, conv_w
     _opt(h0, "h0", (Bsz, D, N), torch.float32, dev)
     _req(y, "y", (Bsz, L, D), io, dev)
     _opt(h_final, "h_final", (Bsz, D, N), torch.float32, dev)
+    if (conv_state_in is not None or conv_state_out is not None) and K == 0:
+        raise ValueError("a conv state needs conv_w")
+    _opt(conv_state_in, "conv_state_in", (Bsz, max(K - 1, 0), D), io, dev)
+    _opt(conv_state_out, "conv_state_out", (Bsz, max(K - 1, 0), D), io, dev)
     a = ScanArgs(batch=Bsz, seqlen=L, dim=D, dstate=N, io_dtype=_io_code(io),
                  delta_softplus=int(bool(delta_softplus)), conv_k=K,
                  x=_ptr(x), delta=_ptr(delta), Bm=_ptr(Bm), Cm=_ptr(Cm), z=_ptr(z), A=_ptr(A),
                  Dskip=_ptr(Dskip), delta_bias=_ptr(delta_bias), conv_w=_ptr(conv_w),
                  conv_b=_ptr(conv_b), h0=_ptr(h0), y=_ptr(y), h_final=_ptr(h_final),
-                 workspace=None, workspace_bytes=0)
+                 workspace=None, workspace_bytes=0, conv_state_in=_ptr(conv_state_in),
+                 conv_state_out=_ptr(conv_state_out))
     return a, dev
 
 
@@ -222,16 +229,26 @@ def selective_scan_fwd(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, Bm
                        h0: Optional[torch.Tensor] = None, return_final_state: bool = False,
                        y: Optional[torch.Tensor] = None,
                        h_final: Optional[torch.Tensor] = None,
-                       workspace: Optional[torch.Tensor] = None
-                       ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
-    """ssm_selective_scan_fwd.  Returns (y, h_final or None)."""
+                       workspace: Optional[torch.Tensor] = None,
+                       conv_state_in: Optional[torch.Tensor] = None,
+                       conv_state_out: Optional[torch.Tensor] = None,
+                       return_conv_state: bool = False):
+    """ssm_selective_scan_fwd.  Returns (y, h_final or None), or with
+    return_conv_state (or a conv_state_out given) (y, h_final or None,
+    conv_state_out); conv states are (B, K-1, D) in x's dtype."""
     if y is None:
         y = torch.empty_like(x)
     if return_final_state and h_final is None:
         h_final = torch.empty(x.shape[0], x.shape[2], A.shape[1], device=x.device,
                               dtype=torch.float32)
+    want_cs = return_conv_state or conv_state_out is not None
+    if return_conv_state and conv_state_out is None:
+        if conv_w is None:
+            raise ValueError("a conv state needs conv_w")
+        conv_state_out = torch.empty(x.shape[0], max(conv_w.shape[1] - 1, 0), x.shape[2],
+                                     device=x.device, dtype=x.dtype)
     a, dev = _scan_args(x, delta, A, Bm, Cm, Dskip, z, delta_bias, delta_softplus, conv_w,
-                        conv_b, h0, y, h_final)
+                        conv_b, h0, y, h_final, conv_state_in, conv_state_out)
     need = lib().ssm_selective_scan_workspace_size(ctypes.byref(a))
     if need == ctypes.c_size_t(-1).value:
         _check(lib().ssm_selective_scan_fwd(ctypes.byref(a), None), "ssm_selective_scan_fwd")
@@ -242,7 +259,7 @@ def selective_scan_fwd(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, Bm
         a.workspace = ws.data_ptr()
         a.workspace_bytes = ws.numel() * ws.element_size()
     _check(lib().ssm_selective_scan_fwd(ctypes.byref(a), _stream(dev)), "ssm_selective_scan_fwd")
-    return y, h_final
+    return (y, h_final, conv_state_out) if want_cs else (y, h_final)
 
 
 def causal_conv1d_silu(x: torch.Tensor, w: torch.Tensor, bias: Optional[torch.Tensor] = None,
@@ -270,9 +287,11 @@ def causal_conv1d_silu(x: torch.Tensor, w: torch.Tensor, bias: Optional[torch.Te
 def state_update(state: torch.Tensor, x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor,
                  Bm: torch.Tensor, Cm: torch.Tensor, Dskip: Optional[torch.Tensor] = None,
                  z: Optional[torch.Tensor] = None, delta_bias: Optional[torch.Tensor] = None,
-                 delta_softplus: bool = False, y: Optional[torch.Tensor] = None
-                 ) -> torch.Tensor:
-    """ssm_state_update: advances `state` (B, D, N) in place and returns y (B, D)."""
+                 delta_softplus: bool = False, y: Optional[torch.Tensor] = None,
+                 conv_w: Optional[torch.Tensor] = None, conv_b: Optional[torch.Tensor] = None,
+                 conv_state: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """ssm_state_update: advances `state` (B, D, N) -- and with conv_w the conv
+    window `conv_state` (B, K-1, D) -- in place and returns y (B, D)."""
     if not isinstance(state, torch.Tensor) or state.dim() != 3 or state.device.type != "cuda":
         raise ValueError("state must be a (B, D, N) float32 GPU tensor")
     dev = state.device
@@ -290,9 +309,22 @@ def state_update(state: torch.Tensor, x: torch.Tensor, delta: torch.Tensor, A: t
     if y is None:
         y = torch.empty_like(x)
     _req(y, "y", (Bsz, D), io, dev)
+    K = 0
+    if conv_w is not None:
+        if conv_w.dim() != 2:
+            raise ValueError("conv_w must be (D, K)")
+        K = conv_w.shape[1]
+        _req(conv_w, "conv_w", (D, K), torch.float32, dev)
+        if K > 1:
+            _req(conv_state, "conv_state", (Bsz, K - 1, D), io, dev)
+    elif conv_b is not None or conv_state is not None:
+        raise ValueError("conv_b/conv_state need conv_w")
+    _opt(conv_b, "conv_b", (D,), torch.float32, dev)
     a = StateUpdateArgs(batch=Bsz, dim=D, dstate=N, io_dtype=_io_code(io),
                         delta_softplus=int(bool(delta_softplus)), state=_ptr(state), x=_ptr(x),
                         delta=_ptr(delta), z=_ptr(z), Bm=_ptr(Bm), Cm=_ptr(Cm), A=_ptr(A),
-                        Dskip=_ptr(Dskip), delta_bias=_ptr(delta_bias), y=_ptr(y))
+                        Dskip=_ptr(Dskip), delta_bias=_ptr(delta_bias), y=_ptr(y), conv_k=K,
+                        conv_w=_ptr(conv_w), conv_b=_ptr(conv_b),
+                        conv_state=_ptr(conv_state) if K > 1 else None)
     _check(lib().ssm_state_update(ctypes.byref(a), _stream(dev)), "ssm_state_update")
     return y

@@ -141,6 +141,35 @@ def test_scan_rejects_bad_arguments(field, value, status):
     assert ssm.lib().ssm_last_error_message().decode() != ""
 
 
+def _no_gpu():
+    import torch
+    return not torch.cuda.is_available()
+
+
+# Conv state (the prefill -> decode handoff): given only with the prologue,
+# aligned, and overlapping nothing except its own input when updated in place.
+@pytest.mark.parametrize("kw,status", [
+    (dict(conv_state_in=addr(11)), ssm.SSM_ERR_BAD_SHAPE),
+    (dict(conv_state_out=addr(11)), ssm.SSM_ERR_BAD_SHAPE),
+    (dict(conv_k=4, conv_w=addr(10), conv_state_out=addr(0, 64)), ssm.SSM_ERR_ALIAS),
+    (dict(conv_k=4, conv_w=addr(10), conv_state_out=addr(7, 64)), ssm.SSM_ERR_ALIAS),
+    (dict(conv_k=4, conv_w=addr(10), conv_state_in=addr(11), conv_state_out=addr(11, 64)),
+     ssm.SSM_ERR_ALIAS),
+    (dict(conv_k=4, conv_w=addr(10), conv_state_in=addr(7, 32)), ssm.SSM_ERR_ALIAS),
+    (dict(conv_k=4, conv_w=addr(10), conv_state_in=addr(11, 1)), ssm.SSM_ERR_ALIGN),
+])
+def test_scan_conv_state_checks(kw, status):
+    assert run_scan(scan_args(**kw)) == status
+
+
+@pytest.mark.skipif("not _no_gpu()", reason="would launch on placeholder addresses")
+def test_scan_conv_state_in_place_passes_the_checks():
+    # Same tensor in and out is allowed: the checks pass and only the launch
+    # (no device here) fails.
+    a = scan_args(conv_k=4, conv_w=addr(10), conv_state_in=addr(11), conv_state_out=addr(11))
+    assert run_scan(a) == ssm.SSM_ERR_HIP
+
+
 def test_scan_null_args_pointer():
     assert ssm.lib().ssm_selective_scan_fwd(None, None) == ssm.SSM_ERR_NULL_ARG
 
@@ -240,6 +269,30 @@ def upd_args(**kw):
 def test_state_update_rejects_bad_arguments(field, value, status):
     a = upd_args(**{field: value})
     assert ssm.lib().ssm_state_update(ctypes.byref(a), None) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(conv_k=-1), ssm.SSM_ERR_BAD_SHAPE),
+    (dict(conv_k=5, conv_w=addr(9)), ssm.SSM_ERR_UNSUPPORTED),
+    (dict(conv_k=4), ssm.SSM_ERR_NULL_ARG),                                   # no conv_w
+    (dict(conv_k=4, conv_w=addr(9)), ssm.SSM_ERR_NULL_ARG),                   # no window
+    (dict(conv_state=addr(10)), ssm.SSM_ERR_BAD_SHAPE),                       # window, no conv
+    (dict(conv_b=addr(10)), ssm.SSM_ERR_BAD_SHAPE),
+    (dict(conv_k=4, conv_w=addr(9), conv_state=addr(0, 256)), ssm.SSM_ERR_ALIAS),  # in the state
+    (dict(conv_k=4, conv_w=addr(9), conv_state=addr(8)), ssm.SSM_ERR_ALIAS),       # == y
+    (dict(conv_k=4, conv_w=addr(9), conv_state=addr(9, 8)), ssm.SSM_ERR_ALIAS),    # in conv_w
+    (dict(conv_k=4, conv_w=addr(9), conv_state=addr(10, 1)), ssm.SSM_ERR_ALIGN),
+    (dict(conv_k=4, conv_w=addr(9, 2), conv_state=addr(10)), ssm.SSM_ERR_ALIGN),
+])
+def test_state_update_conv_checks(kw, status):
+    a = upd_args(**kw)
+    assert ssm.lib().ssm_state_update(ctypes.byref(a), None) == status
+
+
+@pytest.mark.skipif("not _no_gpu()", reason="would launch on placeholder addresses")
+def test_state_update_width_one_conv_needs_no_window():
+    a = upd_args(conv_k=1, conv_w=addr(9))
+    assert ssm.lib().ssm_state_update(ctypes.byref(a), None) == ssm.SSM_ERR_HIP
 
 
 def test_state_update_empty_batch_is_a_noop():
