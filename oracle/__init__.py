@@ -57,6 +57,11 @@ def _load():
         lib.oracle_state_update_f64.argtypes = [I64, I64, I64, P, P, P, P, P, P, P, P, P, I,
                                                 P, P, I64, P, P, I]
         lib.oracle_state_update_f64.restype = I
+        lib.oracle_selective_scan_bwd_f64.argtypes = [I64, I64, I64, I64,
+                                                      P, P, P, P, P, P, P, P, I, P, P, I64,
+                                                      P, P, P,
+                                                      P, P, P, P, P, P, P, P, P, P, P, I]
+        lib.oracle_selective_scan_bwd_f64.restype = I
         _lib = lib
     return _lib
 
@@ -183,3 +188,52 @@ def state_update(state, x, delta, A, Bm, Cm, Dskip=None, z=None, delta_bias=None
     if rc != 0:
         raise ValueError("oracle_state_update_f64 rejected the sizes")
     return (y, st, cs) if conv_w is not None else (y, st)
+
+
+def selective_scan_bwd(x, delta, A, Bm, Cm, dy, Dskip=None, z=None, delta_bias=None,
+                       delta_softplus: bool = False, conv_w=None, conv_b=None, h0=None,
+                       dh_final=None, nthreads: Optional[int] = None):
+    """Gradients of selective_scan for a loss with dL/dy = dy and dL/dh_final = dh_final.
+
+    Returns a dict with dx, ddelta (B,L,D), dA (D,N), dBm, dCm (B,L,N) and, for the
+    optional inputs that were given, dz, dDskip, ddelta_bias, dconv_w, dconv_b, dh0.
+    """
+    x = _f64(x)
+    Bsz, L, D = x.shape
+    A = _f64(A)
+    N = A.shape[1]
+    delta = _f64(delta, (Bsz, L, D))
+    Bm = _f64(Bm, (Bsz, L, N))
+    Cm = _f64(Cm, (Bsz, L, N))
+    Dskip = _f64(Dskip, (D,))
+    z = _f64(z, (Bsz, L, D))
+    delta_bias = _f64(delta_bias, (D,))
+    conv_w = _f64(conv_w)
+    K = 0 if conv_w is None else conv_w.shape[1]
+    conv_b = _f64(conv_b, (D,))
+    h0 = _f64(h0, (Bsz, D, N))
+    dy = _f64(dy, (Bsz, L, D))
+    dh_final = _f64(dh_final, (Bsz, D, N))
+    out = dict(dx=np.zeros((Bsz, L, D)), ddelta=np.zeros((Bsz, L, D)), dA=np.zeros((D, N)),
+               dBm=np.zeros((Bsz, L, N)), dCm=np.zeros((Bsz, L, N)))
+    if z is not None:
+        out["dz"] = np.zeros((Bsz, L, D))
+    if Dskip is not None:
+        out["dDskip"] = np.zeros(D)
+    if delta_softplus:
+        out["ddelta_bias"] = np.zeros(D)
+    if conv_w is not None:
+        out["dconv_w"] = np.zeros((D, K))
+        out["dconv_b"] = np.zeros(D)
+    if h0 is not None:
+        out["dh0"] = np.zeros((Bsz, D, N))
+    g = lambda k: _ptr(out.get(k))
+    rc = _load().oracle_selective_scan_bwd_f64(
+        Bsz, L, D, N, _ptr(x), _ptr(delta), _ptr(A), _ptr(Bm), _ptr(Cm), _ptr(Dskip), _ptr(z),
+        _ptr(delta_bias), int(bool(delta_softplus)), _ptr(conv_w), _ptr(conv_b), K, _ptr(h0),
+        _ptr(dy), _ptr(dh_final), g("dx"), g("ddelta"), g("dz"), g("dA"), g("dBm"), g("dCm"),
+        g("dDskip"), g("ddelta_bias"), g("dconv_w"), g("dconv_b"), g("dh0"),
+        int(nthreads or default_threads()))
+    if rc != 0:
+        raise ValueError("oracle_selective_scan_bwd_f64 rejected the sizes")
+    return out

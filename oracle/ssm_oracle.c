@@ -224,3 +224,188 @@ int oracle_state_update_f64(int64_t Bsz, int64_t D, int64_t N, double *state,
     }
     return 0;
 }
+
+/* d/dz of phi(z) = (e^z - 1)/z, i.e. psi(z) = (e^z (z - 1) + 1) / z^2, with
+ * psi(0) = 1/2; a Taylor series near 0 avoids the cancellation. */
+static double psi(double zv)
+{
+    if (fabs(zv) < 0.1) {
+        /* sum_k (k+1) z^k / (k+2)! for k = 0..9 */
+        double s = 0.0, fact = 2.0, p = 1.0;
+        for (int k = 0; k < 10; ++k) {
+            s += (double)(k + 1) * p / fact;
+            p *= zv;
+            fact *= (double)(k + 3);
+        }
+        return s;
+    }
+    return (exp(zv) * (zv - 1.0) + 1.0) / (zv * zv);
+}
+
+static double sigmoid(double v) { return 1.0 / (1.0 + exp(-v)); }
+
+/* d silu(v) / dv = sigma(v) (1 + v (1 - sigma(v))). */
+static double dsilu(double v)
+{
+    double s = sigmoid(v);
+    return s * (1.0 + v * (1.0 - s));
+}
+
+/*
+ * Gradients of the selective scan above for a scalar loss L whose gradient
+ * with respect to y is dy (B,L,D) and with respect to h_final is dh_final
+ * (B,D,N, or NULL for 0): reverse-mode differentiation of the same loops
+ * (the adjoint of eq. (2a)/(2b) with the ZOH of eq. (4), [P1] sec. 4b; the
+ * pages recompute the states instead of storing them, sec. 4c, which this
+ * plain reference does not need to do).  Per batch row, channel and entry,
+ * with lambda_t = dL/dh_t:
+ *   lambda_t   = C_t gy_t + Abar_{t+1} lambda_{t+1},   gy_t = dy_t silu(z_t)
+ *   dAbar_t    = lambda_t h_{t-1},   dBbar_t = lambda_t u_t,
+ *   du_t      += sum_n lambda_t Bbar_t + Dskip gy_t
+ *   ddt_t     += sum_n (dAbar_t a e_t + dBbar_t B_t e_t)   (Bbar = B (e - 1)/a)
+ *   dA        += sum_t (dAbar_t dt_t e_t + dBbar_t B_t dt_t^2 psi(dt_t a))
+ *   dB_t      += sum_d dBbar_t dt_t phi(dt_t a),   dC_t += sum_d gy_t h_t
+ *   dz_t       = dy_t (C_t h_t + Dskip u_t) silu'(z_t),  dDskip += sum gy_t u_t
+ *   dh0        = Abar_0 lambda_0
+ * then through softplus (ddelta = ddt sigma(delta + bias)) and the conv
+ * prologue (dc_t = du_t silu'(c_t), c_t the pre-activation; dx, dconv_w,
+ * dconv_b by the chain rule of the causal cross-correlation; no conv state
+ * entering).  Outputs (all written, optional ones when non-NULL): dx, ddelta,
+ * dz (B,L,D); dA (D,N); dBm, dCm (B,L,N); dDskip, ddelta_bias, dconv_b (D);
+ * dconv_w (D,K); dh0 (B,D,N).  Threads split batch rows.  Returns 0 or -1.
+ */
+int oracle_selective_scan_bwd_f64(int64_t Bsz, int64_t L, int64_t D, int64_t N,
+                                  const double *x, const double *delta, const double *A,
+                                  const double *Bm, const double *Cm, const double *Dskip,
+                                  const double *z, const double *delta_bias, int delta_softplus,
+                                  const double *conv_w, const double *conv_b, int64_t conv_k,
+                                  const double *h0, const double *dy, const double *dh_final,
+                                  double *dx, double *ddelta, double *dz, double *dA, double *dBm,
+                                  double *dCm, double *dDskip, double *ddelta_bias,
+                                  double *dconv_w, double *dconv_b, double *dh0, int nthreads)
+{
+    if (Bsz < 0 || L < 0 || D < 0 || N < 1 || (conv_w && conv_k < 1)) return -1;
+    if (nthreads < 1) nthreads = 1;
+    int64_t K = conv_w ? conv_k : 0;
+    /* per batch row partial sums of the per-channel parameters */
+    double *pA = (double *)calloc((size_t)(Bsz * D * N + 1), sizeof(double));
+    double *pD = (double *)calloc((size_t)(Bsz * D + 1), sizeof(double));
+    double *pbias = (double *)calloc((size_t)(Bsz * D + 1), sizeof(double));
+    double *pw = (double *)calloc((size_t)(Bsz * D * (K > 0 ? K : 1) + 1), sizeof(double));
+    double *pb = (double *)calloc((size_t)(Bsz * D + 1), sizeof(double));
+    for (int64_t i = 0; i < Bsz * L * N; ++i) { dBm[i] = 0.0; dCm[i] = 0.0; }
+#pragma omp parallel for num_threads(nthreads) schedule(dynamic, 1)
+    for (int64_t b = 0; b < Bsz; ++b) {
+        double *hs = (double *)malloc(sizeof(double) * (size_t)((L + 1) * N));  /* h_{t-1} at row t */
+        double *us = (double *)malloc(sizeof(double) * (size_t)(L + 1));
+        double *cs = (double *)malloc(sizeof(double) * (size_t)(L + 1));
+        double *dts = (double *)malloc(sizeof(double) * (size_t)(L + 1));
+        double *duv = (double *)malloc(sizeof(double) * (size_t)(L + 1));
+        double *lam = (double *)malloc(sizeof(double) * (size_t)N);
+        for (int64_t d = 0; d < D; ++d) {
+            const double *xbd = x + b * L * D + d;
+            /* forward, keeping h_{t-1}, u_t, the conv pre-activation and dt */
+            for (int64_t n = 0; n < N; ++n) hs[n] = h0 ? h0[(b * D + d) * N + n] : 0.0;
+            for (int64_t t = 0; t < L; ++t) {
+                int64_t i = (b * L + t) * D + d;
+                double u = x[i];
+                if (K > 0) {
+                    double c = conv_b ? conv_b[d] : 0.0;
+                    for (int64_t k = 0; k < K; ++k) {
+                        int64_t s = t - (K - 1) + k;
+                        if (s >= 0) c += conv_w[d * K + k] * xbd[s * D];
+                    }
+                    cs[t] = c;
+                    u = silu(c);
+                }
+                us[t] = u;
+                double dt = delta[i];
+                if (delta_softplus) dt = softplus(dt + (delta_bias ? delta_bias[d] : 0.0));
+                dts[t] = dt;
+                for (int64_t n = 0; n < N; ++n) {
+                    double abar, bbar;
+                    zoh(dt, A[d * N + n], Bm[(b * L + t) * N + n], &abar, &bbar);
+                    hs[(t + 1) * N + n] = abar * hs[t * N + n] + bbar * u;
+                }
+            }
+            /* backward */
+            for (int64_t n = 0; n < N; ++n) lam[n] = dh_final ? dh_final[(b * D + d) * N + n] : 0.0;
+            for (int64_t t = L - 1; t >= 0; --t) {
+                int64_t i = (b * L + t) * D + d;
+                double u = us[t], dt = dts[t];
+                double gy = dy[i];
+                if (z) {
+                    double yhat = (Dskip ? Dskip[d] * u : 0.0);
+                    for (int64_t n = 0; n < N; ++n) yhat += Cm[(b * L + t) * N + n] * hs[(t + 1) * N + n];
+                    if (dz) dz[i] = dy[i] * yhat * dsilu(z[i]);
+                    gy = dy[i] * silu(z[i]);
+                }
+                double du = Dskip ? Dskip[d] * gy : 0.0;
+                if (Dskip) pD[b * D + d] += gy * u;
+                double ddt = 0.0;
+                for (int64_t n = 0; n < N; ++n) {
+                    double a = A[d * N + n], bb = Bm[(b * L + t) * N + n];
+                    double cc = Cm[(b * L + t) * N + n];
+                    double hprev = hs[t * N + n], hcur = hs[(t + 1) * N + n];
+                    dCm[(b * L + t) * N + n] += gy * hcur;
+                    double l = lam[n] + cc * gy;           /* dL/dh_t */
+                    double zz = dt * a, e = exp(zz);
+                    double phi = (zz == 0.0) ? 1.0 : expm1(zz) / zz;
+                    double bbar = phi * dt * bb;
+                    double dabar = l * hprev, dbbar = l * u;
+                    du += l * bbar;
+                    ddt += dabar * a * e + dbbar * bb * e;
+                    pA[(b * D + d) * N + n] += dabar * dt * e + dbbar * bb * dt * dt * psi(zz);
+                    dBm[(b * L + t) * N + n] += dbbar * dt * phi;
+                    lam[n] = e * l;                         /* dL/dh_{t-1} */
+                }
+                double draw = ddt;
+                if (delta_softplus) {
+                    double sg = sigmoid(delta[i] + (delta_bias ? delta_bias[d] : 0.0));
+                    draw = ddt * sg;
+                    pbias[b * D + d] += draw;
+                }
+                ddelta[i] = draw;
+                duv[t] = du;
+            }
+            if (dh0)
+                for (int64_t n = 0; n < N; ++n) dh0[(b * D + d) * N + n] = lam[n];
+            /* through the conv prologue */
+            for (int64_t t = 0; t < L; ++t) dx[(b * L + t) * D + d] = K > 0 ? 0.0 : duv[t];
+            if (K > 0) {
+                for (int64_t t = 0; t < L; ++t) {
+                    double dc = duv[t] * dsilu(cs[t]);
+                    pb[b * D + d] += dc;
+                    for (int64_t k = 0; k < K; ++k) {
+                        int64_t s = t - (K - 1) + k;
+                        if (s < 0) continue;
+                        dx[(b * L + s) * D + d] += dc * conv_w[d * K + k];
+                        pw[(b * D + d) * K + k] += dc * xbd[s * D];
+                    }
+                }
+            }
+        }
+        free(hs); free(us); free(cs); free(dts); free(duv); free(lam);
+    }
+    /* sum the per-row partials in a fixed order */
+    for (int64_t d = 0; d < D; ++d) {
+        for (int64_t n = 0; n < N; ++n) {
+            double s = 0.0;
+            for (int64_t b = 0; b < Bsz; ++b) s += pA[(b * D + d) * N + n];
+            dA[d * N + n] = s;
+        }
+        double sd = 0.0, sb = 0.0, sc = 0.0;
+        for (int64_t b = 0; b < Bsz; ++b) { sd += pD[b * D + d]; sb += pbias[b * D + d]; sc += pb[b * D + d]; }
+        if (dDskip) dDskip[d] = sd;
+        if (ddelta_bias) ddelta_bias[d] = sb;
+        if (dconv_b) dconv_b[d] = sc;
+        if (dconv_w)
+            for (int64_t k = 0; k < K; ++k) {
+                double s = 0.0;
+                for (int64_t b = 0; b < Bsz; ++b) s += pw[(b * D + d) * K + k];
+                dconv_w[d * K + k] = s;
+            }
+    }
+    free(pA); free(pD); free(pbias); free(pw); free(pb);
+    return 0;
+}
