@@ -7,7 +7,8 @@
  *     with a fused depthwise causal conv1d + SiLU prologue and a final-state
  *     output;
  *   - ssm_state_update: one recurrent (decode) step on a resident state;
- *   - ssm_causal_conv1d_silu: the conv prologue on its own.
+ *   - ssm_causal_conv1d_silu: the conv prologue on its own;
+ *   - ssm_selective_scan_bwd: the gradients of the scan (training).
  *
  * The operations are defined on these pages (cited by title and section):
  *   [P1] "Mamba: Linear-Time Sequence Modeling with Selective State Spaces"
@@ -57,7 +58,7 @@
 extern "C" {
 #endif
 
-#define SSM_ABI_VERSION 2
+#define SSM_ABI_VERSION 3
 #define SSM_MAX_DSTATE 16 /* largest N the kernels hold in registers */
 #define SSM_MAX_CONV_K 4  /* largest conv1d kernel width */
 
@@ -204,6 +205,53 @@ typedef struct ssm_state_update_args {
 } ssm_state_update_args_t;
 
 ssm_status_t ssm_state_update(const ssm_state_update_args_t *args, void *stream);
+
+/*
+ * Backward pass of the selective scan: the gradients of a scalar loss with
+ * dL/dy = dy and dL/dh_final = dh_final through the forward defined above
+ * ([P1] eq. (4), (2a)/(2b), sec. 4a; the states are recomputed from
+ * checkpoints instead of stored, as [P1] sec. 4c does).  With
+ * lambda_t = dL/dh_t and gy_t = dy_t silu(z_t):
+ *   lambda_t = C_t gy_t + exp(dt_{t+1} A) lambda_{t+1}  (lambda_{L-1} adds dh_final)
+ *   dx       = sum_n lambda Bbar + Dskip gy;   ddelta by the chain rule through
+ *              exp(dt A), Bbar and the softplus;   dz = dy (C h + D u) silu'(z);
+ *   dA, dDskip, ddelta_bias summed over batch and time; dBm, dCm summed over
+ *   channels; dh0 = exp(dt_0 A) lambda_0.
+ * This version supports N == 16 and no conv prologue (conv_k == 0; other
+ * values give SSM_ERR_UNSUPPORTED); the forward's input fields have the same
+ * meaning and shapes as in ssm_scan_args_t.
+ */
+typedef struct ssm_scan_bwd_args {
+    int64_t batch, seqlen, dim, dstate; /* as in ssm_scan_args_t (dstate == 16)  */
+    int32_t io_dtype;       /* of x, delta, Bm, Cm, z, dy, dx, ddelta, dz      */
+    int32_t delta_softplus; /* as in ssm_scan_args_t                           */
+    int64_t conv_k;         /* must be 0                                       */
+    const void *x, *delta, *Bm, *Cm, *z;            /* forward inputs            */
+    const float *A, *Dskip, *delta_bias, *conv_w, *conv_b, *h0; /* conv_w/_b NULL */
+    const void *dy;         /* (B,L,D) io_dtype, required                      */
+    const float *dh_final;  /* (B,D,N) fp32, or NULL (= 0)                     */
+    void *dx;               /* (B,L,D) io_dtype output, required               */
+    void *ddelta;           /* (B,L,D) io_dtype output (w.r.t. the raw delta)  */
+    void *dz;               /* (B,L,D) io_dtype output; required iff z         */
+    float *dA;              /* (D,N) fp32 output, required                     */
+    float *dBm, *dCm;       /* (B,L,N) fp32 outputs, required                  */
+    float *dDskip;          /* (D) fp32 output, or NULL (not written)          */
+    float *ddelta_bias;     /* (D) fp32 output, or NULL; 0 without softplus    */
+    float *dconv_w, *dconv_b; /* must be NULL                                  */
+    float *dh0;             /* (B,D,N) fp32 output, or NULL                    */
+    void *workspace;        /* device scratch, 256-aligned                     */
+    size_t workspace_bytes; /* >= ssm_selective_scan_bwd_workspace_size(args)  */
+} ssm_scan_bwd_args_t;
+
+/* Workspace bytes ssm_selective_scan_bwd needs ((size_t)-1 for invalid sizes). */
+size_t ssm_selective_scan_bwd_workspace_size(const ssm_scan_bwd_args_t *args);
+
+/*
+ * Enqueue the backward pass on `stream`.  Outputs must not overlap any input,
+ * each other or the workspace.  Every output given is overwritten.  Returns
+ * SSM_OK or an error status (see the conventions).
+ */
+ssm_status_t ssm_selective_scan_bwd(const ssm_scan_bwd_args_t *args, void *stream);
 
 /* Static description of a status code (never NULL). */
 const char *ssm_status_string(ssm_status_t status);

@@ -9,11 +9,12 @@ from .ssm import (  # noqa: F401
     abi_version,
     causal_conv1d_silu,
     lib,
+    selective_scan_bwd,
     selective_scan_fwd,
     selective_scan_workspace_size,
     state_update,
     status_string,
 )
 
-__all__ = ["SSMError", "abi_version", "causal_conv1d_silu", "lib", "selective_scan_fwd",
-           "selective_scan_workspace_size", "state_update", "status_string"]
+__all__ = ["SSMError", "abi_version", "causal_conv1d_silu", "lib", "selective_scan_bwd",
+           "selective_scan_fwd", "selective_scan_workspace_size", "state_update", "status_string"]

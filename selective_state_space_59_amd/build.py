@@ -20,7 +20,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libssm_hip.so")
 ARCH = "gfx950"
 
-SOURCES = ["ssm_api.cpp", "scan_fwd.hip", "conv1d.hip", "state_update.hip"]
+SOURCES = ["ssm_api.cpp", "scan_fwd.hip", "scan_bwd.hip", "conv1d.hip", "state_update.hip"]
 
 # Packed-fp32 VALU forms are switched off for all device code; the compiler
 # still emits ordinary fp32 arithmetic.

@@ -1,0 +1,405 @@
+// scan_bwd.hip -- backward pass of the selective scan (S6) on gfx950.
+//
+// Gradients of the forward of "Mamba: Linear-Time Sequence Modeling with
+// Selective State Spaces" (paper summary page, sec. 4b eq. (4) and (2a)/(2b),
+// Algorithm 2, the block of sec. 4a) for a loss with dL/dy = dy and
+// dL/dh_final = dh_final.  The page's backward recomputes the states instead
+// of storing them (sec. 4c); here:
+//   1. a checkpoint pass runs the recurrence forward and stores only the
+//      state entering every 16-step block (1/16 of the expanded states);
+//   2. the backward kernel walks the blocks from last to first.  Per block it
+//      re-runs the 16 steps from the checkpoint, keeping h_{t-1} and
+//      exp(dt A) in registers, and then runs the adjoint recurrence
+//        lambda_t = C_t gy_t + exp(dt_{t+1} A) lambda_{t+1},  gy = dy silu(z)
+//      backwards through them.
+//
+// Lane layout as in the forward: lane (c, n) of a wave owns state entry n of
+// channel c (4 channels per wave, N = 16).  Sums over the 16 entries (the
+// read-out C h for dz, and du and ddelta) are transposed through a wave-
+// private LDS area so that lane (c, k) sums step k.  dB and dC are sums over
+// channels: each workgroup adds its channels in LDS and stores one partial
+// per (batch, workgroup, step, entry); a reduction kernel adds the partials of
+// the workgroups of a batch row.  dA, dD and the delta bias gradient are
+// summed over time per lane and over batch rows by the same reduction.
+//
+// Derivatives used (B_bar = B (e - 1)/A = dt phi(dt A) B, e = exp(dt A)):
+//   d e / d dt = A e,   d B_bar / d dt = B e,   d B_bar / d A = B dt^2 psi(dt A),
+//   psi(z) = phi'(z) = (e^z (z - 1) + 1) / z^2 (series near 0).
+#include "ssm_device.h"
+#include "ssm_internal.h"
+
+#include <algorithm>
+#include <utility>
+
+namespace ssm {
+namespace {
+
+constexpr int kRowN = 16;            // lanes per row = state entries (N = 16)
+constexpr int kStep = 16;            // steps per block
+constexpr int kWavesB = 8;           // waves per workgroup
+constexpr int kChB = 4 * kWavesB;    // channels per workgroup
+constexpr int kTS = kStep + 4;       // padded row stride of a transpose area
+constexpr int kTrArea = 4 * kRowN * kTS;  // floats per wave and transpose area
+
+struct BwdParams {
+    int64_t B, L, D, G;              // G: workgroups per batch row
+    int softplus;
+    const void *x, *delta, *Bm, *Cm, *z, *dy;
+    const float *A, *Dskip, *dbias, *h0, *dh_final;
+    void *dx, *ddelta, *dz;
+    float *dh0;
+    float *ckpt;      // [nblocks][B][D][16]   state entering each block
+    float *partBC;    // [2][B][G][L][16]      per-workgroup sums of dB, dC
+    float *partA;     // [B][D][16]
+    float *partD;     // [B][D]
+    float *partBias;  // [B][D]
+};
+
+template <int I>
+using icb = std::integral_constant<int, I>;
+template <typename F, int... Is>
+__device__ __forceinline__ void sfor_impl(F &&f, std::integer_sequence<int, Is...>) {
+    (f(icb<Is>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void sfor(F &&f) {
+    sfor_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// Value of lane K of this lane's 16-lane row.
+template <int K>
+__device__ __forceinline__ float bcast_row(float v) {
+    return __builtin_amdgcn_update_dpp(0.0f, v, 0x150 + K, 0xf, 0xf, false);
+}
+
+__device__ __forceinline__ float phi_f(float zz, float e) {
+    const float s = 1.0f + zz * (0.5f + zz * (1.0f / 6.0f + zz * (1.0f / 24.0f +
+                    zz * (1.0f / 120.0f + zz * (1.0f / 720.0f + zz * (1.0f / 5040.0f))))));
+    return fabsf(zz) < 0.25f ? s : (e - 1.0f) / zz;
+}
+__device__ __forceinline__ float psi_f(float zz, float e) {
+    const float s = 0.5f + zz * (1.0f / 3.0f + zz * (1.0f / 8.0f + zz * (1.0f / 30.0f +
+                    zz * (1.0f / 144.0f + zz * (1.0f / 840.0f + zz * (1.0f / 5760.0f))))));
+    return fabsf(zz) < 0.25f ? s : (e * (zz - 1.0f) + 1.0f) / (zz * zz);
+}
+__device__ __forceinline__ float sigmoid_f(float v) { return 1.0f / (1.0f + __expf(-v)); }
+__device__ __forceinline__ float dsilu_f(float v) {
+    const float s = sigmoid_f(v);
+    return s * (1.0f + v * (1.0f - s));
+}
+
+// Lane setup shared by both kernels.
+struct LaneB {
+    int64_t b, d;
+    int n, c, wave;
+    bool valid;
+};
+__device__ __forceinline__ LaneB lane_setup(const BwdParams &p) {
+    LaneB l;
+    const int lane = threadIdx.x & 63;
+    l.wave = threadIdx.x >> 6;
+    l.n = lane & 15;
+    l.c = lane >> 4;
+    const int64_t g = blockIdx.x;
+    l.b = g / p.G;
+    l.d = (g % p.G) * kChB + 4 * l.wave + l.c;
+    l.valid = l.d < p.D;
+    return l;
+}
+
+// Own-step inputs of lane (c, n) in block j: step t = 16 j + n of channel c.
+template <typename IO>
+__device__ __forceinline__ void own_inputs(const BwdParams &p, const LaneB &l, int64_t t, float &u,
+                                           float &raw, float &dt) {
+    u = raw = dt = 0.0f;
+    if (l.valid && t < p.L) {
+        const int64_t i = (l.b * p.L + t) * p.D + l.d;
+        u = load_io<IO>(p.x, i);
+        raw = load_io<IO>(p.delta, i);
+        dt = p.softplus ? softplus(raw + (p.dbias ? p.dbias[l.d] : 0.0f)) : raw;
+    }
+}
+
+template <typename IO>
+__device__ __forceinline__ float load_bc(const void *t, const BwdParams &p, const LaneB &l, int64_t step) {
+    return step < p.L ? load_io<IO>(t, (l.b * p.L + step) * kRowN + l.n) : 0.0f;
+}
+
+// Pass 1: states entering every block.
+template <typename IO>
+__global__ __launch_bounds__(64 * kWavesB) void bwd_ckpt_kernel(BwdParams p) {
+    const LaneB l = lane_setup(p);
+    const float a = l.valid ? p.A[l.d * kRowN + l.n] : 0.0f;
+    const float a2 = a * kLog2e;
+    float h = (l.valid && p.h0) ? p.h0[(l.b * p.D + l.d) * kRowN + l.n] : 0.0f;
+    const int64_t nb = (p.L + kStep - 1) / kStep;
+    for (int64_t j = 0; j < nb; ++j) {
+        if (l.valid) p.ckpt[((j * p.B + l.b) * p.D + l.d) * kRowN + l.n] = h;
+        float u, raw, dt;
+        own_inputs<IO>(p, l, j * kStep + l.n, u, raw, dt);
+        sfor<kStep>([&](auto K) {
+            constexpr int k = decltype(K)::value;
+            const float dtk = bcast_row<k>(dt), uk = bcast_row<k>(u);
+            const float bk = load_bc<IO>(p.Bm, p, l, j * kStep + k);
+            const float e = hw_exp2(dtk * a2);
+            h = e * h + (dtk * phi_f(dtk * a, e)) * bk * uk;
+        });
+    }
+}
+
+// Pass 2: the adjoint, blocks from last to first.
+template <typename IO>
+__global__ __launch_bounds__(64 * kWavesB) void bwd_kernel(BwdParams p) {
+    extern __shared__ __attribute__((aligned(16))) float lds[];
+    const LaneB l = lane_setup(p);
+    const int n = l.n, c = l.c;
+    // Two transpose areas per wave ([c][n][k], stride kTS), then the
+    // workgroup's dB / dC partials [2][kChB][16 k][16 n].
+    float *tr0 = lds + (l.wave * 2) * kTrArea;
+    float *tr1 = tr0 + kTrArea;
+    float *red = lds + kWavesB * 2 * kTrArea;
+    const float a = l.valid ? p.A[l.d * kRowN + n] : 0.0f;
+    const float a2 = a * kLog2e;
+    const float dsk = (l.valid && p.Dskip) ? p.Dskip[l.d] : 0.0f;
+    const float bias = (l.valid && p.dbias) ? p.dbias[l.d] : 0.0f;
+    float lam = (l.valid && p.dh_final) ? p.dh_final[(l.b * p.D + l.d) * kRowN + n] : 0.0f;
+    float accA = 0.0f, accD = 0.0f, accBias = 0.0f;
+    const int64_t nb = (p.L + kStep - 1) / kStep;
+    const int64_t grow = blockIdx.x % p.G;  // workgroup within the batch row
+
+    for (int64_t j = nb - 1; j >= 0; --j) {
+        const int64_t t0 = j * kStep;
+        const int64_t tme = t0 + n;  // this lane's own step
+        float u, raw, dt;
+        own_inputs<IO>(p, l, tme, u, raw, dt);
+        float zv = 0.0f, gv = 0.0f;
+        if (l.valid && tme < p.L) {
+            const int64_t i = (l.b * p.L + tme) * p.D + l.d;
+            gv = load_io<IO>(p.dy, i);
+            if (p.z) zv = load_io<IO>(p.z, i);
+        }
+        // -- forward over the block from its checkpoint ----------------------
+        float hp[kStep], ev[kStep];
+        float h = l.valid ? p.ckpt[((j * p.B + l.b) * p.D + l.d) * kRowN + n] : 0.0f;
+        sfor<kStep>([&](auto K) {
+            constexpr int k = decltype(K)::value;
+            const float dtk = bcast_row<k>(dt), uk = bcast_row<k>(u);
+            const float bk = load_bc<IO>(p.Bm, p, l, t0 + k);
+            const float ck = load_bc<IO>(p.Cm, p, l, t0 + k);
+            const float e = hw_exp2(dtk * a2);
+            hp[k] = h;
+            ev[k] = e;
+            h = e * h + (dtk * phi_f(dtk * a, e)) * bk * uk;
+            tr0[(c * kRowN + n) * kTS + k] = ck * h;  // partial read-out of step k
+        });
+        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+        // lane (c, n) finishes its own step n: y_hat, gy, dz
+        float yhat = dsk * u;
+#pragma unroll
+        for (int i = 0; i < kRowN; ++i) yhat += tr0[(c * kRowN + i) * kTS + n];
+        float gy = gv;
+        if (p.z) {
+            gy = gv * silu(zv);
+            if (l.valid && tme < p.L) store_io<IO>(p.dz, (l.b * p.L + tme) * p.D + l.d, gv * yhat * dsilu_f(zv));
+        }
+        accD += gy * u;
+        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+        // -- adjoint over the block, last step first ---------------------------
+        sfor<kStep>([&](auto K) {
+            constexpr int k = kStep - 1 - decltype(K)::value;
+            const float gyk = bcast_row<k>(gy), uk = bcast_row<k>(u), dtk = bcast_row<k>(dt);
+            const float bk = load_bc<IO>(p.Bm, p, l, t0 + k);
+            const float ck = load_bc<IO>(p.Cm, p, l, t0 + k);
+            const float e = ev[k];
+            const float hprev = hp[k];
+            const float hcur = k == kStep - 1 ? h : hp[k + 1 < kStep ? k + 1 : 0];
+            const float lt = __builtin_fmaf(ck, gyk, lam);  // dL/dh_t
+            const float zz = dtk * a;
+            const float ph = phi_f(zz, e);
+            const float bbar = dtk * ph * bk;
+            const float dabar = lt * hprev, dbbar = lt * uk;
+            tr0[(c * kRowN + n) * kTS + k] = lt * bbar;                      // -> du_k
+            tr1[(c * kRowN + n) * kTS + k] = e * (dabar * a + dbbar * bk);   // -> ddt_k
+            accA += e * dabar * dtk + dbbar * bk * dtk * dtk * psi_f(zz, e);
+            red[((0 * kChB + 4 * l.wave + c) * kStep + k) * kRowN + n] = dbbar * dtk * ph;  // dB
+            red[((1 * kChB + 4 * l.wave + c) * kStep + k) * kRowN + n] = gyk * hcur;        // dC
+            lam = e * lt;
+        });
+        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+        {
+            float du = dsk * gy, ddt = 0.0f;
+#pragma unroll
+            for (int i = 0; i < kRowN; ++i) {
+                du += tr0[(c * kRowN + i) * kTS + n];
+                ddt += tr1[(c * kRowN + i) * kTS + n];
+            }
+            float draw = ddt;
+            if (p.softplus) {
+                draw = ddt * sigmoid_f(raw + bias);
+                accBias += draw;
+            }
+            if (l.valid && tme < p.L) {
+                const int64_t i = (l.b * p.L + tme) * p.D + l.d;
+                store_io<IO>(p.dx, i, du);
+                store_io<IO>(p.ddelta, i, draw);
+            }
+        }
+        // -- dB, dC: add the workgroup's channels ----------------------------
+        __syncthreads();
+        for (int item = threadIdx.x; item < 2 * kStep * kRowN; item += 64 * kWavesB) {
+            const int tensor = item / (kStep * kRowN), kn = item % (kStep * kRowN);
+            float s = 0.0f;
+            for (int r = 0; r < kChB; ++r) s += red[(tensor * kChB + r) * kStep * kRowN + kn];
+            const int64_t t = t0 + kn / kRowN;
+            if (t < p.L)
+                p.partBC[(((int64_t)tensor * p.B + l.b) * p.G + grow) * p.L * kRowN + t * kRowN + kn % kRowN] = s;
+        }
+        __syncthreads();
+    }
+    if (l.valid) {
+        if (p.dh0) p.dh0[(l.b * p.D + l.d) * kRowN + n] = lam;
+        p.partA[(l.b * p.D + l.d) * kRowN + n] = accA;
+    }
+    // per-channel sums over the row's own steps
+#pragma unroll
+    for (int s = 8; s >= 1; s /= 2) {
+        accD += __shfl_xor(accD, s, 16);
+        accBias += __shfl_xor(accBias, s, 16);
+    }
+    if (l.valid && n == 0) {
+        p.partD[l.b * p.D + l.d] = accD;
+        p.partBias[l.b * p.D + l.d] = accBias;
+    }
+}
+
+// dB, dC = sums of the workgroup partials of each batch row; fp32 outputs.
+__global__ void bwd_reduce_bc_kernel(const float *partBC, float *dB, float *dC, int64_t B, int64_t G,
+                                     int64_t L) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // over 2 B L 16
+    const int64_t per = B * L * kRowN;
+    if (i >= 2 * per) return;
+    const int64_t tensor = i / per, r = i % per;
+    const int64_t b = r / (L * kRowN), tn = r % (L * kRowN);
+    float s = 0.0f;
+    for (int64_t g = 0; g < G; ++g) s += partBC[((tensor * B + b) * G + g) * L * kRowN + tn];
+    (tensor == 0 ? dB : dC)[r] = s;
+}
+
+// dA, dDskip, ddelta_bias = sums over batch rows.
+__global__ void bwd_reduce_params_kernel(const float *partA, const float *partD, const float *partBias,
+                                         float *dA, float *dD, float *dbias, int64_t B, int64_t D) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // over D 16
+    if (i >= D * kRowN) return;
+    float s = 0.0f;
+    for (int64_t b = 0; b < B; ++b) s += partA[b * D * kRowN + i];
+    dA[i] = s;
+    if (i % kRowN == 0) {
+        const int64_t d = i / kRowN;
+        float sd = 0.0f, sb = 0.0f;
+        for (int64_t b = 0; b < B; ++b) {
+            sd += partD[b * D + d];
+            sb += partBias[b * D + d];
+        }
+        if (dD) dD[d] = sd;
+        if (dbias) dbias[d] = sb;
+    }
+}
+
+// dh0 of an empty sequence: dh_final (or 0); dA etc. are 0.
+__global__ void bwd_empty_kernel(const float *dh_final, float *dh0, int64_t nbdn, float *dA, float *dD,
+                                 float *dbias, int64_t D) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (dh0 && i < nbdn) dh0[i] = dh_final ? dh_final[i] : 0.0f;
+    if (i < D * kRowN) dA[i] = 0.0f;
+    if (i < D) {
+        if (dD) dD[i] = 0.0f;
+        if (dbias) dbias[i] = 0.0f;
+    }
+}
+
+struct BwdLayout {
+    int64_t G, nb;
+    size_t ckpt, partBC, partA, partD, partBias, total;
+};
+
+size_t r256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+BwdLayout bwd_layout(const ssm_scan_bwd_args_t &a) {
+    BwdLayout q;
+    q.G = (a.dim + kChB - 1) / kChB;
+    q.nb = (a.seqlen + kStep - 1) / kStep;
+    q.ckpt = r256((size_t)(q.nb * a.batch * a.dim * kRowN) * sizeof(float));
+    q.partBC = r256((size_t)(2 * a.batch * q.G * a.seqlen * kRowN) * sizeof(float));
+    q.partA = r256((size_t)(a.batch * a.dim * kRowN) * sizeof(float));
+    q.partD = r256((size_t)(a.batch * a.dim) * sizeof(float));
+    q.partBias = q.partD;
+    q.total = q.ckpt + q.partBC + q.partA + q.partD + q.partBias;
+    return q;
+}
+
+template <typename IO>
+hipError_t launch_bwd_typed(const BwdParams &p, const ssm_scan_bwd_args_t &a, hipStream_t stream) {
+    const unsigned grid = (unsigned)(p.G * p.B);
+    bwd_ckpt_kernel<IO><<<grid, 64 * kWavesB, 0, stream>>>(p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const size_t lds = (size_t)(kWavesB * 2 * kTrArea + 2 * kChB * kStep * kRowN) * sizeof(float);
+    bwd_kernel<IO><<<grid, 64 * kWavesB, lds, stream>>>(p);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t nbc = 2 * p.B * p.L * kRowN;
+    bwd_reduce_bc_kernel<<<(unsigned)((nbc + 255) / 256), 256, 0, stream>>>(p.partBC, a.dBm, a.dCm, p.B, p.G, p.L);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    bwd_reduce_params_kernel<<<(unsigned)((p.D * kRowN + 255) / 256), 256, 0, stream>>>(
+        p.partA, p.partD, p.partBias, a.dA, a.dDskip, a.ddelta_bias, p.B, p.D);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+size_t scan_bwd_workspace_bytes(const ssm_scan_bwd_args_t &a) {
+    if (a.batch == 0 || a.seqlen == 0) return 0;
+    return bwd_layout(a).total;
+}
+
+hipError_t launch_scan_bwd(const ssm_scan_bwd_args_t &a, hipStream_t stream) {
+    if (a.seqlen == 0) {
+        const int64_t n = std::max<int64_t>(a.batch * a.dim * kRowN, a.dim * kRowN);
+        bwd_empty_kernel<<<(unsigned)((n + 255) / 256), 256, 0, stream>>>(
+            a.dh_final, a.dh0, a.batch * a.dim * kRowN, a.dA, a.dDskip, a.ddelta_bias, a.dim);
+        return hipGetLastError();
+    }
+    const BwdLayout q = bwd_layout(a);
+    char *ws = static_cast<char *>(a.workspace);
+    BwdParams p;
+    p.B = a.batch;
+    p.L = a.seqlen;
+    p.D = a.dim;
+    p.G = q.G;
+    p.softplus = a.delta_softplus;
+    p.x = a.x;
+    p.delta = a.delta;
+    p.Bm = a.Bm;
+    p.Cm = a.Cm;
+    p.z = a.z;
+    p.dy = a.dy;
+    p.A = a.A;
+    p.Dskip = a.Dskip;
+    p.dbias = a.delta_bias;
+    p.h0 = a.h0;
+    p.dh_final = a.dh_final;
+    p.dx = a.dx;
+    p.ddelta = a.ddelta;
+    p.dz = a.dz;
+    p.dh0 = a.dh0;
+    p.ckpt = reinterpret_cast<float *>(ws);
+    p.partBC = reinterpret_cast<float *>(ws + q.ckpt);
+    p.partA = reinterpret_cast<float *>(ws + q.ckpt + q.partBC);
+    p.partD = reinterpret_cast<float *>(ws + q.ckpt + q.partBC + q.partA);
+    p.partBias = reinterpret_cast<float *>(ws + q.ckpt + q.partBC + q.partA + q.partD);
+    if (a.io_dtype == SSM_BF16) return launch_bwd_typed<io_bf16>(p, a, stream);
+    return launch_bwd_typed<io_f32>(p, a, stream);
+}
+
+}  // namespace ssm

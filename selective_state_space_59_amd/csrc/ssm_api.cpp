@@ -267,4 +267,98 @@ ssm_status_t ssm_state_update(const ssm_state_update_args_t *a, void *stream) {
     return ok();
 }
 
+static ssm_status_t check_bwd(const ssm_scan_bwd_args_t *a, size_t *need_out) {
+    if (!a) return fail(SSM_ERR_NULL_ARG, "args is NULL");
+    if (a->io_dtype != SSM_F32 && a->io_dtype != SSM_BF16)
+        return fail(SSM_ERR_BAD_DTYPE, "io_dtype %d is not SSM_F32 or SSM_BF16", a->io_dtype);
+    if (a->batch < 0 || a->seqlen < 0)
+        return fail(SSM_ERR_BAD_SHAPE, "negative batch (%lld) or seqlen (%lld)", (long long)a->batch,
+                    (long long)a->seqlen);
+    if (a->dim < 1) return fail(SSM_ERR_BAD_SHAPE, "dim must be >= 1");
+    if (a->dstate < 1) return fail(SSM_ERR_BAD_SHAPE, "dstate must be >= 1");
+    if (a->dstate != SSM_MAX_DSTATE)
+        return fail(SSM_ERR_UNSUPPORTED, "the backward pass supports dstate == %d only", SSM_MAX_DSTATE);
+    if (a->conv_k != 0 || a->conv_w || a->conv_b || a->dconv_w || a->dconv_b)
+        return fail(SSM_ERR_UNSUPPORTED, "the backward pass has no conv prologue (conv_k must be 0)");
+    if (a->delta_softplus != 0 && a->delta_softplus != 1)
+        return fail(SSM_ERR_UNSUPPORTED, "delta_softplus must be 0 or 1");
+    if (!mul_ok(a->batch, a->seqlen, a->dim) || !mul_ok(a->batch, a->seqlen, a->dstate) ||
+        !mul_ok(a->batch, a->dim, a->dstate))
+        return fail(SSM_ERR_BAD_SHAPE, "sizes overflow");
+    const int64_t B = a->batch, L = a->seqlen, D = a->dim, N = a->dstate;
+    const int64_t es = io_bytes(a->io_dtype);
+    *need_out = (B > 0) ? ssm::scan_bwd_workspace_bytes(*a) : 0;
+    if (B == 0) return SSM_OK;
+    if (!a->A) return fail(SSM_ERR_NULL_ARG, "A is NULL");
+    if (!a->dA) return fail(SSM_ERR_NULL_ARG, "dA is NULL");
+    if (L > 0) {
+        const struct { const void *p; const char *name; } req[] = {
+            {a->x, "x"}, {a->delta, "delta"}, {a->Bm, "Bm"}, {a->Cm, "Cm"}, {a->dy, "dy"},
+            {a->dx, "dx"}, {a->ddelta, "ddelta"}, {a->dBm, "dBm"}, {a->dCm, "dCm"}};
+        for (const auto &r : req)
+            if (!r.p) return fail(SSM_ERR_NULL_ARG, "%s is NULL", r.name);
+        if (a->z && !a->dz) return fail(SSM_ERR_NULL_ARG, "dz is NULL but z is given");
+    }
+    if (!a->z && a->dz) return fail(SSM_ERR_BAD_SHAPE, "dz given without z");
+    const void *io_ptrs[] = {a->x, a->delta, a->Bm, a->Cm, a->z, a->dy, a->dx, a->ddelta, a->dz};
+    for (const void *p : io_ptrs)
+        if (!aligned(p, es)) return fail(SSM_ERR_ALIGN, "an io_dtype pointer is not %lld-byte aligned", (long long)es);
+    const void *f_ptrs[] = {a->A, a->Dskip, a->delta_bias, a->h0, a->dh_final, a->dA, a->dBm, a->dCm,
+                            a->dDskip, a->ddelta_bias, a->dh0};
+    for (const void *p : f_ptrs)
+        if (!aligned(p, 4)) return fail(SSM_ERR_ALIGN, "an fp32 pointer is not 4-byte aligned");
+    const Range inputs[] = {
+        range(a->x, B * L * D, es, "x"),          range(a->delta, B * L * D, es, "delta"),
+        range(a->Bm, B * L * N, es, "Bm"),        range(a->Cm, B * L * N, es, "Cm"),
+        range(a->z, B * L * D, es, "z"),          range(a->dy, B * L * D, es, "dy"),
+        range(a->A, D * N, 4, "A"),               range(a->Dskip, D, 4, "Dskip"),
+        range(a->delta_bias, D, 4, "delta_bias"), range(a->h0, B * D * N, 4, "h0"),
+        range(a->dh_final, B * D * N, 4, "dh_final"),
+    };
+    const Range outputs[] = {
+        range(a->dx, B * L * D, es, "dx"),        range(a->ddelta, B * L * D, es, "ddelta"),
+        range(a->dz, B * L * D, es, "dz"),        range(a->dA, D * N, 4, "dA"),
+        range(a->dBm, B * L * N, 4, "dBm"),       range(a->dCm, B * L * N, 4, "dCm"),
+        range(a->dDskip, D, 4, "dDskip"),         range(a->ddelta_bias, D, 4, "ddelta_bias"),
+        range(a->dh0, B * D * N, 4, "dh0"),
+    };
+    const int nout = (int)(sizeof(outputs) / sizeof(outputs[0]));
+    for (int i = 0; i < nout; ++i) {
+        for (const Range &r : inputs)
+            if (overlaps(outputs[i], r)) return fail(SSM_ERR_ALIAS, "%s overlaps %s", outputs[i].name, r.name);
+        for (int k = i + 1; k < nout; ++k)
+            if (overlaps(outputs[i], outputs[k]))
+                return fail(SSM_ERR_ALIAS, "%s overlaps %s", outputs[i].name, outputs[k].name);
+    }
+    if (*need_out > 0) {
+        if (!a->workspace) return fail(SSM_ERR_WORKSPACE, "workspace of %zu bytes required", *need_out);
+        if (a->workspace_bytes < *need_out)
+            return fail(SSM_ERR_WORKSPACE, "workspace has %zu bytes, %zu required", a->workspace_bytes, *need_out);
+        if (!aligned(a->workspace, 256)) return fail(SSM_ERR_WORKSPACE, "workspace is not 256-byte aligned");
+        const Range ws = range(a->workspace, (int64_t)*need_out, 1, "workspace");
+        for (const Range &r : inputs)
+            if (overlaps(ws, r)) return fail(SSM_ERR_ALIAS, "workspace overlaps %s", r.name);
+        for (const Range &r : outputs)
+            if (overlaps(ws, r)) return fail(SSM_ERR_ALIAS, "workspace overlaps %s", r.name);
+    }
+    return SSM_OK;
+}
+
+size_t ssm_selective_scan_bwd_workspace_size(const ssm_scan_bwd_args_t *a) {
+    if (!a || a->batch < 0 || a->seqlen < 0 || a->dim < 1 || a->dstate != SSM_MAX_DSTATE ||
+        !mul_ok(a->batch, a->seqlen, a->dim) || !mul_ok(a->batch, a->dim, a->dstate))
+        return (size_t)-1;
+    return a->batch > 0 ? ssm::scan_bwd_workspace_bytes(*a) : 0;
+}
+
+ssm_status_t ssm_selective_scan_bwd(const ssm_scan_bwd_args_t *a, void *stream) {
+    size_t need = 0;
+    const ssm_status_t s = check_bwd(a, &need);
+    if (s != SSM_OK) return s;
+    if (a->batch == 0) return ok();
+    const hipError_t e = ssm::launch_scan_bwd(*a, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(SSM_ERR_HIP, "HIP error: %s", hipGetErrorString(e));
+    return ok();
+}
+
 }  // extern "C"

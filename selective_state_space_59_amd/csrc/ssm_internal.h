@@ -25,6 +25,10 @@ hipError_t launch_conv1d_silu(int64_t B, int64_t L, int64_t D, int K, int io_dty
 // Decode step.  a.batch > 0.
 hipError_t launch_state_update(const ssm_state_update_args_t &a, hipStream_t stream);
 
+// Scan backward: workspace bytes and launch (a.batch > 0; a.seqlen may be 0).
+size_t scan_bwd_workspace_bytes(const ssm_scan_bwd_args_t &a);
+hipError_t launch_scan_bwd(const ssm_scan_bwd_args_t &a, hipStream_t stream);
+
 // Copy or zero-fill the final state for an empty (L == 0) scan.
 hipError_t launch_empty_scan_state(const ssm_scan_args_t &a, hipStream_t stream);
 

@@ -35,7 +35,8 @@ MAX_CONV_K = 4
 
 EXPORTED_SYMBOLS = ("ssm_selective_scan_workspace_size", "ssm_selective_scan_fwd",
                     "ssm_causal_conv1d_silu", "ssm_state_update", "ssm_status_string",
-                    "ssm_last_error_message", "ssm_abi_version")
+                    "ssm_last_error_message", "ssm_abi_version",
+                    "ssm_selective_scan_bwd_workspace_size", "ssm_selective_scan_bwd")
 
 _P = ctypes.c_void_p
 _I64 = ctypes.c_int64
@@ -60,6 +61,18 @@ class StateUpdateArgs(ctypes.Structure):
                 ("state", _P), ("x", _P), ("delta", _P), ("z", _P), ("Bm", _P), ("Cm", _P),
                 ("A", _P), ("Dskip", _P), ("delta_bias", _P), ("y", _P),
                 ("conv_k", _I64), ("conv_w", _P), ("conv_b", _P), ("conv_state", _P)]
+
+
+class ScanBwdArgs(ctypes.Structure):
+    """Mirror of ssm_scan_bwd_args_t."""
+    _fields_ = [("batch", _I64), ("seqlen", _I64), ("dim", _I64), ("dstate", _I64),
+                ("io_dtype", _I32), ("delta_softplus", _I32), ("conv_k", _I64),
+                ("x", _P), ("delta", _P), ("Bm", _P), ("Cm", _P), ("z", _P),
+                ("A", _P), ("Dskip", _P), ("delta_bias", _P), ("conv_w", _P), ("conv_b", _P),
+                ("h0", _P), ("dy", _P), ("dh_final", _P),
+                ("dx", _P), ("ddelta", _P), ("dz", _P), ("dA", _P), ("dBm", _P), ("dCm", _P),
+                ("dDskip", _P), ("ddelta_bias", _P), ("dconv_w", _P), ("dconv_b", _P),
+                ("dh0", _P), ("workspace", _P), ("workspace_bytes", ctypes.c_size_t)]
 
 
 class SSMError(RuntimeError):
@@ -93,6 +106,10 @@ def lib() -> ctypes.CDLL:
         L.ssm_last_error_message.restype = ctypes.c_char_p
         L.ssm_abi_version.argtypes = []
         L.ssm_abi_version.restype = ctypes.c_int
+        L.ssm_selective_scan_bwd_workspace_size.argtypes = [ctypes.POINTER(ScanBwdArgs)]
+        L.ssm_selective_scan_bwd_workspace_size.restype = ctypes.c_size_t
+        L.ssm_selective_scan_bwd.argtypes = [ctypes.POINTER(ScanBwdArgs), _P]
+        L.ssm_selective_scan_bwd.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -328,3 +345,52 @@ def state_update(state: torch.Tensor, x: torch.Tensor, delta: torch.Tensor, A: t
                         conv_state=_ptr(conv_state) if K > 1 else None)
     _check(lib().ssm_state_update(ctypes.byref(a), _stream(dev)), "ssm_state_update")
     return y
+
+
+def selective_scan_bwd(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, Bm: torch.Tensor,
+                       Cm: torch.Tensor, dy: torch.Tensor, Dskip: Optional[torch.Tensor] = None,
+                       z: Optional[torch.Tensor] = None,
+                       delta_bias: Optional[torch.Tensor] = None, delta_softplus: bool = False,
+                       h0: Optional[torch.Tensor] = None,
+                       dh_final: Optional[torch.Tensor] = None,
+                       workspace: Optional[torch.Tensor] = None) -> dict:
+    """ssm_selective_scan_bwd: gradients of the scan (no conv prologue, N = 16).
+
+    Returns a dict with dx, ddelta (x's dtype), dA, dBm, dCm (float32) and, for the
+    optional inputs given, dz, dDskip, ddelta_bias, dh0."""
+    a, dev = _scan_args(x, delta, A, Bm, Cm, Dskip, z, delta_bias, delta_softplus, None, None,
+                        h0, torch.empty_like(x), None)
+    Bsz, L, D = x.shape
+    N = A.shape[1]
+    io = x.dtype
+    _req(dy, "dy", (Bsz, L, D), io, dev)
+    _opt(dh_final, "dh_final", (Bsz, D, N), torch.float32, dev)
+    f32 = dict(device=dev, dtype=torch.float32)
+    out = dict(dx=torch.empty_like(x), ddelta=torch.empty_like(x), dA=torch.empty(D, N, **f32),
+               dBm=torch.empty(Bsz, L, N, **f32), dCm=torch.empty(Bsz, L, N, **f32))
+    if z is not None:
+        out["dz"] = torch.empty_like(x)
+    if Dskip is not None:
+        out["dDskip"] = torch.empty(D, **f32)
+    if delta_softplus:
+        out["ddelta_bias"] = torch.empty(D, **f32)
+    if h0 is not None:
+        out["dh0"] = torch.empty(Bsz, D, N, **f32)
+    g = lambda k: _ptr(out.get(k))
+    b = ScanBwdArgs(batch=Bsz, seqlen=L, dim=D, dstate=N, io_dtype=a.io_dtype,
+                    delta_softplus=a.delta_softplus, conv_k=0, x=a.x, delta=a.delta, Bm=a.Bm,
+                    Cm=a.Cm, z=a.z, A=a.A, Dskip=a.Dskip, delta_bias=a.delta_bias, h0=a.h0,
+                    dy=_ptr(dy), dh_final=_ptr(dh_final), dx=g("dx"), ddelta=g("ddelta"),
+                    dz=g("dz"), dA=g("dA"), dBm=g("dBm"), dCm=g("dCm"), dDskip=g("dDskip"),
+                    ddelta_bias=g("ddelta_bias"), dh0=g("dh0"))
+    need = lib().ssm_selective_scan_bwd_workspace_size(ctypes.byref(b))
+    if need == ctypes.c_size_t(-1).value:
+        _check(lib().ssm_selective_scan_bwd(ctypes.byref(b), None), "ssm_selective_scan_bwd")
+    if need > 0:
+        ws = workspace if workspace is not None else _workspace(dev, need)
+        if ws.device != dev or ws.numel() * ws.element_size() < need:
+            raise ValueError("workspace must be a device tensor of >= %d bytes" % need)
+        b.workspace = ws.data_ptr()
+        b.workspace_bytes = ws.numel() * ws.element_size()
+    _check(lib().ssm_selective_scan_bwd(ctypes.byref(b), _stream(dev)), "ssm_selective_scan_bwd")
+    return out

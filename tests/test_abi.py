@@ -62,6 +62,7 @@ C_LAYOUT = r"""
 int main(void) {
   printf("ssm_scan_args_t size %zu\n", sizeof(ssm_scan_args_t));
   printf("ssm_state_update_args_t size %zu\n", sizeof(ssm_state_update_args_t));
+  printf("ssm_scan_bwd_args_t size %zu\n", sizeof(ssm_scan_bwd_args_t));
   %FIELDS%
   return 0;
 }
@@ -71,7 +72,8 @@ int main(void) {
 def test_ctypes_structs_match_c_layout():
     lines = []
     for cname, cls in (("ssm_scan_args_t", ssm.ScanArgs),
-                       ("ssm_state_update_args_t", ssm.StateUpdateArgs)):
+                       ("ssm_state_update_args_t", ssm.StateUpdateArgs),
+                       ("ssm_scan_bwd_args_t", ssm.ScanBwdArgs)):
         for f, _ in cls._fields_:
             lines.append("F(%s, %s)" % (cname, f))
     with tempfile.TemporaryDirectory() as d:
@@ -88,8 +90,10 @@ def test_ctypes_structs_match_c_layout():
             got[(t, f)] = int(v)
     assert got[("ssm_scan_args_t", "size")] == ctypes.sizeof(ssm.ScanArgs)
     assert got[("ssm_state_update_args_t", "size")] == ctypes.sizeof(ssm.StateUpdateArgs)
+    assert got[("ssm_scan_bwd_args_t", "size")] == ctypes.sizeof(ssm.ScanBwdArgs)
     for cname, cls in (("ssm_scan_args_t", ssm.ScanArgs),
-                       ("ssm_state_update_args_t", ssm.StateUpdateArgs)):
+                       ("ssm_state_update_args_t", ssm.StateUpdateArgs),
+                       ("ssm_scan_bwd_args_t", ssm.ScanBwdArgs)):
         for f, _ in cls._fields_:
             assert got[(cname, f)] == getattr(cls, f).offset, (cname, f)
 
@@ -305,3 +309,48 @@ def test_binding_refuses_cpu_tensors():
     x = torch.zeros(1, 4, 8)
     with pytest.raises(ValueError):
         ssm.selective_scan_fwd(x, x, torch.zeros(8, 4), torch.zeros(1, 4, 4), torch.zeros(1, 4, 4))
+
+
+# ------------------------------------------------------------- backward checks
+def bwd_args(**kw):
+    a = ssm.ScanBwdArgs(batch=2, seqlen=8, dim=64, dstate=16, io_dtype=ssm.SSM_BF16,
+                        delta_softplus=0, conv_k=0, x=addr(0), delta=addr(1), Bm=addr(2),
+                        Cm=addr(3), z=addr(4), A=addr(5), Dskip=addr(6), dy=addr(7),
+                        dx=addr(8), ddelta=addr(9), dz=addr(10), dA=addr(11), dBm=addr(12),
+                        dCm=addr(13), dDskip=addr(14), workspace=addr(15), workspace_bytes=1 << 34)
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def run_bwd(a):
+    return ssm.lib().ssm_selective_scan_bwd(ctypes.byref(a), None)
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("io_dtype", 3, ssm.SSM_ERR_BAD_DTYPE),
+    ("batch", -1, ssm.SSM_ERR_BAD_SHAPE),
+    ("dstate", 8, ssm.SSM_ERR_UNSUPPORTED),       # this version: N == 16
+    ("conv_k", 4, ssm.SSM_ERR_UNSUPPORTED),       # no conv prologue yet
+    ("dy", None, ssm.SSM_ERR_NULL_ARG),
+    ("dx", None, ssm.SSM_ERR_NULL_ARG),
+    ("dBm", None, ssm.SSM_ERR_NULL_ARG),
+    ("dA", None, ssm.SSM_ERR_NULL_ARG),
+    ("dz", None, ssm.SSM_ERR_NULL_ARG),           # z given
+    ("dx", addr(0, 64), ssm.SSM_ERR_ALIAS),       # inside x
+    ("dBm", addr(13), ssm.SSM_ERR_ALIAS),         # == dCm
+    ("dA", addr(15), ssm.SSM_ERR_ALIAS),          # inside the workspace
+    ("dx", addr(8, 1), ssm.SSM_ERR_ALIGN),
+    ("workspace", None, ssm.SSM_ERR_WORKSPACE),
+])
+def test_bwd_rejects_bad_arguments(field, value, status):
+    assert run_bwd(bwd_args(**{field: value})) == status
+
+
+def test_bwd_dz_without_z_and_empty_batch():
+    assert run_bwd(bwd_args(z=None)) == ssm.SSM_ERR_BAD_SHAPE
+    assert run_bwd(bwd_args(batch=0)) == ssm.SSM_OK
+    L = ssm.lib()
+    assert L.ssm_selective_scan_bwd_workspace_size(ctypes.byref(bwd_args(dstate=4))) == \
+        ctypes.c_size_t(-1).value
+    assert 0 < L.ssm_selective_scan_bwd_workspace_size(ctypes.byref(bwd_args())) < (1 << 40)
