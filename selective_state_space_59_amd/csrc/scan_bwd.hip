@@ -36,10 +36,14 @@ namespace {
 
 constexpr int kRowN = 16;            // lanes per row = state entries (N = 16)
 constexpr int kStep = 16;            // steps per block
-constexpr int kWavesB = 8;           // waves per workgroup
+constexpr int kWavesB = 12;          // waves per workgroup (3 per SIMD)
 constexpr int kChB = 4 * kWavesB;    // channels per workgroup
-constexpr int kTS = kStep + 4;       // padded row stride of a transpose area
-constexpr int kTrArea = 4 * kRowN * kTS;  // floats per wave and transpose area
+// Transpose area of one channel: [16 entries][kTS steps], then padding so
+// that the 4 channel areas of a wave start 16 banks apart (336 = 16 mod 32).
+constexpr int kTS = kStep + 4;
+constexpr int kChArea = kRowN * kTS + 16;
+constexpr int kTrWave = 4 * kChArea;          // floats per wave and transpose area
+constexpr int kRedWave = 2 * kRowN * kTS;     // per wave: [dB|dC][16 entries][kTS steps]
 
 struct BwdParams {
     int64_t B, L, D, G;              // G: workgroups per batch row
@@ -72,17 +76,20 @@ __device__ __forceinline__ float bcast_row(float v) {
     return __builtin_amdgcn_update_dpp(0.0f, v, 0x150 + K, 0xf, 0xf, false);
 }
 
-__device__ __forceinline__ float phi_f(float zz, float e) {
+// phi(z) = (e^z - 1)/z and psi(z) = phi'(z) = (e^z - phi(z))/z given e = e^z
+// and r = 1/z: degree-6 series below |z| = 1/4 (no cancellation), the
+// quotients beyond (hardware reciprocal, no division).
+__device__ __forceinline__ float phi_f(float zz, float e, float r) {
     const float s = 1.0f + zz * (0.5f + zz * (1.0f / 6.0f + zz * (1.0f / 24.0f +
                     zz * (1.0f / 120.0f + zz * (1.0f / 720.0f + zz * (1.0f / 5040.0f))))));
-    return fabsf(zz) < 0.25f ? s : (e - 1.0f) / zz;
+    return fabsf(zz) < 0.25f ? s : (e - 1.0f) * r;
 }
-__device__ __forceinline__ float psi_f(float zz, float e) {
+__device__ __forceinline__ float psi_f(float zz, float e, float ph, float r) {
     const float s = 0.5f + zz * (1.0f / 3.0f + zz * (1.0f / 8.0f + zz * (1.0f / 30.0f +
                     zz * (1.0f / 144.0f + zz * (1.0f / 840.0f + zz * (1.0f / 5760.0f))))));
-    return fabsf(zz) < 0.25f ? s : (e * (zz - 1.0f) + 1.0f) / (zz * zz);
+    return fabsf(zz) < 0.25f ? s : (e - ph) * r;
 }
-__device__ __forceinline__ float sigmoid_f(float v) { return 1.0f / (1.0f + __expf(-v)); }
+__device__ __forceinline__ float sigmoid_f(float v) { return hw_rcp(1.0f + hw_exp2(-v * kLog2e)); }
 __device__ __forceinline__ float dsilu_f(float v) {
     const float s = sigmoid_f(v);
     return s * (1.0f + v * (1.0f - s));
@@ -120,45 +127,79 @@ __device__ __forceinline__ void own_inputs(const BwdParams &p, const LaneB &l, i
     }
 }
 
+// Entry n of the B (or C) rows of the block's 16 steps.  Steps past the end
+// read the last row instead (no branches): there dt and u are 0, so those
+// values reach no output.
 template <typename IO>
-__device__ __forceinline__ float load_bc(const void *t, const BwdParams &p, const LaneB &l, int64_t step) {
-    return step < p.L ? load_io<IO>(t, (l.b * p.L + step) * kRowN + l.n) : 0.0f;
+__device__ __forceinline__ void load_rows(const void *t, const BwdParams &p, const LaneB &l, int64_t t0,
+                                          float (&v)[kStep]) {
+    const typename IO::storage *row = static_cast<const typename IO::storage *>(t) + l.b * p.L * kRowN + l.n;
+#pragma unroll
+    for (int k = 0; k < kStep; ++k) {
+        const int64_t tk = t0 + k < p.L ? t0 + k : p.L - 1;
+        v[k] = load_io<IO>(row, tk * kRowN);
+    }
 }
 
 // Pass 1: states entering every block.
-template <typename IO>
-__global__ __launch_bounds__(64 * kWavesB) void bwd_ckpt_kernel(BwdParams p) {
-    const LaneB l = lane_setup(p);
-    const float a = l.valid ? p.A[l.d * kRowN + l.n] : 0.0f;
+// dt phi(dt A) = (e - 1)/A: in waves where every |A| >= 1/16 (FAST) as
+// (e - 1) times 1/A, otherwise through phi (series near 0).
+template <bool FAST>
+__device__ __forceinline__ float dtphi(float dt, float a, float ia, float e) {
+    if (FAST) return (e - 1.0f) * ia;
+    const float zz = dt * a;
+    return dt * phi_f(zz, e, hw_rcp(zz));
+}
+
+template <typename IO, bool FAST>
+__device__ __forceinline__ void ckpt_body(const BwdParams &p, const LaneB &l, float a, float ia, float h) {
     const float a2 = a * kLog2e;
-    float h = (l.valid && p.h0) ? p.h0[(l.b * p.D + l.d) * kRowN + l.n] : 0.0f;
     const int64_t nb = (p.L + kStep - 1) / kStep;
     for (int64_t j = 0; j < nb; ++j) {
         if (l.valid) p.ckpt[((j * p.B + l.b) * p.D + l.d) * kRowN + l.n] = h;
-        float u, raw, dt;
+        float u, raw, dt, bv[kStep];
         own_inputs<IO>(p, l, j * kStep + l.n, u, raw, dt);
+        load_rows<IO>(p.Bm, p, l, j * kStep, bv);
         sfor<kStep>([&](auto K) {
             constexpr int k = decltype(K)::value;
             const float dtk = bcast_row<k>(dt), uk = bcast_row<k>(u);
-            const float bk = load_bc<IO>(p.Bm, p, l, j * kStep + k);
             const float e = hw_exp2(dtk * a2);
-            h = e * h + (dtk * phi_f(dtk * a, e)) * bk * uk;
+            h = __builtin_fmaf(e, h, dtphi<FAST>(dtk, a, ia, e) * (bv[k] * uk));
         });
     }
 }
 
-// Pass 2: the adjoint, blocks from last to first.
 template <typename IO>
-__global__ __launch_bounds__(64 * kWavesB) void bwd_kernel(BwdParams p) {
-    extern __shared__ __attribute__((aligned(16))) float lds[];
+__global__ __launch_bounds__(64 * kWavesB) void bwd_ckpt_kernel(BwdParams p) {
     const LaneB l = lane_setup(p);
+    const float a = l.valid ? p.A[l.d * kRowN + l.n] : 0.0f;
+    const float ia = a != 0.0f ? 1.0f / a : 0.0f;
+    const float h = (l.valid && p.h0) ? p.h0[(l.b * p.D + l.d) * kRowN + l.n] : 0.0f;
+    if (__all(!l.valid || fabsf(a) >= 0.0625f)) ckpt_body<IO, true>(p, l, a, ia, h);
+    else ckpt_body<IO, false>(p, l, a, ia, h);
+}
+
+typedef float mfma4_t __attribute__((ext_vector_type(4)));
+
+// Sum over the wave's 4 channels of each lane's value, for every entry n:
+// a 16x16x4 fp32 MFMA with the ones matrix as A and the lane values as B
+// (B[c][n] is lane (c, n)); every lane gets the sum for its n.
+__device__ __forceinline__ float sum_channels(float v) {
+    const mfma4_t zero = {0.0f, 0.0f, 0.0f, 0.0f};
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(1.0f, v, zero, 0, 0, 0)[0];
+}
+
+// Pass 2: the adjoint, blocks from last to first.
+template <typename IO, bool FAST>
+__device__ __forceinline__ void bwd_body(const BwdParams &p, const LaneB &l, float *lds, float a, float ia) {
     const int n = l.n, c = l.c;
-    // Two transpose areas per wave ([c][n][k], stride kTS), then the
-    // workgroup's dB / dC partials [2][kChB][16 k][16 n].
-    float *tr0 = lds + (l.wave * 2) * kTrArea;
-    float *tr1 = tr0 + kTrArea;
-    float *red = lds + kWavesB * 2 * kTrArea;
-    const float a = l.valid ? p.A[l.d * kRowN + n] : 0.0f;
+    // Per wave: two transpose areas (channel c at c * kChArea, [n][k] with
+    // stride kTS) and the wave's dB / dC sums [2][16 n][kTS].
+    float *tr0 = lds + l.wave * (2 * kTrWave + kRedWave);
+    float *tr1 = tr0 + kTrWave;
+    float *redw = tr1 + kTrWave;
+    float *my0 = tr0 + c * kChArea + n * kTS;  // this lane's row in the areas
+    float *my1 = tr1 + c * kChArea + n * kTS;
     const float a2 = a * kLog2e;
     const float dsk = (l.valid && p.Dskip) ? p.Dskip[l.d] : 0.0f;
     const float bias = (l.valid && p.dbias) ? p.dbias[l.d] : 0.0f;
@@ -170,8 +211,10 @@ __global__ __launch_bounds__(64 * kWavesB) void bwd_kernel(BwdParams p) {
     for (int64_t j = nb - 1; j >= 0; --j) {
         const int64_t t0 = j * kStep;
         const int64_t tme = t0 + n;  // this lane's own step
-        float u, raw, dt;
+        float u, raw, dt, bv[kStep], cv[kStep];
         own_inputs<IO>(p, l, tme, u, raw, dt);
+        load_rows<IO>(p.Bm, p, l, t0, bv);
+        load_rows<IO>(p.Cm, p, l, t0, cv);
         float zv = 0.0f, gv = 0.0f;
         if (l.valid && tme < p.L) {
             const int64_t i = (l.b * p.L + tme) * p.D + l.d;
@@ -179,24 +222,27 @@ __global__ __launch_bounds__(64 * kWavesB) void bwd_kernel(BwdParams p) {
             if (p.z) zv = load_io<IO>(p.z, i);
         }
         // -- forward over the block from its checkpoint ----------------------
-        float hp[kStep], ev[kStep];
+        float hp[kStep], dp[kStep];  // h_{t-1}, dt phi(dt A)
         float h = l.valid ? p.ckpt[((j * p.B + l.b) * p.D + l.d) * kRowN + n] : 0.0f;
-        sfor<kStep>([&](auto K) {
-            constexpr int k = decltype(K)::value;
-            const float dtk = bcast_row<k>(dt), uk = bcast_row<k>(u);
-            const float bk = load_bc<IO>(p.Bm, p, l, t0 + k);
-            const float ck = load_bc<IO>(p.Cm, p, l, t0 + k);
-            const float e = hw_exp2(dtk * a2);
-            hp[k] = h;
-            ev[k] = e;
-            h = e * h + (dtk * phi_f(dtk * a, e)) * bk * uk;
-            tr0[(c * kRowN + n) * kTS + k] = ck * h;  // partial read-out of step k
+        sfor<kStep / 4>([&](auto G) {
+            constexpr int g4 = 4 * decltype(G)::value;
+            float pk[4];
+            sfor<4>([&](auto K) {
+                constexpr int k = g4 + decltype(K)::value;
+                const float dtk = bcast_row<k>(dt), uk = bcast_row<k>(u);
+                const float e = hw_exp2(dtk * a2);
+                hp[k] = h;
+                dp[k] = dtphi<FAST>(dtk, a, ia, e);
+                h = __builtin_fmaf(e, h, dp[k] * (bv[k] * uk));
+                pk[decltype(K)::value] = cv[k] * h;  // partial read-out of step k
+            });
+            *reinterpret_cast<float4 *>(my0 + g4) = make_float4(pk[0], pk[1], pk[2], pk[3]);
         });
         __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
         // lane (c, n) finishes its own step n: y_hat, gy, dz
         float yhat = dsk * u;
 #pragma unroll
-        for (int i = 0; i < kRowN; ++i) yhat += tr0[(c * kRowN + i) * kTS + n];
+        for (int i = 0; i < kRowN; ++i) yhat += tr0[c * kChArea + i * kTS + n];
         float gy = gv;
         if (p.z) {
             gy = gv * silu(zv);
@@ -205,33 +251,41 @@ __global__ __launch_bounds__(64 * kWavesB) void bwd_kernel(BwdParams p) {
         accD += gy * u;
         __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
         // -- adjoint over the block, last step first ---------------------------
-        sfor<kStep>([&](auto K) {
-            constexpr int k = kStep - 1 - decltype(K)::value;
-            const float gyk = bcast_row<k>(gy), uk = bcast_row<k>(u), dtk = bcast_row<k>(dt);
-            const float bk = load_bc<IO>(p.Bm, p, l, t0 + k);
-            const float ck = load_bc<IO>(p.Cm, p, l, t0 + k);
-            const float e = ev[k];
-            const float hprev = hp[k];
-            const float hcur = k == kStep - 1 ? h : hp[k + 1 < kStep ? k + 1 : 0];
-            const float lt = __builtin_fmaf(ck, gyk, lam);  // dL/dh_t
-            const float zz = dtk * a;
-            const float ph = phi_f(zz, e);
-            const float bbar = dtk * ph * bk;
-            const float dabar = lt * hprev, dbbar = lt * uk;
-            tr0[(c * kRowN + n) * kTS + k] = lt * bbar;                      // -> du_k
-            tr1[(c * kRowN + n) * kTS + k] = e * (dabar * a + dbbar * bk);   // -> ddt_k
-            accA += e * dabar * dtk + dbbar * bk * dtk * dtk * psi_f(zz, e);
-            red[((0 * kChB + 4 * l.wave + c) * kStep + k) * kRowN + n] = dbbar * dtk * ph;  // dB
-            red[((1 * kChB + 4 * l.wave + c) * kStep + k) * kRowN + n] = gyk * hcur;        // dC
-            lam = e * lt;
+        sfor<kStep / 4>([&](auto G) {
+            constexpr int g4 = kStep - 4 - 4 * decltype(G)::value;  // 12, 8, 4, 0
+            float pdu[4], pdt[4], sb[4], sc[4];
+            sfor<4>([&](auto K) {
+                constexpr int kk = 3 - decltype(K)::value;
+                constexpr int k = g4 + kk;
+                const float gyk = bcast_row<k>(gy), uk = bcast_row<k>(u), dtk = bcast_row<k>(dt);
+                const float e = hw_exp2(dtk * a2), dtph = dp[k], bk = bv[k];
+                const float hcur = k == kStep - 1 ? h : hp[k + 1 < kStep ? k + 1 : 0];
+                const float lt = __builtin_fmaf(cv[k], gyk, lam);  // dL/dh_t
+                const float dabar = lt * hp[k], dbbar = lt * uk;
+                pdu[kk] = lt * (dtph * bk);
+                pdt[kk] = e * __builtin_fmaf(dabar, a, dbbar * bk);
+                const float zz = dtk * a, r = hw_rcp(zz);
+                const float ph = (e - 1.0f) * r;  // phi where |zz| >= 1/4 (psi's series covers the rest)
+                accA = __builtin_fmaf(e * dabar, dtk, accA);
+                accA = __builtin_fmaf(dbbar * bk * dtk, dtk * psi_f(zz, e, ph, r), accA);
+                sb[kk] = sum_channels(dbbar * dtph);
+                sc[kk] = sum_channels(gyk * hcur);
+                lam = e * lt;
+            });
+            *reinterpret_cast<float4 *>(my0 + g4) = make_float4(pdu[0], pdu[1], pdu[2], pdu[3]);
+            *reinterpret_cast<float4 *>(my1 + g4) = make_float4(pdt[0], pdt[1], pdt[2], pdt[3]);
+            if (c == 0) {
+                *reinterpret_cast<float4 *>(redw + n * kTS + g4) = make_float4(sb[0], sb[1], sb[2], sb[3]);
+                *reinterpret_cast<float4 *>(redw + (kRowN + n) * kTS + g4) = make_float4(sc[0], sc[1], sc[2], sc[3]);
+            }
         });
         __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
         {
             float du = dsk * gy, ddt = 0.0f;
 #pragma unroll
             for (int i = 0; i < kRowN; ++i) {
-                du += tr0[(c * kRowN + i) * kTS + n];
-                ddt += tr1[(c * kRowN + i) * kTS + n];
+                du += tr0[c * kChArea + i * kTS + n];
+                ddt += tr1[c * kChArea + i * kTS + n];
             }
             float draw = ddt;
             if (p.softplus) {
@@ -244,15 +298,17 @@ __global__ __launch_bounds__(64 * kWavesB) void bwd_kernel(BwdParams p) {
                 store_io<IO>(p.ddelta, i, draw);
             }
         }
-        // -- dB, dC: add the workgroup's channels ----------------------------
+        // -- dB, dC: add the workgroup's waves ---------------------------------
         __syncthreads();
         for (int item = threadIdx.x; item < 2 * kStep * kRowN; item += 64 * kWavesB) {
             const int tensor = item / (kStep * kRowN), kn = item % (kStep * kRowN);
+            const int k = kn / kRowN, nn = kn % kRowN;
             float s = 0.0f;
-            for (int r = 0; r < kChB; ++r) s += red[(tensor * kChB + r) * kStep * kRowN + kn];
-            const int64_t t = t0 + kn / kRowN;
+            for (int w = 0; w < kWavesB; ++w)
+                s += lds[w * (2 * kTrWave + kRedWave) + 2 * kTrWave + (tensor * kRowN + nn) * kTS + k];
+            const int64_t t = t0 + k;
             if (t < p.L)
-                p.partBC[(((int64_t)tensor * p.B + l.b) * p.G + grow) * p.L * kRowN + t * kRowN + kn % kRowN] = s;
+                p.partBC[(((int64_t)tensor * p.B + l.b) * p.G + grow) * p.L * kRowN + t * kRowN + nn] = s;
         }
         __syncthreads();
     }
@@ -270,6 +326,17 @@ __global__ __launch_bounds__(64 * kWavesB) void bwd_kernel(BwdParams p) {
         p.partD[l.b * p.D + l.d] = accD;
         p.partBias[l.b * p.D + l.d] = accBias;
     }
+}
+
+template <typename IO>
+__global__ __launch_bounds__(64 * kWavesB) __attribute__((amdgpu_waves_per_eu(3, 3)))
+void bwd_kernel(BwdParams p) {
+    extern __shared__ __attribute__((aligned(16))) float lds[];
+    const LaneB l = lane_setup(p);
+    const float a = l.valid ? p.A[l.d * kRowN + l.n] : 0.0f;
+    const float ia = a != 0.0f ? 1.0f / a : 0.0f;
+    if (__all(!l.valid || fabsf(a) >= 0.0625f)) bwd_body<IO, true>(p, l, lds, a, ia);
+    else bwd_body<IO, false>(p, l, lds, a, ia);
 }
 
 // dB, dC = sums of the workgroup partials of each batch row; fp32 outputs.
@@ -343,7 +410,7 @@ hipError_t launch_bwd_typed(const BwdParams &p, const ssm_scan_bwd_args_t &a, hi
     bwd_ckpt_kernel<IO><<<grid, 64 * kWavesB, 0, stream>>>(p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const size_t lds = (size_t)(kWavesB * 2 * kTrArea + 2 * kChB * kStep * kRowN) * sizeof(float);
+    const size_t lds = (size_t)(kWavesB * (2 * kTrWave + kRedWave)) * sizeof(float);
     bwd_kernel<IO><<<grid, 64 * kWavesB, lds, stream>>>(p);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
