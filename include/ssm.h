@@ -216,18 +216,21 @@ ssm_status_t ssm_state_update(const ssm_state_update_args_t *args, void *stream)
  *   dx       = sum_n lambda Bbar + Dskip gy;   ddelta by the chain rule through
  *              exp(dt A), Bbar and the softplus;   dz = dy (C h + D u) silu'(z);
  *   dA, dDskip, ddelta_bias summed over batch and time; dBm, dCm summed over
- *   channels; dh0 = exp(dt_0 A) lambda_0.
- * This version supports N == 16 and no conv prologue (conv_k == 0; other
- * values give SSM_ERR_UNSUPPORTED); the forward's input fields have the same
- * meaning and shapes as in ssm_scan_args_t.
+ *   channels; dh0 = exp(dt_0 A) lambda_0;
+ *   with the conv prologue (u = silu(c), c the causal conv of x): dc = du
+ *   silu'(c), dx = the conv's transpose applied to dc, dconv_w and dconv_b
+ *   summed over batch and time (no conv state entering the sequence).
+ * This version supports N == 16 (other N give SSM_ERR_UNSUPPORTED); the
+ * forward's input fields have the same meaning and shapes as in
+ * ssm_scan_args_t.
  */
 typedef struct ssm_scan_bwd_args {
     int64_t batch, seqlen, dim, dstate; /* as in ssm_scan_args_t (dstate == 16)  */
     int32_t io_dtype;       /* of x, delta, Bm, Cm, z, dy, dx, ddelta, dz      */
     int32_t delta_softplus; /* as in ssm_scan_args_t                           */
-    int64_t conv_k;         /* must be 0                                       */
+    int64_t conv_k;         /* 0 or 1..SSM_MAX_CONV_K, as in ssm_scan_args_t   */
     const void *x, *delta, *Bm, *Cm, *z;            /* forward inputs            */
-    const float *A, *Dskip, *delta_bias, *conv_w, *conv_b, *h0; /* conv_w/_b NULL */
+    const float *A, *Dskip, *delta_bias, *conv_w, *conv_b, *h0;
     const void *dy;         /* (B,L,D) io_dtype, required                      */
     const float *dh_final;  /* (B,D,N) fp32, or NULL (= 0)                     */
     void *dx;               /* (B,L,D) io_dtype output, required               */
@@ -237,7 +240,8 @@ typedef struct ssm_scan_bwd_args {
     float *dBm, *dCm;       /* (B,L,N) fp32 outputs, required                  */
     float *dDskip;          /* (D) fp32 output, or NULL (not written)          */
     float *ddelta_bias;     /* (D) fp32 output, or NULL; 0 without softplus    */
-    float *dconv_w, *dconv_b; /* must be NULL                                  */
+    float *dconv_w;         /* (D,conv_k) fp32 output; required iff conv_k > 0 */
+    float *dconv_b;         /* (D) fp32 output, or NULL; only with conv_k > 0  */
     float *dh0;             /* (B,D,N) fp32 output, or NULL                    */
     void *workspace;        /* device scratch, 256-aligned                     */
     size_t workspace_bytes; /* >= ssm_selective_scan_bwd_workspace_size(args)  */

@@ -48,6 +48,9 @@ constexpr int kRedWave = 2 * kRowN * kTS;     // per wave: [dB|dC][16 entries][k
 struct BwdParams {
     int64_t B, L, D, G;              // G: workgroups per batch row
     int softplus;
+    int K;                           // conv prologue width, 0 for none
+    const float *conv_w, *conv_b;
+    float *dU;                       // [B][L][D] dL/du when K > 0 (then dx comes from conv_bwd)
     const void *x, *delta, *Bm, *Cm, *z, *dy;
     const float *A, *Dskip, *dbias, *h0, *dh_final;
     void *dx, *ddelta, *dz;
@@ -122,6 +125,14 @@ __device__ __forceinline__ void own_inputs(const BwdParams &p, const LaneB &l, i
     if (l.valid && t < p.L) {
         const int64_t i = (l.b * p.L + t) * p.D + l.d;
         u = load_io<IO>(p.x, i);
+        if (p.K > 0) {  // the conv prologue: u = silu(b + sum_k w_k x_{t-K+1+k})
+            float cacc = p.conv_b ? p.conv_b[l.d] : 0.0f;
+            for (int k = 0; k < p.K; ++k) {
+                const int64_t s = t - (p.K - 1) + k;
+                if (s >= 0) cacc = __builtin_fmaf(p.conv_w[l.d * p.K + k], load_io<IO>(p.x, (l.b * p.L + s) * p.D + l.d), cacc);
+            }
+            u = silu(cacc);
+        }
         raw = load_io<IO>(p.delta, i);
         dt = p.softplus ? softplus(raw + (p.dbias ? p.dbias[l.d] : 0.0f)) : raw;
     }
@@ -294,7 +305,8 @@ __device__ __forceinline__ void bwd_body(const BwdParams &p, const LaneB &l, flo
             }
             if (l.valid && tme < p.L) {
                 const int64_t i = (l.b * p.L + tme) * p.D + l.d;
-                store_io<IO>(p.dx, i, du);
+                if (p.K > 0) p.dU[i] = du;
+                else store_io<IO>(p.dx, i, du);
                 store_io<IO>(p.ddelta, i, draw);
             }
         }
@@ -339,6 +351,81 @@ void bwd_kernel(BwdParams p) {
     else bwd_body<IO, false>(p, l, lds, a, ia);
 }
 
+// Through the conv prologue (u = silu(c), c_t = b + sum_k w_k x_{t-K+1+k}):
+// one thread per (batch, channel, chunk of kConvChunk steps) walks time with
+// rolling windows of x and of dc = du silu'(c), writing
+//   dx_s = sum_k dc_{s+K-1-k} w_k            (three steps behind)
+// and the chunk's partial sums of dw_k = sum_t dc_t x_{t-K+1+k} and db.  The
+// windows are right-aligned to width 4, so no register is indexed by K.
+constexpr int kConvChunk = 256;
+template <typename IO>
+__global__ void conv_bwd_kernel(const void *x, const float *dU, const float *w, const float *cb, void *dx,
+                                float *pw, int64_t B, int64_t L, int64_t D, int K) {
+    const int64_t nch = (L + kConvChunk - 1) / kConvChunk;
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // d fastest
+    if (i >= nch * B * D) return;
+    const int64_t d = i % D, bc = i / D, b = bc % B, ch = bc / B;
+    const int64_t t0 = ch * kConvChunk, t1 = t0 + kConvChunk < L ? t0 + kConvChunk : L;
+    float wr[4], xw[4], dcw[4] = {0.0f, 0.0f, 0.0f, 0.0f}, dwr[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) wr[3 - j] = j < K ? w[d * K + K - 1 - j] : 0.0f;
+    const float bias = cb ? cb[d] : 0.0f;
+    const int64_t base = b * L * D + d;
+    // Before step t, xw[1..3] hold x_{t-3..t-1}; each step shifts one in.
+    xw[0] = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+        const int64_t s = t0 - 3 + j;
+        xw[j + 1] = s >= 0 ? load_io<IO>(x, base + s * D) : 0.0f;
+    }
+    float db = 0.0f;
+    for (int64_t t = t0; t < t1 + 3; ++t) {
+        xw[0] = xw[1];
+        xw[1] = xw[2];
+        xw[2] = xw[3];
+        xw[3] = t < L ? load_io<IO>(x, base + t * D) : 0.0f;
+        float dc = 0.0f;
+        if (t < L) {
+            float c = bias;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) c = __builtin_fmaf(wr[j], xw[j], c);
+            dc = dU[base + t * D] * dsilu_f(c);
+        }
+        if (t < t1) {
+            db += dc;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) dwr[j] = __builtin_fmaf(dc, xw[j], dwr[j]);
+        }
+        dcw[0] = dcw[1];
+        dcw[1] = dcw[2];
+        dcw[2] = dcw[3];
+        dcw[3] = dc;
+        const int64_t s = t - 3;
+        if (s >= t0 && s < t1) {
+            float v = 0.0f;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) v = __builtin_fmaf(dcw[j], wr[3 - j], v);
+            store_io<IO>(dx, base + s * D, v);
+        }
+    }
+    float *o = pw + ((ch * B + b) * D + d) * 5;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) o[j] = dwr[j];
+    o[4] = db;
+}
+
+// dconv_w (right-aligned partials mapped back to taps 0..K-1) and dconv_b.
+__global__ void conv_bwd_reduce_kernel(const float *pw, float *dw, float *db, int64_t nparts, int64_t D, int K) {
+    const int64_t d = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (d >= D) return;
+    float s[5] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+    for (int64_t q = 0; q < nparts; ++q)
+#pragma unroll
+        for (int j = 0; j < 5; ++j) s[j] += pw[(q * D + d) * 5 + j];
+    for (int k = 0; k < K; ++k) dw[d * K + k] = s[4 - K + k];
+    if (db) db[d] = s[4];
+}
+
 // dB, dC = sums of the workgroup partials of each batch row; fp32 outputs.
 __global__ void bwd_reduce_bc_kernel(const float *partBC, float *dB, float *dC, int64_t B, int64_t G,
                                      int64_t L) {
@@ -374,19 +461,21 @@ __global__ void bwd_reduce_params_kernel(const float *partA, const float *partD,
 
 // dh0 of an empty sequence: dh_final (or 0); dA etc. are 0.
 __global__ void bwd_empty_kernel(const float *dh_final, float *dh0, int64_t nbdn, float *dA, float *dD,
-                                 float *dbias, int64_t D) {
+                                 float *dbias, float *dcw, float *dcb, int64_t D, int K) {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (dh0 && i < nbdn) dh0[i] = dh_final ? dh_final[i] : 0.0f;
     if (i < D * kRowN) dA[i] = 0.0f;
+    if (dcw && i < D * K) dcw[i] = 0.0f;
     if (i < D) {
         if (dD) dD[i] = 0.0f;
         if (dbias) dbias[i] = 0.0f;
+        if (dcb) dcb[i] = 0.0f;
     }
 }
 
 struct BwdLayout {
-    int64_t G, nb;
-    size_t ckpt, partBC, partA, partD, partBias, total;
+    int64_t G, nb, nch;
+    size_t ckpt, partBC, partA, partD, partBias, dU, pconv, total;
 };
 
 size_t r256(size_t v) { return (v + 255) & ~(size_t)255; }
@@ -400,12 +489,16 @@ BwdLayout bwd_layout(const ssm_scan_bwd_args_t &a) {
     q.partA = r256((size_t)(a.batch * a.dim * kRowN) * sizeof(float));
     q.partD = r256((size_t)(a.batch * a.dim) * sizeof(float));
     q.partBias = q.partD;
-    q.total = q.ckpt + q.partBC + q.partA + q.partD + q.partBias;
+    q.nch = (a.seqlen + kConvChunk - 1) / kConvChunk;
+    q.dU = a.conv_k > 0 ? r256((size_t)(a.batch * a.seqlen * a.dim) * sizeof(float)) : 0;
+    q.pconv = a.conv_k > 0 ? r256((size_t)(q.nch * a.batch * a.dim * 5) * sizeof(float)) : 0;
+    q.total = q.ckpt + q.partBC + q.partA + q.partD + q.partBias + q.dU + q.pconv;
     return q;
 }
 
 template <typename IO>
-hipError_t launch_bwd_typed(const BwdParams &p, const ssm_scan_bwd_args_t &a, hipStream_t stream) {
+hipError_t launch_bwd_typed(const BwdParams &p, const ssm_scan_bwd_args_t &a, float *pconv, int64_t nch,
+                            hipStream_t stream) {
     const unsigned grid = (unsigned)(p.G * p.B);
     bwd_ckpt_kernel<IO><<<grid, 64 * kWavesB, 0, stream>>>(p);
     hipError_t e = hipGetLastError();
@@ -420,6 +513,15 @@ hipError_t launch_bwd_typed(const BwdParams &p, const ssm_scan_bwd_args_t &a, hi
     if (e != hipSuccess) return e;
     bwd_reduce_params_kernel<<<(unsigned)((p.D * kRowN + 255) / 256), 256, 0, stream>>>(
         p.partA, p.partD, p.partBias, a.dA, a.dDskip, a.ddelta_bias, p.B, p.D);
+    e = hipGetLastError();
+    if (e != hipSuccess || p.K == 0) return e;
+    const int64_t nthr = nch * p.B * p.D;
+    conv_bwd_kernel<IO><<<(unsigned)((nthr + 255) / 256), 256, 0, stream>>>(
+        p.x, p.dU, p.conv_w, p.conv_b, p.dx, pconv, p.B, p.L, p.D, p.K);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    conv_bwd_reduce_kernel<<<(unsigned)((p.D + 255) / 256), 256, 0, stream>>>(pconv, a.dconv_w, a.dconv_b,
+                                                                              nch * p.B, p.D, p.K);
     return hipGetLastError();
 }
 
@@ -434,7 +536,8 @@ hipError_t launch_scan_bwd(const ssm_scan_bwd_args_t &a, hipStream_t stream) {
     if (a.seqlen == 0) {
         const int64_t n = std::max<int64_t>(a.batch * a.dim * kRowN, a.dim * kRowN);
         bwd_empty_kernel<<<(unsigned)((n + 255) / 256), 256, 0, stream>>>(
-            a.dh_final, a.dh0, a.batch * a.dim * kRowN, a.dA, a.dDskip, a.ddelta_bias, a.dim);
+            a.dh_final, a.dh0, a.batch * a.dim * kRowN, a.dA, a.dDskip, a.ddelta_bias, a.dconv_w, a.dconv_b,
+            a.dim, (int)a.conv_k);
         return hipGetLastError();
     }
     const BwdLayout q = bwd_layout(a);
@@ -445,6 +548,11 @@ hipError_t launch_scan_bwd(const ssm_scan_bwd_args_t &a, hipStream_t stream) {
     p.D = a.dim;
     p.G = q.G;
     p.softplus = a.delta_softplus;
+    p.K = (int)a.conv_k;
+    p.conv_w = a.conv_w;
+    p.conv_b = a.conv_b;
+    p.dU = a.conv_k > 0 ? reinterpret_cast<float *>(ws + q.ckpt + q.partBC + q.partA + q.partD + q.partBias)
+                        : nullptr;
     p.x = a.x;
     p.delta = a.delta;
     p.Bm = a.Bm;
@@ -465,8 +573,11 @@ hipError_t launch_scan_bwd(const ssm_scan_bwd_args_t &a, hipStream_t stream) {
     p.partA = reinterpret_cast<float *>(ws + q.ckpt + q.partBC);
     p.partD = reinterpret_cast<float *>(ws + q.ckpt + q.partBC + q.partA);
     p.partBias = reinterpret_cast<float *>(ws + q.ckpt + q.partBC + q.partA + q.partD);
-    if (a.io_dtype == SSM_BF16) return launch_bwd_typed<io_bf16>(p, a, stream);
-    return launch_bwd_typed<io_f32>(p, a, stream);
+    float *pconv = a.conv_k > 0
+                       ? reinterpret_cast<float *>(ws + q.ckpt + q.partBC + q.partA + q.partD + q.partBias + q.dU)
+                       : nullptr;
+    if (a.io_dtype == SSM_BF16) return launch_bwd_typed<io_bf16>(p, a, pconv, q.nch, stream);
+    return launch_bwd_typed<io_f32>(p, a, pconv, q.nch, stream);
 }
 
 }  // namespace ssm

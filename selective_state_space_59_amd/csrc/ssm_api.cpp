@@ -278,19 +278,24 @@ static ssm_status_t check_bwd(const ssm_scan_bwd_args_t *a, size_t *need_out) {
     if (a->dstate < 1) return fail(SSM_ERR_BAD_SHAPE, "dstate must be >= 1");
     if (a->dstate != SSM_MAX_DSTATE)
         return fail(SSM_ERR_UNSUPPORTED, "the backward pass supports dstate == %d only", SSM_MAX_DSTATE);
-    if (a->conv_k != 0 || a->conv_w || a->conv_b || a->dconv_w || a->dconv_b)
-        return fail(SSM_ERR_UNSUPPORTED, "the backward pass has no conv prologue (conv_k must be 0)");
+    if (a->conv_k < 0) return fail(SSM_ERR_BAD_SHAPE, "conv_k must be >= 0");
+    if (a->conv_k > SSM_MAX_CONV_K)
+        return fail(SSM_ERR_UNSUPPORTED, "conv_k %lld exceeds SSM_MAX_CONV_K (%d)", (long long)a->conv_k, SSM_MAX_CONV_K);
+    if (a->conv_k == 0 && (a->conv_w || a->conv_b || a->dconv_w || a->dconv_b))
+        return fail(SSM_ERR_BAD_SHAPE, "conv weights or their gradients given but conv_k == 0");
     if (a->delta_softplus != 0 && a->delta_softplus != 1)
         return fail(SSM_ERR_UNSUPPORTED, "delta_softplus must be 0 or 1");
     if (!mul_ok(a->batch, a->seqlen, a->dim) || !mul_ok(a->batch, a->seqlen, a->dstate) ||
         !mul_ok(a->batch, a->dim, a->dstate))
         return fail(SSM_ERR_BAD_SHAPE, "sizes overflow");
-    const int64_t B = a->batch, L = a->seqlen, D = a->dim, N = a->dstate;
+    const int64_t B = a->batch, L = a->seqlen, D = a->dim, N = a->dstate, K = a->conv_k;
     const int64_t es = io_bytes(a->io_dtype);
     *need_out = (B > 0) ? ssm::scan_bwd_workspace_bytes(*a) : 0;
     if (B == 0) return SSM_OK;
     if (!a->A) return fail(SSM_ERR_NULL_ARG, "A is NULL");
     if (!a->dA) return fail(SSM_ERR_NULL_ARG, "dA is NULL");
+    if (K > 0 && !a->conv_w) return fail(SSM_ERR_NULL_ARG, "conv_w is NULL but conv_k > 0");
+    if (K > 0 && !a->dconv_w) return fail(SSM_ERR_NULL_ARG, "dconv_w is NULL but conv_k > 0");
     if (L > 0) {
         const struct { const void *p; const char *name; } req[] = {
             {a->x, "x"}, {a->delta, "delta"}, {a->Bm, "Bm"}, {a->Cm, "Cm"}, {a->dy, "dy"},
@@ -304,7 +309,7 @@ static ssm_status_t check_bwd(const ssm_scan_bwd_args_t *a, size_t *need_out) {
     for (const void *p : io_ptrs)
         if (!aligned(p, es)) return fail(SSM_ERR_ALIGN, "an io_dtype pointer is not %lld-byte aligned", (long long)es);
     const void *f_ptrs[] = {a->A, a->Dskip, a->delta_bias, a->h0, a->dh_final, a->dA, a->dBm, a->dCm,
-                            a->dDskip, a->ddelta_bias, a->dh0};
+                            a->dDskip, a->ddelta_bias, a->dh0, a->conv_w, a->conv_b, a->dconv_w, a->dconv_b};
     for (const void *p : f_ptrs)
         if (!aligned(p, 4)) return fail(SSM_ERR_ALIGN, "an fp32 pointer is not 4-byte aligned");
     const Range inputs[] = {
@@ -313,14 +318,16 @@ static ssm_status_t check_bwd(const ssm_scan_bwd_args_t *a, size_t *need_out) {
         range(a->z, B * L * D, es, "z"),          range(a->dy, B * L * D, es, "dy"),
         range(a->A, D * N, 4, "A"),               range(a->Dskip, D, 4, "Dskip"),
         range(a->delta_bias, D, 4, "delta_bias"), range(a->h0, B * D * N, 4, "h0"),
-        range(a->dh_final, B * D * N, 4, "dh_final"),
+        range(a->dh_final, B * D * N, 4, "dh_final"), range(a->conv_w, D * K, 4, "conv_w"),
+        range(a->conv_b, D, 4, "conv_b"),
     };
     const Range outputs[] = {
         range(a->dx, B * L * D, es, "dx"),        range(a->ddelta, B * L * D, es, "ddelta"),
         range(a->dz, B * L * D, es, "dz"),        range(a->dA, D * N, 4, "dA"),
         range(a->dBm, B * L * N, 4, "dBm"),       range(a->dCm, B * L * N, 4, "dCm"),
         range(a->dDskip, D, 4, "dDskip"),         range(a->ddelta_bias, D, 4, "ddelta_bias"),
-        range(a->dh0, B * D * N, 4, "dh0"),
+        range(a->dh0, B * D * N, 4, "dh0"),         range(a->dconv_w, D * K, 4, "dconv_w"),
+        range(a->dconv_b, D, 4, "dconv_b"),
     };
     const int nout = (int)(sizeof(outputs) / sizeof(outputs[0]));
     for (int i = 0; i < nout; ++i) {

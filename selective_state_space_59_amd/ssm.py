@@ -353,12 +353,14 @@ def selective_scan_bwd(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, Bm
                        delta_bias: Optional[torch.Tensor] = None, delta_softplus: bool = False,
                        h0: Optional[torch.Tensor] = None,
                        dh_final: Optional[torch.Tensor] = None,
+                       conv_w: Optional[torch.Tensor] = None,
+                       conv_b: Optional[torch.Tensor] = None,
                        workspace: Optional[torch.Tensor] = None) -> dict:
-    """ssm_selective_scan_bwd: gradients of the scan (no conv prologue, N = 16).
+    """ssm_selective_scan_bwd: gradients of the scan (N = 16).
 
     Returns a dict with dx, ddelta (x's dtype), dA, dBm, dCm (float32) and, for the
-    optional inputs given, dz, dDskip, ddelta_bias, dh0."""
-    a, dev = _scan_args(x, delta, A, Bm, Cm, Dskip, z, delta_bias, delta_softplus, None, None,
+    optional inputs given, dz, dDskip, ddelta_bias, dh0, dconv_w, dconv_b."""
+    a, dev = _scan_args(x, delta, A, Bm, Cm, Dskip, z, delta_bias, delta_softplus, conv_w, conv_b,
                         h0, torch.empty_like(x), None)
     Bsz, L, D = x.shape
     N = A.shape[1]
@@ -376,10 +378,14 @@ def selective_scan_bwd(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, Bm
         out["ddelta_bias"] = torch.empty(D, **f32)
     if h0 is not None:
         out["dh0"] = torch.empty(Bsz, D, N, **f32)
+    if conv_w is not None:
+        out["dconv_w"] = torch.empty(D, a.conv_k, **f32)
+        out["dconv_b"] = torch.empty(D, **f32)
     g = lambda k: _ptr(out.get(k))
     b = ScanBwdArgs(batch=Bsz, seqlen=L, dim=D, dstate=N, io_dtype=a.io_dtype,
-                    delta_softplus=a.delta_softplus, conv_k=0, x=a.x, delta=a.delta, Bm=a.Bm,
+                    delta_softplus=a.delta_softplus, conv_k=a.conv_k, x=a.x, delta=a.delta, Bm=a.Bm,
                     Cm=a.Cm, z=a.z, A=a.A, Dskip=a.Dskip, delta_bias=a.delta_bias, h0=a.h0,
+                    conv_w=a.conv_w, conv_b=a.conv_b, dconv_w=g("dconv_w"), dconv_b=g("dconv_b"),
                     dy=_ptr(dy), dh_final=_ptr(dh_final), dx=g("dx"), ddelta=g("ddelta"),
                     dz=g("dz"), dA=g("dA"), dBm=g("dBm"), dCm=g("dCm"), dDskip=g("dDskip"),
                     ddelta_bias=g("ddelta_bias"), dh0=g("dh0"))

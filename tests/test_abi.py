@@ -331,7 +331,9 @@ def run_bwd(a):
     ("io_dtype", 3, ssm.SSM_ERR_BAD_DTYPE),
     ("batch", -1, ssm.SSM_ERR_BAD_SHAPE),
     ("dstate", 8, ssm.SSM_ERR_UNSUPPORTED),       # this version: N == 16
-    ("conv_k", 4, ssm.SSM_ERR_UNSUPPORTED),       # no conv prologue yet
+    ("conv_k", 4, ssm.SSM_ERR_NULL_ARG),          # conv_k without conv_w
+    ("conv_k", 5, ssm.SSM_ERR_UNSUPPORTED),
+    ("conv_w", addr(16), ssm.SSM_ERR_BAD_SHAPE),  # conv weights without conv_k
     ("dy", None, ssm.SSM_ERR_NULL_ARG),
     ("dx", None, ssm.SSM_ERR_NULL_ARG),
     ("dBm", None, ssm.SSM_ERR_NULL_ARG),

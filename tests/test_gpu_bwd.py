@@ -32,6 +32,11 @@ def _check(name, got, ref, tol, scale=0.0):
     err = np.abs(got - ref) / (1.0 + np.abs(ref) + scale)
     worst = float(err.max()) if err.size else 0.0
     print("  %-12s worst scaled error %.2e (tol %.0e)" % (name, worst, tol), flush=True)
+    if worst > tol:
+        bad = np.argwhere(err > tol)
+        idx = tuple(bad[0])
+        print("  %s: %d elements over; first %s got %r ref %r; last %s" % (
+            name, len(bad), idx, got[idx], ref[idx], tuple(bad[-1])), flush=True)
     assert worst <= tol, (name, worst)
 
 
@@ -119,3 +124,29 @@ def test_bwd_130m_layer_sampled_batch_row():
         _check(k, to64(g[k][r]), ref[k], TOL_SUM[dt], float(np.mean(np.abs(ref[k]))))
     del inp, g, dy
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("B,L,D,K,dt", [(2, 70, 40, 4, torch.float32), (1, 300, 70, 3, torch.bfloat16),
+                                        (2, 5, 33, 2, torch.float32), (1, 600, 20, 4, torch.float32),
+                                        (2, 257, 64, 4, torch.bfloat16)])
+def test_bwd_through_conv_prologue(B, L, D, K, dt):
+    """Gradients through the fused causal conv + SiLU prologue (dx via the conv's
+    transpose, dconv_w, dconv_b), including sequences spanning several conv chunks."""
+    print("conv case", B, L, D, K, dt, flush=True)
+    inp = W.make_scan_inputs(B, L, D, 16, io_dtype=dt, seed=600 + L + K, device=DEV, conv_k=K, h0=True)
+    inp["conv_b"] = 0.5 * torch.randn(D, device=DEV, generator=torch.Generator(DEV).manual_seed(8))
+    dy = torch.randn(inp["x"].shape, device=DEV, generator=torch.Generator(DEV).manual_seed(5)).to(dt)
+    g = ssm.selective_scan_bwd(inp["x"], inp["delta"], inp["A"], inp["Bm"], inp["Cm"], dy,
+                               Dskip=inp["Dskip"], z=inp["z"], h0=inp["h0"], conv_w=inp["conv_w"],
+                               conv_b=inp["conv_b"])
+    torch.cuda.synchronize()
+    ref = oracle.selective_scan_bwd(to64(inp["x"]), to64(inp["delta"]), to64(inp["A"]), to64(inp["Bm"]),
+                                    to64(inp["Cm"]), to64(dy), Dskip=to64(inp["Dskip"]), z=to64(inp["z"]),
+                                    h0=to64(inp["h0"]), conv_w=to64(inp["conv_w"]),
+                                    conv_b=to64(inp["conv_b"]))
+    assert set(ref) <= set(g)
+    for k, r in ref.items():
+        if k in PER_ELEM:
+            _check(k, to64(g[k]), r, TOL[dt])
+        else:
+            _check(k, to64(g[k]), r, TOL_SUM[dt], float(np.mean(np.abs(r))))
