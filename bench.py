@@ -129,13 +129,15 @@ def bench_scan(cfg, steps, warmup, nsets=3, final_state=False):
     return ms, nbytes, first
 
 
-def bwd_algorithmic_bytes(B, L, D, N, io_bytes, gate=True, skip=True):
+def bwd_algorithmic_bytes(B, L, D, N, io_bytes, gate=True, skip=True, conv_k=0):
     """Backward pass: x, delta, (z), dy and B, C read once; dx, ddelta, (dz) written once;
-    dB, dC written in fp32; A read and dA written; (Dskip read and dDskip written)."""
-    io = (4 + (1 if gate else 0)) * io_bytes * B * L * D      # x, delta, z, dy
+    dB, dC written in fp32; A read and dA written; (Dskip read and dDskip written);
+    (conv taps read and their gradients written)."""
+    io = (3 + (1 if gate else 0)) * io_bytes * B * L * D      # x, delta, z, dy
     io += (2 + (1 if gate else 0)) * io_bytes * B * L * D     # dx, ddelta, dz
     bc = 2 * io_bytes * B * L * N + 2 * 4 * B * L * N
-    return io + bc + 2 * 4 * D * N + (2 * 4 * D if skip else 0)
+    conv = 2 * 4 * D * conv_k if conv_k else 0
+    return io + bc + 2 * 4 * D * N + (2 * 4 * D if skip else 0) + conv
 
 
 def bench_bwd(cfg, steps, warmup):
@@ -150,12 +152,12 @@ def bench_bwd(cfg, steps, warmup):
 
     def run(_):
         ssm.selective_scan_bwd(s["x"], s["delta"], s["A"], s["Bm"], s["Cm"], dy, Dskip=s["Dskip"],
-                               z=s["z"])
+                               z=s["z"], conv_w=s["conv_w"])
 
     ms = time_launches(run, steps, warmup)
     nbytes = bwd_algorithmic_bytes(cfg.batch, cfg.seqlen, cfg.dim, cfg.dstate,
                                    2 if cfg.io_dtype == torch.bfloat16 else 4,
-                                   gate=cfg.gate, skip=cfg.skip)
+                                   gate=cfg.gate, skip=cfg.skip, conv_k=cfg.conv_k)
     del s, dy
     torch.cuda.empty_cache()
     return ms, nbytes
@@ -314,14 +316,16 @@ def main():
                                  frac_hbm=round(cb / (cms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                                  elems_per_s=round(c.elems / (cms * 1e-3), 1),
                                  algorithmic_bytes=cb)
-        # the backward pass of the 130M-like layer (gradients of every input)
-        name = W.C2_130M.name + "_backward"
-        print("bench extra: %s" % name, file=sys.stderr, flush=True)
-        bms, bb = bench_bwd(W.C2_130M, 20, 3)
-        extra[name] = dict(ms=round(bms, 4), gbs=round(bb / (bms * 1e-3) / 1e9, 2),
-                           frac_hbm=round(bb / (bms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                           state_updates_per_s=round(W.C2_130M.elems * W.C2_130M.dstate / (bms * 1e-3), 1),
-                           algorithmic_bytes=bb)
+        # the backward pass (gradients of every input) of the 130M-like layer
+        # and of the 2.8B-like layer with its conv prologue
+        for c in (W.C2_130M, W.C3_2P8B_CONV):
+            name = c.name + "_backward"
+            print("bench extra: %s" % name, file=sys.stderr, flush=True)
+            bms, bb = bench_bwd(c, 10, 2)
+            extra[name] = dict(ms=round(bms, 4), gbs=round(bb / (bms * 1e-3) / 1e9, 2),
+                               frac_hbm=round(bb / (bms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                               state_updates_per_s=round(c.elems * c.dstate / (bms * 1e-3), 1),
+                               algorithmic_bytes=bb)
         # the decode config, and the same with the d_conv = 4 window of the
         # prefill -> decode handoff
         for name, k in ((W.C5_DECODE.name, 0), (W.C5_DECODE.name + "_conv4_window", 4)):
