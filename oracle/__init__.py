@@ -237,3 +237,56 @@ def selective_scan_bwd(x, delta, A, Bm, Cm, dy, Dskip=None, z=None, delta_bias=N
     if rc != 0:
         raise ValueError("oracle_selective_scan_bwd_f64 rejected the sizes")
     return out
+
+
+def round_bf16(a):
+    """Round to the nearest bfloat16 (ties to even) by way of float32, the precision in
+    which the GPU path holds a value before it stores it as bf16; returned as float64."""
+    a32 = np.ascontiguousarray(np.asarray(a, dtype=np.float32))
+    u = a32.view(np.uint32).astype(np.uint64)
+    r = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16
+    nan = np.isnan(a32)
+    out = r.astype(np.uint32).view(np.float32).astype(np.float64)
+    out[nan] = np.nan
+    return out
+
+
+def rms_norm(h, weight, eps=1e-5):
+    """RMSNorm over the last axis: h / sqrt(mean(h^2) + eps) * weight."""
+    h = _f64(h)
+    return h / np.sqrt(np.mean(h * h, axis=-1, keepdims=True) + eps) * _f64(weight)
+
+
+def mamba_block_fwd(h, norm_w, w_in, conv_w, conv_b, w_x, w_dt, dt_bias, A, Dskip, w_out,
+                    eps=1e-5, bf16=True, nthreads: Optional[int] = None):
+    """One Mamba (S6) block with its pre-norm residual, in float64:
+
+      hn = RMSNorm(h);  x, z = hn W_in[:D]^T, hn W_in[D:]^T        (in_proj, split)
+      u = silu(causal conv1d(x))                                    (the block's Conv1d)
+      dt_low, B, C = u W_x^T split as (R, N, N)                     (x_proj)
+      delta = dt_low W_dt^T;  y = S6(u, softplus(delta + dt_bias), A, B, C, D) * silu(z)
+      h_out = h + y W_out^T                                         (out_proj + residual)
+
+    The block of the paper summary page "Mamba: Linear-Time Sequence Modeling with
+    Selective State Spaces" (sec. 4a; the projections and dt_rank of Algorithm 2).
+    Shapes: h (B,L,d_model); norm_w (d_model,); w_in (2D, d_model); conv_w (D,K); conv_b (D,);
+    w_x (R+2N, D); w_dt (D, R); dt_bias (D,); A (D,N); Dskip (D,); w_out (d_model, D).
+    With bf16=True every tensor the GPU path stores in bf16 (hn, x, z, u, dt_low, B, C, delta,
+    y and h_out) is rounded to bf16 at the same point here.
+    """
+    r = round_bf16 if bf16 else (lambda v: v)
+    h = _f64(h)
+    D = w_in.shape[0] // 2
+    N = A.shape[1]
+    R = w_dt.shape[1]
+    w_in, w_x, w_dt, w_out = (_f64(v) for v in (w_in, w_x, w_dt, w_out))
+    hn = r(rms_norm(h, norm_w, eps))
+    x = r(hn @ w_in[:D].T)
+    z = r(hn @ w_in[D:].T)
+    u = r(causal_conv1d_silu(x, conv_w, conv_b, nthreads=nthreads))
+    xd = u @ w_x.T
+    dt_low, Bm, Cm = r(xd[..., :R]), r(xd[..., R:R + N]), r(xd[..., R + N:])
+    delta = r(dt_low @ w_dt.T)
+    y, _ = selective_scan(u, delta, A, Bm, Cm, Dskip=Dskip, z=z, delta_bias=dt_bias,
+                          delta_softplus=True, nthreads=nthreads)
+    return r(h + r(y) @ w_out.T)
