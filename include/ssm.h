@@ -8,7 +8,8 @@
  *     output;
  *   - ssm_state_update: one recurrent (decode) step on a resident state;
  *   - ssm_causal_conv1d_silu: the conv prologue on its own;
- *   - ssm_selective_scan_bwd: the gradients of the scan (training).
+ *   - ssm_selective_scan_bwd: the gradients of the scan (training);
+ *   - ssm_block_fwd: a whole Mamba block around the scan (with a plan).
  *
  * The operations are defined on these pages (cited by title and section):
  *   [P1] "Mamba: Linear-Time Sequence Modeling with Selective State Spaces"
@@ -24,8 +25,10 @@
  *
  * Conventions common to every entry point
  *   - Every tensor pointer is a DEVICE pointer into memory the caller owns
- *     (e.g. a torch tensor's data_ptr()).  The library allocates nothing,
- *     keeps no state between calls and never frees caller memory.
+ *     (e.g. a torch tensor's data_ptr()).  The library allocates no device
+ *     memory of its own, keeps no state between calls and never frees caller
+ *     memory; the one exception is the block plan (ssm_block_plan_create),
+ *     which holds a hipBLASLt handle until ssm_block_plan_destroy.
  *   - Tensors are dense and row-major with the last index fastest; element
  *     strides are implied by the shapes.  Pointers must be aligned to their
  *     element size (2 bytes for bf16, 4 for fp32).
@@ -58,7 +61,7 @@
 extern "C" {
 #endif
 
-#define SSM_ABI_VERSION 3
+#define SSM_ABI_VERSION 4
 #define SSM_MAX_DSTATE 16 /* largest N the kernels hold in registers */
 #define SSM_MAX_CONV_K 4  /* largest conv1d kernel width */
 
@@ -256,6 +259,81 @@ size_t ssm_selective_scan_bwd_workspace_size(const ssm_scan_bwd_args_t *args);
  * SSM_OK or an error status (see the conventions).
  */
 ssm_status_t ssm_selective_scan_bwd(const ssm_scan_bwd_args_t *args, void *stream);
+
+/*
+ * One Mamba block with its pre-norm residual, the block of [P1] sec. 4a (the
+ * table of tensor shapes: RMSNorm, the expanding Linear to x and the gate z,
+ * Conv1d -> SiLU, the selective SSM, x SiLU(z), the output Linear, + input),
+ * with the projections of [P1] Algorithm 2 (s_B, s_C = Linear_N, s_Delta a
+ * low-rank Linear of rank R followed by Linear_D; the page's Linear_1 +
+ * Broadcast_D is R = 1 with W_dt = 1) and tau_Delta = softplus:
+ *   hn = RMSNorm(h) (eps = norm_eps, weight norm_w)
+ *   x = hn W_in[0:D]^T, z = hn W_in[D:2D]^T, u = silu(conv1d(x))
+ *   dt_low = u W_x[0:R]^T, B = u W_x[R:R+N]^T, C = u W_x[R+N:R+2N]^T
+ *   delta = dt_low W_dt^T;  y = S6(u, softplus(delta + dt_bias), A, B, C, D) * silu(z)
+ *   h_out = h + y W_out^T
+ * I/O and intermediates are bf16 (GEMMs accumulate in fp32); norm_w, conv
+ * weights, dt_bias, A and Dskip are fp32.  The GEMMs run in hipBLASLt.
+ *
+ * Usage: create a plan for the sizes (this creates a hipBLASLt handle and
+ * picks the GEMM algorithms; host memory only, needs the GPU), query its
+ * device workspace size, call ssm_block_fwd any number of times, destroy.
+ */
+typedef struct ssm_block_dims {
+    int64_t batch, seqlen;  /* B >= 1, L >= 1                                  */
+    int64_t d_model;        /* model width, a multiple of 8                    */
+    int64_t d_inner;        /* D = E * d_model (SSM channels), a multiple of 8 */
+    int64_t dstate;         /* N, 1 <= N <= SSM_MAX_DSTATE                     */
+    int64_t dt_rank;        /* R >= 1                                          */
+    int64_t conv_k;         /* 1..SSM_MAX_CONV_K                               */
+} ssm_block_dims_t;
+
+typedef struct ssm_block_weights {
+    const float *norm_w;    /* (d_model) fp32                                  */
+    const void *w_in;       /* (2 D, d_model) bf16: rows of x, then of z       */
+    const float *conv_w;    /* (D, conv_k) fp32                                */
+    const float *conv_b;    /* (D) fp32, or NULL                               */
+    const void *w_x;        /* (R + 2N, D) bf16: rows of dt_low, B, C          */
+    const void *w_dt;       /* (D, R) bf16                                     */
+    const float *dt_bias;   /* (D) fp32                                        */
+    const float *A;         /* (D, N) fp32                                     */
+    const float *Dskip;     /* (D) fp32, or NULL                               */
+    const void *w_out;      /* (d_model, D) bf16                               */
+    float norm_eps;         /* > 0, e.g. 1e-5                                  */
+} ssm_block_weights_t;
+
+typedef struct ssm_block_plan ssm_block_plan_t;
+
+/*
+ * Plan for these sizes.  Returns SSM_OK and *plan, or an error and *plan =
+ * NULL: SSM_ERR_NULL_ARG, SSM_ERR_BAD_SHAPE (a size < 1, dt_rank > d_inner,
+ * B*L >= 2^31), SSM_ERR_UNSUPPORTED (dstate, conv_k or a width not a multiple
+ * of 8; or hipBLASLt offers no algorithm), SSM_ERR_HIP (no device, or the
+ * handle could not be created).  The plan belongs to the device current at
+ * creation.
+ */
+ssm_status_t ssm_block_plan_create(const ssm_block_dims_t *dims, ssm_block_plan_t **plan);
+
+/* Device workspace bytes ssm_block_fwd needs with this plan (0 for NULL). */
+size_t ssm_block_workspace_size(const ssm_block_plan_t *plan);
+
+/*
+ * h_out = the block applied to h_in, both (B, L, d_model) bf16.  h_out may be
+ * h_in itself (updated in place) but may not overlap it otherwise or any
+ * weight; nothing may overlap the workspace (256-aligned, >=
+ * ssm_block_workspace_size).  bf16 tensors (h_in, h_out, w_in, w_x, w_dt,
+ * w_out) must be 16-byte aligned, fp32 ones 4-byte aligned.  The plan may be
+ * shared by calls on different streams only with separate workspaces.
+ * Errors: SSM_ERR_NULL_ARG (plan, h_in, h_out or a required weight NULL),
+ * SSM_ERR_BAD_SHAPE (norm_eps <= 0), SSM_ERR_ALIGN, SSM_ERR_WORKSPACE,
+ * SSM_ERR_ALIAS, SSM_ERR_HIP (a launch or hipBLASLt call failed).
+ */
+ssm_status_t ssm_block_fwd(const ssm_block_plan_t *plan, const ssm_block_weights_t *weights,
+                           const void *h_in, void *h_out, void *workspace, size_t workspace_bytes,
+                           void *stream);
+
+/* Release a plan (NULL is ignored). */
+void ssm_block_plan_destroy(ssm_block_plan_t *plan);
 
 /* Static description of a status code (never NULL). */
 const char *ssm_status_string(ssm_status_t status);

@@ -5,10 +5,12 @@ The compute path is the C-ABI HIP library libssm_hip.so (include/ssm.h); the
 and its absence raises an error; nothing here computes on the CPU.
 """
 from .ssm import (  # noqa: F401
+    BlockPlan,
     SSMError,
     abi_version,
     causal_conv1d_silu,
     lib,
+    mamba_block_fwd,
     selective_scan_bwd,
     selective_scan_fwd,
     selective_scan_workspace_size,
@@ -16,5 +18,6 @@ from .ssm import (  # noqa: F401
     status_string,
 )
 
-__all__ = ["SSMError", "abi_version", "causal_conv1d_silu", "lib", "selective_scan_bwd",
+__all__ = ["BlockPlan", "SSMError", "abi_version", "causal_conv1d_silu", "lib", "mamba_block_fwd",
+           "selective_scan_bwd",
            "selective_scan_fwd", "selective_scan_workspace_size", "state_update", "status_string"]

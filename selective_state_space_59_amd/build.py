@@ -20,7 +20,9 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libssm_hip.so")
 ARCH = "gfx950"
 
-SOURCES = ["ssm_api.cpp", "scan_fwd.hip", "scan_bwd.hip", "conv1d.hip", "state_update.hip"]
+SOURCES = ["ssm_api.cpp", "scan_fwd.hip", "scan_bwd.hip", "conv1d.hip", "state_update.hip", "block.hip"]
+# hipBLASLt runs the plain GEMMs of the Mamba block.
+LIBS = ["-L/opt/rocm/lib", "-lhipblaslt", "-Wl,-rpath,/opt/rocm/lib"]
 
 # Packed-fp32 VALU forms are switched off for all device code; the compiler
 # still emits ordinary fp32 arithmetic.
@@ -74,7 +76,7 @@ def build(verbose: bool = False) -> str:
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
         objs = list(ex.map(_compile, SOURCES))
     tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [hipcc(), "-shared", "-fPIC", "--offload-arch=" + ARCH, "-o", tmp] + objs
+    cmd = [hipcc(), "-shared", "-fPIC", "--offload-arch=" + ARCH, "-o", tmp] + objs + LIBS
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n%s\n%s" % (" ".join(cmd), r.stderr))

@@ -1,12 +1,13 @@
 // ssm_api.cpp -- the C ABI declared in include/ssm.h: argument checking,
 // dispatch to the kernel launchers, status strings.  Nothing here allocates
 // device memory or keeps state between calls (apart from the per-thread text
-// of the last error).
+// of the last error and the block plans the caller creates and destroys).
 #include <hip/hip_runtime.h>
 
 #include <cstdarg>
 #include <cstdio>
 #include <cstdint>
+#include <climits>
 
 #include "ssm_internal.h"
 
@@ -364,6 +365,81 @@ ssm_status_t ssm_selective_scan_bwd(const ssm_scan_bwd_args_t *a, void *stream) 
     if (s != SSM_OK) return s;
     if (a->batch == 0) return ok();
     const hipError_t e = ssm::launch_scan_bwd(*a, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(SSM_ERR_HIP, "HIP error: %s", hipGetErrorString(e));
+    return ok();
+}
+
+ssm_status_t ssm_block_plan_create(const ssm_block_dims_t *d, ssm_block_plan_t **plan) {
+    if (!plan) return fail(SSM_ERR_NULL_ARG, "plan is NULL");
+    *plan = nullptr;
+    if (!d) return fail(SSM_ERR_NULL_ARG, "dims is NULL");
+    if (d->batch < 1 || d->seqlen < 1 || d->d_model < 1 || d->d_inner < 1 || d->dstate < 1 || d->dt_rank < 1)
+        return fail(SSM_ERR_BAD_SHAPE, "block sizes must all be >= 1");
+    if (d->dstate > SSM_MAX_DSTATE)
+        return fail(SSM_ERR_UNSUPPORTED, "dstate %lld exceeds SSM_MAX_DSTATE (%d)", (long long)d->dstate,
+                    SSM_MAX_DSTATE);
+    if (d->d_model % 8 != 0 || d->d_inner % 8 != 0)
+        return fail(SSM_ERR_UNSUPPORTED, "d_model and d_inner must be multiples of 8 (got %lld, %lld)",
+                    (long long)d->d_model, (long long)d->d_inner);
+    if (d->conv_k < 1 || d->conv_k > SSM_MAX_CONV_K)
+        return fail(SSM_ERR_UNSUPPORTED, "conv_k must be 1..%d (got %lld)", SSM_MAX_CONV_K, (long long)d->conv_k);
+    // hipBLASLt takes 32-bit sizes; the largest operands stay well inside them.
+    const int64_t M = d->batch * d->seqlen;
+    if (!mul_ok(d->batch, d->seqlen, 4 * (d->d_model + d->d_inner)) || M > INT32_MAX ||
+        d->d_model > INT32_MAX / 4 || d->d_inner > INT32_MAX / 4 || d->dt_rank > d->d_inner)
+        return fail(SSM_ERR_BAD_SHAPE, "block sizes out of range (dt_rank <= d_inner, B*L < 2^31)");
+    ssm_block_plan *p = nullptr;
+    const ssm_status_t s = ssm::block_plan_create(*d, &p);
+    if (s != SSM_OK) return fail(s, "could not set up the block's GEMMs (hipBLASLt handle or algorithm)");
+    *plan = p;
+    return ok();
+}
+
+size_t ssm_block_workspace_size(const ssm_block_plan_t *plan) {
+    return plan ? ssm::block_workspace_bytes(*plan) : 0;
+}
+
+void ssm_block_plan_destroy(ssm_block_plan_t *plan) { ssm::block_plan_destroy(plan); }
+
+ssm_status_t ssm_block_fwd(const ssm_block_plan_t *plan, const ssm_block_weights_t *w, const void *h_in,
+                           void *h_out, void *workspace, size_t workspace_bytes, void *stream) {
+    if (!plan || !w || !h_in || !h_out) return fail(SSM_ERR_NULL_ARG, "plan, weights, h_in and h_out are required");
+    if (!w->norm_w || !w->w_in || !w->conv_w || !w->w_x || !w->w_dt || !w->dt_bias || !w->A || !w->w_out)
+        return fail(SSM_ERR_NULL_ARG, "a required weight is NULL (only conv_b and Dskip are optional)");
+    if (!(w->norm_eps > 0.0f) || !(w->norm_eps < 1e30f)) return fail(SSM_ERR_BAD_SHAPE, "norm_eps must be > 0");
+    const ssm_block_dims_t &d = ssm::block_dims(*plan);
+    const int64_t M = d.batch * d.seqlen, D = d.d_inner, N = d.dstate, R = d.dt_rank, dm = d.d_model;
+    const void *bf[] = {w->w_in, w->w_x, w->w_dt, w->w_out, h_in, h_out};
+    for (const void *v : bf)
+        if (!aligned(v, 16)) return fail(SSM_ERR_ALIGN, "bf16 tensors must be 16-byte aligned");
+    const void *f4[] = {w->norm_w, w->conv_w, w->conv_b, w->dt_bias, w->A, w->Dskip};
+    for (const void *v : f4)
+        if (!aligned(v, 4)) return fail(SSM_ERR_ALIGN, "fp32 tensors must be 4-byte aligned");
+    const size_t need = ssm::block_workspace_bytes(*plan);
+    if (!workspace) return fail(SSM_ERR_WORKSPACE, "workspace of %zu bytes required", need);
+    if (workspace_bytes < need)
+        return fail(SSM_ERR_WORKSPACE, "workspace has %zu bytes, %zu required", workspace_bytes, need);
+    if (!aligned(workspace, 256)) return fail(SSM_ERR_WORKSPACE, "workspace is not 256-byte aligned");
+    const Range hi = range(h_in, M * dm, 2, "h_in"), ho = range(h_out, M * dm, 2, "h_out");
+    if (h_in != h_out && overlaps(hi, ho)) return fail(SSM_ERR_ALIAS, "h_out overlaps h_in (other than in place)");
+    const Range inputs[] = {hi,
+                            range(w->norm_w, dm, 4, "norm_w"),
+                            range(w->w_in, 2 * D * dm, 2, "w_in"),
+                            range(w->conv_w, D * d.conv_k, 4, "conv_w"),
+                            range(w->conv_b, D, 4, "conv_b"),
+                            range(w->w_x, (R + 2 * N) * D, 2, "w_x"),
+                            range(w->w_dt, D * R, 2, "w_dt"),
+                            range(w->dt_bias, D, 4, "dt_bias"),
+                            range(w->A, D * N, 4, "A"),
+                            range(w->Dskip, D, 4, "Dskip"),
+                            range(w->w_out, dm * D, 2, "w_out")};
+    const Range ws = range(workspace, (int64_t)need, 1, "workspace");
+    for (const Range &r : inputs) {
+        if (overlaps(ws, r)) return fail(SSM_ERR_ALIAS, "workspace overlaps %s", r.name);
+        if (&r != &inputs[0] && overlaps(ho, r)) return fail(SSM_ERR_ALIAS, "h_out overlaps %s", r.name);
+    }
+    if (overlaps(ws, ho)) return fail(SSM_ERR_ALIAS, "workspace overlaps h_out");
+    const hipError_t e = ssm::launch_block_fwd(*plan, *w, h_in, h_out, workspace, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(SSM_ERR_HIP, "HIP error: %s", hipGetErrorString(e));
     return ok();
 }

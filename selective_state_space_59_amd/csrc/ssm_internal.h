@@ -29,6 +29,14 @@ hipError_t launch_state_update(const ssm_state_update_args_t &a, hipStream_t str
 size_t scan_bwd_workspace_bytes(const ssm_scan_bwd_args_t &a);
 hipError_t launch_scan_bwd(const ssm_scan_bwd_args_t &a, hipStream_t stream);
 
+// Mamba block (block.hip).
+ssm_status_t block_plan_create(const ssm_block_dims_t &d, ssm_block_plan **out);
+void block_plan_destroy(ssm_block_plan *p);
+size_t block_workspace_bytes(const ssm_block_plan &p);
+const ssm_block_dims_t &block_dims(const ssm_block_plan &p);
+hipError_t launch_block_fwd(const ssm_block_plan &p, const ssm_block_weights_t &w, const void *h_in, void *h_out,
+                            void *workspace, hipStream_t stream);
+
 // Copy or zero-fill the final state for an empty (L == 0) scan.
 hipError_t launch_empty_scan_state(const ssm_scan_args_t &a, hipStream_t stream);
 

@@ -36,7 +36,9 @@ MAX_CONV_K = 4
 EXPORTED_SYMBOLS = ("ssm_selective_scan_workspace_size", "ssm_selective_scan_fwd",
                     "ssm_causal_conv1d_silu", "ssm_state_update", "ssm_status_string",
                     "ssm_last_error_message", "ssm_abi_version",
-                    "ssm_selective_scan_bwd_workspace_size", "ssm_selective_scan_bwd")
+                    "ssm_selective_scan_bwd_workspace_size", "ssm_selective_scan_bwd",
+                    "ssm_block_plan_create", "ssm_block_workspace_size", "ssm_block_fwd",
+                    "ssm_block_plan_destroy")
 
 _P = ctypes.c_void_p
 _I64 = ctypes.c_int64
@@ -75,6 +77,19 @@ class ScanBwdArgs(ctypes.Structure):
                 ("dh0", _P), ("workspace", _P), ("workspace_bytes", ctypes.c_size_t)]
 
 
+class BlockDims(ctypes.Structure):
+    """Mirror of ssm_block_dims_t."""
+    _fields_ = [("batch", _I64), ("seqlen", _I64), ("d_model", _I64), ("d_inner", _I64),
+                ("dstate", _I64), ("dt_rank", _I64), ("conv_k", _I64)]
+
+
+class BlockWeights(ctypes.Structure):
+    """Mirror of ssm_block_weights_t."""
+    _fields_ = [("norm_w", _P), ("w_in", _P), ("conv_w", _P), ("conv_b", _P), ("w_x", _P),
+                ("w_dt", _P), ("dt_bias", _P), ("A", _P), ("Dskip", _P), ("w_out", _P),
+                ("norm_eps", ctypes.c_float)]
+
+
 class SSMError(RuntimeError):
     def __init__(self, status: int, message: str):
         super().__init__(message)
@@ -110,6 +125,14 @@ def lib() -> ctypes.CDLL:
         L.ssm_selective_scan_bwd_workspace_size.restype = ctypes.c_size_t
         L.ssm_selective_scan_bwd.argtypes = [ctypes.POINTER(ScanBwdArgs), _P]
         L.ssm_selective_scan_bwd.restype = ctypes.c_int
+        L.ssm_block_plan_create.argtypes = [ctypes.POINTER(BlockDims), ctypes.POINTER(_P)]
+        L.ssm_block_plan_create.restype = ctypes.c_int
+        L.ssm_block_workspace_size.argtypes = [_P]
+        L.ssm_block_workspace_size.restype = ctypes.c_size_t
+        L.ssm_block_fwd.argtypes = [_P, ctypes.POINTER(BlockWeights), _P, _P, _P, ctypes.c_size_t, _P]
+        L.ssm_block_fwd.restype = ctypes.c_int
+        L.ssm_block_plan_destroy.argtypes = [_P]
+        L.ssm_block_plan_destroy.restype = None
         _lib = L
     return _lib
 
@@ -399,4 +422,88 @@ def selective_scan_bwd(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, Bm
         b.workspace = ws.data_ptr()
         b.workspace_bytes = ws.numel() * ws.element_size()
     _check(lib().ssm_selective_scan_bwd(ctypes.byref(b), _stream(dev)), "ssm_selective_scan_bwd")
+    return out
+
+
+class BlockPlan:
+    """A plan of ssm_block_fwd for fixed sizes (owns the library's plan handle)."""
+
+    def __init__(self, batch: int, seqlen: int, d_model: int, d_inner: int, dstate: int,
+                 dt_rank: int, conv_k: int):
+        self.dims = BlockDims(batch=batch, seqlen=seqlen, d_model=d_model, d_inner=d_inner,
+                              dstate=dstate, dt_rank=dt_rank, conv_k=conv_k)
+        self._h = _P()
+        self._lib = lib()
+        _check(self._lib.ssm_block_plan_create(ctypes.byref(self.dims), ctypes.byref(self._h)),
+               "ssm_block_plan_create")
+        self.workspace_bytes = int(self._lib.ssm_block_workspace_size(self._h))
+
+    @property
+    def handle(self):
+        return self._h
+
+    def close(self):
+        if self._h:
+            self._lib.ssm_block_plan_destroy(self._h)
+            self._h = _P()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+_plan_cache = {}
+
+
+def mamba_block_fwd(h: torch.Tensor, norm_w: torch.Tensor, w_in: torch.Tensor, conv_w: torch.Tensor,
+                    conv_b: Optional[torch.Tensor], w_x: torch.Tensor, w_dt: torch.Tensor,
+                    dt_bias: torch.Tensor, A: torch.Tensor, Dskip: Optional[torch.Tensor],
+                    w_out: torch.Tensor, eps: float = 1e-5, out: Optional[torch.Tensor] = None,
+                    plan: Optional[BlockPlan] = None, workspace: Optional[torch.Tensor] = None):
+    """One Mamba block with its pre-norm residual (ssm_block_fwd): h (B, L, d_model) bf16 ->
+    h + out_proj(S6(...) * silu(z)).  Weight shapes as in ssm_block_weights_t; `out` may be h."""
+    if not isinstance(h, torch.Tensor) or h.dim() != 3 or h.device.type != "cuda":
+        raise ValueError("h must be a (B, L, d_model) GPU tensor")
+    dev = h.device
+    Bsz, L, dm = h.shape
+    if A.dim() != 2 or w_dt.dim() != 2 or conv_w.dim() != 2:
+        raise ValueError("A, w_dt and conv_w must be 2-D")
+    D, N = A.shape
+    R = w_dt.shape[1]
+    K = conv_w.shape[1]
+    bf, f32 = torch.bfloat16, torch.float32
+    _req(h, "h", (Bsz, L, dm), bf, dev)
+    _req(norm_w, "norm_w", (dm,), f32, dev)
+    _req(w_in, "w_in", (2 * D, dm), bf, dev)
+    _req(conv_w, "conv_w", (D, K), f32, dev)
+    _opt(conv_b, "conv_b", (D,), f32, dev)
+    _req(w_x, "w_x", (R + 2 * N, D), bf, dev)
+    _req(w_dt, "w_dt", (D, R), bf, dev)
+    _req(dt_bias, "dt_bias", (D,), f32, dev)
+    _req(A, "A", (D, N), f32, dev)
+    _opt(Dskip, "Dskip", (D,), f32, dev)
+    _req(w_out, "w_out", (dm, D), bf, dev)
+    if out is None:
+        out = torch.empty_like(h)
+    _req(out, "out", (Bsz, L, dm), bf, dev)
+    if plan is None:
+        key = (dev.index, Bsz, L, dm, D, N, R, K)
+        plan = _plan_cache.get(key)
+        if plan is None:
+            with torch.cuda.device(dev):
+                plan = BlockPlan(Bsz, L, dm, D, N, R, K)
+            _plan_cache[key] = plan
+    d = plan.dims
+    if (d.batch, d.seqlen, d.d_model, d.d_inner, d.dstate, d.dt_rank, d.conv_k) != (Bsz, L, dm, D, N, R, K):
+        raise ValueError("the plan was made for other sizes")
+    if workspace is None:
+        workspace = _workspace(dev, plan.workspace_bytes)
+    wts = BlockWeights(norm_w=_ptr(norm_w), w_in=_ptr(w_in), conv_w=_ptr(conv_w), conv_b=_ptr(conv_b),
+                       w_x=_ptr(w_x), w_dt=_ptr(w_dt), dt_bias=_ptr(dt_bias), A=_ptr(A),
+                       Dskip=_ptr(Dskip), w_out=_ptr(w_out), norm_eps=float(eps))
+    _check(lib().ssm_block_fwd(plan.handle, ctypes.byref(wts), _ptr(h), _ptr(out), _ptr(workspace),
+                               workspace.numel() * workspace.element_size(), _stream(dev)),
+           "ssm_block_fwd")
     return out

@@ -83,6 +83,25 @@ C5_DECODE = DecodeConfig("c5_decode", 256, 5120, 16, 64, torch.bfloat16, seed=4,
 SCAN_CONFIGS = {c.name: c for c in (C1_TINY, C2_130M, C3_2P8B_CONV, C4_DNA_1M)}
 
 
+@dataclasses.dataclass(frozen=True)
+class BlockConfig:
+    """Sizes of one Mamba block (pre-norm residual around in_proj, conv, S6, out_proj)."""
+    name: str
+    batch: int
+    seqlen: int
+    d_model: int
+    d_inner: int
+    dstate: int
+    dt_rank: int
+    conv_k: int
+    seed: int
+
+
+# A 130M-like layer (d_model 768, E = 2, N = 16, dt_rank = d_model / 16, conv width 4)
+# at the same batch and length as the 130M-like scan.
+B2_130M = BlockConfig("b2_mamba130m_block", 8, 2048, 768, 1536, 16, 48, 4, seed=21)
+
+
 def _gen(device, seed: int) -> torch.Generator:
     g = torch.Generator(device=device)
     g.manual_seed(int(seed))
@@ -163,3 +182,42 @@ def make_decode_config_inputs(cfg: DecodeConfig, device="cpu", **overrides):
               gate=cfg.gate, skip=cfg.skip)
     kw.update(overrides)
     return make_decode_inputs(device=device, **kw)
+
+
+def make_block_inputs(batch: int, seqlen: int, d_model: int, d_inner: int, dstate: int,
+                      dt_rank: int, conv_k: int = 4, seed: int = 21, device="cpu",
+                      unit_dt_proj: bool = False) -> Dict[str, Optional[torch.Tensor]]:
+    """Draw one block input set (bf16 activations and matrices, fp32 vectors).
+
+    Order and laws: h ~ N(0,1); norm_w = 1 + 0.1 N(0,1); w_in ~ N(0, 1/d_model);
+    conv_w ~ N(0, 0.25); conv_b ~ N(0, 0.01); w_x ~ N(0, 1/d_inner); w_dt ~ N(0, 1/dt_rank)
+    (all ones with unit_dt_proj: the rank-1 broadcast form); dt_bias ~ U(-7, -2.3), so
+    that softplus(dt_bias) spans about 1e-3 .. 0.1; A the S4D-Real rule; Dskip = 1 +
+    0.1 N(0,1); w_out ~ N(0, 1/d_inner).  Matrices are drawn in fp32 and rounded to bf16.
+    """
+    g = _gen(device, seed)
+    bf = torch.bfloat16
+    D, R, N = d_inner, dt_rank, dstate
+    h = _randn((batch, seqlen, d_model), g, device).to(bf)
+    norm_w = _randn((d_model,), g, device, std=0.1, shift=-1.0)
+    w_in = _randn((2 * D, d_model), g, device, std=d_model ** -0.5).to(bf)
+    conv_w = _randn((D, conv_k), g, device, std=0.5)
+    conv_b = _randn((D,), g, device, std=0.1)
+    w_x = _randn((R + 2 * N, D), g, device, std=D ** -0.5).to(bf)
+    if unit_dt_proj:
+        w_dt = torch.ones((D, R), device=device, dtype=bf)
+    else:
+        w_dt = _randn((D, R), g, device, std=R ** -0.5).to(bf)
+    dt_bias = torch.rand((D,), generator=g, device=device) * 4.7 - 7.0
+    A = s4d_real_A(D, N, device)
+    Dskip = _randn((D,), g, device, std=0.1, shift=-1.0)
+    w_out = _randn((d_model, D), g, device, std=D ** -0.5).to(bf)
+    return dict(h=h, norm_w=norm_w, w_in=w_in, conv_w=conv_w, conv_b=conv_b, w_x=w_x, w_dt=w_dt,
+                dt_bias=dt_bias, A=A, Dskip=Dskip, w_out=w_out)
+
+
+def make_block_config_inputs(cfg: BlockConfig, device="cpu", **overrides):
+    kw = dict(batch=cfg.batch, seqlen=cfg.seqlen, d_model=cfg.d_model, d_inner=cfg.d_inner,
+              dstate=cfg.dstate, dt_rank=cfg.dt_rank, conv_k=cfg.conv_k, seed=cfg.seed)
+    kw.update(overrides)
+    return make_block_inputs(device=device, **kw)

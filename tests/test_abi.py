@@ -63,17 +63,22 @@ int main(void) {
   printf("ssm_scan_args_t size %zu\n", sizeof(ssm_scan_args_t));
   printf("ssm_state_update_args_t size %zu\n", sizeof(ssm_state_update_args_t));
   printf("ssm_scan_bwd_args_t size %zu\n", sizeof(ssm_scan_bwd_args_t));
+  printf("ssm_block_dims_t size %zu\n", sizeof(ssm_block_dims_t));
+  printf("ssm_block_weights_t size %zu\n", sizeof(ssm_block_weights_t));
   %FIELDS%
   return 0;
 }
 """
 
 
+STRUCTS = (("ssm_scan_args_t", ssm.ScanArgs), ("ssm_state_update_args_t", ssm.StateUpdateArgs),
+           ("ssm_scan_bwd_args_t", ssm.ScanBwdArgs), ("ssm_block_dims_t", ssm.BlockDims),
+           ("ssm_block_weights_t", ssm.BlockWeights))
+
+
 def test_ctypes_structs_match_c_layout():
     lines = []
-    for cname, cls in (("ssm_scan_args_t", ssm.ScanArgs),
-                       ("ssm_state_update_args_t", ssm.StateUpdateArgs),
-                       ("ssm_scan_bwd_args_t", ssm.ScanBwdArgs)):
+    for cname, cls in STRUCTS:
         for f, _ in cls._fields_:
             lines.append("F(%s, %s)" % (cname, f))
     with tempfile.TemporaryDirectory() as d:
@@ -88,12 +93,8 @@ def test_ctypes_structs_match_c_layout():
         if line:
             t, f, v = line.split()
             got[(t, f)] = int(v)
-    assert got[("ssm_scan_args_t", "size")] == ctypes.sizeof(ssm.ScanArgs)
-    assert got[("ssm_state_update_args_t", "size")] == ctypes.sizeof(ssm.StateUpdateArgs)
-    assert got[("ssm_scan_bwd_args_t", "size")] == ctypes.sizeof(ssm.ScanBwdArgs)
-    for cname, cls in (("ssm_scan_args_t", ssm.ScanArgs),
-                       ("ssm_state_update_args_t", ssm.StateUpdateArgs),
-                       ("ssm_scan_bwd_args_t", ssm.ScanBwdArgs)):
+    for cname, cls in STRUCTS:
+        assert got[(cname, "size")] == ctypes.sizeof(cls), cname
         for f, _ in cls._fields_:
             assert got[(cname, f)] == getattr(cls, f).offset, (cname, f)
 
@@ -356,3 +357,51 @@ def test_bwd_dz_without_z_and_empty_batch():
     assert L.ssm_selective_scan_bwd_workspace_size(ctypes.byref(bwd_args(dstate=4))) == \
         ctypes.c_size_t(-1).value
     assert 0 < L.ssm_selective_scan_bwd_workspace_size(ctypes.byref(bwd_args())) < (1 << 40)
+
+
+# --------------------------------------------------------------- block checks
+def block_dims(**kw):
+    d = ssm.BlockDims(batch=2, seqlen=8, d_model=64, d_inner=128, dstate=16, dt_rank=4, conv_k=4)
+    for k, v in kw.items():
+        setattr(d, k, v)
+    return d
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("batch", 0, ssm.SSM_ERR_BAD_SHAPE),
+    ("seqlen", -1, ssm.SSM_ERR_BAD_SHAPE),
+    ("d_model", 0, ssm.SSM_ERR_BAD_SHAPE),
+    ("dt_rank", 0, ssm.SSM_ERR_BAD_SHAPE),
+    ("dt_rank", 129, ssm.SSM_ERR_BAD_SHAPE),      # above d_inner
+    ("dstate", 17, ssm.SSM_ERR_UNSUPPORTED),
+    ("conv_k", 0, ssm.SSM_ERR_UNSUPPORTED),
+    ("conv_k", 5, ssm.SSM_ERR_UNSUPPORTED),
+    ("d_model", 60, ssm.SSM_ERR_UNSUPPORTED),     # not a multiple of 8
+    ("d_inner", 100, ssm.SSM_ERR_UNSUPPORTED),
+    ("seqlen", 1 << 31, ssm.SSM_ERR_BAD_SHAPE),   # B*L beyond 32-bit GEMM sizes
+])
+def test_block_plan_rejects_bad_sizes(field, value, status):
+    h = ctypes.c_void_p(12345)
+    assert ssm.lib().ssm_block_plan_create(ctypes.byref(block_dims(**{field: value})),
+                                           ctypes.byref(h)) == status
+    assert not h.value
+
+
+def test_block_null_arguments_and_no_device():
+    L = ssm.lib()
+    h = ctypes.c_void_p()
+    assert L.ssm_block_plan_create(None, ctypes.byref(h)) == ssm.SSM_ERR_NULL_ARG
+    assert L.ssm_block_plan_create(ctypes.byref(block_dims()), None) == ssm.SSM_ERR_NULL_ARG
+    assert L.ssm_block_workspace_size(None) == 0
+    L.ssm_block_plan_destroy(None)
+    w = ssm.BlockWeights()
+    assert L.ssm_block_fwd(None, ctypes.byref(w), addr(0), addr(1), addr(2), 1 << 30, None) == \
+        ssm.SSM_ERR_NULL_ARG
+    # Valid sizes: a plan where a device is present, a clean error (not an exit) where none is.
+    st = L.ssm_block_plan_create(ctypes.byref(block_dims()), ctypes.byref(h))
+    assert st in (ssm.SSM_OK, ssm.SSM_ERR_HIP)
+    if st == ssm.SSM_OK:
+        assert L.ssm_block_workspace_size(h) > 0
+        L.ssm_block_plan_destroy(h)
+    else:
+        assert not h.value
