@@ -163,6 +163,38 @@ def bench_bwd(cfg, steps, warmup):
     return ms, nbytes
 
 
+def block_gemm_flops(cfg):
+    """Multiply-adds x 2 of the block's projections per call: in_proj (2D x d_model),
+    x_proj ((R + 2N) x D), dt_proj (D x R) and out_proj (d_model x D) over B*L rows."""
+    M = cfg.batch * cfg.seqlen
+    D, dm, R, N = cfg.d_inner, cfg.d_model, cfg.dt_rank, cfg.dstate
+    return 2 * M * (2 * D * dm + (R + 2 * N) * D + D * R + dm * D)
+
+
+def bench_block(cfg, steps, warmup):
+    """The whole Mamba block forward of `cfg` (one plan, one workspace, output rotated
+    between two buffers so no call writes what the previous one is still reading)."""
+    import torch
+    import selective_state_space_59_amd as ssm
+    from selective_state_space_59_amd import workloads as W
+    dev = "cuda:0"
+    s = W.make_block_config_inputs(cfg, device=dev)
+    plan = ssm.BlockPlan(cfg.batch, cfg.seqlen, cfg.d_model, cfg.d_inner, cfg.dstate, cfg.dt_rank,
+                         cfg.conv_k)
+    ws = torch.empty(plan.workspace_bytes, dtype=torch.uint8, device=dev)
+    outs = [torch.empty_like(s["h"]) for _ in range(2)]
+    names = ("norm_w", "w_in", "conv_w", "conv_b", "w_x", "w_dt", "dt_bias", "A", "Dskip", "w_out")
+
+    def run(i):
+        ssm.mamba_block_fwd(s["h"], *(s[k] for k in names), out=outs[i % 2], plan=plan, workspace=ws)
+
+    ms = time_launches(run, steps, warmup)
+    del s, outs, ws
+    plan.close()
+    torch.cuda.empty_cache()
+    return ms
+
+
 def bench_decode(cfg, reps=3, conv_k=0):
     """Decode steps of `cfg`; with conv_k, each step also runs the conv prologue on
     its (B, conv_k-1, D) window and shifts it (weights N(0, 0.5), seeded)."""
@@ -234,6 +266,17 @@ def cpu_baseline(inp, cfg):
                                                                   cfg.dstate, nthreads))
 
 
+def block_entry(cfg, steps, warmup):
+    ms = bench_block(cfg, steps, warmup)
+    fl = block_gemm_flops(cfg)
+    tokens = cfg.batch * cfg.seqlen
+    return dict(ms=round(ms, 4), tokens_per_s=round(tokens / (ms * 1e-3), 1),
+                gemm_flops=fl, gemm_tflops_over_block_time=round(fl / (ms * 1e-3) / 1e12, 2),
+                config=dict(batch=cfg.batch, seq_len=cfg.seqlen, d_model=cfg.d_model,
+                            d_inner=cfg.d_inner, dstate=cfg.dstate, dt_rank=cfg.dt_rank,
+                            conv_k=cfg.conv_k, io_dtype="bf16"))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -241,6 +284,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--no-extras", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--block-only", action="store_true",
+                    help="only time the 130M-like Mamba block forward and print its numbers")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (fp32) five times; its "
                          "FETCH_SIZE / WRITE_SIZE counters scale the scan's traffic counters")
@@ -264,6 +309,10 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes_read": 4 * n, "copy_bytes_written": 4 * n, "launches": 5}))
+        return
+
+    if args.block_only:
+        print(json.dumps({W.B2_130M.name: block_entry(W.B2_130M, args.steps, args.warmup)}), flush=True)
         return
 
     cfg = W.C2_130M
@@ -337,6 +386,9 @@ def main():
                 cold_gbs=round(db / (cold * 1e-3) / 1e9, 2),
                 cold_frac_hbm=round(db / (cold * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                 hot_gbs=round(db / (hot * 1e-3) / 1e9, 2), algorithmic_bytes_per_step=db)
+        # the whole Mamba block around the scan (RMSNorm, projections, conv, scan, residual)
+        print("bench extra: %s" % W.B2_130M.name, file=sys.stderr, flush=True)
+        extra[W.B2_130M.name] = block_entry(W.B2_130M, 30, 5)
         out["extra"] = extra
 
     if not args.no_cpu_baseline:

@@ -272,8 +272,10 @@ ssm_status_t ssm_selective_scan_bwd(const ssm_scan_bwd_args_t *args, void *strea
  *   dt_low = u W_x[0:R]^T, B = u W_x[R:R+N]^T, C = u W_x[R+N:R+2N]^T
  *   delta = dt_low W_dt^T;  y = S6(u, softplus(delta + dt_bias), A, B, C, D) * silu(z)
  *   h_out = h + y W_out^T
- * I/O and intermediates are bf16 (GEMMs accumulate in fp32); norm_w, conv
- * weights, dt_bias, A and Dskip are fp32.  The GEMMs run in hipBLASLt.
+ * I/O and intermediates are bf16 (products accumulate in fp32; the step
+ * softplus(delta + dt_bias) is formed in fp32 and stored in bf16); norm_w,
+ * conv weights, dt_bias, A and Dskip are fp32.  in_proj, x_proj and out_proj
+ * run in hipBLASLt, dt_proj in the library's own kernel.
  *
  * Usage: create a plan for the sizes (this creates a hipBLASLt handle and
  * picks the GEMM algorithms; host memory only, needs the GPU), query its
@@ -322,7 +324,8 @@ size_t ssm_block_workspace_size(const ssm_block_plan_t *plan);
  * h_in itself (updated in place) but may not overlap it otherwise or any
  * weight; nothing may overlap the workspace (256-aligned, >=
  * ssm_block_workspace_size).  bf16 tensors (h_in, h_out, w_in, w_x, w_dt,
- * w_out) must be 16-byte aligned, fp32 ones 4-byte aligned.  The plan may be
+ * w_out), norm_w and dt_bias must be 16-byte aligned, the other fp32 ones
+ * 4-byte aligned.  The plan may be
  * shared by calls on different streams only with separate workspaces.
  * Errors: SSM_ERR_NULL_ARG (plan, h_in, h_out or a required weight NULL),
  * SSM_ERR_BAD_SHAPE (norm_eps <= 0), SSM_ERR_ALIGN, SSM_ERR_WORKSPACE,

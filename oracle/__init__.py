@@ -251,6 +251,13 @@ def round_bf16(a):
     return out
 
 
+def _softplus(v):
+    """softplus(v) = log(1 + e^v), tau_Delta of Algorithm 2 on the paper summary page
+    "Mamba: Linear-Time Sequence Modeling with Selective State Spaces" (written as
+    log(e^0 + e^v) so that large v does not overflow)."""
+    return np.logaddexp(0.0, v)
+
+
 def rms_norm(h, weight, eps=1e-5):
     """RMSNorm over the last axis: h / sqrt(mean(h^2) + eps) * weight."""
     h = _f64(h)
@@ -271,8 +278,8 @@ def mamba_block_fwd(h, norm_w, w_in, conv_w, conv_b, w_x, w_dt, dt_bias, A, Dski
     Selective State Spaces" (sec. 4a; the projections and dt_rank of Algorithm 2).
     Shapes: h (B,L,d_model); norm_w (d_model,); w_in (2D, d_model); conv_w (D,K); conv_b (D,);
     w_x (R+2N, D); w_dt (D, R); dt_bias (D,); A (D,N); Dskip (D,); w_out (d_model, D).
-    With bf16=True every tensor the GPU path stores in bf16 (hn, x, z, u, dt_low, B, C, delta,
-    y and h_out) is rounded to bf16 at the same point here.
+    With bf16=True every tensor the GPU path stores in bf16 (hn, x, z, u, dt_low, B, C, the
+    step dt = softplus(delta + dt_bias), y and h_out) is rounded to bf16 at the same point here.
     """
     r = round_bf16 if bf16 else (lambda v: v)
     h = _f64(h)
@@ -286,7 +293,6 @@ def mamba_block_fwd(h, norm_w, w_in, conv_w, conv_b, w_x, w_dt, dt_bias, A, Dski
     u = r(causal_conv1d_silu(x, conv_w, conv_b, nthreads=nthreads))
     xd = u @ w_x.T
     dt_low, Bm, Cm = r(xd[..., :R]), r(xd[..., R:R + N]), r(xd[..., R + N:])
-    delta = r(dt_low @ w_dt.T)
-    y, _ = selective_scan(u, delta, A, Bm, Cm, Dskip=Dskip, z=z, delta_bias=dt_bias,
-                          delta_softplus=True, nthreads=nthreads)
+    dt = r(_softplus(dt_low @ w_dt.T + _f64(dt_bias)))
+    y, _ = selective_scan(u, dt, A, Bm, Cm, Dskip=Dskip, z=z, nthreads=nthreads)
     return r(h + r(y) @ w_out.T)

@@ -173,14 +173,6 @@ __device__ __forceinline__ void buf_st(__amdgpu_buffer_rsrc_t r, uint32_t off, f
         __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, off, 0, 0);
 }
 
-__device__ __forceinline__ float softplus_fast(float v) {
-    // max(v,0) + log(1 + e^-|v|); for tiny w = e^-|v|, log(1+w) ~ w (1 - w/2).
-    const float w = hw_exp2(-fabsf(v) * kLog2e);
-    const float lg = __builtin_amdgcn_logf(1.0f + w) * 0.69314718055994531f;
-    const float small = w * (1.0f - 0.5f * w);
-    return fmaxf(v, 0.0f) + (w < 0.0078125f ? small : lg);
-}
-
 // phi(z) = (e^z - 1) / z given e = e^z; series for small |z|.
 __device__ __forceinline__ float phi_of(float z, float e) {
     const float s = 1.0f + z * (0.5f + z * (1.0f / 6.0f + z * (1.0f / 24.0f +

@@ -409,9 +409,10 @@ ssm_status_t ssm_block_fwd(const ssm_block_plan_t *plan, const ssm_block_weights
     if (!(w->norm_eps > 0.0f) || !(w->norm_eps < 1e30f)) return fail(SSM_ERR_BAD_SHAPE, "norm_eps must be > 0");
     const ssm_block_dims_t &d = ssm::block_dims(*plan);
     const int64_t M = d.batch * d.seqlen, D = d.d_inner, N = d.dstate, R = d.dt_rank, dm = d.d_model;
-    const void *bf[] = {w->w_in, w->w_x, w->w_dt, w->w_out, h_in, h_out};
+    const void *bf[] = {w->w_in, w->w_x, w->w_dt, w->w_out, h_in, h_out, w->norm_w, w->dt_bias};
     for (const void *v : bf)
-        if (!aligned(v, 16)) return fail(SSM_ERR_ALIGN, "bf16 tensors must be 16-byte aligned");
+        if (!aligned(v, 16))
+            return fail(SSM_ERR_ALIGN, "bf16 tensors, norm_w and dt_bias must be 16-byte aligned");
     const void *f4[] = {w->norm_w, w->conv_w, w->conv_b, w->dt_bias, w->A, w->Dskip};
     for (const void *v : f4)
         if (!aligned(v, 4)) return fail(SSM_ERR_ALIGN, "fp32 tensors must be 4-byte aligned");

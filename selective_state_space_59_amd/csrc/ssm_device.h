@@ -24,12 +24,19 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
     return __uint_as_float(bits16 << 16);
 }
 
-// fp32 -> bf16 bits, round to nearest even; NaN stays a (quiet) NaN.
+// fp32 -> bf16 bits, round to nearest even; NaN stays a (quiet) NaN.  gfx950
+// converts in hardware (v_cvt_pk_bf16_f32, two values per instruction).
 __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
+    return __builtin_bit_cast(uint16_t, (__bf16)f);
+}
+
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// Two fp32 values -> packed bf16 bits (lo in bits 0..15), one conversion.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    const f32x2_t v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
 template <typename IO>
@@ -62,6 +69,15 @@ __device__ __forceinline__ float hw_rcp(float v) { return __builtin_amdgcn_rcpf(
 // SiLU(v) = v * sigmoid(v) = v / (1 + e^-v).
 __device__ __forceinline__ float silu(float v) {
     return v * hw_rcp(1.0f + hw_exp2(-v * kLog2e));
+}
+
+// softplus with the hardware exp2 / log2: max(v,0) + log(1 + w), w = e^-|v|;
+// for tiny w, log(1+w) ~ w (1 - w/2) keeps the relative accuracy.
+__device__ __forceinline__ float softplus_fast(float v) {
+    const float w = hw_exp2(-fabsf(v) * kLog2e);
+    const float lg = __builtin_amdgcn_logf(1.0f + w) * 0.69314718055994531f;
+    const float small = w * (1.0f - 0.5f * w);
+    return fmaxf(v, 0.0f) + (w < 0.0078125f ? small : lg);
 }
 
 // softplus(v) = max(v, 0) + log(1 + e^-|v|), the overflow-free form.

@@ -1,7 +1,7 @@
 """Parity of the whole Mamba block (ssm_block_fwd) against the fp64 oracle (needs an MI355X).
 
 The oracle's block rounds to bf16 exactly where the GPU path stores bf16 (hn,
-x, z, u, dt_low, B, C, delta, y, h_out), so both sides see the same kind of
+x, z, u, dt_low, B, C, the step dt, y, h_out), so both sides see the same kind of
 intermediates; the GEMMs accumulate in a different order (fp32 on the GPU,
 fp64 in the oracle), which can move an intermediate by one bf16 ulp.  Bound:
 the bf16 tolerance of the scan, |got - ref| <= 1e-2 (1 + |ref|) per element
@@ -41,6 +41,9 @@ CASES = [
     ("k3_n8_ragged", 3, 129, 48, 96, 8, 6, 3, False),
     ("l1", 2, 1, 64, 128, 16, 4, 4, False),
     ("long_two_tiles", 1, 700, 128, 256, 16, 8, 2, False),
+    ("rank80_stepped", 1, 40, 64, 128, 16, 80, 4, False),   # rank > 64: operands per step
+    ("rank70_narrow", 2, 33, 64, 136, 16, 70, 4, False),    # rank, row stride not multiples of 4
+    ("wide_channels", 1, 20, 256, 1040, 16, 16, 4, False),  # channel blocks with a ragged last one
 ]
 
 

@@ -174,7 +174,13 @@ def test_full_size_config_sampled(cfg):
 @pytest.mark.parametrize("B,L,D,K,dt", [(2, 100, 130, 4, torch.bfloat16),
                                         (1, 65, 64, 3, torch.float32),
                                         (3, 1, 7, 4, torch.float32),
-                                        (1, 200, 33, 1, torch.bfloat16)])
+                                        (1, 200, 33, 1, torch.bfloat16),
+                                        # 16-byte channel groups (D a multiple of 8 / 4)
+                                        (2, 100, 136, 4, torch.bfloat16),
+                                        (1, 70, 64, 2, torch.bfloat16),
+                                        (2, 37, 1536, 4, torch.bfloat16),
+                                        (1, 40, 16, 1, torch.bfloat16),
+                                        (2, 45, 20, 4, torch.float32)])
 def test_conv1d_silu_matches_oracle(B, L, D, K, dt):
     g = torch.Generator(DEV).manual_seed(B * 1000 + L)
     x = torch.randn(B, L, D, device=DEV, generator=g).to(dt)
