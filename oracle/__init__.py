@@ -62,6 +62,9 @@ def _load():
                                                       P, P, P,
                                                       P, P, P, P, P, P, P, P, P, P, P, I]
         lib.oracle_selective_scan_bwd_f64.restype = I
+        lib.oracle_ssd_f64.argtypes = [I64, I64, I64, I64, I64, I64,
+                                       P, P, P, P, P, P, P, P, I, P, P, P, I]
+        lib.oracle_ssd_f64.restype = I
         _lib = lib
     return _lib
 
@@ -296,3 +299,86 @@ def mamba_block_fwd(h, norm_w, w_in, conv_w, conv_b, w_x, w_dt, dt_bias, A, Dski
     dt = r(_softplus(dt_low @ w_dt.T + _f64(dt_bias)))
     y, _ = selective_scan(u, dt, A, Bm, Cm, Dskip=Dskip, z=z, nthreads=nthreads)
     return r(h + r(y) @ w_out.T)
+
+
+def ssd(x, delta, A, Bm, Cm, Dskip=None, z=None, delta_bias=None, delta_softplus: bool = False,
+        h0=None, nthreads: Optional[int] = None):
+    """The SSD (Mamba-2) layer in recurrent mode, in float64 (``oracle_ssd_f64``): per head a
+    scalar A_t = a_t I ("14.1 SSM(State Space Models)과 Mamba 아키텍처의 부상", sec. 5.1),
+    discretised by ZOH (eq. (4) of the paper summary page "Mamba: Linear-Time Sequence
+    Modeling with Selective State Spaces").  Returns (y, h_final).
+
+    x, z: (B, L, H, P); delta: (B, L, H); A, Dskip, delta_bias: (H,); Bm, Cm: (B, L, G, N)
+    with H a multiple of G (head h reads group h // (H // G)); h0, h_final: (B, H, P, N).
+    """
+    x = _f64(x)
+    Bsz, L, H, P = x.shape
+    Bm = _f64(Bm)
+    G, N = Bm.shape[2], Bm.shape[3]
+    delta = _f64(delta, (Bsz, L, H))
+    A = _f64(A, (H,))
+    Bm = _f64(Bm, (Bsz, L, G, N))
+    Cm = _f64(Cm, (Bsz, L, G, N))
+    Dskip = _f64(Dskip, (H,))
+    z = _f64(z, (Bsz, L, H, P))
+    delta_bias = _f64(delta_bias, (H,))
+    h0 = _f64(h0, (Bsz, H, P, N))
+    y = np.zeros((Bsz, L, H, P), np.float64)
+    hf = np.zeros((Bsz, H, P, N), np.float64)
+    rc = _load().oracle_ssd_f64(Bsz, L, H, P, G, N, _ptr(x), _ptr(delta), _ptr(A), _ptr(Bm),
+                                _ptr(Cm), _ptr(Dskip), _ptr(z), _ptr(delta_bias),
+                                int(bool(delta_softplus)), _ptr(h0), _ptr(y), _ptr(hf),
+                                int(nthreads or default_threads()))
+    if rc != 0:
+        raise ValueError("oracle_ssd_f64 rejected the sizes")
+    return y, hf
+
+
+def ssd_quadratic(x, delta, A, Bm, Cm, Dskip=None, z=None, h0=None):
+    """The same layer in its quadratic ("attention") mode, float64 numpy: per (batch, head)
+    Y = (L o (C B^T)) (w X) + D X, the duality form of sec. 5.1 of "14.1 SSM(State Space
+    Models)과 Mamba 아키텍처의 부상", with L[t, s] = prod_{r=s+1..t} alpha_r for s <= t and 0
+    above the diagonal (the causal mask of cumulative decays), alpha_t = exp(dt_t a) and
+    w_s the ZOH input weight.  An entering state h0 adds (prod_{r<=t} alpha_r) C_t h0.
+    Returns (y, h_final) like ``ssd``; delta is the step itself (no softplus here).
+    """
+    x = _f64(x)
+    Bsz, L, H, P = x.shape
+    Bm = _f64(Bm)
+    G, N = Bm.shape[2], Bm.shape[3]
+    delta = _f64(delta, (Bsz, L, H))
+    A = _f64(A, (H,))
+    Cm = _f64(Cm, (Bsz, L, G, N))
+    hpg = H // G
+    y = np.zeros((Bsz, L, H, P))
+    hf = np.zeros((Bsz, H, P, N))
+    t_idx = np.arange(L)
+    for b in range(Bsz):
+        for h in range(H):
+            g = h // hpg
+            za = delta[b, :, h] * A[h]                       # dt_t a, (L,)
+            w = np.where(za == 0.0, delta[b, :, h], np.expm1(za) / np.where(za == 0.0, 1.0, A[h]))
+            cs = np.concatenate([[0.0], np.cumsum(za)])      # cs[t+1] = sum_{r<=t} dt_r a
+            # log L[t, s] = sum_{r=s+1..t} dt_r a = cs[t+1] - cs[s+1]
+            logm = cs[1:, None] - cs[None, 1:]
+            causal = t_idx[:, None] >= t_idx[None, :]
+            mask = np.where(causal, np.exp(np.where(causal, logm, 0.0)), 0.0)
+            M = mask * (Cm[b, :, g, :] @ Bm[b, :, g, :].T)   # (L, L)
+            Xw = w[:, None] * x[b, :, h, :]                  # (L, P)
+            yb = M @ Xw
+            decay_in = np.exp(cs[1:])                        # prod_{r<=t} alpha_r
+            if h0 is not None:
+                yb += decay_in[:, None] * (Cm[b, :, g, :] @ _f64(h0)[b, h].T)
+            if Dskip is not None:
+                yb += _f64(Dskip)[h] * x[b, :, h, :]
+            if z is not None:
+                zz = _f64(z)[b, :, h, :]
+                yb *= zz / (1.0 + np.exp(-zz))
+            y[b, :, h, :] = yb
+            # final state: sum_s (prod_{r=s+1..L-1} alpha_r) w_s x_s B_s^T (+ decayed h0)
+            tail = np.exp(cs[L] - cs[1:]) if L else np.zeros(0)
+            hfin = (tail[:, None] * Xw).T @ Bm[b, :, g, :]   # (P, N)
+            if h0 is not None:
+                hfin += np.exp(cs[L]) * _f64(h0)[b, h]
+            hf[b, h] = hfin
+    return y, hf

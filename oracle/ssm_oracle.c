@@ -18,7 +18,8 @@
  *   [P2] "2. Mamba 상세" (EulerStack mixer tutorial): the YAML example
  *        (d_conv: 4, ssm_state kept for inference).
  *   [P4] "14.1 SSM(State Space Models)과 Mamba 아키텍처의 부상": sec. 3.1
- *        (y = C h + D x, the D skip term), sec. 3.2 (ZOH), sec. 4.1 (selection).
+ *        (y = C h + D x, the D skip term), sec. 3.2 (ZOH), sec. 4.1 (selection),
+ *        sec. 5.1 (SSD: a scalar-times-identity state matrix per head).
  *
  * Readings taken where the pages leave a step open (each one is listed in the
  * design notes):
@@ -86,7 +87,7 @@ static double conv_silu_at(const double *x, const double *hist, int64_t stride, 
     return silu(acc);
 }
 
-int oracle_abi_version(void) { return 2; }
+int oracle_abi_version(void) { return 3; }
 
 /*
  * Selective scan forward ([P1] Algorithm 2 with the block's gate and the
@@ -407,5 +408,66 @@ int oracle_selective_scan_bwd_f64(int64_t Bsz, int64_t L, int64_t D, int64_t N,
             }
     }
     free(pA); free(pD); free(pbias); free(pw); free(pb);
+    return 0;
+}
+
+/*
+ * Structured state-space duality (SSD, the Mamba-2 layer) in its recurrent
+ * ("linear") mode, from [P4] sec. 5.1: the state matrix is a scalar times the
+ * identity, A_t = a_t I, with one scalar per head, so every channel of a head
+ * decays by the same factor.  Discretised like the rest of this oracle by the
+ * ZOH rule of [P1] eq. (4) / [P4] sec. 3.2, which for A = a I reduces to
+ *   alpha_t = exp(dt_t a_h),   w_t = (dt_t a_h)^-1 (exp(dt_t a_h) - 1) dt_t
+ * (= dt_t when dt_t a_h == 0).  Per batch b, head h, head channel p and state
+ * entry n, with g the group of the head (heads split evenly over G groups,
+ * which share B and C):
+ *   S_t[p,n] = alpha_t S_{t-1}[p,n] + w_t B_t[g,n] x_t[h,p]
+ *   y_t[h,p] = (sum_n C_t[g,n] S_t[p,n] + Dskip[h] x_t[h,p]) * silu(z_t[h,p])
+ *
+ * Shapes: x, z, y (B,L,H,P); delta (B,L,H); A, Dskip, delta_bias (H);
+ * Bm, Cm (B,L,G,N); h0, h_final (B,H,P,N).  dt is delta, or softplus(delta +
+ * bias) when requested.  Optional arguments may be NULL.  Threads split the
+ * independent (batch, head) pairs.  Returns 0, or -1 on a bad size.
+ */
+int oracle_ssd_f64(int64_t Bsz, int64_t L, int64_t H, int64_t P, int64_t G, int64_t N,
+                   const double *x, const double *delta, const double *A, const double *Bm,
+                   const double *Cm, const double *Dskip, const double *z,
+                   const double *delta_bias, int delta_softplus, const double *h0, double *y,
+                   double *h_final, int nthreads)
+{
+    if (Bsz < 0 || L < 0 || H < 1 || P < 1 || G < 1 || N < 1 || H % G != 0) return -1;
+    if (nthreads < 1) nthreads = 1;
+    const int64_t heads_per_group = H / G;
+    const int64_t npairs = Bsz * H;
+#pragma omp parallel for num_threads(nthreads) schedule(dynamic, 1)
+    for (int64_t bh = 0; bh < npairs; ++bh) {
+        const int64_t b = bh / H, h = bh % H, g = h / heads_per_group;
+        double *S = (double *)malloc(sizeof(double) * (size_t)(P * N));
+        for (int64_t i = 0; i < P * N; ++i) S[i] = h0 ? h0[bh * P * N + i] : 0.0;
+        for (int64_t t = 0; t < L; ++t) {
+            double dt = delta[(b * L + t) * H + h];
+            if (delta_softplus) dt = softplus(dt + (delta_bias ? delta_bias[h] : 0.0));
+            const double *Bt = Bm + ((b * L + t) * G + g) * N;
+            const double *Ct = Cm + ((b * L + t) * G + g) * N;
+            for (int64_t p = 0; p < P; ++p) {
+                const int64_t i = ((b * L + t) * H + h) * P + p;
+                const double u = x[i];
+                double acc = 0.0;
+                for (int64_t n = 0; n < N; ++n) {
+                    double abar, bbar;
+                    zoh(dt, A[h], Bt[n], &abar, &bbar);
+                    double *s = S + p * N + n;
+                    *s = abar * *s + bbar * u;
+                    acc += Ct[n] * *s;
+                }
+                double yv = acc + (Dskip ? Dskip[h] * u : 0.0);
+                if (z) yv *= silu(z[i]);
+                y[i] = yv;
+            }
+        }
+        if (h_final)
+            for (int64_t i = 0; i < P * N; ++i) h_final[bh * P * N + i] = S[i];
+        free(S);
+    }
     return 0;
 }
