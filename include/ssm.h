@@ -9,7 +9,8 @@
  *   - ssm_state_update: one recurrent (decode) step on a resident state;
  *   - ssm_causal_conv1d_silu: the conv prologue on its own;
  *   - ssm_selective_scan_bwd: the gradients of the scan (training);
- *   - ssm_block_fwd: a whole Mamba block around the scan (with a plan).
+ *   - ssm_block_fwd: a whole Mamba block around the scan (with a plan);
+ *   - ssm_ssd_fwd: the SSD (Mamba-2) layer, chunked on the matrix cores.
  *
  * The operations are defined on these pages (cited by title and section):
  *   [P1] "Mamba: Linear-Time Sequence Modeling with Selective State Spaces"
@@ -21,7 +22,7 @@
  *        ssm_state kept between inference steps.
  *   [P4] "14.1 SSM(State Space Models)과 Mamba 아키텍처의 부상": sec. 3.1
  *        (y = C h + D x, the D skip), sec. 3.2 (ZOH), sec. 4.1 (Delta =
- *        softplus(parameter + projection)).
+ *        softplus(parameter + projection)), sec. 5.1/5.2 (SSD, chunks).
  *
  * Conventions common to every entry point
  *   - Every tensor pointer is a DEVICE pointer into memory the caller owns
@@ -61,7 +62,7 @@
 extern "C" {
 #endif
 
-#define SSM_ABI_VERSION 4
+#define SSM_ABI_VERSION 5
 #define SSM_MAX_DSTATE 16 /* largest N the kernels hold in registers */
 #define SSM_MAX_CONV_K 4  /* largest conv1d kernel width */
 
@@ -337,6 +338,52 @@ ssm_status_t ssm_block_fwd(const ssm_block_plan_t *plan, const ssm_block_weights
 
 /* Release a plan (NULL is ignored). */
 void ssm_block_plan_destroy(ssm_block_plan_t *plan);
+
+/*
+ * The SSD (Mamba-2) layer: [P4] sec. 5.1 restricts the state matrix to a
+ * scalar times the identity per step and head, A_t = a_t I, which makes the
+ * layer the masked product Y = (L o (C B^T)) X with L the causal mask of
+ * cumulative decays; sec. 5.2 evaluates it chunk by chunk (the quadratic form
+ * inside a chunk on the matrix cores, the recurrence between chunks).  With
+ * the ZOH rule of [P1] eq. (4) for A = a I, per batch b, head h, head channel
+ * p, state entry n and step t (g = h / (H / G) the head's group):
+ *   dt      = delta[b,t,h], or softplus(delta[b,t,h] + delta_bias[h])
+ *   S[p,n] <- exp(dt A[h]) S[p,n] + (exp(dt A[h]) - 1) / A[h] Bm[b,t,g,n] x[b,t,h,p]
+ *             (the weight is dt where dt A[h] == 0), from h0 (or 0)
+ *   y[b,t,h,p] = (sum_n Cm[b,t,g,n] S[p,n] + Dskip[h] x[b,t,h,p]) * silu(z[b,t,h,p])
+ * The state layout (B, H, P, N) is the scan's (B, D, N) with D = H P.
+ * This version: bf16 I/O, headdim P == 64, dstate N in {16, 32, 64, 128};
+ * other values give SSM_ERR_UNSUPPORTED.  Products run in bf16 on the matrix
+ * cores with fp32 accumulation; the state is fp32 (its bf16 copy feeds the
+ * product with C).
+ */
+typedef struct ssm_ssd_args {
+    int64_t batch, seqlen;  /* B >= 0, L >= 0                                  */
+    int64_t nheads;         /* H >= 1                                          */
+    int64_t headdim;        /* P (64)                                          */
+    int64_t ngroups;        /* G >= 1, divides H: heads of a group share B, C  */
+    int64_t dstate;         /* N (16, 32, 64 or 128)                           */
+    int32_t io_dtype;       /* SSM_BF16                                        */
+    int32_t delta_softplus; /* 0: delta is the step; 1: softplus(delta + bias) */
+    const void *x;          /* (B,L,H,P) bf16, required                        */
+    const void *delta;      /* (B,L,H) bf16, required                          */
+    const float *A;         /* (H) fp32, required; any finite value            */
+    const void *Bm, *Cm;    /* (B,L,G,N) bf16, required                        */
+    const float *Dskip;     /* (H) fp32, or NULL                               */
+    const void *z;          /* (B,L,H,P) bf16 gate, or NULL                    */
+    const float *delta_bias;/* (H) fp32, or NULL                               */
+    const float *h0;        /* (B,H,P,N) fp32 initial state, or NULL (= 0)     */
+    void *y;                /* (B,L,H,P) bf16 output, required                 */
+    float *h_final;         /* (B,H,P,N) fp32 output, or NULL                  */
+} ssm_ssd_args_t;
+
+/*
+ * Enqueue the SSD layer on `stream`.  x, Bm, Cm, z and y must be 16-byte
+ * aligned, delta 2-byte, the fp32 tensors 4-byte.  y and h_final must not
+ * overlap any input or each other.  L == 0 copies h0 (or zeros) to h_final;
+ * the (B,L,...) pointers may then be NULL.
+ */
+ssm_status_t ssm_ssd_fwd(const ssm_ssd_args_t *args, void *stream);
 
 /* Static description of a status code (never NULL). */
 const char *ssm_status_string(ssm_status_t status);

@@ -20,7 +20,8 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libssm_hip.so")
 ARCH = "gfx950"
 
-SOURCES = ["ssm_api.cpp", "scan_fwd.hip", "scan_bwd.hip", "conv1d.hip", "state_update.hip", "block.hip"]
+SOURCES = ["ssm_api.cpp", "scan_fwd.hip", "scan_bwd.hip", "conv1d.hip", "state_update.hip", "block.hip",
+           "ssd.hip"]
 # hipBLASLt runs the plain GEMMs of the Mamba block.
 LIBS = ["-L/opt/rocm/lib", "-lhipblaslt", "-Wl,-rpath,/opt/rocm/lib"]
 

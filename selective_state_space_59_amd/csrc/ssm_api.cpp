@@ -445,4 +445,50 @@ ssm_status_t ssm_block_fwd(const ssm_block_plan_t *plan, const ssm_block_weights
     return ok();
 }
 
+ssm_status_t ssm_ssd_fwd(const ssm_ssd_args_t *a, void *stream) {
+    if (!a) return fail(SSM_ERR_NULL_ARG, "args is NULL");
+    if (a->io_dtype != SSM_F32 && a->io_dtype != SSM_BF16)
+        return fail(SSM_ERR_BAD_DTYPE, "io_dtype %d is not SSM_F32 or SSM_BF16", a->io_dtype);
+    if (a->batch < 0 || a->seqlen < 0) return fail(SSM_ERR_BAD_SHAPE, "negative batch or seqlen");
+    if (a->nheads < 1 || a->headdim < 1 || a->ngroups < 1 || a->dstate < 1)
+        return fail(SSM_ERR_BAD_SHAPE, "nheads, headdim, ngroups and dstate must be >= 1");
+    if (a->nheads % a->ngroups != 0)
+        return fail(SSM_ERR_BAD_SHAPE, "ngroups (%lld) must divide nheads (%lld)", (long long)a->ngroups,
+                    (long long)a->nheads);
+    if (a->io_dtype != SSM_BF16) return fail(SSM_ERR_UNSUPPORTED, "the SSD layer takes bf16 I/O");
+    if (!ssm::ssd_supported(a->headdim, a->dstate))
+        return fail(SSM_ERR_UNSUPPORTED, "SSD needs headdim 64 and dstate 16, 32, 64 or 128 (got %lld, %lld)",
+                    (long long)a->headdim, (long long)a->dstate);
+    if (a->delta_softplus != 0 && a->delta_softplus != 1)
+        return fail(SSM_ERR_UNSUPPORTED, "delta_softplus must be 0 or 1");
+    const int64_t B = a->batch, L = a->seqlen, H = a->nheads, P = a->headdim, G = a->ngroups, N = a->dstate;
+    if (!mul_ok(B, L, H * P) || !mul_ok(B, L, G * N) || !mul_ok(B, H, P * N))
+        return fail(SSM_ERR_BAD_SHAPE, "sizes overflow");
+    if (!a->A) return fail(SSM_ERR_NULL_ARG, "A is required");
+    if (B * L > 0 && (!a->x || !a->delta || !a->Bm || !a->Cm || !a->y))
+        return fail(SSM_ERR_NULL_ARG, "x, delta, Bm, Cm and y are required");
+    const void *a16[] = {a->x, a->Bm, a->Cm, a->z, a->y};
+    for (const void *v : a16)
+        if (!aligned(v, 16)) return fail(SSM_ERR_ALIGN, "x, Bm, Cm, z and y must be 16-byte aligned");
+    if (!aligned(a->delta, 2)) return fail(SSM_ERR_ALIGN, "delta must be 2-byte aligned");
+    const void *a4[] = {a->A, a->Dskip, a->delta_bias, a->h0, a->h_final};
+    for (const void *v : a4)
+        if (!aligned(v, 4)) return fail(SSM_ERR_ALIGN, "fp32 tensors must be 4-byte aligned");
+    const Range inputs[] = {range(a->x, B * L * H * P, 2, "x"), range(a->delta, B * L * H, 2, "delta"),
+                            range(a->A, H, 4, "A"), range(a->Bm, B * L * G * N, 2, "Bm"),
+                            range(a->Cm, B * L * G * N, 2, "Cm"), range(a->Dskip, H, 4, "Dskip"),
+                            range(a->z, B * L * H * P, 2, "z"), range(a->delta_bias, H, 4, "delta_bias"),
+                            range(a->h0, B * H * P * N, 4, "h0")};
+    const Range y = range(a->y, B * L * H * P, 2, "y"), hf = range(a->h_final, B * H * P * N, 4, "h_final");
+    for (const Range &r : inputs) {
+        if (overlaps(y, r)) return fail(SSM_ERR_ALIAS, "y overlaps %s", r.name);
+        if (overlaps(hf, r)) return fail(SSM_ERR_ALIAS, "h_final overlaps %s", r.name);
+    }
+    if (overlaps(y, hf)) return fail(SSM_ERR_ALIAS, "h_final overlaps y");
+    if (B == 0) return ok();
+    const hipError_t e = ssm::launch_ssd_fwd(*a, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(SSM_ERR_HIP, "HIP error: %s", hipGetErrorString(e));
+    return ok();
+}
+
 }  // extern "C"

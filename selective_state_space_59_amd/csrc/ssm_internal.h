@@ -37,6 +37,10 @@ const ssm_block_dims_t &block_dims(const ssm_block_plan &p);
 hipError_t launch_block_fwd(const ssm_block_plan &p, const ssm_block_weights_t &w, const void *h_in, void *h_out,
                             void *workspace, hipStream_t stream);
 
+// SSD (Mamba-2) layer (ssd.hip).  a.batch > 0; sizes checked by ssd_supported.
+bool ssd_supported(int64_t headdim, int64_t dstate);
+hipError_t launch_ssd_fwd(const ssm_ssd_args_t &a, hipStream_t stream);
+
 // Copy or zero-fill the final state for an empty (L == 0) scan.
 hipError_t launch_empty_scan_state(const ssm_scan_args_t &a, hipStream_t stream);
 

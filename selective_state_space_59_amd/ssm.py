@@ -38,7 +38,7 @@ EXPORTED_SYMBOLS = ("ssm_selective_scan_workspace_size", "ssm_selective_scan_fwd
                     "ssm_last_error_message", "ssm_abi_version",
                     "ssm_selective_scan_bwd_workspace_size", "ssm_selective_scan_bwd",
                     "ssm_block_plan_create", "ssm_block_workspace_size", "ssm_block_fwd",
-                    "ssm_block_plan_destroy")
+                    "ssm_block_plan_destroy", "ssm_ssd_fwd")
 
 _P = ctypes.c_void_p
 _I64 = ctypes.c_int64
@@ -90,6 +90,14 @@ class BlockWeights(ctypes.Structure):
                 ("norm_eps", ctypes.c_float)]
 
 
+class SsdArgs(ctypes.Structure):
+    """Mirror of ssm_ssd_args_t."""
+    _fields_ = [("batch", _I64), ("seqlen", _I64), ("nheads", _I64), ("headdim", _I64),
+                ("ngroups", _I64), ("dstate", _I64), ("io_dtype", _I32), ("delta_softplus", _I32),
+                ("x", _P), ("delta", _P), ("A", _P), ("Bm", _P), ("Cm", _P), ("Dskip", _P),
+                ("z", _P), ("delta_bias", _P), ("h0", _P), ("y", _P), ("h_final", _P)]
+
+
 class SSMError(RuntimeError):
     def __init__(self, status: int, message: str):
         super().__init__(message)
@@ -133,6 +141,8 @@ def lib() -> ctypes.CDLL:
         L.ssm_block_fwd.restype = ctypes.c_int
         L.ssm_block_plan_destroy.argtypes = [_P]
         L.ssm_block_plan_destroy.restype = None
+        L.ssm_ssd_fwd.argtypes = [ctypes.POINTER(SsdArgs), _P]
+        L.ssm_ssd_fwd.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -507,3 +517,42 @@ def mamba_block_fwd(h: torch.Tensor, norm_w: torch.Tensor, w_in: torch.Tensor, c
                                workspace.numel() * workspace.element_size(), _stream(dev)),
            "ssm_block_fwd")
     return out
+
+
+def ssd_fwd(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, Bm: torch.Tensor, Cm: torch.Tensor,
+            Dskip: Optional[torch.Tensor] = None, z: Optional[torch.Tensor] = None,
+            delta_bias: Optional[torch.Tensor] = None, delta_softplus: bool = False,
+            h0: Optional[torch.Tensor] = None, y: Optional[torch.Tensor] = None,
+            h_final: Optional[torch.Tensor] = None, return_final_state: bool = False):
+    """ssm_ssd_fwd: the SSD (Mamba-2) layer.  x, z: (B, L, H, P) bf16; delta: (B, L, H) bf16;
+    A, Dskip, delta_bias: (H,) fp32; Bm, Cm: (B, L, G, N) bf16; h0, h_final: (B, H, P, N) fp32.
+    Returns y, or (y, h_final) with return_final_state or h_final given."""
+    if not isinstance(x, torch.Tensor) or x.dim() != 4 or x.device.type != "cuda":
+        raise ValueError("x must be a (B, L, H, P) GPU tensor")
+    if not isinstance(Bm, torch.Tensor) or Bm.dim() != 4:
+        raise ValueError("Bm must be (B, L, G, N)")
+    dev = x.device
+    Bsz, L, H, P = x.shape
+    G, N = Bm.shape[2], Bm.shape[3]
+    bf, f32 = torch.bfloat16, torch.float32
+    _req(x, "x", (Bsz, L, H, P), bf, dev)
+    _req(delta, "delta", (Bsz, L, H), bf, dev)
+    _req(A, "A", (H,), f32, dev)
+    _req(Bm, "Bm", (Bsz, L, G, N), bf, dev)
+    _req(Cm, "Cm", (Bsz, L, G, N), bf, dev)
+    _opt(Dskip, "Dskip", (H,), f32, dev)
+    _opt(z, "z", (Bsz, L, H, P), bf, dev)
+    _opt(delta_bias, "delta_bias", (H,), f32, dev)
+    _opt(h0, "h0", (Bsz, H, P, N), f32, dev)
+    if y is None:
+        y = torch.empty_like(x)
+    _req(y, "y", (Bsz, L, H, P), bf, dev)
+    if h_final is None and return_final_state:
+        h_final = torch.empty(Bsz, H, P, N, device=dev, dtype=f32)
+    _opt(h_final, "h_final", (Bsz, H, P, N), f32, dev)
+    a = SsdArgs(batch=Bsz, seqlen=L, nheads=H, headdim=P, ngroups=G, dstate=N, io_dtype=SSM_BF16,
+                delta_softplus=int(bool(delta_softplus)), x=_ptr(x), delta=_ptr(delta), A=_ptr(A),
+                Bm=_ptr(Bm), Cm=_ptr(Cm), Dskip=_ptr(Dskip), z=_ptr(z), delta_bias=_ptr(delta_bias),
+                h0=_ptr(h0), y=_ptr(y), h_final=_ptr(h_final))
+    _check(lib().ssm_ssd_fwd(ctypes.byref(a), _stream(dev)), "ssm_ssd_fwd")
+    return (y, h_final) if h_final is not None else y

@@ -102,6 +102,24 @@ class BlockConfig:
 B2_130M = BlockConfig("b2_mamba130m_block", 8, 2048, 768, 1536, 16, 48, 4, seed=21)
 
 
+@dataclasses.dataclass(frozen=True)
+class SsdConfig:
+    """Sizes of one SSD (Mamba-2) layer: H heads of P channels, N state entries."""
+    name: str
+    batch: int
+    seqlen: int
+    nheads: int
+    headdim: int
+    ngroups: int
+    dstate: int
+    seed: int
+
+
+# The 130M-like width (D = 1536 = 24 heads x 64) with the Mamba-2 state size N = 128,
+# at the batch and length of the 130M-like scan.
+S2_MAMBA2_130M = SsdConfig("s2_mamba2_130m_ssd", 8, 2048, 24, 64, 1, 128, seed=31)
+
+
 def _gen(device, seed: int) -> torch.Generator:
     g = torch.Generator(device=device)
     g.manual_seed(int(seed))
@@ -221,3 +239,30 @@ def make_block_config_inputs(cfg: BlockConfig, device="cpu", **overrides):
               dstate=cfg.dstate, dt_rank=cfg.dt_rank, conv_k=cfg.conv_k, seed=cfg.seed)
     kw.update(overrides)
     return make_block_inputs(device=device, **kw)
+
+
+def make_ssd_inputs(batch: int, seqlen: int, nheads: int, headdim: int, ngroups: int, dstate: int,
+                    seed: int = 31, device="cpu", gate: bool = True, skip: bool = True,
+                    h0: bool = False, delta_shift: float = 2.0) -> Dict[str, Optional[torch.Tensor]]:
+    """Draw one SSD input set, in order: x ~ N(0,1); delta = softplus(N(0,1) - shift) (the
+    step, already activated); B, C ~ N(0,1) (as for the scan); z ~ N(0,1);
+    A = -(1 .. H) / H * 4 (one negative scalar per head, spread over (0, 4]); Dskip ~ N(0,1);
+    h0 ~ N(0,1).  Activations in bf16, the per-head vectors and the state in fp32."""
+    g = _gen(device, seed)
+    bf = torch.bfloat16
+    x = _randn((batch, seqlen, nheads, headdim), g, device).to(bf)
+    delta = F.softplus(_randn((batch, seqlen, nheads), g, device, shift=delta_shift)).to(bf)
+    Bm = _randn((batch, seqlen, ngroups, dstate), g, device).to(bf)
+    Cm = _randn((batch, seqlen, ngroups, dstate), g, device).to(bf)
+    z = _randn((batch, seqlen, nheads, headdim), g, device).to(bf) if gate else None
+    A = -4.0 * torch.arange(1, nheads + 1, dtype=torch.float32, device=device) / nheads
+    Dskip = _randn((nheads,), g, device) if skip else None
+    hinit = _randn((batch, nheads, headdim, dstate), g, device) if h0 else None
+    return dict(x=x, delta=delta, A=A, Bm=Bm, Cm=Cm, Dskip=Dskip, z=z, h0=hinit)
+
+
+def make_ssd_config_inputs(cfg: SsdConfig, device="cpu", **overrides):
+    kw = dict(batch=cfg.batch, seqlen=cfg.seqlen, nheads=cfg.nheads, headdim=cfg.headdim,
+              ngroups=cfg.ngroups, dstate=cfg.dstate, seed=cfg.seed)
+    kw.update(overrides)
+    return make_ssd_inputs(device=device, **kw)

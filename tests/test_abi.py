@@ -65,6 +65,7 @@ int main(void) {
   printf("ssm_scan_bwd_args_t size %zu\n", sizeof(ssm_scan_bwd_args_t));
   printf("ssm_block_dims_t size %zu\n", sizeof(ssm_block_dims_t));
   printf("ssm_block_weights_t size %zu\n", sizeof(ssm_block_weights_t));
+  printf("ssm_ssd_args_t size %zu\n", sizeof(ssm_ssd_args_t));
   %FIELDS%
   return 0;
 }
@@ -73,7 +74,7 @@ int main(void) {
 
 STRUCTS = (("ssm_scan_args_t", ssm.ScanArgs), ("ssm_state_update_args_t", ssm.StateUpdateArgs),
            ("ssm_scan_bwd_args_t", ssm.ScanBwdArgs), ("ssm_block_dims_t", ssm.BlockDims),
-           ("ssm_block_weights_t", ssm.BlockWeights))
+           ("ssm_block_weights_t", ssm.BlockWeights), ("ssm_ssd_args_t", ssm.SsdArgs))
 
 
 def test_ctypes_structs_match_c_layout():
@@ -405,3 +406,46 @@ def test_block_null_arguments_and_no_device():
         L.ssm_block_plan_destroy(h)
     else:
         assert not h.value
+
+
+# ----------------------------------------------------------------- SSD checks
+def ssd_args(**kw):
+    a = ssm.SsdArgs(batch=2, seqlen=64, nheads=4, headdim=64, ngroups=1, dstate=128,
+                    io_dtype=ssm.SSM_BF16, delta_softplus=0, x=addr(0), delta=addr(1), A=addr(2),
+                    Bm=addr(3), Cm=addr(4), Dskip=addr(5), z=addr(6), delta_bias=None, h0=None,
+                    y=addr(7), h_final=addr(8))
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def run_ssd(a):
+    return ssm.lib().ssm_ssd_fwd(ctypes.byref(a), None)
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("io_dtype", 5, ssm.SSM_ERR_BAD_DTYPE),
+    ("io_dtype", ssm.SSM_F32, ssm.SSM_ERR_UNSUPPORTED),   # bf16 only in this version
+    ("batch", -1, ssm.SSM_ERR_BAD_SHAPE),
+    ("nheads", 0, ssm.SSM_ERR_BAD_SHAPE),
+    ("ngroups", 3, ssm.SSM_ERR_BAD_SHAPE),                 # does not divide 4 heads
+    ("headdim", 32, ssm.SSM_ERR_UNSUPPORTED),
+    ("dstate", 100, ssm.SSM_ERR_UNSUPPORTED),
+    ("dstate", 256, ssm.SSM_ERR_UNSUPPORTED),
+    ("delta_softplus", 3, ssm.SSM_ERR_UNSUPPORTED),
+    ("x", None, ssm.SSM_ERR_NULL_ARG),
+    ("A", None, ssm.SSM_ERR_NULL_ARG),
+    ("y", None, ssm.SSM_ERR_NULL_ARG),
+    ("x", addr(0, 8), ssm.SSM_ERR_ALIGN),                  # needs 16 bytes
+    ("delta", addr(1, 1), ssm.SSM_ERR_ALIGN),
+    ("y", addr(0, 256), ssm.SSM_ERR_ALIAS),                # inside x
+    ("h_final", addr(7), ssm.SSM_ERR_ALIAS),               # == y
+])
+def test_ssd_rejects_bad_arguments(field, value, status):
+    assert run_ssd(ssd_args(**{field: value})) == status
+
+
+def test_ssd_empty_batch_is_a_noop():
+    assert run_ssd(ssd_args(batch=0)) == ssm.SSM_OK
+    assert run_ssd(ssd_args(batch=0, seqlen=0)) == ssm.SSM_OK
+    assert ssm.lib().ssm_ssd_fwd(None, None) == ssm.SSM_ERR_NULL_ARG
