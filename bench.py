@@ -266,6 +266,54 @@ def cpu_baseline(inp, cfg):
                                                                   cfg.dstate, nthreads))
 
 
+def ssd_algorithmic(cfg, chunk=64):
+    """HBM bytes and matrix FLOPs of one SSD layer call.  Bytes: x, z read and y written
+    (bf16, B*L*H*P each), delta (B*L*H) and B, C (B*L*G*N each) read, h_final written (fp32).
+    FLOPs of the chunked algorithm (2 per multiply-add), per (batch, head, chunk of Q): the
+    causal half of C.B^T (Q(Q+1)/2 * N), its product with X (Q(Q+1)/2 * P), C H^T (Q N P) and
+    the state update B^T X (Q N P)."""
+    B, L, H, P, G, N = cfg.batch, cfg.seqlen, cfg.nheads, cfg.headdim, cfg.ngroups, cfg.dstate
+    nbytes = 3 * 2 * B * L * H * P + 2 * B * L * H + 2 * 2 * B * L * G * N + 4 * B * H * P * N
+    Q = chunk
+    per_chunk = 2 * (Q * (Q + 1) // 2 * (N + P) + 2 * Q * N * P)
+    flops = per_chunk * B * H * ((L + Q - 1) // Q)
+    return nbytes, flops
+
+
+def bench_ssd(cfg, steps, warmup):
+    """The SSD (Mamba-2) layer of `cfg` on one seeded input set, with its final state."""
+    import torch
+    import selective_state_space_59_amd as ssm
+    from selective_state_space_59_amd import workloads as W
+    dev = "cuda:0"
+    s = W.make_ssd_config_inputs(cfg, device=dev)
+    y = torch.empty_like(s["x"])
+    hf = torch.empty(cfg.batch, cfg.nheads, cfg.headdim, cfg.dstate, device=dev)
+
+    def run(_):
+        ssm.ssd_fwd(s["x"], s["delta"], s["A"], s["Bm"], s["Cm"], Dskip=s["Dskip"], z=s["z"],
+                    y=y, h_final=hf)
+
+    ms = time_launches(run, steps, warmup)
+    del s, y, hf
+    torch.cuda.empty_cache()
+    return ms
+
+
+def ssd_entry(cfg, steps, warmup):
+    ms = bench_ssd(cfg, steps, warmup)
+    nbytes, flops = ssd_algorithmic(cfg)
+    tokens = cfg.batch * cfg.seqlen
+    return dict(ms=round(ms, 4), tokens_per_s=round(tokens / (ms * 1e-3), 1),
+                gbs=round(nbytes / (ms * 1e-3) / 1e9, 2),
+                frac_hbm=round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                algorithmic_bytes=nbytes, chunked_flops=flops,
+                tflops=round(flops / (ms * 1e-3) / 1e12, 2),
+                config=dict(batch=cfg.batch, seq_len=cfg.seqlen, nheads=cfg.nheads,
+                            headdim=cfg.headdim, ngroups=cfg.ngroups, dstate=cfg.dstate,
+                            io_dtype="bf16", chunk=64))
+
+
 def block_entry(cfg, steps, warmup):
     ms = bench_block(cfg, steps, warmup)
     fl = block_gemm_flops(cfg)
@@ -284,8 +332,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--no-extras", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--block-only", action="store_true",
-                    help="only time the 130M-like Mamba block forward and print its numbers")
+    ap.add_argument("--only", choices=("block", "ssd"),
+                    help="only time the 130M-like Mamba block forward, or the Mamba-2 130M-like "
+                         "SSD layer, and print its numbers")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (fp32) five times; its "
                          "FETCH_SIZE / WRITE_SIZE counters scale the scan's traffic counters")
@@ -311,8 +360,12 @@ def main():
         print(json.dumps({"copy_bytes_read": 4 * n, "copy_bytes_written": 4 * n, "launches": 5}))
         return
 
-    if args.block_only:
+    if args.only == "block":
         print(json.dumps({W.B2_130M.name: block_entry(W.B2_130M, args.steps, args.warmup)}), flush=True)
+        return
+    if args.only == "ssd":
+        print(json.dumps({W.S2_MAMBA2_130M.name: ssd_entry(W.S2_MAMBA2_130M, args.steps, args.warmup)}),
+              flush=True)
         return
 
     cfg = W.C2_130M
@@ -389,6 +442,9 @@ def main():
         # the whole Mamba block around the scan (RMSNorm, projections, conv, scan, residual)
         print("bench extra: %s" % W.B2_130M.name, file=sys.stderr, flush=True)
         extra[W.B2_130M.name] = block_entry(W.B2_130M, 30, 5)
+        # the SSD (Mamba-2) layer at the 130M-like width with N = 128
+        print("bench extra: %s" % W.S2_MAMBA2_130M.name, file=sys.stderr, flush=True)
+        extra[W.S2_MAMBA2_130M.name] = ssd_entry(W.S2_MAMBA2_130M, 30, 5)
         out["extra"] = extra
 
     if not args.no_cpu_baseline:

@@ -16,21 +16,27 @@
 //         + Dskip x_t,  then x silu(z_t)
 //   H    <- e^{acum[end]} H + sum_s e^{acum[end]-acum[s]} w_s x_s B_s^T
 //
-// One workgroup of 4 waves owns one (batch, head) and walks its chunks in
-// order.  Every product is a 16x16x16 bf16 MFMA with fp32 accumulation:
-//   G^T tiles  B_s . C_t   (A = B rows, B = C rows): the result layout is
-//              exactly the A operand of the next product, so the masked,
-//              scaled tile M goes to LDS only because other waves read it;
-//   Y          C H^T + M X (each wave owns 16 of the 64 head channels);
-//   state      B^T (w' X) (same 16 channels; the fp32 state stays in the
-//              accumulators across chunks, a copy in LDS feeds C H^T).
+// One workgroup of 4 waves owns one (batch, head, 32 head channels) and walks
+// that head's chunks in order; the two channel halves of a head run as two
+// workgroups (they share B and C through the L2).  Every product is a
+// 16x16x16 bf16 MFMA with fp32 accumulation.  Wave w owns the 16 steps
+// t in [16 w, 16 w + 16) of each chunk for the outputs and the state entries
+// n in [32 w, 32 w + 32) (N = 128; N / 4 in general) for the state:
+//   G^T tiles  B_s . C_t for s <= t (A = B rows, B = C rows): the result
+//              layout is exactly the A operand of the next product, so the
+//              causally masked, decayed tile M never leaves the registers;
+//   Y          C H^T + M X;
+//   state      B^T (w' X); the fp32 state stays in the accumulators across
+//              chunks, a copy in LDS feeds C H^T (read before the
+//              workgroup's middle barrier, rewritten after it).
 // x, B and C are bf16 inputs and exact as operands.  The computed operands
 // (M, w' X and the state copy) enter as a sum of two bf16 numbers, hi + lo
 // with lo = bf16(v - hi), and each such product is two MFMAs: about 16
 // significant bits, where a single bf16 rounding (8 bits) would leave errors
 // of order 1% in sums that cancel (C.h is a sum of N terms of either sign).
-// The state tiles, the outputs and the chunk's inputs never leave the CU
-// except as the layer's own inputs and outputs.
+// The chunk's inputs for the next chunk are loaded into registers while this
+// one is computed.  About 71 KB of LDS per workgroup (N = 128): two
+// workgroups share a CU.
 #include "ssm_device.h"
 #include "ssm_internal.h"
 
@@ -38,7 +44,9 @@ namespace ssm {
 namespace {
 
 constexpr int kQ = 64;     // chunk length (4 tiles of 16)
-constexpr int kP = 64;     // head channels (one 16-wide tile per wave)
+constexpr int kP = 64;     // head channels
+constexpr int kPT = 32;    // head channels per workgroup
+constexpr int kPTL = kPT / 16;  // MFMA column tiles per workgroup
 constexpr int kPadE = 8;   // row padding, bf16 elements (16 bytes)
 constexpr int kThreads = 256;
 
@@ -47,20 +55,20 @@ typedef float ssd_f4 __attribute__((ext_vector_type(4)));
 
 template <int N>
 struct SsdLds {
-    static constexpr int nld = N + kPadE;   // rows of N entries: Bs, Cs, HT
-    static constexpr int qld = kQ + kPadE;  // rows of kQ entries: BT, XT, XWT, Mb
-    // HT, XWT and Mb hold a hi plane and then a lo plane.
+    static constexpr int nld = N + kPadE;    // rows of N entries: Bs, Cs, HT
+    static constexpr int tld = kPT + kPadE;  // rows of kPT entries: Xs, Zs (Ys)
+    static constexpr int qld = kQ + kPadE;   // rows of kQ entries: XWT
     static constexpr size_t bs = 0;
     static constexpr size_t cs = bs + (size_t)kQ * nld * 2;
-    static constexpr size_t ht = cs + (size_t)kQ * nld * 2;
-    static constexpr size_t ht_lo = (size_t)kP * nld;  // elements to the lo plane
-    static constexpr size_t bt = ht + 2 * (size_t)kP * nld * 2;
-    static constexpr size_t xt = bt + (size_t)N * qld * 2;
-    static constexpr size_t xwt = xt + (size_t)kP * qld * 2;
-    static_assert(kQ == kP, "XWT (kP rows) and Mb (kQ rows) share one lo-plane offset");
-    static constexpr size_t q_lo = (size_t)kQ * qld;    // elements to the lo plane (XWT, Mb)
-    static constexpr size_t mb = xwt + 2 * (size_t)kP * qld * 2;
-    static constexpr size_t dts = mb + 2 * (size_t)kQ * qld * 2;
+    static constexpr size_t xs = cs + (size_t)kQ * nld * 2;
+    static constexpr size_t zs = xs + (size_t)kQ * tld * 2;
+    // HT: [hi/lo plane][kPT channels][nld]
+    static constexpr size_t ht = zs + (size_t)kQ * tld * 2;
+    static constexpr size_t ht_plane = (size_t)kPT * nld;  // elements
+    // XWT: [hi/lo plane][kPT channels][qld]
+    static constexpr size_t xwt = ht + 2 * ht_plane * 2;
+    static constexpr size_t xwt_plane = (size_t)kPT * qld;
+    static constexpr size_t dts = xwt + 2 * xwt_plane * 2;
     static constexpr size_t total = dts + (size_t)kQ * sizeof(float);
 };
 
@@ -107,95 +115,143 @@ __device__ __forceinline__ ssd_s4 lds4(const uint16_t *p) {
     return __builtin_bit_cast(ssd_s4, *reinterpret_cast<const uint2 *>(p));
 }
 
-// (tile of t, tile of s) pairs of the causal lower triangle of a chunk
-__constant__ int8_t kPairT[10] = {0, 1, 1, 2, 2, 2, 3, 3, 3, 3};
-__constant__ int8_t kPairS[10] = {0, 0, 1, 0, 1, 2, 0, 1, 2, 3};
+// Four bf16 entries of one column of a row-major LDS array (rows r .. r+3),
+// as an MFMA operand whose k index runs down the column.
+__device__ __forceinline__ ssd_s4 col4(const uint16_t *p, int ld) {
+    return ssd_s4{(short)p[0], (short)p[ld], (short)p[2 * ld], (short)p[3 * ld]};
+}
+
+// The chunk's inputs in registers between their global load and their LDS
+// store, so that the next chunk's loads are in flight during this chunk's
+// products.  Each thread owns KB 16-byte pieces of B and of C, and one
+// 16-byte piece each of x and z.
+template <int N>
+struct ChunkRegs {
+    static constexpr int PR = N / 8;  // pieces per B/C row
+    static constexpr int KB = (kQ * PR + kThreads - 1) / kThreads;
+    uint4 b[KB], c[KB], x, z;
+    float dt;
+};
 
 template <int N>
-__global__ __launch_bounds__(kThreads) void ssd_chunk_kernel(SsdParams p) {
+__device__ __forceinline__ void fetch_chunk(const SsdParams &p, int64_t b, int64_t h, int64_t g, int pt,
+                                            int64_t t0, float dbias, int tid, ChunkRegs<N> &r) {
+    using R = ChunkRegs<N>;
+    const int64_t L = p.L;
+#pragma unroll
+    for (int k = 0; k < R::KB; ++k) {
+        const int id = tid + k * kThreads;
+        const int s = id / R::PR, c8 = (id % R::PR) * 8;
+        const int64_t t = t0 + s;
+        r.b[k] = make_uint4(0, 0, 0, 0);
+        r.c[k] = r.b[k];
+        if (id < kQ * R::PR && t < L) {
+            const int64_t off = ((b * L + t) * p.G + g) * N + c8;
+            r.b[k] = *reinterpret_cast<const uint4 *>(p.Bm + off);
+            r.c[k] = *reinterpret_cast<const uint4 *>(p.Cm + off);
+        }
+    }
+    {
+        static_assert(kQ * (kPT / 8) == kThreads, "one x and one z piece per thread");
+        const int s = tid / (kPT / 8), c8 = (tid % (kPT / 8)) * 8;
+        const int64_t t = t0 + s;
+        r.x = make_uint4(0, 0, 0, 0);
+        r.z = r.x;
+        if (t < L) {
+            const int64_t off = ((b * L + t) * p.H + h) * kP + kPT * pt + c8;
+            r.x = *reinterpret_cast<const uint4 *>(p.x + off);
+            if (p.z) r.z = *reinterpret_cast<const uint4 *>(p.z + off);
+        }
+    }
+    r.dt = 0.0f;
+    if (tid < kQ && t0 + tid < L) {
+        float dt = bf(p.delta[(b * L + t0 + tid) * p.H + h]);
+        if (p.softplus) dt = softplus_fast(dt + dbias);
+        r.dt = dt;
+    }
+}
+
+template <int N>
+__device__ __forceinline__ void store_chunk(const ChunkRegs<N> &r, uint16_t *Bs, uint16_t *Cs, uint16_t *Xs,
+                                            uint16_t *Zs, float *dts, int tid) {
+    using R = ChunkRegs<N>;
     using Lay = SsdLds<N>;
-    constexpr int NT = N / 16;
-    constexpr int nld = Lay::nld, qld = Lay::qld;
+#pragma unroll
+    for (int k = 0; k < R::KB; ++k) {
+        const int id = tid + k * kThreads;
+        if (id < kQ * R::PR) {
+            const int s = id / R::PR, c8 = (id % R::PR) * 8;
+            *reinterpret_cast<uint4 *>(Bs + s * Lay::nld + c8) = r.b[k];
+            *reinterpret_cast<uint4 *>(Cs + s * Lay::nld + c8) = r.c[k];
+        }
+    }
+    {
+        const int s = tid / (kPT / 8), c8 = (tid % (kPT / 8)) * 8;
+        *reinterpret_cast<uint4 *>(Xs + s * Lay::tld + c8) = r.x;
+        *reinterpret_cast<uint4 *>(Zs + s * Lay::tld + c8) = r.z;
+    }
+    if (tid < kQ) dts[tid] = r.dt;
+}
+
+template <int N>
+__global__ __launch_bounds__(kThreads, 2) void ssd_chunk_kernel(SsdParams p) {
+    using Lay = SsdLds<N>;
+    constexpr int NT = N / 16;       // state tiles of the head
+    constexpr int NW = NT / 4;       // state tiles per wave (N >= 64); see below for N < 64
+    constexpr int NWT = NW > 0 ? NW : 1;
+    constexpr int nld = Lay::nld, tld = Lay::tld, qld = Lay::qld;
     extern __shared__ __attribute__((aligned(16))) char lds[];
     uint16_t *Bs = reinterpret_cast<uint16_t *>(lds + Lay::bs);
     uint16_t *Cs = reinterpret_cast<uint16_t *>(lds + Lay::cs);
+    uint16_t *Xs = reinterpret_cast<uint16_t *>(lds + Lay::xs);
+    uint16_t *Zs = reinterpret_cast<uint16_t *>(lds + Lay::zs);
     uint16_t *HT = reinterpret_cast<uint16_t *>(lds + Lay::ht);
-    uint16_t *BT = reinterpret_cast<uint16_t *>(lds + Lay::bt);
-    uint16_t *XT = reinterpret_cast<uint16_t *>(lds + Lay::xt);
     uint16_t *XWT = reinterpret_cast<uint16_t *>(lds + Lay::xwt);
-    uint16_t *Mb = reinterpret_cast<uint16_t *>(lds + Lay::mb);
     float *dts = reinterpret_cast<float *>(lds + Lay::dts);
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int r16 = lane & 15, q4 = 4 * (lane >> 4);
-    const int64_t bh = blockIdx.x;
+    const int64_t bhp = blockIdx.x;
+    const int pt = (int)(bhp % (kP / kPT));
+    const int64_t bh = bhp / (kP / kPT);
     const int64_t b = bh / p.H, h = bh % p.H;
     const int64_t g = h / (p.H / p.G);
     const int64_t L = p.L;
     const float a = p.A[h];
     const float dsk = p.Dskip ? p.Dskip[h] : 0.0f;
     const float dbias = p.dbias ? p.dbias[h] : 0.0f;
-    const int pcol = 16 * w + r16;  // this lane's head channel in the wave's tile
+    const int tb = w;  // this wave's 16-step row tile
+    // column tile j: this lane's head channel kPT pt + 16 j + r16 (local 16 j + r16)
 
-    // State tiles of this wave's channels: st[nt][v] is entry n = 16 nt + q4 + v
-    // of channel pcol.
-    ssd_f4 st[NT];
+    // State tiles of this wave: st[i][j][v] is entry n = 16 nt + q4 + v of
+    // local channel 16 j + r16, nt = NW w + i.  (N < 64: waves beyond NT hold
+    // nothing.)
+    ssd_f4 st[NWT][kPTL];
+    auto my_nt = [&](int i) { return NW > 0 ? NW * w + i : w; };
+    const bool owns_state = NW > 0 || w < NT;
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-        float v4[4];
+    for (int i = 0; i < NWT; ++i)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            st[nt][v] = p.h0 ? p.h0[(bh * kP + pcol) * N + 16 * nt + q4 + v] : 0.0f;
-            v4[v] = st[nt][v];
+        for (int j = 0; j < kPTL; ++j) {
+            const int nt = my_nt(i), pl = 16 * j + r16;
+            float v4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+            if (owns_state && p.h0) {
+#pragma unroll
+                for (int v = 0; v < 4; ++v) v4[v] = p.h0[(bh * kP + kPT * pt + pl) * N + 16 * nt + q4 + v];
+            }
+            st[i][j] = ssd_f4{v4[0], v4[1], v4[2], v4[3]};
+            if (owns_state) store_split4(HT + pl * nld + 16 * nt + q4, Lay::ht_plane, v4);
         }
-        store_split4(HT + pcol * nld + 16 * nt + q4, Lay::ht_lo, v4);
-    }
 
     const int64_t nchunks = (L + kQ - 1) / kQ;
+    ChunkRegs<N> regs;
+    if (nchunks > 0) fetch_chunk<N>(p, b, h, g, pt, 0, dbias, tid, regs);
     for (int64_t c = 0; c < nchunks; ++c) {
         const int64_t t0 = c * kQ;
-        // ---- the chunk's inputs into LDS ------------------------------------
-        constexpr int PR = N / 8;  // 16-byte pieces per B/C row
-        for (int id = tid; id < kQ * PR; id += kThreads) {
-            const int s = id / PR, c8 = (id % PR) * 8;
-            const int64_t t = t0 + s;
-            uint4 vb = make_uint4(0, 0, 0, 0), vc = vb;
-            if (t < L) {
-                const int64_t off = ((b * L + t) * p.G + g) * N + c8;
-                vb = *reinterpret_cast<const uint4 *>(p.Bm + off);
-                vc = *reinterpret_cast<const uint4 *>(p.Cm + off);
-            }
-            *reinterpret_cast<uint4 *>(Bs + s * nld + c8) = vb;
-            *reinterpret_cast<uint4 *>(Cs + s * nld + c8) = vc;
-            const uint32_t wb[4] = {vb.x, vb.y, vb.z, vb.w};
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                BT[(c8 + 2 * i) * qld + s] = (uint16_t)(wb[i] & 0xffffu);
-                BT[(c8 + 2 * i + 1) * qld + s] = (uint16_t)(wb[i] >> 16);
-            }
-        }
-        for (int id = tid; id < kQ * (kP / 8); id += kThreads) {
-            const int s = id / (kP / 8), c8 = (id % (kP / 8)) * 8;
-            const int64_t t = t0 + s;
-            uint4 vx = make_uint4(0, 0, 0, 0);
-            if (t < L) vx = *reinterpret_cast<const uint4 *>(p.x + ((b * L + t) * p.H + h) * kP + c8);
-            const uint32_t wx[4] = {vx.x, vx.y, vx.z, vx.w};
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                XT[(c8 + 2 * i) * qld + s] = (uint16_t)(wx[i] & 0xffffu);
-                XT[(c8 + 2 * i + 1) * qld + s] = (uint16_t)(wx[i] >> 16);
-            }
-        }
-        if (tid < kQ) {
-            const int64_t t = t0 + tid;
-            float dt = 0.0f;
-            if (t < L) {
-                dt = bf(p.delta[(b * L + t) * p.H + h]);
-                if (p.softplus) dt = softplus_fast(dt + dbias);
-            }
-            dts[tid] = dt;
-        }
+        store_chunk<N>(regs, Bs, Cs, Xs, Zs, dts, tid);
         __syncthreads();
+        // the next chunk's loads fly while this chunk is computed
+        if (c + 1 < nchunks) fetch_chunk<N>(p, b, h, g, pt, t0 + kQ, dbias, tid, regs);
 
         // ---- chunk scalars, one copy per wave (lane = step s) ----------------
         const float dtl = dts[lane];
@@ -210,98 +266,155 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_kernel(SsdParams p) {
         const float wl = dtl * ssd_phi(zl, hw_exp2(zl * kLog2e));       // ZOH input weight
         const float fl = hw_exp2((aend - acum) * kLog2e) * wl;         // weight in the end state
 
-        // ---- masked, scaled G^T tiles -> Mb[t][s]; X' = f x -> XWT ----------
-        for (int pi = w; pi < 10; pi += 4) {
-            const int tb = kPairT[pi], sb = kPairS[pi];
-            ssd_f4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+        // ---- X' = f x -> XWT[p][s] (hi, lo): wave w writes kPT / 4 channels ----
 #pragma unroll
-            for (int kk = 0; kk < NT; ++kk)
-                acc = SSD_MFMA(lds4(Bs + (16 * sb + r16) * nld + 16 * kk + q4),
-                               lds4(Cs + (16 * tb + r16) * nld + 16 * kk + q4), acc);
-            // lane holds s = 16 sb + q4 + v, t = 16 tb + r16
-            const int t = 16 * tb + r16;
-            const float at = __shfl(acum, t, 64);
-            float m[4];
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const int s = 16 * sb + q4 + v;
-                const float as = __shfl(acum, s, 64), ws = __shfl(wl, s, 64);
-                m[v] = s <= t ? acc[v] * hw_exp2((at - as) * kLog2e) * ws : 0.0f;
-            }
-            store_split4(Mb + t * qld + 16 * sb + q4, Lay::q_lo, m);
-        }
-#pragma unroll 4
-        for (int i = 0; i < 16; ++i) {
-            const int pp = 16 * w + i;
-            const float v = bf(XT[pp * qld + lane]) * fl;
+        for (int i = 0; i < kPT / 4; ++i) {
+            const int pp = (kPT / 4) * w + i;
+            const float v = bf(Xs[lane * tld + pp]) * fl;
             const uint16_t hi = f32_to_bf16_bits(v);
             XWT[pp * qld + lane] = hi;
-            XWT[Lay::q_lo + pp * qld + lane] = f32_to_bf16_bits(v - bf(hi));
+            XWT[Lay::xwt_plane + pp * qld + lane] = f32_to_bf16_bits(v - bf(hi));
         }
-        __syncthreads();
 
-        // ---- outputs of this wave's 16 channels --------------------------------
-        for (int tb = 0; tb < kQ / 16; ++tb) {
-            ssd_f4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+        // ---- this wave's G^T tiles, masked and decayed in place ---------------------
+        // All four s tiles are formed (those above the diagonal are masked to 0
+        // below): straight-line code lets the operand loads run ahead of the
+        // MFMAs, and every wave does the same work.
+        ssd_f4 gacc[kQ / 16];
+#pragma unroll
+        for (int sb = 0; sb < kQ / 16; ++sb) gacc[sb] = ssd_f4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int kk = 0; kk < NT; ++kk) {
+            const ssd_s4 cop = lds4(Cs + (16 * tb + r16) * nld + 16 * kk + q4);
+#pragma unroll
+            for (int sb = 0; sb < kQ / 16; ++sb)
+                gacc[sb] = SSD_MFMA(lds4(Bs + (16 * sb + r16) * nld + 16 * kk + q4), cop, gacc[sb]);
+        }
+        // lane holds s = 16 sb + q4 + v, t = 16 tb + r16: M[t][s], the A operand
+        // (row t, k = s) of M X as it stands
+        ssd_s4 mhi[kQ / 16], mlo[kQ / 16];
+        {
+            const float at = __shfl(acum, 16 * tb + r16, 64);
+#pragma unroll
+            for (int sb = 0; sb < kQ / 16; ++sb) {
+                float m[4];
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const int s = 16 * sb + q4 + v;
+                    const float as = __shfl(acum, s, 64), ws = __shfl(wl, s, 64);
+                    m[v] = (sb <= tb && s <= 16 * tb + r16) ? gacc[sb][v] * hw_exp2((at - as) * kLog2e) * ws : 0.0f;
+                }
+                uint2 hi, lo;
+                split4(m, hi, lo);
+                mhi[sb] = __builtin_bit_cast(ssd_s4, hi);
+                mlo[sb] = __builtin_bit_cast(ssd_s4, lo);
+            }
+        }
+
+        // ---- Y for this wave's 16 steps and the workgroup's channels --------------
+        {
+            ssd_f4 acc[kPTL], acc2[kPTL];
+#pragma unroll
+            for (int j = 0; j < kPTL; ++j) acc[j] = acc2[j] = ssd_f4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
             for (int kk = 0; kk < NT; ++kk) {
                 const ssd_s4 cop = lds4(Cs + (16 * tb + r16) * nld + 16 * kk + q4);
-                const uint16_t *hp = HT + pcol * nld + 16 * kk + q4;
-                acc = SSD_MFMA(cop, lds4(hp), acc);
-                acc = SSD_MFMA(cop, lds4(hp + Lay::ht_lo), acc);
-            }
-            // lane holds t = 16 tb + q4 + v, channel pcol
 #pragma unroll
-            for (int v = 0; v < 4; ++v) acc[v] *= hw_exp2(__shfl(acum, 16 * tb + q4 + v, 64) * kLog2e);
-            for (int sb = 0; sb <= tb; ++sb) {
-                const uint16_t *mp = Mb + (16 * tb + r16) * qld + 16 * sb + q4;
-                const ssd_s4 xop = lds4(XT + pcol * qld + 16 * sb + q4);
-                acc = SSD_MFMA(lds4(mp), xop, acc);
-                acc = SSD_MFMA(lds4(mp + Lay::q_lo), xop, acc);
-            }
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const int t = 16 * tb + q4 + v;
-                const int64_t tt = t0 + t;
-                if (tt < L) {
-                    const int64_t i = ((b * L + tt) * p.H + h) * kP + pcol;
-                    float yv = acc[v] + dsk * bf(XT[pcol * qld + t]);
-                    if (p.z) yv *= silu(bf(p.z[i]));
-                    p.y[i] = f32_to_bf16_bits(yv);
+                for (int j = 0; j < kPTL; ++j) {
+                    const uint16_t *hp = HT + (16 * j + r16) * nld + 16 * kk + q4;
+                    acc[j] = SSD_MFMA(cop, lds4(hp), acc[j]);
+                    acc2[j] = SSD_MFMA(cop, lds4(hp + Lay::ht_plane), acc2[j]);
                 }
             }
+            // lane holds t = 16 tb + q4 + v, local channel 16 j + r16
+            float dec[4];
+#pragma unroll
+            for (int v = 0; v < 4; ++v) dec[v] = hw_exp2(__shfl(acum, 16 * tb + q4 + v, 64) * kLog2e);
+#pragma unroll
+            for (int j = 0; j < kPTL; ++j) {
+                acc[j] += acc2[j];
+#pragma unroll
+                for (int v = 0; v < 4; ++v) acc[j][v] *= dec[v];
+            }
+#pragma unroll
+            for (int sb = 0; sb < kQ / 16; ++sb) {  // tiles above the diagonal are 0
+#pragma unroll
+                for (int j = 0; j < kPTL; ++j) {
+                    const ssd_s4 xop = col4(Xs + (16 * sb + q4) * tld + 16 * j + r16, tld);
+                    acc[j] = SSD_MFMA(mhi[sb], xop, acc[j]);
+                    acc[j] = SSD_MFMA(mlo[sb], xop, acc[j]);
+                }
+            }
+            // skip and gate; the result replaces the gate entry it used
+#pragma unroll
+            for (int j = 0; j < kPTL; ++j)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const int t = 16 * tb + q4 + v, pl = 16 * j + r16;
+                    float yv = acc[j][v] + dsk * bf(Xs[t * tld + pl]);
+                    if (p.z) yv *= silu(bf(Zs[t * tld + pl]));
+                    Zs[t * tld + pl] = f32_to_bf16_bits(yv);
+                }
+        }
+        __syncthreads();  // XWT and Ys (in Zs) complete; every read of HT done
+
+        // ---- outputs leave as 16-byte pieces, one per thread --------------------
+        {
+            const int t = tid / (kPT / 8), c8 = (tid % (kPT / 8)) * 8;
+            const int64_t tt = t0 + t;
+            if (tt < L)
+                *reinterpret_cast<uint4 *>(p.y + ((b * L + tt) * p.H + h) * kP + kPT * pt + c8) =
+                    *reinterpret_cast<const uint4 *>(Zs + t * tld + c8);
         }
 
-        // ---- the state entering the next chunk ---------------------------------
-        const float dend = hw_exp2(aend * kLog2e);
+        // ---- this wave's state tiles for the next chunk ----------------------------
+        if (owns_state) {
+            const float dend = hw_exp2(aend * kLog2e);
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-            ssd_f4 s4v = st[nt] * dend;
+            for (int i = 0; i < NWT; ++i)
+#pragma unroll
+                for (int j = 0; j < kPTL; ++j) st[i][j] *= dend;
 #pragma unroll
             for (int kk = 0; kk < kQ / 16; ++kk) {
-                const ssd_s4 bop = lds4(BT + (16 * nt + r16) * qld + 16 * kk + q4);
-                const uint16_t *xp = XWT + pcol * qld + 16 * kk + q4;
-                s4v = SSD_MFMA(bop, lds4(xp), s4v);
-                s4v = SSD_MFMA(bop, lds4(xp + Lay::q_lo), s4v);
+                ssd_s4 bop[NWT];
+#pragma unroll
+                for (int i = 0; i < NWT; ++i) bop[i] = col4(Bs + (16 * kk + q4) * nld + 16 * my_nt(i) + r16, nld);
+#pragma unroll
+                for (int j = 0; j < kPTL; ++j) {
+                    const uint16_t *xp = XWT + (16 * j + r16) * qld + 16 * kk + q4;
+                    const ssd_s4 xhi = lds4(xp), xlo = lds4(xp + Lay::xwt_plane);
+#pragma unroll
+                    for (int i = 0; i < NWT; ++i) {
+                        st[i][j] = SSD_MFMA(bop[i], xhi, st[i][j]);
+                        st[i][j] = SSD_MFMA(bop[i], xlo, st[i][j]);
+                    }
+                }
             }
-            st[nt] = s4v;
-            const float v4[4] = {s4v[0], s4v[1], s4v[2], s4v[3]};
-            store_split4(HT + pcol * nld + 16 * nt + q4, Lay::ht_lo, v4);
+#pragma unroll
+            for (int i = 0; i < NWT; ++i)
+#pragma unroll
+                for (int j = 0; j < kPTL; ++j) {
+                    const float v4[4] = {st[i][j][0], st[i][j][1], st[i][j][2], st[i][j][3]};
+                    store_split4(HT + (16 * j + r16) * nld + 16 * my_nt(i) + q4, Lay::ht_plane, v4);
+                }
         }
-        __syncthreads();
+        __syncthreads();  // inputs free for the next chunk; HT holds the new state
     }
 
-    if (p.h_final) {
+    if (p.h_final && owns_state) {
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
+        for (int i = 0; i < NWT; ++i)
 #pragma unroll
-            for (int v = 0; v < 4; ++v) p.h_final[(bh * kP + pcol) * N + 16 * nt + q4 + v] = st[nt][v];
+            for (int j = 0; j < kPTL; ++j)
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    p.h_final[(bh * kP + kPT * pt + 16 * j + r16) * N + 16 * my_nt(i) + q4 + v] = st[i][j][v];
     }
 }
 
 template <int N>
 hipError_t launch_n(const SsdParams &p, int64_t B, int64_t H, hipStream_t stream) {
-    ssd_chunk_kernel<N><<<(unsigned)(B * H), kThreads, SsdLds<N>::total, stream>>>(p);
+    ssd_chunk_kernel<N><<<(unsigned)(B * H * (kP / kPT)), kThreads, SsdLds<N>::total, stream>>>(p);
     return hipGetLastError();
 }
 
