@@ -69,7 +69,9 @@ struct SsdLds {
     static constexpr size_t xwt = ht + 2 * ht_plane * 2;
     static constexpr size_t xwt_plane = (size_t)kPT * qld;
     static constexpr size_t dts = xwt + 2 * xwt_plane * 2;
-    static constexpr size_t total = dts + (size_t)kQ * sizeof(float);
+    // per wave: the chunk's prefix sums of dt a, then its ZOH weights (lane = step)
+    static constexpr size_t scal = dts + (size_t)kQ * sizeof(float);
+    static constexpr size_t total = scal + (size_t)4 * 2 * kQ * sizeof(float);
 };
 
 struct SsdParams {
@@ -210,6 +212,9 @@ __global__ __launch_bounds__(kThreads, 2) void ssd_chunk_kernel(SsdParams p) {
     float *dts = reinterpret_cast<float *>(lds + Lay::dts);
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    // this wave's copy of the chunk scalars (written and read by this wave only)
+    float *acum_s = reinterpret_cast<float *>(lds + Lay::scal) + 2 * kQ * w;
+    float *wl_s = acum_s + kQ;
     const int r16 = lane & 15, q4 = 4 * (lane >> 4);
     const int64_t bhp = blockIdx.x;
     const int pt = (int)(bhp % (kP / kPT));
@@ -265,6 +270,8 @@ __global__ __launch_bounds__(kThreads, 2) void ssd_chunk_kernel(SsdParams p) {
         const float aend = __shfl(acum, 63, 64);
         const float wl = dtl * ssd_phi(zl, hw_exp2(zl * kLog2e));       // ZOH input weight
         const float fl = hw_exp2((aend - acum) * kLog2e) * wl;         // weight in the end state
+        acum_s[lane] = acum;
+        wl_s[lane] = wl;
 
         // ---- X' = f x -> XWT[p][s] (hi, lo): wave w writes kPT / 4 channels ----
 #pragma unroll
@@ -294,15 +301,18 @@ __global__ __launch_bounds__(kThreads, 2) void ssd_chunk_kernel(SsdParams p) {
         // (row t, k = s) of M X as it stands
         ssd_s4 mhi[kQ / 16], mlo[kQ / 16];
         {
-            const float at = __shfl(acum, 16 * tb + r16, 64);
+            const float at = acum_s[16 * tb + r16];
 #pragma unroll
             for (int sb = 0; sb < kQ / 16; ++sb) {
+                const float4 as4 = *reinterpret_cast<const float4 *>(acum_s + 16 * sb + q4);
+                const float4 ws4 = *reinterpret_cast<const float4 *>(wl_s + 16 * sb + q4);
+                const float as[4] = {as4.x, as4.y, as4.z, as4.w}, ws[4] = {ws4.x, ws4.y, ws4.z, ws4.w};
                 float m[4];
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
                     const int s = 16 * sb + q4 + v;
-                    const float as = __shfl(acum, s, 64), ws = __shfl(wl, s, 64);
-                    m[v] = (sb <= tb && s <= 16 * tb + r16) ? gacc[sb][v] * hw_exp2((at - as) * kLog2e) * ws : 0.0f;
+                    m[v] = (sb <= tb && s <= 16 * tb + r16) ? gacc[sb][v] * hw_exp2((at - as[v]) * kLog2e) * ws[v]
+                                                           : 0.0f;
                 }
                 uint2 hi, lo;
                 split4(m, hi, lo);
@@ -328,8 +338,13 @@ __global__ __launch_bounds__(kThreads, 2) void ssd_chunk_kernel(SsdParams p) {
             }
             // lane holds t = 16 tb + q4 + v, local channel 16 j + r16
             float dec[4];
-#pragma unroll
-            for (int v = 0; v < 4; ++v) dec[v] = hw_exp2(__shfl(acum, 16 * tb + q4 + v, 64) * kLog2e);
+            {
+                const float4 a4 = *reinterpret_cast<const float4 *>(acum_s + 16 * tb + q4);
+                dec[0] = hw_exp2(a4.x * kLog2e);
+                dec[1] = hw_exp2(a4.y * kLog2e);
+                dec[2] = hw_exp2(a4.z * kLog2e);
+                dec[3] = hw_exp2(a4.w * kLog2e);
+            }
 #pragma unroll
             for (int j = 0; j < kPTL; ++j) {
                 acc[j] += acc2[j];
