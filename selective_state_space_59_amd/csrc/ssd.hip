@@ -123,6 +123,21 @@ __device__ __forceinline__ ssd_s4 col4(const uint16_t *p, int ld) {
     return ssd_s4{(short)p[0], (short)p[ld], (short)p[2 * ld], (short)p[3 * ld]};
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave: within each row of 16
+// lanes by DPP row shifts (lanes shifted in from outside the row read 0),
+// then the totals of the rows before, read from lanes 15, 31 and 47.
+__device__ __forceinline__ float wave_prefix_sum(float v, int lane) {
+    v += __builtin_amdgcn_update_dpp(0.0f, v, 0x111, 0xf, 0xf, false);  // row_shr:1
+    v += __builtin_amdgcn_update_dpp(0.0f, v, 0x112, 0xf, 0xf, false);  // row_shr:2
+    v += __builtin_amdgcn_update_dpp(0.0f, v, 0x114, 0xf, 0xf, false);  // row_shr:4
+    v += __builtin_amdgcn_update_dpp(0.0f, v, 0x118, 0xf, 0xf, false);  // row_shr:8
+    const float t0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 15));
+    const float t1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 31));
+    const float t2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 47));
+    const int row = lane >> 4;
+    return v + (row >= 1 ? t0 : 0.0f) + (row >= 2 ? t1 : 0.0f) + (row >= 3 ? t2 : 0.0f);
+}
+
 // The chunk's inputs in registers between their global load and their LDS
 // store, so that the next chunk's loads are in flight during this chunk's
 // products.  Each thread owns KB 16-byte pieces of B and of C, and one
@@ -261,13 +276,8 @@ __global__ __launch_bounds__(kThreads, 2) void ssd_chunk_kernel(SsdParams p) {
         // ---- chunk scalars, one copy per wave (lane = step s) ----------------
         const float dtl = dts[lane];
         const float zl = dtl * a;
-        float acum = zl;  // inclusive prefix sum of dt a
-#pragma unroll
-        for (int off = 1; off < 64; off *= 2) {
-            const float v = __shfl_up(acum, off, 64);
-            if (lane >= off) acum += v;
-        }
-        const float aend = __shfl(acum, 63, 64);
+        const float acum = wave_prefix_sum(zl, lane);  // inclusive prefix sum of dt a
+        const float aend = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(acum), 63));
         const float wl = dtl * ssd_phi(zl, hw_exp2(zl * kLog2e));       // ZOH input weight
         const float fl = hw_exp2((aend - acum) * kLog2e) * wl;         // weight in the end state
         acum_s[lane] = acum;
