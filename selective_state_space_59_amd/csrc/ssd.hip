@@ -18,8 +18,9 @@
 //
 // One workgroup of 4 waves owns one (batch, head, 32 head channels) and walks
 // that head's chunks in order; the two channel halves of a head run as two
-// workgroups (they share B and C through the L2).  Every product is a
-// 16x16x16 bf16 MFMA with fp32 accumulation.  Wave w owns the 16 steps
+// workgroups (they share B and C through the L2).  Every product is a bf16
+// MFMA with fp32 accumulation (16x16x32; 16x16x16 for the sums over the
+// state entries when N = 16).  Wave w owns the 16 steps
 // t in [16 w, 16 w + 16) of each chunk for the outputs and the state entries
 // n in [32 w, 32 w + 32) (N = 128; N / 4 in general) for the state:
 //   G^T tiles  B_s . C_t for s <= t (A = B rows, B = C rows): the result
@@ -51,6 +52,7 @@ constexpr int kPadE = 8;   // row padding, bf16 elements (16 bytes)
 constexpr int kThreads = 256;
 
 typedef short ssd_s4 __attribute__((ext_vector_type(4)));
+typedef __bf16 ssd_b8 __attribute__((ext_vector_type(8)));
 typedef float ssd_f4 __attribute__((ext_vector_type(4)));
 
 template <int N>
@@ -112,6 +114,10 @@ __device__ __forceinline__ void store_split4(uint16_t *hi_plane, size_t lo_off, 
 }
 
 #define SSD_MFMA(a, b, c) __builtin_amdgcn_mfma_f32_16x16x16bf16_1k((a), (b), (c), 0, 0, 0)
+// The 16x16x32 form: 8 bf16 of k per lane.  A and B take their k slots from
+// the same (lane group, element) positions, so any assignment of the
+// contracted index to slots that both operands share gives the same sum.
+#define SSD_MFMA32(a, b, c) __builtin_amdgcn_mfma_f32_16x16x32_bf16((a), (b), (c), 0, 0, 0)
 
 __device__ __forceinline__ ssd_s4 lds4(const uint16_t *p) {
     return __builtin_bit_cast(ssd_s4, *reinterpret_cast<const uint2 *>(p));
@@ -122,6 +128,21 @@ __device__ __forceinline__ ssd_s4 lds4(const uint16_t *p) {
 __device__ __forceinline__ ssd_s4 col4(const uint16_t *p, int ld) {
     return ssd_s4{(short)p[0], (short)p[ld], (short)p[2 * ld], (short)p[3 * ld]};
 }
+
+__device__ __forceinline__ ssd_b8 lds8(const uint16_t *p) {
+    return __builtin_bit_cast(ssd_b8, *reinterpret_cast<const uint4 *>(p));
+}
+
+// Two 4-entry operands side by side as one 8-entry operand.
+__device__ __forceinline__ ssd_b8 cat8(ssd_s4 a, ssd_s4 b) {
+    struct Pair {
+        ssd_s4 a, b;
+    } t = {a, b};
+    return __builtin_bit_cast(ssd_b8, t);
+}
+
+// Eight entries of one column (rows r .. r+7).
+__device__ __forceinline__ ssd_b8 col8(const uint16_t *p, int ld) { return cat8(col4(p, ld), col4(p + 4 * ld, ld)); }
 
 // Inclusive prefix sum over the 64 lanes of a wave: within each row of 16
 // lanes by DPP row shifts (lanes shifted in from outside the row read 0),
@@ -300,12 +321,22 @@ __global__ __launch_bounds__(kThreads, 2) void ssd_chunk_kernel(SsdParams p) {
         ssd_f4 gacc[kQ / 16];
 #pragma unroll
         for (int sb = 0; sb < kQ / 16; ++sb) gacc[sb] = ssd_f4{0.0f, 0.0f, 0.0f, 0.0f};
+        if constexpr (N >= 32) {
 #pragma unroll
-        for (int kk = 0; kk < NT; ++kk) {
-            const ssd_s4 cop = lds4(Cs + (16 * tb + r16) * nld + 16 * kk + q4);
+            for (int kk = 0; kk < N / 32; ++kk) {
+                const ssd_b8 cop = lds8(Cs + (16 * tb + r16) * nld + 32 * kk + 2 * q4);
 #pragma unroll
-            for (int sb = 0; sb < kQ / 16; ++sb)
-                gacc[sb] = SSD_MFMA(lds4(Bs + (16 * sb + r16) * nld + 16 * kk + q4), cop, gacc[sb]);
+                for (int sb = 0; sb < kQ / 16; ++sb)
+                    gacc[sb] = SSD_MFMA32(lds8(Bs + (16 * sb + r16) * nld + 32 * kk + 2 * q4), cop, gacc[sb]);
+            }
+        } else {
+#pragma unroll
+            for (int kk = 0; kk < NT; ++kk) {
+                const ssd_s4 cop = lds4(Cs + (16 * tb + r16) * nld + 16 * kk + q4);
+#pragma unroll
+                for (int sb = 0; sb < kQ / 16; ++sb)
+                    gacc[sb] = SSD_MFMA(lds4(Bs + (16 * sb + r16) * nld + 16 * kk + q4), cop, gacc[sb]);
+            }
         }
         // lane holds s = 16 sb + q4 + v, t = 16 tb + r16: M[t][s], the A operand
         // (row t, k = s) of M X as it stands
@@ -314,6 +345,10 @@ __global__ __launch_bounds__(kThreads, 2) void ssd_chunk_kernel(SsdParams p) {
             const float at = acum_s[16 * tb + r16];
 #pragma unroll
             for (int sb = 0; sb < kQ / 16; ++sb) {
+                if (sb > tb) {  // above the diagonal (wave-uniform): all zero
+                    mhi[sb] = mlo[sb] = ssd_s4{0, 0, 0, 0};
+                    continue;
+                }
                 const float4 as4 = *reinterpret_cast<const float4 *>(acum_s + 16 * sb + q4);
                 const float4 ws4 = *reinterpret_cast<const float4 *>(wl_s + 16 * sb + q4);
                 const float as[4] = {as4.x, as4.y, as4.z, as4.w}, ws[4] = {ws4.x, ws4.y, ws4.z, ws4.w};
@@ -321,8 +356,7 @@ __global__ __launch_bounds__(kThreads, 2) void ssd_chunk_kernel(SsdParams p) {
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
                     const int s = 16 * sb + q4 + v;
-                    m[v] = (sb <= tb && s <= 16 * tb + r16) ? gacc[sb][v] * hw_exp2((at - as[v]) * kLog2e) * ws[v]
-                                                           : 0.0f;
+                    m[v] = s <= 16 * tb + r16 ? gacc[sb][v] * hw_exp2((at - as[v]) * kLog2e) * ws[v] : 0.0f;
                 }
                 uint2 hi, lo;
                 split4(m, hi, lo);
@@ -336,14 +370,27 @@ __global__ __launch_bounds__(kThreads, 2) void ssd_chunk_kernel(SsdParams p) {
             ssd_f4 acc[kPTL], acc2[kPTL];
 #pragma unroll
             for (int j = 0; j < kPTL; ++j) acc[j] = acc2[j] = ssd_f4{0.0f, 0.0f, 0.0f, 0.0f};
+            if constexpr (N >= 32) {
 #pragma unroll
-            for (int kk = 0; kk < NT; ++kk) {
-                const ssd_s4 cop = lds4(Cs + (16 * tb + r16) * nld + 16 * kk + q4);
+                for (int kk = 0; kk < N / 32; ++kk) {
+                    const ssd_b8 cop = lds8(Cs + (16 * tb + r16) * nld + 32 * kk + 2 * q4);
 #pragma unroll
-                for (int j = 0; j < kPTL; ++j) {
-                    const uint16_t *hp = HT + (16 * j + r16) * nld + 16 * kk + q4;
-                    acc[j] = SSD_MFMA(cop, lds4(hp), acc[j]);
-                    acc2[j] = SSD_MFMA(cop, lds4(hp + Lay::ht_plane), acc2[j]);
+                    for (int j = 0; j < kPTL; ++j) {
+                        const uint16_t *hp = HT + (16 * j + r16) * nld + 32 * kk + 2 * q4;
+                        acc[j] = SSD_MFMA32(cop, lds8(hp), acc[j]);
+                        acc2[j] = SSD_MFMA32(cop, lds8(hp + Lay::ht_plane), acc2[j]);
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int kk = 0; kk < NT; ++kk) {
+                    const ssd_s4 cop = lds4(Cs + (16 * tb + r16) * nld + 16 * kk + q4);
+#pragma unroll
+                    for (int j = 0; j < kPTL; ++j) {
+                        const uint16_t *hp = HT + (16 * j + r16) * nld + 16 * kk + q4;
+                        acc[j] = SSD_MFMA(cop, lds4(hp), acc[j]);
+                        acc2[j] = SSD_MFMA(cop, lds4(hp + Lay::ht_plane), acc2[j]);
+                    }
                 }
             }
             // lane holds t = 16 tb + q4 + v, local channel 16 j + r16
@@ -361,13 +408,18 @@ __global__ __launch_bounds__(kThreads, 2) void ssd_chunk_kernel(SsdParams p) {
 #pragma unroll
                 for (int v = 0; v < 4; ++v) acc[j][v] *= dec[v];
             }
+            // two s tiles per product: slot (lane group, e) is step 16 sb + q4 + e
+            // of the pair's first tile for e < 4, of its second tile for e >= 4
 #pragma unroll
-            for (int sb = 0; sb < kQ / 16; ++sb) {  // tiles above the diagonal are 0
+            for (int sp = 0; sp < kQ / 32; ++sp) {  // tiles above the diagonal are 0
+                const int s0 = 32 * sp, s1 = 32 * sp + 16;
+                const ssd_b8 ahi = cat8(mhi[2 * sp], mhi[2 * sp + 1]), alo = cat8(mlo[2 * sp], mlo[2 * sp + 1]);
 #pragma unroll
                 for (int j = 0; j < kPTL; ++j) {
-                    const ssd_s4 xop = col4(Xs + (16 * sb + q4) * tld + 16 * j + r16, tld);
-                    acc[j] = SSD_MFMA(mhi[sb], xop, acc[j]);
-                    acc[j] = SSD_MFMA(mlo[sb], xop, acc[j]);
+                    const ssd_b8 xop = cat8(col4(Xs + (s0 + q4) * tld + 16 * j + r16, tld),
+                                            col4(Xs + (s1 + q4) * tld + 16 * j + r16, tld));
+                    acc[j] = SSD_MFMA32(ahi, xop, acc[j]);
+                    acc[j] = SSD_MFMA32(alo, xop, acc[j]);
                 }
             }
             // skip and gate; the result replaces the gate entry it used
@@ -399,19 +451,21 @@ __global__ __launch_bounds__(kThreads, 2) void ssd_chunk_kernel(SsdParams p) {
             for (int i = 0; i < NWT; ++i)
 #pragma unroll
                 for (int j = 0; j < kPTL; ++j) st[i][j] *= dend;
+            // slot (lane group, e) is step 32 kk + 2 q4 + e
 #pragma unroll
-            for (int kk = 0; kk < kQ / 16; ++kk) {
-                ssd_s4 bop[NWT];
+            for (int kk = 0; kk < kQ / 32; ++kk) {
+                ssd_b8 bop[NWT];
 #pragma unroll
-                for (int i = 0; i < NWT; ++i) bop[i] = col4(Bs + (16 * kk + q4) * nld + 16 * my_nt(i) + r16, nld);
+                for (int i = 0; i < NWT; ++i)
+                    bop[i] = col8(Bs + (32 * kk + 2 * q4) * nld + 16 * my_nt(i) + r16, nld);
 #pragma unroll
                 for (int j = 0; j < kPTL; ++j) {
-                    const uint16_t *xp = XWT + (16 * j + r16) * qld + 16 * kk + q4;
-                    const ssd_s4 xhi = lds4(xp), xlo = lds4(xp + Lay::xwt_plane);
+                    const uint16_t *xp = XWT + (16 * j + r16) * qld + 32 * kk + 2 * q4;
+                    const ssd_b8 xhi = lds8(xp), xlo = lds8(xp + Lay::xwt_plane);
 #pragma unroll
                     for (int i = 0; i < NWT; ++i) {
-                        st[i][j] = SSD_MFMA(bop[i], xhi, st[i][j]);
-                        st[i][j] = SSD_MFMA(bop[i], xlo, st[i][j]);
+                        st[i][j] = SSD_MFMA32(bop[i], xhi, st[i][j]);
+                        st[i][j] = SSD_MFMA32(bop[i], xlo, st[i][j]);
                     }
                 }
             }
