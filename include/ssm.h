@@ -310,7 +310,7 @@ typedef struct ssm_block_plan ssm_block_plan_t;
 /*
  * Plan for these sizes.  Returns SSM_OK and *plan, or an error and *plan =
  * NULL: SSM_ERR_NULL_ARG, SSM_ERR_BAD_SHAPE (a size < 1, dt_rank > d_inner,
- * B*L >= 2^31), SSM_ERR_UNSUPPORTED (dstate, conv_k or a width not a multiple
+ * B*L >= 2^30), SSM_ERR_UNSUPPORTED (dstate, conv_k or a width not a multiple
  * of 8; or hipBLASLt offers no algorithm), SSM_ERR_HIP (no device, or the
  * handle could not be created).  The plan belongs to the device current at
  * creation.
@@ -352,8 +352,8 @@ void ssm_block_plan_destroy(ssm_block_plan_t *plan);
  *             (the weight is dt where dt A[h] == 0), from h0 (or 0)
  *   y[b,t,h,p] = (sum_n Cm[b,t,g,n] S[p,n] + Dskip[h] x[b,t,h,p]) * silu(z[b,t,h,p])
  * The state layout (B, H, P, N) is the scan's (B, D, N) with D = H P.
- * This version: bf16 I/O, headdim P == 64, dstate N in {16, 32, 64, 128};
- * other values give SSM_ERR_UNSUPPORTED.  Products run in bf16 on the matrix
+ * This version: bf16 I/O, headdim P == 64, dstate N in {16, 32, 64, 128},
+ * batch * nheads <= 2^22; other values give SSM_ERR_UNSUPPORTED.  Products run in bf16 on the matrix
  * cores with fp32 accumulation; the state is fp32 (its bf16 copy feeds the
  * product with C).
  */

@@ -27,6 +27,7 @@
 
 #include <hipblaslt/hipblaslt.h>
 
+#include <algorithm>
 #include <new>
 
 struct ssm_block_plan {
@@ -77,11 +78,8 @@ __device__ __forceinline__ uint4 norm8(const uint4 &q, const float *w, float sca
 }
 
 template <int kNormRegs>
-__global__ __launch_bounds__(256) void rmsnorm_kernel(const uint16_t *h, const float *w, uint16_t *out,
-                                                      int64_t rows, int64_t dm, float eps) {
-    const int64_t row = (int64_t)blockIdx.x * (blockDim.x / 64) + threadIdx.x / 64;
-    const int lane = threadIdx.x & 63;
-    if (row >= rows) return;
+__device__ __forceinline__ void rmsnorm_row(const uint16_t *h, const float *w, uint16_t *out, int64_t row,
+                                            int64_t dm, float eps, int lane) {
     const uint4 *hr = reinterpret_cast<const uint4 *>(h + row * dm);
     uint4 *orow = reinterpret_cast<uint4 *>(out + row * dm);
     const int64_t groups = dm / 8;
@@ -114,6 +112,15 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const uint16_t *h, const f
         if (gi < groups) orow[gi] = norm8(keep[r], w + 8 * gi, scale);
     }
     for (int64_t gi = lane + 64 * kNormRegs; gi < groups; gi += 64) orow[gi] = norm8(hr[gi], w + 8 * gi, scale);
+}
+
+template <int kNormRegs>
+__global__ __launch_bounds__(256) void rmsnorm_kernel(const uint16_t *h, const float *w, uint16_t *out,
+                                                      int64_t rows, int64_t dm, float eps) {
+    const int lane = threadIdx.x & 63;
+    for (int64_t row = (int64_t)blockIdx.x * (blockDim.x / 64) + threadIdx.x / 64; row < rows;
+         row += (int64_t)gridDim.x * (blockDim.x / 64))
+        rmsnorm_row<kNormRegs>(h, w, out, row, dm, eps, lane);
 }
 
 // dt = softplus(dt_low W_dt^T + dt_bias) over all rows, with dt_low the first
@@ -393,7 +400,8 @@ hipError_t launch_block_fwd(const ssm_block_plan &p, const ssm_block_weights_t &
     char *lt_ws = ws + p.o_lt;
     uint16_t *hn = reinterpret_cast<uint16_t *>(ws + p.o_hn);
     {
-        const unsigned blocks = (unsigned)((M + 3) / 4);
+        // grid-stride rows: at most 65536 workgroups of 4 rows
+        const unsigned blocks = (unsigned)std::min<int64_t>((M + 3) / 4, 65536);
         const auto *hi = static_cast<const uint16_t *>(h_in);
         const int64_t per_lane = (dm / 8 + 63) / 64;
         if (per_lane <= 1)

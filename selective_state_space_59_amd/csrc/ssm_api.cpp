@@ -385,9 +385,9 @@ ssm_status_t ssm_block_plan_create(const ssm_block_dims_t *d, ssm_block_plan_t *
         return fail(SSM_ERR_UNSUPPORTED, "conv_k must be 1..%d (got %lld)", SSM_MAX_CONV_K, (long long)d->conv_k);
     // hipBLASLt takes 32-bit sizes; the largest operands stay well inside them.
     const int64_t M = d->batch * d->seqlen;
-    if (!mul_ok(d->batch, d->seqlen, 4 * (d->d_model + d->d_inner)) || M > INT32_MAX ||
+    if (!mul_ok(d->batch, d->seqlen, 4 * (d->d_model + d->d_inner)) || M >= ((int64_t)1 << 30) ||
         d->d_model > INT32_MAX / 4 || d->d_inner > INT32_MAX / 4 || d->dt_rank > d->d_inner)
-        return fail(SSM_ERR_BAD_SHAPE, "block sizes out of range (dt_rank <= d_inner, B*L < 2^31)");
+        return fail(SSM_ERR_BAD_SHAPE, "block sizes out of range (dt_rank <= d_inner, B*L < 2^30)");
     ssm_block_plan *p = nullptr;
     const ssm_status_t s = ssm::block_plan_create(*d, &p);
     if (s != SSM_OK) return fail(s, "could not set up the block's GEMMs (hipBLASLt handle or algorithm)");
@@ -464,6 +464,9 @@ ssm_status_t ssm_ssd_fwd(const ssm_ssd_args_t *a, void *stream) {
     const int64_t B = a->batch, L = a->seqlen, H = a->nheads, P = a->headdim, G = a->ngroups, N = a->dstate;
     if (!mul_ok(B, L, H * P) || !mul_ok(B, L, G * N) || !mul_ok(B, H, P * N))
         return fail(SSM_ERR_BAD_SHAPE, "sizes overflow");
+    // one workgroup of 256 threads per (batch, head, 32 channels): the launch holds < 2^32 threads
+    if (B * H > ((int64_t)1 << 22))
+        return fail(SSM_ERR_UNSUPPORTED, "batch * nheads (%lld) exceeds 2^22", (long long)(B * H));
     if (!a->A) return fail(SSM_ERR_NULL_ARG, "A is required");
     if (B * L > 0 && (!a->x || !a->delta || !a->Bm || !a->Cm || !a->y))
         return fail(SSM_ERR_NULL_ARG, "x, delta, Bm, Cm and y are required");

@@ -379,7 +379,7 @@ def block_dims(**kw):
     ("conv_k", 5, ssm.SSM_ERR_UNSUPPORTED),
     ("d_model", 60, ssm.SSM_ERR_UNSUPPORTED),     # not a multiple of 8
     ("d_inner", 100, ssm.SSM_ERR_UNSUPPORTED),
-    ("seqlen", 1 << 31, ssm.SSM_ERR_BAD_SHAPE),   # B*L beyond 32-bit GEMM sizes
+    ("seqlen", 1 << 29, ssm.SSM_ERR_BAD_SHAPE),   # B*L = 2^30: beyond the launch limits
 ])
 def test_block_plan_rejects_bad_sizes(field, value, status):
     h = ctypes.c_void_p(12345)
@@ -440,6 +440,7 @@ def run_ssd(a):
     ("delta", addr(1, 1), ssm.SSM_ERR_ALIGN),
     ("y", addr(0, 256), ssm.SSM_ERR_ALIAS),                # inside x
     ("h_final", addr(7), ssm.SSM_ERR_ALIAS),               # == y
+    ("nheads", 1 << 22, ssm.SSM_ERR_UNSUPPORTED),          # batch * nheads > 2^22
 ])
 def test_ssd_rejects_bad_arguments(field, value, status):
     assert run_ssd(ssd_args(**{field: value})) == status

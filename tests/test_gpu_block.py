@@ -44,6 +44,7 @@ CASES = [
     ("rank80_stepped", 1, 40, 64, 128, 16, 80, 4, False),   # rank > 64: operands per step
     ("rank70_narrow", 2, 33, 64, 136, 16, 70, 4, False),    # rank, row stride not multiples of 4
     ("wide_channels", 1, 20, 256, 1040, 16, 16, 4, False),  # channel blocks with a ragged last one
+    ("many_rows", 1, 270000, 16, 16, 16, 2, 4, False),      # more rows than one norm grid covers
 ]
 
 
