@@ -67,10 +67,11 @@ struct SsdLds {
     // HT: [hi/lo plane][kPT channels][nld]
     static constexpr size_t ht = zs + (size_t)kQ * tld * 2;
     static constexpr size_t ht_plane = (size_t)kPT * nld;  // elements
-    // XWT: [hi/lo plane][kPT channels][qld]
+    // XWT: [hi/lo plane][kPT channels][qld]; then XT: x transposed, [kPT][qld]
     static constexpr size_t xwt = ht + 2 * ht_plane * 2;
     static constexpr size_t xwt_plane = (size_t)kPT * qld;
-    static constexpr size_t dts = xwt + 2 * xwt_plane * 2;
+    static constexpr size_t xt = xwt + 2 * xwt_plane * 2;
+    static constexpr size_t dts = xt + xwt_plane * 2;
     // per wave: the chunk's prefix sums of dt a, then its ZOH weights (lane = step)
     static constexpr size_t scal = dts + (size_t)kQ * sizeof(float);
     static constexpr size_t total = scal + (size_t)4 * 2 * kQ * sizeof(float);
@@ -168,7 +169,7 @@ struct ChunkRegs {
     static constexpr int PR = N / 8;  // pieces per B/C row
     static constexpr int KB = (kQ * PR + kThreads - 1) / kThreads;
     uint4 b[KB], c[KB], x, z;
-    float dt;
+    uint16_t dt;  // raw bits: converting here would wait for the load
 };
 
 template <int N>
@@ -201,17 +202,14 @@ __device__ __forceinline__ void fetch_chunk(const SsdParams &p, int64_t b, int64
             if (p.z) r.z = *reinterpret_cast<const uint4 *>(p.z + off);
         }
     }
-    r.dt = 0.0f;
-    if (tid < kQ && t0 + tid < L) {
-        float dt = bf(p.delta[(b * L + t0 + tid) * p.H + h]);
-        if (p.softplus) dt = softplus_fast(dt + dbias);
-        r.dt = dt;
-    }
+    r.dt = 0;  // bf16 zero: the step of a row past the end
+    if (tid < kQ && t0 + tid < L) r.dt = p.delta[(b * L + t0 + tid) * p.H + h];
 }
 
 template <int N>
 __device__ __forceinline__ void store_chunk(const ChunkRegs<N> &r, uint16_t *Bs, uint16_t *Cs, uint16_t *Xs,
-                                            uint16_t *Zs, float *dts, int tid) {
+                                            uint16_t *XT, uint16_t *Zs, float *dts, int tid, bool row_live,
+                                            int softplus, float dbias) {
     using R = ChunkRegs<N>;
     using Lay = SsdLds<N>;
 #pragma unroll
@@ -227,8 +225,17 @@ __device__ __forceinline__ void store_chunk(const ChunkRegs<N> &r, uint16_t *Bs,
         const int s = tid / (kPT / 8), c8 = (tid % (kPT / 8)) * 8;
         *reinterpret_cast<uint4 *>(Xs + s * Lay::tld + c8) = r.x;
         *reinterpret_cast<uint4 *>(Zs + s * Lay::tld + c8) = r.z;
+        // x transposed (channel-major), the k-contiguous operand of M X
+        const uint32_t wv[4] = {r.x.x, r.x.y, r.x.z, r.x.w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            XT[(c8 + i) * Lay::qld + s] = (uint16_t)(i % 2 ? wv[i / 2] >> 16 : wv[i / 2] & 0xffffu);
     }
-    if (tid < kQ) dts[tid] = r.dt;
+    if (tid < kQ) {
+        float dt = bf(r.dt);
+        if (softplus && row_live) dt = softplus_fast(dt + dbias);
+        dts[tid] = dt;
+    }
 }
 
 template <int N>
@@ -245,6 +252,7 @@ __global__ __launch_bounds__(kThreads, 2) void ssd_chunk_kernel(SsdParams p) {
     uint16_t *Zs = reinterpret_cast<uint16_t *>(lds + Lay::zs);
     uint16_t *HT = reinterpret_cast<uint16_t *>(lds + Lay::ht);
     uint16_t *XWT = reinterpret_cast<uint16_t *>(lds + Lay::xwt);
+    uint16_t *XT = reinterpret_cast<uint16_t *>(lds + Lay::xt);
     float *dts = reinterpret_cast<float *>(lds + Lay::dts);
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -289,7 +297,7 @@ __global__ __launch_bounds__(kThreads, 2) void ssd_chunk_kernel(SsdParams p) {
     if (nchunks > 0) fetch_chunk<N>(p, b, h, g, pt, 0, dbias, tid, regs);
     for (int64_t c = 0; c < nchunks; ++c) {
         const int64_t t0 = c * kQ;
-        store_chunk<N>(regs, Bs, Cs, Xs, Zs, dts, tid);
+        store_chunk<N>(regs, Bs, Cs, Xs, XT, Zs, dts, tid, t0 + tid < L, p.softplus, dbias);
         __syncthreads();
         // the next chunk's loads fly while this chunk is computed
         if (c + 1 < nchunks) fetch_chunk<N>(p, b, h, g, pt, t0 + kQ, dbias, tid, regs);
@@ -304,14 +312,21 @@ __global__ __launch_bounds__(kThreads, 2) void ssd_chunk_kernel(SsdParams p) {
         acum_s[lane] = acum;
         wl_s[lane] = wl;
 
-        // ---- X' = f x -> XWT[p][s] (hi, lo): wave w writes kPT / 4 channels ----
+        // ---- X' = f x -> XWT[p][s] (hi, lo): wave w takes channels 8w .. 8w+7
+        // of step s = lane, one 16-byte row read (read after the middle barrier)
+        {
+            static_assert(kPT / 4 == 8, "one 16-byte piece of x per lane");
+            const uint4 q = *reinterpret_cast<const uint4 *>(Xs + lane * tld + 8 * w);
+            const uint32_t wv[4] = {q.x, q.y, q.z, q.w};
 #pragma unroll
-        for (int i = 0; i < kPT / 4; ++i) {
-            const int pp = (kPT / 4) * w + i;
-            const float v = bf(Xs[lane * tld + pp]) * fl;
-            const uint16_t hi = f32_to_bf16_bits(v);
-            XWT[pp * qld + lane] = hi;
-            XWT[Lay::xwt_plane + pp * qld + lane] = f32_to_bf16_bits(v - bf(hi));
+            for (int i = 0; i < 8; ++i) {
+                const int pp = 8 * w + i;
+                const uint16_t xb = (uint16_t)(i % 2 ? wv[i / 2] >> 16 : wv[i / 2] & 0xffffu);
+                const float v = bf(xb) * fl;
+                const uint16_t hi = f32_to_bf16_bits(v);
+                XWT[pp * qld + lane] = hi;
+                XWT[Lay::xwt_plane + pp * qld + lane] = f32_to_bf16_bits(v - bf(hi));
+            }
         }
 
         // ---- this wave's G^T tiles, masked and decayed in place ---------------------
@@ -416,8 +431,8 @@ __global__ __launch_bounds__(kThreads, 2) void ssd_chunk_kernel(SsdParams p) {
                 const ssd_b8 ahi = cat8(mhi[2 * sp], mhi[2 * sp + 1]), alo = cat8(mlo[2 * sp], mlo[2 * sp + 1]);
 #pragma unroll
                 for (int j = 0; j < kPTL; ++j) {
-                    const ssd_b8 xop = cat8(col4(Xs + (s0 + q4) * tld + 16 * j + r16, tld),
-                                            col4(Xs + (s1 + q4) * tld + 16 * j + r16, tld));
+                    const uint16_t *xr = XT + (16 * j + r16) * qld;
+                    const ssd_b8 xop = cat8(lds4(xr + s0 + q4), lds4(xr + s1 + q4));
                     acc[j] = SSD_MFMA32(ahi, xop, acc[j]);
                     acc[j] = SSD_MFMA32(alo, xop, acc[j]);
                 }
