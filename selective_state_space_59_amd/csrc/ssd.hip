@@ -36,7 +36,7 @@
 // significant bits, where a single bf16 rounding (8 bits) would leave errors
 // of order 1% in sums that cancel (C.h is a sum of N terms of either sign).
 // The chunk's inputs for the next chunk are loaded into registers while this
-// one is computed.  About 71 KB of LDS per workgroup (N = 128): two
+// one is computed.  About 79 KB of LDS per workgroup (N = 128): two
 // workgroups share a CU.
 #include "ssm_device.h"
 #include "ssm_internal.h"
