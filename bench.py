@@ -338,9 +338,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--no-extras", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=("block", "ssd"),
-                    help="only time the 130M-like Mamba block forward, or the Mamba-2 130M-like "
-                         "SSD layer, and print its numbers")
+    ap.add_argument("--only", choices=("block", "ssd", "ssd_long"),
+                    help="only time the 130M-like Mamba block forward, the Mamba-2 130M-like "
+                         "SSD layer, or that layer on one 65536-token sequence, and print its numbers")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (fp32) five times; its "
                          "FETCH_SIZE / WRITE_SIZE counters scale the scan's traffic counters")
@@ -369,9 +369,9 @@ def main():
     if args.only == "block":
         print(json.dumps({W.B2_130M.name: block_entry(W.B2_130M, args.steps, args.warmup)}), flush=True)
         return
-    if args.only == "ssd":
-        print(json.dumps({W.S2_MAMBA2_130M.name: ssd_entry(W.S2_MAMBA2_130M, args.steps, args.warmup)}),
-              flush=True)
+    if args.only in ("ssd", "ssd_long"):
+        c = W.S2_MAMBA2_130M if args.only == "ssd" else W.S4_MAMBA2_LONG
+        print(json.dumps({c.name: ssd_entry(c, args.steps, args.warmup)}), flush=True)
         return
 
     cfg = W.C2_130M
@@ -451,6 +451,9 @@ def main():
         # the SSD (Mamba-2) layer at the 130M-like width with N = 128
         print("bench extra: %s" % W.S2_MAMBA2_130M.name, file=sys.stderr, flush=True)
         extra[W.S2_MAMBA2_130M.name] = ssd_entry(W.S2_MAMBA2_130M, 30, 5)
+        # one 65536-token sequence at that width: the segmented schedule
+        print("bench extra: %s" % W.S4_MAMBA2_LONG.name, file=sys.stderr, flush=True)
+        extra[W.S4_MAMBA2_LONG.name] = ssd_entry(W.S4_MAMBA2_LONG, 10, 2)
         out["extra"] = extra
 
     if not args.no_cpu_baseline:

@@ -62,7 +62,7 @@
 extern "C" {
 #endif
 
-#define SSM_ABI_VERSION 5
+#define SSM_ABI_VERSION 6
 #define SSM_MAX_DSTATE 16 /* largest N the kernels hold in registers */
 #define SSM_MAX_CONV_K 4  /* largest conv1d kernel width */
 
@@ -375,12 +375,24 @@ typedef struct ssm_ssd_args {
     const float *h0;        /* (B,H,P,N) fp32 initial state, or NULL (= 0)     */
     void *y;                /* (B,L,H,P) bf16 output, required                 */
     float *h_final;         /* (B,H,P,N) fp32 output, or NULL                  */
+    void *workspace;        /* device scratch of workspace_bytes, 256-aligned  */
+    size_t workspace_bytes; /* >= ssm_ssd_workspace_size(args)                 */
 } ssm_ssd_args_t;
 
 /*
+ * Bytes of device workspace ssm_ssd_fwd needs (0 when none; only the size
+ * fields are read).  With few (batch, head) pairs the sequence is cut into
+ * segments that run at once: each segment's end state from a zero start,
+ * then the entering states by the recurrence over segments, then each
+ * segment's outputs from its entering state.  The workspace holds those
+ * states; its contents on entry do not matter.  (size_t)-1 for invalid sizes.
+ */
+size_t ssm_ssd_workspace_size(const ssm_ssd_args_t *args);
+
+/*
  * Enqueue the SSD layer on `stream`.  x, Bm, Cm, z and y must be 16-byte
- * aligned, delta 2-byte, the fp32 tensors 4-byte.  y and h_final must not
- * overlap any input or each other.  L == 0 copies h0 (or zeros) to h_final;
+ * aligned, delta 2-byte, the fp32 tensors 4-byte.  y, h_final and the
+ * workspace must not overlap any input or each other.  L == 0 copies h0 (or zeros) to h_final;
  * the (B,L,...) pointers may then be NULL.
  */
 ssm_status_t ssm_ssd_fwd(const ssm_ssd_args_t *args, void *stream);

@@ -41,6 +41,8 @@
 #include "ssm_device.h"
 #include "ssm_internal.h"
 
+#include <algorithm>
+
 namespace ssm {
 namespace {
 
@@ -84,6 +86,13 @@ struct SsdParams {
     uint16_t *y;
     float *h_final;
     int softplus;
+    // Sequence segments (mode 0: one segment, the whole sequence).  Mode 1:
+    // each segment from a zero state, writing only its end state and its
+    // sum of dt a; mode 2: each segment from its entering state, writing y.
+    int mode;  // selects the kernel instance
+    int64_t nseg, seg_chunks;
+    float *ws_state;  // (nseg, B, H, P, N): end states, then entering states
+    float *ws_lsum;   // (nseg, B, H): sum of dt a over the segment
 };
 
 __device__ __forceinline__ float bf(uint16_t v) { return bf16_bits_to_f32(v); }
@@ -174,7 +183,7 @@ struct ChunkRegs {
 
 template <int N>
 __device__ __forceinline__ void fetch_chunk(const SsdParams &p, int64_t b, int64_t h, int64_t g, int pt,
-                                            int64_t t0, float dbias, int tid, ChunkRegs<N> &r) {
+                                            int64_t t0, bool outputs, int tid, ChunkRegs<N> &r) {
     using R = ChunkRegs<N>;
     const int64_t L = p.L;
 #pragma unroll
@@ -187,7 +196,7 @@ __device__ __forceinline__ void fetch_chunk(const SsdParams &p, int64_t b, int64
         if (id < kQ * R::PR && t < L) {
             const int64_t off = ((b * L + t) * p.G + g) * N + c8;
             r.b[k] = *reinterpret_cast<const uint4 *>(p.Bm + off);
-            r.c[k] = *reinterpret_cast<const uint4 *>(p.Cm + off);
+            if (outputs) r.c[k] = *reinterpret_cast<const uint4 *>(p.Cm + off);
         }
     }
     {
@@ -199,7 +208,7 @@ __device__ __forceinline__ void fetch_chunk(const SsdParams &p, int64_t b, int64
         if (t < L) {
             const int64_t off = ((b * L + t) * p.H + h) * kP + kPT * pt + c8;
             r.x = *reinterpret_cast<const uint4 *>(p.x + off);
-            if (p.z) r.z = *reinterpret_cast<const uint4 *>(p.z + off);
+            if (p.z && outputs) r.z = *reinterpret_cast<const uint4 *>(p.z + off);
         }
     }
     r.dt = 0;  // bf16 zero: the step of a row past the end
@@ -238,7 +247,7 @@ __device__ __forceinline__ void store_chunk(const ChunkRegs<N> &r, uint16_t *Bs,
     }
 }
 
-template <int N>
+template <int N, int MODE>
 __global__ __launch_bounds__(kThreads, 2) void ssd_chunk_kernel(SsdParams p) {
     using Lay = SsdLds<N>;
     constexpr int NT = N / 16;       // state tiles of the head
@@ -260,7 +269,8 @@ __global__ __launch_bounds__(kThreads, 2) void ssd_chunk_kernel(SsdParams p) {
     float *acum_s = reinterpret_cast<float *>(lds + Lay::scal) + 2 * kQ * w;
     float *wl_s = acum_s + kQ;
     const int r16 = lane & 15, q4 = 4 * (lane >> 4);
-    const int64_t bhp = blockIdx.x;
+    const int64_t seg = (int64_t)blockIdx.x % p.nseg;
+    const int64_t bhp = (int64_t)blockIdx.x / p.nseg;
     const int pt = (int)(bhp % (kP / kPT));
     const int64_t bh = bhp / (kP / kPT);
     const int64_t b = bh / p.H, h = bh % p.H;
@@ -278,35 +288,44 @@ __global__ __launch_bounds__(kThreads, 2) void ssd_chunk_kernel(SsdParams p) {
     ssd_f4 st[NWT][kPTL];
     auto my_nt = [&](int i) { return NW > 0 ? NW * w + i : w; };
     const bool owns_state = NW > 0 || w < NT;
+    constexpr bool outputs = MODE != 1;
+    // the entering state: h0 (or 0) for the whole sequence, 0 for a segment's
+    // end state, the combined entering state for a segment's outputs
+    const float *hin = MODE == 0 ? p.h0 : MODE == 2 ? p.ws_state + seg * p.B * p.H * kP * N : nullptr;
+    const float *hin_bh = hin ? hin + bh * kP * N : nullptr;
 #pragma unroll
     for (int i = 0; i < NWT; ++i)
 #pragma unroll
         for (int j = 0; j < kPTL; ++j) {
             const int nt = my_nt(i), pl = 16 * j + r16;
             float v4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-            if (owns_state && p.h0) {
+            if (owns_state && hin_bh) {
 #pragma unroll
-                for (int v = 0; v < 4; ++v) v4[v] = p.h0[(bh * kP + kPT * pt + pl) * N + 16 * nt + q4 + v];
+                for (int v = 0; v < 4; ++v) v4[v] = hin_bh[(kPT * pt + pl) * N + 16 * nt + q4 + v];
             }
             st[i][j] = ssd_f4{v4[0], v4[1], v4[2], v4[3]};
             if (owns_state) store_split4(HT + pl * nld + 16 * nt + q4, Lay::ht_plane, v4);
         }
 
     const int64_t nchunks = (L + kQ - 1) / kQ;
+    const int64_t c_begin = seg * p.seg_chunks;
+    const int64_t c_end = c_begin + p.seg_chunks < nchunks ? c_begin + p.seg_chunks : nchunks;
+    float lsum = 0.0f;  // sum of dt a over this workgroup's chunks
     ChunkRegs<N> regs;
-    if (nchunks > 0) fetch_chunk<N>(p, b, h, g, pt, 0, dbias, tid, regs);
-    for (int64_t c = 0; c < nchunks; ++c) {
+    if (c_begin < c_end) fetch_chunk<N>(p, b, h, g, pt, c_begin * kQ, outputs, tid, regs);
+    for (int64_t c = c_begin; c < c_end; ++c) {
         const int64_t t0 = c * kQ;
         store_chunk<N>(regs, Bs, Cs, Xs, XT, Zs, dts, tid, t0 + tid < L, p.softplus, dbias);
         __syncthreads();
         // the next chunk's loads fly while this chunk is computed
-        if (c + 1 < nchunks) fetch_chunk<N>(p, b, h, g, pt, t0 + kQ, dbias, tid, regs);
+        if (c + 1 < c_end) fetch_chunk<N>(p, b, h, g, pt, t0 + kQ, outputs, tid, regs);
 
         // ---- chunk scalars, one copy per wave (lane = step s) ----------------
         const float dtl = dts[lane];
         const float zl = dtl * a;
         const float acum = wave_prefix_sum(zl, lane);  // inclusive prefix sum of dt a
         const float aend = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(acum), 63));
+        lsum += aend;
         const float wl = dtl * ssd_phi(zl, hw_exp2(zl * kLog2e));       // ZOH input weight
         const float fl = hw_exp2((aend - acum) * kLog2e) * wl;         // weight in the end state
         acum_s[lane] = acum;
@@ -329,134 +348,138 @@ __global__ __launch_bounds__(kThreads, 2) void ssd_chunk_kernel(SsdParams p) {
             }
         }
 
-        // ---- this wave's G^T tiles, masked and decayed in place ---------------------
-        // All four s tiles are formed (those above the diagonal are masked to 0
-        // below): straight-line code lets the operand loads run ahead of the
-        // MFMAs, and every wave does the same work.
-        ssd_f4 gacc[kQ / 16];
-#pragma unroll
-        for (int sb = 0; sb < kQ / 16; ++sb) gacc[sb] = ssd_f4{0.0f, 0.0f, 0.0f, 0.0f};
-        if constexpr (N >= 32) {
-#pragma unroll
-            for (int kk = 0; kk < N / 32; ++kk) {
-                const ssd_b8 cop = lds8(Cs + (16 * tb + r16) * nld + 32 * kk + 2 * q4);
-#pragma unroll
-                for (int sb = 0; sb < kQ / 16; ++sb)
-                    gacc[sb] = SSD_MFMA32(lds8(Bs + (16 * sb + r16) * nld + 32 * kk + 2 * q4), cop, gacc[sb]);
-            }
-        } else {
-#pragma unroll
-            for (int kk = 0; kk < NT; ++kk) {
-                const ssd_s4 cop = lds4(Cs + (16 * tb + r16) * nld + 16 * kk + q4);
-#pragma unroll
-                for (int sb = 0; sb < kQ / 16; ++sb)
-                    gacc[sb] = SSD_MFMA(lds4(Bs + (16 * sb + r16) * nld + 16 * kk + q4), cop, gacc[sb]);
-            }
-        }
-        // lane holds s = 16 sb + q4 + v, t = 16 tb + r16: M[t][s], the A operand
-        // (row t, k = s) of M X as it stands
-        ssd_s4 mhi[kQ / 16], mlo[kQ / 16];
-        {
-            const float at = acum_s[16 * tb + r16];
-#pragma unroll
-            for (int sb = 0; sb < kQ / 16; ++sb) {
-                if (sb > tb) {  // above the diagonal (wave-uniform): all zero
-                    mhi[sb] = mlo[sb] = ssd_s4{0, 0, 0, 0};
-                    continue;
-                }
-                const float4 as4 = *reinterpret_cast<const float4 *>(acum_s + 16 * sb + q4);
-                const float4 ws4 = *reinterpret_cast<const float4 *>(wl_s + 16 * sb + q4);
-                const float as[4] = {as4.x, as4.y, as4.z, as4.w}, ws[4] = {ws4.x, ws4.y, ws4.z, ws4.w};
-                float m[4];
-#pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    const int s = 16 * sb + q4 + v;
-                    m[v] = s <= 16 * tb + r16 ? gacc[sb][v] * hw_exp2((at - as[v]) * kLog2e) * ws[v] : 0.0f;
-                }
-                uint2 hi, lo;
-                split4(m, hi, lo);
-                mhi[sb] = __builtin_bit_cast(ssd_s4, hi);
-                mlo[sb] = __builtin_bit_cast(ssd_s4, lo);
-            }
-        }
-
-        // ---- Y for this wave's 16 steps and the workgroup's channels --------------
-        {
-            ssd_f4 acc[kPTL], acc2[kPTL];
-#pragma unroll
-            for (int j = 0; j < kPTL; ++j) acc[j] = acc2[j] = ssd_f4{0.0f, 0.0f, 0.0f, 0.0f};
+        if constexpr (outputs) {
+            // ---- this wave's G^T tiles, masked and decayed in place ---------------------
+            // All four s tiles are formed (those above the diagonal are masked to 0
+            // below): straight-line code lets the operand loads run ahead of the
+            // MFMAs, and every wave does the same work.
+            ssd_f4 gacc[kQ / 16];
+    #pragma unroll
+            for (int sb = 0; sb < kQ / 16; ++sb) gacc[sb] = ssd_f4{0.0f, 0.0f, 0.0f, 0.0f};
             if constexpr (N >= 32) {
-#pragma unroll
+    #pragma unroll
                 for (int kk = 0; kk < N / 32; ++kk) {
                     const ssd_b8 cop = lds8(Cs + (16 * tb + r16) * nld + 32 * kk + 2 * q4);
-#pragma unroll
-                    for (int j = 0; j < kPTL; ++j) {
-                        const uint16_t *hp = HT + (16 * j + r16) * nld + 32 * kk + 2 * q4;
-                        acc[j] = SSD_MFMA32(cop, lds8(hp), acc[j]);
-                        acc2[j] = SSD_MFMA32(cop, lds8(hp + Lay::ht_plane), acc2[j]);
-                    }
+    #pragma unroll
+                    for (int sb = 0; sb < kQ / 16; ++sb)
+                        gacc[sb] = SSD_MFMA32(lds8(Bs + (16 * sb + r16) * nld + 32 * kk + 2 * q4), cop, gacc[sb]);
                 }
             } else {
-#pragma unroll
+    #pragma unroll
                 for (int kk = 0; kk < NT; ++kk) {
                     const ssd_s4 cop = lds4(Cs + (16 * tb + r16) * nld + 16 * kk + q4);
-#pragma unroll
-                    for (int j = 0; j < kPTL; ++j) {
-                        const uint16_t *hp = HT + (16 * j + r16) * nld + 16 * kk + q4;
-                        acc[j] = SSD_MFMA(cop, lds4(hp), acc[j]);
-                        acc2[j] = SSD_MFMA(cop, lds4(hp + Lay::ht_plane), acc2[j]);
+    #pragma unroll
+                    for (int sb = 0; sb < kQ / 16; ++sb)
+                        gacc[sb] = SSD_MFMA(lds4(Bs + (16 * sb + r16) * nld + 16 * kk + q4), cop, gacc[sb]);
+                }
+            }
+            // lane holds s = 16 sb + q4 + v, t = 16 tb + r16: M[t][s], the A operand
+            // (row t, k = s) of M X as it stands
+            ssd_s4 mhi[kQ / 16], mlo[kQ / 16];
+            {
+                const float at = acum_s[16 * tb + r16];
+    #pragma unroll
+                for (int sb = 0; sb < kQ / 16; ++sb) {
+                    if (sb > tb) {  // above the diagonal (wave-uniform): all zero
+                        mhi[sb] = mlo[sb] = ssd_s4{0, 0, 0, 0};
+                        continue;
+                    }
+                    const float4 as4 = *reinterpret_cast<const float4 *>(acum_s + 16 * sb + q4);
+                    const float4 ws4 = *reinterpret_cast<const float4 *>(wl_s + 16 * sb + q4);
+                    const float as[4] = {as4.x, as4.y, as4.z, as4.w}, ws[4] = {ws4.x, ws4.y, ws4.z, ws4.w};
+                    float m[4];
+    #pragma unroll
+                    for (int v = 0; v < 4; ++v) {
+                        const int s = 16 * sb + q4 + v;
+                        m[v] = s <= 16 * tb + r16 ? gacc[sb][v] * hw_exp2((at - as[v]) * kLog2e) * ws[v] : 0.0f;
+                    }
+                    uint2 hi, lo;
+                    split4(m, hi, lo);
+                    mhi[sb] = __builtin_bit_cast(ssd_s4, hi);
+                    mlo[sb] = __builtin_bit_cast(ssd_s4, lo);
+                }
+            }
+
+            // ---- Y for this wave's 16 steps and the workgroup's channels --------------
+            {
+                ssd_f4 acc[kPTL], acc2[kPTL];
+    #pragma unroll
+                for (int j = 0; j < kPTL; ++j) acc[j] = acc2[j] = ssd_f4{0.0f, 0.0f, 0.0f, 0.0f};
+                if constexpr (N >= 32) {
+    #pragma unroll
+                    for (int kk = 0; kk < N / 32; ++kk) {
+                        const ssd_b8 cop = lds8(Cs + (16 * tb + r16) * nld + 32 * kk + 2 * q4);
+    #pragma unroll
+                        for (int j = 0; j < kPTL; ++j) {
+                            const uint16_t *hp = HT + (16 * j + r16) * nld + 32 * kk + 2 * q4;
+                            acc[j] = SSD_MFMA32(cop, lds8(hp), acc[j]);
+                            acc2[j] = SSD_MFMA32(cop, lds8(hp + Lay::ht_plane), acc2[j]);
+                        }
+                    }
+                } else {
+    #pragma unroll
+                    for (int kk = 0; kk < NT; ++kk) {
+                        const ssd_s4 cop = lds4(Cs + (16 * tb + r16) * nld + 16 * kk + q4);
+    #pragma unroll
+                        for (int j = 0; j < kPTL; ++j) {
+                            const uint16_t *hp = HT + (16 * j + r16) * nld + 16 * kk + q4;
+                            acc[j] = SSD_MFMA(cop, lds4(hp), acc[j]);
+                            acc2[j] = SSD_MFMA(cop, lds4(hp + Lay::ht_plane), acc2[j]);
+                        }
                     }
                 }
-            }
-            // lane holds t = 16 tb + q4 + v, local channel 16 j + r16
-            float dec[4];
-            {
-                const float4 a4 = *reinterpret_cast<const float4 *>(acum_s + 16 * tb + q4);
-                dec[0] = hw_exp2(a4.x * kLog2e);
-                dec[1] = hw_exp2(a4.y * kLog2e);
-                dec[2] = hw_exp2(a4.z * kLog2e);
-                dec[3] = hw_exp2(a4.w * kLog2e);
-            }
-#pragma unroll
-            for (int j = 0; j < kPTL; ++j) {
-                acc[j] += acc2[j];
-#pragma unroll
-                for (int v = 0; v < 4; ++v) acc[j][v] *= dec[v];
-            }
-            // two s tiles per product: slot (lane group, e) is step 16 sb + q4 + e
-            // of the pair's first tile for e < 4, of its second tile for e >= 4
-#pragma unroll
-            for (int sp = 0; sp < kQ / 32; ++sp) {  // tiles above the diagonal are 0
-                const int s0 = 32 * sp, s1 = 32 * sp + 16;
-                const ssd_b8 ahi = cat8(mhi[2 * sp], mhi[2 * sp + 1]), alo = cat8(mlo[2 * sp], mlo[2 * sp + 1]);
-#pragma unroll
+                // lane holds t = 16 tb + q4 + v, local channel 16 j + r16
+                float dec[4];
+                {
+                    const float4 a4 = *reinterpret_cast<const float4 *>(acum_s + 16 * tb + q4);
+                    dec[0] = hw_exp2(a4.x * kLog2e);
+                    dec[1] = hw_exp2(a4.y * kLog2e);
+                    dec[2] = hw_exp2(a4.z * kLog2e);
+                    dec[3] = hw_exp2(a4.w * kLog2e);
+                }
+    #pragma unroll
                 for (int j = 0; j < kPTL; ++j) {
-                    const uint16_t *xr = XT + (16 * j + r16) * qld;
-                    const ssd_b8 xop = cat8(lds4(xr + s0 + q4), lds4(xr + s1 + q4));
-                    acc[j] = SSD_MFMA32(ahi, xop, acc[j]);
-                    acc[j] = SSD_MFMA32(alo, xop, acc[j]);
+                    acc[j] += acc2[j];
+    #pragma unroll
+                    for (int v = 0; v < 4; ++v) acc[j][v] *= dec[v];
                 }
+                // two s tiles per product: slot (lane group, e) is step 16 sb + q4 + e
+                // of the pair's first tile for e < 4, of its second tile for e >= 4
+    #pragma unroll
+                for (int sp = 0; sp < kQ / 32; ++sp) {  // tiles above the diagonal are 0
+                    const int s0 = 32 * sp, s1 = 32 * sp + 16;
+                    const ssd_b8 ahi = cat8(mhi[2 * sp], mhi[2 * sp + 1]), alo = cat8(mlo[2 * sp], mlo[2 * sp + 1]);
+    #pragma unroll
+                    for (int j = 0; j < kPTL; ++j) {
+                        const uint16_t *xr = XT + (16 * j + r16) * qld;
+                        const ssd_b8 xop = cat8(lds4(xr + s0 + q4), lds4(xr + s1 + q4));
+                        acc[j] = SSD_MFMA32(ahi, xop, acc[j]);
+                        acc[j] = SSD_MFMA32(alo, xop, acc[j]);
+                    }
+                }
+                // skip and gate; the result replaces the gate entry it used
+    #pragma unroll
+                for (int j = 0; j < kPTL; ++j)
+    #pragma unroll
+                    for (int v = 0; v < 4; ++v) {
+                        const int t = 16 * tb + q4 + v, pl = 16 * j + r16;
+                        float yv = acc[j][v] + dsk * bf(Xs[t * tld + pl]);
+                        if (p.z) yv *= silu(bf(Zs[t * tld + pl]));
+                        Zs[t * tld + pl] = f32_to_bf16_bits(yv);
+                    }
             }
-            // skip and gate; the result replaces the gate entry it used
-#pragma unroll
-            for (int j = 0; j < kPTL; ++j)
-#pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    const int t = 16 * tb + q4 + v, pl = 16 * j + r16;
-                    float yv = acc[j][v] + dsk * bf(Xs[t * tld + pl]);
-                    if (p.z) yv *= silu(bf(Zs[t * tld + pl]));
-                    Zs[t * tld + pl] = f32_to_bf16_bits(yv);
-                }
         }
         __syncthreads();  // XWT and Ys (in Zs) complete; every read of HT done
 
-        // ---- outputs leave as 16-byte pieces, one per thread --------------------
-        {
-            const int t = tid / (kPT / 8), c8 = (tid % (kPT / 8)) * 8;
-            const int64_t tt = t0 + t;
-            if (tt < L)
-                *reinterpret_cast<uint4 *>(p.y + ((b * L + tt) * p.H + h) * kP + kPT * pt + c8) =
-                    *reinterpret_cast<const uint4 *>(Zs + t * tld + c8);
+        if constexpr (outputs) {
+            // ---- outputs leave as 16-byte pieces, one per thread --------------------
+            {
+                const int t = tid / (kPT / 8), c8 = (tid % (kPT / 8)) * 8;
+                const int64_t tt = t0 + t;
+                if (tt < L)
+                    *reinterpret_cast<uint4 *>(p.y + ((b * L + tt) * p.H + h) * kP + kPT * pt + c8) =
+                        *reinterpret_cast<const uint4 *>(Zs + t * tld + c8);
+            }
         }
 
         // ---- this wave's state tiles for the next chunk ----------------------------
@@ -495,27 +518,104 @@ __global__ __launch_bounds__(kThreads, 2) void ssd_chunk_kernel(SsdParams p) {
         __syncthreads();  // inputs free for the next chunk; HT holds the new state
     }
 
-    if (p.h_final && owns_state) {
+    // the final state (whole sequence), or a segment's end state and decay
+    float *hout = MODE == 0 ? p.h_final : MODE == 1 ? p.ws_state + seg * p.B * p.H * kP * N : nullptr;
+    if (hout && owns_state) {
 #pragma unroll
         for (int i = 0; i < NWT; ++i)
 #pragma unroll
             for (int j = 0; j < kPTL; ++j)
 #pragma unroll
                 for (int v = 0; v < 4; ++v)
-                    p.h_final[(bh * kP + kPT * pt + 16 * j + r16) * N + 16 * my_nt(i) + q4 + v] = st[i][j][v];
+                    hout[(bh * kP + kPT * pt + 16 * j + r16) * N + 16 * my_nt(i) + q4 + v] = st[i][j][v];
     }
+    if (MODE == 1 && pt == 0 && tid == 0) p.ws_lsum[seg * p.B * p.H + bh] = lsum;
+}
+
+// The segments' entering states: H_0 = h0 (or 0), H_{k+1} = e^{lsum_k} H_k +
+// E_k with E_k segment k's end state from a zero start (exact: the layer is
+// linear in its entering state).  Slot k of the workspace trades E_k for H_k;
+// the last H is the final state.  One thread per state entry.
+__global__ __launch_bounds__(256) void ssd_seg_combine_kernel(float *ws_state, const float *ws_lsum, const float *h0,
+                                                              float *h_final, int64_t BH, int64_t PN, int64_t nseg) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= BH * PN) return;
+    const int64_t bh = i / PN;
+    float hs = h0 ? h0[i] : 0.0f;
+    for (int64_t k = 0; k < nseg; ++k) {
+        float *slot = ws_state + k * BH * PN + i;
+        const float e = *slot;
+        *slot = hs;
+        hs = __expf(ws_lsum[k * BH + bh]) * hs + e;
+    }
+    if (h_final) h_final[i] = hs;
 }
 
 template <int N>
-hipError_t launch_n(const SsdParams &p, int64_t B, int64_t H, hipStream_t stream) {
-    ssd_chunk_kernel<N><<<(unsigned)(B * H * (kP / kPT)), kThreads, SsdLds<N>::total, stream>>>(p);
+hipError_t launch_n(const SsdParams &p, hipStream_t stream) {
+    const unsigned grid = (unsigned)(p.B * p.H * (kP / kPT) * p.nseg);
+    const size_t lds = SsdLds<N>::total;
+    if (p.mode == 1)
+        ssd_chunk_kernel<N, 1><<<grid, kThreads, lds, stream>>>(p);
+    else if (p.mode == 2)
+        ssd_chunk_kernel<N, 2><<<grid, kThreads, lds, stream>>>(p);
+    else
+        ssd_chunk_kernel<N, 0><<<grid, kThreads, lds, stream>>>(p);
     return hipGetLastError();
+}
+
+hipError_t launch_dstate(const SsdParams &p, int64_t N, hipStream_t stream) {
+    switch (N) {
+        case 16: return launch_n<16>(p, stream);
+        case 32: return launch_n<32>(p, stream);
+        case 64: return launch_n<64>(p, stream);
+        default: return launch_n<128>(p, stream);
+    }
+}
+
+// Segments: when the (batch, head, channel half) workgroups would fill at
+// most half of the resident slots (two per CU), the sequence is cut into
+// segments of at least kMinSegChunks chunks, as many as still run in one
+// round (up to kMaxSeg).  The end-state pass and the combine cost about half
+// a pass, so fuller launches are left whole.
+constexpr int64_t kSlotsWanted = 2 * 256;
+constexpr int64_t kMinSegChunks = 4;
+constexpr int64_t kMaxSeg = 64;
+
+struct SsdPlan {
+    int64_t nseg, seg_chunks;
+    size_t ws_state, ws_lsum;
+};
+
+SsdPlan ssd_plan(const ssm_ssd_args_t &a) {
+    SsdPlan q{1, 0, 0, 0};
+    const int64_t nchunks = (a.seqlen + kQ - 1) / kQ;
+    q.seg_chunks = nchunks;
+    const int64_t wgs = a.batch * a.nheads * (kP / kPT);
+    if (wgs > 0 && 2 * wgs <= kSlotsWanted) {
+        int64_t s = std::min<int64_t>({kMaxSeg, kSlotsWanted / wgs, nchunks / kMinSegChunks});
+        if (s > 1) {
+            q.seg_chunks = (nchunks + s - 1) / s;
+            q.nseg = (nchunks + q.seg_chunks - 1) / q.seg_chunks;
+        }
+    }
+    if (q.nseg > 1) {
+        auto r256 = [](size_t v) { return (v + 255) & ~(size_t)255; };
+        q.ws_state = r256((size_t)(q.nseg * a.batch * a.nheads * kP * a.dstate) * sizeof(float));
+        q.ws_lsum = r256((size_t)(q.nseg * a.batch * a.nheads) * sizeof(float));
+    }
+    return q;
 }
 
 }  // namespace
 
 bool ssd_supported(int64_t headdim, int64_t dstate) {
     return headdim == kP && (dstate == 16 || dstate == 32 || dstate == 64 || dstate == 128);
+}
+
+size_t ssd_workspace_bytes(const ssm_ssd_args_t &a) {
+    const SsdPlan q = ssd_plan(a);
+    return q.ws_state + q.ws_lsum;
 }
 
 hipError_t launch_ssd_fwd(const ssm_ssd_args_t &a, hipStream_t stream) {
@@ -536,12 +636,28 @@ hipError_t launch_ssd_fwd(const ssm_ssd_args_t &a, hipStream_t stream) {
     p.y = static_cast<uint16_t *>(a.y);
     p.h_final = a.h_final;
     p.softplus = a.delta_softplus;
-    switch (a.dstate) {
-        case 16: return launch_n<16>(p, a.batch, a.nheads, stream);
-        case 32: return launch_n<32>(p, a.batch, a.nheads, stream);
-        case 64: return launch_n<64>(p, a.batch, a.nheads, stream);
-        default: return launch_n<128>(p, a.batch, a.nheads, stream);
+    const SsdPlan q = ssd_plan(a);
+    p.nseg = q.nseg;
+    p.seg_chunks = q.seg_chunks;
+    p.ws_state = nullptr;
+    p.ws_lsum = nullptr;
+    if (q.nseg <= 1) {
+        p.mode = 0;
+        return launch_dstate(p, a.dstate, stream);
     }
+    char *ws = static_cast<char *>(a.workspace);
+    p.ws_state = reinterpret_cast<float *>(ws);
+    p.ws_lsum = reinterpret_cast<float *>(ws + q.ws_state);
+    p.mode = 1;
+    hipError_t e = launch_dstate(p, a.dstate, stream);
+    if (e != hipSuccess) return e;
+    const int64_t BH = a.batch * a.nheads, PN = kP * a.dstate;
+    ssd_seg_combine_kernel<<<(unsigned)((BH * PN + 255) / 256), 256, 0, stream>>>(p.ws_state, p.ws_lsum, a.h0,
+                                                                                 a.h_final, BH, PN, q.nseg);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    p.mode = 2;
+    return launch_dstate(p, a.dstate, stream);
 }
 
 }  // namespace ssm

@@ -445,7 +445,8 @@ ssm_status_t ssm_block_fwd(const ssm_block_plan_t *plan, const ssm_block_weights
     return ok();
 }
 
-ssm_status_t ssm_ssd_fwd(const ssm_ssd_args_t *a, void *stream) {
+namespace {
+ssm_status_t check_ssd_sizes(const ssm_ssd_args_t *a) {
     if (!a) return fail(SSM_ERR_NULL_ARG, "args is NULL");
     if (a->io_dtype != SSM_F32 && a->io_dtype != SSM_BF16)
         return fail(SSM_ERR_BAD_DTYPE, "io_dtype %d is not SSM_F32 or SSM_BF16", a->io_dtype);
@@ -467,6 +468,22 @@ ssm_status_t ssm_ssd_fwd(const ssm_ssd_args_t *a, void *stream) {
     // one workgroup of 256 threads per (batch, head, 32 channels): the launch holds < 2^32 threads
     if (B * H > ((int64_t)1 << 22))
         return fail(SSM_ERR_UNSUPPORTED, "batch * nheads (%lld) exceeds 2^22", (long long)(B * H));
+    return SSM_OK;
+}
+}  // namespace
+
+size_t ssm_ssd_workspace_size(const ssm_ssd_args_t *a) {
+    if (check_ssd_sizes(a) != SSM_OK) return (size_t)-1;
+    if (a->batch == 0 || a->seqlen == 0) return 0;
+    return ssm::ssd_workspace_bytes(*a);
+}
+
+ssm_status_t ssm_ssd_fwd(const ssm_ssd_args_t *a, void *stream) {
+    {
+        const ssm_status_t s = check_ssd_sizes(a);
+        if (s != SSM_OK) return s;
+    }
+    const int64_t B = a->batch, L = a->seqlen, H = a->nheads, P = a->headdim, G = a->ngroups, N = a->dstate;
     if (!a->A) return fail(SSM_ERR_NULL_ARG, "A is required");
     if (B * L > 0 && (!a->x || !a->delta || !a->Bm || !a->Cm || !a->y))
         return fail(SSM_ERR_NULL_ARG, "x, delta, Bm, Cm and y are required");
@@ -489,6 +506,17 @@ ssm_status_t ssm_ssd_fwd(const ssm_ssd_args_t *a, void *stream) {
     }
     if (overlaps(y, hf)) return fail(SSM_ERR_ALIAS, "h_final overlaps y");
     if (B == 0) return ok();
+    const size_t need = L > 0 ? ssm::ssd_workspace_bytes(*a) : 0;
+    if (need > 0) {
+        if (!a->workspace) return fail(SSM_ERR_WORKSPACE, "workspace of %zu bytes required", need);
+        if (a->workspace_bytes < need)
+            return fail(SSM_ERR_WORKSPACE, "workspace has %zu bytes, %zu required", a->workspace_bytes, need);
+        if (!aligned(a->workspace, 256)) return fail(SSM_ERR_WORKSPACE, "workspace is not 256-byte aligned");
+        const Range ws = range(a->workspace, (int64_t)need, 1, "workspace");
+        for (const Range &r : inputs)
+            if (overlaps(ws, r)) return fail(SSM_ERR_ALIAS, "workspace overlaps %s", r.name);
+        if (overlaps(ws, y) || overlaps(ws, hf)) return fail(SSM_ERR_ALIAS, "workspace overlaps an output");
+    }
     const hipError_t e = ssm::launch_ssd_fwd(*a, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(SSM_ERR_HIP, "HIP error: %s", hipGetErrorString(e));
     return ok();

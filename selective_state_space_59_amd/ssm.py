@@ -38,7 +38,7 @@ EXPORTED_SYMBOLS = ("ssm_selective_scan_workspace_size", "ssm_selective_scan_fwd
                     "ssm_last_error_message", "ssm_abi_version",
                     "ssm_selective_scan_bwd_workspace_size", "ssm_selective_scan_bwd",
                     "ssm_block_plan_create", "ssm_block_workspace_size", "ssm_block_fwd",
-                    "ssm_block_plan_destroy", "ssm_ssd_fwd")
+                    "ssm_block_plan_destroy", "ssm_ssd_fwd", "ssm_ssd_workspace_size")
 
 _P = ctypes.c_void_p
 _I64 = ctypes.c_int64
@@ -95,7 +95,8 @@ class SsdArgs(ctypes.Structure):
     _fields_ = [("batch", _I64), ("seqlen", _I64), ("nheads", _I64), ("headdim", _I64),
                 ("ngroups", _I64), ("dstate", _I64), ("io_dtype", _I32), ("delta_softplus", _I32),
                 ("x", _P), ("delta", _P), ("A", _P), ("Bm", _P), ("Cm", _P), ("Dskip", _P),
-                ("z", _P), ("delta_bias", _P), ("h0", _P), ("y", _P), ("h_final", _P)]
+                ("z", _P), ("delta_bias", _P), ("h0", _P), ("y", _P), ("h_final", _P),
+                ("workspace", _P), ("workspace_bytes", ctypes.c_size_t)]
 
 
 class SSMError(RuntimeError):
@@ -143,6 +144,8 @@ def lib() -> ctypes.CDLL:
         L.ssm_block_plan_destroy.restype = None
         L.ssm_ssd_fwd.argtypes = [ctypes.POINTER(SsdArgs), _P]
         L.ssm_ssd_fwd.restype = ctypes.c_int
+        L.ssm_ssd_workspace_size.argtypes = [ctypes.POINTER(SsdArgs)]
+        L.ssm_ssd_workspace_size.restype = ctypes.c_size_t
         _lib = L
     return _lib
 
@@ -553,6 +556,13 @@ def ssd_fwd(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, Bm: torch.Ten
     a = SsdArgs(batch=Bsz, seqlen=L, nheads=H, headdim=P, ngroups=G, dstate=N, io_dtype=SSM_BF16,
                 delta_softplus=int(bool(delta_softplus)), x=_ptr(x), delta=_ptr(delta), A=_ptr(A),
                 Bm=_ptr(Bm), Cm=_ptr(Cm), Dskip=_ptr(Dskip), z=_ptr(z), delta_bias=_ptr(delta_bias),
-                h0=_ptr(h0), y=_ptr(y), h_final=_ptr(h_final))
+                h0=_ptr(h0), y=_ptr(y), h_final=_ptr(h_final), workspace=None, workspace_bytes=0)
+    need = lib().ssm_ssd_workspace_size(ctypes.byref(a))
+    if need == ctypes.c_size_t(-1).value:
+        _check(lib().ssm_ssd_fwd(ctypes.byref(a), _stream(dev)), "ssm_ssd_fwd")  # reports the error
+    if need:
+        ws = _workspace(dev, need)
+        a.workspace = ws.data_ptr()
+        a.workspace_bytes = ws.numel()
     _check(lib().ssm_ssd_fwd(ctypes.byref(a), _stream(dev)), "ssm_ssd_fwd")
     return (y, h_final) if h_final is not None else y

@@ -118,6 +118,9 @@ class SsdConfig:
 # The 130M-like width (D = 1536 = 24 heads x 64) with the Mamba-2 state size N = 128,
 # at the batch and length of the 130M-like scan.
 S2_MAMBA2_130M = SsdConfig("s2_mamba2_130m_ssd", 8, 2048, 24, 64, 1, 128, seed=31)
+# One long sequence at the same width: too few (batch, head) pairs to fill the GPU
+# alone, so the layer runs as sequence segments.
+S4_MAMBA2_LONG = SsdConfig("s4_mamba2_long_b1", 1, 65536, 24, 64, 1, 128, seed=32)
 
 
 def _gen(device, seed: int) -> torch.Generator:

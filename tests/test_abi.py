@@ -446,6 +446,24 @@ def test_ssd_rejects_bad_arguments(field, value, status):
     assert run_ssd(ssd_args(**{field: value})) == status
 
 
+def test_ssd_workspace_checks():
+    L = ssm.lib()
+    # few (batch, head) pairs and a long sequence: segments, so a workspace
+    a = ssd_args(batch=1, nheads=2, seqlen=4096, h_final=addr(8), workspace=None)
+    need = L.ssm_ssd_workspace_size(ctypes.byref(a))
+    assert 0 < need < (1 << 30)
+    assert run_ssd(a) == ssm.SSM_ERR_WORKSPACE
+    a.workspace, a.workspace_bytes = addr(9), need - 1
+    assert run_ssd(a) == ssm.SSM_ERR_WORKSPACE
+    a.workspace, a.workspace_bytes = addr(9, 16), need
+    assert run_ssd(a) == ssm.SSM_ERR_WORKSPACE          # not 256-aligned
+    a.workspace = addr(0)
+    assert run_ssd(a) == ssm.SSM_ERR_ALIAS              # == x
+    # enough (batch, head) pairs: one pass, no workspace
+    assert L.ssm_ssd_workspace_size(ctypes.byref(ssd_args(batch=8, nheads=64, seqlen=4096))) == 0
+    assert L.ssm_ssd_workspace_size(ctypes.byref(ssd_args(dstate=100))) == ctypes.c_size_t(-1).value
+
+
 def test_ssd_empty_batch_is_a_noop():
     assert run_ssd(ssd_args(batch=0)) == ssm.SSM_OK
     assert run_ssd(ssd_args(batch=0, seqlen=0)) == ssm.SSM_OK

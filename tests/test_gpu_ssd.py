@@ -58,6 +58,10 @@ CASES = [
     ("no_gate_no_skip", 2, 64, 2, 1, 64, dict(gate=False, skip=False)),
     ("l1", 2, 1, 3, 1, 128, dict(h0=True)),
     ("long_n128", 1, 1000, 2, 1, 128, {}),
+    # few (batch, head) pairs: the sequence runs as segments (end states, combine, outputs)
+    ("segments_h0_n64", 1, 3000, 2, 1, 64, dict(h0=True)),
+    ("segments_groups_n128", 1, 1100, 4, 2, 128, dict(h0=True)),
+    ("segments_n16", 2, 2500, 1, 1, 16, {}),
 ]
 
 
@@ -79,6 +83,19 @@ def test_ssd_softplus_bias_zero_and_positive_A():
     inp["delta"] = (torch.randn(1, 150, 4, device=DEV, generator=g) - 1.0).to(torch.bfloat16)
     bias = 0.5 * torch.randn(4, device=DEV, generator=g)
     inp["A"] = torch.tensor([-1.5, 0.0, 0.05, -8.0], device=DEV)
+    y, hf = _run(inp, softplus=True, bias=bias)
+    yr, hr = _oracle(inp, softplus=True, bias=bias)
+    assert_close(to64(y), yr, TOL_BF16, "y")
+    assert_close(to64(hf), hr, TOL_BF16, "h_final")
+
+
+def test_ssd_segments_softplus_bias():
+    """Segmented run with the softplus step and a bias (rows past the end of the last chunk
+    must not move the state)."""
+    inp = W.make_ssd_inputs(1, 2049, 2, 64, 1, 32, seed=854, device=DEV, h0=True)
+    g = torch.Generator(DEV).manual_seed(10)
+    inp["delta"] = (torch.randn(1, 2049, 2, device=DEV, generator=g) - 2.0).to(torch.bfloat16)
+    bias = 0.5 * torch.randn(2, device=DEV, generator=g)
     y, hf = _run(inp, softplus=True, bias=bias)
     yr, hr = _oracle(inp, softplus=True, bias=bias)
     assert_close(to64(y), yr, TOL_BF16, "y")
@@ -108,6 +125,22 @@ def test_ssd_state_handover_equals_one_pass():
     yr, hr = _oracle(inp)
     assert_close(to64(torch.cat([y1, y2], 1)), yr, TOL_BF16, "y in two calls")
     assert_close(to64(h2), hr, TOL_BF16, "h_final in two calls")
+
+
+def test_ssd_long_single_sequence_sampled_head():
+    """One 65536-token sequence (24 heads, N = 128): the segmented schedule at full size;
+    the oracle checks head 17 over the whole sequence."""
+    cfg = W.S4_MAMBA2_LONG
+    print("config", cfg.name, flush=True)
+    inp = W.make_ssd_config_inputs(cfg, device=DEV)
+    y, hf = _run(inp)
+    h = 17
+    yr, hr = _oracle(inp, b=slice(0, 1), h=slice(h, h + 1))
+    wy = assert_close(to64(y[:, :, h:h + 1]), yr, TOL_BF16, "y head %d" % h)
+    wh = assert_close(to64(hf[:, h:h + 1]), hr, TOL_BF16, "h_final head %d" % h)
+    print("  head %d worst y %.2e, h_final %.2e" % (h, wy, wh), flush=True)
+    del inp, y, hf
+    torch.cuda.empty_cache()
 
 
 def test_ssd_mamba2_130m_like_sampled_heads():
