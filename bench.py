@@ -320,6 +320,67 @@ def ssd_entry(cfg, steps, warmup):
                             io_dtype="bf16", chunk=64))
 
 
+def ssd_step_algorithmic(cfg):
+    """HBM bytes of one SSD decode step over the batch: the fp32 state read and written
+    (B*H*P*N each), x, z read and y written (bf16, B*H*P each), delta (B*H) and B, C
+    (B*G*N each) read, A and D (fp32, H each)."""
+    B, H, P, G, N = cfg.batch, cfg.nheads, cfg.headdim, cfg.ngroups, cfg.dstate
+    return 2 * 4 * B * H * P * N + 3 * 2 * B * H * P + 2 * B * H + 2 * 2 * B * G * N + 2 * 4 * H
+
+
+def bench_ssd_step(cfg, reps=10):
+    """`cfg.seqlen` decode steps of the SSD layer on a resident state: hot (steps back to
+    back, per step) and cold (the last-level cache flushed before each timed step)."""
+    import torch
+    import selective_state_space_59_amd as ssm
+    from selective_state_space_59_amd import workloads as W
+    dev = "cuda:0"
+    s = W.make_ssd_config_inputs(cfg, device=dev, h0=True)
+    per_step = {k: s[k].transpose(0, 1).contiguous() for k in ("x", "delta", "Bm", "Cm", "z")}
+    st = s["h0"]
+    ys = torch.empty_like(per_step["x"])
+    T = cfg.seqlen
+
+    def step(t):
+        ssm.ssd_step(st, per_step["x"][t], per_step["delta"][t], s["A"], per_step["Bm"][t],
+                     per_step["Cm"][t], Dskip=s["Dskip"], z=per_step["z"][t], y=ys[t])
+
+    def run_all(_):
+        for t in range(T):
+            step(t)
+
+    hot_ms = time_launches(run_all, reps, 1) / T
+    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    cold = []
+    for t in range(T):
+        flush.fill_(float(t))
+        start.record()
+        step(t)
+        stop.record()
+        torch.cuda.synchronize()
+        cold.append(start.elapsed_time(stop))
+    cold.sort()
+    cold_ms = cold[len(cold) // 2]
+    del s, per_step, st, ys, flush
+    torch.cuda.empty_cache()
+    return hot_ms, cold_ms
+
+
+def ssd_step_entry(cfg):
+    hot, cold = bench_ssd_step(cfg)
+    db = ssd_step_algorithmic(cfg)
+    return dict(hot_ms_per_step=round(hot, 5), cold_ms_per_step=round(cold, 5),
+                hot_tokens_per_s=round(cfg.batch * 1e3 / hot, 1),
+                cold_gbs=round(db / (cold * 1e-3) / 1e9, 2),
+                cold_frac_hbm=round(db / (cold * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                hot_gbs=round(db / (hot * 1e-3) / 1e9, 2), algorithmic_bytes_per_step=db,
+                config=dict(batch=cfg.batch, nheads=cfg.nheads, headdim=cfg.headdim,
+                            ngroups=cfg.ngroups, dstate=cfg.dstate, steps=cfg.seqlen,
+                            io_dtype="bf16", state_dtype="f32"))
+
+
 def block_entry(cfg, steps, warmup):
     ms = bench_block(cfg, steps, warmup)
     fl = block_gemm_flops(cfg)
@@ -338,9 +399,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--no-extras", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=("block", "ssd", "ssd_long"),
+    ap.add_argument("--only", choices=("block", "ssd", "ssd_long", "ssd_decode"),
                     help="only time the 130M-like Mamba block forward, the Mamba-2 130M-like "
-                         "SSD layer, or that layer on one 65536-token sequence, and print its numbers")
+                         "SSD layer, that layer on one 65536-token sequence, or the 2.7B-like "
+                         "SSD decode step, and print its numbers")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (fp32) five times; its "
                          "FETCH_SIZE / WRITE_SIZE counters scale the scan's traffic counters")
@@ -372,6 +434,10 @@ def main():
     if args.only in ("ssd", "ssd_long"):
         c = W.S2_MAMBA2_130M if args.only == "ssd" else W.S4_MAMBA2_LONG
         print(json.dumps({c.name: ssd_entry(c, args.steps, args.warmup)}), flush=True)
+        return
+    if args.only == "ssd_decode":
+        c = W.S5_MAMBA2_DECODE
+        print(json.dumps({c.name: ssd_step_entry(c)}), flush=True)
         return
 
     cfg = W.C2_130M
@@ -454,6 +520,9 @@ def main():
         # one 65536-token sequence at that width: the segmented schedule
         print("bench extra: %s" % W.S4_MAMBA2_LONG.name, file=sys.stderr, flush=True)
         extra[W.S4_MAMBA2_LONG.name] = ssd_entry(W.S4_MAMBA2_LONG, 10, 2)
+        # decode steps of a 2.7B-like Mamba-2 layer on its resident fp32 state
+        print("bench extra: %s" % W.S5_MAMBA2_DECODE.name, file=sys.stderr, flush=True)
+        extra[W.S5_MAMBA2_DECODE.name] = ssd_step_entry(W.S5_MAMBA2_DECODE)
         out["extra"] = extra
 
     if not args.no_cpu_baseline:

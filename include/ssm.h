@@ -10,7 +10,8 @@
  *   - ssm_causal_conv1d_silu: the conv prologue on its own;
  *   - ssm_selective_scan_bwd: the gradients of the scan (training);
  *   - ssm_block_fwd: a whole Mamba block around the scan (with a plan);
- *   - ssm_ssd_fwd: the SSD (Mamba-2) layer, chunked on the matrix cores.
+ *   - ssm_ssd_fwd: the SSD (Mamba-2) layer, chunked on the matrix cores;
+ *   - ssm_ssd_step: one decode step of that layer on a resident state.
  *
  * The operations are defined on these pages (cited by title and section):
  *   [P1] "Mamba: Linear-Time Sequence Modeling with Selective State Spaces"
@@ -62,7 +63,7 @@
 extern "C" {
 #endif
 
-#define SSM_ABI_VERSION 6
+#define SSM_ABI_VERSION 7
 #define SSM_MAX_DSTATE 16 /* largest N the kernels hold in registers */
 #define SSM_MAX_CONV_K 4  /* largest conv1d kernel width */
 
@@ -396,6 +397,34 @@ size_t ssm_ssd_workspace_size(const ssm_ssd_args_t *args);
  * the (B,L,...) pointers may then be NULL.
  */
 ssm_status_t ssm_ssd_fwd(const ssm_ssd_args_t *args, void *stream);
+
+/*
+ * One decode step of the SSD layer: the recurrence above for a single token
+ * on a state kept between calls (updated IN PLACE), for every batch b, head
+ * h, head channel p and state entry n (g = h / (H / G)):
+ *   dt = delta[b,h] (or softplus(delta[b,h] + delta_bias[h]))
+ *   state[b,h,p,n] <- exp(dt A[h]) state[b,h,p,n] + w(dt, A[h]) Bm[b,g,n] x[b,h,p]
+ *   y[b,h,p] = (sum_n Cm[b,g,n] state[b,h,p,n] + Dskip[h] x[b,h,p]) * silu(z[b,h,p])
+ * with w the ZOH weight of ssm_ssd_fwd; the state layout is that function's
+ * h0/h_final, so a prefill hands over to decode directly.  bf16 I/O; any
+ * head dim; dstate a power of two from 4 to 256.
+ */
+typedef struct ssm_ssd_step_args {
+    int64_t batch, nheads, headdim, ngroups, dstate; /* B >= 0, H, P, G | H, N */
+    int32_t io_dtype;       /* SSM_BF16                                        */
+    int32_t delta_softplus; /* as in ssm_ssd_args_t                            */
+    float *state;           /* (B,H,P,N) fp32, updated in place; 16-byte aligned */
+    const void *x;          /* (B,H,P) bf16, required                          */
+    const void *delta;      /* (B,H) bf16, required                            */
+    const float *A;         /* (H) fp32, required                              */
+    const void *Bm, *Cm;    /* (B,G,N) bf16, required; 8-byte aligned          */
+    const float *Dskip;     /* (H) fp32, or NULL                               */
+    const void *z;          /* (B,H,P) bf16 gate, or NULL                      */
+    const float *delta_bias;/* (H) fp32, or NULL                               */
+    void *y;                /* (B,H,P) bf16 output; must not overlap any input or the state */
+} ssm_ssd_step_args_t;
+
+ssm_status_t ssm_ssd_step(const ssm_ssd_step_args_t *args, void *stream);
 
 /* Static description of a status code (never NULL). */
 const char *ssm_status_string(ssm_status_t status);

@@ -607,7 +607,146 @@ SsdPlan ssd_plan(const ssm_ssd_args_t &a) {
     return q;
 }
 
+// ---- decode: one token on a resident state -----------------------------------
+//
+// The same layer in recurrent mode for one step: per (batch, head, channel p)
+// the state row S[p, :] (N fp32) becomes alpha S + w x B and y = (S . C +
+// D x) silu(z).  A workgroup takes 2 * 256 / (N / 4) channels of one (batch,
+// head), so the step, its decay and weight, and the B and C rows are the same
+// for all of its lanes; each lane owns 4 consecutive state entries of one
+// channel in each of two rounds (16 bytes, loaded and stored once, both loads
+// issued first) and the N / 4 lanes of a channel, one aligned lane group, sum
+// their partial S . C by xor shuffles.  Bound by moving the fp32 state
+// through HBM.
+struct SsdStepParams {
+    int64_t B, H, P, G;
+    const uint16_t *x, *delta, *Bm, *Cm, *z;
+    const float *A, *Dskip, *dbias;
+    float *state;
+    uint16_t *y;
+    int softplus;
+};
+
+constexpr int kStepRounds = 2;
+
+// Tile t: channels [tile * 2 CPR, (tile + 1) * 2 CPR) of (batch, head) bh, t = bh * ntiles + tile.
+template <int Q4>  // lanes per channel: N = 4 Q4
+__device__ __forceinline__ void ssd_step_tile(const SsdStepParams &p, int64_t t, int64_t ntiles) {
+    constexpr int N = 4 * Q4;
+    constexpr int CPR = 256 / Q4;  // channels per round
+    typedef float f4v __attribute__((ext_vector_type(4)));
+    const int64_t bh = t / ntiles;
+    const int64_t tile = t - bh * ntiles;
+    const int64_t h = bh % p.H, b = bh / p.H;
+    const int64_t grp = h / (p.H / p.G);
+    const int q = threadIdx.x % Q4;
+    const int c0 = threadIdx.x / Q4;
+    f4v s[kStepRounds];
+    int64_t pch[kStepRounds];
+#pragma unroll
+    for (int r = 0; r < kStepRounds; ++r) {
+        pch[r] = tile * (kStepRounds * CPR) + r * CPR + c0;
+        const int64_t pc = pch[r] < p.P ? pch[r] : 0;
+        s[r] = __builtin_nontemporal_load(reinterpret_cast<const f4v *>(p.state + (bh * p.P + pc) * N + 4 * q));
+    }
+    const uint2 bq = *reinterpret_cast<const uint2 *>(p.Bm + (b * p.G + grp) * N + 4 * q);
+    const uint2 cq = *reinterpret_cast<const uint2 *>(p.Cm + (b * p.G + grp) * N + 4 * q);
+    float dt = bf(p.delta[bh]);
+    if (p.softplus) dt = softplus_fast(dt + (p.dbias ? p.dbias[h] : 0.0f));
+    const float za = dt * p.A[h];
+    const float e = hw_exp2(za * kLog2e);  // decay of the step
+    const float wdt = dt * ssd_phi(za, e);  // ZOH input weight
+    const float dsk = p.Dskip ? p.Dskip[h] : 0.0f;
+    const float bv[4] = {__uint_as_float(bq.x << 16), __uint_as_float(bq.x & 0xffff0000u),
+                         __uint_as_float(bq.y << 16), __uint_as_float(bq.y & 0xffff0000u)};
+    const float cv[4] = {__uint_as_float(cq.x << 16), __uint_as_float(cq.x & 0xffff0000u),
+                         __uint_as_float(cq.y << 16), __uint_as_float(cq.y & 0xffff0000u)};
+#pragma unroll
+    for (int r = 0; r < kStepRounds; ++r) {
+        const bool live = pch[r] < p.P;
+        const int64_t ch = bh * p.P + (live ? pch[r] : 0);
+        const float u = bf(p.x[ch]);
+        const float wu = wdt * u;
+        float hn[4];
+        float part = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            hn[i] = __builtin_fmaf(e, s[r][i], wu * bv[i]);
+            part = __builtin_fmaf(hn[i], cv[i], part);
+        }
+#pragma unroll
+        for (int m = Q4 / 2; m >= 1; m /= 2) part += __shfl_xor(part, m, 64);
+        if (live) {
+            const f4v o = {hn[0], hn[1], hn[2], hn[3]};
+            __builtin_nontemporal_store(o, reinterpret_cast<f4v *>(p.state + ch * N + 4 * q));
+            if (q == 0) {
+                float yv = part + dsk * u;
+                if (p.z) yv *= silu(bf(p.z[ch]));
+                p.y[ch] = f32_to_bf16_bits(yv);
+            }
+        }
+    }
+}
+
+// One tile per workgroup; a loop over tiles where there are more than one grid
+// takes (a loop costs ~9% of the step even when it runs once, so it is kept out
+// of the common case).
+template <int Q4, bool LOOP>
+__global__ __launch_bounds__(256) void ssd_step_kernel(SsdStepParams p, int64_t ntiles, int64_t total) {
+    if (!LOOP) {
+        ssd_step_tile<Q4>(p, blockIdx.x, ntiles);
+        return;
+    }
+    for (int64_t t = blockIdx.x; t < total; t += gridDim.x) ssd_step_tile<Q4>(p, t, ntiles);
+}
+
+constexpr int64_t kStepMaxGrid = (int64_t)1 << 22;
+
+template <int Q4>
+void launch_step_q4(const SsdStepParams &p, hipStream_t stream) {
+    const int64_t per_tile = kStepRounds * (256 / Q4);
+    const int64_t ntiles = (p.P + per_tile - 1) / per_tile;
+    const int64_t total = p.B * p.H * ntiles;
+    if (total <= kStepMaxGrid)
+        ssd_step_kernel<Q4, false><<<(unsigned)total, 256, 0, stream>>>(p, ntiles, total);
+    else
+        ssd_step_kernel<Q4, true><<<(unsigned)kStepMaxGrid, 256, 0, stream>>>(p, ntiles, total);
+}
+
 }  // namespace
+
+bool ssd_step_supported(int64_t dstate) {
+    return dstate >= 4 && dstate <= 256 && (dstate & (dstate - 1)) == 0;
+}
+
+hipError_t launch_ssd_step(const ssm_ssd_step_args_t &a, hipStream_t stream) {
+    SsdStepParams p;
+    p.B = a.batch;
+    p.H = a.nheads;
+    p.P = a.headdim;
+    p.G = a.ngroups;
+    p.x = static_cast<const uint16_t *>(a.x);
+    p.delta = static_cast<const uint16_t *>(a.delta);
+    p.Bm = static_cast<const uint16_t *>(a.Bm);
+    p.Cm = static_cast<const uint16_t *>(a.Cm);
+    p.z = static_cast<const uint16_t *>(a.z);
+    p.A = a.A;
+    p.Dskip = a.Dskip;
+    p.dbias = a.delta_bias;
+    p.state = a.state;
+    p.y = static_cast<uint16_t *>(a.y);
+    p.softplus = a.delta_softplus;
+    switch (a.dstate / 4) {
+        case 1: launch_step_q4<1>(p, stream); break;
+        case 2: launch_step_q4<2>(p, stream); break;
+        case 4: launch_step_q4<4>(p, stream); break;
+        case 8: launch_step_q4<8>(p, stream); break;
+        case 16: launch_step_q4<16>(p, stream); break;
+        case 32: launch_step_q4<32>(p, stream); break;
+        default: launch_step_q4<64>(p, stream); break;
+    }
+    return hipGetLastError();
+}
 
 bool ssd_supported(int64_t headdim, int64_t dstate) {
     return headdim == kP && (dstate == 16 || dstate == 32 || dstate == 64 || dstate == 128);

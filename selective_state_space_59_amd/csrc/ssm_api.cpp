@@ -522,4 +522,47 @@ ssm_status_t ssm_ssd_fwd(const ssm_ssd_args_t *a, void *stream) {
     return ok();
 }
 
+ssm_status_t ssm_ssd_step(const ssm_ssd_step_args_t *a, void *stream) {
+    if (!a) return fail(SSM_ERR_NULL_ARG, "args is NULL");
+    if (a->io_dtype != SSM_F32 && a->io_dtype != SSM_BF16)
+        return fail(SSM_ERR_BAD_DTYPE, "io_dtype %d is not SSM_F32 or SSM_BF16", a->io_dtype);
+    if (a->batch < 0) return fail(SSM_ERR_BAD_SHAPE, "negative batch");
+    if (a->nheads < 1 || a->headdim < 1 || a->ngroups < 1 || a->dstate < 1)
+        return fail(SSM_ERR_BAD_SHAPE, "nheads, headdim, ngroups and dstate must be >= 1");
+    if (a->nheads % a->ngroups != 0) return fail(SSM_ERR_BAD_SHAPE, "ngroups must divide nheads");
+    if (a->io_dtype != SSM_BF16) return fail(SSM_ERR_UNSUPPORTED, "the SSD step takes bf16 I/O");
+    if (!ssm::ssd_step_supported(a->dstate))
+        return fail(SSM_ERR_UNSUPPORTED, "dstate must be a power of two from 4 to 256 (got %lld)",
+                    (long long)a->dstate);
+    if (a->delta_softplus != 0 && a->delta_softplus != 1)
+        return fail(SSM_ERR_UNSUPPORTED, "delta_softplus must be 0 or 1");
+    const int64_t B = a->batch, H = a->nheads, P = a->headdim, G = a->ngroups, N = a->dstate;
+    if (!mul_ok(B, H, P * N) || B * H * P * (N / 4) > ((int64_t)1 << 31))
+        return fail(SSM_ERR_BAD_SHAPE, "sizes out of range (B*H*P*N/4 <= 2^31)");
+    if (B == 0) return ok();
+    if (!a->state || !a->x || !a->delta || !a->A || !a->Bm || !a->Cm || !a->y)
+        return fail(SSM_ERR_NULL_ARG, "state, x, delta, A, Bm, Cm and y are required");
+    if (!aligned(a->state, 16)) return fail(SSM_ERR_ALIGN, "state must be 16-byte aligned");
+    if (!aligned(a->Bm, 8) || !aligned(a->Cm, 8)) return fail(SSM_ERR_ALIGN, "Bm and Cm must be 8-byte aligned");
+    const void *a2[] = {a->x, a->delta, a->z, a->y};
+    for (const void *v : a2)
+        if (!aligned(v, 2)) return fail(SSM_ERR_ALIGN, "bf16 tensors must be 2-byte aligned");
+    const void *a4[] = {a->A, a->Dskip, a->delta_bias};
+    for (const void *v : a4)
+        if (!aligned(v, 4)) return fail(SSM_ERR_ALIGN, "fp32 tensors must be 4-byte aligned");
+    const Range inputs[] = {range(a->x, B * H * P, 2, "x"), range(a->delta, B * H, 2, "delta"),
+                            range(a->A, H, 4, "A"), range(a->Bm, B * G * N, 2, "Bm"),
+                            range(a->Cm, B * G * N, 2, "Cm"), range(a->Dskip, H, 4, "Dskip"),
+                            range(a->z, B * H * P, 2, "z"), range(a->delta_bias, H, 4, "delta_bias")};
+    const Range st = range(a->state, B * H * P * N, 4, "state"), y = range(a->y, B * H * P, 2, "y");
+    for (const Range &r : inputs) {
+        if (overlaps(st, r)) return fail(SSM_ERR_ALIAS, "state overlaps %s", r.name);
+        if (overlaps(y, r)) return fail(SSM_ERR_ALIAS, "y overlaps %s", r.name);
+    }
+    if (overlaps(y, st)) return fail(SSM_ERR_ALIAS, "y overlaps the state");
+    const hipError_t e = ssm::launch_ssd_step(*a, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(SSM_ERR_HIP, "HIP error: %s", hipGetErrorString(e));
+    return ok();
+}
+
 }  // extern "C"

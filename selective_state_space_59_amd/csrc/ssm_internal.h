@@ -40,6 +40,8 @@ hipError_t launch_block_fwd(const ssm_block_plan &p, const ssm_block_weights_t &
 // SSD (Mamba-2) layer (ssd.hip).  a.batch > 0; sizes checked by ssd_supported.
 bool ssd_supported(int64_t headdim, int64_t dstate);
 size_t ssd_workspace_bytes(const ssm_ssd_args_t &a);
+bool ssd_step_supported(int64_t dstate);
+hipError_t launch_ssd_step(const ssm_ssd_step_args_t &a, hipStream_t stream);
 hipError_t launch_ssd_fwd(const ssm_ssd_args_t &a, hipStream_t stream);
 
 // Copy or zero-fill the final state for an empty (L == 0) scan.

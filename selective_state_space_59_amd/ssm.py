@@ -38,7 +38,8 @@ EXPORTED_SYMBOLS = ("ssm_selective_scan_workspace_size", "ssm_selective_scan_fwd
                     "ssm_last_error_message", "ssm_abi_version",
                     "ssm_selective_scan_bwd_workspace_size", "ssm_selective_scan_bwd",
                     "ssm_block_plan_create", "ssm_block_workspace_size", "ssm_block_fwd",
-                    "ssm_block_plan_destroy", "ssm_ssd_fwd", "ssm_ssd_workspace_size")
+                    "ssm_block_plan_destroy", "ssm_ssd_fwd", "ssm_ssd_workspace_size",
+                    "ssm_ssd_step")
 
 _P = ctypes.c_void_p
 _I64 = ctypes.c_int64
@@ -99,6 +100,14 @@ class SsdArgs(ctypes.Structure):
                 ("workspace", _P), ("workspace_bytes", ctypes.c_size_t)]
 
 
+class SsdStepArgs(ctypes.Structure):
+    """Mirror of ssm_ssd_step_args_t."""
+    _fields_ = [("batch", _I64), ("nheads", _I64), ("headdim", _I64), ("ngroups", _I64),
+                ("dstate", _I64), ("io_dtype", _I32), ("delta_softplus", _I32), ("state", _P),
+                ("x", _P), ("delta", _P), ("A", _P), ("Bm", _P), ("Cm", _P), ("Dskip", _P),
+                ("z", _P), ("delta_bias", _P), ("y", _P)]
+
+
 class SSMError(RuntimeError):
     def __init__(self, status: int, message: str):
         super().__init__(message)
@@ -145,6 +154,8 @@ def lib() -> ctypes.CDLL:
         L.ssm_ssd_fwd.argtypes = [ctypes.POINTER(SsdArgs), _P]
         L.ssm_ssd_fwd.restype = ctypes.c_int
         L.ssm_ssd_workspace_size.argtypes = [ctypes.POINTER(SsdArgs)]
+        L.ssm_ssd_step.argtypes = [ctypes.POINTER(SsdStepArgs), _P]
+        L.ssm_ssd_step.restype = ctypes.c_int
         L.ssm_ssd_workspace_size.restype = ctypes.c_size_t
         _lib = L
     return _lib
@@ -566,3 +577,38 @@ def ssd_fwd(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, Bm: torch.Ten
         a.workspace_bytes = ws.numel()
     _check(lib().ssm_ssd_fwd(ctypes.byref(a), _stream(dev)), "ssm_ssd_fwd")
     return (y, h_final) if h_final is not None else y
+
+
+def ssd_step(state: torch.Tensor, x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor,
+             Bm: torch.Tensor, Cm: torch.Tensor, Dskip: Optional[torch.Tensor] = None,
+             z: Optional[torch.Tensor] = None, delta_bias: Optional[torch.Tensor] = None,
+             delta_softplus: bool = False, y: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """ssm_ssd_step: one decode step of the SSD layer; advances `state` (B, H, P, N) fp32 in
+    place.  x, z: (B, H, P) bf16; delta: (B, H) bf16; A, Dskip, delta_bias: (H,) fp32;
+    Bm, Cm: (B, G, N) bf16.  Returns y (B, H, P) bf16."""
+    if not isinstance(state, torch.Tensor) or state.dim() != 4 or state.device.type != "cuda":
+        raise ValueError("state must be a (B, H, P, N) GPU tensor")
+    if not isinstance(Bm, torch.Tensor) or Bm.dim() != 3:
+        raise ValueError("Bm must be (B, G, N)")
+    dev = state.device
+    Bsz, H, P, N = state.shape
+    G = Bm.shape[1]
+    bf, f32 = torch.bfloat16, torch.float32
+    _req(state, "state", (Bsz, H, P, N), f32, dev)
+    _req(x, "x", (Bsz, H, P), bf, dev)
+    _req(delta, "delta", (Bsz, H), bf, dev)
+    _req(A, "A", (H,), f32, dev)
+    _req(Bm, "Bm", (Bsz, G, N), bf, dev)
+    _req(Cm, "Cm", (Bsz, G, N), bf, dev)
+    _opt(Dskip, "Dskip", (H,), f32, dev)
+    _opt(z, "z", (Bsz, H, P), bf, dev)
+    _opt(delta_bias, "delta_bias", (H,), f32, dev)
+    if y is None:
+        y = torch.empty_like(x)
+    _req(y, "y", (Bsz, H, P), bf, dev)
+    a = SsdStepArgs(batch=Bsz, nheads=H, headdim=P, ngroups=G, dstate=N, io_dtype=SSM_BF16,
+                    delta_softplus=int(bool(delta_softplus)), state=_ptr(state), x=_ptr(x),
+                    delta=_ptr(delta), A=_ptr(A), Bm=_ptr(Bm), Cm=_ptr(Cm), Dskip=_ptr(Dskip),
+                    z=_ptr(z), delta_bias=_ptr(delta_bias), y=_ptr(y))
+    _check(lib().ssm_ssd_step(ctypes.byref(a), _stream(dev)), "ssm_ssd_step")
+    return y

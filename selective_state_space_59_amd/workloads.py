@@ -121,6 +121,9 @@ S2_MAMBA2_130M = SsdConfig("s2_mamba2_130m_ssd", 8, 2048, 24, 64, 1, 128, seed=3
 # One long sequence at the same width: too few (batch, head) pairs to fill the GPU
 # alone, so the layer runs as sequence segments.
 S4_MAMBA2_LONG = SsdConfig("s4_mamba2_long_b1", 1, 65536, 24, 64, 1, 128, seed=32)
+# Decode of a 2.7B-like Mamba-2 layer (d_model 2560, E = 2: 80 heads x 64, N = 128) for
+# 256 sequences; seqlen is the number of decode steps drawn.
+S5_MAMBA2_DECODE = SsdConfig("s5_mamba2_2p7b_decode", 256, 16, 80, 64, 1, 128, seed=33)
 
 
 def _gen(device, seed: int) -> torch.Generator:

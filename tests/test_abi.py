@@ -66,6 +66,7 @@ int main(void) {
   printf("ssm_block_dims_t size %zu\n", sizeof(ssm_block_dims_t));
   printf("ssm_block_weights_t size %zu\n", sizeof(ssm_block_weights_t));
   printf("ssm_ssd_args_t size %zu\n", sizeof(ssm_ssd_args_t));
+  printf("ssm_ssd_step_args_t size %zu\n", sizeof(ssm_ssd_step_args_t));
   %FIELDS%
   return 0;
 }
@@ -74,7 +75,8 @@ int main(void) {
 
 STRUCTS = (("ssm_scan_args_t", ssm.ScanArgs), ("ssm_state_update_args_t", ssm.StateUpdateArgs),
            ("ssm_scan_bwd_args_t", ssm.ScanBwdArgs), ("ssm_block_dims_t", ssm.BlockDims),
-           ("ssm_block_weights_t", ssm.BlockWeights), ("ssm_ssd_args_t", ssm.SsdArgs))
+           ("ssm_block_weights_t", ssm.BlockWeights), ("ssm_ssd_args_t", ssm.SsdArgs),
+           ("ssm_ssd_step_args_t", ssm.SsdStepArgs))
 
 
 def test_ctypes_structs_match_c_layout():
@@ -468,3 +470,50 @@ def test_ssd_empty_batch_is_a_noop():
     assert run_ssd(ssd_args(batch=0)) == ssm.SSM_OK
     assert run_ssd(ssd_args(batch=0, seqlen=0)) == ssm.SSM_OK
     assert ssm.lib().ssm_ssd_fwd(None, None) == ssm.SSM_ERR_NULL_ARG
+
+
+# ------------------------------------------------------------ SSD step checks
+def ssd_step_args(**kw):
+    a = ssm.SsdStepArgs(batch=2, nheads=4, headdim=64, ngroups=1, dstate=128,
+                        io_dtype=ssm.SSM_BF16, delta_softplus=0, state=addr(0), x=addr(1),
+                        delta=addr(2), A=addr(3), Bm=addr(4), Cm=addr(5), Dskip=addr(6), z=addr(7),
+                        delta_bias=None, y=addr(8))
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def run_ssd_step(a):
+    return ssm.lib().ssm_ssd_step(ctypes.byref(a), None)
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("io_dtype", 5, ssm.SSM_ERR_BAD_DTYPE),
+    ("io_dtype", ssm.SSM_F32, ssm.SSM_ERR_UNSUPPORTED),
+    ("batch", -1, ssm.SSM_ERR_BAD_SHAPE),
+    ("headdim", 0, ssm.SSM_ERR_BAD_SHAPE),
+    ("ngroups", 3, ssm.SSM_ERR_BAD_SHAPE),
+    ("dstate", 2, ssm.SSM_ERR_UNSUPPORTED),
+    ("dstate", 96, ssm.SSM_ERR_UNSUPPORTED),
+    ("dstate", 512, ssm.SSM_ERR_UNSUPPORTED),
+    ("delta_softplus", 2, ssm.SSM_ERR_UNSUPPORTED),
+    ("state", None, ssm.SSM_ERR_NULL_ARG),
+    ("Cm", None, ssm.SSM_ERR_NULL_ARG),
+    ("y", None, ssm.SSM_ERR_NULL_ARG),
+    ("state", addr(0, 8), ssm.SSM_ERR_ALIGN),
+    ("Bm", addr(4, 4), ssm.SSM_ERR_ALIGN),
+    ("x", addr(1, 1), ssm.SSM_ERR_ALIGN),
+    ("A", addr(3, 2), ssm.SSM_ERR_ALIGN),
+    ("y", addr(1), ssm.SSM_ERR_ALIAS),                  # == x
+    ("y", addr(0, 1024), ssm.SSM_ERR_ALIAS),            # inside the state
+    ("x", addr(0, 64), ssm.SSM_ERR_ALIAS),              # inside the state
+    ("nheads", 1 << 20, ssm.SSM_ERR_BAD_SHAPE),         # B*H*P*N/4 > 2^31
+])
+def test_ssd_step_rejects_bad_arguments(field, value, status):
+    assert run_ssd_step(ssd_step_args(**{field: value})) == status
+
+
+def test_ssd_step_empty_batch_and_null_args():
+    assert run_ssd_step(ssd_step_args(batch=0, state=None, x=None)) == ssm.SSM_OK
+    assert ssm.lib().ssm_ssd_step(None, None) == ssm.SSM_ERR_NULL_ARG
+
