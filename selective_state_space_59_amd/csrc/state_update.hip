@@ -14,9 +14,10 @@
 // small (x, delta, z, y per channel; B, C per batch row; A and D per channel,
 // shared by all batch rows and so served from the caches).  Four lanes share
 // one channel, each holding four consecutive state entries, so a wave moves
-// 16 channels x 64 bytes of state with one 16-byte access per lane.  Each
-// thread handles two such quarters (a grid-size stride apart) and issues all
-// their loads before any arithmetic.  The state is streamed with
+// 16 channels x 64 bytes of state with one 16-byte access per lane.  A
+// workgroup takes 128 channels of one batch row (so the row's B and C are the
+// same for all of it) as two rounds of 64, and each thread issues the loads of
+// both its quarters before any arithmetic.  The state is streamed with
 // non-temporal loads and stores (it is touched once per step).  The four
 // partial read-outs of a channel are summed with two DPP quad swaps.
 //
@@ -32,7 +33,9 @@ namespace {
 
 constexpr int kLanesPerChannel = 4;
 constexpr int kPerLane = SSM_MAX_DSTATE / kLanesPerChannel;  // 4 state entries per lane
-constexpr int kQuartersPerThread = 2;
+constexpr int kRounds = 2;                                  // quarters per thread
+constexpr int kTileChannels = kRounds * 256 / kLanesPerChannel;  // channels per workgroup
+constexpr int64_t kMaxGrid = (int64_t)1 << 22;
 
 struct UpdateParams {
     int64_t B, D;
@@ -108,90 +111,97 @@ __device__ __forceinline__ float quad_sum(float v) {
     return v;
 }
 
-// N = 16 with 16-byte aligned state, A, B and C: quarter q of the
-// (B*D*4) quarters is entries 4(q%4)..+3 of channel q/4.
+// N = 16 with 16-byte aligned state, A, B and C.  Tile t = (batch row b,
+// channel run): round r gives lane l channel d = run * 128 + r * 64 + l / 4
+// and entries 4 (l % 4) .. +3 of it.
 template <typename IO>
-__global__ __launch_bounds__(256) void state_update_vec_kernel(UpdateParams p, int64_t nq) {
-    constexpr int K = kQuartersPerThread;
-    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    const int64_t q0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    float4 st[K], av[K], bv[K], cv[K];
-    float xv[K], dv[K], zv[K], dsk[K];
-    ConvLane cin[K];
-    int64_t bb_[K], dd_[K];
-    const int jq = (int)(threadIdx.x & 3);  // quarter of the channel (the stride keeps it)
+__device__ __forceinline__ void state_update_tile(const UpdateParams &p, int64_t t, int64_t ntiles) {
+    constexpr int R = kRounds;
+    const int64_t b = t / ntiles;
+    const int64_t run = t - b * ntiles;
+    const int jq = (int)(threadIdx.x & 3);
+    const int dl = (int)(threadIdx.x >> 2);
+    float4 st[R], av[R];
+    float xv[R], dv[R], zv[R], dsk[R];
+    ConvLane cin[R];
+    int64_t dd[R];
     // All loads first.
 #pragma unroll
-    for (int k = 0; k < K; ++k) {
-        const int64_t q = q0 + k * stride;
-        const int64_t qc = q < nq ? q : 0;
-        const int64_t ch = qc >> 2;
-        const int j = (int)(qc & 3);
-        // 32-bit division when the channel count allows it (always in practice).
-        const int64_t b = p.B * p.D <= 0xFFFFFFFFLL ? (int64_t)((uint32_t)ch / (uint32_t)p.D) : ch / p.D;
-        const int64_t d = ch - b * p.D;
+    for (int r = 0; r < R; ++r) {
+        dd[r] = run * kTileChannels + r * (256 / kLanesPerChannel) + dl;
+        const int64_t dc = dd[r] < p.D ? dd[r] : 0;
+        const int64_t ch = b * p.D + dc;
         {
             typedef float f4v __attribute__((ext_vector_type(4)));
-            const f4v v = __builtin_nontemporal_load(reinterpret_cast<const f4v *>(p.state + ch * SSM_MAX_DSTATE + 4 * j));
-            st[k] = make_float4(v.x, v.y, v.z, v.w);
+            const f4v v = __builtin_nontemporal_load(reinterpret_cast<const f4v *>(p.state + ch * SSM_MAX_DSTATE + 4 * jq));
+            st[r] = make_float4(v.x, v.y, v.z, v.w);
         }
-        av[k] = *reinterpret_cast<const float4 *>(p.A + d * SSM_MAX_DSTATE + 4 * j);
-        bv[k] = load4_io<IO>(p.Bm, b * SSM_MAX_DSTATE + 4 * j);
-        cv[k] = load4_io<IO>(p.Cm, b * SSM_MAX_DSTATE + 4 * j);
-        xv[k] = load_io<IO>(p.x, ch);
-        dv[k] = load_io<IO>(p.delta, ch);
-        zv[k] = p.z ? load_io<IO>(p.z, ch) : 0.0f;
-        dsk[k] = p.Dskip ? p.Dskip[d] : 0.0f;
-        if (p.softplus) dv[k] = softplus(dv[k] + (p.dbias ? p.dbias[d] : 0.0f));
-        bb_[k] = b;
-        dd_[k] = d;
-        if (p.K > 0) cin[k] = load_conv<IO>(p, b, d, jq);
+        av[r] = *reinterpret_cast<const float4 *>(p.A + dc * SSM_MAX_DSTATE + 4 * jq);
+        xv[r] = load_io<IO>(p.x, ch);
+        dv[r] = load_io<IO>(p.delta, ch);
+        zv[r] = p.z ? load_io<IO>(p.z, ch) : 0.0f;
+        dsk[r] = p.Dskip ? p.Dskip[dc] : 0.0f;
+        if (p.softplus) dv[r] = softplus(dv[r] + (p.dbias ? p.dbias[dc] : 0.0f));
+        if (p.K > 0) cin[r] = load_conv<IO>(p, b, dc, jq);
     }
+    const float4 bv = load4_io<IO>(p.Bm, b * SSM_MAX_DSTATE + 4 * jq);
+    const float4 cv = load4_io<IO>(p.Cm, b * SSM_MAX_DSTATE + 4 * jq);
     bool big = true;
 #pragma unroll
-    for (int k = 0; k < K; ++k)
-        big = big && fabsf(av[k].x) >= 0.0625f && fabsf(av[k].y) >= 0.0625f &&
-              fabsf(av[k].z) >= 0.0625f && fabsf(av[k].w) >= 0.0625f;
+    for (int r = 0; r < R; ++r)
+        big = big && fabsf(av[r].x) >= 0.0625f && fabsf(av[r].y) >= 0.0625f &&
+              fabsf(av[r].z) >= 0.0625f && fabsf(av[r].w) >= 0.0625f;
     const bool fast = __all(big);
+    const float bb[4] = {bv.x, bv.y, bv.z, bv.w};
+    const float cc[4] = {cv.x, cv.y, cv.z, cv.w};
 #pragma unroll
-    for (int k = 0; k < K; ++k) {
-        const int64_t q = q0 + k * stride;
-        const float dt = dv[k];
-        const float vin = p.K > 0 ? conv_in(cin[k], jq, xv[k]) : 0.0f;
-        const float u = p.K > 0 ? conv_u(cin[k], vin) : xv[k];
+    for (int r = 0; r < R; ++r) {
+        const bool live = dd[r] < p.D;
+        const int64_t ch = b * p.D + (live ? dd[r] : 0);
+        const float dt = dv[r];
+        const float vin = p.K > 0 ? conv_in(cin[r], jq, xv[r]) : 0.0f;
+        const float u = p.K > 0 ? conv_u(cin[r], vin) : xv[r];
         const float nwin = p.K > 1 ? conv_shift(vin) : 0.0f;
-        const float a[4] = {av[k].x, av[k].y, av[k].z, av[k].w};
-        const float bb[4] = {bv[k].x, bv[k].y, bv[k].z, bv[k].w};
-        const float cc[4] = {cv[k].x, cv[k].y, cv[k].z, cv[k].w};
-        float h[4] = {st[k].x, st[k].y, st[k].z, st[k].w};
+        const float a[4] = {av[r].x, av[r].y, av[r].z, av[r].w};
+        float h[4] = {st[r].x, st[r].y, st[r].z, st[r].w};
         float acc = 0.0f;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const float zz = dt * a[r];
+        for (int i = 0; i < 4; ++i) {
+            const float zz = dt * a[i];
             const float e = hw_exp2(zz * kLog2e);
             if (fast) {
-                const float qq = (bb[r] * u) * hw_rcp(a[r]);
-                h[r] = __builtin_fmaf(e, h[r], __builtin_fmaf(e, qq, -qq));
+                const float qq = (bb[i] * u) * hw_rcp(a[i]);
+                h[i] = __builtin_fmaf(e, h[i], __builtin_fmaf(e, qq, -qq));
             } else {
-                h[r] = e * h[r] + (dt * phi_of(zz, e)) * (bb[r] * u);
+                h[i] = e * h[i] + (dt * phi_of(zz, e)) * (bb[i] * u);
             }
-            acc += cc[r] * h[r];
+            acc += cc[i] * h[i];
         }
-        if (q < nq)
-        {
+        if (live) {
             typedef float f4v __attribute__((ext_vector_type(4)));
             const f4v v = {h[0], h[1], h[2], h[3]};
-            __builtin_nontemporal_store(v, reinterpret_cast<f4v *>(p.state + (q >> 2) * SSM_MAX_DSTATE + 4 * (q & 3)));
+            __builtin_nontemporal_store(v, reinterpret_cast<f4v *>(p.state + ch * SSM_MAX_DSTATE + 4 * jq));
         }
         acc = quad_sum(acc);
         // The window was read above by every lane of the quad (loads first).
-        if (q < nq && p.K > 1) store_window<IO>(p, bb_[k], dd_[k], jq, nwin);
-        if (q < nq && (q & 3) == 0) {
-            float yv = acc + dsk[k] * u;
-            if (p.z) yv *= silu(zv[k]);
-            store_io<IO>(p.y, q >> 2, yv);
+        if (live && p.K > 1) store_window<IO>(p, b, dd[r], jq, nwin);
+        if (live && jq == 0) {
+            float yv = acc + dsk[r] * u;
+            if (p.z) yv *= silu(zv[r]);
+            store_io<IO>(p.y, ch, yv);
         }
     }
+}
+
+// One tile per workgroup; a loop over tiles only where they outnumber one
+// grid (the loop costs time even when it runs once).
+template <typename IO, bool LOOP>
+__global__ __launch_bounds__(256) void state_update_vec_kernel(UpdateParams p, int64_t ntiles, int64_t total) {
+    if (!LOOP) {
+        state_update_tile<IO>(p, blockIdx.x, ntiles);
+        return;
+    }
+    for (int64_t t = blockIdx.x; t < total; t += gridDim.x) state_update_tile<IO>(p, t, ntiles);
 }
 
 // Any N <= 16 and any alignment: one quarter per thread, element loads.
@@ -251,9 +261,12 @@ template <typename IO>
 hipError_t launch_typed(const UpdateParams &p, bool vec, hipStream_t stream) {
     const int64_t nq = p.B * p.D * kLanesPerChannel;
     if (vec) {
-        const int64_t threads = (nq + kQuartersPerThread - 1) / kQuartersPerThread;
-        const unsigned blocks = (unsigned)((threads + 255) / 256);
-        state_update_vec_kernel<IO><<<blocks, 256, 0, stream>>>(p, nq);
+        const int64_t ntiles = (p.D + kTileChannels - 1) / kTileChannels;
+        const int64_t total = p.B * ntiles;
+        if (total <= kMaxGrid)
+            state_update_vec_kernel<IO, false><<<(unsigned)total, 256, 0, stream>>>(p, ntiles, total);
+        else
+            state_update_vec_kernel<IO, true><<<(unsigned)kMaxGrid, 256, 0, stream>>>(p, ntiles, total);
     } else {
         const unsigned blocks = (unsigned)((nq + 255) / 256);
         state_update_kernel<IO><<<blocks, 256, 0, stream>>>(p);

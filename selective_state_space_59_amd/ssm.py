@@ -356,6 +356,17 @@ def state_update(state: torch.Tensor, x: torch.Tensor, delta: torch.Tensor, A: t
                  conv_state: Optional[torch.Tensor] = None) -> torch.Tensor:
     """ssm_state_update: advances `state` (B, D, N) -- and with conv_w the conv
     window `conv_state` (B, K-1, D) -- in place and returns y (B, D)."""
+    a, y = state_update_args(state, x, delta, A, Bm, Cm, Dskip, z, delta_bias, delta_softplus, y,
+                             conv_w, conv_b, conv_state)
+    _check(lib().ssm_state_update(ctypes.byref(a), _stream(state.device)), "ssm_state_update")
+    return y
+
+
+def state_update_args(state, x, delta, A, Bm, Cm, Dskip=None, z=None, delta_bias=None,
+                      delta_softplus=False, y=None, conv_w=None, conv_b=None, conv_state=None):
+    """The checked ssm_state_update_args_t of a state_update call, and its y (allocated
+    when not given), for callers that launch the same step repeatedly through
+    lib().ssm_state_update.  The tensors must outlive the struct."""
     if not isinstance(state, torch.Tensor) or state.dim() != 3 or state.device.type != "cuda":
         raise ValueError("state must be a (B, D, N) float32 GPU tensor")
     dev = state.device
@@ -390,8 +401,7 @@ def state_update(state: torch.Tensor, x: torch.Tensor, delta: torch.Tensor, A: t
                         Dskip=_ptr(Dskip), delta_bias=_ptr(delta_bias), y=_ptr(y), conv_k=K,
                         conv_w=_ptr(conv_w), conv_b=_ptr(conv_b),
                         conv_state=_ptr(conv_state) if K > 1 else None)
-    _check(lib().ssm_state_update(ctypes.byref(a), _stream(dev)), "ssm_state_update")
-    return y
+    return a, y
 
 
 def selective_scan_bwd(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, Bm: torch.Tensor,
@@ -586,6 +596,16 @@ def ssd_step(state: torch.Tensor, x: torch.Tensor, delta: torch.Tensor, A: torch
     """ssm_ssd_step: one decode step of the SSD layer; advances `state` (B, H, P, N) fp32 in
     place.  x, z: (B, H, P) bf16; delta: (B, H) bf16; A, Dskip, delta_bias: (H,) fp32;
     Bm, Cm: (B, G, N) bf16.  Returns y (B, H, P) bf16."""
+    a, y = ssd_step_args(state, x, delta, A, Bm, Cm, Dskip, z, delta_bias, delta_softplus, y)
+    _check(lib().ssm_ssd_step(ctypes.byref(a), _stream(state.device)), "ssm_ssd_step")
+    return y
+
+
+def ssd_step_args(state, x, delta, A, Bm, Cm, Dskip=None, z=None, delta_bias=None,
+                  delta_softplus=False, y=None):
+    """The checked ssm_ssd_step_args_t of an ssd_step call, and its y (allocated when not
+    given), for callers that launch the same step repeatedly through lib().ssm_ssd_step.
+    The tensors must outlive the struct."""
     if not isinstance(state, torch.Tensor) or state.dim() != 4 or state.device.type != "cuda":
         raise ValueError("state must be a (B, H, P, N) GPU tensor")
     if not isinstance(Bm, torch.Tensor) or Bm.dim() != 3:
@@ -610,5 +630,4 @@ def ssd_step(state: torch.Tensor, x: torch.Tensor, delta: torch.Tensor, A: torch
                     delta_softplus=int(bool(delta_softplus)), state=_ptr(state), x=_ptr(x),
                     delta=_ptr(delta), A=_ptr(A), Bm=_ptr(Bm), Cm=_ptr(Cm), Dskip=_ptr(Dskip),
                     z=_ptr(z), delta_bias=_ptr(delta_bias), y=_ptr(y))
-    _check(lib().ssm_ssd_step(ctypes.byref(a), _stream(dev)), "ssm_ssd_step")
-    return y
+    return a, y

@@ -204,7 +204,8 @@ def _decode(inp, steps, y_dtype):
 
 
 @pytest.mark.parametrize("B,D,N,dt", [(3, 70, 16, torch.float32), (4, 64, 5, torch.bfloat16),
-                                      (2, 33, 16, torch.bfloat16), (1, 1, 1, torch.float32)])
+                                      (2, 33, 16, torch.bfloat16), (1, 1, 1, torch.float32),
+                                      (2, 300, 16, torch.bfloat16)])  # 128-channel tiles, ragged
 def test_state_update_matches_oracle(B, D, N, dt):
     inp = W.make_decode_inputs(B, D, N, 8, io_dtype=dt, seed=B + D + N, device=DEV)
     ys, st = _decode(inp, 8, dt)
@@ -233,6 +234,25 @@ def test_state_update_small_and_zero_A():
                                       Dskip=to64(inp["Dskip"]), z=to64(inp["z"][t]))
         assert_close(to64(ys[t]), yr, 1e-4, "y step %d" % t)
     assert_close(to64(st), ref, 1e-4, "state")
+
+
+def test_state_update_capped_grid_sampled_rows():
+    """More (batch row, channel run) tiles than one launch grid holds (2^22 workgroups):
+    each workgroup takes further tiles in turn; the oracle checks three rows."""
+    B = (1 << 22) + 2
+    inp = W.make_decode_inputs(B, 8, 16, 2, io_dtype=torch.bfloat16, seed=77, device=DEV)
+    ys, st = _decode(inp, 2, torch.bfloat16)
+    rows = [0, 1 << 21, B - 1]
+    ref = inp["state0"][rows].double().cpu().numpy()
+    for t in range(2):
+        yr, ref = oracle.state_update(ref, to64(inp["x"][t][rows]), to64(inp["delta"][t][rows]),
+                                      to64(inp["A"]), to64(inp["Bm"][t][rows]),
+                                      to64(inp["Cm"][t][rows]), Dskip=to64(inp["Dskip"]),
+                                      z=to64(inp["z"][t][rows]))
+        assert_close(to64(ys[t][rows]), yr, TOL[torch.bfloat16], "y step %d" % t)
+    assert_close(to64(st[rows]), ref, TOL[torch.bfloat16], "state")
+    del inp, ys, st
+    torch.cuda.empty_cache()
 
 
 def test_decode_config_sampled_rows():
