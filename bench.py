@@ -84,7 +84,7 @@ def _counter_traffic(kernel_key):
     if not ent:
         return None
     from selective_state_space_59_amd import build as B
-    if ent.get("source_hash") != B.source_hash():
+    if ent.get("source_hash") != B.source_hash(ent.get("sources")):
         return None
     return ent.get("bytes_per_launch")
 

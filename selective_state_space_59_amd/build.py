@@ -41,17 +41,21 @@ def _code_only(text: bytes) -> bytes:
     return " ".join(t.split()).encode()
 
 
-def source_hash() -> str:
-    """sha256 over the code of the library's sources and public header (comments
-    excluded), identifying a kernel build for measurements taken on it."""
+def source_hash(sources=None) -> str:
+    """sha256 over the code (comments excluded) of the library sources `sources` (file
+    names under csrc/) and the compile flags, or of every library source and the public
+    header when None: it identifies a kernel build for measurements taken on it."""
     import hashlib
     h = hashlib.sha256()
-    names = sorted(os.listdir(CSRC))
+    names = sorted(os.listdir(CSRC)) if sources is None else sorted(sources)
+    if sources is not None:
+        h.update(" ".join(COMMON).encode() + b"\0")
     for n in names:
         with open(os.path.join(CSRC, n), "rb") as f:
             h.update(n.encode() + b"\0" + _code_only(f.read()))
-    with open(os.path.join(PKG, "..", "include", "ssm.h"), "rb") as f:
-        h.update(_code_only(f.read()))
+    if sources is None:
+        with open(os.path.join(PKG, "..", "include", "ssm.h"), "rb") as f:
+            h.update(_code_only(f.read()))
     return h.hexdigest()[:16]
 
 

@@ -11,12 +11,13 @@
         --fetch A_counter_collection.csv --write B_counter_collection.csv \\
         --copy-fetch C_counter_collection.csv --copy-write D_counter_collection.csv \\
         --copy-bytes BYTES --kernel SUBSTRING --key NAME --algorithmic-bytes N \\
-        --commands "cmd1" "cmd2" "cmd3" "cmd4" \\
+        --commands "cmd1" "cmd2" "cmd3" "cmd4" [--sources scan_fwd.hip ...] \\
         --out-json profiles/hbm_counters.json --out profiles/NAME.md
 
 FETCH_SIZE and WRITE_SIZE are reported in KiB per dispatch.  The JSON entry
-carries the hash of the library sources it was measured on; bench.py uses
-it only while that hash matches the current sources.
+names the library sources the kernel is built from (--sources, file names
+under csrc/; default: all) and carries their hash with the compile flags;
+bench.py uses it only while that hash matches the current sources.
 """
 from __future__ import annotations
 
@@ -76,7 +77,9 @@ def cmd_counters(a):
     total = fb + wb
     sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
     from selective_state_space_59_amd import build
-    entry = dict(source_hash=build.source_hash(), kernel=a.kernel, bytes_per_launch=round(total),
+    sources = sorted(a.sources) if a.sources else None
+    entry = dict(source_hash=build.source_hash(sources), sources=sources, kernel=a.kernel,
+                 bytes_per_launch=round(total),
                  fetch_bytes=round(fb), write_bytes=round(wb), fetch_scale=round(fscale, 4),
                  write_scale=round(wscale, 4), dispatches=len(fetch),
                  algorithmic_bytes_per_launch=a.algorithmic_bytes)
@@ -102,7 +105,8 @@ def cmd_counters(a):
              "| HBM bytes per launch | %.0f |" % total,
              "| algorithmic bytes per launch | %d |" % a.algorithmic_bytes,
              "| traffic / algorithmic | %.4f |" % (total / a.algorithmic_bytes),
-             "| library source hash (code, comments excluded) | %s |" % entry["source_hash"]]
+             "| hash of the kernel's sources (%s; code only) and flags | %s |"
+             % (", ".join(sources) if sources else "all library sources", entry["source_hash"])]
     _write(a.out, "\n".join(lines) + "\n")
 
 
@@ -132,6 +136,8 @@ def main(argv=None):
     c.add_argument("--copy-bytes", type=int, required=True)
     c.add_argument("--algorithmic-bytes", type=int, required=True)
     c.add_argument("--commands", nargs="+", required=True)
+    c.add_argument("--sources", nargs="+", default=None,
+                   help="library sources the kernel is built from (file names under csrc/)")
     a = ap.parse_args(argv)
     {"stats": cmd_stats, "counters": cmd_counters}[a.cmd](a)
 
