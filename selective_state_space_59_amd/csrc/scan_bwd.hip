@@ -233,7 +233,10 @@ __device__ __forceinline__ void bwd_body(const BwdParams &p, const LaneB &l, flo
             if (p.z) zv = load_io<IO>(p.z, i);
         }
         // -- forward over the block from its checkpoint ----------------------
-        float hp[kStep], dp[kStep];  // h_{t-1}, dt phi(dt A)
+        // Only h_{t-1} is kept per step; dt phi(dt A) is formed again, by the
+        // same expression, in the adjoint (holding it cost 16 registers and
+        // spills).
+        float hp[kStep];
         float h = l.valid ? p.ckpt[((j * p.B + l.b) * p.D + l.d) * kRowN + n] : 0.0f;
         sfor<kStep / 4>([&](auto G) {
             constexpr int g4 = 4 * decltype(G)::value;
@@ -243,8 +246,7 @@ __device__ __forceinline__ void bwd_body(const BwdParams &p, const LaneB &l, flo
                 const float dtk = bcast_row<k>(dt), uk = bcast_row<k>(u);
                 const float e = hw_exp2(dtk * a2);
                 hp[k] = h;
-                dp[k] = dtphi<FAST>(dtk, a, ia, e);
-                h = __builtin_fmaf(e, h, dp[k] * (bv[k] * uk));
+                h = __builtin_fmaf(e, h, dtphi<FAST>(dtk, a, ia, e) * (bv[k] * uk));
                 pk[decltype(K)::value] = cv[k] * h;  // partial read-out of step k
             });
             *reinterpret_cast<float4 *>(my0 + g4) = make_float4(pk[0], pk[1], pk[2], pk[3]);
@@ -269,16 +271,25 @@ __device__ __forceinline__ void bwd_body(const BwdParams &p, const LaneB &l, flo
                 constexpr int kk = 3 - decltype(K)::value;
                 constexpr int k = g4 + kk;
                 const float gyk = bcast_row<k>(gy), uk = bcast_row<k>(u), dtk = bcast_row<k>(dt);
-                const float e = hw_exp2(dtk * a2), dtph = dp[k], bk = bv[k];
+                const float e = hw_exp2(dtk * a2), dtph = dtphi<FAST>(dtk, a, ia, e), bk = bv[k];
                 const float hcur = k == kStep - 1 ? h : hp[k + 1 < kStep ? k + 1 : 0];
                 const float lt = __builtin_fmaf(cv[k], gyk, lam);  // dL/dh_t
                 const float dabar = lt * hp[k], dbbar = lt * uk;
+                const float xb = dbbar * bk;  // dL/dh_t u B
                 pdu[kk] = lt * (dtph * bk);
-                pdt[kk] = e * __builtin_fmaf(dabar, a, dbbar * bk);
-                const float zz = dtk * a, r = hw_rcp(zz);
-                const float ph = (e - 1.0f) * r;  // phi where |zz| >= 1/4 (psi's series covers the rest)
-                accA = __builtin_fmaf(e * dabar, dtk, accA);
-                accA = __builtin_fmaf(dbbar * bk * dtk, dtk * psi_f(zz, e, ph, r), accA);
+                pdt[kk] = e * __builtin_fmaf(dabar, a, xb);
+                if (FAST) {
+                    // d B_bar / dA = B (dt e - dt phi) / A: no psi where |A| >= 1/16.  The
+                    // difference cancels for small dt A, but the term is then small
+                    // next to dt e h (its error is ~1 ulp of B u / A, A >= 1/16).
+                    accA = __builtin_fmaf(dtk * e, __builtin_fmaf(xb, ia, dabar), accA);
+                    accA = __builtin_fmaf(-(xb * dtph), ia, accA);
+                } else {
+                    const float zz = dtk * a, r = hw_rcp(zz);
+                    const float ph = (e - 1.0f) * r;  // phi where |zz| >= 1/4 (psi's series covers the rest)
+                    accA = __builtin_fmaf(e * dabar, dtk, accA);
+                    accA = __builtin_fmaf(xb * dtk, dtk * psi_f(zz, e, ph, r), accA);
+                }
                 sb[kk] = sum_channels(dbbar * dtph);
                 sc[kk] = sum_channels(gyk * hcur);
                 lam = e * lt;
