@@ -162,15 +162,107 @@ __device__ __forceinline__ float dtphi(float dt, float a, float ia, float e) {
     return dt * phi_f(zz, e, hw_rcp(zz));
 }
 
+// Raw I/O bits, loaded now and widened later, so that a load can be issued a
+// block before its value is used (widening at once would wait for it).
+template <typename IO>
+__device__ __forceinline__ uint32_t load_bits(const void *p, int64_t i) {
+    if constexpr (sizeof(typename IO::storage) == 2) return static_cast<const uint16_t *>(p)[i];
+    else return __float_as_uint(static_cast<const float *>(p)[i]);
+}
+template <typename IO>
+__device__ __forceinline__ float bits_f32(uint32_t v) {
+    if constexpr (sizeof(typename IO::storage) == 2) return __uint_as_float(v << 16);
+    else return __uint_as_float(v);
+}
+
+// The own-step inputs of lane (c, n) at step t as raw bits: x at t-3 .. t
+// (only x_t without a conv prologue) and delta.  Indices are clamped into the
+// tensors and the lanes and window slots outside them are masked when the
+// values are used, so no load sits in a branch.
+struct OwnRaw {
+    uint32_t xr[4];
+    uint32_t draw;
+    int wm;  // bit j: x_{t-3+j} exists (all 0 for a lane or step outside the tensors)
+};
+template <typename IO>
+__device__ __forceinline__ OwnRaw own_raw(const BwdParams &p, const LaneB &l, int64_t t) {
+    OwnRaw r;
+    const bool live = l.valid && t < p.L;
+    const int64_t tc = live ? t : 0, dc = l.valid ? l.d : 0;
+    const int64_t i = (l.b * p.L + tc) * p.D + dc;
+    r.xr[3] = load_bits<IO>(p.x, i);
+    r.draw = load_bits<IO>(p.delta, i);
+    r.wm = live ? 8 : 0;
+    r.xr[0] = r.xr[1] = r.xr[2] = 0u;
+    if (p.K > 0) {
+#pragma unroll
+        for (int j = 0; j < 3; ++j) {
+            // before t = 0 the clamped index is step 0's (masked below)
+            const bool in = tc - 3 + j >= 0;
+            const int64_t s = in ? tc - 3 + j : 0;
+            r.xr[j] = load_bits<IO>(p.x, (l.b * p.L + s) * p.D + dc);
+            r.wm |= (live && in) ? (1 << j) : 0;
+        }
+    }
+    return r;
+}
+// u and dt from the raw inputs; wr = the conv taps right-aligned to width 4
+// (wr[3] weighs x_t; taps past K are 0).
+template <typename IO>
+__device__ __forceinline__ void own_finish(const BwdParams &p, const OwnRaw &r, const float (&wr)[4], float cb,
+                                           float bias, float &u, float &dt) {
+    float xw[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) xw[j] = (r.wm >> j) & 1 ? bits_f32<IO>(r.xr[j]) : 0.0f;
+    u = xw[3];
+    if (p.K > 0) {
+        float c = cb;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) c = __builtin_fmaf(wr[j], xw[j], c);
+        u = r.wm ? silu(c) : 0.0f;
+    }
+    const float raw = r.wm ? bits_f32<IO>(r.draw) : 0.0f;
+    dt = p.softplus ? softplus(raw + bias) : raw;
+    if (!r.wm) dt = 0.0f;
+}
+
+// Raw bits of entry n of the B (or C) rows of 16 steps from t0 (steps past
+// the end read the last row, as load_rows).
+template <typename IO>
+__device__ __forceinline__ void load_rows_bits(const void *t, const BwdParams &p, const LaneB &l, int64_t t0,
+                                               uint32_t (&v)[kStep]) {
+#pragma unroll
+    for (int k = 0; k < kStep; ++k) {
+        const int64_t tk = t0 + k < p.L ? t0 + k : p.L - 1;
+        v[k] = load_bits<IO>(t, (l.b * p.L + tk) * kRowN + l.n);
+    }
+}
+
 template <typename IO, bool FAST>
 __device__ __forceinline__ void ckpt_body(const BwdParams &p, const LaneB &l, float a, float ia, float h) {
     const float a2 = a * kLog2e;
     const int64_t nb = (p.L + kStep - 1) / kStep;
+    float wr[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    float cb = 0.0f;
+    if (p.K > 0 && l.valid) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) wr[3 - j] = j < p.K ? p.conv_w[l.d * p.K + p.K - 1 - j] : 0.0f;
+        cb = p.conv_b ? p.conv_b[l.d] : 0.0f;
+    }
+    const float bias = (l.valid && p.dbias) ? p.dbias[l.d] : 0.0f;
+    // Block j's inputs are requested while block j - 1 runs (the request
+    // after the last block reads clamped rows and is not used).
+    OwnRaw rn = own_raw<IO>(p, l, l.n);
+    uint32_t bn[kStep];
+    load_rows_bits<IO>(p.Bm, p, l, 0, bn);
     for (int64_t j = 0; j < nb; ++j) {
         if (l.valid) p.ckpt[((j * p.B + l.b) * p.D + l.d) * kRowN + l.n] = h;
-        float u, raw, dt, bv[kStep];
-        own_inputs<IO>(p, l, j * kStep + l.n, u, raw, dt);
-        load_rows<IO>(p.Bm, p, l, j * kStep, bv);
+        float u, dt, bv[kStep];
+        own_finish<IO>(p, rn, wr, cb, bias, u, dt);
+#pragma unroll
+        for (int k = 0; k < kStep; ++k) bv[k] = bits_f32<IO>(bn[k]);
+        rn = own_raw<IO>(p, l, (j + 1) * kStep + l.n);
+        load_rows_bits<IO>(p.Bm, p, l, (j + 1) * kStep, bn);
         sfor<kStep>([&](auto K) {
             constexpr int k = decltype(K)::value;
             const float dtk = bcast_row<k>(dt), uk = bcast_row<k>(u);
