@@ -117,41 +117,6 @@ __device__ __forceinline__ LaneB lane_setup(const BwdParams &p) {
     return l;
 }
 
-// Own-step inputs of lane (c, n) in block j: step t = 16 j + n of channel c.
-template <typename IO>
-__device__ __forceinline__ void own_inputs(const BwdParams &p, const LaneB &l, int64_t t, float &u,
-                                           float &raw, float &dt) {
-    u = raw = dt = 0.0f;
-    if (l.valid && t < p.L) {
-        const int64_t i = (l.b * p.L + t) * p.D + l.d;
-        u = load_io<IO>(p.x, i);
-        if (p.K > 0) {  // the conv prologue: u = silu(b + sum_k w_k x_{t-K+1+k})
-            float cacc = p.conv_b ? p.conv_b[l.d] : 0.0f;
-            for (int k = 0; k < p.K; ++k) {
-                const int64_t s = t - (p.K - 1) + k;
-                if (s >= 0) cacc = __builtin_fmaf(p.conv_w[l.d * p.K + k], load_io<IO>(p.x, (l.b * p.L + s) * p.D + l.d), cacc);
-            }
-            u = silu(cacc);
-        }
-        raw = load_io<IO>(p.delta, i);
-        dt = p.softplus ? softplus(raw + (p.dbias ? p.dbias[l.d] : 0.0f)) : raw;
-    }
-}
-
-// Entry n of the B (or C) rows of the block's 16 steps.  Steps past the end
-// read the last row instead (no branches): there dt and u are 0, so those
-// values reach no output.
-template <typename IO>
-__device__ __forceinline__ void load_rows(const void *t, const BwdParams &p, const LaneB &l, int64_t t0,
-                                          float (&v)[kStep]) {
-    const typename IO::storage *row = static_cast<const typename IO::storage *>(t) + l.b * p.L * kRowN + l.n;
-#pragma unroll
-    for (int k = 0; k < kStep; ++k) {
-        const int64_t tk = t0 + k < p.L ? t0 + k : p.L - 1;
-        v[k] = load_io<IO>(row, tk * kRowN);
-    }
-}
-
 // Pass 1: states entering every block.
 // dt phi(dt A) = (e - 1)/A: in waves where every |A| >= 1/16 (FAST) as
 // (e - 1) times 1/A, otherwise through phi (series near 0).
@@ -226,8 +191,9 @@ __device__ __forceinline__ void own_finish(const BwdParams &p, const OwnRaw &r, 
     if (!r.wm) dt = 0.0f;
 }
 
-// Raw bits of entry n of the B (or C) rows of 16 steps from t0 (steps past
-// the end read the last row, as load_rows).
+// Raw bits of entry n of the B (or C) rows of 16 steps from t0.  Steps past
+// the end read the last row instead (no branches): there dt and u are 0, so
+// those values reach no output.
 template <typename IO>
 __device__ __forceinline__ void load_rows_bits(const void *t, const BwdParams &p, const LaneB &l, int64_t t0,
                                                uint32_t (&v)[kStep]) {
@@ -236,6 +202,27 @@ __device__ __forceinline__ void load_rows_bits(const void *t, const BwdParams &p
         const int64_t tk = t0 + k < p.L ? t0 + k : p.L - 1;
         v[k] = load_bits<IO>(t, (l.b * p.L + tk) * kRowN + l.n);
     }
+}
+
+// The adjoint's per-step inputs of block jb, as raw bits (see own_raw).  The
+// B and C rows (the same for the whole workgroup, so mostly cache hits) are
+// read when the block starts: holding them a block ahead does not fit the
+// register budget of 3 waves per SIMD.
+struct BlockRaw {
+    OwnRaw own;
+    uint32_t g, z;
+    float h;  // the checkpoint
+};
+template <typename IO>
+__device__ __forceinline__ void request_block(const BwdParams &p, const LaneB &l, int64_t jb, BlockRaw &r) {
+    const int64_t t = jb * kStep + l.n;
+    r.own = own_raw<IO>(p, l, t);
+    const bool live = l.valid && t < p.L;
+    const int64_t dc = l.valid ? l.d : 0;
+    const int64_t i = (l.b * p.L + (live ? t : 0)) * p.D + dc;
+    r.g = load_bits<IO>(p.dy, i);
+    r.z = p.z ? load_bits<IO>(p.z, i) : 0u;
+    r.h = p.ckpt[((jb * p.B + l.b) * p.D + dc) * kRowN + l.n];
 }
 
 template <typename IO, bool FAST>
@@ -310,26 +297,45 @@ __device__ __forceinline__ void bwd_body(const BwdParams &p, const LaneB &l, flo
     float accA = 0.0f, accD = 0.0f, accBias = 0.0f;
     const int64_t nb = (p.L + kStep - 1) / kStep;
     const int64_t grow = blockIdx.x % p.G;  // workgroup within the batch row
+    float wr[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    float cb = 0.0f;
+    if (p.K > 0 && l.valid) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) wr[3 - q] = q < p.K ? p.conv_w[l.d * p.K + p.K - 1 - q] : 0.0f;
+        cb = p.conv_b ? p.conv_b[l.d] : 0.0f;
+    }
+
+    // Block j's inputs as raw bits, requested during block j + 1 once its
+    // adjoint is done (then the block's own registers are free), so that they
+    // arrive while the sums and the workgroup reduction run.
+    BlockRaw nx;
+    request_block<IO>(p, l, nb - 1, nx);
 
     for (int64_t j = nb - 1; j >= 0; --j) {
         const int64_t t0 = j * kStep;
         const int64_t tme = t0 + n;  // this lane's own step
-        float u, raw, dt, bv[kStep], cv[kStep];
-        own_inputs<IO>(p, l, tme, u, raw, dt);
-        load_rows<IO>(p.Bm, p, l, t0, bv);
-        load_rows<IO>(p.Cm, p, l, t0, cv);
-        float zv = 0.0f, gv = 0.0f;
-        if (l.valid && tme < p.L) {
-            const int64_t i = (l.b * p.L + tme) * p.D + l.d;
-            gv = load_io<IO>(p.dy, i);
-            if (p.z) zv = load_io<IO>(p.z, i);
+        const bool live = nx.own.wm != 0;  // l.valid && tme < p.L
+        float u, dt, bv[kStep], cv[kStep];
+        own_finish<IO>(p, nx.own, wr, cb, bias, u, dt);
+        const float raw = live ? bits_f32<IO>(nx.own.draw) : 0.0f;
+        {
+            uint32_t rb[kStep], rc[kStep];
+            load_rows_bits<IO>(p.Bm, p, l, t0, rb);
+            load_rows_bits<IO>(p.Cm, p, l, t0, rc);
+#pragma unroll
+            for (int k = 0; k < kStep; ++k) {
+                bv[k] = bits_f32<IO>(rb[k]);
+                cv[k] = bits_f32<IO>(rc[k]);
+            }
         }
+        const float gv = live ? bits_f32<IO>(nx.g) : 0.0f;
+        const float zv = (live && p.z) ? bits_f32<IO>(nx.z) : 0.0f;
         // -- forward over the block from its checkpoint ----------------------
         // Only h_{t-1} is kept per step; dt phi(dt A) is formed again, by the
         // same expression, in the adjoint (holding it cost 16 registers and
         // spills).
         float hp[kStep];
-        float h = l.valid ? p.ckpt[((j * p.B + l.b) * p.D + l.d) * kRowN + n] : 0.0f;
+        float h = l.valid ? nx.h : 0.0f;
         sfor<kStep / 4>([&](auto G) {
             constexpr int g4 = 4 * decltype(G)::value;
             float pk[4];
@@ -394,6 +400,7 @@ __device__ __forceinline__ void bwd_body(const BwdParams &p, const LaneB &l, flo
             }
         });
         __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+        request_block<IO>(p, l, j > 0 ? j - 1 : 0, nx);  // the request after block 0 is not used
         {
             float du = dsk * gy, ddt = 0.0f;
 #pragma unroll
@@ -404,9 +411,11 @@ __device__ __forceinline__ void bwd_body(const BwdParams &p, const LaneB &l, flo
             float draw = ddt;
             if (p.softplus) {
                 draw = ddt * sigmoid_f(raw + bias);
-                accBias += draw;
+                // Steps past the end have dt = 0 but a nonzero ddt where dh_final
+                // is given: they must not reach the bias gradient.
+                if (live) accBias += draw;
             }
-            if (l.valid && tme < p.L) {
+            if (live) {
                 const int64_t i = (l.b * p.L + tme) * p.D + l.d;
                 if (p.K > 0) p.dU[i] = du;
                 else store_io<IO>(p.dx, i, du);

@@ -96,6 +96,23 @@ def test_bwd_softplus_bias_and_zero_A():
             _check(k, to64(g[k]), r, TOL_SUM[torch.float32], float(np.mean(np.abs(r))))
 
 
+def test_bwd_softplus_bias_with_final_state_gradient_ragged():
+    """Softplus with a bias, a gradient on the final state and a length that ends inside a
+    16-step block: the steps past the end (dt = 0) carry dh_final back unchanged and must
+    add nothing to the bias gradient."""
+    inp = W.make_scan_inputs(2, 70, 40, 16, io_dtype=torch.float32, seed=533, device=DEV, h0=True)
+    g0 = torch.Generator(DEV).manual_seed(8)
+    inp["delta"] = (torch.randn(inp["delta"].shape, device=DEV, generator=g0) - 1.0).contiguous()
+    bias = 0.3 * torch.randn(40, device=DEV, generator=g0)
+    dhf = torch.randn(2, 40, 16, device=DEV, generator=g0)
+    g, ref = _run(inp, torch.float32, softplus=True, bias=bias, dh_final=dhf)
+    for k, r in ref.items():
+        if k in PER_ELEM:
+            _check(k, to64(g[k]), r, TOL[torch.float32])
+        else:
+            _check(k, to64(g[k]), r, TOL_SUM[torch.float32], float(np.mean(np.abs(r))))
+
+
 def test_bwd_empty_sequence():
     inp = W.make_scan_inputs(2, 0, 32, 16, io_dtype=torch.float32, seed=532, device=DEV, h0=True)
     dhf = torch.randn(2, 32, 16, device=DEV)
