@@ -149,7 +149,7 @@ struct OwnRaw {
     uint32_t draw;
     int wm;  // bit j: x_{t-3+j} exists (all 0 for a lane or step outside the tensors)
 };
-template <typename IO>
+template <typename IO, bool CONV>
 __device__ __forceinline__ OwnRaw own_raw(const BwdParams &p, const LaneB &l, int64_t t) {
     OwnRaw r;
     const bool live = l.valid && t < p.L;
@@ -159,7 +159,7 @@ __device__ __forceinline__ OwnRaw own_raw(const BwdParams &p, const LaneB &l, in
     r.draw = load_bits<IO>(p.delta, i);
     r.wm = live ? 8 : 0;
     r.xr[0] = r.xr[1] = r.xr[2] = 0u;
-    if (p.K > 0) {
+    if (CONV) {
 #pragma unroll
         for (int j = 0; j < 3; ++j) {
             // before t = 0 the clamped index is step 0's (masked below)
@@ -173,14 +173,14 @@ __device__ __forceinline__ OwnRaw own_raw(const BwdParams &p, const LaneB &l, in
 }
 // u and dt from the raw inputs; wr = the conv taps right-aligned to width 4
 // (wr[3] weighs x_t; taps past K are 0).
-template <typename IO>
+template <typename IO, bool CONV>
 __device__ __forceinline__ void own_finish(const BwdParams &p, const OwnRaw &r, const float (&wr)[4], float cb,
                                            float bias, float &u, float &dt) {
     float xw[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) xw[j] = (r.wm >> j) & 1 ? bits_f32<IO>(r.xr[j]) : 0.0f;
     u = xw[3];
-    if (p.K > 0) {
+    if (CONV) {
         float c = cb;
 #pragma unroll
         for (int j = 0; j < 4; ++j) c = __builtin_fmaf(wr[j], xw[j], c);
@@ -213,10 +213,10 @@ struct BlockRaw {
     uint32_t g, z;
     float h;  // the checkpoint
 };
-template <typename IO>
+template <typename IO, bool CONV>
 __device__ __forceinline__ void request_block(const BwdParams &p, const LaneB &l, int64_t jb, BlockRaw &r) {
     const int64_t t = jb * kStep + l.n;
-    r.own = own_raw<IO>(p, l, t);
+    r.own = own_raw<IO, CONV>(p, l, t);
     const bool live = l.valid && t < p.L;
     const int64_t dc = l.valid ? l.d : 0;
     const int64_t i = (l.b * p.L + (live ? t : 0)) * p.D + dc;
@@ -225,13 +225,13 @@ __device__ __forceinline__ void request_block(const BwdParams &p, const LaneB &l
     r.h = p.ckpt[((jb * p.B + l.b) * p.D + dc) * kRowN + l.n];
 }
 
-template <typename IO, bool FAST>
+template <typename IO, bool FAST, bool CONV>
 __device__ __forceinline__ void ckpt_body(const BwdParams &p, const LaneB &l, float a, float ia, float h) {
     const float a2 = a * kLog2e;
     const int64_t nb = (p.L + kStep - 1) / kStep;
     float wr[4] = {0.0f, 0.0f, 0.0f, 0.0f};
     float cb = 0.0f;
-    if (p.K > 0 && l.valid) {
+    if (CONV && l.valid) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) wr[3 - j] = j < p.K ? p.conv_w[l.d * p.K + p.K - 1 - j] : 0.0f;
         cb = p.conv_b ? p.conv_b[l.d] : 0.0f;
@@ -239,16 +239,16 @@ __device__ __forceinline__ void ckpt_body(const BwdParams &p, const LaneB &l, fl
     const float bias = (l.valid && p.dbias) ? p.dbias[l.d] : 0.0f;
     // Block j's inputs are requested while block j - 1 runs (the request
     // after the last block reads clamped rows and is not used).
-    OwnRaw rn = own_raw<IO>(p, l, l.n);
+    OwnRaw rn = own_raw<IO, CONV>(p, l, l.n);
     uint32_t bn[kStep];
     load_rows_bits<IO>(p.Bm, p, l, 0, bn);
     for (int64_t j = 0; j < nb; ++j) {
         if (l.valid) p.ckpt[((j * p.B + l.b) * p.D + l.d) * kRowN + l.n] = h;
         float u, dt, bv[kStep];
-        own_finish<IO>(p, rn, wr, cb, bias, u, dt);
+        own_finish<IO, CONV>(p, rn, wr, cb, bias, u, dt);
 #pragma unroll
         for (int k = 0; k < kStep; ++k) bv[k] = bits_f32<IO>(bn[k]);
-        rn = own_raw<IO>(p, l, (j + 1) * kStep + l.n);
+        rn = own_raw<IO, CONV>(p, l, (j + 1) * kStep + l.n);
         load_rows_bits<IO>(p.Bm, p, l, (j + 1) * kStep, bn);
         sfor<kStep>([&](auto K) {
             constexpr int k = decltype(K)::value;
@@ -259,14 +259,16 @@ __device__ __forceinline__ void ckpt_body(const BwdParams &p, const LaneB &l, fl
     }
 }
 
-template <typename IO>
+// CONV: with the conv prologue (K > 0); a separate instance keeps the taps
+// out of the registers of the plain scan.
+template <typename IO, bool CONV>
 __global__ __launch_bounds__(64 * kWavesB) void bwd_ckpt_kernel(BwdParams p) {
     const LaneB l = lane_setup(p);
     const float a = l.valid ? p.A[l.d * kRowN + l.n] : 0.0f;
     const float ia = a != 0.0f ? 1.0f / a : 0.0f;
     const float h = (l.valid && p.h0) ? p.h0[(l.b * p.D + l.d) * kRowN + l.n] : 0.0f;
-    if (__all(!l.valid || fabsf(a) >= 0.0625f)) ckpt_body<IO, true>(p, l, a, ia, h);
-    else ckpt_body<IO, false>(p, l, a, ia, h);
+    if (__all(!l.valid || fabsf(a) >= 0.0625f)) ckpt_body<IO, true, CONV>(p, l, a, ia, h);
+    else ckpt_body<IO, false, CONV>(p, l, a, ia, h);
 }
 
 typedef float mfma4_t __attribute__((ext_vector_type(4)));
@@ -280,7 +282,7 @@ __device__ __forceinline__ float sum_channels(float v) {
 }
 
 // Pass 2: the adjoint, blocks from last to first.
-template <typename IO, bool FAST>
+template <typename IO, bool FAST, bool CONV>
 __device__ __forceinline__ void bwd_body(const BwdParams &p, const LaneB &l, float *lds, float a, float ia) {
     const int n = l.n, c = l.c;
     // Per wave: two transpose areas (channel c at c * kChArea, [n][k] with
@@ -299,7 +301,7 @@ __device__ __forceinline__ void bwd_body(const BwdParams &p, const LaneB &l, flo
     const int64_t grow = blockIdx.x % p.G;  // workgroup within the batch row
     float wr[4] = {0.0f, 0.0f, 0.0f, 0.0f};
     float cb = 0.0f;
-    if (p.K > 0 && l.valid) {
+    if (CONV && l.valid) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) wr[3 - q] = q < p.K ? p.conv_w[l.d * p.K + p.K - 1 - q] : 0.0f;
         cb = p.conv_b ? p.conv_b[l.d] : 0.0f;
@@ -309,14 +311,14 @@ __device__ __forceinline__ void bwd_body(const BwdParams &p, const LaneB &l, flo
     // adjoint is done (then the block's own registers are free), so that they
     // arrive while the sums and the workgroup reduction run.
     BlockRaw nx;
-    request_block<IO>(p, l, nb - 1, nx);
+    request_block<IO, CONV>(p, l, nb - 1, nx);
 
     for (int64_t j = nb - 1; j >= 0; --j) {
         const int64_t t0 = j * kStep;
         const int64_t tme = t0 + n;  // this lane's own step
         const bool live = nx.own.wm != 0;  // l.valid && tme < p.L
         float u, dt, bv[kStep], cv[kStep];
-        own_finish<IO>(p, nx.own, wr, cb, bias, u, dt);
+        own_finish<IO, CONV>(p, nx.own, wr, cb, bias, u, dt);
         const float raw = live ? bits_f32<IO>(nx.own.draw) : 0.0f;
         {
             uint32_t rb[kStep], rc[kStep];
@@ -400,7 +402,7 @@ __device__ __forceinline__ void bwd_body(const BwdParams &p, const LaneB &l, flo
             }
         });
         __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-        request_block<IO>(p, l, j > 0 ? j - 1 : 0, nx);  // the request after block 0 is not used
+        request_block<IO, CONV>(p, l, j > 0 ? j - 1 : 0, nx);  // the request after block 0 is not used
         {
             float du = dsk * gy, ddt = 0.0f;
 #pragma unroll
@@ -417,7 +419,7 @@ __device__ __forceinline__ void bwd_body(const BwdParams &p, const LaneB &l, flo
             }
             if (live) {
                 const int64_t i = (l.b * p.L + tme) * p.D + l.d;
-                if (p.K > 0) p.dU[i] = du;
+                if (CONV) p.dU[i] = du;
                 else store_io<IO>(p.dx, i, du);
                 store_io<IO>(p.ddelta, i, draw);
             }
@@ -452,15 +454,15 @@ __device__ __forceinline__ void bwd_body(const BwdParams &p, const LaneB &l, flo
     }
 }
 
-template <typename IO>
+template <typename IO, bool CONV>
 __global__ __launch_bounds__(64 * kWavesB) __attribute__((amdgpu_waves_per_eu(3, 3)))
 void bwd_kernel(BwdParams p) {
     extern __shared__ __attribute__((aligned(16))) float lds[];
     const LaneB l = lane_setup(p);
     const float a = l.valid ? p.A[l.d * kRowN + l.n] : 0.0f;
     const float ia = a != 0.0f ? 1.0f / a : 0.0f;
-    if (__all(!l.valid || fabsf(a) >= 0.0625f)) bwd_body<IO, true>(p, l, lds, a, ia);
-    else bwd_body<IO, false>(p, l, lds, a, ia);
+    if (__all(!l.valid || fabsf(a) >= 0.0625f)) bwd_body<IO, true, CONV>(p, l, lds, a, ia);
+    else bwd_body<IO, false, CONV>(p, l, lds, a, ia);
 }
 
 // Through the conv prologue (u = silu(c), c_t = b + sum_k w_k x_{t-K+1+k}):
@@ -612,11 +614,13 @@ template <typename IO>
 hipError_t launch_bwd_typed(const BwdParams &p, const ssm_scan_bwd_args_t &a, float *pconv, int64_t nch,
                             hipStream_t stream) {
     const unsigned grid = (unsigned)(p.G * p.B);
-    bwd_ckpt_kernel<IO><<<grid, 64 * kWavesB, 0, stream>>>(p);
+    if (p.K > 0) bwd_ckpt_kernel<IO, true><<<grid, 64 * kWavesB, 0, stream>>>(p);
+    else bwd_ckpt_kernel<IO, false><<<grid, 64 * kWavesB, 0, stream>>>(p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const size_t lds = (size_t)(kWavesB * (2 * kTrWave + kRedWave)) * sizeof(float);
-    bwd_kernel<IO><<<grid, 64 * kWavesB, lds, stream>>>(p);
+    if (p.K > 0) bwd_kernel<IO, true><<<grid, 64 * kWavesB, lds, stream>>>(p);
+    else bwd_kernel<IO, false><<<grid, 64 * kWavesB, lds, stream>>>(p);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t nbc = 2 * p.B * p.L * kRowN;
