@@ -281,8 +281,43 @@ __device__ __forceinline__ float sum_channels(float v) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(1.0f, v, zero, 0, 0, 0)[0];
 }
 
+// The B and C rows of a block, staged in LDS for the whole workgroup (bf16
+// I/O): [tensor][entry n][step k] as bf16, rows 40 bytes apart so that the 16
+// lanes of a row read their 8 bytes from distinct banks.  Threads 0..255
+// fetch one 4-byte pair of entries each (tensor q / 128, step (q % 128) / 8,
+// entries 2 (q % 8), +1) a block ahead and store it during the reduction.
+constexpr int kBcRow = 40;
+constexpr int kBcLdsBytes = 2 * kRowN * kBcRow;
+constexpr int kBcFetchers = 2 * kStep * kRowN / 2;
+__device__ __forceinline__ uint32_t bc_fetch(const BwdParams &p, int64_t b, int64_t jb, int q) {
+    const int tensor = q >> 7, s = (q & 127) >> 3, part = q & 7;
+    const int64_t t = jb * kStep + s;
+    const int64_t tc = t < p.L ? t : p.L - 1;  // past the end: the last row (unused there)
+    const uint16_t *base = static_cast<const uint16_t *>(tensor ? p.Cm : p.Bm);
+    return *reinterpret_cast<const uint32_t *>(base + (b * p.L + tc) * kRowN + 2 * part);
+}
+__device__ __forceinline__ void bc_store(char *bcl, uint32_t v, int q) {
+    const int tensor = q >> 7, s = (q & 127) >> 3, part = q & 7;
+    uint16_t *col = reinterpret_cast<uint16_t *>(bcl + (tensor * kRowN + 2 * part) * kBcRow) + s;
+    col[0] = (uint16_t)(v & 0xffffu);
+    col[kBcRow / 2] = (uint16_t)(v >> 16);
+}
+__device__ __forceinline__ void bc_read(const char *bcl, int tensor, int n, float (&v)[kStep]) {
+    const uint2 *row = reinterpret_cast<const uint2 *>(bcl + (tensor * kRowN + n) * kBcRow);
+#pragma unroll
+    for (int q = 0; q < kStep / 4; ++q) {
+        const uint2 d = row[q];
+        v[4 * q] = __uint_as_float(d.x << 16);
+        v[4 * q + 1] = __uint_as_float(d.x & 0xffff0000u);
+        v[4 * q + 2] = __uint_as_float(d.y << 16);
+        v[4 * q + 3] = __uint_as_float(d.y & 0xffff0000u);
+    }
+}
+
 // Pass 2: the adjoint, blocks from last to first.
-template <typename IO, bool FAST, bool CONV>
+// STAGE: B and C through the LDS tile above (bf16 with 4-byte aligned B, C);
+// otherwise every lane loads its entries of the 16 rows itself.
+template <typename IO, bool FAST, bool CONV, bool STAGE>
 __device__ __forceinline__ void bwd_body(const BwdParams &p, const LaneB &l, float *lds, float a, float ia) {
     const int n = l.n, c = l.c;
     // Per wave: two transpose areas (channel c at c * kChArea, [n][k] with
@@ -312,6 +347,13 @@ __device__ __forceinline__ void bwd_body(const BwdParams &p, const LaneB &l, flo
     // arrive while the sums and the workgroup reduction run.
     BlockRaw nx;
     request_block<IO, CONV>(p, l, nb - 1, nx);
+    char *bcl = reinterpret_cast<char *>(lds + kWavesB * (2 * kTrWave + kRedWave));
+    const int q = threadIdx.x;
+    uint32_t bcv = 0u;
+    if (STAGE) {
+        if (q < kBcFetchers) bc_store(bcl, bc_fetch(p, l.b, nb - 1, q), q);
+        __syncthreads();
+    }
 
     for (int64_t j = nb - 1; j >= 0; --j) {
         const int64_t t0 = j * kStep;
@@ -320,7 +362,10 @@ __device__ __forceinline__ void bwd_body(const BwdParams &p, const LaneB &l, flo
         float u, dt, bv[kStep], cv[kStep];
         own_finish<IO, CONV>(p, nx.own, wr, cb, bias, u, dt);
         const float raw = live ? bits_f32<IO>(nx.own.draw) : 0.0f;
-        {
+        if (STAGE) {
+            bc_read(bcl, 0, n, bv);
+            bc_read(bcl, 1, n, cv);
+        } else {
             uint32_t rb[kStep], rc[kStep];
             load_rows_bits<IO>(p.Bm, p, l, t0, rb);
             load_rows_bits<IO>(p.Cm, p, l, t0, rc);
@@ -403,6 +448,7 @@ __device__ __forceinline__ void bwd_body(const BwdParams &p, const LaneB &l, flo
         });
         __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
         request_block<IO, CONV>(p, l, j > 0 ? j - 1 : 0, nx);  // the request after block 0 is not used
+        if (STAGE && q < kBcFetchers) bcv = bc_fetch(p, l.b, j > 0 ? j - 1 : 0, q);
         {
             float du = dsk * gy, ddt = 0.0f;
 #pragma unroll
@@ -426,6 +472,8 @@ __device__ __forceinline__ void bwd_body(const BwdParams &p, const LaneB &l, flo
         }
         // -- dB, dC: add the workgroup's waves ---------------------------------
         __syncthreads();
+        // Every wave has read this block's B and C: the next block's replace them.
+        if (STAGE && q < kBcFetchers) bc_store(bcl, bcv, q);
         for (int item = threadIdx.x; item < 2 * kStep * kRowN; item += 64 * kWavesB) {
             const int tensor = item / (kStep * kRowN), kn = item % (kStep * kRowN);
             const int k = kn / kRowN, nn = kn % kRowN;
@@ -454,15 +502,15 @@ __device__ __forceinline__ void bwd_body(const BwdParams &p, const LaneB &l, flo
     }
 }
 
-template <typename IO, bool CONV>
+template <typename IO, bool CONV, bool STAGE>
 __global__ __launch_bounds__(64 * kWavesB) __attribute__((amdgpu_waves_per_eu(3, 3)))
 void bwd_kernel(BwdParams p) {
     extern __shared__ __attribute__((aligned(16))) float lds[];
     const LaneB l = lane_setup(p);
     const float a = l.valid ? p.A[l.d * kRowN + l.n] : 0.0f;
     const float ia = a != 0.0f ? 1.0f / a : 0.0f;
-    if (__all(!l.valid || fabsf(a) >= 0.0625f)) bwd_body<IO, true, CONV>(p, l, lds, a, ia);
-    else bwd_body<IO, false, CONV>(p, l, lds, a, ia);
+    if (__all(!l.valid || fabsf(a) >= 0.0625f)) bwd_body<IO, true, CONV, STAGE>(p, l, lds, a, ia);
+    else bwd_body<IO, false, CONV, STAGE>(p, l, lds, a, ia);
 }
 
 // Through the conv prologue (u = silu(c), c_t = b + sum_k w_k x_{t-K+1+k}):
@@ -619,8 +667,16 @@ hipError_t launch_bwd_typed(const BwdParams &p, const ssm_scan_bwd_args_t &a, fl
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const size_t lds = (size_t)(kWavesB * (2 * kTrWave + kRedWave)) * sizeof(float);
-    if (p.K > 0) bwd_kernel<IO, true><<<grid, 64 * kWavesB, lds, stream>>>(p);
-    else bwd_kernel<IO, false><<<grid, 64 * kWavesB, lds, stream>>>(p);
+    // B and C staged in LDS: bf16 rows read as 4-byte pairs.
+    const bool stage = sizeof(typename IO::storage) == 2 && (uintptr_t)p.Bm % 4 == 0 && (uintptr_t)p.Cm % 4 == 0;
+    if (stage) {
+        constexpr bool kStage = sizeof(typename IO::storage) == 2;
+        if (p.K > 0) bwd_kernel<IO, true, kStage><<<grid, 64 * kWavesB, lds + kBcLdsBytes, stream>>>(p);
+        else bwd_kernel<IO, false, kStage><<<grid, 64 * kWavesB, lds + kBcLdsBytes, stream>>>(p);
+    } else {
+        if (p.K > 0) bwd_kernel<IO, true, false><<<grid, 64 * kWavesB, lds, stream>>>(p);
+        else bwd_kernel<IO, false, false><<<grid, 64 * kWavesB, lds, stream>>>(p);
+    }
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t nbc = 2 * p.B * p.L * kRowN;
