@@ -119,10 +119,10 @@ __device__ __forceinline__ LaneB lane_setup(const BwdParams &p) {
 
 // Pass 1: states entering every block.
 // dt phi(dt A) = (e - 1)/A: in waves where every |A| >= 1/16 (FAST) as
-// (e - 1) times 1/A, otherwise through phi (series near 0).
+// e/A - 1/A in one fma, otherwise through phi (series near 0).
 template <bool FAST>
 __device__ __forceinline__ float dtphi(float dt, float a, float ia, float e) {
-    if (FAST) return (e - 1.0f) * ia;
+    if (FAST) return __builtin_fmaf(e, ia, -ia);
     const float zz = dt * a;
     return dt * phi_f(zz, e, hw_rcp(zz));
 }
