@@ -48,8 +48,9 @@ def source_hash(sources=None) -> str:
     import hashlib
     h = hashlib.sha256()
     names = sorted(os.listdir(CSRC)) if sources is None else sorted(sources)
-    if sources is not None:
-        h.update(" ".join(COMMON).encode() + b"\0")
+    if sources is not None:  # the flags, less the include path (it differs between checkouts)
+        flags = [f for i, f in enumerate(COMMON) if f != "-I" and (i == 0 or COMMON[i - 1] != "-I")]
+        h.update(" ".join(flags).encode() + b"\0")
     for n in names:
         with open(os.path.join(CSRC, n), "rb") as f:
             h.update(n.encode() + b"\0" + _code_only(f.read()))
