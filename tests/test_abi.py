@@ -517,3 +517,16 @@ def test_ssd_step_empty_batch_and_null_args():
     assert run_ssd_step(ssd_step_args(batch=0, state=None, x=None)) == ssm.SSM_OK
     assert ssm.lib().ssm_ssd_step(None, None) == ssm.SSM_ERR_NULL_ARG
 
+
+
+# ------------------------------------------------------------ measurement keys
+def test_kernel_source_hash_ignores_the_checkout_path(monkeypatch):
+    """The hash that keys committed counter readings to a kernel build covers the kernel's
+    sources and compile flags, not where the repository sits."""
+    from selective_state_space_59_amd import build as B
+    srcs = ["scan_fwd.hip", "ssm_device.h"]
+    ref = B.source_hash(srcs)
+    monkeypatch.setattr(B, "COMMON", [f.replace(ROOT, "/elsewhere/checkout") for f in B.COMMON])
+    assert B.source_hash(srcs) == ref
+    monkeypatch.setattr(B, "COMMON", B.COMMON + ["-DSOMETHING"])
+    assert B.source_hash(srcs) != ref
