@@ -225,8 +225,45 @@ __device__ __forceinline__ void request_block(const BwdParams &p, const LaneB &l
     r.h = p.ckpt[((jb * p.B + l.b) * p.D + dc) * kRowN + l.n];
 }
 
-template <typename IO, bool FAST, bool CONV>
-__device__ __forceinline__ void ckpt_body(const BwdParams &p, const LaneB &l, float a, float ia, float h) {
+// bf16 B (or C) tiles in LDS are [entry n][step k] with rows 40 bytes apart:
+// the 16 lanes of a row read 8 bytes each from distinct banks.
+constexpr int kBcRow = 40;
+// Entry n's 16 steps of tile `tensor` (of two consecutive tiles), widened.
+__device__ __forceinline__ void bc_read(const char *bcl, int tensor, int n, float (&v)[kStep]) {
+    const uint2 *row = reinterpret_cast<const uint2 *>(bcl + (tensor * kRowN + n) * kBcRow);
+#pragma unroll
+    for (int q = 0; q < kStep / 4; ++q) {
+        const uint2 d = row[q];
+        v[4 * q] = __uint_as_float(d.x << 16);
+        v[4 * q + 1] = __uint_as_float(d.x & 0xffff0000u);
+        v[4 * q + 2] = __uint_as_float(d.y << 16);
+        v[4 * q + 3] = __uint_as_float(d.y & 0xffff0000u);
+    }
+}
+
+// The checkpoint pass's B rows through a wave-private LDS tile (bf16 I/O,
+// 8-byte aligned B): lane q fetches entries 4 (q % 4) .. +3 of step q / 4 as
+// one 8-byte load, the wave writes them transposed ([entry][step], rows 40
+// bytes apart) and every lane reads its entry's 16 steps back (bc_read).  The
+// 4 channel rows of a wave share B, so this replaces 16 two-byte loads per
+// lane and block; LDS order within a wave needs no barrier.
+constexpr int kCkptTile = kRowN * kBcRow;
+__device__ __forceinline__ uint2 ckpt_fetch(const BwdParams &p, int64_t b, int64_t jb, int lane) {
+    const int64_t t = jb * kStep + (lane >> 2);
+    const int64_t tc = t < p.L ? t : p.L - 1;
+    return *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(p.Bm) + (b * p.L + tc) * kRowN + 4 * (lane & 3));
+}
+__device__ __forceinline__ void ckpt_store(char *tile, uint2 v, int lane) {
+    uint16_t *col = reinterpret_cast<uint16_t *>(tile + 4 * (lane & 3) * kBcRow) + (lane >> 2);
+    col[0] = (uint16_t)(v.x & 0xffffu);
+    col[kBcRow / 2] = (uint16_t)(v.x >> 16);
+    col[kBcRow] = (uint16_t)(v.y & 0xffffu);
+    col[3 * kBcRow / 2] = (uint16_t)(v.y >> 16);
+}
+
+template <typename IO, bool FAST, bool CONV, bool STAGE>
+__device__ __forceinline__ void ckpt_body(const BwdParams &p, const LaneB &l, float a, float ia, float h,
+                                          char *tile) {
     const float a2 = a * kLog2e;
     const int64_t nb = (p.L + kStep - 1) / kStep;
     float wr[4] = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -239,17 +276,27 @@ __device__ __forceinline__ void ckpt_body(const BwdParams &p, const LaneB &l, fl
     const float bias = (l.valid && p.dbias) ? p.dbias[l.d] : 0.0f;
     // Block j's inputs are requested while block j - 1 runs (the request
     // after the last block reads clamped rows and is not used).
+    const int lane = threadIdx.x & 63;
     OwnRaw rn = own_raw<IO, CONV>(p, l, l.n);
-    uint32_t bn[kStep];
-    load_rows_bits<IO>(p.Bm, p, l, 0, bn);
+    uint32_t bn[STAGE ? 1 : kStep];
+    uint2 bq = make_uint2(0u, 0u);
+    if (STAGE) bq = ckpt_fetch(p, l.b, 0, lane);
+    else load_rows_bits<IO>(p.Bm, p, l, 0, reinterpret_cast<uint32_t (&)[kStep]>(bn));
     for (int64_t j = 0; j < nb; ++j) {
         if (l.valid) p.ckpt[((j * p.B + l.b) * p.D + l.d) * kRowN + l.n] = h;
         float u, dt, bv[kStep];
         own_finish<IO, CONV>(p, rn, wr, cb, bias, u, dt);
+        if (STAGE) {
+            ckpt_store(tile, bq, lane);
+            __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+            bc_read(tile, 0, l.n, bv);
+            bq = ckpt_fetch(p, l.b, j + 1, lane);
+        } else {
 #pragma unroll
-        for (int k = 0; k < kStep; ++k) bv[k] = bits_f32<IO>(bn[k]);
+            for (int k = 0; k < kStep; ++k) bv[k] = bits_f32<IO>(bn[k]);
+            load_rows_bits<IO>(p.Bm, p, l, (j + 1) * kStep, reinterpret_cast<uint32_t (&)[kStep]>(bn));
+        }
         rn = own_raw<IO, CONV>(p, l, (j + 1) * kStep + l.n);
-        load_rows_bits<IO>(p.Bm, p, l, (j + 1) * kStep, bn);
         sfor<kStep>([&](auto K) {
             constexpr int k = decltype(K)::value;
             const float dtk = bcast_row<k>(dt), uk = bcast_row<k>(u);
@@ -260,15 +307,17 @@ __device__ __forceinline__ void ckpt_body(const BwdParams &p, const LaneB &l, fl
 }
 
 // CONV: with the conv prologue (K > 0); a separate instance keeps the taps
-// out of the registers of the plain scan.
-template <typename IO, bool CONV>
+// out of the registers of the plain scan.  STAGE: B through the wave tiles.
+template <typename IO, bool CONV, bool STAGE>
 __global__ __launch_bounds__(64 * kWavesB) void bwd_ckpt_kernel(BwdParams p) {
+    __shared__ __attribute__((aligned(16))) char tiles[STAGE ? kWavesB * kCkptTile : 16];
     const LaneB l = lane_setup(p);
+    char *tile = tiles + (STAGE ? l.wave * kCkptTile : 0);
     const float a = l.valid ? p.A[l.d * kRowN + l.n] : 0.0f;
     const float ia = a != 0.0f ? 1.0f / a : 0.0f;
     const float h = (l.valid && p.h0) ? p.h0[(l.b * p.D + l.d) * kRowN + l.n] : 0.0f;
-    if (__all(!l.valid || fabsf(a) >= 0.0625f)) ckpt_body<IO, true, CONV>(p, l, a, ia, h);
-    else ckpt_body<IO, false, CONV>(p, l, a, ia, h);
+    if (__all(!l.valid || fabsf(a) >= 0.0625f)) ckpt_body<IO, true, CONV, STAGE>(p, l, a, ia, h, tile);
+    else ckpt_body<IO, false, CONV, STAGE>(p, l, a, ia, h, tile);
 }
 
 typedef float mfma4_t __attribute__((ext_vector_type(4)));
@@ -286,7 +335,6 @@ __device__ __forceinline__ float sum_channels(float v) {
 // lanes of a row read their 8 bytes from distinct banks.  Threads 0..255
 // fetch one 4-byte pair of entries each (tensor q / 128, step (q % 128) / 8,
 // entries 2 (q % 8), +1) a block ahead and store it during the reduction.
-constexpr int kBcRow = 40;
 constexpr int kBcLdsBytes = 2 * kRowN * kBcRow;
 constexpr int kBcFetchers = 2 * kStep * kRowN / 2;
 __device__ __forceinline__ uint32_t bc_fetch(const BwdParams &p, int64_t b, int64_t jb, int q) {
@@ -301,17 +349,6 @@ __device__ __forceinline__ void bc_store(char *bcl, uint32_t v, int q) {
     uint16_t *col = reinterpret_cast<uint16_t *>(bcl + (tensor * kRowN + 2 * part) * kBcRow) + s;
     col[0] = (uint16_t)(v & 0xffffu);
     col[kBcRow / 2] = (uint16_t)(v >> 16);
-}
-__device__ __forceinline__ void bc_read(const char *bcl, int tensor, int n, float (&v)[kStep]) {
-    const uint2 *row = reinterpret_cast<const uint2 *>(bcl + (tensor * kRowN + n) * kBcRow);
-#pragma unroll
-    for (int q = 0; q < kStep / 4; ++q) {
-        const uint2 d = row[q];
-        v[4 * q] = __uint_as_float(d.x << 16);
-        v[4 * q + 1] = __uint_as_float(d.x & 0xffff0000u);
-        v[4 * q + 2] = __uint_as_float(d.y << 16);
-        v[4 * q + 3] = __uint_as_float(d.y & 0xffff0000u);
-    }
 }
 
 // Pass 2: the adjoint, blocks from last to first.
@@ -662,8 +699,14 @@ template <typename IO>
 hipError_t launch_bwd_typed(const BwdParams &p, const ssm_scan_bwd_args_t &a, float *pconv, int64_t nch,
                             hipStream_t stream) {
     const unsigned grid = (unsigned)(p.G * p.B);
-    if (p.K > 0) bwd_ckpt_kernel<IO, true><<<grid, 64 * kWavesB, 0, stream>>>(p);
-    else bwd_ckpt_kernel<IO, false><<<grid, 64 * kWavesB, 0, stream>>>(p);
+    constexpr bool kBf16 = sizeof(typename IO::storage) == 2;
+    if (kBf16 && (uintptr_t)p.Bm % 8 == 0) {
+        if (p.K > 0) bwd_ckpt_kernel<IO, true, kBf16><<<grid, 64 * kWavesB, 0, stream>>>(p);
+        else bwd_ckpt_kernel<IO, false, kBf16><<<grid, 64 * kWavesB, 0, stream>>>(p);
+    } else {
+        if (p.K > 0) bwd_ckpt_kernel<IO, true, false><<<grid, 64 * kWavesB, 0, stream>>>(p);
+        else bwd_ckpt_kernel<IO, false, false><<<grid, 64 * kWavesB, 0, stream>>>(p);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const size_t lds = (size_t)(kWavesB * (2 * kTrWave + kRedWave)) * sizeof(float);
