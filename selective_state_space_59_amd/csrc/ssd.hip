@@ -133,12 +133,6 @@ __device__ __forceinline__ ssd_s4 lds4(const uint16_t *p) {
     return __builtin_bit_cast(ssd_s4, *reinterpret_cast<const uint2 *>(p));
 }
 
-// Four bf16 entries of one column of a row-major LDS array (rows r .. r+3),
-// as an MFMA operand whose k index runs down the column.
-__device__ __forceinline__ ssd_s4 col4(const uint16_t *p, int ld) {
-    return ssd_s4{(short)p[0], (short)p[ld], (short)p[2 * ld], (short)p[3 * ld]};
-}
-
 __device__ __forceinline__ ssd_b8 lds8(const uint16_t *p) {
     return __builtin_bit_cast(ssd_b8, *reinterpret_cast<const uint4 *>(p));
 }
@@ -151,8 +145,29 @@ __device__ __forceinline__ ssd_b8 cat8(ssd_s4 a, ssd_s4 b) {
     return __builtin_bit_cast(ssd_b8, t);
 }
 
-// Eight entries of one column (rows r .. r+7).
-__device__ __forceinline__ ssd_b8 col8(const uint16_t *p, int ld) { return cat8(col4(p, ld), col4(p + 4 * ld, ld)); }
+// The state update's contracted index (the 32 steps of a half chunk) in the
+// slots of lane group g and element e (slot 8 g + e) is step
+//   8 c + 2 (g ^ c) + (e & 1),  c = e >> 1,
+// a permutation chosen so that the four lane groups' 2-byte column reads of
+// one element fall in four disjoint 32-byte bank ranges (rows 2 apart are 32
+// bytes apart in the bank cycle; rows 8 apart, the identity's choice, hit the
+// same banks).  The weighted x it pairs with is stored in slot order.
+__device__ __forceinline__ int ssd_slot_of_step(int s) {  // s in 0..63
+    const int c = (s >> 3) & 3, g = ((s >> 1) & 3) ^ c;
+    return (s & 32) + 8 * g + 2 * c + (s & 1);
+}
+// Row offsets (elements, row stride ld) of the steps of elements 2c, 2c + 1
+// for lane group g.
+__device__ __forceinline__ void ssd_slot_rows(int g, int ld, int (&off)[4]) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) off[c] = (8 * c + 2 * ((g ^ c) & 3)) * ld;
+}
+// The eight column entries of a lane's slots (p: the half chunk's first row).
+__device__ __forceinline__ ssd_b8 col8_slots(const uint16_t *p, const int (&off)[4], int ld) {
+    const ssd_s4 a = {(short)p[off[0]], (short)p[off[0] + ld], (short)p[off[1]], (short)p[off[1] + ld]};
+    const ssd_s4 b = {(short)p[off[2]], (short)p[off[2] + ld], (short)p[off[3]], (short)p[off[3] + ld]};
+    return cat8(a, b);
+}
 
 // Inclusive prefix sum over the 64 lanes of a wave: within each row of 16
 // lanes by DPP row shifts (lanes shifted in from outside the row read 0),
@@ -269,6 +284,9 @@ __global__ __launch_bounds__(kThreads, 2) void ssd_chunk_kernel(SsdParams p) {
     float *acum_s = reinterpret_cast<float *>(lds + Lay::scal) + 2 * kQ * w;
     float *wl_s = acum_s + kQ;
     const int r16 = lane & 15, q4 = 4 * (lane >> 4);
+    const int kslot = ssd_slot_of_step(lane);  // where step `lane` sits in XWT
+    int brow[4];
+    ssd_slot_rows(lane >> 4, nld, brow);
     const int64_t seg = (int64_t)blockIdx.x % p.nseg;
     const int64_t bhp = (int64_t)blockIdx.x / p.nseg;
     const int pt = (int)(bhp % (kP / kPT));
@@ -331,7 +349,7 @@ __global__ __launch_bounds__(kThreads, 2) void ssd_chunk_kernel(SsdParams p) {
         acum_s[lane] = acum;
         wl_s[lane] = wl;
 
-        // ---- X' = f x -> XWT[p][s] (hi, lo): wave w takes channels 8w .. 8w+7
+        // ---- X' = f x -> XWT[p][slot of s] (hi, lo): wave w takes channels 8w .. 8w+7
         // of step s = lane, one 16-byte row read (read after the middle barrier)
         {
             static_assert(kPT / 4 == 8, "one 16-byte piece of x per lane");
@@ -343,8 +361,8 @@ __global__ __launch_bounds__(kThreads, 2) void ssd_chunk_kernel(SsdParams p) {
                 const uint16_t xb = (uint16_t)(i % 2 ? wv[i / 2] >> 16 : wv[i / 2] & 0xffffu);
                 const float v = bf(xb) * fl;
                 const uint16_t hi = f32_to_bf16_bits(v);
-                XWT[pp * qld + lane] = hi;
-                XWT[Lay::xwt_plane + pp * qld + lane] = f32_to_bf16_bits(v - bf(hi));
+                XWT[pp * qld + kslot] = hi;
+                XWT[Lay::xwt_plane + pp * qld + kslot] = f32_to_bf16_bits(v - bf(hi));
             }
         }
 
@@ -489,13 +507,13 @@ __global__ __launch_bounds__(kThreads, 2) void ssd_chunk_kernel(SsdParams p) {
             for (int i = 0; i < NWT; ++i)
 #pragma unroll
                 for (int j = 0; j < kPTL; ++j) st[i][j] *= dend;
-            // slot (lane group, e) is step 32 kk + 2 q4 + e
+            // slot (lane group g, e) holds step 32 kk + 8 c + 2 (g ^ c) + (e & 1), c = e / 2
 #pragma unroll
             for (int kk = 0; kk < kQ / 32; ++kk) {
                 ssd_b8 bop[NWT];
 #pragma unroll
                 for (int i = 0; i < NWT; ++i)
-                    bop[i] = col8(Bs + (32 * kk + 2 * q4) * nld + 16 * my_nt(i) + r16, nld);
+                    bop[i] = col8_slots(Bs + 32 * kk * nld + 16 * my_nt(i) + r16, brow, nld);
 #pragma unroll
                 for (int j = 0; j < kPTL; ++j) {
                     const uint16_t *xp = XWT + (16 * j + r16) * qld + 32 * kk + 2 * q4;
