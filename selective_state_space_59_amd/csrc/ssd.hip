@@ -62,6 +62,9 @@ struct SsdLds {
     static constexpr int nld = N + kPadE;    // rows of N entries: Bs, Cs, HT
     static constexpr int tld = kPT + kPadE;  // rows of kPT entries: Xs, Zs (Ys)
     static constexpr int qld = kQ + kPadE;   // rows of kQ entries: XWT
+    // XT is read 8 bytes at a time only: rows 136 bytes apart put the 16 rows
+    // of one read in disjoint 8-byte bank slots (144, as XWT, pairs rows r, r + 8)
+    static constexpr int xld = kQ + 4;
     static constexpr size_t bs = 0;
     static constexpr size_t cs = bs + (size_t)kQ * nld * 2;
     static constexpr size_t xs = cs + (size_t)kQ * nld * 2;
@@ -69,14 +72,15 @@ struct SsdLds {
     // HT: [hi/lo plane][kPT channels][nld]
     static constexpr size_t ht = zs + (size_t)kQ * tld * 2;
     static constexpr size_t ht_plane = (size_t)kPT * nld;  // elements
-    // XWT: [hi/lo plane][kPT channels][qld]; then XT: x transposed, [kPT][qld]
+    // XWT: [hi/lo plane][kPT channels][qld]; then XT: x transposed, [kPT][xld]
     static constexpr size_t xwt = ht + 2 * ht_plane * 2;
     static constexpr size_t xwt_plane = (size_t)kPT * qld;
     static constexpr size_t xt = xwt + 2 * xwt_plane * 2;
-    static constexpr size_t dts = xt + xwt_plane * 2;
+    static constexpr size_t dts = xt + (size_t)kPT * xld * 2;  // 16-byte aligned (32 rows of 136 bytes)
     // per wave: the chunk's prefix sums of dt a, then its ZOH weights (lane = step)
     static constexpr size_t scal = dts + (size_t)kQ * sizeof(float);
     static constexpr size_t total = scal + (size_t)4 * 2 * kQ * sizeof(float);
+    static_assert(xt % 16 == 0 && dts % 16 == 0 && scal % 16 == 0, "16-byte aligned LDS arrays");
 };
 
 struct SsdParams {
@@ -253,7 +257,7 @@ __device__ __forceinline__ void store_chunk(const ChunkRegs<N> &r, uint16_t *Bs,
         const uint32_t wv[4] = {r.x.x, r.x.y, r.x.z, r.x.w};
 #pragma unroll
         for (int i = 0; i < 8; ++i)
-            XT[(c8 + i) * Lay::qld + s] = (uint16_t)(i % 2 ? wv[i / 2] >> 16 : wv[i / 2] & 0xffffu);
+            XT[(c8 + i) * Lay::xld + s] = (uint16_t)(i % 2 ? wv[i / 2] >> 16 : wv[i / 2] & 0xffffu);
     }
     if (tid < kQ) {
         float dt = bf(r.dt);
@@ -469,7 +473,7 @@ __global__ __launch_bounds__(kThreads, 2) void ssd_chunk_kernel(SsdParams p) {
                     const ssd_b8 ahi = cat8(mhi[2 * sp], mhi[2 * sp + 1]), alo = cat8(mlo[2 * sp], mlo[2 * sp + 1]);
     #pragma unroll
                     for (int j = 0; j < kPTL; ++j) {
-                        const uint16_t *xr = XT + (16 * j + r16) * qld;
+                        const uint16_t *xr = XT + (16 * j + r16) * Lay::xld;
                         const ssd_b8 xop = cat8(lds4(xr + s0 + q4), lds4(xr + s1 + q4));
                         acc[j] = SSD_MFMA32(ahi, xop, acc[j]);
                         acc[j] = SSD_MFMA32(alo, xop, acc[j]);
