@@ -261,8 +261,9 @@ _ws_cache = {}
 
 
 def _workspace(dev: torch.device, nbytes: int) -> torch.Tensor:
-    """Per-device cached scratch tensor (grown on demand; calls on one stream reuse it)."""
-    key = (dev.type, dev.index)
+    """Cached scratch tensor per device and stream (grown on demand).  Calls on one stream
+    run in order and share it; calls on different streams get different ones."""
+    key = (dev.type, dev.index, torch.cuda.current_stream(dev).cuda_stream)
     buf = _ws_cache.get(key)
     if buf is None or buf.numel() < nbytes:
         buf = torch.empty(max(nbytes, 1 << 20), dtype=torch.uint8, device=dev)

@@ -82,3 +82,29 @@ def test_outputs_outside_y_untouched():
     torch.cuda.synchronize()
     assert torch.isnan(buf[:2048].float()).all() and torch.isnan(buf[2048 + n:].float()).all()
     assert torch.isfinite(y.float()).all()
+
+
+def test_concurrent_streams_use_separate_workspaces():
+    """Two segmented scans (which need the workspace) launched on two streams at once give
+    the results of the same calls run one after the other: each stream has its own scratch."""
+    ins = [W.make_scan_inputs(1, 12000, 64, 16, io_dtype=torch.bfloat16, seed=60 + k, device=DEV, h0=True)
+           for k in range(2)]
+
+    def call(inp):
+        return ssm.selective_scan_fwd(inp["x"], inp["delta"], inp["A"], inp["Bm"], inp["Cm"],
+                                      Dskip=inp["Dskip"], z=inp["z"], h0=inp["h0"], return_final_state=True)
+
+    ref = [call(inp) for inp in ins]
+    torch.cuda.synchronize()
+    ref = [(y.clone(), h.clone()) for y, h in ref]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for s in streams:
+        s.wait_stream(torch.cuda.current_stream())
+    outs = []
+    for _ in range(3):
+        for inp, s in zip(ins, streams):
+            with torch.cuda.stream(s):
+                outs.append(call(inp))
+    torch.cuda.synchronize()
+    for i, (y, h) in enumerate(outs):
+        assert torch.equal(y, ref[i % 2][0]) and torch.equal(h, ref[i % 2][1]), i
