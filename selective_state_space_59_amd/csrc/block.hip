@@ -254,27 +254,37 @@ __global__ __launch_bounds__(256) void dtproj_kernel(const uint16_t *__restrict_
             }
         }
     }
-    __shared__ __attribute__((aligned(16))) uint16_t stage[4][64][72];
+    // Each wave stages its 64 x 64 outputs through its own LDS area, 32 rows at
+    // a time (18 KB per workgroup: six workgroups fit a CU, so the launch runs
+    // in one round), and stores them as 16-byte pieces.
+    __shared__ __attribute__((aligned(16))) uint16_t stage[4][32][72];
+    float4 bb[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int64_t d = d0 + 16 * i + kq;
-        const float4 bb = d < D ? *reinterpret_cast<const float4 *>(bias + d) : make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const dt_f32x4 v = acc[i][j];
-            const uint32_t lo = pack_bf16x2(softplus_fast(v[0] + bb.x), softplus_fast(v[1] + bb.y));
-            const uint32_t hi = pack_bf16x2(softplus_fast(v[2] + bb.z), softplus_fast(v[3] + bb.w));
-            *reinterpret_cast<uint2 *>(&stage[wave][16 * j + r16][16 * i + kq]) = make_uint2(lo, hi);
-        }
+        bb[i] = d < D ? *reinterpret_cast<const float4 *>(bias + d) : make_float4(0.f, 0.f, 0.f, 0.f);
     }
-    __syncthreads();
     const int c8 = (lane & 7) * 8;
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
-        const int row = 8 * s + (lane >> 3);
-        const int64_t m = m0 + row, d = d0 + c8;
-        if (m < M && d < D)
-            *reinterpret_cast<uint4 *>(dt + m * D + d) = *reinterpret_cast<const uint4 *>(&stage[wave][row][c8]);
+    for (int half = 0; half < 2; ++half) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj) {
+                const dt_f32x4 v = acc[i][2 * half + jj];
+                const uint32_t lo = pack_bf16x2(softplus_fast(v[0] + bb[i].x), softplus_fast(v[1] + bb[i].y));
+                const uint32_t hi = pack_bf16x2(softplus_fast(v[2] + bb[i].z), softplus_fast(v[3] + bb[i].w));
+                *reinterpret_cast<uint2 *>(&stage[wave][16 * jj + r16][16 * i + kq]) = make_uint2(lo, hi);
+            }
+        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const int row = 8 * s + (lane >> 3);
+            const int64_t m = m0 + 32 * half + row, d = d0 + c8;
+            if (m < M && d < D)
+                *reinterpret_cast<uint4 *>(dt + m * D + d) = *reinterpret_cast<const uint4 *>(&stage[wave][row][c8]);
+        }
+        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");  // reads done before the next half's writes
     }
 }
 
