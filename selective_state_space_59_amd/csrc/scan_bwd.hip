@@ -628,14 +628,42 @@ __global__ void conv_bwd_reduce_kernel(const float *pw, float *dw, float *db, in
 // dB, dC = sums of the workgroup partials of each batch row; fp32 outputs.
 __global__ void bwd_reduce_bc_kernel(const float *partBC, float *dB, float *dC, int64_t B, int64_t G,
                                      int64_t L) {
-    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // over 2 B L 16
-    const int64_t per = B * L * kRowN;
+    // 4 consecutive (step, entry) values of one (tensor, batch row) per thread, as 16-byte
+    // loads; four independent running sums over the workgroups (a fixed order), so the
+    // loads of the G partials overlap instead of waiting one for another.
+    const int64_t i = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
+    const int64_t per = B * L * kRowN;  // a multiple of 16
     if (i >= 2 * per) return;
     const int64_t tensor = i / per, r = i % per;
     const int64_t b = r / (L * kRowN), tn = r % (L * kRowN);
-    float s = 0.0f;
-    for (int64_t g = 0; g < G; ++g) s += partBC[((tensor * B + b) * G + g) * L * kRowN + tn];
-    (tensor == 0 ? dB : dC)[r] = s;
+    const int64_t gs = L * kRowN / 4;  // float4s between the partials of two workgroups
+    const float4 *src = reinterpret_cast<const float4 *>(partBC + (tensor * B + b) * G * L * kRowN + tn);
+    float4 acc[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) acc[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+    int64_t g = 0;
+    for (; g + 4 <= G; g += 4) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const float4 v = src[(g + u) * gs];
+            acc[u].x += v.x;
+            acc[u].y += v.y;
+            acc[u].z += v.z;
+            acc[u].w += v.w;
+        }
+    }
+    for (; g < G; ++g) {
+        const float4 v = src[g * gs];
+        acc[0].x += v.x;
+        acc[0].y += v.y;
+        acc[0].z += v.z;
+        acc[0].w += v.w;
+    }
+    float *dst = (tensor == 0 ? dB : dC) + r;
+    dst[0] = (acc[0].x + acc[1].x) + (acc[2].x + acc[3].x);
+    dst[1] = (acc[0].y + acc[1].y) + (acc[2].y + acc[3].y);
+    dst[2] = (acc[0].z + acc[1].z) + (acc[2].z + acc[3].z);
+    dst[3] = (acc[0].w + acc[1].w) + (acc[2].w + acc[3].w);
 }
 
 // dA, dDskip, ddelta_bias = sums over batch rows.
@@ -722,7 +750,7 @@ hipError_t launch_bwd_typed(const BwdParams &p, const ssm_scan_bwd_args_t &a, fl
     }
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int64_t nbc = 2 * p.B * p.L * kRowN;
+    const int64_t nbc = 2 * p.B * p.L * kRowN / 4;  // threads: 4 values each
     bwd_reduce_bc_kernel<<<(unsigned)((nbc + 255) / 256), 256, 0, stream>>>(p.partBC, a.dBm, a.dCm, p.B, p.G, p.L);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
