@@ -617,10 +617,20 @@ __global__ void conv_bwd_kernel(const void *x, const float *dU, const float *w, 
 __global__ void conv_bwd_reduce_kernel(const float *pw, float *dw, float *db, int64_t nparts, int64_t D, int K) {
     const int64_t d = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (d >= D) return;
-    float s[5] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
-    for (int64_t q = 0; q < nparts; ++q)
+    // four independent running sums over the partials (a fixed order), so their loads overlap
+    float acc[4][5] = {};
+    int64_t q = 0;
+    for (; q + 4 <= nparts; q += 4)
 #pragma unroll
-        for (int j = 0; j < 5; ++j) s[j] += pw[(q * D + d) * 5 + j];
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int j = 0; j < 5; ++j) acc[u][j] += pw[((q + u) * D + d) * 5 + j];
+    for (; q < nparts; ++q)
+#pragma unroll
+        for (int j = 0; j < 5; ++j) acc[0][j] += pw[(q * D + d) * 5 + j];
+    float s[5];
+#pragma unroll
+    for (int j = 0; j < 5; ++j) s[j] = (acc[0][j] + acc[1][j]) + (acc[2][j] + acc[3][j]);
     for (int k = 0; k < K; ++k) dw[d * K + k] = s[4 - K + k];
     if (db) db[d] = s[4];
 }
