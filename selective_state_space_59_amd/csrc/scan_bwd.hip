@@ -578,33 +578,49 @@ __global__ void conv_bwd_kernel(const void *x, const float *dU, const float *w, 
         xw[j + 1] = s >= 0 ? load_io<IO>(x, base + s * D) : 0.0f;
     }
     float db = 0.0f;
-    for (int64_t t = t0; t < t1 + 3; ++t) {
-        xw[0] = xw[1];
-        xw[1] = xw[2];
-        xw[2] = xw[3];
-        xw[3] = t < L ? load_io<IO>(x, base + t * D) : 0.0f;
-        float dc = 0.0f;
-        if (t < L) {
-            float c = bias;
+    // Steps in groups of 8 whose 16 loads are issued first (indices clamped into the
+    // tensors, values outside them masked), so they overlap.
+    constexpr int kG = 8;
+    for (int64_t tg = t0; tg < t1 + 3; tg += kG) {
+        float xg[kG], ug[kG];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) c = __builtin_fmaf(wr[j], xw[j], c);
-            dc = dU[base + t * D] * dsilu_f(c);
+        for (int u = 0; u < kG; ++u) {
+            const int64_t t = tg + u;
+            const int64_t tc = t < L ? t : t0;
+            xg[u] = load_io<IO>(x, base + tc * D);
+            ug[u] = dU[base + tc * D];
         }
-        if (t < t1) {
-            db += dc;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) dwr[j] = __builtin_fmaf(dc, xw[j], dwr[j]);
-        }
-        dcw[0] = dcw[1];
-        dcw[1] = dcw[2];
-        dcw[2] = dcw[3];
-        dcw[3] = dc;
-        const int64_t s = t - 3;
-        if (s >= t0 && s < t1) {
-            float v = 0.0f;
+        for (int u = 0; u < kG; ++u) {
+            const int64_t t = tg + u;
+            if (t >= t1 + 3) break;
+            xw[0] = xw[1];
+            xw[1] = xw[2];
+            xw[2] = xw[3];
+            xw[3] = t < L ? xg[u] : 0.0f;
+            float dc = 0.0f;
+            if (t < L) {
+                float c = bias;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) v = __builtin_fmaf(dcw[j], wr[3 - j], v);
-            store_io<IO>(dx, base + s * D, v);
+                for (int j = 0; j < 4; ++j) c = __builtin_fmaf(wr[j], xw[j], c);
+                dc = ug[u] * dsilu_f(c);
+            }
+            if (t < t1) {
+                db += dc;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) dwr[j] = __builtin_fmaf(dc, xw[j], dwr[j]);
+            }
+            dcw[0] = dcw[1];
+            dcw[1] = dcw[2];
+            dcw[2] = dcw[3];
+            dcw[3] = dc;
+            const int64_t s = t - 3;
+            if (s >= t0 && s < t1) {
+                float v = 0.0f;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) v = __builtin_fmaf(dcw[j], wr[3 - j], v);
+                store_io<IO>(dx, base + s * D, v);
+            }
         }
     }
     float *o = pw + ((ch * B + b) * D + d) * 5;
