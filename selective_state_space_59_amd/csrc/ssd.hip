@@ -77,7 +77,7 @@ struct SsdLds {
     static constexpr size_t xwt_plane = (size_t)kPT * qld;
     static constexpr size_t xt = xwt + 2 * xwt_plane * 2;
     static constexpr size_t dts = xt + (size_t)kPT * xld * 2;  // 16-byte aligned (32 rows of 136 bytes)
-    // per wave: the chunk's prefix sums of dt a, then its ZOH weights (lane = step)
+    // per wave: the chunk's prefix sums of dt a (times log2 e), then its ZOH weights (lane = step)
     static constexpr size_t scal = dts + (size_t)kQ * sizeof(float);
     static constexpr size_t total = scal + (size_t)4 * 2 * kQ * sizeof(float);
     static_assert(xt % 16 == 0 && dts % 16 == 0 && scal % 16 == 0, "16-byte aligned LDS arrays");
@@ -350,7 +350,7 @@ __global__ __launch_bounds__(kThreads, 2) void ssd_chunk_kernel(SsdParams p) {
         lsum += aend;
         const float wl = dtl * ssd_phi(zl, hw_exp2(zl * kLog2e));       // ZOH input weight
         const float fl = hw_exp2((aend - acum) * kLog2e) * wl;         // weight in the end state
-        acum_s[lane] = acum;
+        acum_s[lane] = acum * kLog2e;  // kept in log2 units: the readers exponentiate base 2
         wl_s[lane] = wl;
 
         // ---- X' = f x -> XWT[p][slot of s] (hi, lo): wave w takes channels 8w .. 8w+7
@@ -399,7 +399,7 @@ __global__ __launch_bounds__(kThreads, 2) void ssd_chunk_kernel(SsdParams p) {
             // (row t, k = s) of M X as it stands
             ssd_s4 mhi[kQ / 16], mlo[kQ / 16];
             {
-                const float at = acum_s[16 * tb + r16];
+                const float at = acum_s[16 * tb + r16];  // log2 units
     #pragma unroll
                 for (int sb = 0; sb < kQ / 16; ++sb) {
                     if (sb > tb) {  // above the diagonal (wave-uniform): all zero
@@ -410,10 +410,15 @@ __global__ __launch_bounds__(kThreads, 2) void ssd_chunk_kernel(SsdParams p) {
                     const float4 ws4 = *reinterpret_cast<const float4 *>(wl_s + 16 * sb + q4);
                     const float as[4] = {as4.x, as4.y, as4.z, as4.w}, ws[4] = {ws4.x, ws4.y, ws4.z, ws4.w};
                     float m[4];
+                    if (sb < tb) {  // below the diagonal (wave-uniform): every s <= t
     #pragma unroll
-                    for (int v = 0; v < 4; ++v) {
-                        const int s = 16 * sb + q4 + v;
-                        m[v] = s <= 16 * tb + r16 ? gacc[sb][v] * hw_exp2((at - as[v]) * kLog2e) * ws[v] : 0.0f;
+                        for (int v = 0; v < 4; ++v) m[v] = gacc[sb][v] * hw_exp2(at - as[v]) * ws[v];
+                    } else {
+    #pragma unroll
+                        for (int v = 0; v < 4; ++v) {
+                            const int s = 16 * sb + q4 + v;
+                            m[v] = s <= 16 * tb + r16 ? gacc[sb][v] * hw_exp2(at - as[v]) * ws[v] : 0.0f;
+                        }
                     }
                     uint2 hi, lo;
                     split4(m, hi, lo);
@@ -454,10 +459,10 @@ __global__ __launch_bounds__(kThreads, 2) void ssd_chunk_kernel(SsdParams p) {
                 float dec[4];
                 {
                     const float4 a4 = *reinterpret_cast<const float4 *>(acum_s + 16 * tb + q4);
-                    dec[0] = hw_exp2(a4.x * kLog2e);
-                    dec[1] = hw_exp2(a4.y * kLog2e);
-                    dec[2] = hw_exp2(a4.z * kLog2e);
-                    dec[3] = hw_exp2(a4.w * kLog2e);
+                    dec[0] = hw_exp2(a4.x);
+                    dec[1] = hw_exp2(a4.y);
+                    dec[2] = hw_exp2(a4.z);
+                    dec[3] = hw_exp2(a4.w);
                 }
     #pragma unroll
                 for (int j = 0; j < kPTL; ++j) {
