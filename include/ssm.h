@@ -399,9 +399,11 @@ size_t ssm_ssd_workspace_size(const ssm_ssd_args_t *args);
 ssm_status_t ssm_ssd_fwd(const ssm_ssd_args_t *args, void *stream);
 
 /*
- * One decode step of the SSD layer: the recurrence above for a single token
- * on a state kept between calls (updated IN PLACE), for every batch b, head
- * h, head channel p and state entry n (g = h / (H / G)):
+ * One decode step of the SSD layer: the recurrence above ([P4] sec. 5.1, the
+ * state matrix a_t I per step; the recurrent mode of [P1] sec. 4b used for
+ * decoding) for a single token on a state kept between calls (updated IN
+ * PLACE), for every batch b, head h, head channel p and state entry n
+ * (g = h / (H / G)):
  *   dt = delta[b,h] (or softplus(delta[b,h] + delta_bias[h]))
  *   state[b,h,p,n] <- exp(dt A[h]) state[b,h,p,n] + w(dt, A[h]) Bm[b,g,n] x[b,h,p]
  *   y[b,h,p] = (sum_n Cm[b,g,n] state[b,h,p,n] + Dskip[h] x[b,h,p]) * silu(z[b,h,p])
