@@ -2,17 +2,20 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extras] [--no-cpu-baseline]
 
-A step is one selective-scan forward over one batch of the Mamba-130M-like
-layer workload (B=8, L=2048, D=1536, N=16, bf16 I/O, fp32 state, SiLU gate,
-D skip).  Three independent input sets (3 x 202 MB) rotate between steps, so
-the 256 MB last-level cache cannot hold the next step's inputs.  Inputs are
-resident in HBM before the timed region starts.
+A step is one selective-scan forward over the 1M-token DNA-like workload
+(B=1, L=1,048,576, D=1024, N=16, bf16 I/O, fp32 state, SiLU gate, D skip,
+final state out), the largest scan configuration that one GPU holds.  The
+sequence is scanned in 16 segments at once: a segment pass, a combine of the
+segments' end states and a rescan of each segment's head, three launches per
+step.  Inputs (8.6 GB) are resident in HBM before the timed region starts;
+every timed call goes straight to the C ABI with arguments marshalled once.
 
 Prints ONE JSON line.  `value` is algorithmic HBM bytes per second (GB/s):
 the minimum bytes a scan must move (each of x, delta, z read once, y written
-once, the B/C rows read once, A and D once) divided by the time per step.
-`roofline` relates the kernel to the MI355X HBM peak and to the vector-ALU
-peak; `cpu_baseline` times the fp64 oracle on the host cores.
+once, the B/C rows read once, A and D once, the final state written once)
+divided by the time per step.  `roofline` relates that to the MI355X HBM
+peak, with the vector-ALU view beside it; `cpu_baseline` times the fp64
+oracle on the host cores over a bounded prefix of the same sequence.
 """
 from __future__ import annotations
 
@@ -100,30 +103,53 @@ def time_launches(fn, steps, warmup):
     return start.elapsed_time(stop) / steps  # ms per launch
 
 
-def bench_scan(cfg, steps, warmup, nsets=3, final_state=False):
+def bench_scan(cfg, steps, warmup, nsets=1):
+    """The scan of `cfg` over `nsets` independent input sets (rotated between steps so a
+    set that fits the last-level cache is not read back from it).  Every set's arguments
+    are checked and marshalled once; the timed calls go straight to the C ABI."""
     import torch
     import selective_state_space_59_amd as ssm
     from selective_state_space_59_amd import workloads as W
     dev = "cuda:0"
     sets = [W.make_config_inputs(cfg, device=dev, seed=cfg.seed + 100 * k) for k in range(nsets)]
-    ys = [torch.empty_like(s["x"]) for s in sets]
-    hfs = [torch.empty(cfg.batch, cfg.dim, cfg.dstate, device=dev) if final_state else None
-           for _ in sets]
+    args = []
+    for s in sets:
+        hf = (torch.empty(cfg.batch, cfg.dim, cfg.dstate, device=dev) if cfg.final_state
+              else None)
+        args.append((hf,) + ssm.selective_scan_args(
+            s["x"], s["delta"], s["A"], s["Bm"], s["Cm"], Dskip=s["Dskip"], z=s["z"],
+            conv_w=s["conv_w"], h_final=hf))
+    L = ssm.lib()
+    stream = torch.cuda.current_stream().cuda_stream
 
     def run(i):
-        s = sets[i % nsets]
-        ssm.selective_scan_fwd(s["x"], s["delta"], s["A"], s["Bm"], s["Cm"], Dskip=s["Dskip"],
-                               z=s["z"], conv_w=s["conv_w"], y=ys[i % nsets],
-                               h_final=hfs[i % nsets])
+        st = L.ssm_selective_scan_fwd(ctypes.byref(args[i % nsets][1]), stream)
+        if st != 0:
+            raise RuntimeError("ssm_selective_scan_fwd: %s" % ssm.status_string(st))
 
     ms = time_launches(run, steps, warmup)
     nbytes = scan_algorithmic_bytes(cfg.batch, cfg.seqlen, cfg.dim, cfg.dstate,
                                     2 if cfg.io_dtype == torch.bfloat16 else 4, cfg.conv_k,
-                                    final_state, gate=cfg.gate, skip=cfg.skip)
+                                    cfg.final_state, gate=cfg.gate, skip=cfg.skip)
     first = sets[0]
-    del sets, ys, hfs
+    del sets, args
     torch.cuda.empty_cache()
     return ms, nbytes, first
+
+
+def scan_entry(cfg, ms, nbytes):
+    """Throughput figures of one timed scan configuration, in the HBM frame (algorithmic
+    bytes over time against the 8 TB/s peak) with the vector-ALU frame beside it."""
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    upd = cfg.elems * cfg.dstate
+    alu = SLOTS_PER_UPDATE * upd / (ms * 1e-3) / 1e12
+    return dict(ms=round(ms, 5), gbs=round(gbs, 2), frac_hbm=round(gbs / HBM_PEAK_GBS, 4),
+                elems_per_s=round(cfg.elems / (ms * 1e-3), 1), algorithmic_bytes=nbytes,
+                valu=dict(achieved=round(alu, 3), peak=round(VALU_PEAK_LANE_SLOTS / 1e12, 2),
+                          unit="T VALU lane-slots/s",
+                          frac=round(alu * 1e12 / VALU_PEAK_LANE_SLOTS, 4),
+                          algorithmic_slots_per_update=SLOTS_PER_UPDATE,
+                          state_updates_per_launch=upd))
 
 
 def bwd_algorithmic_bytes(B, L, D, N, io_bytes, gate=True, skip=True, conv_k=0):
@@ -249,35 +275,40 @@ def bench_decode(cfg, reps=3, conv_k=0):
     return hot_ms, cold_ms, nbytes
 
 
-def cpu_baseline(inp, cfg, min_seconds=10.0, max_passes=60):
-    """The fp64 oracle as it stands, on the host cores, over the whole workload of one input
-    set, repeated until about `min_seconds` of CPU work have run (the mean pass is reported)."""
+def cpu_baseline(inp, cfg, min_seconds=10.0, block_rows=8192):
+    """The fp64 oracle as it stands, on the host cores, over a prefix of the workload: the
+    sequence is streamed in `block_rows`-row blocks (every batch row and channel), each
+    entered with the previous block's final state as h0, until about `min_seconds` of
+    oracle time have run or the sequence ends.  Only the oracle calls are timed (not the
+    copies from the device or the widening to float64)."""
     import oracle
     nthreads = oracle.default_threads()
-    Lb = cfg.seqlen
-    f = lambda t: None if t is None else t[:, :Lb].double().cpu().numpy()
     g = lambda t: None if t is None else t.double().cpu().numpy()
-    args = (f(inp["x"]), f(inp["delta"]), g(inp["A"]), f(inp["Bm"]), f(inp["Cm"]))
-    kw = dict(Dskip=g(inp["Dskip"]), z=f(inp["z"]), conv_w=g(inp["conv_w"]), nthreads=nthreads)
-    passes = 0
-    t0 = time.perf_counter()
-    while True:
-        oracle.selective_scan(*args, **kw)
-        passes += 1
-        if time.perf_counter() - t0 >= min_seconds or passes >= max_passes:
-            break
-    total = time.perf_counter() - t0
-    dt = total / passes
-    elems = cfg.batch * Lb * cfg.dim
-    nbytes = scan_algorithmic_bytes(cfg.batch, Lb, cfg.dim, cfg.dstate,
+    A, Dskip, conv_w = g(inp["A"]), g(inp["Dskip"]), g(inp["conv_w"])
+    h = None
+    rows = 0
+    spent = 0.0
+    while rows < cfg.seqlen and spent < min_seconds:
+        r1 = min(cfg.seqlen, rows + block_rows)
+        f = lambda t: None if t is None else t[:, rows:r1].cpu().double().numpy()
+        args = (f(inp["x"]), f(inp["delta"]), A, f(inp["Bm"]), f(inp["Cm"]))
+        kw = dict(Dskip=Dskip, z=f(inp["z"]), conv_w=conv_w, h0=h, nthreads=nthreads)
+        if conv_w is not None and rows > 0:
+            raise RuntimeError("the streamed baseline does not carry a conv state")
+        t0 = time.perf_counter()
+        _, h = oracle.selective_scan(*args, **kw)
+        spent += time.perf_counter() - t0
+        rows = r1
+    elems = cfg.batch * rows * cfg.dim
+    nbytes = scan_algorithmic_bytes(cfg.batch, rows, cfg.dim, cfg.dstate,
                                     2 if str(inp["x"].dtype).endswith("bfloat16") else 4,
-                                    cfg.conv_k, gate=cfg.gate, skip=cfg.skip)
-    return dict(value=round(nbytes / dt / 1e9, 4), unit="GB/s", cores=nthreads, kind="oracle",
-                elems_per_s=round(elems / dt, 1), seconds_per_pass=round(dt, 3),
-                seconds_total=round(total, 2), passes=passes,
-                sample="%d full passes of the workload (B=%d, L=%d, D=%d, N=%d), fp64, "
-                       "%d threads over independent channels; mean pass reported"
-                       % (passes, cfg.batch, Lb, cfg.dim, cfg.dstate, nthreads))
+                                    cfg.conv_k, cfg.final_state, gate=cfg.gate, skip=cfg.skip)
+    return dict(value=round(nbytes / spent / 1e9, 4), unit="GB/s", cores=nthreads, kind="oracle",
+                elems_per_s=round(elems / spent, 1), seconds=round(spent, 2), rows=rows,
+                sample="the first %d of %d rows of the workload (B=%d, D=%d, N=%d), in "
+                       "%d-row blocks chained through the final state; fp64, %d threads "
+                       "over independent channels" % (rows, cfg.seqlen, cfg.batch, cfg.dim,
+                                                      cfg.dstate, block_rows, nthreads))
 
 
 def ssd_algorithmic(cfg, chunk=64):
@@ -410,14 +441,16 @@ def block_entry(cfg, steps, warmup):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=500)
-    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-extras", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=("block", "ssd", "ssd_long", "ssd_decode"),
-                    help="only time the 130M-like Mamba block forward, the Mamba-2 130M-like "
-                         "SSD layer, that layer on one 65536-token sequence, or the 2.7B-like "
-                         "SSD decode step, and print its numbers")
+    ap.add_argument("--only", choices=("c2", "c3", "c4", "block", "ssd", "ssd_long", "ssd_decode"),
+                    help="only time one scan config (the 130M-like layer, the 2.8B-like layer "
+                         "with its conv, the 1M-token sequence), the 130M-like Mamba block "
+                         "forward, the Mamba-2 130M-like SSD layer, that layer on one "
+                         "65536-token sequence, or the 2.7B-like SSD decode step, and print "
+                         "its numbers")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (fp32) five times; its "
                          "FETCH_SIZE / WRITE_SIZE counters scale the scan's traffic counters")
@@ -455,24 +488,27 @@ def main():
         print(json.dumps({c.name: ssd_step_entry(c)}), flush=True)
         return
 
-    cfg = W.C2_130M
+    if args.only in ("c2", "c3", "c4"):
+        c = {"c2": W.C2_130M, "c3": W.C3_2P8B_CONV, "c4": W.C4_DNA_1M}[args.only]
+        ms, nb, _ = bench_scan(c, args.steps, args.warmup, nsets=3 if c.elems < 1e8 else 1)
+        print(json.dumps({c.name: scan_entry(c, ms, nb)}), flush=True)
+        return
+
+    cfg = W.C4_DNA_1M
     print("bench: %s, %d warmup + %d timed steps" % (cfg.name, args.warmup, args.steps),
           file=sys.stderr, flush=True)
     ms, nbytes, first = bench_scan(cfg, args.steps, args.warmup)
+    ent = scan_entry(cfg, ms, nbytes)
     gbs = nbytes / (ms * 1e-3) / 1e9
-    elems = cfg.elems
-    upd = elems * cfg.dstate
-    traffic = _counter_traffic("scan_" + cfg.name)
-    # The scan is bound by the vector ALU (7 lane-slots per update against
-    # 8 bytes per 16 updates of HBM traffic); the HBM view is reported beside it.
-    alu = SLOTS_PER_UPDATE * upd / (ms * 1e-3) / 1e12
-    alu_peak = VALU_PEAK_LANE_SLOTS / 1e12
-    roof = dict(bound="alu", achieved=round(alu, 3), peak=round(alu_peak, 2),
-                unit="T VALU lane-slots/s", frac=round(alu / alu_peak, 4), traffic=traffic,
-                algorithmic_slots_per_update=SLOTS_PER_UPDATE, state_updates_per_launch=upd,
-                launch_ms=round(ms, 5), state_updates_per_s=round(upd / (ms * 1e-3), 1),
-                hbm=dict(achieved=round(gbs, 2), peak=HBM_PEAK_GBS, unit="GB/s",
-                         frac=round(gbs / HBM_PEAK_GBS, 4), algorithmic_bytes_per_launch=nbytes))
+    # The dominant kernel is the scan itself; one step is its segment pass, the
+    # combine of the segments' end states and the rescan of the segments' heads.
+    roof = dict(bound="hbm", achieved=round(gbs, 2), peak=HBM_PEAK_GBS, unit="GB/s",
+                frac=round(gbs / HBM_PEAK_GBS, 4),
+                traffic=_counter_traffic("scan_" + cfg.name),
+                algorithmic_bytes_per_launch=nbytes, launch_ms=round(ms, 5),
+                launch="one ssm_selective_scan_fwd call: scan_tiles_kernel segment pass + "
+                       "seg_combine_kernel + scan_tiles_kernel head pass",
+                valu=ent["valu"])
 
     out = {
         "metric": METRIC,
@@ -489,22 +525,20 @@ def main():
         "data": "synthetic",
         "config": {"workload": cfg.name, "batch": cfg.batch, "seq_len": cfg.seqlen,
                    "dim": cfg.dim, "dstate": cfg.dstate, "io_dtype": "bf16",
-                   "gate": cfg.gate, "skip": cfg.skip, "input_sets_rotated": 3,
-                   "parallelism": "single GPU"},
-        "elems_per_s": round(elems / (ms * 1e-3), 1),
+                   "state_dtype": "f32", "gate": cfg.gate, "skip": cfg.skip,
+                   "final_state": cfg.final_state, "parallelism": "single GPU"},
+        "elems_per_s": ent["elems_per_s"],
         "roofline": roof,
     }
 
     if not args.no_extras:
         extra = {}
-        for c in (W.C3_2P8B_CONV, W.C4_DNA_1M):
+        for c in (W.C2_130M, W.C3_2P8B_CONV):
             print("bench extra: %s" % c.name, file=sys.stderr, flush=True)
-            reps, warm = (5, 2) if c.seqlen > 100000 else (30, 5)
-            cms, cb, _ = bench_scan(c, reps, warm, nsets=1, final_state=c.final_state)
-            extra[c.name] = dict(ms=round(cms, 4), gbs=round(cb / (cms * 1e-3) / 1e9, 2),
-                                 frac_hbm=round(cb / (cms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                                 elems_per_s=round(c.elems / (cms * 1e-3), 1),
-                                 algorithmic_bytes=cb)
+            nsets = 3 if c.elems < 1e8 else 1   # the 130M-like set (202 MB) fits the cache
+            cms, cb, _ = bench_scan(c, 200 if nsets > 1 else 50, 20, nsets=nsets)
+            extra[c.name] = scan_entry(c, cms, cb)
+            extra[c.name]["input_sets_rotated"] = nsets
         # the backward pass (gradients of every input) of the 130M-like layer
         # and of the 2.8B-like layer with its conv prologue
         for c in (W.C2_130M, W.C3_2P8B_CONV):
@@ -543,6 +577,7 @@ def main():
     if not args.no_cpu_baseline:
         print("bench: cpu baseline (oracle)", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(first, cfg)
+    del first
     print(json.dumps(out), flush=True)
 
 

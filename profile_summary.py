@@ -1,13 +1,13 @@
 """Condense rocprofv3 CSV output into the short summaries kept under profiles/.
 
     # per-kernel durations of a --kernel-trace --stats run
-    python -m selective_state_space_59_amd.profile_summary stats \\
+    python profile_summary.py stats \\
         --csv OUT_kernel_stats.csv --command "rocprofv3 ..." --out profiles/NAME.md
 
     # HBM bytes per launch of one kernel from two --pmc runs (FETCH_SIZE, then
     # WRITE_SIZE), each scaled by what the same counter reads for a plain
     # device copy of known size (bench.py --copy-calibration MIB)
-    python -m selective_state_space_59_amd.profile_summary counters \\
+    python profile_summary.py counters \\
         --fetch A_counter_collection.csv --write B_counter_collection.csv \\
         --copy-fetch C_counter_collection.csv --copy-write D_counter_collection.csv \\
         --copy-bytes BYTES --kernel SUBSTRING --key NAME --algorithmic-bytes N \\
@@ -75,7 +75,7 @@ def cmd_counters(a):
     fb = statistics.median(fetch) * 1024.0 * fscale
     wb = statistics.median(write) * 1024.0 * wscale
     total = fb + wb
-    sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
     from selective_state_space_59_amd import build
     sources = sorted(a.sources) if a.sources else None
     entry = dict(source_hash=build.source_hash(sources), sources=sources, kernel=a.kernel,

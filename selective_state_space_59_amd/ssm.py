@@ -262,7 +262,14 @@ _ws_cache = {}
 
 def _workspace(dev: torch.device, nbytes: int) -> torch.Tensor:
     """Cached scratch tensor per device and stream (grown on demand).  Calls on one stream
-    run in order and share it; calls on different streams get different ones."""
+    run in order and share it; calls on different streams get different ones.
+
+    A call made while the current stream is being captured into a HIP graph gets a fresh
+    tensor of its own instead: every capture without an explicit stream runs on the same
+    side stream, and two graphs that recorded one cached buffer would race on it when
+    replayed at the same time.  The graph's memory pool keeps that tensor alive."""
+    if torch.cuda.is_current_stream_capturing():
+        return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
     key = (dev.type, dev.index, torch.cuda.current_stream(dev).cuda_stream)
     buf = _ws_cache.get(key)
     if buf is None or buf.numel() < nbytes:
@@ -325,6 +332,28 @@ def selective_scan_fwd(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, Bm
         a.workspace_bytes = ws.numel() * ws.element_size()
     _check(lib().ssm_selective_scan_fwd(ctypes.byref(a), _stream(dev)), "ssm_selective_scan_fwd")
     return (y, h_final, conv_state_out) if want_cs else (y, h_final)
+
+
+def selective_scan_args(x, delta, A, Bm, Cm, Dskip=None, z=None, delta_bias=None,
+                        delta_softplus=False, conv_w=None, conv_b=None, h0=None, y=None,
+                        h_final=None, conv_state_in=None, conv_state_out=None):
+    """The checked ssm_scan_args_t of a selective_scan_fwd call with a workspace of its own,
+    for callers that launch the same scan repeatedly through lib().ssm_selective_scan_fwd.
+    Returns (args, y, workspace or None); y is allocated when not given.  The tensors must
+    outlive the struct."""
+    if y is None:
+        y = torch.empty_like(x)
+    a, dev = _scan_args(x, delta, A, Bm, Cm, Dskip, z, delta_bias, delta_softplus, conv_w,
+                        conv_b, h0, y, h_final, conv_state_in, conv_state_out)
+    need = lib().ssm_selective_scan_workspace_size(ctypes.byref(a))
+    if need == ctypes.c_size_t(-1).value:
+        _check(lib().ssm_selective_scan_fwd(ctypes.byref(a), None), "ssm_selective_scan_fwd")
+    ws = None
+    if need > 0:
+        ws = torch.empty(need, dtype=torch.uint8, device=dev)
+        a.workspace = ws.data_ptr()
+        a.workspace_bytes = need
+    return a, y, ws
 
 
 def causal_conv1d_silu(x: torch.Tensor, w: torch.Tensor, bias: Optional[torch.Tensor] = None,

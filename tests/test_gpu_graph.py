@@ -5,7 +5,9 @@ is captured into a torch CUDA graph (on ROCm a HIP graph) after an eager
 warm-up, then replayed several times with eager work and synchronisations in
 between; each replay must give exactly the bits of the same call run eagerly.
 The library issues no memsets, allocations or synchronisations inside its
-calls, so its launches record as plain kernel nodes.
+calls, so its launches record as plain kernel nodes.  A workspace the binding
+needs during a capture is a fresh tensor from the graph's own memory pool,
+never the binding's cached one.
 """
 import pytest
 import torch
@@ -22,7 +24,7 @@ def _capture(fn):
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
-        fn()  # warm-up: any workspace is allocated here, outside the capture
+        fn()  # eager warm-up on a side stream (library load, plan and GEMM set-up)
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
