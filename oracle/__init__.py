@@ -268,7 +268,7 @@ def rms_norm(h, weight, eps=1e-5):
 
 
 def mamba_block_fwd(h, norm_w, w_in, conv_w, conv_b, w_x, w_dt, dt_bias, A, Dskip, w_out,
-                    eps=1e-5, bf16=True, nthreads: Optional[int] = None):
+                    eps=1e-5, bf16=True, perturb=None, nthreads: Optional[int] = None):
     """One Mamba (S6) block with its pre-norm residual, in float64:
 
       hn = RMSNorm(h);  x, z = hn W_in[:D]^T, hn W_in[D:]^T        (in_proj, split)
@@ -281,10 +281,20 @@ def mamba_block_fwd(h, norm_w, w_in, conv_w, conv_b, w_x, w_dt, dt_bias, A, Dski
     Selective State Spaces" (sec. 4a; the projections and dt_rank of Algorithm 2).
     Shapes: h (B,L,d_model); norm_w (d_model,); w_in (2D, d_model); conv_w (D,K); conv_b (D,);
     w_x (R+2N, D); w_dt (D, R); dt_bias (D,); A (D,N); Dskip (D,); w_out (d_model, D).
-    With bf16=True every tensor the GPU path stores in bf16 (hn, x, z, u, dt_low, B, C, the
-    step dt = softplus(delta + dt_bias), y and h_out) is rounded to bf16 at the same point here.
+
+    bf16=True rounds the output of every operation of that list to bf16 (the block's
+    activations are bf16 tensors between its operations): hn, x, z, u, the x_proj outputs
+    dt_low, B, C, the step dt = softplus(dt_low W_dt^T + dt_bias) (the tau_Delta of
+    Algorithm 2 is one operation), y and h_out.  bf16=False rounds nothing.
+    perturb, if given, is applied after that rounding to every one of those tensors and to
+    the two values inside an operation, the conv output before its SiLU and the step before
+    its softplus; it is how the error bound of `mamba_block_error_bound` is exercised.
     """
     r = round_bf16 if bf16 else (lambda v: v)
+    if perturb is not None:
+        rr = r
+        r = lambda v: perturb(rr(v))
+    q = perturb if perturb is not None else (lambda v: v)
     h = _f64(h)
     D = w_in.shape[0] // 2
     N = A.shape[1]
@@ -293,12 +303,163 @@ def mamba_block_fwd(h, norm_w, w_in, conv_w, conv_b, w_x, w_dt, dt_bias, A, Dski
     hn = r(rms_norm(h, norm_w, eps))
     x = r(hn @ w_in[:D].T)
     z = r(hn @ w_in[D:].T)
-    u = r(causal_conv1d_silu(x, conv_w, conv_b, nthreads=nthreads))
+    if perturb is None:
+        u = r(causal_conv1d_silu(x, conv_w, conv_b, nthreads=nthreads))
+    else:
+        c = q(_causal_conv1d(x, conv_w, conv_b))
+        u = r(c / (1.0 + np.exp(-c)))
     xd = u @ w_x.T
     dt_low, Bm, Cm = r(xd[..., :R]), r(xd[..., R:R + N]), r(xd[..., R + N:])
-    dt = r(_softplus(dt_low @ w_dt.T + _f64(dt_bias)))
+    dt = r(_softplus(q(dt_low @ w_dt.T + _f64(dt_bias))))
     y, _ = selective_scan(u, dt, A, Bm, Cm, Dskip=Dskip, z=z, nthreads=nthreads)
     return r(h + r(y) @ w_out.T)
+
+
+def _causal_conv1d(x, w, b=None):
+    """c[t] = sum_k w[k] x[t-K+1+k] (+ b), zero before t = 0 (the conv orientation of the
+    scan's prologue); x (B,L,D), w (D,K)."""
+    x = _f64(x)
+    w = _f64(w)
+    K = w.shape[1]
+    L = x.shape[1]
+    c = np.zeros_like(x) if b is None else np.broadcast_to(_f64(b), x.shape).copy()
+    for k in range(K):
+        s = K - 1 - k                    # tap k reads x s steps back
+        if s < L:
+            c[:, s:, :] += w[:, k] * x[:, :L - s, :]
+    return c
+
+
+U_BF16 = 2.0 ** -8   # unit roundoff of bf16 (8 significant bits), round to nearest
+U_F32 = 2.0 ** -24   # unit roundoff of fp32
+
+
+def mamba_block_error_bound(h, norm_w, w_in, conv_w, conv_b, w_x, w_dt, dt_bias, A, Dskip,
+                            w_out, eps=1e-5, lam=10.0):
+    """(h_out, tol, sigma): the block of `mamba_block_fwd` in float64 with no rounding; a
+    per-element tolerance for an implementation that stores the block's intermediates in
+    bf16; and the standard deviation of its error that the tolerance is built from.
+
+    Error model.  The implementation may round to bf16 the output of any operation of the
+    block (hn, x, z, the conv output before and after its SiLU, dt_low, B, C, the step
+    before and after its softplus, y: relative error at most U_BF16 each) and rounds h_out
+    to bf16; inside an operation it works in fp32 (a sum of K terms errs by at most
+    K U_F32 of the sum of their magnitudes; exp, SiLU and softplus by a few U_F32; the ZOH
+    input weight (e^{dt a} - 1)/a by a few U_F32 of 1/|a|, since e^{dt a} - 1 cancels
+    for small dt a).
+
+    Propagation.  As in probabilistic rounding error analysis, each rounding error is
+    taken as an independent zero-mean variable, uniform on [-u|v|, u|v|] (variance
+    u^2 v^2 / 3); to first order the output error is a linear combination of them, and its
+    variance is carried through the block: a projection v W^T maps variances by W^2, an
+    elementwise function by its squared derivative, and the recurrence of eq. (2a) on the
+    paper summary page "Mamba: Linear-Time Sequence Modeling with Selective State
+    Spaces" (sec. 4b) carries the state variance by A_bar^2 and adds the squared
+    sensitivities of h_t to dt_t (a A_bar h + A_bar B u), B_t and u_t.  The fp32 terms
+    are added as if they were roundings of the same size.
+
+    tol = lam * sigma + U_BF16 |h_out|: lam standard deviations of the first-order error
+    plus the rounding of h_out itself, which every bf16 output carries.
+    """
+    ub, uf = U_BF16, U_F32
+    h = _f64(h)
+    Bsz, L, dm = h.shape
+    D = w_in.shape[0] // 2
+    A = _f64(A)
+    N = A.shape[1]
+    R = w_dt.shape[1]
+    K = conv_w.shape[1]
+    w_in, w_x, w_dt, w_out, conv_w = (_f64(v) for v in (w_in, w_x, w_dt, w_out, conv_w))
+    conv_b = None if conv_b is None else _f64(conv_b)
+    Dsk = _f64(Dskip)
+    third = 1.0 / 3.0
+    rnd = lambda v, u: third * (u * v) ** 2          # variance of one rounding of v
+
+    def lin(v, var_v, W, rounded=True):
+        """v W^T and its error variance (K = W's inner size)."""
+        o = v @ W.T
+        var = var_v @ (W * W).T + rnd(np.abs(v) @ np.abs(W).T, W.shape[1] * uf)
+        return o, var + (rnd(o, ub) if rounded else 0.0)
+
+    # RMSNorm (sum of squares over d_model, a square root and a division, then the weight)
+    hn = rms_norm(h, norm_w, eps)
+    var_hn = rnd(hn, (dm + 8) * uf) + rnd(hn, ub)
+    x, var_x = lin(hn, var_hn, w_in[:D])
+    z, var_z = lin(hn, var_hn, w_in[D:])
+    # causal conv1d, then SiLU with derivative s(c)(1 + c(1 - s(c)))
+    c = _causal_conv1d(x, conv_w, conv_b)
+    var_c = (_causal_conv1d(var_x, conv_w * conv_w)
+             + rnd(_causal_conv1d(np.abs(x), np.abs(conv_w),
+                                  None if conv_b is None else np.abs(conv_b)), (K + 1) * uf)
+             + rnd(c, ub))
+    sg = 1.0 / (1.0 + np.exp(-c))
+    u = c * sg
+    du = sg * (1.0 + c * (1.0 - sg))
+    var_u = du * du * var_c + rnd(u, 4 * uf) + rnd(u, ub)
+    # x_proj
+    xd, var_xd = lin(u, var_u, w_x)
+    dt_low, Bm, Cm = xd[..., :R], xd[..., R:R + N], xd[..., R + N:]
+    v_dl, v_B, v_C = var_xd[..., :R], var_xd[..., R:R + N], var_xd[..., R + N:]
+    # dt_proj + bias, then softplus (derivative: the logistic function)
+    pre, var_pre = lin(dt_low, v_dl, w_dt, rounded=False)
+    pre = pre + _f64(dt_bias)
+    var_pre += rnd(_f64(dt_bias), uf) + rnd(pre, ub)
+    dt = _softplus(pre)
+    sig = 1.0 / (1.0 + np.exp(-pre))
+    var_dt = sig * sig * var_pre + rnd(dt, 4 * uf) + rnd(dt, ub)
+    # the recurrence per (b, d, n), in the order of eq. (2a)/(2b); the terms that do not
+    # depend on the state are formed for a chunk of steps at once
+    hs = np.zeros((Bsz, D, N))
+    var_hs = np.zeros((Bsz, D, N))
+    y = np.zeros((Bsz, L, D))
+    var_y = np.zeros((Bsz, L, D))
+    a = A[None, None, :, :]
+    a_nz = a != 0.0
+    inv_a = np.where(a_nz, 1.0 / np.where(a_nz, np.abs(a), 1.0), 0.0)
+    T = max(8, min(512, (1 << 18) // max(1, Bsz * D * N)))
+    for t0 in range(0, L, T):
+        t1 = min(L, t0 + T)
+        dtt = dt[:, t0:t1, :, None]
+        ut, vut = u[:, t0:t1, :, None], var_u[:, t0:t1, :, None]
+        Bt, vBt = Bm[:, t0:t1, None, :], v_B[:, t0:t1, None, :]
+        Ct, vCt = Cm[:, t0:t1, None, :], v_C[:, t0:t1, None, :]
+        za = dtt * a
+        ab = np.exp(za)
+        w = np.where(a_nz, np.expm1(za) / np.where(a_nz, a, 1.0), dtt)
+        bu = Bt * ut
+        wbu = w * bu
+        src = ((w * ut) ** 2 * vBt + (w * Bt) ** 2 * vut + rnd(wbu, 4 * uf)
+               + rnd(bu * inv_a, 4 * uf))
+        ab2, aab, abbu = ab * ab, a * ab, ab * bu
+        rel = third * ((np.abs(za) + 4) * uf) ** 2 * ab2      # rounding of A_bar h, per h^2
+        vdt = var_dt[:, t0:t1, :, None]
+        H = np.empty_like(ab)
+        VH = np.empty_like(ab)
+        for k in range(t1 - t0):
+            sens = aab[:, k] * hs + abbu[:, k]
+            var_hs = (ab2[:, k] * var_hs + sens * sens * vdt[:, k] + src[:, k]
+                      + rel[:, k] * hs * hs)
+            hs = ab[:, k] * hs + wbu[:, k]
+            H[:, k] = hs
+            VH[:, k] = var_hs
+        us = u[:, t0:t1]
+        ys = (Ct * H).sum(-1) + Dsk * us
+        var_ys = ((Ct * Ct * VH + H * H * vCt).sum(-1) + Dsk * Dsk * var_u[:, t0:t1]
+                  + rnd(np.abs(Ct * H).sum(-1) + np.abs(Dsk * us), (N + 2) * uf))
+        zt = z[:, t0:t1]
+        sz_sig = 1.0 / (1.0 + np.exp(-zt))
+        sz = zt * sz_sig
+        dsz = sz_sig * (1.0 + zt * (1.0 - sz_sig))
+        yt = ys * sz
+        y[:, t0:t1] = yt
+        var_y[:, t0:t1] = (sz * sz * var_ys + (ys * dsz) ** 2 * var_z[:, t0:t1]
+                           + rnd(yt, 4 * uf) + rnd(yt, ub))
+    # out_proj + residual
+    o, var_o = lin(y, var_y, w_out, rounded=False)
+    out = h + o
+    var_out = var_o + rnd(np.abs(h), (D + 1) * uf)
+    sigma = np.sqrt(var_out)
+    return out, lam * sigma + ub * np.abs(out), sigma
 
 
 def ssd(x, delta, A, Bm, Cm, Dskip=None, z=None, delta_bias=None, delta_softplus: bool = False,

@@ -7,6 +7,7 @@ F.conv1d, softplus and the recurrence written out), closed forms of the norm,
 and special cases.
 """
 import numpy as np
+import pytest
 import torch
 
 import oracle
@@ -93,3 +94,81 @@ def test_round_bf16():
     assert r[4] == 0.0 and r[5] == np.inf and np.isnan(r[6])
     t = torch.tensor(np.random.default_rng(3).standard_normal(1000), dtype=torch.float32)
     assert np.array_equal(oracle.round_bf16(t.numpy()), t.to(torch.bfloat16).double().numpy())
+
+
+# ---------------------------------------------------------------------------
+# The tolerance of the block: mamba_block_error_bound.  It must contain every
+# outcome its error model admits (the block with bf16 storage, random roundings
+# at every operation output) and must still reject plausible mistakes.
+BOUND_CASES = [(32, 64, 16, 4, 4, 300), (48, 96, 8, 6, 3, 129)]
+
+
+def _bound_case(dm, D, N, R, K, L):
+    rng = RNG(dm)
+    w = _weights(rng, dm=dm, D=D, N=N, R=R, K=K)
+    h = oracle.round_bf16(rng.standard_normal((2, L, dm)))
+    ref, tol, sigma = oracle.mamba_block_error_bound(h, **w)
+    return w, h, ref, tol, sigma
+
+
+def test_error_bound_reference_is_the_unrounded_block():
+    w, h, ref, tol, sigma = _bound_case(*BOUND_CASES[0])
+    np.testing.assert_allclose(ref, oracle.mamba_block_fwd(h, **w, bf16=False), rtol=1e-12,
+                               atol=1e-12)
+    assert np.all(sigma > 0) and np.all(tol > oracle.U_BF16 * np.abs(ref))
+
+
+def test_bf16_unit_roundoff():
+    """u = 2^-8: eight significant bits, so 1 + u is the midpoint between 1 and the next
+    bf16 number, and no rounding moves a value by more than u of its size."""
+    assert oracle.round_bf16(np.array([1.0 + oracle.U_BF16]))[0] == 1.0           # tie to even
+    assert oracle.round_bf16(np.array([1.0 + 1.01 * oracle.U_BF16]))[0] == 1.0 + 2 * oracle.U_BF16
+    v = RNG(7).standard_normal(100000) * 10.0 ** RNG(8).uniform(-3, 3, 100000)
+    assert np.max(np.abs(oracle.round_bf16(v) - v) / np.abs(v)) <= oracle.U_BF16
+
+
+@pytest.mark.parametrize("case", BOUND_CASES, ids=lambda c: "D%d_N%d" % (c[1], c[2]))
+def test_error_bound_contains_bf16_storage(case):
+    w, h, ref, tol, _ = _bound_case(*case)
+    got = oracle.mamba_block_fwd(h, **w, bf16=True)
+    assert np.max(np.abs(got - ref) / tol) < 0.8
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_error_bound_contains_random_roundings_everywhere(seed):
+    """Every operation output, the conv output before its SiLU and the step before its
+    softplus each perturbed by an independent relative error of at most u."""
+    w, h, ref, tol, _ = _bound_case(*BOUND_CASES[seed % 2])
+    g = RNG(200 + seed)
+    pert = lambda v: v * (1.0 + oracle.U_BF16 * g.uniform(-1.0, 1.0, np.shape(v)))
+    got = oracle.mamba_block_fwd(h, **w, bf16=False, perturb=pert)
+    assert np.max(np.abs(got - ref) / tol) < 0.8
+    # extreme roundings (every one at +u or -u) as well
+    pert2 = lambda v: v * (1.0 + oracle.U_BF16 * g.choice([-1.0, 1.0], np.shape(v)))
+    got2 = oracle.mamba_block_fwd(h, **w, bf16=False, perturb=pert2)
+    assert np.max(np.abs(got2 - ref) / tol) < 1.0
+
+
+@pytest.mark.parametrize("mistake", ["no_skip", "one_A_sign", "B_for_C", "gate_off",
+                                     "conv_taps_reversed", "no_residual_norm_weight"])
+def test_error_bound_rejects_plausible_mistakes(mistake):
+    """Each of these mistakes moves most outputs outside the tolerance."""
+    w, h, ref, tol, _ = _bound_case(*BOUND_CASES[0])
+    w2 = {k: np.array(v, copy=True) for k, v in w.items()}
+    D = w["w_in"].shape[0] // 2
+    N = w["A"].shape[1]
+    R = w["w_dt"].shape[1]
+    if mistake == "no_skip":
+        w2["Dskip"][:] = 0.0
+    elif mistake == "one_A_sign":
+        w2["A"][:, 0] *= -1.0
+    elif mistake == "B_for_C":
+        w2["w_x"][R + N:] = w["w_x"][R:R + N]
+    elif mistake == "gate_off":                     # silu(z) replaced by a constant branch
+        w2["w_in"][D:] = 0.0
+    elif mistake == "conv_taps_reversed":
+        w2["conv_w"] = w["conv_w"][:, ::-1].copy()
+    elif mistake == "no_residual_norm_weight":
+        w2["norm_w"][:] = 1.0
+    got = oracle.mamba_block_fwd(h, **w2, bf16=False)
+    assert np.mean(np.abs(got - ref) > tol) > 0.5
