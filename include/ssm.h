@@ -63,7 +63,7 @@
 extern "C" {
 #endif
 
-#define SSM_ABI_VERSION 7
+#define SSM_ABI_VERSION 8
 #define SSM_MAX_DSTATE 16 /* largest N the kernels hold in registers */
 #define SSM_MAX_CONV_K 4  /* largest conv1d kernel width */
 
@@ -158,6 +158,33 @@ size_t ssm_selective_scan_workspace_size(const ssm_scan_args_t *args);
  * status (see the conventions).
  */
 ssm_status_t ssm_selective_scan_fwd(const ssm_scan_args_t *args, void *stream);
+
+/* Bytes of the device scratch array behind ssm_selective_scan_fwd_noalloc (32 MiB). */
+#define SSM_NOALLOC_SCRATCH_BYTES (32u << 20)
+
+/*
+ * ssm_selective_scan_fwd for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  It computes exactly what ssm_selective_scan_fwd computes, with
+ * the same kernels, but its workspace is a device array of
+ * SSM_NOALLOC_SCRATCH_BYTES that the library holds on each device it runs on
+ * until the process ends (a 1M-token sequence at D = 1024 needs about 2 MiB).
+ * args->workspace must be NULL and args->workspace_bytes 0.  The caller still
+ * passes every input and output.
+ *
+ * Errors: besides those of ssm_selective_scan_fwd, SSM_ERR_WORKSPACE when
+ * ssm_selective_scan_workspace_size(args) exceeds SSM_NOALLOC_SCRATCH_BYTES
+ * (before any HIP call) or a workspace is passed; SSM_ERR_HIP if the array's
+ * address cannot be obtained on the stream's device.  The call allocates
+ * nothing; the first call on a device looks up the array's address there.
+ *
+ * Every call on one device shares that device's array, and the array keeps
+ * whatever the last call left in it (no call depends on its contents on
+ * entry).  Calls that may overlap in time on one device -- on different
+ * streams, or from different threads without ordering -- race on it: order
+ * them on one stream, or use ssm_selective_scan_fwd with separate workspaces.
+ */
+ssm_status_t ssm_selective_scan_fwd_noalloc(const ssm_scan_args_t *args, void *stream);
 
 /*
  * Depthwise causal conv1d + SiLU, the prologue of [P1] sec. 4a with the

@@ -5,6 +5,7 @@ The compute path is the C-ABI HIP library libssm_hip.so (include/ssm.h); the
 and its absence raises an error; nothing here computes on the CPU.
 """
 from .ssm import (  # noqa: F401
+    NOALLOC_SCRATCH_BYTES,
     BlockPlan,
     SSMError,
     abi_version,
@@ -12,7 +13,9 @@ from .ssm import (  # noqa: F401
     lib,
     mamba_block_fwd,
     selective_scan_bwd,
+    selective_scan_args,
     selective_scan_fwd,
+    selective_scan_fwd_noalloc,
     selective_scan_workspace_size,
     ssd_fwd,
     ssd_step,
@@ -22,6 +25,7 @@ from .ssm import (  # noqa: F401
     status_string,
 )
 
-__all__ = ["BlockPlan", "SSMError", "abi_version", "causal_conv1d_silu", "lib", "mamba_block_fwd",
-           "selective_scan_bwd", "selective_scan_fwd", "selective_scan_workspace_size", "ssd_fwd",
+__all__ = ["NOALLOC_SCRATCH_BYTES", "BlockPlan", "SSMError", "abi_version", "causal_conv1d_silu", "lib", "mamba_block_fwd",
+           "selective_scan_args", "selective_scan_bwd", "selective_scan_fwd",
+           "selective_scan_fwd_noalloc", "selective_scan_workspace_size", "ssd_fwd",
            "ssd_step", "ssd_step_args", "state_update", "state_update_args", "status_string"]

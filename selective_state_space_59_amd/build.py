@@ -21,7 +21,7 @@ LIB = os.path.join(PKG, "libssm_hip.so")
 ARCH = "gfx950"
 
 SOURCES = ["ssm_api.cpp", "scan_fwd.hip", "scan_bwd.hip", "conv1d.hip", "state_update.hip", "block.hip",
-           "ssd.hip"]
+           "ssd.hip", "scan_noalloc.hip"]
 # hipBLASLt runs the plain GEMMs of the Mamba block.
 LIBS = ["-L/opt/rocm/lib", "-lhipblaslt", "-Wl,-rpath,/opt/rocm/lib"]
 

@@ -109,7 +109,13 @@ size_t ssm_selective_scan_workspace_size(const ssm_scan_args_t *a) {
     return ssm::scan_workspace_bytes(*a);
 }
 
-ssm_status_t ssm_selective_scan_fwd(const ssm_scan_args_t *a, void *stream) {
+}  // extern "C"
+
+namespace {
+
+// The checks and launch of both scan entry points.  With `noalloc` the
+// workspace comes from the library's scratch array and the caller passes none.
+ssm_status_t scan_fwd(const ssm_scan_args_t *a, void *stream, bool noalloc) {
     ssm_status_t s = check_scan_sizes(a);
     if (s != SSM_OK) return s;
     const int64_t B = a->batch, L = a->seqlen, D = a->dim, N = a->dstate, K = a->conv_k;
@@ -160,7 +166,14 @@ ssm_status_t ssm_selective_scan_fwd(const ssm_scan_args_t *a, void *stream) {
     if (overlaps(cso, y) || overlaps(cso, hf)) return fail(SSM_ERR_ALIAS, "conv_state_out overlaps an output");
 
     const size_t need = work ? ssm::scan_workspace_bytes(*a) : 0;
-    if (need > 0) {
+    if (noalloc) {
+        if (a->workspace || a->workspace_bytes)
+            return fail(SSM_ERR_WORKSPACE, "the no-allocation scan takes no workspace (use its scratch array)");
+        if (need > (size_t)SSM_NOALLOC_SCRATCH_BYTES)
+            return fail(SSM_ERR_WORKSPACE, "these sizes need %zu bytes of workspace; the no-allocation "
+                        "scan has %zu (use ssm_selective_scan_fwd with a workspace)",
+                        need, (size_t)SSM_NOALLOC_SCRATCH_BYTES);
+    } else if (need > 0) {
         if (!a->workspace) return fail(SSM_ERR_WORKSPACE, "workspace of %zu bytes required", need);
         if (a->workspace_bytes < need)
             return fail(SSM_ERR_WORKSPACE, "workspace has %zu bytes, %zu required", a->workspace_bytes, need);
@@ -177,11 +190,30 @@ ssm_status_t ssm_selective_scan_fwd(const ssm_scan_args_t *a, void *stream) {
     if (B == 0) return ok();
     if (L == 0) {
         e = ssm::launch_empty_scan_state(*a, st);
+    } else if (noalloc && need > 0) {
+        ssm_scan_args_t b = *a;
+        e = ssm::noalloc_scratch(st, &b.workspace);
+        if (e != hipSuccess)
+            return fail(SSM_ERR_HIP, "scratch array address: %s", hipGetErrorString(e));
+        b.workspace_bytes = SSM_NOALLOC_SCRATCH_BYTES;
+        e = ssm::launch_scan_fwd(b, st);
     } else {
         e = ssm::launch_scan_fwd(*a, st);
     }
     if (e != hipSuccess) return fail(SSM_ERR_HIP, "HIP error: %s", hipGetErrorString(e));
     return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+ssm_status_t ssm_selective_scan_fwd(const ssm_scan_args_t *a, void *stream) {
+    return scan_fwd(a, stream, false);
+}
+
+ssm_status_t ssm_selective_scan_fwd_noalloc(const ssm_scan_args_t *a, void *stream) {
+    return scan_fwd(a, stream, true);
 }
 
 ssm_status_t ssm_causal_conv1d_silu(int64_t B, int64_t L, int64_t D, int64_t K, int32_t io_dtype,

@@ -17,6 +17,10 @@ size_t scan_workspace_bytes(const ssm_scan_args_t &a);
 // Scan: enqueue the kernels.  a.batch, a.seqlen > 0.
 hipError_t launch_scan_fwd(const ssm_scan_args_t &a, hipStream_t stream);
 
+// Device address of the no-allocation scan's scratch array
+// (SSM_NOALLOC_SCRATCH_BYTES, 256-aligned) on the device of `stream`.
+hipError_t noalloc_scratch(hipStream_t stream, void **out);
+
 // Standalone conv1d + SiLU.  B, L > 0.
 hipError_t launch_conv1d_silu(int64_t B, int64_t L, int64_t D, int K, int io_dtype,
                               const void *x, const float *w, const float *bias, void *u,

@@ -39,7 +39,8 @@ EXPORTED_SYMBOLS = ("ssm_selective_scan_workspace_size", "ssm_selective_scan_fwd
                     "ssm_selective_scan_bwd_workspace_size", "ssm_selective_scan_bwd",
                     "ssm_block_plan_create", "ssm_block_workspace_size", "ssm_block_fwd",
                     "ssm_block_plan_destroy", "ssm_ssd_fwd", "ssm_ssd_workspace_size",
-                    "ssm_ssd_step")
+                    "ssm_ssd_step", "ssm_selective_scan_fwd_noalloc")
+NOALLOC_SCRATCH_BYTES = 32 << 20
 
 _P = ctypes.c_void_p
 _I64 = ctypes.c_int64
@@ -129,6 +130,8 @@ def lib() -> ctypes.CDLL:
         L.ssm_selective_scan_workspace_size.restype = ctypes.c_size_t
         L.ssm_selective_scan_fwd.argtypes = [ctypes.POINTER(ScanArgs), _P]
         L.ssm_selective_scan_fwd.restype = ctypes.c_int
+        L.ssm_selective_scan_fwd_noalloc.argtypes = [ctypes.POINTER(ScanArgs), _P]
+        L.ssm_selective_scan_fwd_noalloc.restype = ctypes.c_int
         L.ssm_causal_conv1d_silu.argtypes = [_I64, _I64, _I64, _I64, _I32, _P, _P, _P, _P, _P]
         L.ssm_causal_conv1d_silu.restype = ctypes.c_int
         L.ssm_state_update.argtypes = [ctypes.POINTER(StateUpdateArgs), _P]
@@ -332,6 +335,32 @@ def selective_scan_fwd(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, Bm
         a.workspace_bytes = ws.numel() * ws.element_size()
     _check(lib().ssm_selective_scan_fwd(ctypes.byref(a), _stream(dev)), "ssm_selective_scan_fwd")
     return (y, h_final, conv_state_out) if want_cs else (y, h_final)
+
+
+def selective_scan_fwd_noalloc(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor,
+                               Bm: torch.Tensor, Cm: torch.Tensor,
+                               Dskip: Optional[torch.Tensor] = None,
+                               z: Optional[torch.Tensor] = None,
+                               delta_bias: Optional[torch.Tensor] = None,
+                               delta_softplus: bool = False,
+                               conv_w: Optional[torch.Tensor] = None,
+                               conv_b: Optional[torch.Tensor] = None,
+                               h0: Optional[torch.Tensor] = None,
+                               y: Optional[torch.Tensor] = None,
+                               h_final: Optional[torch.Tensor] = None,
+                               conv_state_in: Optional[torch.Tensor] = None,
+                               conv_state_out: Optional[torch.Tensor] = None):
+    """ssm_selective_scan_fwd_noalloc: the scan with its workspace in the library's
+    scratch array on the device (no workspace tensor).  The outputs y, h_final and
+    conv_state_out must be given when wanted (nothing is allocated here either).
+    Returns (y, h_final)."""
+    if y is None:
+        raise ValueError("y is required (the no-allocation scan allocates nothing)")
+    a, dev = _scan_args(x, delta, A, Bm, Cm, Dskip, z, delta_bias, delta_softplus, conv_w,
+                        conv_b, h0, y, h_final, conv_state_in, conv_state_out)
+    _check(lib().ssm_selective_scan_fwd_noalloc(ctypes.byref(a), _stream(dev)),
+           "ssm_selective_scan_fwd_noalloc")
+    return y, h_final
 
 
 def selective_scan_args(x, delta, A, Bm, Cm, Dskip=None, z=None, delta_bias=None,

@@ -157,6 +157,57 @@ def test_scan_rejects_bad_arguments(field, value, status):
     assert ssm.lib().ssm_last_error_message().decode() != ""
 
 
+# The no-allocation scan: the same argument checks, no caller workspace, and a
+# size limit checked before any HIP call.
+def run_scan_noalloc(a):
+    return ssm.lib().ssm_selective_scan_fwd_noalloc(ctypes.byref(a), None)
+
+
+def test_noalloc_scan_rejects_a_workspace():
+    assert run_scan_noalloc(scan_args()) == ssm.SSM_ERR_WORKSPACE
+    assert "no workspace" in ssm.lib().ssm_last_error_message().decode()
+    assert run_scan_noalloc(scan_args(workspace=None, workspace_bytes=64)) == ssm.SSM_ERR_WORKSPACE
+
+
+def test_noalloc_scan_rejects_sizes_beyond_its_scratch():
+    # 300000 rows of 8192 bf16 channels span more than one launch, so the carry
+    # between launches needs B * D * N * 4 = 64 MiB of workspace: beyond the array.
+    far = {k: addr(200 * i) for i, k in enumerate(("x", "delta", "Bm", "Cm", "z", "A", "Dskip",
+                                                    "y", "h_final"))}
+    a = scan_args(batch=128, seqlen=300000, dim=8192, workspace=None, workspace_bytes=0, **far)
+    need = ssm.lib().ssm_selective_scan_workspace_size(ctypes.byref(a))
+    assert need > ssm.NOALLOC_SCRATCH_BYTES
+    assert run_scan_noalloc(a) == ssm.SSM_ERR_WORKSPACE
+    msg = ssm.lib().ssm_last_error_message().decode()
+    assert str(need) in msg and str(ssm.NOALLOC_SCRATCH_BYTES) in msg
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("io_dtype", 7, ssm.SSM_ERR_BAD_DTYPE),
+    ("dstate", 17, ssm.SSM_ERR_UNSUPPORTED),
+    ("x", None, ssm.SSM_ERR_NULL_ARG),
+    ("y", addr(0, 64), ssm.SSM_ERR_ALIAS),
+    ("x", addr(0, 1), ssm.SSM_ERR_ALIGN),
+])
+def test_noalloc_scan_checks_arguments_like_the_scan(field, value, status):
+    a = scan_args(workspace=None, workspace_bytes=0, **{field: value})
+    assert run_scan_noalloc(a) == status
+    assert run_scan(scan_args(**{field: value})) == status
+
+
+def test_noalloc_scan_scratch_size_matches_the_header():
+    v = re.search(r"#define SSM_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", open(HEADER).read())
+    assert int(v.group(1)) << int(v.group(2)) == ssm.NOALLOC_SCRATCH_BYTES
+
+
+def test_noalloc_scan_without_a_device_reports_hip():
+    # Valid arguments whose plan needs a workspace (a long single row is cut into
+    # segments): the call gets as far as the scratch lookup, which fails here.
+    a = scan_args(batch=1, seqlen=20000, dim=64, workspace=None, workspace_bytes=0)
+    assert ssm.lib().ssm_selective_scan_workspace_size(ctypes.byref(a)) > 0
+    assert run_scan_noalloc(a) == ssm.SSM_ERR_HIP
+
+
 # Conv state (the prefill -> decode handoff): given only with the prologue,
 # aligned, and overlapping nothing except its own input when updated in place.
 @pytest.mark.parametrize("kw,status", [
