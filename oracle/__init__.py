@@ -59,8 +59,8 @@ def _load():
         lib.oracle_state_update_f64.restype = I
         lib.oracle_selective_scan_bwd_f64.argtypes = [I64, I64, I64, I64,
                                                       P, P, P, P, P, P, P, P, I, P, P, I64,
-                                                      P, P, P,
-                                                      P, P, P, P, P, P, P, P, P, P, P, I]
+                                                      P, P, P, P,
+                                                      P, P, P, P, P, P, P, P, P, P, P, P, I]
         lib.oracle_selective_scan_bwd_f64.restype = I
         lib.oracle_ssd_f64.argtypes = [I64, I64, I64, I64, I64, I64,
                                        P, P, P, P, P, P, P, P, I, P, P, P, I]
@@ -195,11 +195,12 @@ def state_update(state, x, delta, A, Bm, Cm, Dskip=None, z=None, delta_bias=None
 
 def selective_scan_bwd(x, delta, A, Bm, Cm, dy, Dskip=None, z=None, delta_bias=None,
                        delta_softplus: bool = False, conv_w=None, conv_b=None, h0=None,
-                       dh_final=None, nthreads: Optional[int] = None):
+                       dh_final=None, conv_state_in=None, nthreads: Optional[int] = None):
     """Gradients of selective_scan for a loss with dL/dy = dy and dL/dh_final = dh_final.
 
     Returns a dict with dx, ddelta (B,L,D), dA (D,N), dBm, dCm (B,L,N) and, for the
-    optional inputs that were given, dz, dDskip, ddelta_bias, dconv_w, dconv_b, dh0.
+    optional inputs that were given, dz, dDskip, ddelta_bias, dconv_w, dconv_b, dh0 and
+    dconv_state_in (B,K-1,D), the gradient of the conv state entering the sequence.
     """
     x = _f64(x)
     Bsz, L, D = x.shape
@@ -217,6 +218,9 @@ def selective_scan_bwd(x, delta, A, Bm, Cm, dy, Dskip=None, z=None, delta_bias=N
     h0 = _f64(h0, (Bsz, D, N))
     dy = _f64(dy, (Bsz, L, D))
     dh_final = _f64(dh_final, (Bsz, D, N))
+    if conv_state_in is not None and conv_w is None:
+        raise ValueError("a conv state needs conv_w")
+    conv_state_in = _f64(conv_state_in, (Bsz, max(K - 1, 0), D))
     out = dict(dx=np.zeros((Bsz, L, D)), ddelta=np.zeros((Bsz, L, D)), dA=np.zeros((D, N)),
                dBm=np.zeros((Bsz, L, N)), dCm=np.zeros((Bsz, L, N)))
     if z is not None:
@@ -230,13 +234,15 @@ def selective_scan_bwd(x, delta, A, Bm, Cm, dy, Dskip=None, z=None, delta_bias=N
         out["dconv_b"] = np.zeros(D)
     if h0 is not None:
         out["dh0"] = np.zeros((Bsz, D, N))
+    if conv_state_in is not None:
+        out["dconv_state_in"] = np.zeros((Bsz, K - 1, D))
     g = lambda k: _ptr(out.get(k))
     rc = _load().oracle_selective_scan_bwd_f64(
         Bsz, L, D, N, _ptr(x), _ptr(delta), _ptr(A), _ptr(Bm), _ptr(Cm), _ptr(Dskip), _ptr(z),
-        _ptr(delta_bias), int(bool(delta_softplus)), _ptr(conv_w), _ptr(conv_b), K, _ptr(h0),
-        _ptr(dy), _ptr(dh_final), g("dx"), g("ddelta"), g("dz"), g("dA"), g("dBm"), g("dCm"),
-        g("dDskip"), g("ddelta_bias"), g("dconv_w"), g("dconv_b"), g("dh0"),
-        int(nthreads or default_threads()))
+        _ptr(delta_bias), int(bool(delta_softplus)), _ptr(conv_w), _ptr(conv_b), K,
+        _ptr(conv_state_in), _ptr(h0), _ptr(dy), _ptr(dh_final), g("dx"), g("ddelta"), g("dz"),
+        g("dA"), g("dBm"), g("dCm"), g("dDskip"), g("ddelta_bias"), g("dconv_w"), g("dconv_b"),
+        g("dh0"), g("dconv_state_in"), int(nthreads or default_threads()))
     if rc != 0:
         raise ValueError("oracle_selective_scan_bwd_f64 rejected the sizes")
     return out

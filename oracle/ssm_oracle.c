@@ -270,22 +270,28 @@ static double dsilu(double v)
  *   dh0        = Abar_0 lambda_0
  * then through softplus (ddelta = ddt sigma(delta + bias)) and the conv
  * prologue (dc_t = du_t silu'(c_t), c_t the pre-activation; dx, dconv_w,
- * dconv_b by the chain rule of the causal cross-correlation; no conv state
- * entering).  Outputs (all written, optional ones when non-NULL): dx, ddelta,
- * dz (B,L,D); dA (D,N); dBm, dCm (B,L,N); dDskip, ddelta_bias, dconv_b (D);
- * dconv_w (D,K); dh0 (B,D,N).  Threads split batch rows.  Returns 0 or -1.
+ * dconv_b by the chain rule of the causal cross-correlation).  With
+ * conv_state_in (B,K-1,D), the inputs before t = 0 that the forward's conv
+ * reads in place of zeros, dconv_state_in (B,K-1,D) receives their gradient
+ * by the same chain rule.  Outputs (all written, optional ones when
+ * non-NULL): dx, ddelta, dz (B,L,D); dA (D,N); dBm, dCm (B,L,N); dDskip,
+ * ddelta_bias, dconv_b (D); dconv_w (D,K); dh0 (B,D,N); dconv_state_in
+ * (B,K-1,D).  Threads split batch rows.  Returns 0 or -1.
  */
 int oracle_selective_scan_bwd_f64(int64_t Bsz, int64_t L, int64_t D, int64_t N,
                                   const double *x, const double *delta, const double *A,
                                   const double *Bm, const double *Cm, const double *Dskip,
                                   const double *z, const double *delta_bias, int delta_softplus,
                                   const double *conv_w, const double *conv_b, int64_t conv_k,
-                                  const double *h0, const double *dy, const double *dh_final,
+                                  const double *conv_state_in, const double *h0,
+                                  const double *dy, const double *dh_final,
                                   double *dx, double *ddelta, double *dz, double *dA, double *dBm,
                                   double *dCm, double *dDskip, double *ddelta_bias,
-                                  double *dconv_w, double *dconv_b, double *dh0, int nthreads)
+                                  double *dconv_w, double *dconv_b, double *dh0,
+                                  double *dconv_state_in, int nthreads)
 {
     if (Bsz < 0 || L < 0 || D < 0 || N < 1 || (conv_w && conv_k < 1)) return -1;
+    if ((conv_state_in || dconv_state_in) && !conv_w) return -1;
     if (nthreads < 1) nthreads = 1;
     int64_t K = conv_w ? conv_k : 0;
     /* per batch row partial sums of the per-channel parameters */
@@ -305,6 +311,8 @@ int oracle_selective_scan_bwd_f64(int64_t Bsz, int64_t L, int64_t D, int64_t N,
         double *lam = (double *)malloc(sizeof(double) * (size_t)N);
         for (int64_t d = 0; d < D; ++d) {
             const double *xbd = x + b * L * D + d;
+            const double *hist = conv_state_in ? conv_state_in + b * (conv_k - 1) * D + d : NULL;
+            double *dhist = dconv_state_in ? dconv_state_in + b * (conv_k - 1) * D + d : NULL;
             /* forward, keeping h_{t-1}, u_t, the conv pre-activation and dt */
             for (int64_t n = 0; n < N; ++n) hs[n] = h0 ? h0[(b * D + d) * N + n] : 0.0;
             for (int64_t t = 0; t < L; ++t) {
@@ -312,10 +320,8 @@ int oracle_selective_scan_bwd_f64(int64_t Bsz, int64_t L, int64_t D, int64_t N,
                 double u = x[i];
                 if (K > 0) {
                     double c = conv_b ? conv_b[d] : 0.0;
-                    for (int64_t k = 0; k < K; ++k) {
-                        int64_t s = t - (K - 1) + k;
-                        if (s >= 0) c += conv_w[d * K + k] * xbd[s * D];
-                    }
+                    for (int64_t k = 0; k < K; ++k)
+                        c += conv_w[d * K + k] * x_at(xbd, hist, D, t - (K - 1) + k, K);
                     cs[t] = c;
                     u = silu(c);
                 }
@@ -373,15 +379,19 @@ int oracle_selective_scan_bwd_f64(int64_t Bsz, int64_t L, int64_t D, int64_t N,
                 for (int64_t n = 0; n < N; ++n) dh0[(b * D + d) * N + n] = lam[n];
             /* through the conv prologue */
             for (int64_t t = 0; t < L; ++t) dx[(b * L + t) * D + d] = K > 0 ? 0.0 : duv[t];
+            if (dhist)
+                for (int64_t k = 0; k < K - 1; ++k) dhist[k * D] = 0.0;
             if (K > 0) {
                 for (int64_t t = 0; t < L; ++t) {
                     double dc = duv[t] * dsilu(cs[t]);
                     pb[b * D + d] += dc;
                     for (int64_t k = 0; k < K; ++k) {
                         int64_t s = t - (K - 1) + k;
-                        if (s < 0) continue;
-                        dx[(b * L + s) * D + d] += dc * conv_w[d * K + k];
-                        pw[(b * D + d) * K + k] += dc * xbd[s * D];
+                        pw[(b * D + d) * K + k] += dc * x_at(xbd, hist, D, s, K);
+                        if (s >= 0)
+                            dx[(b * L + s) * D + d] += dc * conv_w[d * K + k];
+                        else if (dhist)
+                            dhist[(K - 1 + s) * D] += dc * conv_w[d * K + k];
                     }
                 }
             }

@@ -131,3 +131,81 @@ def test_gradient_of_zero_loss_is_zero_and_shapes():
     assert set(g) == {"dx", "ddelta", "dA", "dBm", "dCm", "dh0"}
     for v in g.values():
         assert not np.any(v)
+
+
+# ---------------------------------------------------------------------------
+# A conv state entering the sequence: the inputs before t = 0 that the conv
+# prologue reads in place of zeros (the prefill -> decode handoff of the
+# EulerStack tutorial's d_conv window, run backwards).
+def _loss_cs(p, cs, W, V):
+    y, hf = oracle.selective_scan(p["x"], p["delta"], p["A"], p["Bm"], p["Cm"], Dskip=p["Dskip"],
+                                  z=p["z"], delta_bias=p["delta_bias"], delta_softplus=True,
+                                  conv_w=p["conv_w"], conv_b=p["conv_b"], h0=p["h0"],
+                                  conv_state_in=cs, nthreads=1)
+    return float(np.sum(y * W) + np.sum(hf * V))
+
+
+@pytest.mark.parametrize("K", [2, 3, 4])
+def test_conv_state_gradient_matches_central_differences(K):
+    """dconv_state_in and the gradients that the state changes (dconv_w, dx near t = 0)
+    against central differences of the forward with the same conv state."""
+    rng = RNG(120 + K)
+    p = _problem(rng, B=2, L=5, D=3, N=2, K=K)
+    cs = rng.standard_normal((2, K - 1, 3))
+    W = rng.standard_normal(p["x"].shape)
+    V = rng.standard_normal(p["h0"].shape)
+    g = oracle.selective_scan_bwd(p["x"], p["delta"], p["A"], p["Bm"], p["Cm"], W,
+                                  Dskip=p["Dskip"], z=p["z"], delta_bias=p["delta_bias"],
+                                  delta_softplus=True, conv_w=p["conv_w"], conv_b=p["conv_b"],
+                                  h0=p["h0"], dh_final=V, conv_state_in=cs, nthreads=1)
+    targets = [("conv_state_in", cs, "dconv_state_in"), ("conv_w", p["conv_w"], "dconv_w"),
+               ("x", p["x"], "dx"), ("conv_b", p["conv_b"], "dconv_b")]
+    for name, arr, gname in targets:
+        fd = np.zeros_like(arr)
+        for idx in np.ndindex(arr.shape):
+            old = arr[idx]
+            h = 1e-6 * max(1.0, abs(old))
+            arr[idx] = old + h
+            lp = _loss_cs(p, cs, W, V)
+            arr[idx] = old - h
+            lm = _loss_cs(p, cs, W, V)
+            arr[idx] = old
+            fd[idx] = (lp - lm) / (2 * h)
+        np.testing.assert_allclose(g[gname], fd, rtol=2e-6, atol=2e-6, err_msg=name)
+
+
+def test_conv_state_gradient_equals_gradient_of_the_concatenated_sequence():
+    """The state is the K-1 inputs before the sequence: the gradients equal those of
+    one pass over [state, x] (autograd through the independent torch forward), whose
+    leading rows carry zero output weight and whose conv reads zeros before them."""
+    rng = RNG(130)
+    K = 4
+    p = _problem(rng, B=2, L=20, D=4, N=3, K=K)
+    cs = rng.standard_normal((2, K - 1, 4))
+    W = rng.standard_normal(p["x"].shape)
+    V = rng.standard_normal(p["h0"].shape)
+    g = oracle.selective_scan_bwd(p["x"], p["delta"], p["A"], p["Bm"], p["Cm"], W,
+                                  Dskip=p["Dskip"], z=p["z"], delta_bias=p["delta_bias"],
+                                  delta_softplus=True, conv_w=p["conv_w"], conv_b=p["conv_b"],
+                                  h0=p["h0"], dh_final=V, conv_state_in=cs)
+    # torch: conv over [cs, x] with zero left padding, keeping the last L outputs
+    tp = {k: torch.tensor(v, requires_grad=True) for k, v in p.items()}
+    tcs = torch.tensor(cs, requires_grad=True)
+    xx = torch.cat([tcs, tp["x"]], 1)
+    xp = torch.nn.functional.pad(xx.transpose(1, 2), (K - 1, 0))
+    c = torch.nn.functional.conv1d(xp, tp["conv_w"][:, None, :], tp["conv_b"], groups=4)
+    u = torch.nn.functional.silu(c).transpose(1, 2)[:, K - 1:]
+    dt = torch.nn.functional.softplus(tp["delta"] + tp["delta_bias"])
+    h = tp["h0"]
+    ys = []
+    for t in range(20):
+        e = torch.exp(dt[:, t, :, None] * tp["A"])
+        h = e * h + (e - 1.0) / tp["A"] * tp["Bm"][:, t, None, :] * u[:, t, :, None]
+        ys.append(((h * tp["Cm"][:, t, None, :]).sum(-1) + tp["Dskip"] * u[:, t])
+                  * torch.nn.functional.silu(tp["z"][:, t]))
+    y = torch.stack(ys, 1)
+    loss = (y * torch.tensor(W)).sum() + (h * torch.tensor(V)).sum()
+    gcs, gx, gw = torch.autograd.grad(loss, [tcs, tp["x"], tp["conv_w"]])
+    np.testing.assert_allclose(g["dconv_state_in"], gcs.numpy(), rtol=1e-10, atol=1e-10)
+    np.testing.assert_allclose(g["dx"], gx.numpy(), rtol=1e-10, atol=1e-10)
+    np.testing.assert_allclose(g["dconv_w"], gw.numpy(), rtol=1e-10, atol=1e-10)
