@@ -63,7 +63,7 @@
 extern "C" {
 #endif
 
-#define SSM_ABI_VERSION 8
+#define SSM_ABI_VERSION 9
 #define SSM_MAX_DSTATE 16 /* largest N the kernels hold in registers */
 #define SSM_MAX_CONV_K 4  /* largest conv1d kernel width */
 
@@ -251,13 +251,18 @@ ssm_status_t ssm_state_update(const ssm_state_update_args_t *args, void *stream)
  *   channels; dh0 = exp(dt_0 A) lambda_0;
  *   with the conv prologue (u = silu(c), c the causal conv of x): dc = du
  *   silu'(c), dx = the conv's transpose applied to dc, dconv_w and dconv_b
- *   summed over batch and time (no conv state entering the sequence).
- * This version supports N == 16 (other N give SSM_ERR_UNSUPPORTED); the
- * forward's input fields have the same meaning and shapes as in
- * ssm_scan_args_t.
+ *   summed over batch and time; with a conv state entering the sequence
+ *   (the forward's conv_state_in) its rows are read at negative times and
+ *   dconv_state_in is the conv's transpose at those times.
+ * 1 <= N <= SSM_MAX_DSTATE.  The kernels hold 16 state entries per channel;
+ * for N < 16 the workspace also holds 16-wide copies of Bm, Cm, A, h0 and
+ * dh_final (extra entries B = C = 0, h0 = dh_final = 0, A = -1, whose state
+ * and adjoint stay 0) and of the gradients dA, dBm, dCm and dh0, which are
+ * copied back to N-wide rows.  The forward's input fields have the same
+ * meaning and shapes as in ssm_scan_args_t.
  */
 typedef struct ssm_scan_bwd_args {
-    int64_t batch, seqlen, dim, dstate; /* as in ssm_scan_args_t (dstate == 16)  */
+    int64_t batch, seqlen, dim, dstate; /* as in ssm_scan_args_t (1 <= N <= 16) */
     int32_t io_dtype;       /* of x, delta, Bm, Cm, z, dy, dx, ddelta, dz      */
     int32_t delta_softplus; /* as in ssm_scan_args_t                           */
     int64_t conv_k;         /* 0 or 1..SSM_MAX_CONV_K, as in ssm_scan_args_t   */
@@ -277,6 +282,11 @@ typedef struct ssm_scan_bwd_args {
     float *dh0;             /* (B,D,N) fp32 output, or NULL                    */
     void *workspace;        /* device scratch, 256-aligned                     */
     size_t workspace_bytes; /* >= ssm_selective_scan_bwd_workspace_size(args)  */
+    const void *conv_state_in; /* (B,K-1,D) io_dtype: the inputs before t = 0 the
+                                  forward's conv read (its conv_state_in), or
+                                  NULL (= 0); only with conv_k > 1          */
+    void *dconv_state_in;   /* (B,K-1,D) io_dtype output: its gradient, or NULL;
+                               only with conv_k > 1                            */
 } ssm_scan_bwd_args_t;
 
 /* Workspace bytes ssm_selective_scan_bwd needs ((size_t)-1 for invalid sizes). */

@@ -50,6 +50,8 @@ struct BwdParams {
     int softplus;
     int K;                           // conv prologue width, 0 for none
     const float *conv_w, *conv_b;
+    const void *cs_in;               // [B][K-1][D] x before t = 0, or NULL (= 0)
+    void *dcs;                       // [B][K-1][D] its gradient, or NULL
     float *dU;                       // [B][L][D] dL/du when K > 0 (then dx comes from conv_bwd)
     const void *x, *delta, *Bm, *Cm, *z, *dy;
     const float *A, *Dskip, *dbias, *h0, *dh_final;
@@ -162,11 +164,17 @@ __device__ __forceinline__ OwnRaw own_raw(const BwdParams &p, const LaneB &l, in
     if (CONV) {
 #pragma unroll
         for (int j = 0; j < 3; ++j) {
-            // before t = 0 the clamped index is step 0's (masked below)
-            const bool in = tc - 3 + j >= 0;
-            const int64_t s = in ? tc - 3 + j : 0;
-            r.xr[j] = load_bits<IO>(p.x, (l.b * p.L + s) * p.D + dc);
-            r.wm |= (live && in) ? (1 << j) : 0;
+            // before t = 0 the input comes from the entering conv state (the K-1
+            // steps before the sequence) or is 0: then the clamped index is step
+            // 0's and the slot is masked below
+            const int64_t s = tc - 3 + j;
+            const bool in = s >= 0;
+            const bool hist = !in && p.cs_in != nullptr && s >= -(int64_t)(p.K - 1);
+            const void *src = hist ? p.cs_in : p.x;
+            const int64_t idx = in ? (l.b * p.L + s) * p.D + dc
+                                   : hist ? (l.b * (p.K - 1) + (p.K - 1) + s) * p.D + dc : l.b * p.L * p.D + dc;
+            r.xr[j] = load_bits<IO>(src, idx);
+            r.wm |= (live && (in || hist)) ? (1 << j) : 0;
         }
     }
     return r;
@@ -557,9 +565,13 @@ void bwd_kernel(BwdParams p) {
 // and the chunk's partial sums of dw_k = sum_t dc_t x_{t-K+1+k} and db.  The
 // windows are right-aligned to width 4, so no register is indexed by K.
 constexpr int kConvChunk = 256;
+// With an entering conv state cs (the K-1 inputs before t = 0) the window
+// starts from it, and the first chunk also writes the state's gradient dcs
+// (the transpose at the negative steps s = -(K-1) .. -1).
 template <typename IO>
 __global__ void conv_bwd_kernel(const void *x, const float *dU, const float *w, const float *cb, void *dx,
-                                float *pw, int64_t B, int64_t L, int64_t D, int K) {
+                                float *pw, int64_t B, int64_t L, int64_t D, int K, const void *cs,
+                                void *dcs) {
     const int64_t nch = (L + kConvChunk - 1) / kConvChunk;
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // d fastest
     if (i >= nch * B * D) return;
@@ -575,7 +587,8 @@ __global__ void conv_bwd_kernel(const void *x, const float *dU, const float *w, 
 #pragma unroll
     for (int j = 0; j < 3; ++j) {
         const int64_t s = t0 - 3 + j;
-        xw[j + 1] = s >= 0 ? load_io<IO>(x, base + s * D) : 0.0f;
+        xw[j + 1] = s >= 0 ? load_io<IO>(x, base + s * D)
+                  : (cs && s >= -(int64_t)(K - 1)) ? load_io<IO>(cs, (b * (K - 1) + (K - 1) + s) * D + d) : 0.0f;
     }
     float db = 0.0f;
     // Steps in groups of 8 whose 16 loads are issued first (indices clamped into the
@@ -620,6 +633,11 @@ __global__ void conv_bwd_kernel(const void *x, const float *dU, const float *w, 
 #pragma unroll
                 for (int j = 0; j < 4; ++j) v = __builtin_fmaf(dcw[j], wr[3 - j], v);
                 store_io<IO>(dx, base + s * D, v);
+            } else if (dcs && s < 0 && s >= -(int64_t)(K - 1)) {
+                float v = 0.0f;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) v = __builtin_fmaf(dcw[j], wr[3 - j], v);
+                store_io<IO>(dcs, (b * (K - 1) + (K - 1) + s) * D + d, v);
             }
         }
     }
@@ -713,11 +731,14 @@ __global__ void bwd_reduce_params_kernel(const float *partA, const float *partD,
 }
 
 // dh0 of an empty sequence: dh_final (or 0); dA etc. are 0.
+template <typename IO>
 __global__ void bwd_empty_kernel(const float *dh_final, float *dh0, int64_t nbdn, float *dA, float *dD,
-                                 float *dbias, float *dcw, float *dcb, int64_t D, int K) {
+                                 float *dbias, float *dcw, float *dcb, void *dcs, int64_t ncs, int64_t D,
+                                 int N, int K) {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (dh0 && i < nbdn) dh0[i] = dh_final ? dh_final[i] : 0.0f;
-    if (i < D * kRowN) dA[i] = 0.0f;
+    if (dcs && i < ncs) store_io<IO>(dcs, i, 0.0f);
+    if (i < D * N) dA[i] = 0.0f;
     if (dcw && i < D * K) dcw[i] = 0.0f;
     if (i < D) {
         if (dD) dD[i] = 0.0f;
@@ -726,12 +747,67 @@ __global__ void bwd_empty_kernel(const float *dh_final, float *dh0, int64_t nbdn
     }
 }
 
+// N < 16: the kernels above run on 16 state entries per channel.  The
+// per-entry tensors are copied into 16-wide buffers whose extra entries hold
+// B = C = 0, h0 = dh_final = 0 and A = -1; those entries then keep a zero
+// state and a zero adjoint, add nothing to any gradient of the real entries,
+// and their own gradients are dropped when dA, dB, dC and dh0 are copied
+// back to N-wide rows.
+//   rows x N (elements of `bytes` bytes) -> rows x 16, extra entries = fill.
+template <typename T>
+__global__ void pad_rows_kernel(const T *src, T *dst, int64_t rows, int N, T fill) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // rows * 16
+    if (i >= rows * kRowN) return;
+    const int64_t r = i / kRowN;
+    const int n = (int)(i % kRowN);
+    dst[i] = n < N ? src[r * N + n] : fill;
+}
+//   rows x 16 -> rows x N
+__global__ void compact_rows_kernel(const float *src, float *dst, int64_t rows, int N) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // rows * N
+    if (i >= rows * N) return;
+    dst[i] = src[(i / N) * kRowN + i % N];
+}
+
+template <typename T>
+hipError_t pad_rows(const void *src, void *dst, int64_t rows, int N, T fill, hipStream_t stream) {
+    const int64_t n = rows * kRowN;
+    pad_rows_kernel<T><<<(unsigned)((n + 255) / 256), 256, 0, stream>>>(static_cast<const T *>(src),
+                                                                     static_cast<T *>(dst), rows, N, fill);
+    return hipGetLastError();
+}
+hipError_t compact_rows(const float *src, float *dst, int64_t rows, int N, hipStream_t stream) {
+    const int64_t n = rows * N;
+    compact_rows_kernel<<<(unsigned)((n + 255) / 256), 256, 0, stream>>>(src, dst, rows, N);
+    return hipGetLastError();
+}
+
+size_t r256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+// Workspace of the 16-wide copies when N < 16 (0 when N == 16).
+struct PadLayout {
+    size_t B, C, A, h0, dhf, dA, dB, dC, dh0, total;
+};
+PadLayout pad_layout(const ssm_scan_bwd_args_t &a) {
+    PadLayout q{};
+    if (a.dstate == kRowN) return q;
+    const size_t es = a.io_dtype == SSM_BF16 ? 2 : 4;
+    const size_t bl = (size_t)(a.batch * a.seqlen) * kRowN, bd = (size_t)(a.batch * a.dim) * kRowN;
+    q.B = q.C = r256(bl * es);
+    q.A = r256((size_t)a.dim * kRowN * sizeof(float));
+    q.h0 = a.h0 ? r256(bd * sizeof(float)) : 0;
+    q.dhf = a.dh_final ? r256(bd * sizeof(float)) : 0;
+    q.dA = q.A;
+    q.dB = q.dC = r256(bl * sizeof(float));
+    q.dh0 = a.dh0 ? r256(bd * sizeof(float)) : 0;
+    q.total = q.B + q.C + q.A + q.h0 + q.dhf + q.dA + q.dB + q.dC + q.dh0;
+    return q;
+}
+
 struct BwdLayout {
     int64_t G, nb, nch;
     size_t ckpt, partBC, partA, partD, partBias, dU, pconv, total;
 };
-
-size_t r256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 BwdLayout bwd_layout(const ssm_scan_bwd_args_t &a) {
     BwdLayout q;
@@ -786,7 +862,7 @@ hipError_t launch_bwd_typed(const BwdParams &p, const ssm_scan_bwd_args_t &a, fl
     if (e != hipSuccess || p.K == 0) return e;
     const int64_t nthr = nch * p.B * p.D;
     conv_bwd_kernel<IO><<<(unsigned)((nthr + 255) / 256), 256, 0, stream>>>(
-        p.x, p.dU, p.conv_w, p.conv_b, p.dx, pconv, p.B, p.L, p.D, p.K);
+        p.x, p.dU, p.conv_w, p.conv_b, p.dx, pconv, p.B, p.L, p.D, p.K, p.cs_in, p.dcs);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     conv_bwd_reduce_kernel<<<(unsigned)((p.D + 255) / 256), 256, 0, stream>>>(pconv, a.dconv_w, a.dconv_b,
@@ -798,19 +874,76 @@ hipError_t launch_bwd_typed(const BwdParams &p, const ssm_scan_bwd_args_t &a, fl
 
 size_t scan_bwd_workspace_bytes(const ssm_scan_bwd_args_t &a) {
     if (a.batch == 0 || a.seqlen == 0) return 0;
-    return bwd_layout(a).total;
+    return pad_layout(a).total + bwd_layout(a).total;
+}
+
+namespace {
+hipError_t launch_scan_bwd16(const ssm_scan_bwd_args_t &a, char *ws, hipStream_t stream);
 }
 
 hipError_t launch_scan_bwd(const ssm_scan_bwd_args_t &a, hipStream_t stream) {
+    const int N = (int)a.dstate;
     if (a.seqlen == 0) {
-        const int64_t n = std::max<int64_t>(a.batch * a.dim * kRowN, a.dim * kRowN);
-        bwd_empty_kernel<<<(unsigned)((n + 255) / 256), 256, 0, stream>>>(
-            a.dh_final, a.dh0, a.batch * a.dim * kRowN, a.dA, a.dDskip, a.ddelta_bias, a.dconv_w, a.dconv_b,
-            a.dim, (int)a.conv_k);
+        // nothing reads the entering conv state: its gradient is 0
+        void *dcs = a.conv_k > 1 ? a.dconv_state_in : nullptr;
+        const int64_t ncs = dcs ? a.batch * (a.conv_k - 1) * a.dim : 0;
+        const int64_t n = std::max<int64_t>(std::max<int64_t>(a.batch * a.dim * N, ncs),
+                                            std::max<int64_t>(a.dim * N, a.dim * a.conv_k));
+        const unsigned g = (unsigned)((n + 255) / 256);
+        if (a.io_dtype == SSM_BF16)
+            bwd_empty_kernel<io_bf16><<<g, 256, 0, stream>>>(a.dh_final, a.dh0, a.batch * a.dim * N, a.dA,
+                                                           a.dDskip, a.ddelta_bias, a.dconv_w, a.dconv_b, dcs,
+                                                           ncs, a.dim, N, (int)a.conv_k);
+        else
+            bwd_empty_kernel<io_f32><<<g, 256, 0, stream>>>(a.dh_final, a.dh0, a.batch * a.dim * N, a.dA,
+                                                          a.dDskip, a.ddelta_bias, a.dconv_w, a.dconv_b, dcs,
+                                                          ncs, a.dim, N, (int)a.conv_k);
         return hipGetLastError();
     }
-    const BwdLayout q = bwd_layout(a);
     char *ws = static_cast<char *>(a.workspace);
+    if (N == kRowN) return launch_scan_bwd16(a, ws, stream);
+    // 16-wide copies of the per-entry tensors, the kernels, then the gradients back.
+    const PadLayout q = pad_layout(a);
+    ssm_scan_bwd_args_t b = a;
+    b.dstate = kRowN;
+    char *w = ws;
+    auto take = [&](size_t n) { char *r = n ? w : nullptr; w += n; return r; };
+    b.Bm = take(q.B);
+    b.Cm = take(q.C);
+    b.A = reinterpret_cast<float *>(take(q.A));
+    b.h0 = reinterpret_cast<float *>(take(q.h0));
+    b.dh_final = reinterpret_cast<float *>(take(q.dhf));
+    b.dA = reinterpret_cast<float *>(take(q.dA));
+    b.dBm = reinterpret_cast<float *>(take(q.dB));
+    b.dCm = reinterpret_cast<float *>(take(q.dC));
+    b.dh0 = reinterpret_cast<float *>(take(q.dh0));
+    const int64_t bl = a.batch * a.seqlen, bd = a.batch * a.dim;
+    hipError_t e;
+    if (a.io_dtype == SSM_BF16) {
+        if ((e = pad_rows<uint16_t>(a.Bm, const_cast<void *>(b.Bm), bl, N, 0, stream)) != hipSuccess) return e;
+        if ((e = pad_rows<uint16_t>(a.Cm, const_cast<void *>(b.Cm), bl, N, 0, stream)) != hipSuccess) return e;
+    } else {
+        if ((e = pad_rows<float>(a.Bm, const_cast<void *>(b.Bm), bl, N, 0.0f, stream)) != hipSuccess) return e;
+        if ((e = pad_rows<float>(a.Cm, const_cast<void *>(b.Cm), bl, N, 0.0f, stream)) != hipSuccess) return e;
+    }
+    if ((e = pad_rows<float>(a.A, const_cast<float *>(b.A), a.dim, N, -1.0f, stream)) != hipSuccess) return e;
+    if (a.h0 && (e = pad_rows<float>(a.h0, const_cast<float *>(b.h0), bd, N, 0.0f, stream)) != hipSuccess)
+        return e;
+    if (a.dh_final &&
+        (e = pad_rows<float>(a.dh_final, const_cast<float *>(b.dh_final), bd, N, 0.0f, stream)) != hipSuccess)
+        return e;
+    if ((e = launch_scan_bwd16(b, w, stream)) != hipSuccess) return e;
+    if ((e = compact_rows(b.dA, a.dA, a.dim, N, stream)) != hipSuccess) return e;
+    if ((e = compact_rows(b.dBm, a.dBm, bl, N, stream)) != hipSuccess) return e;
+    if ((e = compact_rows(b.dCm, a.dCm, bl, N, stream)) != hipSuccess) return e;
+    if (a.dh0 && (e = compact_rows(b.dh0, a.dh0, bd, N, stream)) != hipSuccess) return e;
+    return hipSuccess;
+}
+
+namespace {
+// The backward pass with N == 16 on the workspace `ws` (bwd_layout's size).
+hipError_t launch_scan_bwd16(const ssm_scan_bwd_args_t &a, char *ws, hipStream_t stream) {
+    const BwdLayout q = bwd_layout(a);
     BwdParams p;
     p.B = a.batch;
     p.L = a.seqlen;
@@ -820,6 +953,8 @@ hipError_t launch_scan_bwd(const ssm_scan_bwd_args_t &a, hipStream_t stream) {
     p.K = (int)a.conv_k;
     p.conv_w = a.conv_w;
     p.conv_b = a.conv_b;
+    p.cs_in = a.conv_k > 1 ? a.conv_state_in : nullptr;
+    p.dcs = a.conv_k > 1 ? a.dconv_state_in : nullptr;
     p.dU = a.conv_k > 0 ? reinterpret_cast<float *>(ws + q.ckpt + q.partBC + q.partA + q.partD + q.partBias)
                         : nullptr;
     p.x = a.x;
@@ -848,5 +983,6 @@ hipError_t launch_scan_bwd(const ssm_scan_bwd_args_t &a, hipStream_t stream) {
     if (a.io_dtype == SSM_BF16) return launch_bwd_typed<io_bf16>(p, a, pconv, q.nch, stream);
     return launch_bwd_typed<io_f32>(p, a, pconv, q.nch, stream);
 }
+}  // namespace
 
 }  // namespace ssm

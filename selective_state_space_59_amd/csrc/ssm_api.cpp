@@ -309,13 +309,16 @@ static ssm_status_t check_bwd(const ssm_scan_bwd_args_t *a, size_t *need_out) {
                     (long long)a->seqlen);
     if (a->dim < 1) return fail(SSM_ERR_BAD_SHAPE, "dim must be >= 1");
     if (a->dstate < 1) return fail(SSM_ERR_BAD_SHAPE, "dstate must be >= 1");
-    if (a->dstate != SSM_MAX_DSTATE)
-        return fail(SSM_ERR_UNSUPPORTED, "the backward pass supports dstate == %d only", SSM_MAX_DSTATE);
+    if (a->dstate > SSM_MAX_DSTATE)
+        return fail(SSM_ERR_UNSUPPORTED, "dstate %lld exceeds SSM_MAX_DSTATE (%d)", (long long)a->dstate,
+                    SSM_MAX_DSTATE);
     if (a->conv_k < 0) return fail(SSM_ERR_BAD_SHAPE, "conv_k must be >= 0");
     if (a->conv_k > SSM_MAX_CONV_K)
         return fail(SSM_ERR_UNSUPPORTED, "conv_k %lld exceeds SSM_MAX_CONV_K (%d)", (long long)a->conv_k, SSM_MAX_CONV_K);
     if (a->conv_k == 0 && (a->conv_w || a->conv_b || a->dconv_w || a->dconv_b))
         return fail(SSM_ERR_BAD_SHAPE, "conv weights or their gradients given but conv_k == 0");
+    if (a->conv_k < 2 && (a->conv_state_in || a->dconv_state_in))
+        return fail(SSM_ERR_BAD_SHAPE, "a conv state or its gradient given but conv_k < 2");
     if (a->delta_softplus != 0 && a->delta_softplus != 1)
         return fail(SSM_ERR_UNSUPPORTED, "delta_softplus must be 0 or 1");
     if (!mul_ok(a->batch, a->seqlen, a->dim) || !mul_ok(a->batch, a->seqlen, a->dstate) ||
@@ -338,7 +341,8 @@ static ssm_status_t check_bwd(const ssm_scan_bwd_args_t *a, size_t *need_out) {
         if (a->z && !a->dz) return fail(SSM_ERR_NULL_ARG, "dz is NULL but z is given");
     }
     if (!a->z && a->dz) return fail(SSM_ERR_BAD_SHAPE, "dz given without z");
-    const void *io_ptrs[] = {a->x, a->delta, a->Bm, a->Cm, a->z, a->dy, a->dx, a->ddelta, a->dz};
+    const void *io_ptrs[] = {a->x, a->delta, a->Bm, a->Cm, a->z, a->dy, a->dx, a->ddelta, a->dz,
+                             a->conv_state_in, a->dconv_state_in};
     for (const void *p : io_ptrs)
         if (!aligned(p, es)) return fail(SSM_ERR_ALIGN, "an io_dtype pointer is not %lld-byte aligned", (long long)es);
     const void *f_ptrs[] = {a->A, a->Dskip, a->delta_bias, a->h0, a->dh_final, a->dA, a->dBm, a->dCm,
@@ -353,6 +357,7 @@ static ssm_status_t check_bwd(const ssm_scan_bwd_args_t *a, size_t *need_out) {
         range(a->delta_bias, D, 4, "delta_bias"), range(a->h0, B * D * N, 4, "h0"),
         range(a->dh_final, B * D * N, 4, "dh_final"), range(a->conv_w, D * K, 4, "conv_w"),
         range(a->conv_b, D, 4, "conv_b"),
+        range(a->conv_state_in, B * (K > 0 ? K - 1 : 0) * D, es, "conv_state_in"),
     };
     const Range outputs[] = {
         range(a->dx, B * L * D, es, "dx"),        range(a->ddelta, B * L * D, es, "ddelta"),
@@ -361,6 +366,7 @@ static ssm_status_t check_bwd(const ssm_scan_bwd_args_t *a, size_t *need_out) {
         range(a->dDskip, D, 4, "dDskip"),         range(a->ddelta_bias, D, 4, "ddelta_bias"),
         range(a->dh0, B * D * N, 4, "dh0"),         range(a->dconv_w, D * K, 4, "dconv_w"),
         range(a->dconv_b, D, 4, "dconv_b"),
+        range(a->dconv_state_in, B * (K > 0 ? K - 1 : 0) * D, es, "dconv_state_in"),
     };
     const int nout = (int)(sizeof(outputs) / sizeof(outputs[0]));
     for (int i = 0; i < nout; ++i) {
@@ -385,7 +391,7 @@ static ssm_status_t check_bwd(const ssm_scan_bwd_args_t *a, size_t *need_out) {
 }
 
 size_t ssm_selective_scan_bwd_workspace_size(const ssm_scan_bwd_args_t *a) {
-    if (!a || a->batch < 0 || a->seqlen < 0 || a->dim < 1 || a->dstate != SSM_MAX_DSTATE ||
+    if (!a || a->batch < 0 || a->seqlen < 0 || a->dim < 1 || a->dstate < 1 || a->dstate > SSM_MAX_DSTATE ||
         !mul_ok(a->batch, a->seqlen, a->dim) || !mul_ok(a->batch, a->dim, a->dstate))
         return (size_t)-1;
     return a->batch > 0 ? ssm::scan_bwd_workspace_bytes(*a) : 0;

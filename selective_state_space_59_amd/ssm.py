@@ -76,7 +76,8 @@ class ScanBwdArgs(ctypes.Structure):
                 ("h0", _P), ("dy", _P), ("dh_final", _P),
                 ("dx", _P), ("ddelta", _P), ("dz", _P), ("dA", _P), ("dBm", _P), ("dCm", _P),
                 ("dDskip", _P), ("ddelta_bias", _P), ("dconv_w", _P), ("dconv_b", _P),
-                ("dh0", _P), ("workspace", _P), ("workspace_bytes", ctypes.c_size_t)]
+                ("dh0", _P), ("workspace", _P), ("workspace_bytes", ctypes.c_size_t),
+                ("conv_state_in", _P), ("dconv_state_in", _P)]
 
 
 class BlockDims(ctypes.Structure):
@@ -471,13 +472,15 @@ def selective_scan_bwd(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, Bm
                        dh_final: Optional[torch.Tensor] = None,
                        conv_w: Optional[torch.Tensor] = None,
                        conv_b: Optional[torch.Tensor] = None,
-                       workspace: Optional[torch.Tensor] = None) -> dict:
-    """ssm_selective_scan_bwd: gradients of the scan (N = 16).
+                       workspace: Optional[torch.Tensor] = None,
+                       conv_state_in: Optional[torch.Tensor] = None) -> dict:
+    """ssm_selective_scan_bwd: gradients of the scan (1 <= N <= 16).
 
     Returns a dict with dx, ddelta (x's dtype), dA, dBm, dCm (float32) and, for the
-    optional inputs given, dz, dDskip, ddelta_bias, dh0, dconv_w, dconv_b."""
+    optional inputs given, dz, dDskip, ddelta_bias, dh0, dconv_w, dconv_b and
+    dconv_state_in (x's dtype, the gradient of the conv state entering the sequence)."""
     a, dev = _scan_args(x, delta, A, Bm, Cm, Dskip, z, delta_bias, delta_softplus, conv_w, conv_b,
-                        h0, torch.empty_like(x), None)
+                        h0, torch.empty_like(x), None, conv_state_in=conv_state_in)
     Bsz, L, D = x.shape
     N = A.shape[1]
     io = x.dtype
@@ -497,6 +500,8 @@ def selective_scan_bwd(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, Bm
     if conv_w is not None:
         out["dconv_w"] = torch.empty(D, a.conv_k, **f32)
         out["dconv_b"] = torch.empty(D, **f32)
+    if conv_state_in is not None:
+        out["dconv_state_in"] = torch.empty_like(conv_state_in)
     g = lambda k: _ptr(out.get(k))
     b = ScanBwdArgs(batch=Bsz, seqlen=L, dim=D, dstate=N, io_dtype=a.io_dtype,
                     delta_softplus=a.delta_softplus, conv_k=a.conv_k, x=a.x, delta=a.delta, Bm=a.Bm,
@@ -504,7 +509,8 @@ def selective_scan_bwd(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, Bm
                     conv_w=a.conv_w, conv_b=a.conv_b, dconv_w=g("dconv_w"), dconv_b=g("dconv_b"),
                     dy=_ptr(dy), dh_final=_ptr(dh_final), dx=g("dx"), ddelta=g("ddelta"),
                     dz=g("dz"), dA=g("dA"), dBm=g("dBm"), dCm=g("dCm"), dDskip=g("dDskip"),
-                    ddelta_bias=g("ddelta_bias"), dh0=g("dh0"))
+                    ddelta_bias=g("ddelta_bias"), dh0=g("dh0"), conv_state_in=a.conv_state_in,
+                    dconv_state_in=g("dconv_state_in"))
     need = lib().ssm_selective_scan_bwd_workspace_size(ctypes.byref(b))
     if need == ctypes.c_size_t(-1).value:
         _check(lib().ssm_selective_scan_bwd(ctypes.byref(b), None), "ssm_selective_scan_bwd")

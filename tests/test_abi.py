@@ -383,10 +383,42 @@ def run_bwd(a):
     return ssm.lib().ssm_selective_scan_bwd(ctypes.byref(a), None)
 
 
+def _conv_bwd(**kw):
+    base = dict(conv_k=4, conv_w=addr(16), dconv_w=addr(18))
+    base.update(kw)
+    return bwd_args(**base)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(conv_state_in=addr(19), dconv_state_in=addr(0, 64)), ssm.SSM_ERR_ALIAS),  # grad inside x
+    (dict(conv_state_in=addr(8, 2)), ssm.SSM_ERR_ALIAS),            # state inside dx
+    (dict(conv_state_in=addr(19), dconv_state_in=addr(19)), ssm.SSM_ERR_ALIAS),
+    (dict(conv_state_in=addr(19, 1)), ssm.SSM_ERR_ALIGN),
+    (dict(conv_k=1, conv_state_in=addr(19)), ssm.SSM_ERR_BAD_SHAPE),
+])
+def test_bwd_conv_state_checks(kw, status):
+    assert run_bwd(_conv_bwd(**kw)) == status
+
+
+@pytest.mark.parametrize("N", [1, 5, 15])
+def test_bwd_small_dstate_passes_the_checks_and_needs_more_workspace(N):
+    """N < 16 is accepted; its workspace holds the 16-wide copies on top of the
+    N = 16 workspace (the launch itself fails here: no device)."""
+    a16 = bwd_args(workspace=None, workspace_bytes=0)
+    aN = bwd_args(dstate=N, workspace=None, workspace_bytes=0)
+    n16 = ssm.lib().ssm_selective_scan_bwd_workspace_size(ctypes.byref(a16))
+    nN = ssm.lib().ssm_selective_scan_bwd_workspace_size(ctypes.byref(aN))
+    assert nN > n16
+    assert run_bwd(bwd_args(dstate=N)) == ssm.SSM_ERR_HIP
+
+
 @pytest.mark.parametrize("field,value,status", [
     ("io_dtype", 3, ssm.SSM_ERR_BAD_DTYPE),
     ("batch", -1, ssm.SSM_ERR_BAD_SHAPE),
-    ("dstate", 8, ssm.SSM_ERR_UNSUPPORTED),       # this version: N == 16
+    ("dstate", 17, ssm.SSM_ERR_UNSUPPORTED),      # N <= 16
+    ("dstate", 0, ssm.SSM_ERR_BAD_SHAPE),
+    ("conv_state_in", addr(17), ssm.SSM_ERR_BAD_SHAPE),   # a conv state without conv_k > 1
+    ("dconv_state_in", addr(17), ssm.SSM_ERR_BAD_SHAPE),
     ("conv_k", 4, ssm.SSM_ERR_NULL_ARG),          # conv_k without conv_w
     ("conv_k", 5, ssm.SSM_ERR_UNSUPPORTED),
     ("conv_w", addr(16), ssm.SSM_ERR_BAD_SHAPE),  # conv weights without conv_k
@@ -409,7 +441,7 @@ def test_bwd_dz_without_z_and_empty_batch():
     assert run_bwd(bwd_args(z=None)) == ssm.SSM_ERR_BAD_SHAPE
     assert run_bwd(bwd_args(batch=0)) == ssm.SSM_OK
     L = ssm.lib()
-    assert L.ssm_selective_scan_bwd_workspace_size(ctypes.byref(bwd_args(dstate=4))) == \
+    assert L.ssm_selective_scan_bwd_workspace_size(ctypes.byref(bwd_args(dstate=17))) == \
         ctypes.c_size_t(-1).value
     assert 0 < L.ssm_selective_scan_bwd_workspace_size(ctypes.byref(bwd_args())) < (1 << 40)
 
