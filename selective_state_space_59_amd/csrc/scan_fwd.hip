@@ -566,14 +566,16 @@ struct LaneConst {
 };
 
 // Read-out of one step: the sum over the 16 state entries of the partials
-// C g that the lanes of this row transposed into prow.  The fast form keeps
-// g = A h, so each partial is first multiplied by 1/A of its entry (ia, the
-// channel's 16 values, held in registers by every lane of the row).
-template <bool FAST>
-__device__ __forceinline__ float readout(const float *prow, const float (&ia)[kRow], int n) {
-    float part[kRow];
+// C g that the lanes of this row transposed into prow (load_partials reads
+// them, sum_partials adds them).  The fast form keeps g = A h, so each
+// partial is first multiplied by 1/A of its entry (ia, the channel's 16
+// values, held in registers by every lane of the row).
+__device__ __forceinline__ void load_partials(const float *prow, int n, float (&part)[kRow]) {
 #pragma unroll
     for (int i = 0; i < kRow; ++i) part[i] = prow[i * kPStride + n];
+}
+template <bool FAST>
+__device__ __forceinline__ float sum_partials(float (&part)[kRow], const float (&ia)[kRow]) {
     if (FAST) {
         float s0 = part[0] * ia[0], s1 = part[1] * ia[1];
 #pragma unroll
@@ -597,9 +599,16 @@ struct Carry {
     float u_prev, z_prev;  // u and z of this lane's step in the previous block
     float x_prev;          // conv history: x of the previous block (lanes 13..15 used)
     float h;               // state (A h in the fast form)
-    float scum;            // segment pass: sum of dt of the channel so far
+    float acc;             // read-out sum C h of this lane's step in the previous block
+    float dsum;            // segment pass: this lane's dt summed since the last check
+    float scum;            // segment pass: sum of dt of the channel up to the last check
     int head;              // segment pass: blocks until the entering state is forgotten, or -1
 };
+
+// The segment pass checks whether the entering state has been forgotten every
+// kHeadCheck blocks (a head is then a multiple of that many blocks; checking
+// less often only lengthens heads, which stays exact).
+constexpr int kHeadCheck = 8;
 
 // Sum over the 16 lanes of a row (every lane gets it): four rotations.
 __device__ __forceinline__ float row_sum(float v) {
@@ -628,40 +637,46 @@ __device__ __forceinline__ void read_own(const Tiles &T, const char *lds, int sl
 }
 
 // One 16-step block of one wave, software-pipelined across blocks:
-//   * the LDS reads whose results this block needs later (its partial
-//     read-outs of the previous block, the next block's own inputs, the
-//     outputs two blocks back) are issued first;
-//   * the previous block's outputs are finished while those reads and the
-//     B/C broadcasts are in flight;
-//   * then the 16 recurrence steps, whose partial read-outs are transposed
-//     through LDS and summed one block later;
-//   * finally block j+2 is copied from registers into LDS and block j+4 is
-//     requested from global memory.
-// PAR = j % 2 selects the ybuf halves; TAIL masks steps past the sequence
-// end; STAGE is off in the last block.
-template <typename IO, bool CONV, bool VEC, bool FAST, bool STATS, bool TAIL, int PAR, bool STAGE>
+//   * right after the workgroup barrier, the LDS reads whose results are
+//     needed later are issued: the next block's own inputs and B/C tiles
+//     (staged before this barrier) and the outputs two blocks back;
+//   * the previous block's outputs are finished from its read-out sum, which
+//     that block left in registers, so nothing after the barrier waits for
+//     LDS before the step loop;
+//   * the 16 recurrence steps run on this block's B/C tiles, read one block
+//     earlier; their partial read-outs are transposed through the wave's own
+//     LDS area and read back at once;
+//   * block j+2 is copied from registers into LDS, block j+4 is requested
+//     from global memory, and then the partial read-outs are summed.
+// PAR = j % 2 selects the ybuf halves; SLOT = j % 3 when it is known at
+// compile time; TAIL masks steps past the sequence end; STAGE is off in the
+// last block.
+template <typename IO, bool CONV, bool VEC, bool FAST, bool STATS, bool TAIL, int PAR, bool STAGE,
+          int SLOT = -1>
 __device__ __forceinline__ void block_iter(const ScanKernelParams &p, const Span &sp, const Geo &geo,
                                            const Tiles &T, char *lds, int wave, int c, int n,
                                            int lane, const BcastSel &sel, const LaneConst &k,
-                                           const float (&iat)[kRow], const Duty &du, int j, int s_cur,
-                                           Fetch<VEC> &f,
+                                           const float (&iat)[kRow], const Duty &du, int j, int s_run,
+                                           Fetch<VEC> &f, BcBlock<IO> &bop, BcBlock<IO> &cop,
                                            Carry &cy) {
     constexpr int es = sizeof(typename IO::storage);
     const int tid = threadIdx.x, nthreads = blockDim.x;
     const int ci = 4 * wave + c;
+    // LDS slot of this block: fixed at compile time (SLOT >= 0: every LDS offset
+    // of the block is then an immediate) or the scalar s_run
+    const int s_cur = SLOT >= 0 ? SLOT : s_run;
     const int s_next = s_cur == kSlots - 1 ? 0 : s_cur + 1;
     const int s_stage = s_next == kSlots - 1 ? 0 : s_next + 1;
     float *prow = reinterpret_cast<float *>(lds + T.part) + (wave * kChPerWave + c) * kPRow;
-    const char *brows = lds + T.bc + s_cur * T.bc_slot;
-    const char *crows = brows + kBcTile<IO>;
 
     __syncthreads();
-    // -- LDS reads first ------------------------------------------------------
-    const float acc = readout<FAST>(prow, iat, n);
+    // -- LDS reads of later blocks first ------------------------------------------
     float own_next[3];
     read_own<IO>(T, lds, s_next, n, ci, own_next);
     const YChunk<VEC> yst = read_ybuf<IO, VEC>(du, T, lds, PAR, tid);
-    const BcBlock<IO> bop = load_bc_block<IO>(brows, lane), cop = load_bc_block<IO>(crows, lane);
+    const char *brows_n = lds + T.bc + s_next * T.bc_slot;
+    const BcBlock<IO> bop_n = load_bc_block<IO>(brows_n, lane);
+    const BcBlock<IO> cop_n = load_bc_block<IO>(brows_n + kBcTile<IO>, lane);
 
     // -- this block's inputs ---------------------------------------------------
     const float xv = cy.own[0];
@@ -681,14 +696,18 @@ __device__ __forceinline__ void block_iter(const ScanKernelParams &p, const Span
         u = 0.0f;
     }
     if constexpr (STATS) {
-        // Decay of the entering state through this block: exp(A sum(dt)).
-        cy.scum += row_sum(dt);
-        if (cy.head < 0 && __all(!k.live || k.a2 * cy.scum < kForgetExp2)) cy.head = (int)j + 1;
+        // Decay of the entering state through the blocks so far: exp(A sum(dt)).
+        cy.dsum += dt;
+        if ((j & (kHeadCheck - 1)) == kHeadCheck - 1) {
+            cy.scum += row_sum(cy.dsum);
+            cy.dsum = 0.0f;
+            if (cy.head < 0 && __all(!k.live || k.a2 * cy.scum < kForgetExp2)) cy.head = (int)j + 1;
+        }
     }
 
     // -- outputs of block j-1 (lane (c, n) finishes its step n) ---------------
     {
-        float yv = acc + k.dsk * cy.u_prev;
+        float yv = cy.acc + k.dsk * cy.u_prev;
         if (p.z) yv *= silu(cy.z_prev);
         char *ydst = lds + T.ybuf + (1 - PAR) * T.ybuf_slot + n * T.rs + ci * es;
         if constexpr (es == 2)
@@ -731,19 +750,27 @@ __device__ __forceinline__ void block_iter(const ScanKernelParams &p, const Span
         });
         *reinterpret_cast<float4 *>(&prow[n * kPStride + g4]) = make_float4(pk[0], pk[1], pk[2], pk[3]);
     });
+    // The partials are this wave's own: read them back at once (LDS operations
+    // of one wave complete in order), sum them after the staging below.
+    float part[kRow];
+    load_partials(prow, n, part);
 
     cy.u_prev = u;
     cy.z_prev = zv;
 #pragma unroll
     for (int i = 0; i < 3; ++i) cy.own[i] = own_next[i];
+    bop = bop_n;
+    cop = cop_n;
 
     if (STAGE) {
+        __builtin_amdgcn_sched_barrier(0);
         stage_block<IO, VEC>(geo, du, T, lds, s_stage, tid, nthreads, f);
         // Keep the refill after the copy, so the new data can land in the
         // same registers.
         __builtin_amdgcn_sched_barrier(0);
         fetch_block<IO, VEC>(geo, du, j + 4, tid, nthreads, f);
     }
+    cy.acc = sum_partials<FAST>(part, iat);
 }
 
 template <typename IO, bool CONV, bool VEC, bool FAST, bool STATS>
@@ -775,6 +802,8 @@ __device__ __forceinline__ void scan_tiles_body(const ScanKernelParams &p, const
     fetch_block<IO, VEC>(geo, du, 3, tid, nthreads, fb);
     __syncthreads();
     read_own<IO>(T, lds, 0, n, ci, cy.own);
+    BcBlock<IO> bop = load_bc_block<IO>(lds + T.bc, lane);
+    BcBlock<IO> cop = load_bc_block<IO>(lds + T.bc + kBcTile<IO>, lane);
     // 1/A of the channel's 16 entries (the fast form's read-out weights).
     float iat[kRow];
     {
@@ -790,40 +819,64 @@ __device__ __forceinline__ void scan_tiles_body(const ScanKernelParams &p, const
     }
     cy.u_prev = 0.0f;
     cy.z_prev = 0.0f;
+    cy.acc = 0.0f;
 
     int s = 0;  // LDS slot of block j
     int j = 0;
-    // The slot index is kept scalar (it is the same for the whole workgroup).
+    // Six blocks per iteration (wide path): the ring slot (j % 3) and the ybuf
+    // half (j % 2) are then compile-time constants, so no LDS address is
+    // computed per block.  The element path holds more registers per block and
+    // keeps the two-block loop.
+    if constexpr (VEC) for (; j + 6 < nblocks; j += 6) {
+        block_iter<IO, CONV, VEC, FAST, STATS, false, 0, true, 0>(p, sp, geo, T, lds, wave, c, n, lane, sel,
+                                                                k, iat, du, j, 0, fa, bop, cop, cy);
+        block_iter<IO, CONV, VEC, FAST, STATS, false, 1, true, 1>(p, sp, geo, T, lds, wave, c, n, lane, sel,
+                                                                k, iat, du, j + 1, 0, fb, bop, cop, cy);
+        block_iter<IO, CONV, VEC, FAST, STATS, false, 0, true, 2>(p, sp, geo, T, lds, wave, c, n, lane, sel,
+                                                                k, iat, du, j + 2, 0, fa, bop, cop, cy);
+        block_iter<IO, CONV, VEC, FAST, STATS, false, 1, true, 0>(p, sp, geo, T, lds, wave, c, n, lane, sel,
+                                                                k, iat, du, j + 3, 0, fb, bop, cop, cy);
+        block_iter<IO, CONV, VEC, FAST, STATS, false, 0, true, 1>(p, sp, geo, T, lds, wave, c, n, lane, sel,
+                                                                k, iat, du, j + 4, 0, fa, bop, cop, cy);
+        block_iter<IO, CONV, VEC, FAST, STATS, false, 1, true, 2>(p, sp, geo, T, lds, wave, c, n, lane, sel,
+                                                                k, iat, du, j + 5, 0, fb, bop, cop, cy);
+    }
+    // The remaining blocks (j % 6 == 0, so the slot is 0 again): pairs with the
+    // slot kept scalar (it is the same for the whole workgroup).
     auto advance = [&]() { s = __builtin_amdgcn_readfirstlane(s == kSlots - 1 ? 0 : s + 1); };
     for (; j + 2 < nblocks; j += 2) {
         block_iter<IO, CONV, VEC, FAST, STATS, false, 0, true>(p, sp, geo, T, lds, wave, c, n, lane, sel, k,
-                                                        iat, du, j, s, fa, cy);
+                                                        iat, du, j, s, fa, bop, cop, cy);
         advance();
         block_iter<IO, CONV, VEC, FAST, STATS, false, 1, true>(p, sp, geo, T, lds, wave, c, n, lane, sel, k,
-                                                        iat, du, j + 1, s, fb, cy);
+                                                        iat, du, j + 1, s, fb, bop, cop, cy);
         advance();
     }
     // One or two blocks remain (j is even).
     int last_par;
     if (j + 1 < nblocks) {
         block_iter<IO, CONV, VEC, FAST, STATS, false, 0, true>(p, sp, geo, T, lds, wave, c, n, lane, sel, k,
-                                                        iat, du, j, s, fa, cy);
+                                                        iat, du, j, s, fa, bop, cop, cy);
         advance();
         block_iter<IO, CONV, VEC, FAST, STATS, true, 1, false>(p, sp, geo, T, lds, wave, c, n, lane, sel, k,
-                                                        iat, du, j + 1, s, fb, cy);
+                                                        iat, du, j + 1, s, fb, bop, cop, cy);
         last_par = 1;
     } else {
         block_iter<IO, CONV, VEC, FAST, STATS, true, 0, false>(p, sp, geo, T, lds, wave, c, n, lane, sel, k,
-                                                        iat, du, j, s, fa, cy);
+                                                        iat, du, j, s, fa, bop, cop, cy);
         last_par = 0;
+    }
+    if constexpr (STATS) {
+        // the dt of the blocks since the last check
+        cy.scum += row_sum(cy.dsum);
+        if (cy.head < 0 && __all(!k.live || k.a2 * cy.scum < kForgetExp2)) cy.head = nblocks;
     }
     // Outputs of the last block and of the one before it.
     constexpr int es = sizeof(typename IO::storage);
     const int jl = nblocks - 1;
     __syncthreads();  // every wave has read ybuf[last_par] for its store
     {
-        const float *prow = reinterpret_cast<const float *>(lds + T.part) + (wave * kChPerWave + c) * kPRow;
-        float yv = readout<FAST>(prow, iat, n) + k.dsk * cy.u_prev;
+        float yv = cy.acc + k.dsk * cy.u_prev;
         if (p.z) yv *= silu(cy.z_prev);
         char *ydst = lds + T.ybuf + last_par * T.ybuf_slot + n * T.rs + ci * es;
         if constexpr (es == 2)
@@ -842,12 +895,12 @@ __device__ __forceinline__ void scan_tiles_body(const ScanKernelParams &p, const
 
 // blockDim.x = 64 W; workgroup g covers channels [4 W q, 4 W q + 4 W) of
 // batch row g / groups_per_b, with q = g % groups_per_b.
-// Register budget: the wide-tile variants fit 5 waves per SIMD (<= 96
-// VGPRs; their block loops keep everything in registers), so two 10-wave
-// workgroups share a CU and a 2.8B-like layer (5120 waves) is resident at
-// once; the element path may use 128 (4 waves).
+// Register budget: 4 waves per SIMD (<= 128 VGPRs).  A 96-VGPR budget (5
+// waves per SIMD, two 10-wave workgroups per CU on the 2.8B-like layer)
+// spilled in the conv variants and ran slower on every measured layer than
+// this budget with fewer waves resident.
 template <bool VEC>
-constexpr int kWavesPerSimd = VEC ? 5 : 4;
+constexpr int kWavesPerSimd = 4;
 
 template <typename IO, bool CONV, bool VEC, bool STATS>
 __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(kWavesPerSimd<VEC>, 8)))
@@ -933,6 +986,7 @@ void scan_tiles_kernel(ScanKernelParams p) {
     Carry cy;
     cy.h = (live && h_in) ? h_in[(b * D + d) * N + n] : 0.0f;
     cy.scum = 0.0f;
+    cy.dsum = 0.0f;
     cy.head = -1;
     // Conv history entering the rows: x at rows t0 - 16 + n (only the last
     // three lanes of a row are used); before row 0 it comes from the
