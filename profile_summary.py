@@ -4,15 +4,21 @@
     python profile_summary.py stats \\
         --csv OUT_kernel_stats.csv --command "rocprofv3 ..." --out profiles/NAME.md
 
-    # HBM bytes per launch of one kernel from two --pmc runs (FETCH_SIZE, then
-    # WRITE_SIZE), each scaled by what the same counter reads for a plain
-    # device copy of known size (bench.py --copy-calibration MIB)
+    # HBM bytes per step from two --pmc runs (FETCH_SIZE, then WRITE_SIZE), each
+    # scaled by what the same counter reads for a plain device copy of known size
+    # (bench.py --copy-calibration MIB); with several --kernel substrings the
+    # step's kernels are summed (median per dispatch of each)
     python profile_summary.py counters \\
         --fetch A_counter_collection.csv --write B_counter_collection.csv \\
         --copy-fetch C_counter_collection.csv --copy-write D_counter_collection.csv \\
-        --copy-bytes BYTES --kernel SUBSTRING --key NAME --algorithmic-bytes N \\
-        --commands "cmd1" "cmd2" "cmd3" "cmd4" [--sources scan_fwd.hip ...] \\
-        --out-json profiles/hbm_counters.json --out profiles/NAME.md
+        --copy-bytes BYTES --kernel SUBSTRING [SUBSTRING ...] --key NAME \\
+        --algorithmic-bytes N --commands "cmd1" "cmd2" "cmd3" "cmd4" \\
+        [--sources scan_fwd.hip ...] --out-json profiles/hbm_counters.json --out profiles/NAME.md
+
+    # instruction and wait counters (SQ block) of one kernel, with per-update figures
+    python profile_summary.py sq --csv A_counter_collection.csv [B_...csv] \\
+        --kernel SUBSTRING --updates N --duration-us T --title "..." \\
+        --commands "cmd1" ["cmd2"] --out profiles/NAME.md
 
 FETCH_SIZE and WRITE_SIZE are reported in KiB per dispatch.  The JSON entry
 names the library sources the kernel is built from (--sources, file names
@@ -63,25 +69,28 @@ def _counter_per_dispatch(path, counter, match):
 
 
 def cmd_counters(a):
-    fetch = _counter_per_dispatch(a.fetch, "FETCH_SIZE", a.kernel)
-    write = _counter_per_dispatch(a.write, "WRITE_SIZE", a.kernel)
+    fetch = [_counter_per_dispatch(a.fetch, "FETCH_SIZE", k) for k in a.kernel]
+    write = [_counter_per_dispatch(a.write, "WRITE_SIZE", k) for k in a.kernel]
     cf = _counter_per_dispatch(a.copy_fetch, "FETCH_SIZE", a.copy_kernel)
     cw = _counter_per_dispatch(a.copy_write, "WRITE_SIZE", a.copy_kernel)
-    if not (fetch and write and cf and cw):
+    if not (all(fetch) and all(write) and cf and cw):
         sys.exit("no matching dispatches (kernel %r, copy %r)" % (a.kernel, a.copy_kernel))
     # scale: true bytes per counter KiB, from the copy of known size
     fscale = a.copy_bytes / (statistics.median(cf) * 1024.0)
     wscale = a.copy_bytes / (statistics.median(cw) * 1024.0)
-    fb = statistics.median(fetch) * 1024.0 * fscale
-    wb = statistics.median(write) * 1024.0 * wscale
+    fmed = [statistics.median(v) for v in fetch]
+    wmed = [statistics.median(v) for v in write]
+    fb = sum(fmed) * 1024.0 * fscale
+    wb = sum(wmed) * 1024.0 * wscale
     total = fb + wb
     sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
     from selective_state_space_59_amd import build
     sources = sorted(a.sources) if a.sources else None
-    entry = dict(source_hash=build.source_hash(sources), sources=sources, kernel=a.kernel,
+    entry = dict(source_hash=build.source_hash(sources), sources=sources,
+                 kernel=a.kernel[0] if len(a.kernel) == 1 else list(a.kernel),
                  bytes_per_launch=round(total),
                  fetch_bytes=round(fb), write_bytes=round(wb), fetch_scale=round(fscale, 4),
-                 write_scale=round(wscale, 4), dispatches=len(fetch),
+                 write_scale=round(wscale, 4), dispatches=len(fetch[0]),
                  algorithmic_bytes_per_launch=a.algorithmic_bytes)
     rec = {}
     if os.path.exists(a.out_json):
@@ -89,13 +98,15 @@ def cmd_counters(a):
             rec = json.load(f)
     rec[a.key] = entry
     _write(a.out_json, json.dumps(rec, indent=1, sort_keys=True) + "\n")
-    lines = ["# HBM traffic of `%s` (%s)" % (_short(a.kernel, 80), a.key), "",
+    title = " + ".join("`%s`" % _short(k, 80) for k in a.kernel)
+    lines = ["# HBM traffic of %s (%s)" % (title, a.key), "",
              "Commands (from the repository root):", "", "```"] + list(a.commands) + [
              "```", "",
-             "| quantity | value |", "|---|---:|",
-             "| FETCH_SIZE per dispatch (KiB, median of %d) | %.0f |" % (len(fetch), statistics.median(fetch)),
-             "| WRITE_SIZE per dispatch (KiB, median of %d) | %.0f |" % (len(write), statistics.median(write)),
-             "| copy calibration: bytes copied | %d |" % a.copy_bytes,
+             "| quantity | value |", "|---|---:|"]
+    for k, fv, wv, fm, wm in zip(a.kernel, fetch, write, fmed, wmed):
+        lines += ["| FETCH_SIZE per dispatch of `%s` (KiB, median of %d) | %.0f |" % (_short(k, 60), len(fv), fm),
+                  "| WRITE_SIZE per dispatch of `%s` (KiB, median of %d) | %.0f |" % (_short(k, 60), len(wv), wm)]
+    lines += ["| copy calibration: bytes copied | %d |" % a.copy_bytes,
              "| copy calibration: FETCH_SIZE (KiB) | %.0f |" % statistics.median(cf),
              "| copy calibration: WRITE_SIZE (KiB) | %.0f |" % statistics.median(cw),
              "| fetch scale (bytes per counted byte) | %.4f |" % fscale,
@@ -107,6 +118,64 @@ def cmd_counters(a):
              "| traffic / algorithmic | %.4f |" % (total / a.algorithmic_bytes),
              "| hash of the kernel's sources (%s; code only) and flags | %s |"
              % (", ".join(sources) if sources else "all library sources", entry["source_hash"])]
+    _write(a.out, "\n".join(lines) + "\n")
+
+
+SQ_NOTES = {
+    "SQ_WAVES": "waves launched",
+    "SQ_INSTS_VALU": "vector ALU instructions issued (per wave, all kinds)",
+    "SQ_INSTS_VALU_TRANS_F32": "of which fp32 transcendentals (exp, rcp, ...)",
+    "SQ_ACTIVE_INST_VALU": "wave-cycles executing VALU instructions",
+    "SQ_WAVE_CYCLES": "wave-cycles resident",
+    "SQ_WAIT_ANY": "wave-cycles waiting for anything",
+    "SQ_WAIT_INST_LDS": "wave-cycles waiting to issue LDS instructions",
+    "SQ_WAIT_INST_ANY": "wave-cycles waiting to issue any instruction",
+    "SQ_INSTS_LDS": "LDS instructions",
+    "SQ_LDS_BANK_CONFLICT": "LDS bank-conflict cycles",
+    "SQ_INSTS_MFMA": "matrix-core instructions",
+    "SQ_INSTS_SALU": "scalar ALU instructions",
+    "SQ_INSTS_VMEM_RD": "vector memory reads",
+}
+
+
+def cmd_sq(a):
+    vals = {}
+    for path in a.csv:
+        names = sorted({r["Counter_Name"] for r in _rows(path) if a.kernel in r.get("Kernel_Name", "")})
+        for n in names:
+            v = _counter_per_dispatch(path, n, a.kernel)
+            if v:
+                vals[n] = (statistics.median(v), len(v))
+    if not vals:
+        sys.exit("no dispatches of %r" % a.kernel)
+    g = lambda n: vals[n][0] if n in vals else None
+    lines = ["# %s" % a.title, "", "Commands (from the repository root):", "", "```"] + list(a.commands) + [
+             "```", "", "Kernel: `%s`. Counters are per dispatch (median over dispatches), summed over "
+             "the GPU." % _short(a.kernel, 100), "",
+             "| counter | value | meaning |", "|---|---:|---|"]
+    for n in sorted(vals):
+        lines.append("| %s | %.4g | %s |" % (n, vals[n][0], SQ_NOTES.get(n, "")))
+    lines += ["", "| derived | value |", "|---|---:|"]
+    if a.updates and g("SQ_INSTS_VALU") is not None:
+        lines.append("| state updates per dispatch | %d |" % a.updates)
+        lines.append("| VALU instructions per update (64 lanes each; the step loop's core is 6) | %.3f |"
+                     % (g("SQ_INSTS_VALU") * 64 / a.updates))
+        if g("SQ_INSTS_VALU_TRANS_F32") is not None:
+            lines.append("| fp32 transcendentals per update (one exp is the core) | %.3f |"
+                         % (g("SQ_INSTS_VALU_TRANS_F32") * 64 / a.updates))
+    if g("SQ_WAVE_CYCLES"):
+        for n in ("SQ_WAIT_ANY", "SQ_WAIT_INST_LDS", "SQ_WAIT_INST_ANY", "SQ_ACTIVE_INST_VALU"):
+            if g(n) is not None:
+                lines.append("| %s / SQ_WAVE_CYCLES | %.3f |" % (n, g(n) / g("SQ_WAVE_CYCLES")))
+    if a.duration_us and g("SQ_INSTS_VALU") is not None:
+        # a wave64 VALU instruction occupies a SIMD16 for 4 cycles, an fp32
+        # transcendental for 8; 1024 SIMDs at 2.4 GHz
+        trans = g("SQ_INSTS_VALU_TRANS_F32") or 0.0
+        cyc = (g("SQ_INSTS_VALU") + trans) * 4.0
+        avail = 1024 * a.duration_us * 1e-6 * 2.4e9
+        lines.append("| kernel duration (us, from the kernel trace) | %.2f |" % a.duration_us)
+        lines.append("| VALU issue cycles / SIMD cycles (4 per instruction, 8 per transcendental) | %.3f |"
+                     % (cyc / avail))
     _write(a.out, "\n".join(lines) + "\n")
 
 
@@ -129,17 +198,26 @@ def main(argv=None):
     s.add_argument("--title", default="Kernel durations (rocprofv3 --kernel-trace --stats)")
     s.add_argument("--top", type=int, default=12)
     c = sub.add_parser("counters")
-    for k in ("--fetch", "--write", "--copy-fetch", "--copy-write", "--kernel", "--key",
-              "--out-json", "--out"):
+    for k in ("--fetch", "--write", "--copy-fetch", "--copy-write", "--key", "--out-json", "--out"):
         c.add_argument(k, required=True)
+    c.add_argument("--kernel", nargs="+", required=True,
+                   help="kernel name substrings; the step's kernels are summed")
     c.add_argument("--copy-kernel", default="copyBuffer")
     c.add_argument("--copy-bytes", type=int, required=True)
     c.add_argument("--algorithmic-bytes", type=int, required=True)
     c.add_argument("--commands", nargs="+", required=True)
     c.add_argument("--sources", nargs="+", default=None,
                    help="library sources the kernel is built from (file names under csrc/)")
+    q = sub.add_parser("sq")
+    q.add_argument("--csv", nargs="+", required=True)
+    q.add_argument("--kernel", required=True)
+    q.add_argument("--updates", type=int, default=0, help="state updates per dispatch")
+    q.add_argument("--duration-us", type=float, default=0.0)
+    q.add_argument("--title", required=True)
+    q.add_argument("--commands", nargs="+", required=True)
+    q.add_argument("--out", required=True)
     a = ap.parse_args(argv)
-    {"stats": cmd_stats, "counters": cmd_counters}[a.cmd](a)
+    {"stats": cmd_stats, "counters": cmd_counters, "sq": cmd_sq}[a.cmd](a)
 
 
 if __name__ == "__main__":
