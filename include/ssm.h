@@ -229,7 +229,8 @@ typedef struct ssm_state_update_args {
     const float *Dskip;     /* (D) fp32, or NULL                          */
     const float *delta_bias;/* (D) fp32, or NULL                          */
     void *y;                /* (B,D) io_dtype output; must not overlap any input or the state */
-    int64_t conv_k;         /* 0: no prologue; 1..SSM_MAX_CONV_K: causal conv1d + SiLU on x */
+    int64_t conv_k;         /* 0: no prologue; 1..SSM_MAX_CONV_K: causal conv1d + SiLU on x
+                               (then D <= 2^28, else SSM_ERR_UNSUPPORTED) */
     const float *conv_w;    /* (D,conv_k) fp32; required iff conv_k > 0   */
     const float *conv_b;    /* (D) fp32, or NULL (= 0)                    */
     void *conv_state;       /* (B,conv_k-1,D) io_dtype, updated in place; required iff

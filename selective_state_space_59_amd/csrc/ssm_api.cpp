@@ -260,6 +260,8 @@ ssm_status_t ssm_state_update(const ssm_state_update_args_t *a, void *stream) {
         return fail(SSM_ERR_UNSUPPORTED, "conv_k %lld exceeds SSM_MAX_CONV_K (%d)", (long long)a->conv_k, SSM_MAX_CONV_K);
     if (a->conv_k == 0 && (a->conv_w || a->conv_b || a->conv_state))
         return fail(SSM_ERR_BAD_SHAPE, "conv_w/conv_b/conv_state given but conv_k == 0");
+    if (a->conv_k > 0 && a->dim > ((int64_t)1 << 28))
+        return fail(SSM_ERR_UNSUPPORTED, "dim %lld with a conv window exceeds 2^28", (long long)a->dim);
     const int64_t B = a->batch, D = a->dim, N = a->dstate, K = a->conv_k;
     const int64_t es = io_bytes(a->io_dtype);
     if (B == 0) return ok();

@@ -57,12 +57,15 @@ struct UpdateParams {
 struct ConvLane {
     float tap, win, bias;
 };
+// `win_b` is the window of batch row b (the (K-1, D) slab at b (K-1) D); the
+// offsets within it, and within conv_w, fit 32 bits (checked at launch).
 template <typename IO>
-__device__ __forceinline__ ConvLane load_conv(const UpdateParams &p, int64_t b, int64_t d, int j) {
+__device__ __forceinline__ ConvLane load_conv(const UpdateParams &p, const char *win_b, int d, int j) {
+    constexpr int es = sizeof(typename IO::storage);
     const int r = p.K - 4 + j;  // tap index = window row of this lane
     ConvLane c;
     c.tap = r >= 0 ? p.conv_w[d * p.K + r] : 0.0f;
-    c.win = (j < 3 && r >= 0) ? load_io<IO>(p.cs, (b * (p.K - 1) + r) * p.D + d) : 0.0f;
+    c.win = (j < 3 && r >= 0) ? load_io<IO>(win_b + (uint32_t)(r * (int)p.D + d) * es, 0) : 0.0f;
     c.bias = (j == 3 && p.conv_b) ? p.conv_b[d] : 0.0f;
     return c;
 }
@@ -78,9 +81,10 @@ __device__ __forceinline__ float conv_shift(float v) {
     return __builtin_amdgcn_update_dpp(0.0f, v, 0xF9, 0xf, 0xf, false);  // quad_perm [1,2,3,3]
 }
 template <typename IO>
-__device__ __forceinline__ void store_window(const UpdateParams &p, int64_t b, int64_t d, int j, float nv) {
+__device__ __forceinline__ void store_window(const UpdateParams &p, char *win_b, int d, int j, float nv) {
+    constexpr int es = sizeof(typename IO::storage);
     const int r = p.K - 4 + j;
-    if (j < 3 && r >= 0) store_io<IO>(p.cs, (b * (p.K - 1) + r) * p.D + d, nv);
+    if (j < 3 && r >= 0) store_io<IO>(win_b + (uint32_t)(r * (int)p.D + d) * es, 0, nv);
 }
 
 // phi(z) = (e^z - 1) / z given e = e^z.
@@ -114,7 +118,7 @@ __device__ __forceinline__ float quad_sum(float v) {
 // N = 16 with 16-byte aligned state, A, B and C.  Tile t = (batch row b,
 // channel run): round r gives lane l channel d = run * 128 + r * 64 + l / 4
 // and entries 4 (l % 4) .. +3 of it.
-template <typename IO>
+template <typename IO, bool CONV>
 __device__ __forceinline__ void state_update_tile(const UpdateParams &p, int64_t t, int64_t ntiles) {
     constexpr int R = kRounds;
     const int64_t b = t / ntiles;
@@ -125,6 +129,8 @@ __device__ __forceinline__ void state_update_tile(const UpdateParams &p, int64_t
     float xv[R], dv[R], zv[R], dsk[R];
     ConvLane cin[R];
     int64_t dd[R];
+    constexpr int es = sizeof(typename IO::storage);
+    char *win_b = CONV ? static_cast<char *>(p.cs) + b * (p.K - 1) * p.D * es : nullptr;
     // All loads first.
 #pragma unroll
     for (int r = 0; r < R; ++r) {
@@ -142,7 +148,7 @@ __device__ __forceinline__ void state_update_tile(const UpdateParams &p, int64_t
         zv[r] = p.z ? load_io<IO>(p.z, ch) : 0.0f;
         dsk[r] = p.Dskip ? p.Dskip[dc] : 0.0f;
         if (p.softplus) dv[r] = softplus(dv[r] + (p.dbias ? p.dbias[dc] : 0.0f));
-        if (p.K > 0) cin[r] = load_conv<IO>(p, b, dc, jq);
+        if (CONV) cin[r] = load_conv<IO>(p, win_b, (int)dc, jq);
     }
     const float4 bv = load4_io<IO>(p.Bm, b * SSM_MAX_DSTATE + 4 * jq);
     const float4 cv = load4_io<IO>(p.Cm, b * SSM_MAX_DSTATE + 4 * jq);
@@ -159,9 +165,9 @@ __device__ __forceinline__ void state_update_tile(const UpdateParams &p, int64_t
         const bool live = dd[r] < p.D;
         const int64_t ch = b * p.D + (live ? dd[r] : 0);
         const float dt = dv[r];
-        const float vin = p.K > 0 ? conv_in(cin[r], jq, xv[r]) : 0.0f;
-        const float u = p.K > 0 ? conv_u(cin[r], vin) : xv[r];
-        const float nwin = p.K > 1 ? conv_shift(vin) : 0.0f;
+        const float vin = CONV ? conv_in(cin[r], jq, xv[r]) : 0.0f;
+        const float u = CONV ? conv_u(cin[r], vin) : xv[r];
+        const float nwin = CONV ? conv_shift(vin) : 0.0f;
         const float a[4] = {av[r].x, av[r].y, av[r].z, av[r].w};
         float h[4] = {st[r].x, st[r].y, st[r].z, st[r].w};
         float acc = 0.0f;
@@ -184,7 +190,7 @@ __device__ __forceinline__ void state_update_tile(const UpdateParams &p, int64_t
         }
         acc = quad_sum(acc);
         // The window was read above by every lane of the quad (loads first).
-        if (live && p.K > 1) store_window<IO>(p, b, dd[r], jq, nwin);
+        if (CONV && live && p.K > 1) store_window<IO>(p, win_b, (int)dd[r], jq, nwin);
         if (live && jq == 0) {
             float yv = acc + dsk[r] * u;
             if (p.z) yv *= silu(zv[r]);
@@ -195,13 +201,15 @@ __device__ __forceinline__ void state_update_tile(const UpdateParams &p, int64_t
 
 // One tile per workgroup; a loop over tiles only where they outnumber one
 // grid (the loop costs time even when it runs once).
-template <typename IO, bool LOOP>
+// CONV: the conv prologue runs on the window (conv_k > 0), a compile-time
+// choice so that neither path carries the other's branches.
+template <typename IO, bool LOOP, bool CONV>
 __global__ __launch_bounds__(256) void state_update_vec_kernel(UpdateParams p, int64_t ntiles, int64_t total) {
     if (!LOOP) {
-        state_update_tile<IO>(p, blockIdx.x, ntiles);
+        state_update_tile<IO, CONV>(p, blockIdx.x, ntiles);
         return;
     }
-    for (int64_t t = blockIdx.x; t < total; t += gridDim.x) state_update_tile<IO>(p, t, ntiles);
+    for (int64_t t = blockIdx.x; t < total; t += gridDim.x) state_update_tile<IO, CONV>(p, t, ntiles);
 }
 
 // Any N <= 16 and any alignment: one quarter per thread, element loads.
@@ -220,7 +228,9 @@ __global__ __launch_bounds__(256) void state_update_kernel(UpdateParams p) {
     if (p.softplus) dt = softplus(dt + (p.dbias ? p.dbias[d] : 0.0f));
     const float xin = load_io<IO>(p.x, chc);
     ConvLane cin{0.0f, 0.0f, 0.0f};
-    if (p.K > 0) cin = load_conv<IO>(p, b, d, j);
+    constexpr int es = sizeof(typename IO::storage);
+    char *win_b = p.K > 0 ? static_cast<char *>(p.cs) + b * (p.K - 1) * p.D * es : nullptr;
+    if (p.K > 0) cin = load_conv<IO>(p, win_b, (int)d, j);
     const float vin = p.K > 0 ? conv_in(cin, j, xin) : 0.0f;
     const float u = p.K > 0 ? conv_u(cin, vin) : xin;
     const float nwin = p.K > 1 ? conv_shift(vin) : 0.0f;
@@ -249,7 +259,7 @@ __global__ __launch_bounds__(256) void state_update_kernel(UpdateParams p) {
             if (n0 + k < N) sp[k] = hs[k];
     }
     acc = quad_sum(acc);
-    if (live && p.K > 1) store_window<IO>(p, b, d, j, nwin);
+    if (live && p.K > 1) store_window<IO>(p, win_b, (int)d, j, nwin);
     if (live && j == 0) {
         float yv = acc + (p.Dskip ? p.Dskip[d] * u : 0.0f);
         if (p.z) yv *= silu(load_io<IO>(p.z, chc));
@@ -263,10 +273,14 @@ hipError_t launch_typed(const UpdateParams &p, bool vec, hipStream_t stream) {
     if (vec) {
         const int64_t ntiles = (p.D + kTileChannels - 1) / kTileChannels;
         const int64_t total = p.B * ntiles;
-        if (total <= kMaxGrid)
-            state_update_vec_kernel<IO, false><<<(unsigned)total, 256, 0, stream>>>(p, ntiles, total);
-        else
-            state_update_vec_kernel<IO, true><<<(unsigned)kMaxGrid, 256, 0, stream>>>(p, ntiles, total);
+        const unsigned grid = (unsigned)(total <= kMaxGrid ? total : kMaxGrid);
+        if (total <= kMaxGrid) {
+            if (p.K > 0) state_update_vec_kernel<IO, false, true><<<grid, 256, 0, stream>>>(p, ntiles, total);
+            else state_update_vec_kernel<IO, false, false><<<grid, 256, 0, stream>>>(p, ntiles, total);
+        } else {
+            if (p.K > 0) state_update_vec_kernel<IO, true, true><<<grid, 256, 0, stream>>>(p, ntiles, total);
+            else state_update_vec_kernel<IO, true, false><<<grid, 256, 0, stream>>>(p, ntiles, total);
+        }
     } else {
         const unsigned blocks = (unsigned)((nq + 255) / 256);
         state_update_kernel<IO><<<blocks, 256, 0, stream>>>(p);
