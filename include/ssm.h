@@ -391,15 +391,16 @@ void ssm_block_plan_destroy(ssm_block_plan_t *plan);
  *             (the weight is dt where dt A[h] == 0), from h0 (or 0)
  *   y[b,t,h,p] = (sum_n Cm[b,t,g,n] S[p,n] + Dskip[h] x[b,t,h,p]) * silu(z[b,t,h,p])
  * The state layout (B, H, P, N) is the scan's (B, D, N) with D = H P.
- * This version: bf16 I/O, headdim P == 64, dstate N in {16, 32, 64, 128},
- * batch * nheads <= 2^22; other values give SSM_ERR_UNSUPPORTED.  Products run in bf16 on the matrix
+ * This version: bf16 I/O, headdim P a multiple of 32 up to 4096, dstate N in
+ * {16, 32, 64, 128}, batch * nheads * P / 32 <= 2^23; other values give
+ * SSM_ERR_UNSUPPORTED.  Products run in bf16 on the matrix
  * cores with fp32 accumulation; the state is fp32 (its bf16 copy feeds the
  * product with C).
  */
 typedef struct ssm_ssd_args {
     int64_t batch, seqlen;  /* B >= 0, L >= 0                                  */
     int64_t nheads;         /* H >= 1                                          */
-    int64_t headdim;        /* P (64)                                          */
+    int64_t headdim;        /* P, a multiple of 32 (<= 4096)                   */
     int64_t ngroups;        /* G >= 1, divides H: heads of a group share B, C  */
     int64_t dstate;         /* N (16, 32, 64 or 128)                           */
     int32_t io_dtype;       /* SSM_BF16                                        */

@@ -47,8 +47,8 @@ namespace ssm {
 namespace {
 
 constexpr int kQ = 64;     // chunk length (4 tiles of 16)
-constexpr int kP = 64;     // head channels
-constexpr int kPT = 32;    // head channels per workgroup
+constexpr int64_t kMaxHeadDim = 4096;
+constexpr int kPT = 32;    // head channels per workgroup (the head dim P is a multiple)
 constexpr int kPTL = kPT / 16;  // MFMA column tiles per workgroup
 constexpr int kPadE = 8;   // row padding, bf16 elements (16 bytes)
 constexpr int kThreads = 256;
@@ -85,6 +85,7 @@ struct SsdLds {
 
 struct SsdParams {
     int64_t B, L, H, G;
+    int64_t P;  // head dim, a multiple of kPT
     const uint16_t *x, *delta, *Bm, *Cm, *z;
     const float *A, *Dskip, *dbias, *h0;
     uint16_t *y;
@@ -225,7 +226,7 @@ __device__ __forceinline__ void fetch_chunk(const SsdParams &p, int64_t b, int64
         r.x = make_uint4(0, 0, 0, 0);
         r.z = r.x;
         if (t < L) {
-            const int64_t off = ((b * L + t) * p.H + h) * kP + kPT * pt + c8;
+            const int64_t off = ((b * L + t) * p.H + h) * p.P + kPT * pt + c8;
             r.x = *reinterpret_cast<const uint4 *>(p.x + off);
             if (p.z && outputs) r.z = *reinterpret_cast<const uint4 *>(p.z + off);
         }
@@ -293,8 +294,8 @@ __global__ __launch_bounds__(kThreads, 2) void ssd_chunk_kernel(SsdParams p) {
     ssd_slot_rows(lane >> 4, nld, brow);
     const int64_t seg = (int64_t)blockIdx.x % p.nseg;
     const int64_t bhp = (int64_t)blockIdx.x / p.nseg;
-    const int pt = (int)(bhp % (kP / kPT));
-    const int64_t bh = bhp / (kP / kPT);
+    const int pt = (int)(bhp % (p.P / kPT));
+    const int64_t bh = bhp / (p.P / kPT);
     const int64_t b = bh / p.H, h = bh % p.H;
     const int64_t g = h / (p.H / p.G);
     const int64_t L = p.L;
@@ -313,8 +314,8 @@ __global__ __launch_bounds__(kThreads, 2) void ssd_chunk_kernel(SsdParams p) {
     constexpr bool outputs = MODE != 1;
     // the entering state: h0 (or 0) for the whole sequence, 0 for a segment's
     // end state, the combined entering state for a segment's outputs
-    const float *hin = MODE == 0 ? p.h0 : MODE == 2 ? p.ws_state + seg * p.B * p.H * kP * N : nullptr;
-    const float *hin_bh = hin ? hin + bh * kP * N : nullptr;
+    const float *hin = MODE == 0 ? p.h0 : MODE == 2 ? p.ws_state + seg * p.B * p.H * p.P * N : nullptr;
+    const float *hin_bh = hin ? hin + bh * p.P * N : nullptr;
 #pragma unroll
     for (int i = 0; i < NWT; ++i)
 #pragma unroll
@@ -504,7 +505,7 @@ __global__ __launch_bounds__(kThreads, 2) void ssd_chunk_kernel(SsdParams p) {
                 const int t = tid / (kPT / 8), c8 = (tid % (kPT / 8)) * 8;
                 const int64_t tt = t0 + t;
                 if (tt < L)
-                    *reinterpret_cast<uint4 *>(p.y + ((b * L + tt) * p.H + h) * kP + kPT * pt + c8) =
+                    *reinterpret_cast<uint4 *>(p.y + ((b * L + tt) * p.H + h) * p.P + kPT * pt + c8) =
                         *reinterpret_cast<const uint4 *>(Zs + t * tld + c8);
             }
         }
@@ -546,7 +547,7 @@ __global__ __launch_bounds__(kThreads, 2) void ssd_chunk_kernel(SsdParams p) {
     }
 
     // the final state (whole sequence), or a segment's end state and decay
-    float *hout = MODE == 0 ? p.h_final : MODE == 1 ? p.ws_state + seg * p.B * p.H * kP * N : nullptr;
+    float *hout = MODE == 0 ? p.h_final : MODE == 1 ? p.ws_state + seg * p.B * p.H * p.P * N : nullptr;
     if (hout && owns_state) {
 #pragma unroll
         for (int i = 0; i < NWT; ++i)
@@ -554,7 +555,7 @@ __global__ __launch_bounds__(kThreads, 2) void ssd_chunk_kernel(SsdParams p) {
             for (int j = 0; j < kPTL; ++j)
 #pragma unroll
                 for (int v = 0; v < 4; ++v)
-                    hout[(bh * kP + kPT * pt + 16 * j + r16) * N + 16 * my_nt(i) + q4 + v] = st[i][j][v];
+                    hout[(bh * p.P + kPT * pt + 16 * j + r16) * N + 16 * my_nt(i) + q4 + v] = st[i][j][v];
     }
     if (MODE == 1 && pt == 0 && tid == 0) p.ws_lsum[seg * p.B * p.H + bh] = lsum;
 }
@@ -580,7 +581,7 @@ __global__ __launch_bounds__(256) void ssd_seg_combine_kernel(float *ws_state, c
 
 template <int N>
 hipError_t launch_n(const SsdParams &p, hipStream_t stream) {
-    const unsigned grid = (unsigned)(p.B * p.H * (kP / kPT) * p.nseg);
+    const unsigned grid = (unsigned)(p.B * p.H * (p.P / kPT) * p.nseg);
     const size_t lds = SsdLds<N>::total;
     if (p.mode == 1)
         ssd_chunk_kernel<N, 1><<<grid, kThreads, lds, stream>>>(p);
@@ -618,7 +619,7 @@ SsdPlan ssd_plan(const ssm_ssd_args_t &a) {
     SsdPlan q{1, 0, 0, 0};
     const int64_t nchunks = (a.seqlen + kQ - 1) / kQ;
     q.seg_chunks = nchunks;
-    const int64_t wgs = a.batch * a.nheads * (kP / kPT);
+    const int64_t wgs = a.batch * a.nheads * (a.headdim / kPT);
     if (wgs > 0 && 2 * wgs <= kSlotsWanted) {
         int64_t s = std::min<int64_t>({kMaxSeg, kSlotsWanted / wgs, nchunks / kMinSegChunks});
         if (s > 1) {
@@ -628,7 +629,7 @@ SsdPlan ssd_plan(const ssm_ssd_args_t &a) {
     }
     if (q.nseg > 1) {
         auto r256 = [](size_t v) { return (v + 255) & ~(size_t)255; };
-        q.ws_state = r256((size_t)(q.nseg * a.batch * a.nheads * kP * a.dstate) * sizeof(float));
+        q.ws_state = r256((size_t)(q.nseg * a.batch * a.nheads * a.headdim * a.dstate) * sizeof(float));
         q.ws_lsum = r256((size_t)(q.nseg * a.batch * a.nheads) * sizeof(float));
     }
     return q;
@@ -776,7 +777,8 @@ hipError_t launch_ssd_step(const ssm_ssd_step_args_t &a, hipStream_t stream) {
 }
 
 bool ssd_supported(int64_t headdim, int64_t dstate) {
-    return headdim == kP && (dstate == 16 || dstate == 32 || dstate == 64 || dstate == 128);
+    return headdim >= kPT && headdim <= kMaxHeadDim && headdim % kPT == 0 &&
+           (dstate == 16 || dstate == 32 || dstate == 64 || dstate == 128);
 }
 
 size_t ssd_workspace_bytes(const ssm_ssd_args_t &a) {
@@ -790,6 +792,7 @@ hipError_t launch_ssd_fwd(const ssm_ssd_args_t &a, hipStream_t stream) {
     p.L = a.seqlen;
     p.H = a.nheads;
     p.G = a.ngroups;
+    p.P = a.headdim;
     p.x = static_cast<const uint16_t *>(a.x);
     p.delta = static_cast<const uint16_t *>(a.delta);
     p.Bm = static_cast<const uint16_t *>(a.Bm);
@@ -817,7 +820,7 @@ hipError_t launch_ssd_fwd(const ssm_ssd_args_t &a, hipStream_t stream) {
     p.mode = 1;
     hipError_t e = launch_dstate(p, a.dstate, stream);
     if (e != hipSuccess) return e;
-    const int64_t BH = a.batch * a.nheads, PN = kP * a.dstate;
+    const int64_t BH = a.batch * a.nheads, PN = a.headdim * a.dstate;
     ssd_seg_combine_kernel<<<(unsigned)((BH * PN + 255) / 256), 256, 0, stream>>>(p.ws_state, p.ws_lsum, a.h0,
                                                                                  a.h_final, BH, PN, q.nseg);
     e = hipGetLastError();

@@ -498,7 +498,8 @@ ssm_status_t check_ssd_sizes(const ssm_ssd_args_t *a) {
                     (long long)a->nheads);
     if (a->io_dtype != SSM_BF16) return fail(SSM_ERR_UNSUPPORTED, "the SSD layer takes bf16 I/O");
     if (!ssm::ssd_supported(a->headdim, a->dstate))
-        return fail(SSM_ERR_UNSUPPORTED, "SSD needs headdim 64 and dstate 16, 32, 64 or 128 (got %lld, %lld)",
+        return fail(SSM_ERR_UNSUPPORTED,
+                    "SSD needs headdim a multiple of 32 up to 4096 and dstate 16, 32, 64 or 128 (got %lld, %lld)",
                     (long long)a->headdim, (long long)a->dstate);
     if (a->delta_softplus != 0 && a->delta_softplus != 1)
         return fail(SSM_ERR_UNSUPPORTED, "delta_softplus must be 0 or 1");
@@ -506,8 +507,9 @@ ssm_status_t check_ssd_sizes(const ssm_ssd_args_t *a) {
     if (!mul_ok(B, L, H * P) || !mul_ok(B, L, G * N) || !mul_ok(B, H, P * N))
         return fail(SSM_ERR_BAD_SHAPE, "sizes overflow");
     // one workgroup of 256 threads per (batch, head, 32 channels): the launch holds < 2^32 threads
-    if (B * H > ((int64_t)1 << 22))
-        return fail(SSM_ERR_UNSUPPORTED, "batch * nheads (%lld) exceeds 2^22", (long long)(B * H));
+    if (B * H * (P / 32) > ((int64_t)1 << 23))
+        return fail(SSM_ERR_UNSUPPORTED, "batch * nheads * headdim / 32 (%lld) exceeds 2^23",
+                    (long long)(B * H * (P / 32)));
     return SSM_OK;
 }
 }  // namespace

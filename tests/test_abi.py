@@ -515,7 +515,8 @@ def run_ssd(a):
     ("batch", -1, ssm.SSM_ERR_BAD_SHAPE),
     ("nheads", 0, ssm.SSM_ERR_BAD_SHAPE),
     ("ngroups", 3, ssm.SSM_ERR_BAD_SHAPE),                 # does not divide 4 heads
-    ("headdim", 32, ssm.SSM_ERR_UNSUPPORTED),
+    ("headdim", 48, ssm.SSM_ERR_UNSUPPORTED),             # not a multiple of 32
+    ("headdim", 8192, ssm.SSM_ERR_UNSUPPORTED),
     ("dstate", 100, ssm.SSM_ERR_UNSUPPORTED),
     ("dstate", 256, ssm.SSM_ERR_UNSUPPORTED),
     ("delta_softplus", 3, ssm.SSM_ERR_UNSUPPORTED),
@@ -526,7 +527,7 @@ def run_ssd(a):
     ("delta", addr(1, 1), ssm.SSM_ERR_ALIGN),
     ("y", addr(0, 256), ssm.SSM_ERR_ALIAS),                # inside x
     ("h_final", addr(7), ssm.SSM_ERR_ALIAS),               # == y
-    ("nheads", 1 << 22, ssm.SSM_ERR_UNSUPPORTED),          # batch * nheads > 2^22
+    ("nheads", 1 << 22, ssm.SSM_ERR_UNSUPPORTED),          # batch * nheads * P / 32 > 2^23
 ])
 def test_ssd_rejects_bad_arguments(field, value, status):
     assert run_ssd(ssd_args(**{field: value})) == status

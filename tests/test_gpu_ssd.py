@@ -77,6 +77,30 @@ def test_ssd_matches_oracle(name, B, L, H, G, N, extra):
     assert _ssm_part_matters(y, inp) > 0.1
 
 
+HEADDIM_CASES = [
+    # name, B, L, H, P, G, N, extra
+    ("p32_one_workgroup_per_head", 2, 150, 3, 32, 1, 64, dict(h0=True)),
+    ("p96_three_workgroups", 1, 130, 2, 96, 1, 128, {}),
+    ("p128_groups", 1, 200, 4, 128, 2, 32, dict(h0=True)),
+    ("p32_segments", 1, 2600, 2, 32, 1, 16, dict(h0=True)),
+    ("p256_segments_n128", 1, 1500, 1, 256, 1, 128, {}),
+]
+
+
+@pytest.mark.parametrize("name,B,L,H,P,G,N,extra", HEADDIM_CASES, ids=[c[0] for c in HEADDIM_CASES])
+def test_ssd_head_dims(name, B, L, H, P, G, N, extra):
+    """Head dims other than 64 (any multiple of 32: one workgroup per 32 channels of a
+    head), whole sequences and segmented ones, against the oracle."""
+    print("case", name, flush=True)
+    inp = W.make_ssd_inputs(B, L, H, P, G, N, seed=820 + L + P, device=DEV, **extra)
+    y, hf = _run(inp)
+    yr, hr = _oracle(inp)
+    wy = assert_close(to64(y), yr, TOL_BF16, "y")
+    wh = assert_close(to64(hf), hr, TOL_BF16, "h_final")
+    print("  worst scaled error y %.2e, h_final %.2e" % (wy, wh), flush=True)
+    assert _ssm_part_matters(y, inp) > 0.1
+
+
 def test_ssd_softplus_bias_zero_and_positive_A():
     inp = W.make_ssd_inputs(1, 150, 4, 64, 1, 64, seed=851, device=DEV)
     g = torch.Generator(DEV).manual_seed(9)
