@@ -311,27 +311,28 @@ def cpu_baseline(inp, cfg, min_seconds=10.0, block_rows=8192):
                                                       cfg.dstate, block_rows, nthreads))
 
 
-def ssd_algorithmic(cfg, chunk=64):
+def ssd_algorithmic(cfg, chunk=64, io_bytes=2):
     """HBM bytes and matrix FLOPs of one SSD layer call.  Bytes: x, z read and y written
     (bf16, B*L*H*P each), delta (B*L*H) and B, C (B*L*G*N each) read, h_final written (fp32).
     FLOPs of the chunked algorithm (2 per multiply-add), per (batch, head, chunk of Q): the
     causal half of C.B^T (Q(Q+1)/2 * N), its product with X (Q(Q+1)/2 * P), C H^T (Q N P) and
     the state update B^T X (Q N P)."""
     B, L, H, P, G, N = cfg.batch, cfg.seqlen, cfg.nheads, cfg.headdim, cfg.ngroups, cfg.dstate
-    nbytes = 3 * 2 * B * L * H * P + 2 * B * L * H + 2 * 2 * B * L * G * N + 4 * B * H * P * N
+    nbytes = (3 * io_bytes * B * L * H * P + io_bytes * B * L * H + 2 * io_bytes * B * L * G * N
+              + 4 * B * H * P * N)
     Q = chunk
     per_chunk = 2 * (Q * (Q + 1) // 2 * (N + P) + 2 * Q * N * P)
     flops = per_chunk * B * H * ((L + Q - 1) // Q)
     return nbytes, flops
 
 
-def bench_ssd(cfg, steps, warmup):
+def bench_ssd(cfg, steps, warmup, io_dtype=None):
     """The SSD (Mamba-2) layer of `cfg` on one seeded input set, with its final state."""
     import torch
     import selective_state_space_59_amd as ssm
     from selective_state_space_59_amd import workloads as W
     dev = "cuda:0"
-    s = W.make_ssd_config_inputs(cfg, device=dev)
+    s = W.make_ssd_config_inputs(cfg, device=dev, io_dtype=io_dtype or torch.bfloat16)
     y = torch.empty_like(s["x"])
     hf = torch.empty(cfg.batch, cfg.nheads, cfg.headdim, cfg.dstate, device=dev)
 
@@ -345,9 +346,10 @@ def bench_ssd(cfg, steps, warmup):
     return ms
 
 
-def ssd_entry(cfg, steps, warmup):
-    ms = bench_ssd(cfg, steps, warmup)
-    nbytes, flops = ssd_algorithmic(cfg)
+def ssd_entry(cfg, steps, warmup, f32=False):
+    import torch
+    ms = bench_ssd(cfg, steps, warmup, io_dtype=torch.float32 if f32 else None)
+    nbytes, flops = ssd_algorithmic(cfg, io_bytes=4 if f32 else 2)
     tokens = cfg.batch * cfg.seqlen
     return dict(ms=round(ms, 4), tokens_per_s=round(tokens / (ms * 1e-3), 1),
                 gbs=round(nbytes / (ms * 1e-3) / 1e9, 2),
@@ -356,7 +358,8 @@ def ssd_entry(cfg, steps, warmup):
                 tflops=round(flops / (ms * 1e-3) / 1e12, 2),
                 config=dict(batch=cfg.batch, seq_len=cfg.seqlen, nheads=cfg.nheads,
                             headdim=cfg.headdim, ngroups=cfg.ngroups, dstate=cfg.dstate,
-                            io_dtype="bf16", chunk=64))
+                            io_dtype="f32" if f32 else "bf16",
+                            form="recurrent (fp32)" if f32 else "chunked, matrix cores", chunk=64))
 
 
 def ssd_step_algorithmic(cfg):
@@ -566,6 +569,9 @@ def main():
         # the SSD (Mamba-2) layer at the 130M-like width with N = 128
         print("bench extra: %s" % W.S2_MAMBA2_130M.name, file=sys.stderr, flush=True)
         extra[W.S2_MAMBA2_130M.name] = ssd_entry(W.S2_MAMBA2_130M, 30, 5)
+        # the same layer with fp32 I/O: its recurrent form
+        print("bench extra: %s_f32" % W.S2_MAMBA2_130M.name, file=sys.stderr, flush=True)
+        extra[W.S2_MAMBA2_130M.name + "_f32"] = ssd_entry(W.S2_MAMBA2_130M, 10, 2, f32=True)
         # one 65536-token sequence at that width: the segmented schedule
         print("bench extra: %s" % W.S4_MAMBA2_LONG.name, file=sys.stderr, flush=True)
         extra[W.S4_MAMBA2_LONG.name] = ssd_entry(W.S4_MAMBA2_LONG, 10, 2)

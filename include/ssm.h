@@ -391,9 +391,12 @@ void ssm_block_plan_destroy(ssm_block_plan_t *plan);
  *             (the weight is dt where dt A[h] == 0), from h0 (or 0)
  *   y[b,t,h,p] = (sum_n Cm[b,t,g,n] S[p,n] + Dskip[h] x[b,t,h,p]) * silu(z[b,t,h,p])
  * The state layout (B, H, P, N) is the scan's (B, D, N) with D = H P.
- * This version: bf16 I/O, headdim P a multiple of 32 up to 4096, dstate N in
+ * This version: headdim P a multiple of 32 up to 4096, dstate N in
  * {16, 32, 64, 128}, batch * nheads * P / 32 <= 2^23; other values give
- * SSM_ERR_UNSUPPORTED.  Products run in bf16 on the matrix
+ * SSM_ERR_UNSUPPORTED.  bf16 I/O runs the chunked form below.  fp32 I/O runs
+ * the recurrent form (the same map, [P4] sec. 5.1) sequentially in time with
+ * the state in registers, in fp32 throughout, and needs no workspace; its
+ * Bm, Cm, h0 and h_final must be 16-byte aligned.  Products run in bf16 on the matrix
  * cores with fp32 accumulation; the state is fp32 (its bf16 copy feeds the
  * product with C).
  */
@@ -403,17 +406,17 @@ typedef struct ssm_ssd_args {
     int64_t headdim;        /* P, a multiple of 32 (<= 4096)                   */
     int64_t ngroups;        /* G >= 1, divides H: heads of a group share B, C  */
     int64_t dstate;         /* N (16, 32, 64 or 128)                           */
-    int32_t io_dtype;       /* SSM_BF16                                        */
+    int32_t io_dtype;       /* of x, delta, Bm, Cm, z, y: SSM_BF16 or SSM_F32  */
     int32_t delta_softplus; /* 0: delta is the step; 1: softplus(delta + bias) */
-    const void *x;          /* (B,L,H,P) bf16, required                        */
-    const void *delta;      /* (B,L,H) bf16, required                          */
+    const void *x;          /* (B,L,H,P) io_dtype, required                    */
+    const void *delta;      /* (B,L,H) io_dtype, required                      */
     const float *A;         /* (H) fp32, required; any finite value            */
-    const void *Bm, *Cm;    /* (B,L,G,N) bf16, required                        */
+    const void *Bm, *Cm;    /* (B,L,G,N) io_dtype, required                    */
     const float *Dskip;     /* (H) fp32, or NULL                               */
-    const void *z;          /* (B,L,H,P) bf16 gate, or NULL                    */
+    const void *z;          /* (B,L,H,P) io_dtype gate, or NULL                */
     const float *delta_bias;/* (H) fp32, or NULL                               */
     const float *h0;        /* (B,H,P,N) fp32 initial state, or NULL (= 0)     */
-    void *y;                /* (B,L,H,P) bf16 output, required                 */
+    void *y;                /* (B,L,H,P) io_dtype output, required             */
     float *h_final;         /* (B,H,P,N) fp32 output, or NULL                  */
     void *workspace;        /* device scratch of workspace_bytes, 256-aligned  */
     size_t workspace_bytes; /* >= ssm_ssd_workspace_size(args)                 */
@@ -452,7 +455,7 @@ ssm_status_t ssm_ssd_fwd(const ssm_ssd_args_t *args, void *stream);
  */
 typedef struct ssm_ssd_step_args {
     int64_t batch, nheads, headdim, ngroups, dstate; /* B >= 0, H, P, G | H, N */
-    int32_t io_dtype;       /* SSM_BF16                                        */
+    int32_t io_dtype;       /* of x, delta, Bm, Cm, z, y: SSM_BF16 or SSM_F32  */
     int32_t delta_softplus; /* as in ssm_ssd_args_t                            */
     float *state;           /* (B,H,P,N) fp32, updated in place; 16-byte aligned */
     const void *x;          /* (B,H,P) bf16, required                          */

@@ -741,6 +741,142 @@ void launch_step_q4(const SsdStepParams &p, hipStream_t stream) {
         ssd_step_kernel<Q4, true><<<(unsigned)kStepMaxGrid, 256, 0, stream>>>(p, ntiles, total);
 }
 
+// ---- fp32 I/O: the recurrent form over the whole sequence ---------------------
+//
+// The matrix-core chunks take bf16 operands, which fp32 inputs do not fit
+// without losing the fp32 bound, so fp32 I/O runs the layer in its recurrent
+// form ("14.1 SSM(State Space Models)과 Mamba 아키텍처의 부상", sec. 5.1: the
+// same map as the quadratic form): sequential in time with the state in
+// registers, as the decode step lays it out.  N / 4 lanes of an aligned group
+// hold 4 consecutive state entries of one channel each; a workgroup takes
+// 256 / (N / 4) channels of one (batch, head), so the step's decay, weight, B
+// and C rows are the same for all of it.  Per step: the state update, the
+// read-out summed by xor shuffles, skip and gate, one lane's store.  The
+// inputs of the next 4 steps are requested before the current 4 compute.
+struct SsdF32Params {
+    int64_t B, L, H, P, G;
+    const float *x, *delta, *Bm, *Cm, *z, *A, *Dskip, *dbias, *h0;
+    float *y, *h_final;
+    int softplus;
+};
+
+struct F32In {
+    float x, z, dt;
+    float4 b, c;
+};
+
+constexpr int kF32Steps = 4;
+
+template <int Q4>
+__global__ __launch_bounds__(256) void ssd_scan_f32_kernel(SsdF32Params p, int64_t ntiles) {
+    constexpr int N = 4 * Q4;
+    constexpr int CPW = 256 / Q4;  // channels per workgroup
+    const int64_t bh = blockIdx.x / ntiles;
+    const int64_t tile = blockIdx.x - bh * ntiles;
+    const int64_t h = bh % p.H, b = bh / p.H;
+    const int64_t grp = h / (p.H / p.G);
+    const int q = threadIdx.x % Q4;
+    const int64_t pc = tile * CPW + threadIdx.x / Q4;
+    const bool live = pc < p.P;
+    const int64_t pcc = live ? pc : 0;
+    const int64_t L = p.L;
+    const float a = p.A[h];
+    const float dsk = p.Dskip ? p.Dskip[h] : 0.0f;
+    const float dbias = p.dbias ? p.dbias[h] : 0.0f;
+    const int64_t chan = bh * p.P + pcc;  // (b, h, pc) as a (B, H, P) index
+    float4 st = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    if (p.h0) st = *reinterpret_cast<const float4 *>(p.h0 + chan * N + 4 * q);
+    // step t of x, z, y: (b, t, h, pc); delta: (b, t, h); B, C: (b, t, grp, 4q..4q+3)
+    const int64_t xs = p.H * p.P, bs = p.G * N;
+    const float *xb = p.x + b * L * xs + h * p.P + pcc;
+    const float *zb = p.z ? p.z + b * L * xs + h * p.P + pcc : nullptr;
+    float *yb = p.y + b * L * xs + h * p.P + pcc;
+    const float *db = p.delta + b * L * p.H + h;
+    const float *bb = p.Bm + b * L * bs + grp * N + 4 * q;
+    const float *cb = p.Cm + b * L * bs + grp * N + 4 * q;
+    auto load = [&](int64_t t, F32In &v) {
+        const int64_t tc = t < L ? t : (L > 0 ? L - 1 : 0);  // past the end: a row that exists
+        v.x = xb[tc * xs];
+        v.z = zb ? zb[tc * xs] : 0.0f;
+        v.dt = db[tc * p.H];
+        v.b = *reinterpret_cast<const float4 *>(bb + tc * bs);
+        v.c = *reinterpret_cast<const float4 *>(cb + tc * bs);
+    };
+    F32In nxt[kF32Steps];
+    if (L > 0) {
+#pragma unroll
+        for (int k = 0; k < kF32Steps; ++k) load(k, nxt[k]);
+    }
+    for (int64_t t0 = 0; t0 < L; t0 += kF32Steps) {
+        F32In cur[kF32Steps];
+#pragma unroll
+        for (int k = 0; k < kF32Steps; ++k) cur[k] = nxt[k];
+#pragma unroll
+        for (int k = 0; k < kF32Steps; ++k) load(t0 + kF32Steps + k, nxt[k]);
+#pragma unroll
+        for (int k = 0; k < kF32Steps; ++k) {
+            const int64_t t = t0 + k;
+            if (t >= L) break;  // uniform: the same t for the whole workgroup
+            float dt = cur[k].dt;
+            if (p.softplus) dt = softplus(dt + dbias);
+            const float za = dt * a;
+            const float e = expf(za);          // decay of the step
+            const float wu = dt * ssd_phi(za, e) * cur[k].x;  // ZOH input weight times x
+            st.x = __builtin_fmaf(e, st.x, wu * cur[k].b.x);
+            st.y = __builtin_fmaf(e, st.y, wu * cur[k].b.y);
+            st.z = __builtin_fmaf(e, st.z, wu * cur[k].b.z);
+            st.w = __builtin_fmaf(e, st.w, wu * cur[k].b.w);
+            float part = st.x * cur[k].c.x;
+            part = __builtin_fmaf(st.y, cur[k].c.y, part);
+            part = __builtin_fmaf(st.z, cur[k].c.z, part);
+            part = __builtin_fmaf(st.w, cur[k].c.w, part);
+#pragma unroll
+            for (int m = Q4 / 2; m >= 1; m /= 2) part += __shfl_xor(part, m, 64);
+            if (live && q == 0) {
+                float yv = part + dsk * cur[k].x;
+                if (zb) yv *= silu(cur[k].z);
+                yb[t * xs] = yv;
+            }
+        }
+    }
+    if (p.h_final && live) *reinterpret_cast<float4 *>(p.h_final + chan * N + 4 * q) = st;
+}
+
+template <int Q4>
+hipError_t launch_f32_q4(const SsdF32Params &p, hipStream_t stream) {
+    constexpr int64_t CPW = 256 / Q4;
+    const int64_t ntiles = (p.P + CPW - 1) / CPW;
+    ssd_scan_f32_kernel<Q4><<<(unsigned)(p.B * p.H * ntiles), 256, 0, stream>>>(p, ntiles);
+    return hipGetLastError();
+}
+
+hipError_t launch_ssd_f32(const ssm_ssd_args_t &a, hipStream_t stream) {
+    SsdF32Params p;
+    p.B = a.batch;
+    p.L = a.seqlen;
+    p.H = a.nheads;
+    p.P = a.headdim;
+    p.G = a.ngroups;
+    p.x = static_cast<const float *>(a.x);
+    p.delta = static_cast<const float *>(a.delta);
+    p.Bm = static_cast<const float *>(a.Bm);
+    p.Cm = static_cast<const float *>(a.Cm);
+    p.z = static_cast<const float *>(a.z);
+    p.A = a.A;
+    p.Dskip = a.Dskip;
+    p.dbias = a.delta_bias;
+    p.h0 = a.h0;
+    p.y = static_cast<float *>(a.y);
+    p.h_final = a.h_final;
+    p.softplus = a.delta_softplus;
+    switch (a.dstate) {
+        case 16: return launch_f32_q4<4>(p, stream);
+        case 32: return launch_f32_q4<8>(p, stream);
+        case 64: return launch_f32_q4<16>(p, stream);
+        default: return launch_f32_q4<32>(p, stream);
+    }
+}
+
 }  // namespace
 
 bool ssd_step_supported(int64_t dstate) {
@@ -782,11 +918,13 @@ bool ssd_supported(int64_t headdim, int64_t dstate) {
 }
 
 size_t ssd_workspace_bytes(const ssm_ssd_args_t &a) {
+    if (a.io_dtype == SSM_F32) return 0;  // the recurrent form needs none
     const SsdPlan q = ssd_plan(a);
     return q.ws_state + q.ws_lsum;
 }
 
 hipError_t launch_ssd_fwd(const ssm_ssd_args_t &a, hipStream_t stream) {
+    if (a.io_dtype == SSM_F32) return launch_ssd_f32(a, stream);
     SsdParams p;
     p.B = a.batch;
     p.L = a.seqlen;

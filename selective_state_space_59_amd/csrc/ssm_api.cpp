@@ -496,7 +496,6 @@ ssm_status_t check_ssd_sizes(const ssm_ssd_args_t *a) {
     if (a->nheads % a->ngroups != 0)
         return fail(SSM_ERR_BAD_SHAPE, "ngroups (%lld) must divide nheads (%lld)", (long long)a->ngroups,
                     (long long)a->nheads);
-    if (a->io_dtype != SSM_BF16) return fail(SSM_ERR_UNSUPPORTED, "the SSD layer takes bf16 I/O");
     if (!ssm::ssd_supported(a->headdim, a->dstate))
         return fail(SSM_ERR_UNSUPPORTED,
                     "SSD needs headdim a multiple of 32 up to 4096 and dstate 16, 32, 64 or 128 (got %lld, %lld)",
@@ -529,19 +528,31 @@ ssm_status_t ssm_ssd_fwd(const ssm_ssd_args_t *a, void *stream) {
     if (!a->A) return fail(SSM_ERR_NULL_ARG, "A is required");
     if (B * L > 0 && (!a->x || !a->delta || !a->Bm || !a->Cm || !a->y))
         return fail(SSM_ERR_NULL_ARG, "x, delta, Bm, Cm and y are required");
-    const void *a16[] = {a->x, a->Bm, a->Cm, a->z, a->y};
-    for (const void *v : a16)
-        if (!aligned(v, 16)) return fail(SSM_ERR_ALIGN, "x, Bm, Cm, z and y must be 16-byte aligned");
-    if (!aligned(a->delta, 2)) return fail(SSM_ERR_ALIGN, "delta must be 2-byte aligned");
+    const int64_t es = io_bytes(a->io_dtype);
+    if (a->io_dtype == SSM_BF16) {
+        const void *a16[] = {a->x, a->Bm, a->Cm, a->z, a->y};
+        for (const void *v : a16)
+            if (!aligned(v, 16)) return fail(SSM_ERR_ALIGN, "x, Bm, Cm, z and y must be 16-byte aligned");
+        if (!aligned(a->delta, 2)) return fail(SSM_ERR_ALIGN, "delta must be 2-byte aligned");
+    } else {
+        // fp32: the B and C rows are read as 16-byte groups of 4 entries
+        if (!aligned(a->Bm, 16) || !aligned(a->Cm, 16))
+            return fail(SSM_ERR_ALIGN, "fp32 Bm and Cm must be 16-byte aligned");
+        const void *a4io[] = {a->x, a->z, a->y, a->delta};
+        for (const void *v : a4io)
+            if (!aligned(v, 4)) return fail(SSM_ERR_ALIGN, "fp32 x, z, y and delta must be 4-byte aligned");
+    }
     const void *a4[] = {a->A, a->Dskip, a->delta_bias, a->h0, a->h_final};
     for (const void *v : a4)
         if (!aligned(v, 4)) return fail(SSM_ERR_ALIGN, "fp32 tensors must be 4-byte aligned");
-    const Range inputs[] = {range(a->x, B * L * H * P, 2, "x"), range(a->delta, B * L * H, 2, "delta"),
-                            range(a->A, H, 4, "A"), range(a->Bm, B * L * G * N, 2, "Bm"),
-                            range(a->Cm, B * L * G * N, 2, "Cm"), range(a->Dskip, H, 4, "Dskip"),
-                            range(a->z, B * L * H * P, 2, "z"), range(a->delta_bias, H, 4, "delta_bias"),
+    if (a->io_dtype == SSM_F32 && (!aligned(a->h0, 16) || !aligned(a->h_final, 16)))
+        return fail(SSM_ERR_ALIGN, "with fp32 I/O h0 and h_final must be 16-byte aligned");
+    const Range inputs[] = {range(a->x, B * L * H * P, es, "x"), range(a->delta, B * L * H, es, "delta"),
+                            range(a->A, H, 4, "A"), range(a->Bm, B * L * G * N, es, "Bm"),
+                            range(a->Cm, B * L * G * N, es, "Cm"), range(a->Dskip, H, 4, "Dskip"),
+                            range(a->z, B * L * H * P, es, "z"), range(a->delta_bias, H, 4, "delta_bias"),
                             range(a->h0, B * H * P * N, 4, "h0")};
-    const Range y = range(a->y, B * L * H * P, 2, "y"), hf = range(a->h_final, B * H * P * N, 4, "h_final");
+    const Range y = range(a->y, B * L * H * P, es, "y"), hf = range(a->h_final, B * H * P * N, 4, "h_final");
     for (const Range &r : inputs) {
         if (overlaps(y, r)) return fail(SSM_ERR_ALIAS, "y overlaps %s", r.name);
         if (overlaps(hf, r)) return fail(SSM_ERR_ALIAS, "h_final overlaps %s", r.name);

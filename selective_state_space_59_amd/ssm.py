@@ -613,8 +613,9 @@ def ssd_fwd(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, Bm: torch.Ten
             delta_bias: Optional[torch.Tensor] = None, delta_softplus: bool = False,
             h0: Optional[torch.Tensor] = None, y: Optional[torch.Tensor] = None,
             h_final: Optional[torch.Tensor] = None, return_final_state: bool = False):
-    """ssm_ssd_fwd: the SSD (Mamba-2) layer.  x, z: (B, L, H, P) bf16; delta: (B, L, H) bf16;
-    A, Dskip, delta_bias: (H,) fp32; Bm, Cm: (B, L, G, N) bf16; h0, h_final: (B, H, P, N) fp32.
+    """ssm_ssd_fwd: the SSD (Mamba-2) layer.  x, z: (B, L, H, P) and delta: (B, L, H), bf16
+    (chunked on the matrix cores) or fp32 (the recurrent form); A, Dskip, delta_bias: (H,)
+    fp32; Bm, Cm: (B, L, G, N) in x's dtype; h0, h_final: (B, H, P, N) fp32.
     Returns y, or (y, h_final) with return_final_state or h_final given."""
     if not isinstance(x, torch.Tensor) or x.dim() != 4 or x.device.type != "cuda":
         raise ValueError("x must be a (B, L, H, P) GPU tensor")
@@ -623,7 +624,8 @@ def ssd_fwd(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, Bm: torch.Ten
     dev = x.device
     Bsz, L, H, P = x.shape
     G, N = Bm.shape[2], Bm.shape[3]
-    bf, f32 = torch.bfloat16, torch.float32
+    bf, f32 = x.dtype, torch.float32
+    _io_code(bf)
     _req(x, "x", (Bsz, L, H, P), bf, dev)
     _req(delta, "delta", (Bsz, L, H), bf, dev)
     _req(A, "A", (H,), f32, dev)
@@ -639,7 +641,7 @@ def ssd_fwd(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, Bm: torch.Ten
     if h_final is None and return_final_state:
         h_final = torch.empty(Bsz, H, P, N, device=dev, dtype=f32)
     _opt(h_final, "h_final", (Bsz, H, P, N), f32, dev)
-    a = SsdArgs(batch=Bsz, seqlen=L, nheads=H, headdim=P, ngroups=G, dstate=N, io_dtype=SSM_BF16,
+    a = SsdArgs(batch=Bsz, seqlen=L, nheads=H, headdim=P, ngroups=G, dstate=N, io_dtype=_io_code(bf),
                 delta_softplus=int(bool(delta_softplus)), x=_ptr(x), delta=_ptr(delta), A=_ptr(A),
                 Bm=_ptr(Bm), Cm=_ptr(Cm), Dskip=_ptr(Dskip), z=_ptr(z), delta_bias=_ptr(delta_bias),
                 h0=_ptr(h0), y=_ptr(y), h_final=_ptr(h_final), workspace=None, workspace_bytes=0)

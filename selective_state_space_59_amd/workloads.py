@@ -249,13 +249,15 @@ def make_block_config_inputs(cfg: BlockConfig, device="cpu", **overrides):
 
 def make_ssd_inputs(batch: int, seqlen: int, nheads: int, headdim: int, ngroups: int, dstate: int,
                     seed: int = 31, device="cpu", gate: bool = True, skip: bool = True,
-                    h0: bool = False, delta_shift: float = 2.0) -> Dict[str, Optional[torch.Tensor]]:
+                    h0: bool = False, delta_shift: float = 2.0,
+                    io_dtype: torch.dtype = torch.bfloat16) -> Dict[str, Optional[torch.Tensor]]:
     """Draw one SSD input set, in order: x ~ N(0,1); delta = softplus(N(0,1) - shift) (the
     step, already activated); B, C ~ N(0,1) (as for the scan); z ~ N(0,1);
     A = -(1 .. H) / H * 4 (one negative scalar per head, spread over (0, 4]); Dskip ~ N(0,1);
-    h0 ~ N(0,1).  Activations in bf16, the per-head vectors and the state in fp32."""
+    h0 ~ N(0,1).  Activations in io_dtype (bf16 by default), the per-head vectors and the
+    state in fp32."""
     g = _gen(device, seed)
-    bf = torch.bfloat16
+    bf = io_dtype
     x = _randn((batch, seqlen, nheads, headdim), g, device).to(bf)
     delta = F.softplus(_randn((batch, seqlen, nheads), g, device, shift=delta_shift)).to(bf)
     Bm = _randn((batch, seqlen, ngroups, dstate), g, device).to(bf)

@@ -511,7 +511,7 @@ def run_ssd(a):
 
 @pytest.mark.parametrize("field,value,status", [
     ("io_dtype", 5, ssm.SSM_ERR_BAD_DTYPE),
-    ("io_dtype", ssm.SSM_F32, ssm.SSM_ERR_UNSUPPORTED),   # bf16 only in this version
+    ("io_dtype", 5, ssm.SSM_ERR_BAD_DTYPE),
     ("batch", -1, ssm.SSM_ERR_BAD_SHAPE),
     ("nheads", 0, ssm.SSM_ERR_BAD_SHAPE),
     ("ngroups", 3, ssm.SSM_ERR_BAD_SHAPE),                 # does not divide 4 heads
@@ -531,6 +531,23 @@ def run_ssd(a):
 ])
 def test_ssd_rejects_bad_arguments(field, value, status):
     assert run_ssd(ssd_args(**{field: value})) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(Bm=addr(3, 4)), ssm.SSM_ERR_ALIGN),       # fp32 B rows are read 16 bytes at a time
+    (dict(h0=addr(9, 4)), ssm.SSM_ERR_ALIGN),
+    (dict(x=addr(0, 2)), ssm.SSM_ERR_ALIGN),
+    (dict(y=addr(0, 4)), ssm.SSM_ERR_ALIAS),         # inside x
+])
+def test_ssd_fp32_checks(kw, status):
+    assert run_ssd(ssd_args(io_dtype=ssm.SSM_F32, **kw)) == status
+
+
+def test_ssd_fp32_needs_no_workspace_and_passes_the_checks():
+    L = ssm.lib()
+    a = ssd_args(io_dtype=ssm.SSM_F32, batch=1, nheads=2, seqlen=4096, workspace=None)
+    assert L.ssm_ssd_workspace_size(ctypes.byref(a)) == 0
+    assert run_ssd(ssd_args(io_dtype=ssm.SSM_F32, x=addr(0, 4))) == ssm.SSM_ERR_HIP   # no device here
 
 
 def test_ssd_workspace_checks():

@@ -101,6 +101,63 @@ def test_ssd_head_dims(name, B, L, H, P, G, N, extra):
     assert _ssm_part_matters(y, inp) > 0.1
 
 
+F32_CASES = [
+    # name, B, L, H, P, G, N, extra
+    ("f32_n16_ragged", 2, 37, 3, 32, 1, 16, dict(h0=True)),
+    ("f32_n128_groups", 1, 201, 4, 64, 2, 128, {}),
+    ("f32_n64_l1", 3, 1, 2, 96, 1, 64, dict(h0=True)),
+    ("f32_n32_no_gate_no_skip", 2, 130, 2, 64, 1, 32, dict(gate=False, skip=False)),
+    ("f32_long_n128", 1, 3000, 2, 64, 1, 128, dict(h0=True)),
+]
+
+
+@pytest.mark.parametrize("name,B,L,H,P,G,N,extra", F32_CASES, ids=[c[0] for c in F32_CASES])
+def test_ssd_fp32_io(name, B, L, H, P, G, N, extra):
+    """fp32 I/O: the recurrent form in fp32, held to the fp32 bound 1e-4 (1 + |ref|)."""
+    print("case", name, flush=True)
+    inp = W.make_ssd_inputs(B, L, H, P, G, N, seed=840 + L + N, device=DEV,
+                            io_dtype=torch.float32, **extra)
+    y, hf = _run(inp)
+    yr, hr = _oracle(inp)
+    tol = TOL[torch.float32]
+    wy = assert_close(to64(y), yr, tol, "y")
+    wh = assert_close(to64(hf), hr, tol, "h_final")
+    print("  worst scaled error y %.2e, h_final %.2e" % (wy, wh), flush=True)
+    assert _ssm_part_matters(y, inp) > 0.1
+
+
+def test_ssd_fp32_softplus_bias_and_zero_A():
+    """A = 0 (the weight's limit dt) and a small positive A.  A positive A makes the
+    recurrence grow like exp(A sum(dt)), which amplifies every rounding by the same
+    factor; A = 0.05 over these 150 steps grows the state about e^5, so the fp32 bound
+    stays meaningful (at A = 0.3 the outputs reach 4e11 and no fp32 arithmetic holds a
+    1e-4 relative bound)."""
+    inp = W.make_ssd_inputs(2, 150, 3, 64, 1, 64, seed=851, device=DEV, io_dtype=torch.float32,
+                            h0=True)
+    g0 = torch.Generator(DEV).manual_seed(12)
+    inp["delta"] = torch.randn(inp["delta"].shape, device=DEV, generator=g0) - 1.0
+    inp["A"] = torch.tensor([0.0, -0.5, 0.05], device=DEV)
+    bias = 0.3 * torch.randn(3, device=DEV, generator=g0)
+    y, hf = _run(inp, softplus=True, bias=bias)
+    yr, hr = _oracle(inp, softplus=True, bias=bias)
+    tol = TOL[torch.float32]
+    assert_close(to64(y), yr, tol, "y")
+    assert_close(to64(hf), hr, tol, "h_final")
+
+
+def test_ssd_fp32_matches_bf16_path_on_bf16_values():
+    """The recurrent fp32 form and the chunked bf16 form compute the same map: on inputs
+    that are bf16 values, the fp32 run (rounded to bf16) agrees with the bf16 run within
+    the bf16 bound."""
+    inp = W.make_ssd_inputs(2, 300, 4, 64, 2, 128, seed=852, device=DEV, h0=True)
+    f32 = {k: (None if v is None else (v.float() if v.dtype == torch.bfloat16 else v))
+           for k, v in inp.items()}
+    y16, h16 = _run(inp)
+    y32, h32 = _run(f32)
+    assert_close(to64(y16), to64(y32), TOL_BF16, "y")
+    assert_close(to64(h16), to64(h32), TOL_BF16, "h_final")
+
+
 def test_ssd_softplus_bias_zero_and_positive_A():
     inp = W.make_ssd_inputs(1, 150, 4, 64, 1, 64, seed=851, device=DEV)
     g = torch.Generator(DEV).manual_seed(9)
