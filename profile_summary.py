@@ -15,6 +15,10 @@
         --algorithmic-bytes N --commands "cmd1" "cmd2" "cmd3" "cmd4" \\
         [--sources scan_fwd.hip ...] --out-json profiles/hbm_counters.json --out profiles/NAME.md
 
+    # per (kernel, grid, workgroup) durations of a --kernel-trace run
+    python profile_summary.py dispatches --csv OUT_kernel_trace.csv [--match SUBSTRING ...] \\
+        --title "..." --command "rocprofv3 ..." --out profiles/NAME.md
+
     # instruction and wait counters (SQ block) of one kernel, with per-update figures
     python profile_summary.py sq --csv A_counter_collection.csv [B_...csv] \\
         --kernel SUBSTRING --updates N --duration-us T --title "..." \\
@@ -121,6 +125,27 @@ def cmd_counters(a):
     _write(a.out, "\n".join(lines) + "\n")
 
 
+def cmd_dispatches(a):
+    """Per (kernel, grid, workgroup) durations from a --kernel-trace CSV: launches of one
+    kernel instance with different shapes (different workloads) are kept apart."""
+    import collections
+    groups = collections.OrderedDict()
+    for r in _rows(a.csv):
+        if a.match and not any(m in r["Kernel_Name"] for m in a.match):
+            continue
+        key = (r["Kernel_Name"], r.get("Grid_Size_X", ""), r.get("Workgroup_Size_X", ""))
+        groups.setdefault(key, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    lines = ["# %s" % a.title, "", "Command (from the repository root):", "", "```", a.command, "```", "",
+             "| kernel | grid (work-items) | workgroup | launches | median us | mean us | min us | max us |",
+             "|---|---:|---:|---:|---:|---:|---:|---:|"]
+    for (name, grid, wg), v in groups.items():
+        lines.append("| `%s` | %s | %s | %d | %.2f | %.2f | %.2f | %.2f |" % (
+            _short(name, 90), grid, wg, len(v), statistics.median(v), sum(v) / len(v), min(v), max(v)))
+    if a.note:
+        lines += ["", a.note]
+    _write(a.out, "\n".join(lines) + "\n")
+
+
 SQ_NOTES = {
     "SQ_WAVES": "waves launched",
     "SQ_INSTS_VALU": "vector ALU instructions issued (per wave, all kinds)",
@@ -216,8 +241,15 @@ def main(argv=None):
     q.add_argument("--title", required=True)
     q.add_argument("--commands", nargs="+", required=True)
     q.add_argument("--out", required=True)
+    dd = sub.add_parser("dispatches")
+    dd.add_argument("--csv", required=True, help="the kernel_trace.csv of a --kernel-trace run")
+    dd.add_argument("--match", nargs="*", default=None, help="kernel name substrings to keep")
+    dd.add_argument("--title", required=True)
+    dd.add_argument("--command", required=True)
+    dd.add_argument("--note", default="")
+    dd.add_argument("--out", required=True)
     a = ap.parse_args(argv)
-    {"stats": cmd_stats, "counters": cmd_counters, "sq": cmd_sq}[a.cmd](a)
+    {"stats": cmd_stats, "counters": cmd_counters, "sq": cmd_sq, "dispatches": cmd_dispatches}[a.cmd](a)
 
 
 if __name__ == "__main__":
