@@ -26,27 +26,28 @@
 //     channel and computes u (conv prologue, its 3-step history from the
 //     neighbouring lanes through DPP shifts) and dt there, once per
 //     (t, channel);
-//   * the recurrence of step k reads dt and u of step k from lane k of the
-//     row through a DPP row broadcast folded into the multiply;
-//   * the B and C rows (shared by all channels) reach every row of the wave
-//     through the matrix cores: one MFMA with a 0/1 selector matrix copies
-//     4 steps x 16 entries of B (or C) into 4 registers of every lane,
-//     exactly (bf16 -> fp32 for free), keeping the broadcast off the vector
-//     ALU;
-//   * each lane's 16 partial read-outs C_{t,n} h_{t,n} are transposed
-//     through LDS, so lane (c, j) sums the 16 partials of step t0 + j and
+//   * three products of the step loop run on the matrix cores, 4 steps
+//     x 16 entries x 4 channels per MFMA: dt A (a 4x4x1 MFMA whose A-block
+//     broadcast hands every lane of a row the dt of steps 4g..4g+3), u B
+//     (bf16 I/O without the conv prologue: a 4x4x4 bf16 MFMA on the raw u
+//     and B, exact), and the read-out weights C x (x = 1/A in the fast form,
+//     1 otherwise; see WSel).  Otherwise B reaches every row through a 0/1
+//     selector MFMA and u B is a vector product with u of step k read from
+//     lane k of the row through a DPP row broadcast;
+//   * each lane's 16 states h_{t,n} are transposed through LDS, so lane
+//     (c, j) sums the 16 states of step t0 + j times their weights and
 //     applies the skip and the gate; y goes out through LDS with coalesced
 //     16-byte stores.
 // The block loop is software-pipelined: loads run four blocks ahead through
 // a three-slot LDS ring, a block's read-outs are summed and its y stored
-// during the next block, and the B/C broadcasts run one step group ahead.
+// during the next block, and the MFMAs run one step group ahead.
 //
 // Vector-ALU cost per state update (the binding resource): one exp (two
-// issue slots on gfx950) and five fp32 ops in the fast form, which carries
-// g = A h:
-//   zz = dt*A*log2e; e = 2^zz; bu = B*u; bx = e*bu - bu (fused);
-//   g = e*g + bx (fused); p = C*g   (and C h = p / A in the read-out).
+// issue slots on gfx950) and two fused fp32 ops in the fast form, which
+// carries g = A h, plus one fused op of the read-out sum:
+//   e = 2^(dt A log2e); bx = e*bu - bu; g = e*g + bx; y += g * w.
 // bx = fma(e, bu, -bu) makes dt = 0 hold the state exactly (e = 1 gives 0).
+// With the conv prologue, or fp32 I/O, bu = u*B adds one more.
 //
 // Accuracy: e - 1 inherits the absolute rounding error of e (~1e-7), so the
 // fast form errs by ~1e-7 |B u / A| per step.  Waves in which some
@@ -233,13 +234,19 @@ __device__ __host__ constexpr int row_dwords(int W) {
 }
 template <typename IO>
 constexpr uint32_t kPlane = (uint32_t)kTB * 4u * row_dwords<IO>(kMaxW);
-// Staged B (or C) tile of one block.  bf16 is entry-major with rows of 20
-// elements (40 bytes = 10 dwords): the 16 lanes that read one 8-byte piece
-// each (the same steps of the 16 entries) then hit 16 distinct bank pairs.
-// fp32 is step-major ([16 steps][16 entries]).
+// Staged B and C tiles of one block (B first, then C, in each ring slot).
+// bf16 B is entry-major with rows of 20 elements (40 bytes = 10 dwords): the
+// 16 lanes that read one 8-byte piece each (the same steps of the 16
+// entries) then hit 16 distinct bank pairs.  bf16 C is step-major with rows
+// of 24 elements (48 bytes = 12 dwords): the lanes that read one 16-byte
+// piece each (the same entries of 8 steps) then hit 32 distinct banks.
+// fp32 B and C are step-major ([16 steps][16 entries]).
 constexpr uint32_t kBcRowBytes = 40;
+constexpr uint32_t kCRowBytes = 48;
 template <typename IO>
-constexpr uint32_t kBcTile = sizeof(typename IO::storage) == 2 ? kRow * kBcRowBytes : kTB * kRow * 4;
+constexpr uint32_t kBTile = sizeof(typename IO::storage) == 2 ? kRow * kBcRowBytes : kTB * kRow * 4;
+template <typename IO>
+constexpr uint32_t kCTile = sizeof(typename IO::storage) == 2 ? kTB * kCRowBytes : kTB * kRow * 4;
 
 struct Tiles {
     int CH;
@@ -255,7 +262,7 @@ __device__ __host__ __forceinline__ Tiles tile_layout(int W) {
     t.CH = 4 * W;
     t.rs = 4u * (uint32_t)row_dwords<IO>(W);
     t.own_slot = 3 * kPlane<IO>;
-    t.bc_slot = 2 * kBcTile<IO>;
+    t.bc_slot = kBTile<IO> + kCTile<IO>;
     t.ybuf_slot = kTB * t.rs;
     t.own = 0;
     t.bc = t.own + kSlots * t.own_slot;
@@ -295,6 +302,7 @@ struct Duty {
     uint32_t goff;      // the thread's chunk within a block, or kOOB
     uint32_t lds;       // LDS offset of the chunk within a slot of the own or bc area
     int to_bc;          // the duty fills the bc area (uniform)
+    int scatter;        // bf16 B rows: the chunk is written entry-major (uniform)
     int ystore;         // the wave stores y chunks (uniform)
     uint32_t ylds;      // ybuf offset of the thread's y chunk
 };
@@ -320,6 +328,7 @@ __device__ __forceinline__ Duty make_duty(const ScanKernelParams &p, const Span 
     const int role = wave < 3 * a ? wave / a : 3 + (wave - 3 * a);  // uniform
     Duty d;
     d.to_bc = __builtin_amdgcn_readfirstlane(role == 3 || role == 4 ? 1 : 0);
+    d.scatter = __builtin_amdgcn_readfirstlane(es == 2 && role == 3 ? 1 : 0);
     d.ystore = __builtin_amdgcn_readfirstlane(role == 0 ? 1 : 0);
     d.goff = kOOB;
     d.lds = 0;
@@ -346,10 +355,11 @@ __device__ __forceinline__ Duty make_duty(const ScanKernelParams &p, const Span 
         d.step = (uint32_t)(kTB * N * es);
         if (role <= 4 && lane * 16 < kTB * kRow * es) {
             d.goff = (uint32_t)(lane * 16);
-            // bf16: the chunk is entries 8 (lane % 2) .. +7 of step lane / 2,
-            // stored entry-major (see stage_block)
-            d.lds = (uint32_t)(role - 3) * kBcTile<IO> +
-                    (es == 2 ? (uint32_t)(8 * (lane % 2) * kBcRowBytes + (lane / 2) * es) : (uint32_t)(lane * 16));
+            // bf16: the chunk is entries 8 (lane % 2) .. +7 of step lane / 2;
+            // B stores it entry-major (see stage_block), C into its step row
+            if (es != 2) d.lds = (role == 3 ? 0u : kBTile<IO>) + (uint32_t)(lane * 16);
+            else if (role == 3) d.lds = (uint32_t)(8 * (lane % 2) * kBcRowBytes + (lane / 2) * es);
+            else d.lds = kBTile<IO> + (uint32_t)((lane / 2) * kCRowBytes + 16 * (lane % 2));
         }
     }
     d.grec = __builtin_amdgcn_readfirstlane(d.grec);
@@ -431,7 +441,7 @@ __device__ __forceinline__ void stage_block(const Geo &g, const Duty &d, const T
         // channels past D are never stored, so their staged values do not matter.
         char *base = lds + (d.to_bc ? T.bc + slot * T.bc_slot : T.own + slot * T.own_slot);
         if (d.goff != kOOB) {
-            if (es == 2 && d.to_bc) {
+            if (es == 2 && d.scatter) {
                 // bf16 B/C rows go in entry-major: 8 entries of one step, a
                 // column of the [n][t] tile.
                 char *dst = base + d.lds;
@@ -446,7 +456,7 @@ __device__ __forceinline__ void stage_block(const Geo &g, const Duty &d, const T
     } else {
         char *own = lds + T.own + slot * T.own_slot;
         char *bc = lds + T.bc + slot * T.bc_slot;
-        char *cc = bc + kBcTile<IO>;
+        char *cc = bc + kBTile<IO>;
         const int row = tid / T.CH, ci = tid % T.CH;
         char *dst = own + row * T.rs + ci * es;
 #pragma unroll
@@ -460,8 +470,9 @@ __device__ __forceinline__ void stage_block(const Geo &g, const Duty &d, const T
             if (e < kTB * kRow) {
                 if constexpr (es == 2) {
                     const int te = (e % kRow) * kBcRowBytes + (e / kRow) * es;  // entry-major
+                    const int tc = (e / kRow) * kCRowBytes + (e % kRow) * es;   // step-major
                     *reinterpret_cast<uint16_t *>(bc + te) = (uint16_t)f.bce[i];
-                    *reinterpret_cast<uint16_t *>(cc + te) = (uint16_t)f.bce[4 + i];
+                    *reinterpret_cast<uint16_t *>(cc + tc) = (uint16_t)f.bce[4 + i];
                 } else {
                     *reinterpret_cast<uint32_t *>(bc + e * es) = f.bce[i];
                     *reinterpret_cast<uint32_t *>(cc + e * es) = f.bce[4 + i];
@@ -522,10 +533,51 @@ __device__ __forceinline__ void store_y(const ScanKernelParams &p, const Geo &g,
     }
 }
 
-// MFMA data operands of one block's B (or C) rows held by a lane.
-//  bf16: the B operand of the whole block, staged entry-major ([n][t]):
-//        steps 4*(lane/16) .. +3 of entry lane%16 (each value read once);
-//  fp32: per step group g, row 4g + lane/16, entry lane%16 (B operand).
+// Three products of the step loop run on the matrix cores.
+//
+// dt A log2(e) of steps 4g..4g+3 (dta): the 4x4x1 MFMA multiplies, per block
+// of 4 lanes, a 4-vector by a 4-vector.  Lane (c, n) gives its own A log2(e)
+// as the B operand; the A operand of every 4-lane block of a wave row is
+// broadcast from the row's block g (CBSZ 2, ABID g), that is from lanes
+// (c, 4g..4g+3), which hold dt of steps 4g..4g+3.  Register r of lane (c, n)
+// then holds dt_{4g+r} A_n log2(e), rounded once as on the vector ALU.
+template <int G>
+__device__ __forceinline__ mfma_f32x4 dta_group(float dt, float a2) {
+    const mfma_f32x4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
+    return __builtin_amdgcn_mfma_f32_4x4x1f32(dt, a2, zero, 2, G, 0);
+}
+
+// u B of steps 4g..4g+3, where u is a bf16 input (bf16 I/O without the conv
+// prologue: u is x itself).  4x4x4 bf16 MFMA, again with the A operand
+// broadcast from the row's block g: lane (c, t) gives its u at position t % 4
+// of four (zeros elsewhere, udiag), so that block's A is the diagonal of
+// u_{4g..4g+3}; lane (c, n) gives steps 4g..4g+3 of B's entry n as the B
+// operand.  Register r of lane (c, n) holds u_{4g+r} B_{4g+r,n}: one exact
+// product of two bf16 values.
+// (The element path, which holds more registers per block, keeps the
+// broadcast below.)
+template <typename IO, bool CONV, bool VEC>
+constexpr bool kBuMfma = std::is_same<IO, io_bf16>::value && !CONV && VEC;
+
+__device__ __forceinline__ uint2 make_udiag(float u, uint32_t m0, uint32_t m1) {
+    const uint32_t b = __builtin_bit_cast(uint32_t, u);  // a widened bf16: low half is 0
+    const uint32_t two = b | (b >> 16);
+    return make_uint2(two & m0, two & m1);
+}
+template <int G>
+__device__ __forceinline__ mfma_f32x4 bu_group(uint2 udiag, uint2 bsteps) {
+    const mfma_f32x4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
+    return __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(__builtin_bit_cast(mfma_bf16x4, udiag),
+                                                  __builtin_bit_cast(mfma_bf16x4, bsteps), zero, 2, G, 0);
+}
+
+// Otherwise (conv prologue, or fp32 I/O) B reaches every wave row through a
+// 0/1 selector MFMA and u B is a vector-ALU product.  Operands of one block's
+// B rows held by a lane:
+//  bf16 broadcast: staged entry-major ([n][t]), steps 4*(lane/16) .. +3 of
+//        entry lane%16 (each value read once);
+//  bf16 u B MFMA: steps 4g .. 4g+3 of entry lane%16, for g = 0..3;
+//  fp32: per step group g, row 4g + lane/16, entry lane%16.
 template <typename IO>
 struct BcBlock;
 template <>
@@ -536,15 +588,27 @@ template <>
 struct BcBlock<io_f32> {
     float v[4];
 };
-template <typename IO>
-__device__ __forceinline__ BcBlock<IO> load_bc_block(const char *rows, int lane) {
-    BcBlock<IO> o;
-    if constexpr (std::is_same<IO, io_bf16>::value) {
-        o.v = *reinterpret_cast<const uint2 *>(rows + (lane & 15) * kBcRowBytes + 8 * (lane >> 4));
+template <typename IO, bool MF>
+struct BOp {
+    BcBlock<IO> v;
+};
+template <>
+struct BOp<io_bf16, true> {
+    uint2 g[4];
+};
+template <typename IO, bool MF>
+__device__ __forceinline__ BOp<IO, MF> load_bop(const char *rows, int lane) {
+    BOp<IO, MF> o;
+    if constexpr (MF) {
+        const char *r = rows + (lane & 15) * kBcRowBytes;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) o.g[g] = *reinterpret_cast<const uint2 *>(r + 8 * g);
+    } else if constexpr (std::is_same<IO, io_bf16>::value) {
+        o.v.v = *reinterpret_cast<const uint2 *>(rows + (lane & 15) * kBcRowBytes + 8 * (lane >> 4));
     } else {
 #pragma unroll
         for (int g = 0; g < 4; ++g)
-            o.v[g] = *reinterpret_cast<const float *>(rows + ((4 * g + (lane >> 4)) * kRow + (lane & 15)) * 4);
+            o.v.v[g] = *reinterpret_cast<const float *>(rows + ((4 * g + (lane >> 4)) * kRow + (lane & 15)) * 4);
     }
     return o;
 }
@@ -560,37 +624,122 @@ __device__ __forceinline__ mfma_f32x4 bcast(const BcBlock<IO> &op, const BcastSe
         return __builtin_amdgcn_mfma_f32_16x16x4f32(sel.f, op.v[g], zero, 0, 0, 0);
 }
 
+// Read-out weights.  After the transpose, lane (c, t) sums over the entries
+// n of its channel the states of step t times w_n = C_{t,n} x_n, where x_n is
+// 1/A_n in the fast form (which carries g = A h) and 1 otherwise.  The
+// weights come from four MFMAs per block, one per entry group q; register r
+// of group q holds w for entry 4q + r:
+//  bf16 (16x16x16): D[4c + r][t] = sum_k X[4c + r][k] Y[k][t] with
+//     Y[4s + i][t] = C_{t,4q+i} for every K block s (each lane reads entries
+//     4q..4q+3 of its step row t), and X[4c + r][4s + i] = part s of x_{c,4q+r}
+//     when i == r and s < 3, 0 otherwise.  x is cut into three bf16 parts
+//     (hi, mid, lo: each the leading 8 bits of what the previous parts left),
+//     which add up to x exactly, so each product is exact and w is x C
+//     rounded in the MFMA's fp32 sums;
+//  fp32 (16x16x4): Y[k][t] = C_{t,4q+k}, X[4c + r][k] = x_{c,4q+r} when k == r.
+// X is constant per wave (WSel).
+template <typename IO>
+struct WSel;
+template <>
+struct WSel<io_bf16> {
+    mfma_bf16x4 q[4];
+};
+template <>
+struct WSel<io_f32> {
+    float q[4];
+};
+template <typename IO>
+struct COp;
+template <>
+struct COp<io_bf16> {
+    uint4 v[2];  // entries 0..15 of step lane % 16
+};
+template <>
+struct COp<io_f32> {
+    float v[4];  // entry 4q + lane / 16 of step lane % 16, q = 0..3
+};
+
+// x of (channel cw0 + (lane % 16) / 4, entry 4q + lane % 4), the entry a lane
+// gives to the A operand of the weight MFMAs.
+template <bool FAST>
+__device__ __forceinline__ float weight_x(const ScanKernelParams &p, int64_t cw0, int lane, int q) {
+    const int64_t dd = cw0 + (lane & 15) / 4;
+    const int e = 4 * q + (lane & 3);
+    if (dd >= p.D || e >= p.N) return 0.0f;
+    if (!FAST) return 1.0f;
+    const float a = p.A[dd * p.N + e];
+    return a != 0.0f ? 1.0f / a : 0.0f;
+}
+__device__ __forceinline__ uint32_t lead8(float v) {  // leading 8 significant bits of v
+    return __builtin_bit_cast(uint32_t, v) & 0xFFFF0000u;
+}
+template <typename IO, bool FAST>
+__device__ __forceinline__ WSel<IO> make_wsel(const ScanKernelParams &p, int64_t cw0, int lane) {
+    WSel<IO> w;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const float x = weight_x<FAST>(p, cw0, lane, q);
+        if constexpr (std::is_same<IO, io_bf16>::value) {
+            const uint32_t hi = lead8(x);
+            const float r1 = x - __builtin_bit_cast(float, hi);
+            const uint32_t mid = lead8(r1);
+            const uint32_t lo = lead8(r1 - __builtin_bit_cast(float, mid));
+            const int s = lane >> 4;
+            const uint32_t part = s == 0 ? hi : s == 1 ? mid : s == 2 ? lo : 0u;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) w.q[q][i] = i == (lane & 3) ? (short)(part >> 16) : (short)0;
+        } else {
+            w.q[q] = (lane >> 4) == (lane & 3) ? x : 0.0f;
+        }
+    }
+    return w;
+}
+template <typename IO>
+__device__ __forceinline__ COp<IO> load_cop(const char *ctile, int lane) {
+    COp<IO> o;
+    if constexpr (std::is_same<IO, io_bf16>::value) {
+        const char *r = ctile + (lane & 15) * kCRowBytes;
+        o.v[0] = *reinterpret_cast<const uint4 *>(r);
+        o.v[1] = *reinterpret_cast<const uint4 *>(r + 16);
+    } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            o.v[q] = *reinterpret_cast<const float *>(ctile + ((lane & 15) * kRow + 4 * q + (lane >> 4)) * 4);
+    }
+    return o;
+}
+template <typename IO, int Q>
+__device__ __forceinline__ mfma_f32x4 weight_group(const WSel<IO> &ws, const COp<IO> &co) {
+    const mfma_f32x4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
+    if constexpr (std::is_same<IO, io_bf16>::value) {
+        const uint4 v = co.v[Q / 2];
+        const uint2 y = Q % 2 == 0 ? make_uint2(v.x, v.y) : make_uint2(v.z, v.w);
+        return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ws.q[Q], __builtin_bit_cast(mfma_bf16x4, y), zero, 0,
+                                                         0, 0);
+    } else {
+        return __builtin_amdgcn_mfma_f32_16x16x4f32(ws.q[Q], co.v[Q], zero, 0, 0, 0);
+    }
+}
+
 struct LaneConst {
     float a, a2, ia, dsk, dbias, cb, wp0, wp1, wp2, wp3;
     bool live;  // the lane holds a real (channel, entry)
 };
 
-// Read-out of one step: the sum over the 16 state entries of the partials
-// C g that the lanes of this row transposed into prow (load_partials reads
-// them, sum_partials adds them).  The fast form keeps g = A h, so each
-// partial is first multiplied by 1/A of its entry (ia, the channel's 16
-// values, held in registers by every lane of the row).
+// Read-out of one step: lane (c, t) reads the 16 states of step t that the
+// lanes of its row transposed into prow, and sums them times the weights.
 __device__ __forceinline__ void load_partials(const float *prow, int n, float (&part)[kRow]) {
 #pragma unroll
     for (int i = 0; i < kRow; ++i) part[i] = prow[i * kPStride + n];
 }
-template <bool FAST>
-__device__ __forceinline__ float sum_partials(float (&part)[kRow], const float (&ia)[kRow]) {
-    if (FAST) {
-        float s0 = part[0] * ia[0], s1 = part[1] * ia[1];
+__device__ __forceinline__ float sum_partials(const float (&part)[kRow], const mfma_f32x4 (&w)[4]) {
+    float s0 = part[0] * w[0][0], s1 = part[1] * w[0][1];
 #pragma unroll
-        for (int i = 2; i < kRow; i += 2) {
-            s0 = __builtin_fmaf(part[i], ia[i], s0);
-            s1 = __builtin_fmaf(part[i + 1], ia[i + 1], s1);
-        }
-        return s0 + s1;
-    } else {
-#pragma unroll
-        for (int w = kRow / 2; w >= 1; w /= 2)
-#pragma unroll
-            for (int i = 0; i < w; ++i) part[i] += part[i + w];
-        return part[0];
+    for (int i = 2; i < kRow; i += 2) {
+        s0 = __builtin_fmaf(part[i], w[i / 4][i % 4], s0);
+        s1 = __builtin_fmaf(part[i + 1], w[i / 4][(i + 1) % 4], s1);
     }
+    return s0 + s1;
 }
 
 // Per-lane values carried from one block to the next.
@@ -636,18 +785,44 @@ __device__ __forceinline__ void read_own(const Tiles &T, const char *lds, int sl
     }
 }
 
+// Workgroup barrier of the wide block loop.  Every LDS operation that other
+// waves depend on (the staging and ybuf writes, and the reads of a ring slot
+// that a later block overwrites) has completed before it; only the wave's
+// last SSM_PART_READ_OPS LDS instructions, the read-back of its own states (a
+// wave-private area, reused only by this wave's next block), may still be in
+// flight.  LDS instructions of one wave complete in order, so waiting until
+// at most that many are outstanding covers all the earlier ones.  The
+// read-back is at least SSM_PART_READ_OPS instructions (16 values, read at most
+// two per instruction), and no LDS or scalar-memory instruction is issued
+// between it and this barrier.
+#define SSM_PART_READ_OPS 6
+#define SSM_STR_(x) #x
+#define SSM_STR(x) SSM_STR_(x)
+__device__ __forceinline__ void wave_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(" SSM_STR(SSM_PART_READ_OPS) ")\n\ts_barrier" ::: "memory");
+}
+
+// Per-wave constants of the matrix-core products.
+template <typename IO>
+struct WaveOps {
+    BcastSel sel;      // 0/1 selectors of the B broadcast
+    WSel<IO> ws;       // read-out weight factors
+    uint32_t um0, um1; // udiag masks: the half of the 4 x bf16 A operand that holds u
+};
+
 // One 16-step block of one wave, software-pipelined across blocks:
 //   * right after the workgroup barrier, the LDS reads whose results are
-//     needed later are issued: the next block's own inputs and B/C tiles
+//     needed later are issued: the next block's own inputs and B tile
 //     (staged before this barrier) and the outputs two blocks back;
 //   * the previous block's outputs are finished from its read-out sum, which
 //     that block left in registers, so nothing after the barrier waits for
 //     LDS before the step loop;
-//   * the 16 recurrence steps run on this block's B/C tiles, read one block
-//     earlier; their partial read-outs are transposed through the wave's own
-//     LDS area and read back at once;
+//   * the 16 recurrence steps run on this block's B tile, read one block
+//     earlier; their states are transposed through the wave's own LDS area
+//     and read back at once, with this block's C rows;
 //   * block j+2 is copied from registers into LDS, block j+4 is requested
-//     from global memory, and then the partial read-outs are summed.
+//     from global memory, the read-out weights are formed and the states
+//     are summed.
 // PAR = j % 2 selects the ybuf halves; SLOT = j % 3 when it is known at
 // compile time; TAIL masks steps past the sequence end; STAGE is off in the
 // last block.
@@ -655,10 +830,10 @@ template <typename IO, bool CONV, bool VEC, bool FAST, bool STATS, bool TAIL, in
           int SLOT = -1>
 __device__ __forceinline__ void block_iter(const ScanKernelParams &p, const Span &sp, const Geo &geo,
                                            const Tiles &T, char *lds, int wave, int c, int n,
-                                           int lane, const BcastSel &sel, const LaneConst &k,
-                                           const float (&iat)[kRow], const Duty &du, int j, int s_run,
-                                           Fetch<VEC> &f, BcBlock<IO> &bop, BcBlock<IO> &cop,
-                                           Carry &cy) {
+                                           int lane, const WaveOps<IO> &ops, const LaneConst &k,
+                                           const Duty &du, int j, int s_run, Fetch<VEC> &f,
+                                           BOp<IO, kBuMfma<IO, CONV, VEC>> &bop, Carry &cy) {
+    constexpr bool MF = kBuMfma<IO, CONV, VEC>;
     constexpr int es = sizeof(typename IO::storage);
     const int tid = threadIdx.x, nthreads = blockDim.x;
     const int ci = 4 * wave + c;
@@ -669,14 +844,13 @@ __device__ __forceinline__ void block_iter(const ScanKernelParams &p, const Span
     const int s_stage = s_next == kSlots - 1 ? 0 : s_next + 1;
     float *prow = reinterpret_cast<float *>(lds + T.part) + (wave * kChPerWave + c) * kPRow;
 
-    __syncthreads();
+    if constexpr (VEC) wave_barrier();
+    else __syncthreads();
     // -- LDS reads of later blocks first ------------------------------------------
     float own_next[3];
     read_own<IO>(T, lds, s_next, n, ci, own_next);
     const YChunk<VEC> yst = read_ybuf<IO, VEC>(du, T, lds, PAR, tid);
-    const char *brows_n = lds + T.bc + s_next * T.bc_slot;
-    const BcBlock<IO> bop_n = load_bc_block<IO>(brows_n, lane);
-    const BcBlock<IO> cop_n = load_bc_block<IO>(brows_n + kBcTile<IO>, lane);
+    const BOp<IO, MF> bop_n = load_bop<IO, MF>(lds + T.bc + s_next * T.bc_slot, lane);
 
     // -- this block's inputs ---------------------------------------------------
     const float xv = cy.own[0];
@@ -719,58 +893,79 @@ __device__ __forceinline__ void block_iter(const ScanKernelParams &p, const Span
     if (j >= 2 && (!VEC || du.ystore)) store_y<IO, VEC>(p, geo, du, yst, j - 2, tid);
 
     // -- the 16 steps ----------------------------------------------------------
-    // Steps in groups of four: one broadcast MFMA each for B and C per
-    // group, issued one group ahead so the matrix cores' latency is hidden,
-    // and one 128-bit LDS write of the group's four partial read-outs.
-    mfma_f32x4 Bn = bcast<IO>(bop, sel, 0), Cn = bcast<IO>(cop, sel, 0);
+    // Steps in groups of four: the group's dt A and u B (or B) come from
+    // MFMAs issued one group ahead, so the matrix cores' latency is hidden,
+    // and the group's four states leave with one 128-bit LDS write.
+    uint2 ud = make_uint2(0u, 0u);
+    if constexpr (MF) ud = make_udiag(u, ops.um0, ops.um1);
+    auto bu_of = [&](auto G) -> mfma_f32x4 {
+        constexpr int g = decltype(G)::value;
+        if constexpr (MF) return bu_group<g>(ud, bop.g[g]);
+        else return bcast<IO>(bop.v, ops.sel, g);
+    };
+    mfma_f32x4 Zn = dta_group<0>(dt, k.a2), Bn = bu_of(ic<0>{});
     static_for<kTB / 4>([&](auto G) {
         constexpr int gi = decltype(G)::value;
         constexpr int g4 = 4 * gi;
-        const mfma_f32x4 Bk = Bn, Ck = Cn;
+        const mfma_f32x4 Zk = Zn, Bk = Bn;
         if constexpr (gi + 1 < kTB / 4) {
-            Bn = bcast<IO>(bop, sel, gi + 1);
-            Cn = bcast<IO>(cop, sel, gi + 1);
+            Zn = dta_group<gi + 1>(dt, k.a2);
+            Bn = bu_of(ic<gi + 1>{});
         }
         float pk[4];
         static_for<4>([&](auto K) {
             constexpr int kk = decltype(K)::value;
             constexpr int kx = g4 + kk;
-            const float dtk = row_bcast<kx>(dt);
-            const float uk = row_bcast<kx>(u);
-            const float e = hw_exp2(dtk * k.a2);
-            const float bu = uk * Bk[kk];
+            const float e = hw_exp2(Zk[kk]);
+            float bu;
+            if constexpr (MF) bu = Bk[kk];
+            else bu = row_bcast<kx>(u) * Bk[kk];
             float bx;
             if (FAST) {
                 bx = __builtin_fmaf(e, bu, -bu);  // h holds A h here
             } else {
+                const float dtk = row_bcast<kx>(dt);
                 bx = (dtk * phi_of(dtk * k.a, e)) * bu;
             }
             cy.h = __builtin_fmaf(e, cy.h, bx);
-            pk[kk] = Ck[kk] * cy.h;
+            pk[kk] = cy.h;
         });
         *reinterpret_cast<float4 *>(&prow[n * kPStride + g4]) = make_float4(pk[0], pk[1], pk[2], pk[3]);
     });
-    // The partials are this wave's own: read them back at once (LDS operations
-    // of one wave complete in order), sum them after the staging below.
+    // The states are this wave's own: they are read back (LDS operations of
+    // one wave complete in order) after this block's C rows and the staging
+    // writes, so that the reads may still be in flight at the next barrier
+    // (wide path; see wave_barrier).  The element path reads C after
+    // staging (its fetch registers are live until then).
     float part[kRow];
-    load_partials(prow, n, part);
+    COp<IO> cop;
+    if constexpr (VEC) cop = load_cop<IO>(lds + T.bc + s_cur * T.bc_slot + kBTile<IO>, lane);
+    else load_partials(prow, n, part);
 
     cy.u_prev = u;
     cy.z_prev = zv;
 #pragma unroll
     for (int i = 0; i < 3; ++i) cy.own[i] = own_next[i];
     bop = bop_n;
-    cop = cop_n;
 
     if (STAGE) {
         __builtin_amdgcn_sched_barrier(0);
         stage_block<IO, VEC>(geo, du, T, lds, s_stage, tid, nthreads, f);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    if constexpr (VEC) {
+        load_partials(prow, n, part);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    if (STAGE) {
         // Keep the refill after the copy, so the new data can land in the
         // same registers.
-        __builtin_amdgcn_sched_barrier(0);
         fetch_block<IO, VEC>(geo, du, j + 4, tid, nthreads, f);
     }
-    cy.acc = sum_partials<FAST>(part, iat);
+    if constexpr (!VEC) cop = load_cop<IO>(lds + T.bc + s_cur * T.bc_slot + kBTile<IO>, lane);
+    const mfma_f32x4 w[4] = {weight_group<IO, 0>(ops.ws, cop), weight_group<IO, 1>(ops.ws, cop),
+                             weight_group<IO, 2>(ops.ws, cop), weight_group<IO, 3>(ops.ws, cop)};
+    cy.acc = sum_partials(part, w);
 }
 
 template <typename IO, bool CONV, bool VEC, bool FAST, bool STATS>
@@ -780,7 +975,11 @@ __device__ __forceinline__ void scan_tiles_body(const ScanKernelParams &p, const
     const int tid = threadIdx.x, nthreads = blockDim.x;
     const int lane = tid & 63;
     const int ci = 4 * wave + c;
-    const BcastSel sel = make_sel(lane);
+    WaveOps<IO> ops;
+    ops.sel = make_sel(lane);
+    ops.ws = make_wsel<IO, FAST>(p, geo.d0 + 4 * wave, lane);
+    ops.um0 = (n & 3) == 0 ? 0x0000FFFFu : (n & 3) == 1 ? 0xFFFF0000u : 0u;
+    ops.um1 = (n & 3) == 2 ? 0x0000FFFFu : (n & 3) == 3 ? 0xFFFF0000u : 0u;
     const int64_t rows = sp.t1 - sp.t0;
     const int nblocks = (int)((rows + kTB - 1) / kTB);
 
@@ -802,21 +1001,7 @@ __device__ __forceinline__ void scan_tiles_body(const ScanKernelParams &p, const
     fetch_block<IO, VEC>(geo, du, 3, tid, nthreads, fb);
     __syncthreads();
     read_own<IO>(T, lds, 0, n, ci, cy.own);
-    BcBlock<IO> bop = load_bc_block<IO>(lds + T.bc, lane);
-    BcBlock<IO> cop = load_bc_block<IO>(lds + T.bc + kBcTile<IO>, lane);
-    // 1/A of the channel's 16 entries (the fast form's read-out weights).
-    float iat[kRow];
-    {
-        const float *src = reinterpret_cast<const float *>(lds + T.part) + (wave * kChPerWave + c) * kPRow + kRow * kPStride;
-#pragma unroll
-        for (int i = 0; i < kRow; i += 4) {
-            const float4 v = FAST ? *reinterpret_cast<const float4 *>(src + i) : make_float4(0.f, 0.f, 0.f, 0.f);
-            iat[i] = v.x;
-            iat[i + 1] = v.y;
-            iat[i + 2] = v.z;
-            iat[i + 3] = v.w;
-        }
-    }
+    BOp<IO, kBuMfma<IO, CONV, VEC>> bop = load_bop<IO, kBuMfma<IO, CONV, VEC>>(lds + T.bc, lane);
     cy.u_prev = 0.0f;
     cy.z_prev = 0.0f;
     cy.acc = 0.0f;
@@ -828,42 +1013,42 @@ __device__ __forceinline__ void scan_tiles_body(const ScanKernelParams &p, const
     // computed per block.  The element path holds more registers per block and
     // keeps the two-block loop.
     if constexpr (VEC) for (; j + 6 < nblocks; j += 6) {
-        block_iter<IO, CONV, VEC, FAST, STATS, false, 0, true, 0>(p, sp, geo, T, lds, wave, c, n, lane, sel,
-                                                                k, iat, du, j, 0, fa, bop, cop, cy);
-        block_iter<IO, CONV, VEC, FAST, STATS, false, 1, true, 1>(p, sp, geo, T, lds, wave, c, n, lane, sel,
-                                                                k, iat, du, j + 1, 0, fb, bop, cop, cy);
-        block_iter<IO, CONV, VEC, FAST, STATS, false, 0, true, 2>(p, sp, geo, T, lds, wave, c, n, lane, sel,
-                                                                k, iat, du, j + 2, 0, fa, bop, cop, cy);
-        block_iter<IO, CONV, VEC, FAST, STATS, false, 1, true, 0>(p, sp, geo, T, lds, wave, c, n, lane, sel,
-                                                                k, iat, du, j + 3, 0, fb, bop, cop, cy);
-        block_iter<IO, CONV, VEC, FAST, STATS, false, 0, true, 1>(p, sp, geo, T, lds, wave, c, n, lane, sel,
-                                                                k, iat, du, j + 4, 0, fa, bop, cop, cy);
-        block_iter<IO, CONV, VEC, FAST, STATS, false, 1, true, 2>(p, sp, geo, T, lds, wave, c, n, lane, sel,
-                                                                k, iat, du, j + 5, 0, fb, bop, cop, cy);
+        block_iter<IO, CONV, VEC, FAST, STATS, false, 0, true, 0>(p, sp, geo, T, lds, wave, c, n, lane, ops,
+                                                                k, du, j, 0, fa, bop, cy);
+        block_iter<IO, CONV, VEC, FAST, STATS, false, 1, true, 1>(p, sp, geo, T, lds, wave, c, n, lane, ops,
+                                                                k, du, j + 1, 0, fb, bop, cy);
+        block_iter<IO, CONV, VEC, FAST, STATS, false, 0, true, 2>(p, sp, geo, T, lds, wave, c, n, lane, ops,
+                                                                k, du, j + 2, 0, fa, bop, cy);
+        block_iter<IO, CONV, VEC, FAST, STATS, false, 1, true, 0>(p, sp, geo, T, lds, wave, c, n, lane, ops,
+                                                                k, du, j + 3, 0, fb, bop, cy);
+        block_iter<IO, CONV, VEC, FAST, STATS, false, 0, true, 1>(p, sp, geo, T, lds, wave, c, n, lane, ops,
+                                                                k, du, j + 4, 0, fa, bop, cy);
+        block_iter<IO, CONV, VEC, FAST, STATS, false, 1, true, 2>(p, sp, geo, T, lds, wave, c, n, lane, ops,
+                                                                k, du, j + 5, 0, fb, bop, cy);
     }
     // The remaining blocks (j % 6 == 0, so the slot is 0 again): pairs with the
     // slot kept scalar (it is the same for the whole workgroup).
     auto advance = [&]() { s = __builtin_amdgcn_readfirstlane(s == kSlots - 1 ? 0 : s + 1); };
     for (; j + 2 < nblocks; j += 2) {
-        block_iter<IO, CONV, VEC, FAST, STATS, false, 0, true>(p, sp, geo, T, lds, wave, c, n, lane, sel, k,
-                                                        iat, du, j, s, fa, bop, cop, cy);
+        block_iter<IO, CONV, VEC, FAST, STATS, false, 0, true>(p, sp, geo, T, lds, wave, c, n, lane, ops, k,
+                                                        du, j, s, fa, bop, cy);
         advance();
-        block_iter<IO, CONV, VEC, FAST, STATS, false, 1, true>(p, sp, geo, T, lds, wave, c, n, lane, sel, k,
-                                                        iat, du, j + 1, s, fb, bop, cop, cy);
+        block_iter<IO, CONV, VEC, FAST, STATS, false, 1, true>(p, sp, geo, T, lds, wave, c, n, lane, ops, k,
+                                                        du, j + 1, s, fb, bop, cy);
         advance();
     }
     // One or two blocks remain (j is even).
     int last_par;
     if (j + 1 < nblocks) {
-        block_iter<IO, CONV, VEC, FAST, STATS, false, 0, true>(p, sp, geo, T, lds, wave, c, n, lane, sel, k,
-                                                        iat, du, j, s, fa, bop, cop, cy);
+        block_iter<IO, CONV, VEC, FAST, STATS, false, 0, true>(p, sp, geo, T, lds, wave, c, n, lane, ops, k,
+                                                        du, j, s, fa, bop, cy);
         advance();
-        block_iter<IO, CONV, VEC, FAST, STATS, true, 1, false>(p, sp, geo, T, lds, wave, c, n, lane, sel, k,
-                                                        iat, du, j + 1, s, fb, bop, cop, cy);
+        block_iter<IO, CONV, VEC, FAST, STATS, true, 1, false>(p, sp, geo, T, lds, wave, c, n, lane, ops, k,
+                                                        du, j + 1, s, fb, bop, cy);
         last_par = 1;
     } else {
-        block_iter<IO, CONV, VEC, FAST, STATS, true, 0, false>(p, sp, geo, T, lds, wave, c, n, lane, sel, k,
-                                                        iat, du, j, s, fa, bop, cop, cy);
+        block_iter<IO, CONV, VEC, FAST, STATS, true, 0, false>(p, sp, geo, T, lds, wave, c, n, lane, ops, k,
+                                                        du, j, s, fa, bop, cy);
         last_par = 0;
     }
     if constexpr (STATS) {
@@ -895,15 +1080,16 @@ __device__ __forceinline__ void scan_tiles_body(const ScanKernelParams &p, const
 
 // blockDim.x = 64 W; workgroup g covers channels [4 W q, 4 W q + 4 W) of
 // batch row g / groups_per_b, with q = g % groups_per_b.
-// Register budget: 4 waves per SIMD (<= 128 VGPRs).  A 96-VGPR budget (5
-// waves per SIMD, two 10-wave workgroups per CU on the 2.8B-like layer)
-// spilled in the conv variants and ran slower on every measured layer than
-// this budget with fewer waves resident.
+// Register budget: the wide path 4 waves per SIMD (<= 128 VGPRs; a 96-VGPR
+// budget, 5 waves per SIMD, spilled in the conv variants and ran slower on
+// every measured layer), the element path 3 (<= 168 VGPRs: it holds more
+// registers per block and spilled in its block loop at 128).
 template <bool VEC>
-constexpr int kWavesPerSimd = 4;
+constexpr int kWavesPerSimd = VEC ? 4 : 3;
 
 template <typename IO, bool CONV, bool VEC, bool STATS>
-__global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(kWavesPerSimd<VEC>, 8)))
+__global__ __launch_bounds__(256 * kWavesPerSimd<VEC>)
+__attribute__((amdgpu_waves_per_eu(kWavesPerSimd<VEC>, 8)))
 void scan_tiles_kernel(ScanKernelParams p) {
     extern __shared__ __attribute__((aligned(16))) char lds[];
     constexpr int es = sizeof(typename IO::storage);
@@ -978,10 +1164,6 @@ void scan_tiles_kernel(ScanKernelParams p) {
         if (K >= 3) k.wp1 = w[K - 3];
         if (K >= 4) k.wp0 = w[K - 4];
         if (p.conv_b) k.cb = p.conv_b[d];
-    }
-    {
-        float *prow = reinterpret_cast<float *>(lds + T.part) + (wave * kChPerWave + c) * kPRow;
-        prow[kRow * kPStride + n] = k.ia;
     }
     Carry cy;
     cy.h = (live && h_in) ? h_in[(b * D + d) * N + n] : 0.0f;
@@ -1111,7 +1293,7 @@ int choose_waves(int64_t batch, int64_t dim, bool wide, int64_t es) {
     const int64_t waves_per_cu = 4 * (wide ? kWavesPerSimd<true> : kWavesPerSimd<false>);
     int best = 0;
     double best_cost = 1e300;
-    for (int W = 1; W <= kMaxW; ++W) {
+    for (int W = 1; W <= std::min<int64_t>(kMaxW, waves_per_cu); ++W) {
         if (wide && !wide_w_ok(W, es)) continue;
         const int64_t lds = (int64_t)(es == 2 ? tile_lds_bytes<io_bf16>(W) : tile_lds_bytes<io_f32>(W));
         const int64_t per_row = (dim + 4 * W - 1) / (4 * W);
