@@ -31,13 +31,15 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
-# Vector ALU: 256 CUs x 4 SIMDs x 16 fp32 lanes per clock x 2.4 GHz = 39.3 T lane-slots/s
-# (one fp32 add, mul or fma per lane per slot; no packed-fp32 forms; exp2 takes two slots).
-VALU_PEAK_LANE_SLOTS = 256 * 4 * 16 * 2.4e9
-# Algorithmic VALU work of one state update (b, t, d, n) of the ZOH scan:
-#   dt*A (1), exp (2), B*x (1), (Abar - 1) * Bx / A folded into one fma (1),
-#   Abar*h + Bbar*x (1), C*h accumulated into y (1)  ->  7 lane-slots.
-SLOTS_PER_UPDATE = 7
+# Vector ALU: the published fp32 vector peak, 157.3 TFLOP/s, is 78.6 T fp32 fma lane-ops/s
+# (256 CUs x 4 SIMDs x 32 lanes per clock x 2.4 GHz; no packed-fp32 forms are needed for
+# it: a wave64 fma issues every 2 clocks).  Transcendentals run at a quarter of that rate,
+# so one exp2 counts as 4 fma-equivalents.
+VALU_PEAK_LANE_SLOTS = 256 * 4 * 32 * 2.4e9
+# Algorithmic VALU work of one state update (b, t, d, n) of the ZOH scan, in fma-equivalents:
+#   dt*A (1), exp (4), B*x (1), (Abar - 1) * Bx / A folded into one fma (1),
+#   Abar*h + Bbar*x (1), C*h accumulated into y (1)  ->  9.
+SLOTS_PER_UPDATE = 9
 
 
 def scan_algorithmic_bytes(B, L, D, N, io_bytes, conv_k=0, final_state=False, h0=False,
@@ -146,7 +148,7 @@ def scan_entry(cfg, ms, nbytes):
     return dict(ms=round(ms, 5), gbs=round(gbs, 2), frac_hbm=round(gbs / HBM_PEAK_GBS, 4),
                 elems_per_s=round(cfg.elems / (ms * 1e-3), 1), algorithmic_bytes=nbytes,
                 valu=dict(achieved=round(alu, 3), peak=round(VALU_PEAK_LANE_SLOTS / 1e12, 2),
-                          unit="T VALU lane-slots/s",
+                          unit="T fp32 fma-equivalent lane-ops/s",
                           frac=round(alu * 1e12 / VALU_PEAK_LANE_SLOTS, 4),
                           algorithmic_slots_per_update=SLOTS_PER_UPDATE,
                           state_updates_per_launch=upd))

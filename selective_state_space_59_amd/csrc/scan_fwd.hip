@@ -26,14 +26,15 @@
 //     channel and computes u (conv prologue, its 3-step history from the
 //     neighbouring lanes through DPP shifts) and dt there, once per
 //     (t, channel);
-//   * three products of the step loop run on the matrix cores, 4 steps
-//     x 16 entries x 4 channels per MFMA: dt A (a 4x4x1 MFMA whose A-block
-//     broadcast hands every lane of a row the dt of steps 4g..4g+3), u B
-//     (bf16 I/O without the conv prologue: a 4x4x4 bf16 MFMA on the raw u
-//     and B, exact), and the read-out weights C x (x = 1/A in the fast form,
-//     1 otherwise; see WSel).  Otherwise B reaches every row through a 0/1
-//     selector MFMA and u B is a vector product with u of step k read from
-//     lane k of the row through a DPP row broadcast;
+//   * the recurrence of step k reads dt of step k from lane k of the row
+//     through a DPP row broadcast folded into the multiply;
+//   * two products of the step loop run on the matrix cores, 4 steps x 16
+//     entries x 4 channels per MFMA: u B (bf16 I/O without the conv
+//     prologue: a 4x4x4 bf16 MFMA on the raw u and B, exact) and the
+//     read-out weights C x (x = 1/A in the fast form, 1 otherwise; see
+//     WSel).  Otherwise B reaches every row through a 0/1 selector MFMA and
+//     u B is a vector product with u of step k read through a DPP row
+//     broadcast;
 //   * each lane's 16 states h_{t,n} are transposed through LDS, so lane
 //     (c, j) sums the 16 states of step t0 + j times their weights and
 //     applies the skip and the gate; y goes out through LDS with coalesced
@@ -42,9 +43,9 @@
 // a three-slot LDS ring, a block's read-outs are summed and its y stored
 // during the next block, and the MFMAs run one step group ahead.
 //
-// Vector-ALU cost per state update (the binding resource): one exp (two
-// issue slots on gfx950) and two fused fp32 ops in the fast form, which
-// carries g = A h, plus one fused op of the read-out sum:
+// Vector-ALU cost per state update (the binding resource): one exp (a
+// quarter-rate transcendental on gfx950), dt A, and two fused fp32 ops in
+// the fast form, which carries g = A h, plus one fused op of the read-out sum:
 //   e = 2^(dt A log2e); bx = e*bu - bu; g = e*g + bx; y += g * w.
 // bx = fma(e, bu, -bu) makes dt = 0 hold the state exactly (e = 1 gives 0).
 // With the conv prologue, or fp32 I/O, bu = u*B adds one more.
@@ -533,23 +534,15 @@ __device__ __forceinline__ void store_y(const ScanKernelParams &p, const Geo &g,
     }
 }
 
-// Three products of the step loop run on the matrix cores.
+// Two products of the step loop can run on the matrix cores.  (dt A stays
+// on the vector ALU: a 4x4x1 MFMA per step group, whose A-block broadcast
+// hands every lane of a row the dt of steps 4g..4g+3, measured no faster than
+// the 16 multiplies with dt read from lane k through a DPP row broadcast.)
 //
-// dt A log2(e) of steps 4g..4g+3 (dta): the 4x4x1 MFMA multiplies, per block
-// of 4 lanes, a 4-vector by a 4-vector.  Lane (c, n) gives its own A log2(e)
-// as the B operand; the A operand of every 4-lane block of a wave row is
-// broadcast from the row's block g (CBSZ 2, ABID g), that is from lanes
-// (c, 4g..4g+3), which hold dt of steps 4g..4g+3.  Register r of lane (c, n)
-// then holds dt_{4g+r} A_n log2(e), rounded once as on the vector ALU.
-template <int G>
-__device__ __forceinline__ mfma_f32x4 dta_group(float dt, float a2) {
-    const mfma_f32x4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
-    return __builtin_amdgcn_mfma_f32_4x4x1f32(dt, a2, zero, 2, G, 0);
-}
-
 // u B of steps 4g..4g+3, where u is a bf16 input (bf16 I/O without the conv
-// prologue: u is x itself).  4x4x4 bf16 MFMA, again with the A operand
-// broadcast from the row's block g: lane (c, t) gives its u at position t % 4
+// prologue: u is x itself).  4x4x4 bf16 MFMA: a wave is 16 blocks of 4
+// lanes, and the A operand of every block of a wave row is broadcast from
+// the row's block g (CBSZ 2, ABID g).  Lane (c, t) gives its u at position t % 4
 // of four (zeros elsewhere, udiag), so that block's A is the diagonal of
 // u_{4g..4g+3}; lane (c, n) gives steps 4g..4g+3 of B's entry n as the B
 // operand.  Register r of lane (c, n) holds u_{4g+r} B_{4g+r,n}: one exact
@@ -893,9 +886,9 @@ __device__ __forceinline__ void block_iter(const ScanKernelParams &p, const Span
     if (j >= 2 && (!VEC || du.ystore)) store_y<IO, VEC>(p, geo, du, yst, j - 2, tid);
 
     // -- the 16 steps ----------------------------------------------------------
-    // Steps in groups of four: the group's dt A and u B (or B) come from
-    // MFMAs issued one group ahead, so the matrix cores' latency is hidden,
-    // and the group's four states leave with one 128-bit LDS write.
+    // Steps in groups of four: the group's u B (or B) comes from an MFMA
+    // issued one group ahead, so the matrix cores' latency is hidden, and the
+    // group's four states leave with one 128-bit LDS write.
     uint2 ud = make_uint2(0u, 0u);
     if constexpr (MF) ud = make_udiag(u, ops.um0, ops.um1);
     auto bu_of = [&](auto G) -> mfma_f32x4 {
@@ -903,20 +896,19 @@ __device__ __forceinline__ void block_iter(const ScanKernelParams &p, const Span
         if constexpr (MF) return bu_group<g>(ud, bop.g[g]);
         else return bcast<IO>(bop.v, ops.sel, g);
     };
-    mfma_f32x4 Zn = dta_group<0>(dt, k.a2), Bn = bu_of(ic<0>{});
+    mfma_f32x4 Bn = bu_of(ic<0>{});
     static_for<kTB / 4>([&](auto G) {
         constexpr int gi = decltype(G)::value;
         constexpr int g4 = 4 * gi;
-        const mfma_f32x4 Zk = Zn, Bk = Bn;
+        const mfma_f32x4 Bk = Bn;
         if constexpr (gi + 1 < kTB / 4) {
-            Zn = dta_group<gi + 1>(dt, k.a2);
             Bn = bu_of(ic<gi + 1>{});
         }
         float pk[4];
         static_for<4>([&](auto K) {
             constexpr int kk = decltype(K)::value;
             constexpr int kx = g4 + kk;
-            const float e = hw_exp2(Zk[kk]);
+            const float e = hw_exp2(row_bcast<kx>(dt) * k.a2);
             float bu;
             if constexpr (MF) bu = Bk[kk];
             else bu = row_bcast<kx>(u) * Bk[kk];
