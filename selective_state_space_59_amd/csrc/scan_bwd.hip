@@ -328,14 +328,27 @@ __global__ __launch_bounds__(64 * kWavesB) void bwd_ckpt_kernel(BwdParams p) {
     else ckpt_body<IO, false, CONV, STAGE>(p, l, a, ia, h, tile);
 }
 
-typedef float mfma4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 
-// Sum over the wave's 4 channels of each lane's value, for every entry n:
-// a 16x16x4 fp32 MFMA with the ones matrix as A and the lane values as B
-// (B[c][n] is lane (c, n)); every lane gets the sum for its n.
-__device__ __forceinline__ float sum_channels(float v) {
-    const mfma4_t zero = {0.0f, 0.0f, 0.0f, 0.0f};
-    return __builtin_amdgcn_mfma_f32_16x16x4f32(1.0f, v, zero, 0, 0, 0)[0];
+// Sums over the wave's 4 channels (its 4 rows of 16 lanes) of four values
+// v[0..3] per lane, for every entry n: row k of the result holds the sum of
+// v[k].  v_permlane16_swap exchanges the odd rows of its first operand with
+// the even rows of its second, v_permlane32_swap the upper half of the first
+// with the lower half of the second; each swap plus an add halves the
+// rows still to be added:
+//   (v0, v1) -> rows (v0: r0+r1, v1: r0+r1, v0: r2+r3, v1: r2+r3), same for (v2, v3);
+//   then the two results -> rows (v0, v1, v2, v3: r0+r1+r2+r3).
+// (The swap's two results are taken from a named vector: passed straight
+// into a function parameter, both elements read as the first one.)
+__device__ __forceinline__ float sum_channels4(const float (&v)[4]) {
+    auto u = [](float f) { return __builtin_bit_cast(unsigned, f); };
+    auto f = [](unsigned x) { return __builtin_bit_cast(float, x); };
+    const u32x2_t a = __builtin_amdgcn_permlane16_swap(u(v[0]), u(v[1]), false, false);
+    const float s01 = f(a.x) + f(a.y);
+    const u32x2_t b = __builtin_amdgcn_permlane16_swap(u(v[2]), u(v[3]), false, false);
+    const float s23 = f(b.x) + f(b.y);
+    const u32x2_t c = __builtin_amdgcn_permlane32_swap(u(s01), u(s23), false, false);
+    return f(c.x) + f(c.y);
 }
 
 // The B and C rows of a block, staged in LDS for the whole workgroup (bf16
@@ -480,16 +493,15 @@ __device__ __forceinline__ void bwd_body(const BwdParams &p, const LaneB &l, flo
                     accA = __builtin_fmaf(e * dabar, dtk, accA);
                     accA = __builtin_fmaf(xb * dtk, dtk * psi_f(zz, e, ph, r), accA);
                 }
-                sb[kk] = sum_channels(dbbar * dtph);
-                sc[kk] = sum_channels(gyk * hcur);
+                sb[kk] = dbbar * dtph;
+                sc[kk] = gyk * hcur;
                 lam = e * lt;
             });
             *reinterpret_cast<float4 *>(my0 + g4) = make_float4(pdu[0], pdu[1], pdu[2], pdu[3]);
             *reinterpret_cast<float4 *>(my1 + g4) = make_float4(pdt[0], pdt[1], pdt[2], pdt[3]);
-            if (c == 0) {
-                *reinterpret_cast<float4 *>(redw + n * kTS + g4) = make_float4(sb[0], sb[1], sb[2], sb[3]);
-                *reinterpret_cast<float4 *>(redw + (kRowN + n) * kTS + g4) = make_float4(sc[0], sc[1], sc[2], sc[3]);
-            }
+            // row c of the wave holds the channel sums of step g4 + c
+            redw[n * kTS + g4 + c] = sum_channels4(sb);
+            redw[(kRowN + n) * kTS + g4 + c] = sum_channels4(sc);
         });
         __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
         request_block<IO, CONV>(p, l, j > 0 ? j - 1 : 0, nx);  // the request after block 0 is not used
