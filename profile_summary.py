@@ -178,28 +178,35 @@ def cmd_sq(a):
              "```", "", "Kernel: `%s`. Counters are per dispatch (median over dispatches), summed over "
              "the GPU." % _short(a.kernel, 100), "",
              "| counter | value | meaning |", "|---|---:|---|"]
+    saturated = [n for n in sorted(vals) if abs(vals[n][0] - 2.0 ** 31) < 2.0]  # a 32-bit counter at its limit
     for n in sorted(vals):
-        lines.append("| %s | %.4g | %s |" % (n, vals[n][0], SQ_NOTES.get(n, "")))
+        if n not in saturated:
+            lines.append("| %s | %.4g | %s |" % (n, vals[n][0], SQ_NOTES.get(n, "")))
+    if saturated:
+        lines += ["", "Not shown, read at the 32-bit limit (2^31): %s." % ", ".join(saturated)]
     lines += ["", "| derived | value |", "|---|---:|"]
     if a.updates and g("SQ_INSTS_VALU") is not None:
         lines.append("| state updates per dispatch | %d |" % a.updates)
-        lines.append("| VALU instructions per update (64 lanes each; the step loop's core is 6) | %.3f |"
+        lines.append("| VALU instructions per update (64 lanes each) | %.3f |"
                      % (g("SQ_INSTS_VALU") * 64 / a.updates))
         if g("SQ_INSTS_VALU_TRANS_F32") is not None:
             lines.append("| fp32 transcendentals per update (one exp is the core) | %.3f |"
                          % (g("SQ_INSTS_VALU_TRANS_F32") * 64 / a.updates))
+        if g("SQ_INSTS_MFMA") is not None:
+            lines.append("| MFMA instructions per update | %.4f |" % (g("SQ_INSTS_MFMA") * 64 / a.updates))
     if g("SQ_WAVE_CYCLES"):
         for n in ("SQ_WAIT_ANY", "SQ_WAIT_INST_LDS", "SQ_WAIT_INST_ANY", "SQ_ACTIVE_INST_VALU"):
             if g(n) is not None:
                 lines.append("| %s / SQ_WAVE_CYCLES | %.3f |" % (n, g(n) / g("SQ_WAVE_CYCLES")))
     if a.duration_us and g("SQ_INSTS_VALU") is not None:
-        # a wave64 VALU instruction occupies a SIMD16 for 4 cycles, an fp32
-        # transcendental for 8; 1024 SIMDs at 2.4 GHz
+        # issue cost model from microbenchmarks on gfx950 (4 waves per SIMD):
+        # ~2 cycles per wave64 fp32 VALU instruction, 8 per fp32 transcendental;
+        # 1024 SIMDs at 2.4 GHz
         trans = g("SQ_INSTS_VALU_TRANS_F32") or 0.0
-        cyc = (g("SQ_INSTS_VALU") + trans) * 4.0
+        cyc = (g("SQ_INSTS_VALU") - trans) * 2.0 + trans * 8.0
         avail = 1024 * a.duration_us * 1e-6 * 2.4e9
         lines.append("| kernel duration (us, from the kernel trace) | %.2f |" % a.duration_us)
-        lines.append("| VALU issue cycles / SIMD cycles (4 per instruction, 8 per transcendental) | %.3f |"
+        lines.append("| VALU issue cycles / SIMD cycles (2 per instruction, 8 per transcendental) | %.3f |"
                      % (cyc / avail))
     _write(a.out, "\n".join(lines) + "\n")
 
