@@ -6,7 +6,9 @@
 // dL/dh_final = dh_final.  The page's backward recomputes the states instead
 // of storing them (sec. 4c); here:
 //   1. a checkpoint pass runs the recurrence forward and stores only the
-//      state entering every 16-step block (1/16 of the expanded states);
+//      state entering every 16-step block (1/16 of the expanded states): the
+//      forward scan kernel's checkpoint variant (launch_scan_ckpt), with its
+//      workgroup-staged loads and no read-out;
 //   2. the backward kernel walks the blocks from last to first.  Per block it
 //      re-runs the 16 steps from the checkpoint, keeping h_{t-1} and
 //      exp(dt A) in registers, and then runs the adjoint recurrence
@@ -119,7 +121,6 @@ __device__ __forceinline__ LaneB lane_setup(const BwdParams &p) {
     return l;
 }
 
-// Pass 1: states entering every block.
 // dt phi(dt A) = (e - 1)/A: in waves where every |A| >= 1/16 (FAST) as
 // e/A - 1/A in one fma, otherwise through phi (series near 0).
 template <bool FAST>
@@ -247,85 +248,6 @@ __device__ __forceinline__ void bc_read(const char *bcl, int tensor, int n, floa
         v[4 * q + 2] = __uint_as_float(d.y << 16);
         v[4 * q + 3] = __uint_as_float(d.y & 0xffff0000u);
     }
-}
-
-// The checkpoint pass's B rows through a wave-private LDS tile (bf16 I/O,
-// 8-byte aligned B): lane q fetches entries 4 (q % 4) .. +3 of step q / 4 as
-// one 8-byte load, the wave writes them transposed ([entry][step], rows 40
-// bytes apart) and every lane reads its entry's 16 steps back (bc_read).  The
-// 4 channel rows of a wave share B, so this replaces 16 two-byte loads per
-// lane and block; LDS order within a wave needs no barrier.
-constexpr int kCkptTile = kRowN * kBcRow;
-__device__ __forceinline__ uint2 ckpt_fetch(const BwdParams &p, int64_t b, int64_t jb, int lane) {
-    const int64_t t = jb * kStep + (lane >> 2);
-    const int64_t tc = t < p.L ? t : p.L - 1;
-    return *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(p.Bm) + (b * p.L + tc) * kRowN + 4 * (lane & 3));
-}
-__device__ __forceinline__ void ckpt_store(char *tile, uint2 v, int lane) {
-    uint16_t *col = reinterpret_cast<uint16_t *>(tile + 4 * (lane & 3) * kBcRow) + (lane >> 2);
-    col[0] = (uint16_t)(v.x & 0xffffu);
-    col[kBcRow / 2] = (uint16_t)(v.x >> 16);
-    col[kBcRow] = (uint16_t)(v.y & 0xffffu);
-    col[3 * kBcRow / 2] = (uint16_t)(v.y >> 16);
-}
-
-template <typename IO, bool FAST, bool CONV, bool STAGE>
-__device__ __forceinline__ void ckpt_body(const BwdParams &p, const LaneB &l, float a, float ia, float h,
-                                          char *tile) {
-    const float a2 = a * kLog2e;
-    const int64_t nb = (p.L + kStep - 1) / kStep;
-    float wr[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    float cb = 0.0f;
-    if (CONV && l.valid) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) wr[3 - j] = j < p.K ? p.conv_w[l.d * p.K + p.K - 1 - j] : 0.0f;
-        cb = p.conv_b ? p.conv_b[l.d] : 0.0f;
-    }
-    const float bias = (l.valid && p.dbias) ? p.dbias[l.d] : 0.0f;
-    // Block j's inputs are requested while block j - 1 runs (the request
-    // after the last block reads clamped rows and is not used).
-    const int lane = threadIdx.x & 63;
-    OwnRaw rn = own_raw<IO, CONV>(p, l, l.n);
-    uint32_t bn[STAGE ? 1 : kStep];
-    uint2 bq = make_uint2(0u, 0u);
-    if (STAGE) bq = ckpt_fetch(p, l.b, 0, lane);
-    else load_rows_bits<IO>(p.Bm, p, l, 0, reinterpret_cast<uint32_t (&)[kStep]>(bn));
-    for (int64_t j = 0; j < nb; ++j) {
-        if (l.valid) p.ckpt[((j * p.B + l.b) * p.D + l.d) * kRowN + l.n] = h;
-        float u, dt, bv[kStep];
-        own_finish<IO, CONV>(p, rn, wr, cb, bias, u, dt);
-        if (STAGE) {
-            ckpt_store(tile, bq, lane);
-            __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-            bc_read(tile, 0, l.n, bv);
-            bq = ckpt_fetch(p, l.b, j + 1, lane);
-        } else {
-#pragma unroll
-            for (int k = 0; k < kStep; ++k) bv[k] = bits_f32<IO>(bn[k]);
-            load_rows_bits<IO>(p.Bm, p, l, (j + 1) * kStep, reinterpret_cast<uint32_t (&)[kStep]>(bn));
-        }
-        rn = own_raw<IO, CONV>(p, l, (j + 1) * kStep + l.n);
-        sfor<kStep>([&](auto K) {
-            constexpr int k = decltype(K)::value;
-            const float dtk = bcast_row<k>(dt), uk = bcast_row<k>(u);
-            const float e = hw_exp2(dtk * a2);
-            h = __builtin_fmaf(e, h, dtphi<FAST>(dtk, a, ia, e) * (bv[k] * uk));
-        });
-    }
-}
-
-// CONV: with the conv prologue (K > 0); a separate instance keeps the taps
-// out of the registers of the plain scan.  STAGE: B through the wave tiles.
-template <typename IO, bool CONV, bool STAGE>
-__global__ __launch_bounds__(64 * kWavesB) void bwd_ckpt_kernel(BwdParams p) {
-    __shared__ __attribute__((aligned(16))) char tiles[STAGE ? kWavesB * kCkptTile : 16];
-    const LaneB l = lane_setup(p);
-    char *tile = tiles + (STAGE ? l.wave * kCkptTile : 0);
-    const float a = l.valid ? p.A[l.d * kRowN + l.n] : 0.0f;
-    const float ia = a != 0.0f ? 1.0f / a : 0.0f;
-    const float h = (l.valid && p.h0) ? p.h0[(l.b * p.D + l.d) * kRowN + l.n] : 0.0f;
-    if (__all(!l.valid || fabsf(a) >= 0.0625f)) ckpt_body<IO, true, CONV, STAGE>(p, l, a, ia, h, tile);
-    else ckpt_body<IO, false, CONV, STAGE>(p, l, a, ia, h, tile);
 }
 
 typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
@@ -841,15 +763,27 @@ template <typename IO>
 hipError_t launch_bwd_typed(const BwdParams &p, const ssm_scan_bwd_args_t &a, float *pconv, int64_t nch,
                             hipStream_t stream) {
     const unsigned grid = (unsigned)(p.G * p.B);
-    constexpr bool kBf16 = sizeof(typename IO::storage) == 2;
-    if (kBf16 && (uintptr_t)p.Bm % 8 == 0) {
-        if (p.K > 0) bwd_ckpt_kernel<IO, true, kBf16><<<grid, 64 * kWavesB, 0, stream>>>(p);
-        else bwd_ckpt_kernel<IO, false, kBf16><<<grid, 64 * kWavesB, 0, stream>>>(p);
-    } else {
-        if (p.K > 0) bwd_ckpt_kernel<IO, true, false><<<grid, 64 * kWavesB, 0, stream>>>(p);
-        else bwd_ckpt_kernel<IO, false, false><<<grid, 64 * kWavesB, 0, stream>>>(p);
-    }
-    hipError_t e = hipGetLastError();
+    // Pass 1, the checkpoints: the forward scan kernel in its checkpoint
+    // variant (staged loads; no read-out), on the 16-entry rows.
+    ssm_scan_args_t f{};
+    f.batch = p.B;
+    f.seqlen = p.L;
+    f.dim = p.D;
+    f.dstate = kRowN;
+    f.io_dtype = a.io_dtype;
+    f.delta_softplus = p.softplus;
+    f.conv_k = p.K;
+    f.x = p.x;
+    f.delta = p.delta;
+    f.Bm = p.Bm;
+    f.Cm = p.Cm;
+    f.A = p.A;
+    f.delta_bias = p.dbias;
+    f.conv_w = p.conv_w;
+    f.conv_b = p.conv_b;
+    f.h0 = p.h0;
+    f.conv_state_in = p.cs_in;
+    hipError_t e = launch_scan_ckpt(f, p.ckpt, stream);
     if (e != hipSuccess) return e;
     const size_t lds = (size_t)(kWavesB * (2 * kTrWave + kRedWave)) * sizeof(float);
     // B and C staged in LDS: bf16 rows read as 4-byte pairs.

@@ -90,6 +90,9 @@ struct ScanKernelParams {
     const void *cs_in;  // conv state (B, K-1, D): x before row 0, or NULL (= 0)
     void *y;
     float *h_out;       // state after row t_end - 1, or NULL
+    // Checkpoint launches (the backward's first pass) write the state entering
+    // every 16-step block, [nblocks][B][D][16] (entry n < N at n), and no outputs.
+    float *ckpt;
     // Sequence segments (see launch_segmented): mode 0 scans [t_begin, t_end)
     // as one piece; mode 1 scans every segment of seg_len rows from a zero
     // state (the first from h_in) and records its end state, its sum of dt
@@ -716,7 +719,9 @@ __device__ __forceinline__ mfma_f32x4 weight_group(const WSel<IO> &ws, const COp
 
 struct LaneConst {
     float a, a2, ia, dsk, dbias, cb, wp0, wp1, wp2, wp3;
-    bool live;  // the lane holds a real (channel, entry)
+    bool live;     // the lane holds a real (channel, entry)
+    bool dvalid;   // the lane's channel is real
+    int64_t ckpt;  // (b D + d) 16 + n: the lane's place in a checkpoint slab
 };
 
 // Read-out of one step: lane (c, t) reads the 16 states of step t that the
@@ -819,7 +824,7 @@ struct WaveOps {
 // PAR = j % 2 selects the ybuf halves; SLOT = j % 3 when it is known at
 // compile time; TAIL masks steps past the sequence end; STAGE is off in the
 // last block.
-template <typename IO, bool CONV, bool VEC, bool FAST, bool STATS, bool TAIL, int PAR, bool STAGE,
+template <typename IO, bool CONV, bool VEC, bool FAST, int KIND, bool TAIL, int PAR, bool STAGE,
           int SLOT = -1>
 __device__ __forceinline__ void block_iter(const ScanKernelParams &p, const Span &sp, const Geo &geo,
                                            const Tiles &T, char *lds, int wave, int c, int n,
@@ -827,6 +832,7 @@ __device__ __forceinline__ void block_iter(const ScanKernelParams &p, const Span
                                            const Duty &du, int j, int s_run, Fetch<VEC> &f,
                                            BOp<IO, kBuMfma<IO, CONV, VEC>> &bop, Carry &cy) {
     constexpr bool MF = kBuMfma<IO, CONV, VEC>;
+    constexpr bool STATS = KIND == 1, CKPT = KIND == 2;
     constexpr int es = sizeof(typename IO::storage);
     const int tid = threadIdx.x, nthreads = blockDim.x;
     const int ci = 4 * wave + c;
@@ -837,12 +843,19 @@ __device__ __forceinline__ void block_iter(const ScanKernelParams &p, const Span
     const int s_stage = s_next == kSlots - 1 ? 0 : s_next + 1;
     float *prow = reinterpret_cast<float *>(lds + T.part) + (wave * kChPerWave + c) * kPRow;
 
-    if constexpr (VEC) wave_barrier();
+    // (A checkpoint launch reads no states back before its barrier.)
+    if constexpr (VEC && !CKPT) wave_barrier();
     else __syncthreads();
+    if constexpr (CKPT) {
+        // the state entering this block (the fast form carries A h)
+        if (k.dvalid)
+            p.ckpt[(sp.t0 / kTB + j) * (p.B * p.D * kRow) + k.ckpt] = FAST ? cy.h * k.ia : cy.h;
+    }
     // -- LDS reads of later blocks first ------------------------------------------
     float own_next[3];
     read_own<IO>(T, lds, s_next, n, ci, own_next);
-    const YChunk<VEC> yst = read_ybuf<IO, VEC>(du, T, lds, PAR, tid);
+    YChunk<VEC> yst;
+    if constexpr (!CKPT) yst = read_ybuf<IO, VEC>(du, T, lds, PAR, tid);
     const BOp<IO, MF> bop_n = load_bop<IO, MF>(lds + T.bc + s_next * T.bc_slot, lane);
 
     // -- this block's inputs ---------------------------------------------------
@@ -873,7 +886,7 @@ __device__ __forceinline__ void block_iter(const ScanKernelParams &p, const Span
     }
 
     // -- outputs of block j-1 (lane (c, n) finishes its step n) ---------------
-    {
+    if constexpr (!CKPT) {
         float yv = cy.acc + k.dsk * cy.u_prev;
         if (p.z) yv *= silu(cy.z_prev);
         char *ydst = lds + T.ybuf + (1 - PAR) * T.ybuf_slot + n * T.rs + ci * es;
@@ -883,7 +896,8 @@ __device__ __forceinline__ void block_iter(const ScanKernelParams &p, const Span
             *reinterpret_cast<float *>(ydst) = yv;
     }
     // -- outputs of block j-2 leave ----------------------------------------------
-    if (j >= 2 && (!VEC || du.ystore)) store_y<IO, VEC>(p, geo, du, yst, j - 2, tid);
+    if constexpr (!CKPT)
+        if (j >= 2 && (!VEC || du.ystore)) store_y<IO, VEC>(p, geo, du, yst, j - 2, tid);
 
     // -- the 16 steps ----------------------------------------------------------
     // Steps in groups of four: the group's u B (or B) comes from an MFMA
@@ -922,7 +936,8 @@ __device__ __forceinline__ void block_iter(const ScanKernelParams &p, const Span
             cy.h = __builtin_fmaf(e, cy.h, bx);
             pk[kk] = cy.h;
         });
-        *reinterpret_cast<float4 *>(&prow[n * kPStride + g4]) = make_float4(pk[0], pk[1], pk[2], pk[3]);
+        if constexpr (!CKPT)
+            *reinterpret_cast<float4 *>(&prow[n * kPStride + g4]) = make_float4(pk[0], pk[1], pk[2], pk[3]);
     });
     // The states are this wave's own: they are read back (LDS operations of
     // one wave complete in order) after this block's C rows and the staging
@@ -931,8 +946,12 @@ __device__ __forceinline__ void block_iter(const ScanKernelParams &p, const Span
     // staging (its fetch registers are live until then).
     float part[kRow];
     COp<IO> cop;
-    if constexpr (VEC) cop = load_cop<IO>(lds + T.bc + s_cur * T.bc_slot + kBTile<IO>, lane);
-    else load_partials(prow, n, part);
+    if constexpr (CKPT) {
+    } else if constexpr (VEC) {
+        cop = load_cop<IO>(lds + T.bc + s_cur * T.bc_slot + kBTile<IO>, lane);
+    } else {
+        load_partials(prow, n, part);
+    }
 
     cy.u_prev = u;
     cy.z_prev = zv;
@@ -945,7 +964,7 @@ __device__ __forceinline__ void block_iter(const ScanKernelParams &p, const Span
         stage_block<IO, VEC>(geo, du, T, lds, s_stage, tid, nthreads, f);
         __builtin_amdgcn_sched_barrier(0);
     }
-    if constexpr (VEC) {
+    if constexpr (VEC && !CKPT) {
         load_partials(prow, n, part);
         __builtin_amdgcn_sched_barrier(0);
     }
@@ -954,16 +973,19 @@ __device__ __forceinline__ void block_iter(const ScanKernelParams &p, const Span
         // same registers.
         fetch_block<IO, VEC>(geo, du, j + 4, tid, nthreads, f);
     }
-    if constexpr (!VEC) cop = load_cop<IO>(lds + T.bc + s_cur * T.bc_slot + kBTile<IO>, lane);
-    const mfma_f32x4 w[4] = {weight_group<IO, 0>(ops.ws, cop), weight_group<IO, 1>(ops.ws, cop),
-                             weight_group<IO, 2>(ops.ws, cop), weight_group<IO, 3>(ops.ws, cop)};
-    cy.acc = sum_partials(part, w);
+    if constexpr (!CKPT) {
+        if constexpr (!VEC) cop = load_cop<IO>(lds + T.bc + s_cur * T.bc_slot + kBTile<IO>, lane);
+        const mfma_f32x4 w[4] = {weight_group<IO, 0>(ops.ws, cop), weight_group<IO, 1>(ops.ws, cop),
+                                 weight_group<IO, 2>(ops.ws, cop), weight_group<IO, 3>(ops.ws, cop)};
+        cy.acc = sum_partials(part, w);
+    }
 }
 
-template <typename IO, bool CONV, bool VEC, bool FAST, bool STATS>
+template <typename IO, bool CONV, bool VEC, bool FAST, int KIND>
 __device__ __forceinline__ void scan_tiles_body(const ScanKernelParams &p, const Span &sp, const Geo &geo,
                                                 const Tiles &T, char *lds, int64_t b, int wave,
                                                 int c, int n, const LaneConst &k, Carry &cy) {
+    constexpr bool STATS = KIND == 1, CKPT = KIND == 2;
     const int tid = threadIdx.x, nthreads = blockDim.x;
     const int lane = tid & 63;
     const int ci = 4 * wave + c;
@@ -1005,41 +1027,41 @@ __device__ __forceinline__ void scan_tiles_body(const ScanKernelParams &p, const
     // computed per block.  The element path holds more registers per block and
     // keeps the two-block loop.
     if constexpr (VEC) for (; j + 6 < nblocks; j += 6) {
-        block_iter<IO, CONV, VEC, FAST, STATS, false, 0, true, 0>(p, sp, geo, T, lds, wave, c, n, lane, ops,
+        block_iter<IO, CONV, VEC, FAST, KIND, false, 0, true, 0>(p, sp, geo, T, lds, wave, c, n, lane, ops,
                                                                 k, du, j, 0, fa, bop, cy);
-        block_iter<IO, CONV, VEC, FAST, STATS, false, 1, true, 1>(p, sp, geo, T, lds, wave, c, n, lane, ops,
+        block_iter<IO, CONV, VEC, FAST, KIND, false, 1, true, 1>(p, sp, geo, T, lds, wave, c, n, lane, ops,
                                                                 k, du, j + 1, 0, fb, bop, cy);
-        block_iter<IO, CONV, VEC, FAST, STATS, false, 0, true, 2>(p, sp, geo, T, lds, wave, c, n, lane, ops,
+        block_iter<IO, CONV, VEC, FAST, KIND, false, 0, true, 2>(p, sp, geo, T, lds, wave, c, n, lane, ops,
                                                                 k, du, j + 2, 0, fa, bop, cy);
-        block_iter<IO, CONV, VEC, FAST, STATS, false, 1, true, 0>(p, sp, geo, T, lds, wave, c, n, lane, ops,
+        block_iter<IO, CONV, VEC, FAST, KIND, false, 1, true, 0>(p, sp, geo, T, lds, wave, c, n, lane, ops,
                                                                 k, du, j + 3, 0, fb, bop, cy);
-        block_iter<IO, CONV, VEC, FAST, STATS, false, 0, true, 1>(p, sp, geo, T, lds, wave, c, n, lane, ops,
+        block_iter<IO, CONV, VEC, FAST, KIND, false, 0, true, 1>(p, sp, geo, T, lds, wave, c, n, lane, ops,
                                                                 k, du, j + 4, 0, fa, bop, cy);
-        block_iter<IO, CONV, VEC, FAST, STATS, false, 1, true, 2>(p, sp, geo, T, lds, wave, c, n, lane, ops,
+        block_iter<IO, CONV, VEC, FAST, KIND, false, 1, true, 2>(p, sp, geo, T, lds, wave, c, n, lane, ops,
                                                                 k, du, j + 5, 0, fb, bop, cy);
     }
     // The remaining blocks (j % 6 == 0, so the slot is 0 again): pairs with the
     // slot kept scalar (it is the same for the whole workgroup).
     auto advance = [&]() { s = __builtin_amdgcn_readfirstlane(s == kSlots - 1 ? 0 : s + 1); };
     for (; j + 2 < nblocks; j += 2) {
-        block_iter<IO, CONV, VEC, FAST, STATS, false, 0, true>(p, sp, geo, T, lds, wave, c, n, lane, ops, k,
+        block_iter<IO, CONV, VEC, FAST, KIND, false, 0, true>(p, sp, geo, T, lds, wave, c, n, lane, ops, k,
                                                         du, j, s, fa, bop, cy);
         advance();
-        block_iter<IO, CONV, VEC, FAST, STATS, false, 1, true>(p, sp, geo, T, lds, wave, c, n, lane, ops, k,
+        block_iter<IO, CONV, VEC, FAST, KIND, false, 1, true>(p, sp, geo, T, lds, wave, c, n, lane, ops, k,
                                                         du, j + 1, s, fb, bop, cy);
         advance();
     }
     // One or two blocks remain (j is even).
     int last_par;
     if (j + 1 < nblocks) {
-        block_iter<IO, CONV, VEC, FAST, STATS, false, 0, true>(p, sp, geo, T, lds, wave, c, n, lane, ops, k,
+        block_iter<IO, CONV, VEC, FAST, KIND, false, 0, true>(p, sp, geo, T, lds, wave, c, n, lane, ops, k,
                                                         du, j, s, fa, bop, cy);
         advance();
-        block_iter<IO, CONV, VEC, FAST, STATS, true, 1, false>(p, sp, geo, T, lds, wave, c, n, lane, ops, k,
+        block_iter<IO, CONV, VEC, FAST, KIND, true, 1, false>(p, sp, geo, T, lds, wave, c, n, lane, ops, k,
                                                         du, j + 1, s, fb, bop, cy);
         last_par = 1;
     } else {
-        block_iter<IO, CONV, VEC, FAST, STATS, true, 0, false>(p, sp, geo, T, lds, wave, c, n, lane, ops, k,
+        block_iter<IO, CONV, VEC, FAST, KIND, true, 0, false>(p, sp, geo, T, lds, wave, c, n, lane, ops, k,
                                                         du, j, s, fa, bop, cy);
         last_par = 0;
     }
@@ -1048,6 +1070,7 @@ __device__ __forceinline__ void scan_tiles_body(const ScanKernelParams &p, const
         cy.scum += row_sum(cy.dsum);
         if (cy.head < 0 && __all(!k.live || k.a2 * cy.scum < kForgetExp2)) cy.head = nblocks;
     }
+    if constexpr (CKPT) return;
     // Outputs of the last block and of the one before it.
     constexpr int es = sizeof(typename IO::storage);
     const int jl = nblocks - 1;
@@ -1079,10 +1102,11 @@ __device__ __forceinline__ void scan_tiles_body(const ScanKernelParams &p, const
 template <bool VEC>
 constexpr int kWavesPerSimd = VEC ? 4 : 3;
 
-template <typename IO, bool CONV, bool VEC, bool STATS>
+template <typename IO, bool CONV, bool VEC, int KIND>
 __global__ __launch_bounds__(256 * kWavesPerSimd<VEC>)
 __attribute__((amdgpu_waves_per_eu(kWavesPerSimd<VEC>, 8)))
 void scan_tiles_kernel(ScanKernelParams p) {
+    constexpr bool STATS = KIND == 1;
     extern __shared__ __attribute__((aligned(16))) char lds[];
     constexpr int es = sizeof(typename IO::storage);
     const int W = blockDim.x / 64;
@@ -1141,6 +1165,8 @@ void scan_tiles_kernel(ScanKernelParams p) {
 
     LaneConst k;
     k.live = live;
+    k.dvalid = dvalid;
+    k.ckpt = ((b * D + d) * kRow) + n;
     k.a = live ? p.A[d * N + n] : 0.0f;
     k.a2 = k.a * kLog2e;
     k.ia = (k.a != 0.0f) ? 1.0f / k.a : 0.0f;
@@ -1179,10 +1205,10 @@ void scan_tiles_kernel(ScanKernelParams p) {
         if (fast) {
             // The fast form carries g = A h (the 1/A moves to the read-out).
             cy.h *= k.a;
-            scan_tiles_body<IO, CONV, VEC, true, STATS>(p, sp, geo, T, lds, b, wave, c, n, k, cy);
+            scan_tiles_body<IO, CONV, VEC, true, KIND>(p, sp, geo, T, lds, b, wave, c, n, k, cy);
             cy.h *= k.ia;
         } else {
-            scan_tiles_body<IO, CONV, VEC, false, STATS>(p, sp, geo, T, lds, b, wave, c, n, k, cy);
+            scan_tiles_body<IO, CONV, VEC, false, KIND>(p, sp, geo, T, lds, b, wave, c, n, k, cy);
         }
     }
     if (h_out && live) h_out[(b * D + d) * N + n] = cy.h;
@@ -1310,14 +1336,19 @@ hipError_t launch_typed(const ScanKernelParams &p, int W, hipStream_t stream) {
     const size_t lds = tile_lds_bytes<IO>(W);
     if (p.mode == 1) {
         if (p.K > 0)
-            scan_tiles_kernel<IO, true, VEC, true><<<grid, 64 * W, lds, stream>>>(p);
+            scan_tiles_kernel<IO, true, VEC, 1><<<grid, 64 * W, lds, stream>>>(p);
         else
-            scan_tiles_kernel<IO, false, VEC, true><<<grid, 64 * W, lds, stream>>>(p);
+            scan_tiles_kernel<IO, false, VEC, 1><<<grid, 64 * W, lds, stream>>>(p);
+    } else if (p.ckpt) {
+        if (p.K > 0)
+            scan_tiles_kernel<IO, true, VEC, 2><<<grid, 64 * W, lds, stream>>>(p);
+        else
+            scan_tiles_kernel<IO, false, VEC, 2><<<grid, 64 * W, lds, stream>>>(p);
     } else {
         if (p.K > 0)
-            scan_tiles_kernel<IO, true, VEC, false><<<grid, 64 * W, lds, stream>>>(p);
+            scan_tiles_kernel<IO, true, VEC, 0><<<grid, 64 * W, lds, stream>>>(p);
         else
-            scan_tiles_kernel<IO, false, VEC, false><<<grid, 64 * W, lds, stream>>>(p);
+            scan_tiles_kernel<IO, false, VEC, 0><<<grid, 64 * W, lds, stream>>>(p);
     }
     return hipGetLastError();
 }
@@ -1359,7 +1390,7 @@ struct Plan {
 
 size_t round256(size_t v) { return (v + 255) & ~(size_t)255; }
 
-Plan make_plan(const ssm_scan_args_t &a) {
+Plan make_plan(const ssm_scan_args_t &a, bool segments = true) {
     Plan q;
     const int64_t es = a.io_dtype == SSM_BF16 ? 2 : 4;
     // Wide (16-byte chunk) staging needs whole chunks per row, N = 16 and
@@ -1371,7 +1402,7 @@ Plan make_plan(const ssm_scan_args_t &a) {
     const int64_t rows = std::min(a.seqlen, q.chunk);  // rows of the longest launch
     const int64_t waves = a.batch * ((a.dim + 3) / 4);
     int64_t S = 1;
-    if (waves * 2 < kWaveTarget)
+    if (segments && waves * 2 < kWaveTarget)
         S = std::max<int64_t>(1, std::min({kMaxSegs, kWaveTarget / std::max<int64_t>(waves, 1),
                                            rows / kMinSegRows}));
     q.nseg = (int)S;
@@ -1430,6 +1461,7 @@ hipError_t launch_scan_fwd(const ssm_scan_args_t &a, hipStream_t stream) {
     p.conv_b = a.conv_b;
     p.cs_in = a.conv_k > 0 ? a.conv_state_in : nullptr;
     p.y = a.y;
+    p.ckpt = nullptr;
     p.mode = 0;
     p.nseg = 1;
     p.seg_len = q.seg_len;
@@ -1469,6 +1501,52 @@ hipError_t launch_scan_fwd(const ssm_scan_args_t &a, hipStream_t stream) {
     // The conv state is written after every pass has read the entering one
     // (it may be the same tensor).
     if (e == hipSuccess) e = launch_conv_state_out(a, stream);
+    return e;
+}
+
+hipError_t launch_scan_ckpt(const ssm_scan_args_t &a, float *ckpt, hipStream_t stream) {
+    const Plan q = make_plan(a, false);
+    const int64_t es = a.io_dtype == SSM_BF16 ? 2 : 4;
+    if (q.W == 0 || q.ngroups > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    if (q.chunk < 2 * kTB || a.dim * es > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    ScanKernelParams p{};
+    p.B = a.batch;
+    p.L = a.seqlen;
+    p.D = a.dim;
+    p.N = (int)a.dstate;
+    p.K = (int)a.conv_k;
+    p.softplus = a.delta_softplus;
+    p.groups_per_b = q.groups_per_b;
+    p.ngroups = q.ngroups;
+    p.x = a.x;
+    p.delta = a.delta;
+    p.Bm = a.Bm;
+    p.Cm = a.Cm;
+    p.z = nullptr;
+    p.A = a.A;
+    p.Dskip = nullptr;
+    p.dbias = a.delta_bias;
+    p.conv_w = a.conv_w;
+    p.conv_b = a.conv_b;
+    p.cs_in = a.conv_k > 0 ? a.conv_state_in : nullptr;
+    p.y = nullptr;
+    p.ckpt = ckpt;
+    p.mode = 0;
+    p.nseg = 1;
+    p.seg_len = q.seg_len;
+    // Launches start on block boundaries (q.chunk is a multiple of 32 rows),
+    // so the state between two launches is the checkpoint of the second's
+    // first block: each launch leaves it there and the next one starts from it.
+    const int64_t slab = a.batch * a.dim * (int64_t)kRow;
+    hipError_t e = hipSuccess;
+    for (int64_t t = 0; t < a.seqlen && e == hipSuccess; t += q.chunk) {
+        const bool first = t == 0, last = t + q.chunk >= a.seqlen;
+        p.t_begin = t;
+        p.t_end = last ? a.seqlen : t + q.chunk;
+        p.h_in = first ? a.h0 : ckpt + (t / kTB) * slab;
+        p.h_out = last ? nullptr : ckpt + (p.t_end / kTB) * slab;
+        e = launch_pass(a, p, q, stream);
+    }
     return e;
 }
 

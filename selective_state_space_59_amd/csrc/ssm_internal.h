@@ -16,6 +16,11 @@ namespace ssm {
 size_t scan_workspace_bytes(const ssm_scan_args_t &a);
 // Scan: enqueue the kernels.  a.batch, a.seqlen > 0.
 hipError_t launch_scan_fwd(const ssm_scan_args_t &a, hipStream_t stream);
+// Scan checkpoints for the backward: the state entering every 16-step block,
+// [ceil(L / 16)][B][D][16] fp32 at `ckpt` (a.dstate == 16), from a.x, a.delta,
+// a.A, a.Bm, a.h0, the delta bias/softplus and the conv prologue; no outputs
+// (a.y, a.z, a.Dskip, a.h_final and a.workspace are not used).  a.batch, a.seqlen > 0.
+hipError_t launch_scan_ckpt(const ssm_scan_args_t &a, float *ckpt, hipStream_t stream);
 
 // Device address of the no-allocation scan's scratch array
 // (SSM_NOALLOC_SCRATCH_BYTES, 256-aligned) on the device of `stream`.
