@@ -77,10 +77,11 @@ __device__ __forceinline__ void sfor(F &&f) {
     sfor_impl(f, std::make_integer_sequence<int, N>{});
 }
 
-// Value of lane K of this lane's 16-lane row.
+// Value of lane K of this lane's 16-lane row (row_newbcast: every lane has a
+// source, so no old value is needed and bound_ctrl lets the compiler skip one).
 template <int K>
 __device__ __forceinline__ float bcast_row(float v) {
-    return __builtin_amdgcn_update_dpp(0.0f, v, 0x150 + K, 0xf, 0xf, false);
+    return __builtin_amdgcn_update_dpp(0.0f, v, 0x150 + K, 0xf, 0xf, true);
 }
 
 // phi(z) = (e^z - 1)/z and psi(z) = phi'(z) = (e^z - phi(z))/z given e = e^z
@@ -407,8 +408,11 @@ __device__ __forceinline__ void bwd_body(const BwdParams &p, const LaneB &l, flo
                     // d B_bar / dA = B (dt e - dt phi) / A: no psi where |A| >= 1/16.  The
                     // difference cancels for small dt A, but the term is then small
                     // next to dt e h (its error is ~1 ulp of B u / A, A >= 1/16).
-                    accA = __builtin_fmaf(dtk * e, __builtin_fmaf(xb, ia, dabar), accA);
-                    accA = __builtin_fmaf(-(xb * dtph), ia, accA);
+                    // dL/dA = dt e (dabar + xb / A) - xb dtph / A
+                    //       = (dt pdt - xb dtph) / A,  as pdt = e (dabar A + xb):
+                    // summed here without the 1/A, which the end applies once.
+                    accA = __builtin_fmaf(dtk, pdt[kk], accA);
+                    accA = __builtin_fmaf(-xb, dtph, accA);
                 } else {
                     const float zz = dtk * a, r = hw_rcp(zz);
                     const float ph = (e - 1.0f) * r;  // phi where |zz| >= 1/4 (psi's series covers the rest)
@@ -467,7 +471,7 @@ __device__ __forceinline__ void bwd_body(const BwdParams &p, const LaneB &l, flo
     }
     if (l.valid) {
         if (p.dh0) p.dh0[(l.b * p.D + l.d) * kRowN + n] = lam;
-        p.partA[(l.b * p.D + l.d) * kRowN + n] = accA;
+        p.partA[(l.b * p.D + l.d) * kRowN + n] = FAST ? accA * ia : accA;
     }
     // per-channel sums over the row's own steps
 #pragma unroll

@@ -126,7 +126,8 @@ __device__ __forceinline__ void static_for(F &&f) {
 // Value of lane K of this lane's 16-lane row (DPP row_newbcast).
 template <int K>
 __device__ __forceinline__ float row_bcast(float v) {
-    return __builtin_amdgcn_update_dpp(0.0f, v, 0x150 + K, 0xf, 0xf, false);
+    // row_newbcast: every lane has a source, so no old value is needed
+    return __builtin_amdgcn_update_dpp(0.0f, v, 0x150 + K, 0xf, 0xf, true);
 }
 // Lane n receives `cur` of lane n-K of its row, or `prev` of lane n-K+16
 // when n < K (the previous block's tail): the x history of the conv.
