@@ -801,6 +801,11 @@ __device__ __forceinline__ void wave_barrier() {
     asm volatile("s_waitcnt lgkmcnt(" SSM_STR(SSM_PART_READ_OPS) ")\n\ts_barrier" ::: "memory");
 }
 
+// Kernel variants (a template argument): the whole rows of a launch; a
+// sequence segment's first pass (also recording what the combine needs); the
+// backward's checkpoints (the state entering every block, no outputs).
+constexpr int kWhole = 0, kSegPass = 1, kCkptPass = 2;
+
 // Per-wave constants of the matrix-core products.
 template <typename IO>
 struct WaveOps {
@@ -833,7 +838,7 @@ __device__ __forceinline__ void block_iter(const ScanKernelParams &p, const Span
                                            const Duty &du, int j, int s_run, Fetch<VEC> &f,
                                            BOp<IO, kBuMfma<IO, CONV, VEC>> &bop, Carry &cy) {
     constexpr bool MF = kBuMfma<IO, CONV, VEC>;
-    constexpr bool STATS = KIND == 1, CKPT = KIND == 2;
+    constexpr bool STATS = KIND == kSegPass, CKPT = KIND == kCkptPass;
     constexpr int es = sizeof(typename IO::storage);
     const int tid = threadIdx.x, nthreads = blockDim.x;
     const int ci = 4 * wave + c;
@@ -986,7 +991,7 @@ template <typename IO, bool CONV, bool VEC, bool FAST, int KIND>
 __device__ __forceinline__ void scan_tiles_body(const ScanKernelParams &p, const Span &sp, const Geo &geo,
                                                 const Tiles &T, char *lds, int64_t b, int wave,
                                                 int c, int n, const LaneConst &k, Carry &cy) {
-    constexpr bool STATS = KIND == 1, CKPT = KIND == 2;
+    constexpr bool STATS = KIND == kSegPass, CKPT = KIND == kCkptPass;
     const int tid = threadIdx.x, nthreads = blockDim.x;
     const int lane = tid & 63;
     const int ci = 4 * wave + c;
@@ -1107,7 +1112,7 @@ template <typename IO, bool CONV, bool VEC, int KIND>
 __global__ __launch_bounds__(256 * kWavesPerSimd<VEC>)
 __attribute__((amdgpu_waves_per_eu(kWavesPerSimd<VEC>, 8)))
 void scan_tiles_kernel(ScanKernelParams p) {
-    constexpr bool STATS = KIND == 1;
+    constexpr bool STATS = KIND == kSegPass;
     extern __shared__ __attribute__((aligned(16))) char lds[];
     constexpr int es = sizeof(typename IO::storage);
     const int W = blockDim.x / 64;
@@ -1337,19 +1342,19 @@ hipError_t launch_typed(const ScanKernelParams &p, int W, hipStream_t stream) {
     const size_t lds = tile_lds_bytes<IO>(W);
     if (p.mode == 1) {
         if (p.K > 0)
-            scan_tiles_kernel<IO, true, VEC, 1><<<grid, 64 * W, lds, stream>>>(p);
+            scan_tiles_kernel<IO, true, VEC, kSegPass><<<grid, 64 * W, lds, stream>>>(p);
         else
-            scan_tiles_kernel<IO, false, VEC, 1><<<grid, 64 * W, lds, stream>>>(p);
+            scan_tiles_kernel<IO, false, VEC, kSegPass><<<grid, 64 * W, lds, stream>>>(p);
     } else if (p.ckpt) {
         if (p.K > 0)
-            scan_tiles_kernel<IO, true, VEC, 2><<<grid, 64 * W, lds, stream>>>(p);
+            scan_tiles_kernel<IO, true, VEC, kCkptPass><<<grid, 64 * W, lds, stream>>>(p);
         else
-            scan_tiles_kernel<IO, false, VEC, 2><<<grid, 64 * W, lds, stream>>>(p);
+            scan_tiles_kernel<IO, false, VEC, kCkptPass><<<grid, 64 * W, lds, stream>>>(p);
     } else {
         if (p.K > 0)
-            scan_tiles_kernel<IO, true, VEC, 0><<<grid, 64 * W, lds, stream>>>(p);
+            scan_tiles_kernel<IO, true, VEC, kWhole><<<grid, 64 * W, lds, stream>>>(p);
         else
-            scan_tiles_kernel<IO, false, VEC, 0><<<grid, 64 * W, lds, stream>>>(p);
+            scan_tiles_kernel<IO, false, VEC, kWhole><<<grid, 64 * W, lds, stream>>>(p);
     }
     return hipGetLastError();
 }
