@@ -63,7 +63,7 @@
 extern "C" {
 #endif
 
-#define SSM_ABI_VERSION 9
+#define SSM_ABI_VERSION 10
 #define SSM_MAX_DSTATE 16 /* largest N the kernels hold in registers */
 #define SSM_MAX_CONV_K 4  /* largest conv1d kernel width */
 
@@ -137,7 +137,24 @@ typedef struct ssm_scan_args {
     const void *conv_state_in; /* (B,K-1,D) io_dtype, or NULL (= 0); only with conv_k > 0 */
     void *conv_state_out;   /* (B,K-1,D) io_dtype output, or NULL; only with conv_k > 0;
                                may be exactly conv_state_in (updated in place)    */
+    float *checkpoints;     /* (ceil(L/SSM_SCAN_BLOCK), B, D, SSM_MAX_DSTATE) fp32
+                               output, or NULL: see below                         */
 } ssm_scan_args_t;
+
+/*
+ * Checkpoints (for training: the forward hands them to the backward, which
+ * then does not recompute them).  checkpoints[j][b][d][n] is the state
+ * h[b,d,n] entering time step SSM_SCAN_BLOCK * j (the state after step
+ * SSM_SCAN_BLOCK * j - 1, or h0 for j = 0), for n < N; entries n >= N are 0.
+ * Where the scan splits a long sequence into segments run at the same time,
+ * each segment but the first is scanned from a zero state and its first
+ * blocks again from its true entering state, up to the block after which
+ * exp(A times the segment's sum of dt) is below 2^-160 for every entry; the
+ * states from there on are the zero-start ones, which differ from the true
+ * states by that factor times the entering state.  Must not overlap any
+ * other argument or the workspace.
+ */
+#define SSM_SCAN_BLOCK 16
 
 /*
  * Bytes of device workspace ssm_selective_scan_fwd needs for these sizes and
@@ -288,6 +305,11 @@ typedef struct ssm_scan_bwd_args {
                                   NULL (= 0); only with conv_k > 1          */
     void *dconv_state_in;   /* (B,K-1,D) io_dtype output: its gradient, or NULL;
                                only with conv_k > 1                            */
+    const float *checkpoints; /* (ceil(L/SSM_SCAN_BLOCK), B, D, SSM_MAX_DSTATE) fp32: the
+                                 checkpoints an ssm_selective_scan_fwd call wrote for the
+                                 same x, delta, A, Bm, h0, delta options, conv weights
+                                 and conv_state_in; or NULL, and the backward computes
+                                 them (in its workspace, which is then larger) */
 } ssm_scan_bwd_args_t;
 
 /* Workspace bytes ssm_selective_scan_bwd needs ((size_t)-1 for invalid sizes). */

@@ -751,7 +751,8 @@ BwdLayout bwd_layout(const ssm_scan_bwd_args_t &a) {
     BwdLayout q;
     q.G = (a.dim + kChB - 1) / kChB;
     q.nb = (a.seqlen + kStep - 1) / kStep;
-    q.ckpt = r256((size_t)(q.nb * a.batch * a.dim * kRowN) * sizeof(float));
+    // (none when the caller passes the forward's checkpoints)
+    q.ckpt = a.checkpoints ? 0 : r256((size_t)(q.nb * a.batch * a.dim * kRowN) * sizeof(float));
     q.partBC = r256((size_t)(2 * a.batch * q.G * a.seqlen * kRowN) * sizeof(float));
     q.partA = r256((size_t)(a.batch * a.dim * kRowN) * sizeof(float));
     q.partD = r256((size_t)(a.batch * a.dim) * sizeof(float));
@@ -787,7 +788,7 @@ hipError_t launch_bwd_typed(const BwdParams &p, const ssm_scan_bwd_args_t &a, fl
     f.conv_b = p.conv_b;
     f.h0 = p.h0;
     f.conv_state_in = p.cs_in;
-    hipError_t e = launch_scan_ckpt(f, p.ckpt, stream);
+    hipError_t e = a.checkpoints ? hipSuccess : launch_scan_ckpt(f, p.ckpt, stream);
     if (e != hipSuccess) return e;
     const size_t lds = (size_t)(kWavesB * (2 * kTrWave + kRedWave)) * sizeof(float);
     // B and C staged in LDS: bf16 rows read as 4-byte pairs.
@@ -922,7 +923,7 @@ hipError_t launch_scan_bwd16(const ssm_scan_bwd_args_t &a, char *ws, hipStream_t
     p.ddelta = a.ddelta;
     p.dz = a.dz;
     p.dh0 = a.dh0;
-    p.ckpt = reinterpret_cast<float *>(ws);
+    p.ckpt = a.checkpoints ? const_cast<float *>(a.checkpoints) : reinterpret_cast<float *>(ws);
     p.partBC = reinterpret_cast<float *>(ws + q.ckpt);
     p.partA = reinterpret_cast<float *>(ws + q.ckpt + q.partBC);
     p.partD = reinterpret_cast<float *>(ws + q.ckpt + q.partBC + q.partA);

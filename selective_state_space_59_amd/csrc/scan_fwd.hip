@@ -90,9 +90,11 @@ struct ScanKernelParams {
     const void *cs_in;  // conv state (B, K-1, D): x before row 0, or NULL (= 0)
     void *y;
     float *h_out;       // state after row t_end - 1, or NULL
-    // Checkpoint launches (the backward's first pass) write the state entering
-    // every 16-step block, [nblocks][B][D][16] (entry n < N at n), and no outputs.
+    // The state entering every 16-step block, [nblocks][B][D][16] (entry
+    // n < N at n), or NULL.  ckpt_only launches (the backward's first pass)
+    // write these and no outputs.
     float *ckpt;
+    int ckpt_only;
     // Sequence segments (see launch_segmented): mode 0 scans [t_begin, t_end)
     // as one piece; mode 1 scans every segment of seg_len rows from a zero
     // state (the first from h_in) and records its end state, its sum of dt
@@ -852,7 +854,7 @@ __device__ __forceinline__ void block_iter(const ScanKernelParams &p, const Span
     // (A checkpoint launch reads no states back before its barrier.)
     if constexpr (VEC && !CKPT) wave_barrier();
     else __syncthreads();
-    if constexpr (CKPT) {
+    if (CKPT || p.ckpt) {
         // the state entering this block (the fast form carries A h)
         if (k.dvalid)
             p.ckpt[(sp.t0 / kTB + j) * (p.B * p.D * kRow) + k.ckpt] = FAST ? cy.h * k.ia : cy.h;
@@ -1345,7 +1347,7 @@ hipError_t launch_typed(const ScanKernelParams &p, int W, hipStream_t stream) {
             scan_tiles_kernel<IO, true, VEC, kSegPass><<<grid, 64 * W, lds, stream>>>(p);
         else
             scan_tiles_kernel<IO, false, VEC, kSegPass><<<grid, 64 * W, lds, stream>>>(p);
-    } else if (p.ckpt) {
+    } else if (p.ckpt_only) {
         if (p.K > 0)
             scan_tiles_kernel<IO, true, VEC, kCkptPass><<<grid, 64 * W, lds, stream>>>(p);
         else
@@ -1467,7 +1469,8 @@ hipError_t launch_scan_fwd(const ssm_scan_args_t &a, hipStream_t stream) {
     p.conv_b = a.conv_b;
     p.cs_in = a.conv_k > 0 ? a.conv_state_in : nullptr;
     p.y = a.y;
-    p.ckpt = nullptr;
+    p.ckpt = a.checkpoints;
+    p.ckpt_only = 0;
     p.mode = 0;
     p.nseg = 1;
     p.seg_len = q.seg_len;
@@ -1537,6 +1540,7 @@ hipError_t launch_scan_ckpt(const ssm_scan_args_t &a, float *ckpt, hipStream_t s
     p.cs_in = a.conv_k > 0 ? a.conv_state_in : nullptr;
     p.y = nullptr;
     p.ckpt = ckpt;
+    p.ckpt_only = 1;
     p.mode = 0;
     p.nseg = 1;
     p.seg_len = q.seg_len;

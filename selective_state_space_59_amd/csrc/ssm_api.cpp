@@ -136,7 +136,8 @@ ssm_status_t scan_fwd(const ssm_scan_args_t *a, void *stream, bool noalloc) {
                              a->conv_state_out};
     for (const void *p : io_ptrs)
         if (!aligned(p, es)) return fail(SSM_ERR_ALIGN, "an io_dtype pointer is not %lld-byte aligned", (long long)es);
-    const void *f_ptrs[] = {a->A, a->Dskip, a->delta_bias, a->conv_w, a->conv_b, a->h0, a->h_final};
+    const void *f_ptrs[] = {a->A, a->Dskip, a->delta_bias, a->conv_w, a->conv_b, a->h0, a->h_final,
+                            a->checkpoints};
     for (const void *p : f_ptrs)
         if (!aligned(p, 4)) return fail(SSM_ERR_ALIGN, "an fp32 pointer is not 4-byte aligned");
 
@@ -164,6 +165,14 @@ ssm_status_t scan_fwd(const ssm_scan_args_t *a, void *stream, bool noalloc) {
     }
     if (overlaps(y, hf)) return fail(SSM_ERR_ALIAS, "y overlaps h_final");
     if (overlaps(cso, y) || overlaps(cso, hf)) return fail(SSM_ERR_ALIAS, "conv_state_out overlaps an output");
+    const int64_t nblk = (L + SSM_SCAN_BLOCK - 1) / SSM_SCAN_BLOCK;
+    if (a->checkpoints && !mul_ok(nblk, B * D, SSM_MAX_DSTATE))
+        return fail(SSM_ERR_BAD_SHAPE, "checkpoint sizes overflow");
+    const Range ck = range(a->checkpoints, nblk * B * D * SSM_MAX_DSTATE, 4, "checkpoints");
+    for (const Range &r : inputs)
+        if (overlaps(ck, r)) return fail(SSM_ERR_ALIAS, "checkpoints overlap %s", r.name);
+    if (overlaps(ck, y) || overlaps(ck, hf) || overlaps(ck, cso))
+        return fail(SSM_ERR_ALIAS, "checkpoints overlap an output");
 
     const size_t need = work ? ssm::scan_workspace_bytes(*a) : 0;
     if (noalloc) {
@@ -181,7 +190,7 @@ ssm_status_t scan_fwd(const ssm_scan_args_t *a, void *stream, bool noalloc) {
         const Range ws = range(a->workspace, (int64_t)need, 1, "workspace");
         for (const Range &r : inputs)
             if (overlaps(ws, r)) return fail(SSM_ERR_ALIAS, "workspace overlaps %s", r.name);
-        if (overlaps(ws, y) || overlaps(ws, hf) || overlaps(ws, cso))
+        if (overlaps(ws, y) || overlaps(ws, hf) || overlaps(ws, cso) || overlaps(ws, ck))
             return fail(SSM_ERR_ALIAS, "workspace overlaps an output");
     }
 
@@ -348,7 +357,8 @@ static ssm_status_t check_bwd(const ssm_scan_bwd_args_t *a, size_t *need_out) {
     for (const void *p : io_ptrs)
         if (!aligned(p, es)) return fail(SSM_ERR_ALIGN, "an io_dtype pointer is not %lld-byte aligned", (long long)es);
     const void *f_ptrs[] = {a->A, a->Dskip, a->delta_bias, a->h0, a->dh_final, a->dA, a->dBm, a->dCm,
-                            a->dDskip, a->ddelta_bias, a->dh0, a->conv_w, a->conv_b, a->dconv_w, a->dconv_b};
+                            a->dDskip, a->ddelta_bias, a->dh0, a->conv_w, a->conv_b, a->dconv_w, a->dconv_b,
+                            a->checkpoints};
     for (const void *p : f_ptrs)
         if (!aligned(p, 4)) return fail(SSM_ERR_ALIGN, "an fp32 pointer is not 4-byte aligned");
     const Range inputs[] = {
@@ -360,6 +370,8 @@ static ssm_status_t check_bwd(const ssm_scan_bwd_args_t *a, size_t *need_out) {
         range(a->dh_final, B * D * N, 4, "dh_final"), range(a->conv_w, D * K, 4, "conv_w"),
         range(a->conv_b, D, 4, "conv_b"),
         range(a->conv_state_in, B * (K > 0 ? K - 1 : 0) * D, es, "conv_state_in"),
+        range(a->checkpoints, ((L + SSM_SCAN_BLOCK - 1) / SSM_SCAN_BLOCK) * B * D * SSM_MAX_DSTATE, 4,
+              "checkpoints"),
     };
     const Range outputs[] = {
         range(a->dx, B * L * D, es, "dx"),        range(a->ddelta, B * L * D, es, "ddelta"),

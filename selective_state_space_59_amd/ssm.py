@@ -55,7 +55,7 @@ class ScanArgs(ctypes.Structure):
                 ("A", _P), ("Dskip", _P), ("delta_bias", _P), ("conv_w", _P), ("conv_b", _P),
                 ("h0", _P), ("y", _P), ("h_final", _P),
                 ("workspace", _P), ("workspace_bytes", ctypes.c_size_t),
-                ("conv_state_in", _P), ("conv_state_out", _P)]
+                ("conv_state_in", _P), ("conv_state_out", _P), ("checkpoints", _P)]
 
 
 class StateUpdateArgs(ctypes.Structure):
@@ -77,7 +77,7 @@ class ScanBwdArgs(ctypes.Structure):
                 ("dx", _P), ("ddelta", _P), ("dz", _P), ("dA", _P), ("dBm", _P), ("dCm", _P),
                 ("dDskip", _P), ("ddelta_bias", _P), ("dconv_w", _P), ("dconv_b", _P),
                 ("dh0", _P), ("workspace", _P), ("workspace_bytes", ctypes.c_size_t),
-                ("conv_state_in", _P), ("dconv_state_in", _P)]
+                ("conv_state_in", _P), ("dconv_state_in", _P), ("checkpoints", _P)]
 
 
 class BlockDims(ctypes.Structure):
@@ -218,7 +218,7 @@ def _stream(device: torch.device) -> int:
 
 
 def _scan_args(x, delta, A, Bm, Cm, Dskip, z, delta_bias, delta_softplus, conv_w, conv_b, h0,
-               y, h_final, conv_state_in=None, conv_state_out=None):
+               y, h_final, conv_state_in=None, conv_state_out=None, checkpoints=None):
     if not isinstance(x, torch.Tensor) or x.dim() != 3:
         raise ValueError("x must be a (B, L, D) tensor")
     if x.device.type != "cuda":
@@ -251,14 +251,25 @@ def _scan_args(x, delta, A, Bm, Cm, Dskip, z, delta_bias, delta_softplus, conv_w
         raise ValueError("a conv state needs conv_w")
     _opt(conv_state_in, "conv_state_in", (Bsz, max(K - 1, 0), D), io, dev)
     _opt(conv_state_out, "conv_state_out", (Bsz, max(K - 1, 0), D), io, dev)
+    _opt(checkpoints, "checkpoints", checkpoint_shape(Bsz, L, D), torch.float32, dev)
     a = ScanArgs(batch=Bsz, seqlen=L, dim=D, dstate=N, io_dtype=_io_code(io),
                  delta_softplus=int(bool(delta_softplus)), conv_k=K,
                  x=_ptr(x), delta=_ptr(delta), Bm=_ptr(Bm), Cm=_ptr(Cm), z=_ptr(z), A=_ptr(A),
                  Dskip=_ptr(Dskip), delta_bias=_ptr(delta_bias), conv_w=_ptr(conv_w),
                  conv_b=_ptr(conv_b), h0=_ptr(h0), y=_ptr(y), h_final=_ptr(h_final),
                  workspace=None, workspace_bytes=0, conv_state_in=_ptr(conv_state_in),
-                 conv_state_out=_ptr(conv_state_out))
+                 conv_state_out=_ptr(conv_state_out), checkpoints=_ptr(checkpoints))
     return a, dev
+
+
+SCAN_BLOCK = 16  # SSM_SCAN_BLOCK
+MAX_DSTATE = 16  # SSM_MAX_DSTATE
+
+
+def checkpoint_shape(batch: int, seqlen: int, dim: int) -> tuple:
+    """Shape of the fp32 checkpoint tensor a forward writes for the backward: the state
+    entering every SCAN_BLOCK-step block, (ceil(L / SCAN_BLOCK), B, D, MAX_DSTATE)."""
+    return ((seqlen + SCAN_BLOCK - 1) // SCAN_BLOCK, batch, dim, MAX_DSTATE)
 
 
 _ws_cache = {}
@@ -308,10 +319,13 @@ def selective_scan_fwd(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, Bm
                        workspace: Optional[torch.Tensor] = None,
                        conv_state_in: Optional[torch.Tensor] = None,
                        conv_state_out: Optional[torch.Tensor] = None,
-                       return_conv_state: bool = False):
+                       return_conv_state: bool = False,
+                       checkpoints: Optional[torch.Tensor] = None):
     """ssm_selective_scan_fwd.  Returns (y, h_final or None), or with
     return_conv_state (or a conv_state_out given) (y, h_final or None,
-    conv_state_out); conv states are (B, K-1, D) in x's dtype."""
+    conv_state_out); conv states are (B, K-1, D) in x's dtype.  A float32 tensor
+    `checkpoints` of checkpoint_shape(B, L, D) also receives the state entering every
+    SCAN_BLOCK-step block, for selective_scan_bwd(checkpoints=...)."""
     if y is None:
         y = torch.empty_like(x)
     if return_final_state and h_final is None:
@@ -324,7 +338,7 @@ def selective_scan_fwd(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, Bm
         conv_state_out = torch.empty(x.shape[0], max(conv_w.shape[1] - 1, 0), x.shape[2],
                                      device=x.device, dtype=x.dtype)
     a, dev = _scan_args(x, delta, A, Bm, Cm, Dskip, z, delta_bias, delta_softplus, conv_w,
-                        conv_b, h0, y, h_final, conv_state_in, conv_state_out)
+                        conv_b, h0, y, h_final, conv_state_in, conv_state_out, checkpoints)
     need = lib().ssm_selective_scan_workspace_size(ctypes.byref(a))
     if need == ctypes.c_size_t(-1).value:
         _check(lib().ssm_selective_scan_fwd(ctypes.byref(a), None), "ssm_selective_scan_fwd")
@@ -473,14 +487,18 @@ def selective_scan_bwd(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, Bm
                        conv_w: Optional[torch.Tensor] = None,
                        conv_b: Optional[torch.Tensor] = None,
                        workspace: Optional[torch.Tensor] = None,
-                       conv_state_in: Optional[torch.Tensor] = None) -> dict:
-    """ssm_selective_scan_bwd: gradients of the scan (1 <= N <= 16).
+                       conv_state_in: Optional[torch.Tensor] = None,
+                       checkpoints: Optional[torch.Tensor] = None) -> dict:
+    """ssm_selective_scan_bwd: gradients of the scan (1 <= N <= 16).  `checkpoints` are
+    the ones a selective_scan_fwd call with the same inputs wrote (else the backward
+    recomputes them).
 
     Returns a dict with dx, ddelta (x's dtype), dA, dBm, dCm (float32) and, for the
     optional inputs given, dz, dDskip, ddelta_bias, dh0, dconv_w, dconv_b and
     dconv_state_in (x's dtype, the gradient of the conv state entering the sequence)."""
     a, dev = _scan_args(x, delta, A, Bm, Cm, Dskip, z, delta_bias, delta_softplus, conv_w, conv_b,
-                        h0, torch.empty_like(x), None, conv_state_in=conv_state_in)
+                        h0, torch.empty_like(x), None, conv_state_in=conv_state_in,
+                        checkpoints=checkpoints)
     Bsz, L, D = x.shape
     N = A.shape[1]
     io = x.dtype
@@ -510,7 +528,7 @@ def selective_scan_bwd(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, Bm
                     dy=_ptr(dy), dh_final=_ptr(dh_final), dx=g("dx"), ddelta=g("ddelta"),
                     dz=g("dz"), dA=g("dA"), dBm=g("dBm"), dCm=g("dCm"), dDskip=g("dDskip"),
                     ddelta_bias=g("ddelta_bias"), dh0=g("dh0"), conv_state_in=a.conv_state_in,
-                    dconv_state_in=g("dconv_state_in"))
+                    dconv_state_in=g("dconv_state_in"), checkpoints=_ptr(checkpoints))
     need = lib().ssm_selective_scan_bwd_workspace_size(ctypes.byref(b))
     if need == ctypes.c_size_t(-1).value:
         _check(lib().ssm_selective_scan_bwd(ctypes.byref(b), None), "ssm_selective_scan_bwd")

@@ -275,6 +275,26 @@ def test_scan_workspace_checks():
     assert run_scan(a) == ssm.SSM_ERR_WORKSPACE
 
 
+# Checkpoints (the forward -> backward handoff): fp32, aligned, overlapping
+# nothing; with them the backward's workspace is smaller (it skips its own).
+@pytest.mark.parametrize("kw,status", [
+    (dict(checkpoints=addr(12, 2)), ssm.SSM_ERR_ALIGN),
+    (dict(checkpoints=addr(0, 64)), ssm.SSM_ERR_ALIAS),      # inside x
+    (dict(checkpoints=addr(7, 64)), ssm.SSM_ERR_ALIAS),      # inside y
+    (dict(checkpoints=addr(8)), ssm.SSM_ERR_ALIAS),          # == h_final
+    # inside the workspace (a long row is cut into segments, which need one)
+    (dict(checkpoints=addr(9, 256), batch=1, seqlen=20000), ssm.SSM_ERR_ALIAS),
+    (dict(checkpoints=addr(12), seqlen=1 << 60), ssm.SSM_ERR_BAD_SHAPE),
+])
+def test_scan_checkpoint_checks(kw, status):
+    assert run_scan(scan_args(**kw)) == status
+
+
+def test_scan_checkpoints_pass_the_checks():
+    assert run_scan(scan_args(checkpoints=addr(12))) == ssm.SSM_ERR_HIP
+    assert ssm.checkpoint_shape(2, 33, 64) == (3, 2, 64, 16)
+
+
 # ----------------------------------------------------------------- conv checks
 def run_conv(B=2, L=8, D=64, K=4, dt=ssm.SSM_BF16, x=addr(0), w=addr(1), b=addr(2), u=addr(3)):
     return ssm.lib().ssm_causal_conv1d_silu(B, L, D, K, dt, x, w, b, u, None)
@@ -435,6 +455,28 @@ def test_bwd_small_dstate_passes_the_checks_and_needs_more_workspace(N):
 ])
 def test_bwd_rejects_bad_arguments(field, value, status):
     assert run_bwd(bwd_args(**{field: value})) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(checkpoints=addr(20, 2)), ssm.SSM_ERR_ALIGN),
+    (dict(checkpoints=addr(8, 64)), ssm.SSM_ERR_ALIAS),      # inside dx
+    (dict(checkpoints=addr(15, 256)), ssm.SSM_ERR_ALIAS),    # inside the workspace
+])
+def test_bwd_checkpoint_checks(kw, status):
+    assert run_bwd(bwd_args(**kw)) == status
+
+
+@pytest.mark.parametrize("N", [16, 5])
+def test_bwd_with_checkpoints_needs_less_workspace(N):
+    L = ssm.lib()
+    plain = bwd_args(dstate=N, workspace=None, workspace_bytes=0)
+    given = bwd_args(dstate=N, workspace=None, workspace_bytes=0, checkpoints=addr(20))
+    n0 = L.ssm_selective_scan_bwd_workspace_size(ctypes.byref(plain))
+    n1 = L.ssm_selective_scan_bwd_workspace_size(ctypes.byref(given))
+    assert n1 < n0
+    # the checkpoints of B=2, L=8, D=64: one block of 2 * 64 * 16 fp32 (256-rounded)
+    assert n0 - n1 >= 2 * 64 * 16 * 4
+    assert run_bwd(bwd_args(dstate=N, checkpoints=addr(20))) == ssm.SSM_ERR_HIP
 
 
 def test_bwd_dz_without_z_and_empty_batch():
