@@ -58,14 +58,21 @@ struct ConvLane {
     float tap, win, bias;
 };
 // `win_b` is the window of batch row b (the (K-1, D) slab at b (K-1) D); the
-// offsets within it, and within conv_w, fit 32 bits (checked at launch).
+// offsets within it, and within conv_w, fit 32 bits (checked at launch).  The
+// window is touched once per step, like the state: non-temporal loads and
+// stores.
 template <typename IO>
 __device__ __forceinline__ ConvLane load_conv(const UpdateParams &p, const char *win_b, int d, int j) {
     constexpr int es = sizeof(typename IO::storage);
     const int r = p.K - 4 + j;  // tap index = window row of this lane
     ConvLane c;
     c.tap = r >= 0 ? p.conv_w[d * p.K + r] : 0.0f;
-    c.win = (j < 3 && r >= 0) ? load_io<IO>(win_b + (uint32_t)(r * (int)p.D + d) * es, 0) : 0.0f;
+    c.win = 0.0f;
+    if (j < 3 && r >= 0) {
+        const char *q = win_b + (uint32_t)(r * (int)p.D + d) * es;
+        if constexpr (es == 2) c.win = __uint_as_float((uint32_t)__builtin_nontemporal_load(reinterpret_cast<const uint16_t *>(q)) << 16);
+        else c.win = __builtin_nontemporal_load(reinterpret_cast<const float *>(q));
+    }
     c.bias = (j == 3 && p.conv_b) ? p.conv_b[d] : 0.0f;
     return c;
 }
@@ -84,7 +91,11 @@ template <typename IO>
 __device__ __forceinline__ void store_window(const UpdateParams &p, char *win_b, int d, int j, float nv) {
     constexpr int es = sizeof(typename IO::storage);
     const int r = p.K - 4 + j;
-    if (j < 3 && r >= 0) store_io<IO>(win_b + (uint32_t)(r * (int)p.D + d) * es, 0, nv);
+    if (j < 3 && r >= 0) {
+        char *q = win_b + (uint32_t)(r * (int)p.D + d) * es;
+        if constexpr (es == 2) __builtin_nontemporal_store(f32_to_bf16_bits(nv), reinterpret_cast<uint16_t *>(q));
+        else __builtin_nontemporal_store(nv, reinterpret_cast<float *>(q));
+    }
 }
 
 // phi(z) = (e^z - 1) / z given e = e^z.
