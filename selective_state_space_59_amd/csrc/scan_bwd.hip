@@ -197,7 +197,7 @@ __device__ __forceinline__ void own_finish(const BwdParams &p, const OwnRaw &r, 
         u = r.wm ? silu(c) : 0.0f;
     }
     const float raw = r.wm ? bits_f32<IO>(r.draw) : 0.0f;
-    dt = p.softplus ? softplus(raw + bias) : raw;
+    dt = p.softplus ? softplus_fast(raw + bias) : raw;  // the forward's softplus, so the states match
     if (!r.wm) dt = 0.0f;
 }
 
@@ -235,20 +235,16 @@ __device__ __forceinline__ void request_block(const BwdParams &p, const LaneB &l
     r.h = p.ckpt[((jb * p.B + l.b) * p.D + dc) * kRowN + l.n];
 }
 
-// bf16 B (or C) tiles in LDS are [entry n][step k] with rows 40 bytes apart:
-// the 16 lanes of a row read 8 bytes each from distinct banks.
-constexpr int kBcRow = 40;
-// Entry n's 16 steps of tile `tensor` (of two consecutive tiles), widened.
-__device__ __forceinline__ void bc_read(const char *bcl, int tensor, int n, float (&v)[kStep]) {
-    const uint2 *row = reinterpret_cast<const uint2 *>(bcl + (tensor * kRowN + n) * kBcRow);
-#pragma unroll
-    for (int q = 0; q < kStep / 4; ++q) {
-        const uint2 d = row[q];
-        v[4 * q] = __uint_as_float(d.x << 16);
-        v[4 * q + 1] = __uint_as_float(d.x & 0xffff0000u);
-        v[4 * q + 2] = __uint_as_float(d.y << 16);
-        v[4 * q + 3] = __uint_as_float(d.y & 0xffff0000u);
-    }
+// B (or C) tiles in LDS are fp32 [entry n][step k], rows 80 bytes apart
+// (16-byte aligned; see the staging below).
+constexpr int kBcRow = 80;
+// Steps 4 g .. 4 g + 3 of entry n of tile `tensor` (of two consecutive tiles).
+__device__ __forceinline__ void bc_quad(const char *bcl, int tensor, int n, int g, float (&v)[4]) {
+    const float4 q = reinterpret_cast<const float4 *>(bcl + (tensor * kRowN + n) * kBcRow)[g];
+    v[0] = q.x;
+    v[1] = q.y;
+    v[2] = q.z;
+    v[3] = q.w;
 }
 
 typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
@@ -275,11 +271,13 @@ __device__ __forceinline__ float sum_channels4(const float (&v)[4]) {
 }
 
 // The B and C rows of a block, staged in LDS for the whole workgroup (bf16
-// I/O): [tensor][entry n][step k] as bf16, rows 40 bytes apart so that the 16
-// lanes of a row read their 8 bytes from distinct banks.  Threads 0..255
-// fetch one 4-byte pair of entries each (tensor q / 128, step (q % 128) / 8,
-// entries 2 (q % 8), +1) a block ahead and store it during the reduction.
+// I/O) and widened there once: [tensor][entry n][step k] as fp32, so that the
+// lanes read their steps four at a time with no conversion, in the forward
+// over the block and again in the adjoint.  Threads 0..255 fetch one 4-byte
+// pair of entries each (tensor q / 128, step (q % 128) / 8, entries
+// 2 (q % 8), +1) a block ahead and store it during the reduction.
 constexpr int kBcLdsBytes = 2 * kRowN * kBcRow;
+static_assert(kWavesB * (2 * kTrWave + kRedWave) * 4 + kBcLdsBytes <= 160 * 1024, "LDS of one workgroup");
 constexpr int kBcFetchers = 2 * kStep * kRowN / 2;
 __device__ __forceinline__ uint32_t bc_fetch(const BwdParams &p, int64_t b, int64_t jb, int q) {
     const int tensor = q >> 7, s = (q & 127) >> 3, part = q & 7;
@@ -290,9 +288,9 @@ __device__ __forceinline__ uint32_t bc_fetch(const BwdParams &p, int64_t b, int6
 }
 __device__ __forceinline__ void bc_store(char *bcl, uint32_t v, int q) {
     const int tensor = q >> 7, s = (q & 127) >> 3, part = q & 7;
-    uint16_t *col = reinterpret_cast<uint16_t *>(bcl + (tensor * kRowN + 2 * part) * kBcRow) + s;
-    col[0] = (uint16_t)(v & 0xffffu);
-    col[kBcRow / 2] = (uint16_t)(v >> 16);
+    float *col = reinterpret_cast<float *>(bcl + (tensor * kRowN + 2 * part) * kBcRow) + s;
+    col[0] = __uint_as_float(v << 16);
+    col[kBcRow / 4] = __uint_as_float(v & 0xffff0000u);
 }
 
 // Pass 2: the adjoint, blocks from last to first.
@@ -340,12 +338,14 @@ __device__ __forceinline__ void bwd_body(const BwdParams &p, const LaneB &l, flo
         const int64_t t0 = j * kStep;
         const int64_t tme = t0 + n;  // this lane's own step
         const bool live = nx.own.wm != 0;  // l.valid && tme < p.L
-        float u, dt, bv[kStep], cv[kStep];
+        // With the B and C tile staged, B and C are read from it where used
+        // (in the forward over the block and again in the adjoint), which
+        // leaves room for the 16 exp(dt A) of the forward: the adjoint reuses
+        // them.
+        float u, dt, bv[kStep], cv[kStep], ev[kStep];
         own_finish<IO, CONV>(p, nx.own, wr, cb, bias, u, dt);
         const float raw = live ? bits_f32<IO>(nx.own.draw) : 0.0f;
         if (STAGE) {
-            bc_read(bcl, 0, n, bv);
-            bc_read(bcl, 1, n, cv);
         } else {
             uint32_t rb[kStep], rc[kStep];
             load_rows_bits<IO>(p.Bm, p, l, t0, rb);
@@ -364,16 +364,32 @@ __device__ __forceinline__ void bwd_body(const BwdParams &p, const LaneB &l, flo
         // spills).
         float hp[kStep];
         float h = l.valid ? nx.h : 0.0f;
+        // B and C of steps g4 .. g4 + 3
+        auto bc_group = [&](int g4, float (&bq)[4], float (&cq)[4]) {
+            if constexpr (STAGE) {
+                bc_quad(bcl, 0, n, g4 / 4, bq);
+                bc_quad(bcl, 1, n, g4 / 4, cq);
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    bq[i] = bv[g4 + i];
+                    cq[i] = cv[g4 + i];
+                }
+            }
+        };
         sfor<kStep / 4>([&](auto G) {
             constexpr int g4 = 4 * decltype(G)::value;
-            float pk[4];
+            float pk[4], bq[4], cq[4];
+            bc_group(g4, bq, cq);
             sfor<4>([&](auto K) {
-                constexpr int k = g4 + decltype(K)::value;
+                constexpr int kk = decltype(K)::value;
+                constexpr int k = g4 + kk;
                 const float dtk = bcast_row<k>(dt), uk = bcast_row<k>(u);
                 const float e = hw_exp2(dtk * a2);
+                if constexpr (STAGE) ev[k] = e;
                 hp[k] = h;
-                h = __builtin_fmaf(e, h, dtphi<FAST>(dtk, a, ia, e) * (bv[k] * uk));
-                pk[decltype(K)::value] = cv[k] * h;  // partial read-out of step k
+                h = __builtin_fmaf(e, h, dtphi<FAST>(dtk, a, ia, e) * (bq[kk] * uk));
+                pk[kk] = cq[kk] * h;  // partial read-out of step k
             });
             *reinterpret_cast<float4 *>(my0 + g4) = make_float4(pk[0], pk[1], pk[2], pk[3]);
         });
@@ -392,14 +408,16 @@ __device__ __forceinline__ void bwd_body(const BwdParams &p, const LaneB &l, flo
         // -- adjoint over the block, last step first ---------------------------
         sfor<kStep / 4>([&](auto G) {
             constexpr int g4 = kStep - 4 - 4 * decltype(G)::value;  // 12, 8, 4, 0
-            float pdu[4], pdt[4], sb[4], sc[4];
+            float pdu[4], pdt[4], sb[4], sc[4], bq[4], cq[4];
+            bc_group(g4, bq, cq);
             sfor<4>([&](auto K) {
                 constexpr int kk = 3 - decltype(K)::value;
                 constexpr int k = g4 + kk;
                 const float gyk = bcast_row<k>(gy), uk = bcast_row<k>(u), dtk = bcast_row<k>(dt);
-                const float e = hw_exp2(dtk * a2), dtph = dtphi<FAST>(dtk, a, ia, e), bk = bv[k];
+                const float e = STAGE ? ev[k] : hw_exp2(dtk * a2);
+                const float dtph = dtphi<FAST>(dtk, a, ia, e), bk = bq[kk];
                 const float hcur = k == kStep - 1 ? h : hp[k + 1 < kStep ? k + 1 : 0];
-                const float lt = __builtin_fmaf(cv[k], gyk, lam);  // dL/dh_t
+                const float lt = __builtin_fmaf(cq[kk], gyk, lam);  // dL/dh_t
                 const float dabar = lt * hp[k], dbbar = lt * uk;
                 const float xb = dbbar * bk;  // dL/dh_t u B
                 pdu[kk] = lt * (dtph * bk);
