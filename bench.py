@@ -248,6 +248,34 @@ def bench_block(cfg, steps, warmup):
     return ms
 
 
+def cold_step_ms(step, nsteps, dev):
+    """Median time of single steps, each after evicting the caches with 1 GiB (four
+    times the last-level cache): by reading a buffer (the caches then hold clean lines,
+    as after the weight reads of the layers between two steps of one layer), and, for
+    comparison, by writing it (the caches then hold dirty lines, whose write-back lands
+    inside the timed step).  Returns (ms after the read, ms after the write)."""
+    import torch
+    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+
+    def median(evict):
+        times = []
+        for t in range(nsteps):
+            evict(t)
+            start.record()
+            step(t)
+            stop.record()
+            torch.cuda.synchronize()
+            times.append(start.elapsed_time(stop))
+        times.sort()
+        return times[len(times) // 2]
+
+    out = median(lambda t: flush.sum()), median(lambda t: flush.fill_(float(t)))
+    del flush
+    return out
+
+
 def bench_decode(cfg, reps=3, conv_k=0):
     """Decode steps of `cfg`; with conv_k, each step also runs the conv prologue on
     its (B, conv_k-1, D) window and shifts it (weights N(0, 0.5), seeded)."""
@@ -283,26 +311,32 @@ def bench_decode(cfg, reps=3, conv_k=0):
         for t in range(cfg.steps):
             step(t)
 
-    hot_ms = time_launches(run_all, reps, 1) / cfg.steps
-    # Cold: evict the last-level cache (write 1 GiB) before each timed step.
-    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
-    start = torch.cuda.Event(enable_timing=True)
-    stop = torch.cuda.Event(enable_timing=True)
-    cold = []
-    for t in range(cfg.steps):
-        flush.fill_(float(t))
-        start.record()
-        step(t)
-        stop.record()
-        torch.cuda.synchronize()
-        cold.append(start.elapsed_time(stop))
-    cold.sort()
-    cold_ms = cold[len(cold) // 2]
+    hot_loop_ms = time_launches(run_all, reps, 1)  # the whole 64-step loop, launch gaps included
+    hot_ms = hot_loop_ms / cfg.steps
+    cold_ms, cold_fill_ms = cold_step_ms(step, cfg.steps, dev)
     nbytes = decode_algorithmic_bytes(cfg.batch, cfg.dim, cfg.dstate,
                                       2 if cfg.io_dtype == torch.bfloat16 else 4, conv_k=conv_k)
-    del inp, st, ys, flush, conv, steps
+    del inp, st, ys, conv, steps
     torch.cuda.empty_cache()
-    return hot_ms, cold_ms, nbytes
+    return hot_ms, cold_ms, nbytes, hot_loop_ms, cold_fill_ms
+
+
+def copy_bandwidth(gib=4, reps=5):
+    """Achievable HBM bandwidth: a device-to-device copy of `gib` GiB (torch's copy
+    kernel), bytes read plus written per second, median of `reps` after a warm-up."""
+    import torch
+    n = gib << 28  # fp32 elements
+    src = torch.empty(n, dtype=torch.float32, device="cuda:0").fill_(1.0)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    times = []
+    for _ in range(reps):
+        times.append(time_launches(lambda _: dst.copy_(src), 1, 0))
+    times.sort()
+    ms = times[len(times) // 2]
+    del src, dst
+    torch.cuda.empty_cache()
+    return 2 * 4 * n / (ms * 1e-3) / 1e9
 
 
 def cpu_baseline(inp, cfg, min_seconds=10.0, block_rows=8192):
@@ -402,7 +436,7 @@ def ssd_step_algorithmic(cfg):
 
 def bench_ssd_step(cfg, reps=10):
     """`cfg.seqlen` decode steps of the SSD layer on a resident state: hot (steps back to
-    back, per step) and cold (the last-level cache flushed before each timed step)."""
+    back, per step) and cold (the caches evicted before each timed step, cold_step_ms)."""
     import torch
     import selective_state_space_59_amd as ssm
     from selective_state_space_59_amd import workloads as W
@@ -429,28 +463,18 @@ def bench_ssd_step(cfg, reps=10):
             step(t)
 
     hot_ms = time_launches(run_all, reps, 1) / T
-    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
-    start = torch.cuda.Event(enable_timing=True)
-    stop = torch.cuda.Event(enable_timing=True)
-    cold = []
-    for t in range(T):
-        flush.fill_(float(t))
-        start.record()
-        step(t)
-        stop.record()
-        torch.cuda.synchronize()
-        cold.append(start.elapsed_time(stop))
-    cold.sort()
-    cold_ms = cold[len(cold) // 2]
-    del s, per_step, st, ys, flush, args
+    cold_ms, cold_fill_ms = cold_step_ms(step, T, dev)
+    del s, per_step, st, ys, args
     torch.cuda.empty_cache()
-    return hot_ms, cold_ms
+    return hot_ms, cold_ms, cold_fill_ms
 
 
 def ssd_step_entry(cfg):
-    hot, cold = bench_ssd_step(cfg)
+    hot, cold, cold_fill = bench_ssd_step(cfg)
     db = ssd_step_algorithmic(cfg)
     return dict(hot_ms_per_step=round(hot, 5), cold_ms_per_step=round(cold, 5),
+                cold_fill_ms_per_step=round(cold_fill, 5),
+                cold_fill_frac_hbm=round(db / (cold_fill * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                 hot_tokens_per_s=round(cfg.batch * 1e3 / hot, 1),
                 cold_gbs=round(db / (cold * 1e-3) / 1e9, 2),
                 cold_frac_hbm=round(db / (cold * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
@@ -541,8 +565,11 @@ def main():
     gbs = nbytes / (ms * 1e-3) / 1e9
     # The dominant kernel is the scan itself; one step is its segment pass, the
     # combine of the segments' end states and the rescan of the segments' heads.
+    copy_gbs = copy_bandwidth()
     roof = dict(bound="hbm", achieved=round(gbs, 2), peak=HBM_PEAK_GBS, unit="GB/s",
                 frac=round(gbs / HBM_PEAK_GBS, 4),
+                # against what a plain 4 GiB device copy reaches in the same run
+                copy_gbs=round(copy_gbs, 1), frac_of_copy=round(gbs / copy_gbs, 4),
                 traffic=_counter_traffic("scan_" + cfg.name),
                 algorithmic_bytes_per_launch=nbytes, launch_ms=round(ms, 5),
                 launch="one ssm_selective_scan_fwd call: scan_tiles_kernel segment pass + "
@@ -588,9 +615,13 @@ def main():
         # prefill -> decode handoff
         for name, k in ((W.C5_DECODE.name, 0), (W.C5_DECODE.name + "_conv4_window", 4)):
             print("bench extra: %s" % name, file=sys.stderr, flush=True)
-            hot, cold, db = bench_decode(W.C5_DECODE, conv_k=k)
+            hot, cold, db, loop, cold_fill = bench_decode(W.C5_DECODE, conv_k=k)
             extra[name] = dict(
                 hot_ms_per_step=round(hot, 5), cold_ms_per_step=round(cold, 5),
+                hot_loop_ms=round(loop, 4),
+                # caches evicted by writing instead of reading (dirty lines written back in the step)
+                cold_fill_ms_per_step=round(cold_fill, 5),
+                cold_fill_frac_hbm=round(db / (cold_fill * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                 hot_steps_per_s=round(1e3 / hot, 1), cold_steps_per_s=round(1e3 / cold, 1),
                 cold_gbs=round(db / (cold * 1e-3) / 1e9, 2),
                 cold_frac_hbm=round(db / (cold * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),

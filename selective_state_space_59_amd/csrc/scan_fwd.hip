@@ -724,7 +724,11 @@ struct LaneConst {
     float a, a2, ia, dsk, dbias, cb, wp0, wp1, wp2, wp3;
     bool live;     // the lane holds a real (channel, entry)
     bool dvalid;   // the lane's channel is real
-    int64_t ckpt;  // (b D + d) 16 + n: the lane's place in a checkpoint slab
+    // A checkpoint slab entry (b D + d) 16 + n as the workgroup's uniform part
+    // (b D + d0) 16 and the lane's part ((d - d0) 16 + n, below 2^10): the
+    // store then takes a scalar base and a fixed lane offset.
+    int64_t ckpt_wg;
+    uint32_t ckpt_lane;
 };
 
 // Read-out of one step: lane (c, t) reads the 16 states of step t that the
@@ -857,7 +861,7 @@ __device__ __forceinline__ void block_iter(const ScanKernelParams &p, const Span
     if (CKPT || p.ckpt) {
         // the state entering this block (the fast form carries A h)
         if (k.dvalid)
-            p.ckpt[(sp.t0 / kTB + j) * (p.B * p.D * kRow) + k.ckpt] = FAST ? cy.h * k.ia : cy.h;
+            (p.ckpt + (sp.t0 / kTB + j) * (p.B * p.D * kRow) + k.ckpt_wg)[k.ckpt_lane] = FAST ? cy.h * k.ia : cy.h;
     }
     // -- LDS reads of later blocks first ------------------------------------------
     float own_next[3];
@@ -1174,7 +1178,8 @@ void scan_tiles_kernel(ScanKernelParams p) {
     LaneConst k;
     k.live = live;
     k.dvalid = dvalid;
-    k.ckpt = ((b * D + d) * kRow) + n;
+    k.ckpt_wg = (b * D + d0) * kRow;
+    k.ckpt_lane = (uint32_t)((4 * wave + c) * kRow + n);
     k.a = live ? p.A[d * N + n] : 0.0f;
     k.a2 = k.a * kLog2e;
     k.ia = (k.a != 0.0f) ? 1.0f / k.a : 0.0f;

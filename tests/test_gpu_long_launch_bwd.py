@@ -18,7 +18,8 @@ backward tests' scaled bound).  dB and dC are sums over all 5120 channels and
 are checked at normal sizes by the other backward tests.
 
 About 100 GB of device memory (inputs, gradients and the workspace's 18 GB of
-checkpoints and 12 GB of dB/dC partial sums).
+checkpoints and 12 GB of dB/dC partial sums); about 110 GB when the forward
+writes the checkpoints (with its y) and the backward's workspace holds none.
 """
 import numpy as np
 import pytest
@@ -71,15 +72,25 @@ def _check(name, got, ref, tol, scale=0.0):
     assert worst <= tol, (name, worst)
 
 
-@pytest.mark.parametrize("conv", [False, True], ids=["plain", "conv4"])
-def test_chained_checkpoints_match_one_recurrence(long_inputs, conv):
+@pytest.mark.parametrize("conv,from_fwd", [(False, False), (True, False), (True, True)],
+                         ids=["plain", "conv4", "conv4_forward_checkpoints"])
+def test_chained_checkpoints_match_one_recurrence(long_inputs, conv, from_fwd):
+    """from_fwd: the checkpoints come from the forward (three chained launches,
+    each cut into sequence segments at this width) instead of the backward's
+    own first pass."""
     inp = long_inputs
     conv_w = inp["conv_w"] if conv else None
-    print("case conv=%s" % conv, flush=True)
+    print("case conv=%s from_fwd=%s" % (conv, from_fwd), flush=True)
+    ck = None
+    if from_fwd:
+        ck = torch.empty(ssm.checkpoint_shape(B, L, D), device=DEV)
+        ssm.selective_scan_fwd(inp["x"], inp["delta"], inp["A"], inp["Bm"], inp["Cm"], Dskip=inp["Dskip"],
+                               z=inp["z"], h0=inp["h0"], conv_w=conv_w, checkpoints=ck)
     g = ssm.selective_scan_bwd(inp["x"], inp["delta"], inp["A"], inp["Bm"], inp["Cm"], inp["dy"],
                                Dskip=inp["Dskip"], z=inp["z"], h0=inp["h0"], dh_final=inp["dh_final"],
-                               conv_w=conv_w)
+                               conv_w=conv_w, checkpoints=ck)
     torch.cuda.synchronize()
+    del ck
     print("  backward done; oracle on sampled channels", flush=True)
     rng = np.random.default_rng(7 + int(conv))
     ds = rng.choice(D, 6, replace=False)

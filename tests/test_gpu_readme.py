@@ -19,3 +19,6 @@ def test_readme_example_runs():
     y, h, y1 = env["y"], env["h"], env["y1"]
     assert y.shape == (2, 4096, 1536) and h.shape == (2, 1536, 16) and y1.shape == (2, 1536)
     assert torch.isfinite(y.float()).all() and torch.isfinite(h).all() and torch.isfinite(y1.float()).all()
+    g = env["grads"]
+    assert g["dx"].shape == (2, 4096, 1536) and g["dA"].shape == (1536, 16)
+    assert all(torch.isfinite(v.float()).all() for v in g.values())
