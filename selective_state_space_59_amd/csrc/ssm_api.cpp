@@ -56,6 +56,14 @@ bool mul_ok(int64_t a, int64_t b, int64_t c = 1) {
     return ab <= lim / c;
 }
 
+// Elements of a checkpoint buffer, (ceil(L / SSM_SCAN_BLOCK), B, D, SSM_MAX_DSTATE),
+// or -1 where that product is too large.
+int64_t checkpoint_elems(int64_t B, int64_t L, int64_t D) {
+    const int64_t nblk = (L + SSM_SCAN_BLOCK - 1) / SSM_SCAN_BLOCK;
+    if (!mul_ok(B, D) || !mul_ok(nblk, B * D, SSM_MAX_DSTATE)) return -1;
+    return nblk * B * D * SSM_MAX_DSTATE;
+}
+
 ssm_status_t check_scan_sizes(const ssm_scan_args_t *a) {
     if (!a) return fail(SSM_ERR_NULL_ARG, "args is NULL");
     if (a->io_dtype != SSM_F32 && a->io_dtype != SSM_BF16)
@@ -77,6 +85,8 @@ ssm_status_t check_scan_sizes(const ssm_scan_args_t *a) {
     if (!mul_ok(a->batch, a->seqlen, a->dim) || !mul_ok(a->batch, a->seqlen, a->dstate) ||
         !mul_ok(a->batch, a->dim, a->dstate))
         return fail(SSM_ERR_BAD_SHAPE, "sizes overflow");
+    if (a->checkpoints && checkpoint_elems(a->batch, a->seqlen, a->dim) < 0)
+        return fail(SSM_ERR_BAD_SHAPE, "checkpoint sizes overflow");
     return SSM_OK;
 }
 
@@ -165,10 +175,8 @@ ssm_status_t scan_fwd(const ssm_scan_args_t *a, void *stream, bool noalloc) {
     }
     if (overlaps(y, hf)) return fail(SSM_ERR_ALIAS, "y overlaps h_final");
     if (overlaps(cso, y) || overlaps(cso, hf)) return fail(SSM_ERR_ALIAS, "conv_state_out overlaps an output");
-    const int64_t nblk = (L + SSM_SCAN_BLOCK - 1) / SSM_SCAN_BLOCK;
-    if (a->checkpoints && !mul_ok(nblk, B * D, SSM_MAX_DSTATE))
-        return fail(SSM_ERR_BAD_SHAPE, "checkpoint sizes overflow");
-    const Range ck = range(a->checkpoints, nblk * B * D * SSM_MAX_DSTATE, 4, "checkpoints");
+    const int64_t nck = a->checkpoints ? checkpoint_elems(B, L, D) : 0;  // >= 0 (checked above)
+    const Range ck = range(a->checkpoints, nck, 4, "checkpoints");
     for (const Range &r : inputs)
         if (overlaps(ck, r)) return fail(SSM_ERR_ALIAS, "checkpoints overlap %s", r.name);
     if (overlaps(ck, y) || overlaps(ck, hf) || overlaps(ck, cso))
@@ -332,8 +340,9 @@ static ssm_status_t check_bwd(const ssm_scan_bwd_args_t *a, size_t *need_out) {
         return fail(SSM_ERR_BAD_SHAPE, "a conv state or its gradient given but conv_k < 2");
     if (a->delta_softplus != 0 && a->delta_softplus != 1)
         return fail(SSM_ERR_UNSUPPORTED, "delta_softplus must be 0 or 1");
+    // (the backward's checkpoints, in its workspace or the caller's, must be addressable too)
     if (!mul_ok(a->batch, a->seqlen, a->dim) || !mul_ok(a->batch, a->seqlen, a->dstate) ||
-        !mul_ok(a->batch, a->dim, a->dstate))
+        !mul_ok(a->batch, a->dim, a->dstate) || checkpoint_elems(a->batch, a->seqlen, a->dim) < 0)
         return fail(SSM_ERR_BAD_SHAPE, "sizes overflow");
     const int64_t B = a->batch, L = a->seqlen, D = a->dim, N = a->dstate, K = a->conv_k;
     const int64_t es = io_bytes(a->io_dtype);
@@ -361,6 +370,8 @@ static ssm_status_t check_bwd(const ssm_scan_bwd_args_t *a, size_t *need_out) {
                             a->checkpoints};
     for (const void *p : f_ptrs)
         if (!aligned(p, 4)) return fail(SSM_ERR_ALIGN, "an fp32 pointer is not 4-byte aligned");
+    const int64_t nck = a->checkpoints ? checkpoint_elems(B, L, D) : 0;
+    if (nck < 0) return fail(SSM_ERR_BAD_SHAPE, "checkpoint sizes overflow");
     const Range inputs[] = {
         range(a->x, B * L * D, es, "x"),          range(a->delta, B * L * D, es, "delta"),
         range(a->Bm, B * L * N, es, "Bm"),        range(a->Cm, B * L * N, es, "Cm"),
@@ -370,8 +381,7 @@ static ssm_status_t check_bwd(const ssm_scan_bwd_args_t *a, size_t *need_out) {
         range(a->dh_final, B * D * N, 4, "dh_final"), range(a->conv_w, D * K, 4, "conv_w"),
         range(a->conv_b, D, 4, "conv_b"),
         range(a->conv_state_in, B * (K > 0 ? K - 1 : 0) * D, es, "conv_state_in"),
-        range(a->checkpoints, ((L + SSM_SCAN_BLOCK - 1) / SSM_SCAN_BLOCK) * B * D * SSM_MAX_DSTATE, 4,
-              "checkpoints"),
+        range(a->checkpoints, nck, 4, "checkpoints"),
     };
     const Range outputs[] = {
         range(a->dx, B * L * D, es, "dx"),        range(a->ddelta, B * L * D, es, "ddelta"),
@@ -406,7 +416,8 @@ static ssm_status_t check_bwd(const ssm_scan_bwd_args_t *a, size_t *need_out) {
 
 size_t ssm_selective_scan_bwd_workspace_size(const ssm_scan_bwd_args_t *a) {
     if (!a || a->batch < 0 || a->seqlen < 0 || a->dim < 1 || a->dstate < 1 || a->dstate > SSM_MAX_DSTATE ||
-        !mul_ok(a->batch, a->seqlen, a->dim) || !mul_ok(a->batch, a->dim, a->dstate))
+        !mul_ok(a->batch, a->seqlen, a->dim) || !mul_ok(a->batch, a->dim, a->dstate) ||
+        checkpoint_elems(a->batch, a->seqlen, a->dim) < 0)
         return (size_t)-1;
     return a->batch > 0 ? ssm::scan_bwd_workspace_bytes(*a) : 0;
 }

@@ -364,15 +364,16 @@ def selective_scan_fwd_noalloc(x: torch.Tensor, delta: torch.Tensor, A: torch.Te
                                y: Optional[torch.Tensor] = None,
                                h_final: Optional[torch.Tensor] = None,
                                conv_state_in: Optional[torch.Tensor] = None,
-                               conv_state_out: Optional[torch.Tensor] = None):
+                               conv_state_out: Optional[torch.Tensor] = None,
+                               checkpoints: Optional[torch.Tensor] = None):
     """ssm_selective_scan_fwd_noalloc: the scan with its workspace in the library's
-    scratch array on the device (no workspace tensor).  The outputs y, h_final and
-    conv_state_out must be given when wanted (nothing is allocated here either).
-    Returns (y, h_final)."""
+    scratch array on the device (no workspace tensor).  The outputs y, h_final,
+    conv_state_out and checkpoints must be given when wanted (nothing is allocated here
+    either).  Returns (y, h_final)."""
     if y is None:
         raise ValueError("y is required (the no-allocation scan allocates nothing)")
     a, dev = _scan_args(x, delta, A, Bm, Cm, Dskip, z, delta_bias, delta_softplus, conv_w,
-                        conv_b, h0, y, h_final, conv_state_in, conv_state_out)
+                        conv_b, h0, y, h_final, conv_state_in, conv_state_out, checkpoints)
     _check(lib().ssm_selective_scan_fwd_noalloc(ctypes.byref(a), _stream(dev)),
            "ssm_selective_scan_fwd_noalloc")
     return y, h_final
@@ -380,7 +381,7 @@ def selective_scan_fwd_noalloc(x: torch.Tensor, delta: torch.Tensor, A: torch.Te
 
 def selective_scan_args(x, delta, A, Bm, Cm, Dskip=None, z=None, delta_bias=None,
                         delta_softplus=False, conv_w=None, conv_b=None, h0=None, y=None,
-                        h_final=None, conv_state_in=None, conv_state_out=None):
+                        h_final=None, conv_state_in=None, conv_state_out=None, checkpoints=None):
     """The checked ssm_scan_args_t of a selective_scan_fwd call with a workspace of its own,
     for callers that launch the same scan repeatedly through lib().ssm_selective_scan_fwd.
     Returns (args, y, workspace or None); y is allocated when not given.  The tensors must
@@ -388,7 +389,7 @@ def selective_scan_args(x, delta, A, Bm, Cm, Dskip=None, z=None, delta_bias=None
     if y is None:
         y = torch.empty_like(x)
     a, dev = _scan_args(x, delta, A, Bm, Cm, Dskip, z, delta_bias, delta_softplus, conv_w,
-                        conv_b, h0, y, h_final, conv_state_in, conv_state_out)
+                        conv_b, h0, y, h_final, conv_state_in, conv_state_out, checkpoints)
     need = lib().ssm_selective_scan_workspace_size(ctypes.byref(a))
     if need == ctypes.c_size_t(-1).value:
         _check(lib().ssm_selective_scan_fwd(ctypes.byref(a), None), "ssm_selective_scan_fwd")

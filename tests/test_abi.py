@@ -285,6 +285,8 @@ def test_scan_workspace_checks():
     # inside the workspace (a long row is cut into segments, which need one)
     (dict(checkpoints=addr(9, 256), batch=1, seqlen=20000), ssm.SSM_ERR_ALIAS),
     (dict(checkpoints=addr(12), seqlen=1 << 60), ssm.SSM_ERR_BAD_SHAPE),
+    # B L D and B D N fit, the 16-wide checkpoints of 2^59 channels do not
+    (dict(checkpoints=addr(12), batch=1, seqlen=1, dim=1 << 59, dstate=1), ssm.SSM_ERR_BAD_SHAPE),
 ])
 def test_scan_checkpoint_checks(kw, status):
     assert run_scan(scan_args(**kw)) == status
@@ -477,6 +479,13 @@ def test_bwd_with_checkpoints_needs_less_workspace(N):
     # the checkpoints of B=2, L=8, D=64: one block of 2 * 64 * 16 fp32 (256-rounded)
     assert n0 - n1 >= 2 * 64 * 16 * 4
     assert run_bwd(bwd_args(dstate=N, checkpoints=addr(20))) == ssm.SSM_ERR_HIP
+
+
+def test_bwd_checkpoint_sizes_overflow():
+    # B L D and B D N fit, but the 16-wide checkpoints of 2^59 channels do not
+    a = bwd_args(seqlen=1, dim=1 << 59, dstate=1)
+    assert run_bwd(a) == ssm.SSM_ERR_BAD_SHAPE
+    assert ssm.lib().ssm_selective_scan_bwd_workspace_size(ctypes.byref(a)) == ctypes.c_size_t(-1).value
 
 
 def test_bwd_dz_without_z_and_empty_batch():

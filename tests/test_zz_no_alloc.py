@@ -75,3 +75,23 @@ def test_no_alloc_scan_without_a_workspace_need():
     got = _no_alloc(inp)
     torch.cuda.synchronize()
     _compare(got, ref, "no-workspace shape")
+
+
+def test_no_alloc_scan_writes_the_same_checkpoints():
+    """The forward's block checkpoints (an output the caller passes) through the
+    no-allocation scan equal those of the scan with a workspace, on a segmented row."""
+    B, L, D, K = BIG
+    inp = _inputs(B, L, D, K, seed=97)
+    shape = ssm.checkpoint_shape(B, L, D)
+    ck_ref = torch.full(shape, float("nan"), device=DEV)
+    ck = torch.full(shape, float("nan"), device=DEV)
+    ref = ssm.selective_scan_fwd(inp["x"], inp["delta"], inp["A"], inp["Bm"], inp["Cm"],
+                                 Dskip=inp["Dskip"], z=inp["z"], conv_w=inp["conv_w"], h0=inp["h0"],
+                                 return_final_state=True, checkpoints=ck_ref)
+    y, hf = torch.empty_like(inp["x"]), torch.empty_like(inp["h0"])
+    got = ssm.selective_scan_fwd_noalloc(inp["x"], inp["delta"], inp["A"], inp["Bm"], inp["Cm"],
+                                         Dskip=inp["Dskip"], z=inp["z"], conv_w=inp["conv_w"],
+                                         h0=inp["h0"], y=y, h_final=hf, checkpoints=ck)
+    torch.cuda.synchronize()
+    _compare(got, ref, "with checkpoints")
+    assert torch.equal(ck, ck_ref)
