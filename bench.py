@@ -367,7 +367,12 @@ def cpu_baseline(inp, cfg, min_seconds=10.0, block_rows=8192):
     nbytes = scan_algorithmic_bytes(cfg.batch, rows, cfg.dim, cfg.dstate,
                                     2 if str(inp["x"].dtype).endswith("bfloat16") else 4,
                                     cfg.conv_k, cfg.final_state, gate=cfg.gate, skip=cfg.skip)
+    try:
+        usable = len(os.sched_getaffinity(0))  # what nproc reports
+    except AttributeError:
+        usable = os.cpu_count()
     return dict(value=round(nbytes / spent / 1e9, 4), unit="GB/s", cores=nthreads, kind="oracle",
+                host_cpu_count=os.cpu_count(), host_usable_cpus=usable,
                 elems_per_s=round(elems / spent, 1), seconds=round(spent, 2), rows=rows,
                 sample="the first %d of %d rows of the workload (B=%d, D=%d, N=%d), in "
                        "%d-row blocks chained through the final state; fp64, %d threads "

@@ -85,20 +85,21 @@ def _close(name, got, ref, tol, scale=0.0):
 
 
 CASES = [
-    # name, B, L, D, N, dtype, conv, softplus
+    # name, B, L, D, N, dtype, conv, softplus (h0 is given except in the last case)
     ("bf16_vec", 2, 77, 64, 16, torch.bfloat16, False, False),
     ("bf16_vec_conv", 2, 100, 48, 16, torch.bfloat16, True, True),
     ("f32_vec", 1, 64, 40, 16, torch.float32, False, True),
     ("f32_elem_conv", 2, 45, 37, 16, torch.float32, True, False),
     ("bf16_N5_conv", 1, 50, 24, 5, torch.bfloat16, True, False),
     ("f32_N1", 2, 33, 20, 1, torch.float32, False, False),
+    ("bf16_no_h0", 3, 40, 32, 16, torch.bfloat16, True, False),
 ]
 
 
 @pytest.mark.parametrize("name,B,L,D,N,dt,conv,softplus", CASES, ids=[c[0] for c in CASES])
 def test_checkpoints_are_the_prefix_states(name, B, L, D, N, dt, conv, softplus):
     print("case %s" % name, flush=True)
-    inp = _inputs(B, L, D, N, dt, seed=71, conv=conv)
+    inp = _inputs(B, L, D, N, dt, seed=71, conv=conv, h0=not name.endswith("no_h0"))
     bias = torch.randn(D, device=DEV, generator=torch.Generator(DEV).manual_seed(3)) if softplus else None
     y, hf, ck = _fwd(inp, softplus, bias)
     torch.cuda.synchronize()
@@ -124,7 +125,7 @@ GRADS = ("dx", "ddelta", "dz", "dA", "dBm", "dCm", "dDskip", "ddelta_bias", "dh0
 @pytest.mark.parametrize("name,B,L,D,N,dt,conv,softplus", CASES, ids=[c[0] for c in CASES])
 def test_backward_from_forward_checkpoints(name, B, L, D, N, dt, conv, softplus):
     print("case %s" % name, flush=True)
-    inp = _inputs(B, L, D, N, dt, seed=73, conv=conv)
+    inp = _inputs(B, L, D, N, dt, seed=73, conv=conv, h0=not name.endswith("no_h0"))
     bias = torch.randn(D, device=DEV, generator=torch.Generator(DEV).manual_seed(4)) if softplus else None
     _, _, ck = _fwd(inp, softplus, bias)
     g1 = _bwd(inp, ck, softplus, bias)
