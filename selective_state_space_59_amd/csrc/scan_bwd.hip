@@ -8,7 +8,8 @@
 //   1. a checkpoint pass runs the recurrence forward and stores only the
 //      state entering every 16-step block (1/16 of the expanded states): the
 //      forward scan kernel's checkpoint variant (launch_scan_ckpt), with its
-//      workgroup-staged loads and no read-out;
+//      workgroup-staged loads and no read-out.  In training the forward
+//      writes them beside y instead, and this pass is skipped;
 //   2. the backward kernel walks the blocks from last to first.  Per block it
 //      re-runs the 16 steps from the checkpoint, keeping h_{t-1} and
 //      exp(dt A) in registers, and then runs the adjoint recurrence
@@ -345,8 +346,7 @@ __device__ __forceinline__ void bwd_body(const BwdParams &p, const LaneB &l, flo
         float u, dt, bv[kStep], cv[kStep], ev[kStep];
         own_finish<IO, CONV>(p, nx.own, wr, cb, bias, u, dt);
         const float raw = live ? bits_f32<IO>(nx.own.draw) : 0.0f;
-        if (STAGE) {
-        } else {
+        if constexpr (!STAGE) {
             uint32_t rb[kStep], rc[kStep];
             load_rows_bits<IO>(p.Bm, p, l, t0, rb);
             load_rows_bits<IO>(p.Cm, p, l, t0, rc);

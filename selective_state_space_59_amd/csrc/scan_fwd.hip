@@ -38,7 +38,10 @@
 //   * each lane's 16 states h_{t,n} are transposed through LDS, so lane
 //     (c, j) sums the 16 states of step t0 + j times their weights and
 //     applies the skip and the gate; y goes out through LDS with coalesced
-//     16-byte stores.
+//     16-byte stores;
+//   * optionally (training) the state entering the block is stored as the
+//     backward's checkpoint of that block; the backward's own first pass is
+//     this kernel with that store and no outputs (kCkptPass).
 // The block loop is software-pipelined: loads run four blocks ahead through
 // a three-slot LDS ring, a block's read-outs are summed and its y stored
 // during the next block, and the MFMAs run one step group ahead.
