@@ -13,6 +13,7 @@ from .ssm import (  # noqa: F401
     checkpoint_shape,
     lib,
     mamba_block_fwd,
+    selective_scan,
     selective_scan_bwd,
     selective_scan_args,
     selective_scan_fwd,
@@ -27,6 +28,6 @@ from .ssm import (  # noqa: F401
 )
 
 __all__ = ["NOALLOC_SCRATCH_BYTES", "BlockPlan", "SSMError", "abi_version", "causal_conv1d_silu", "checkpoint_shape", "lib", "mamba_block_fwd",
-           "selective_scan_args", "selective_scan_bwd", "selective_scan_fwd",
+           "selective_scan", "selective_scan_args", "selective_scan_bwd", "selective_scan_fwd",
            "selective_scan_fwd_noalloc", "selective_scan_workspace_size", "ssd_fwd",
            "ssd_step", "ssd_step_args", "state_update", "state_update_args", "status_string"]

@@ -543,6 +543,48 @@ def selective_scan_bwd(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, Bm
     return out
 
 
+class _SelectiveScanFn(torch.autograd.Function):
+    """selective_scan as a torch autograd function: the forward writes the block
+    checkpoints, the backward reads them (ssm_selective_scan_fwd / _bwd)."""
+
+    @staticmethod
+    def forward(ctx, x, delta, A, Bm, Cm, Dskip, z, delta_bias, h0, conv_w, conv_b, delta_softplus):
+        ck = torch.empty(checkpoint_shape(x.shape[0], x.shape[1], x.shape[2]), device=x.device,
+                         dtype=torch.float32)
+        y, hf = selective_scan_fwd(x, delta, A, Bm, Cm, Dskip=Dskip, z=z, delta_bias=delta_bias,
+                                   delta_softplus=delta_softplus, conv_w=conv_w, conv_b=conv_b, h0=h0,
+                                   return_final_state=True, checkpoints=ck)
+        ctx.save_for_backward(x, delta, A, Bm, Cm, Dskip, z, delta_bias, h0, conv_w, conv_b, ck)
+        ctx.delta_softplus = delta_softplus
+        return y, hf
+
+    @staticmethod
+    def backward(ctx, dy, dh_final):
+        x, delta, A, Bm, Cm, Dskip, z, delta_bias, h0, conv_w, conv_b, ck = ctx.saved_tensors
+        if dy is None:
+            dy = torch.zeros_like(x)
+        g = selective_scan_bwd(x, delta, A, Bm, Cm, dy.contiguous(), Dskip=Dskip, z=z,
+                               delta_bias=delta_bias, delta_softplus=ctx.delta_softplus, h0=h0,
+                               dh_final=None if dh_final is None else dh_final.contiguous(),
+                               conv_w=conv_w, conv_b=conv_b, checkpoints=ck)
+        given = lambda t, k: g.get(k) if t is not None else None
+        return (g["dx"], g["ddelta"], g["dA"], g["dBm"], g["dCm"], given(Dskip, "dDskip"), given(z, "dz"),
+                given(delta_bias, "ddelta_bias"), given(h0, "dh0"), given(conv_w, "dconv_w"),
+                given(conv_b, "dconv_b"), None)
+
+
+def selective_scan(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, Bm: torch.Tensor,
+                   Cm: torch.Tensor, Dskip: Optional[torch.Tensor] = None,
+                   z: Optional[torch.Tensor] = None, delta_bias: Optional[torch.Tensor] = None,
+                   delta_softplus: bool = False, h0: Optional[torch.Tensor] = None,
+                   conv_w: Optional[torch.Tensor] = None, conv_b: Optional[torch.Tensor] = None):
+    """The scan as a differentiable torch op (1 <= N <= 16): returns (y, h_final), and
+    backward() runs ssm_selective_scan_bwd from the checkpoints the forward kept.  The
+    gradients of B and C are computed in fp32 and cast to their dtype by autograd."""
+    return _SelectiveScanFn.apply(x, delta, A, Bm, Cm, Dskip, z, delta_bias, h0, conv_w, conv_b,
+                                  bool(delta_softplus))
+
+
 class BlockPlan:
     """A plan of ssm_block_fwd for fixed sizes (owns the library's plan handle)."""
 

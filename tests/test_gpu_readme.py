@@ -22,3 +22,5 @@ def test_readme_example_runs():
     g = env["grads"]
     assert g["dx"].shape == (2, 4096, 1536) and g["dA"].shape == (1536, 16)
     assert all(torch.isfinite(v.float()).all() for v in g.values())
+    xs = env["xs"]
+    assert xs.grad is not None and xs.grad.shape == xs.shape and torch.isfinite(xs.grad.float()).all()
