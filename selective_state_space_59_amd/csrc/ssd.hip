@@ -747,12 +747,20 @@ void launch_step_q4(const SsdStepParams &p, hipStream_t stream) {
 // without losing the fp32 bound, so fp32 I/O runs the layer in its recurrent
 // form ("14.1 SSM(State Space Models)과 Mamba 아키텍처의 부상", sec. 5.1: the
 // same map as the quadratic form): sequential in time with the state in
-// registers, as the decode step lays it out.  N / 4 lanes of an aligned group
-// hold 4 consecutive state entries of one channel each; a workgroup takes
-// 256 / (N / 4) channels of one (batch, head), so the step's decay, weight, B
-// and C rows are the same for all of it.  Per step: the state update, the
-// read-out summed by xor shuffles, skip and gate, one lane's store.  The
-// inputs of the next 4 steps are requested before the current 4 compute.
+// registers, in fp32 throughout.
+//
+// Lanes are channels.  A wave holds 64 (head, channel) pairs of one (batch,
+// group) and state entries [8w, 8w + 8) of each, so a step's B and C entries
+// are the same for every lane of the wave.  Each wave fetches its entries of
+// B and C for 16 steps with one 16-byte load per lane, a round ahead, and
+// keeps them in a wave-private LDS area from which every step reads them as
+// a broadcast (all lanes one address), instead of every lane fetching its own
+// copy through the caches.  The N / 8 waves of a workgroup hold the other
+// entries of the same pairs.  Per step each wave adds its entries' share of
+// C h into LDS; every 16 steps the workgroup adds the shares in a fixed
+// order, one step row per wave, and applies the skip and the gate.  Steps
+// past the end run with dt = 0 and x = 0, which leaves the state as it is,
+// and store nothing.
 struct SsdF32Params {
     int64_t B, L, H, P, G;
     const float *x, *delta, *Bm, *Cm, *z, *A, *Dskip, *dbias, *h0;
@@ -760,114 +768,151 @@ struct SsdF32Params {
     int softplus;
 };
 
-struct F32In {
-    float x, z, dt;
-    float4 b, c;
+constexpr int kF32E = 8;   // state entries per wave
+constexpr int kF32K = 16;  // steps per read-out round
+constexpr int kF32U = 4;   // steps whose x and dt are requested together
+
+struct F32Lane {
+    const float *xl, *zl, *dl, *bw, *cw;
+    float *yl;
+    float a2, ia, dsk, dbias;
+    int lane;
+    bool live;
 };
 
-constexpr int kF32Steps = 4;
-
-// Sum over each aligned group of Q4 lanes (Q4 = 4, 8, 16 or 32), every lane of
-// the group receiving it: quad swaps, then the half-row and row mirrors (each
-// lane's partner holds the other half's uniform sum), then for 32 lanes one
-// exchange with the neighbouring row.  (v_permlane16_swap of a value with
-// itself would do that last step in registers, but the compiler reads both of
-// its results as the first one when the two operands are the same value.)
-template <int Q4>
-__device__ __forceinline__ float group_sum(float v) {
-    v += __builtin_amdgcn_update_dpp(0.0f, v, 0xB1, 0xf, 0xf, false);  // quad_perm [1,0,3,2]
-    v += __builtin_amdgcn_update_dpp(0.0f, v, 0x4E, 0xf, 0xf, false);  // quad_perm [2,3,0,1]
-    if constexpr (Q4 >= 8) v += __builtin_amdgcn_update_dpp(0.0f, v, 0x141, 0xf, 0xf, false);  // row_half_mirror
-    if constexpr (Q4 >= 16) v += __builtin_amdgcn_update_dpp(0.0f, v, 0x140, 0xf, 0xf, false);  // row_mirror
-    if constexpr (Q4 >= 32) v += __shfl_xor(v, 16, 64);
-    return v;
-}
-
-template <int Q4>
-__global__ __launch_bounds__(256) void ssd_scan_f32_kernel(SsdF32Params p, int64_t ntiles) {
-    constexpr int N = 4 * Q4;
-    constexpr int CPW = 256 / Q4;  // channels per workgroup
-    const int64_t bh = blockIdx.x / ntiles;
-    const int64_t tile = blockIdx.x - bh * ntiles;
-    const int64_t h = bh % p.H, b = bh / p.H;
-    const int64_t grp = h / (p.H / p.G);
-    const int q = threadIdx.x % Q4;
-    const int64_t pc = tile * CPW + threadIdx.x / Q4;
-    const bool live = pc < p.P;
-    const int64_t pcc = live ? pc : 0;
-    const int64_t L = p.L;
-    const float a = p.A[h];
-    const float dsk = p.Dskip ? p.Dskip[h] : 0.0f;
-    const float dbias = p.dbias ? p.dbias[h] : 0.0f;
-    // The step's decay and input weight depend on (b, t, h) only.  Where |a| >=
-    // 1/16 the weight (e - 1)/a is one fma with 1/a (as the S6 scan's fast form);
-    // otherwise dt phi(dt a) (series near 0).  The choice is uniform per workgroup.
-    const bool fast = fabsf(a) >= 0.0625f;
-    const float ia = fast ? 1.0f / a : 0.0f;
-    const float a2 = a * kLog2e;
-    const int64_t chan = bh * p.P + pcc;  // (b, h, pc) as a (B, H, P) index
-    float4 st = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-    if (p.h0) st = *reinterpret_cast<const float4 *>(p.h0 + chan * N + 4 * q);
-    // step t of x, z, y: (b, t, h, pc); delta: (b, t, h); B, C: (b, t, grp, 4q..4q+3)
-    const int64_t xs = p.H * p.P, bs = p.G * N;
-    const float *xb = p.x + b * L * xs + h * p.P + pcc;
-    const float *zb = p.z ? p.z + b * L * xs + h * p.P + pcc : nullptr;
-    float *yb = p.y + b * L * xs + h * p.P + pcc;
-    const float *db = p.delta + b * L * p.H + h;
-    const float *bb = p.Bm + b * L * bs + grp * N + 4 * q;
-    const float *cb = p.Cm + b * L * bs + grp * N + 4 * q;
-    auto load = [&](int64_t t, F32In &v) {
-        const int64_t tc = t < L ? t : (L > 0 ? L - 1 : 0);  // past the end: a row that exists
-        v.x = xb[tc * xs];
-        v.z = zb ? zb[tc * xs] : 0.0f;
-        v.dt = db[tc * p.H];
-        v.b = *reinterpret_cast<const float4 *>(bb + tc * bs);
-        v.c = *reinterpret_cast<const float4 *>(cb + tc * bs);
+// The rounds of 16 steps.  FAST: every head of the wave has |a| >= 1/16, and
+// the input weight (e - 1)/a is one fma with 1/a (as the S6 scan's fast form);
+// otherwise dt phi(dt a), series near 0.  Both variants pass the same
+// barriers.
+template <int S, bool FAST, bool SOFTPLUS>
+__device__ __forceinline__ void f32_rounds(const SsdF32Params &p, const F32Lane &l, float (&st)[kF32E],
+                                           float (&share)[S][kF32K][64], float4 (&bcs)[kF32K * 4], int w, float a) {
+    const int64_t L = p.L, HP = p.H * p.P, GN = p.G * kF32E * S;
+    const int lane = l.lane;
+    if (L == 0) return;  // the state passes through
+    // this lane's piece of the wave's B and C for steps t0 .. t0 + 15: step
+    // lane / 4, piece lane % 4 (B 0..3, B 4..7, C 0..3, C 4..7)
+    auto fetch_bc = [&](int64_t t0) -> float4 {
+        const int64_t t = t0 + (lane >> 2);
+        const int64_t tb = t < L ? t : L - 1;  // a step that exists (unused past the end)
+        const float *src = ((lane & 2) ? l.cw : l.bw) + tb * GN + 4 * (lane & 1);
+        return *reinterpret_cast<const float4 *>(src);
     };
-    F32In nxt[kF32Steps];
-    if (L > 0) {
+    float xs[kF32U], ds[kF32U];
+    auto request = [&](int64_t t0) {  // x and raw dt of steps t0 .. t0 + kF32U - 1 (0 past the end)
 #pragma unroll
-        for (int k = 0; k < kF32Steps; ++k) load(k, nxt[k]);
-    }
-    for (int64_t t0 = 0; t0 < L; t0 += kF32Steps) {
-        F32In cur[kF32Steps];
+        for (int u = 0; u < kF32U; ++u) {
+            const bool in = l.live && t0 + u < L;
+            const int64_t tc = in ? t0 + u : 0;
+            xs[u] = in ? l.xl[tc * HP] : 0.0f;
+            ds[u] = in ? l.dl[tc * p.H] : 0.0f;
+        }
+    };
+    float4 bc_next = fetch_bc(0);
+    request(0);
+    for (int64_t t0 = 0; t0 < L; t0 += kF32K) {
+        bcs[lane] = bc_next;  // wave-private: read back by this wave only
+        __builtin_amdgcn_wave_barrier();
+        bc_next = fetch_bc(t0 + kF32K);
+        // each step's B and C are read from LDS one step ahead of their use
+        float4 q0 = bcs[0], q1 = bcs[1], q2 = bcs[2], q3 = bcs[3];
+        for (int k0 = 0; k0 < kF32K; k0 += kF32U) {
+            float xc[kF32U], dc[kF32U];
 #pragma unroll
-        for (int k = 0; k < kF32Steps; ++k) cur[k] = nxt[k];
+            for (int u = 0; u < kF32U; ++u) {
+                xc[u] = xs[u];
+                dc[u] = ds[u];
+            }
+            request(t0 + k0 + kF32U);
 #pragma unroll
-        for (int k = 0; k < kF32Steps; ++k) load(t0 + kF32Steps + k, nxt[k]);
+            for (int u = 0; u < kF32U; ++u) {
+                const int k = k0 + u;
+                const float4 b0 = q0, b1 = q1, c0 = q2, c1 = q3;
+                const int kn = k + 1 < kF32K ? k + 1 : k;
+                q0 = bcs[4 * kn];
+                q1 = bcs[4 * kn + 1];
+                q2 = bcs[4 * kn + 2];
+                q3 = bcs[4 * kn + 3];
+                const float bt[kF32E] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+                const float ct[kF32E] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+                float dt = dc[u];
+                if (SOFTPLUS) dt = t0 + k < L ? softplus_fast(dt + l.dbias) : 0.0f;
+                const float e = hw_exp2(dt * l.a2);
+                const float wdt = FAST ? __builtin_fmaf(e, l.ia, -l.ia) : dt * ssd_phi(dt * a, e);
+                const float wx = wdt * xc[u];
+                float part = 0.0f;
 #pragma unroll
-        for (int k = 0; k < kF32Steps; ++k) {
-            const int64_t t = t0 + k;
-            if (t >= L) break;  // uniform: the same t for the whole workgroup
-            float dt = cur[k].dt;
-            if (p.softplus) dt = softplus_fast(dt + dbias);
-            const float e = hw_exp2(dt * a2);  // decay of the step
-            const float wdt = fast ? __builtin_fmaf(e, ia, -ia) : dt * ssd_phi(dt * a, e);  // ZOH input weight
-            const float wu = wdt * cur[k].x;
-            st.x = __builtin_fmaf(e, st.x, wu * cur[k].b.x);
-            st.y = __builtin_fmaf(e, st.y, wu * cur[k].b.y);
-            st.z = __builtin_fmaf(e, st.z, wu * cur[k].b.z);
-            st.w = __builtin_fmaf(e, st.w, wu * cur[k].b.w);
-            float part = st.x * cur[k].c.x;
-            part = __builtin_fmaf(st.y, cur[k].c.y, part);
-            part = __builtin_fmaf(st.z, cur[k].c.z, part);
-            part = __builtin_fmaf(st.w, cur[k].c.w, part);
-            part = group_sum<Q4>(part);
-            if (live && q == 0) {
-                float yv = part + dsk * cur[k].x;
-                if (zb) yv *= silu(cur[k].z);
-                yb[t * xs] = yv;
+                for (int i = 0; i < kF32E; ++i) {
+                    st[i] = __builtin_fmaf(e, st[i], wx * bt[i]);
+                    part = __builtin_fmaf(st[i], ct[i], part);
+                }
+                share[w][k][lane] = part;
             }
         }
+        __syncthreads();
+        for (int k = w; k < kF32K; k += S) {
+            const int64_t t = t0 + k;
+            float sum = 0.0f;
+#pragma unroll
+            for (int s = 0; s < S; ++s) sum += share[s][k][lane];
+            if (l.live && t < L) {
+                float yv = sum + l.dsk * l.xl[t * HP];
+                if (l.zl) yv *= silu(l.zl[t * HP]);
+                l.yl[t * HP] = yv;
+            }
+        }
+        __syncthreads();
     }
-    if (p.h_final && live) *reinterpret_cast<float4 *>(p.h_final + chan * N + 4 * q) = st;
 }
 
-template <int Q4>
-hipError_t launch_f32_q4(const SsdF32Params &p, hipStream_t stream) {
-    constexpr int64_t CPW = 256 / Q4;
-    const int64_t ntiles = (p.P + CPW - 1) / CPW;
-    ssd_scan_f32_kernel<Q4><<<(unsigned)(p.B * p.H * ntiles), 256, 0, stream>>>(p, ntiles);
+template <int S, bool SOFTPLUS>
+__global__ __launch_bounds__(64 * S) void ssd_scan_f32_kernel(SsdF32Params p, int64_t ntiles) {
+    constexpr int N = kF32E * S;
+    __shared__ float share[S][kF32K][64];
+    __shared__ float4 bcs[S][kF32K * 4];
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;  // w: uniform
+    const int64_t bg = blockIdx.x / ntiles, tile = blockIdx.x - bg * ntiles;
+    const int64_t b = bg / p.G, g = bg - b * p.G;
+    const int64_t hpg = p.H / p.G;
+    const int64_t pair = tile * 64 + lane;  // (head within the group) P + channel
+    F32Lane l;
+    l.lane = lane;
+    l.live = pair < hpg * p.P;
+    const int64_t pr = l.live ? pair : 0;
+    const int64_t hl = pr / p.P;
+    const int64_t h = g * hpg + hl, pc = pr - hl * p.P;
+    const int64_t L = p.L, HP = p.H * p.P;
+    const float a = p.A[h];
+    l.ia = fabsf(a) >= 0.0625f ? 1.0f / a : 0.0f;
+    l.a2 = a * kLog2e;
+    l.dsk = p.Dskip ? p.Dskip[h] : 0.0f;
+    l.dbias = p.dbias ? p.dbias[h] : 0.0f;
+    l.xl = p.x + b * L * HP + h * p.P + pc;  // step t at t HP
+    l.zl = p.z ? p.z + b * L * HP + h * p.P + pc : nullptr;
+    l.yl = p.y + b * L * HP + h * p.P + pc;
+    l.dl = p.delta + b * L * p.H + h;  // step t at t H
+    l.bw = p.Bm + (b * L * p.G + g) * N + kF32E * w;  // step t at t G N
+    l.cw = p.Cm + (b * L * p.G + g) * N + kF32E * w;
+    const int64_t slot = ((b * p.H + h) * p.P + pc) * N + kF32E * w;  // this lane's entries of h0 / h_final
+    float st[kF32E];
+#pragma unroll
+    for (int i = 0; i < kF32E; ++i) st[i] = (p.h0 && l.live) ? p.h0[slot + i] : 0.0f;
+    if (__all(fabsf(a) >= 0.0625f))
+        f32_rounds<S, true, SOFTPLUS>(p, l, st, share, bcs[w], w, a);
+    else
+        f32_rounds<S, false, SOFTPLUS>(p, l, st, share, bcs[w], w, a);
+    if (p.h_final && l.live) {
+#pragma unroll
+        for (int i = 0; i < kF32E; ++i) p.h_final[slot + i] = st[i];
+    }
+}
+
+template <int S>
+hipError_t launch_f32_s(const SsdF32Params &p, hipStream_t stream) {
+    const int64_t ntiles = (p.H / p.G * p.P + 63) / 64;
+    const unsigned grid = (unsigned)(p.B * p.G * ntiles);
+    if (p.softplus) ssd_scan_f32_kernel<S, true><<<grid, 64 * S, 0, stream>>>(p, ntiles);
+    else ssd_scan_f32_kernel<S, false><<<grid, 64 * S, 0, stream>>>(p, ntiles);
     return hipGetLastError();
 }
 
@@ -891,10 +936,10 @@ hipError_t launch_ssd_f32(const ssm_ssd_args_t &a, hipStream_t stream) {
     p.h_final = a.h_final;
     p.softplus = a.delta_softplus;
     switch (a.dstate) {
-        case 16: return launch_f32_q4<4>(p, stream);
-        case 32: return launch_f32_q4<8>(p, stream);
-        case 64: return launch_f32_q4<16>(p, stream);
-        default: return launch_f32_q4<32>(p, stream);
+        case 16: return launch_f32_s<2>(p, stream);
+        case 32: return launch_f32_s<4>(p, stream);
+        case 64: return launch_f32_s<8>(p, stream);
+        default: return launch_f32_s<16>(p, stream);
     }
 }
 
