@@ -749,18 +749,18 @@ void launch_step_q4(const SsdStepParams &p, hipStream_t stream) {
 // same map as the quadratic form): sequential in time with the state in
 // registers, in fp32 throughout.
 //
-// Lanes are channels.  A wave holds 64 (head, channel) pairs of one (batch,
-// group) and state entries [8w, 8w + 8) of each, so a step's B and C entries
-// are the same for every lane of the wave.  Each wave fetches its entries of
-// B and C for 16 steps with one 16-byte load per lane, a round ahead, and
-// keeps them in a wave-private LDS area from which every step reads them as
-// a broadcast (all lanes one address), instead of every lane fetching its own
-// copy through the caches.  The N / 8 waves of a workgroup hold the other
-// entries of the same pairs.  Per step each wave adds its entries' share of
-// C h into LDS; every 16 steps the workgroup adds the shares in a fixed
-// order, one step row per wave, and applies the skip and the gate.  Steps
-// past the end run with dt = 0 and x = 0, which leaves the state as it is,
-// and store nothing.
+// A lane holds 8 consecutive state entries (a slice) of one (head, channel)
+// pair.  A wave holds Q slices of 64 / Q pairs of one (batch, group), Q = 4
+// (2 when N = 16): lane = q (64 / Q) + channel.  The W = N / (8 Q) waves of a
+// workgroup hold the other slices of the same pairs, so the workgroup covers
+// 64 / Q pairs whole.  A step's B and C entries depend on the slice only.
+// Each wave fetches its slices' B and C for 16 steps with Q 16-byte loads per
+// lane, a round ahead, and keeps them in a wave-private LDS area from which
+// every step reads them as broadcasts (Q addresses per read, in disjoint
+// banks).  Per step each lane adds its slice's share of C h into LDS; every
+// 16 steps the workgroup adds the shares of each (step, pair) in a fixed
+// order and applies the skip and the gate.  Steps past the end run with
+// dt = 0 and x = 0, which leaves the state as it is, and store nothing.
 struct SsdF32Params {
     int64_t B, L, H, P, G;
     const float *x, *delta, *Bm, *Cm, *z, *A, *Dskip, *dbias, *h0;
@@ -768,9 +768,17 @@ struct SsdF32Params {
     int softplus;
 };
 
-constexpr int kF32E = 8;   // state entries per wave
+constexpr int kF32E = 8;   // state entries per lane (a slice)
 constexpr int kF32K = 16;  // steps per read-out round
 constexpr int kF32U = 4;   // steps whose x and dt are requested together
+
+// Slices per wave, pairs per wave and waves per workgroup for N / 8 slices.
+template <int S>
+struct F32Shape {
+    static constexpr int Q = S < 4 ? S : 4;
+    static constexpr int C = 64 / Q;
+    static constexpr int W = S / Q;
+};
 
 struct F32Lane {
     const float *xl, *zl, *dl, *bw, *cw;
@@ -780,22 +788,28 @@ struct F32Lane {
     bool live;
 };
 
-// The rounds of 16 steps.  FAST: every head of the wave has |a| >= 1/16, and
+// The rounds of 16 steps.  FAST: every pair of the wave has |a| >= 1/16, and
 // the input weight (e - 1)/a is one fma with 1/a (as the S6 scan's fast form);
 // otherwise dt phi(dt a), series near 0.  Both variants pass the same
 // barriers.
 template <int S, bool FAST, bool SOFTPLUS>
 __device__ __forceinline__ void f32_rounds(const SsdF32Params &p, const F32Lane &l, float (&st)[kF32E],
-                                           float (&share)[S][kF32K][64], float4 (&bcs)[kF32K * 4], int w, float a) {
+                                           float (&share)[F32Shape<S>::W][kF32K][64],
+                                           float4 (&bcs)[kF32K * F32Shape<S>::Q * 4], int w, float a) {
+    using Sh = F32Shape<S>;
+    constexpr int Q = Sh::Q, C = Sh::C, W = Sh::W;
     const int64_t L = p.L, HP = p.H * p.P, GN = p.G * kF32E * S;
-    const int lane = l.lane;
+    const int lane = l.lane, q = lane / C;
     if (L == 0) return;  // the state passes through
-    // this lane's piece of the wave's B and C for steps t0 .. t0 + 15: step
-    // lane / 4, piece lane % 4 (B 0..3, B 4..7, C 0..3, C 4..7)
-    auto fetch_bc = [&](int64_t t0) -> float4 {
-        const int64_t t = t0 + (lane >> 2);
+    // piece j of this lane's share of the wave's B and C for steps t0 ..
+    // t0 + 15: element (j 64 + lane) of bcs, laid out as [step][slice][B lo,
+    // B hi, C lo, C hi]
+    auto fetch_bc = [&](int64_t t0, int j) -> float4 {
+        const int idx = j * 64 + lane;
+        const int k = idx / (4 * Q), qq = (idx >> 2) % Q, piece = idx & 3;
+        const int64_t t = t0 + k;
         const int64_t tb = t < L ? t : L - 1;  // a step that exists (unused past the end)
-        const float *src = ((lane & 2) ? l.cw : l.bw) + tb * GN + 4 * (lane & 1);
+        const float *src = ((piece & 2) ? l.cw : l.bw) + tb * GN + kF32E * qq + 4 * (piece & 1);
         return *reinterpret_cast<const float4 *>(src);
     };
     float xs[kF32U], ds[kF32U];
@@ -808,14 +822,19 @@ __device__ __forceinline__ void f32_rounds(const SsdF32Params &p, const F32Lane 
             ds[u] = in ? l.dl[tc * p.H] : 0.0f;
         }
     };
-    float4 bc_next = fetch_bc(0);
+    float4 bc_next[Q];
+#pragma unroll
+    for (int j = 0; j < Q; ++j) bc_next[j] = fetch_bc(0, j);
     request(0);
     for (int64_t t0 = 0; t0 < L; t0 += kF32K) {
-        bcs[lane] = bc_next;  // wave-private: read back by this wave only
+#pragma unroll
+        for (int j = 0; j < Q; ++j) bcs[j * 64 + lane] = bc_next[j];  // wave-private
         __builtin_amdgcn_wave_barrier();
-        bc_next = fetch_bc(t0 + kF32K);
+#pragma unroll
+        for (int j = 0; j < Q; ++j) bc_next[j] = fetch_bc(t0 + kF32K, j);
         // each step's B and C are read from LDS one step ahead of their use
-        float4 q0 = bcs[0], q1 = bcs[1], q2 = bcs[2], q3 = bcs[3];
+        const float4 *mine = bcs + 4 * q;
+        float4 q0 = mine[0], q1 = mine[1], q2 = mine[2], q3 = mine[3];
         for (int k0 = 0; k0 < kF32K; k0 += kF32U) {
             float xc[kF32U], dc[kF32U];
 #pragma unroll
@@ -829,10 +848,11 @@ __device__ __forceinline__ void f32_rounds(const SsdF32Params &p, const F32Lane 
                 const int k = k0 + u;
                 const float4 b0 = q0, b1 = q1, c0 = q2, c1 = q3;
                 const int kn = k + 1 < kF32K ? k + 1 : k;
-                q0 = bcs[4 * kn];
-                q1 = bcs[4 * kn + 1];
-                q2 = bcs[4 * kn + 2];
-                q3 = bcs[4 * kn + 3];
+                const float4 *nx = mine + kn * 4 * Q;
+                q0 = nx[0];
+                q1 = nx[1];
+                q2 = nx[2];
+                q3 = nx[3];
                 const float bt[kF32E] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
                 const float ct[kF32E] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
                 float dt = dc[u];
@@ -850,15 +870,21 @@ __device__ __forceinline__ void f32_rounds(const SsdF32Params &p, const F32Lane 
             }
         }
         __syncthreads();
-        for (int k = w; k < kF32K; k += S) {
+        // y of (step k, pair c): the N / 8 slice shares, waves outer, slices inner
+        for (int o = threadIdx.x; o < kF32K * C; o += 64 * W) {
+            const int k = o / C, c = o - k * C;
             const int64_t t = t0 + k;
             float sum = 0.0f;
 #pragma unroll
-            for (int s = 0; s < S; ++s) sum += share[s][k][lane];
+            for (int ww = 0; ww < W; ++ww)
+#pragma unroll
+                for (int qq = 0; qq < Q; ++qq) sum += share[ww][k][qq * C + c];
+            // x, z and y of pair c sit c - (lane mod C) channels from this lane's
+            const int64_t off = t * HP + (c - (lane % C));
             if (l.live && t < L) {
-                float yv = sum + l.dsk * l.xl[t * HP];
-                if (l.zl) yv *= silu(l.zl[t * HP]);
-                l.yl[t * HP] = yv;
+                float yv = sum + l.dsk * l.xl[off];
+                if (l.zl) yv *= silu(l.zl[off]);
+                l.yl[off] = yv;
             }
         }
         __syncthreads();
@@ -866,15 +892,17 @@ __device__ __forceinline__ void f32_rounds(const SsdF32Params &p, const F32Lane 
 }
 
 template <int S, bool SOFTPLUS>
-__global__ __launch_bounds__(64 * S) void ssd_scan_f32_kernel(SsdF32Params p, int64_t ntiles) {
-    constexpr int N = kF32E * S;
-    __shared__ float share[S][kF32K][64];
-    __shared__ float4 bcs[S][kF32K * 4];
+__global__ __launch_bounds__(64 * F32Shape<S>::W) void ssd_scan_f32_kernel(SsdF32Params p, int64_t ntiles) {
+    using Sh = F32Shape<S>;
+    constexpr int N = kF32E * S, Q = Sh::Q, C = Sh::C, W = Sh::W;
+    __shared__ float share[W][kF32K][64];
+    __shared__ float4 bcs[W][kF32K * Q * 4];
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;  // w: uniform
+    const int q = lane / C, slice = w * Q + q;
     const int64_t bg = blockIdx.x / ntiles, tile = blockIdx.x - bg * ntiles;
     const int64_t b = bg / p.G, g = bg - b * p.G;
     const int64_t hpg = p.H / p.G;
-    const int64_t pair = tile * 64 + lane;  // (head within the group) P + channel
+    const int64_t pair = tile * C + lane % C;  // (head within the group) P + channel
     F32Lane l;
     l.lane = lane;
     l.live = pair < hpg * p.P;
@@ -891,9 +919,9 @@ __global__ __launch_bounds__(64 * S) void ssd_scan_f32_kernel(SsdF32Params p, in
     l.zl = p.z ? p.z + b * L * HP + h * p.P + pc : nullptr;
     l.yl = p.y + b * L * HP + h * p.P + pc;
     l.dl = p.delta + b * L * p.H + h;  // step t at t H
-    l.bw = p.Bm + (b * L * p.G + g) * N + kF32E * w;  // step t at t G N
-    l.cw = p.Cm + (b * L * p.G + g) * N + kF32E * w;
-    const int64_t slot = ((b * p.H + h) * p.P + pc) * N + kF32E * w;  // this lane's entries of h0 / h_final
+    l.bw = p.Bm + (b * L * p.G + g) * N + kF32E * Q * w;  // the wave's slices; step t at t G N
+    l.cw = p.Cm + (b * L * p.G + g) * N + kF32E * Q * w;
+    const int64_t slot = ((b * p.H + h) * p.P + pc) * N + kF32E * slice;  // this lane's entries of h0 / h_final
     float st[kF32E];
 #pragma unroll
     for (int i = 0; i < kF32E; ++i) st[i] = (p.h0 && l.live) ? p.h0[slot + i] : 0.0f;
@@ -909,10 +937,11 @@ __global__ __launch_bounds__(64 * S) void ssd_scan_f32_kernel(SsdF32Params p, in
 
 template <int S>
 hipError_t launch_f32_s(const SsdF32Params &p, hipStream_t stream) {
-    const int64_t ntiles = (p.H / p.G * p.P + 63) / 64;
+    using Sh = F32Shape<S>;
+    const int64_t ntiles = (p.H / p.G * p.P + Sh::C - 1) / Sh::C;
     const unsigned grid = (unsigned)(p.B * p.G * ntiles);
-    if (p.softplus) ssd_scan_f32_kernel<S, true><<<grid, 64 * S, 0, stream>>>(p, ntiles);
-    else ssd_scan_f32_kernel<S, false><<<grid, 64 * S, 0, stream>>>(p, ntiles);
+    if (p.softplus) ssd_scan_f32_kernel<S, true><<<grid, 64 * Sh::W, 0, stream>>>(p, ntiles);
+    else ssd_scan_f32_kernel<S, false><<<grid, 64 * Sh::W, 0, stream>>>(p, ntiles);
     return hipGetLastError();
 }
 
