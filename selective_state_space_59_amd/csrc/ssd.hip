@@ -16,9 +16,9 @@
 //         + Dskip x_t,  then x silu(z_t)
 //   H    <- e^{acum[end]} H + sum_s e^{acum[end]-acum[s]} w_s x_s B_s^T
 //
-// One workgroup of 4 waves owns one (batch, head, 16 or 32 head channels)
-// and walks that head's chunks in order; the channel tiles of a head run as
-// separate workgroups (they share B and C through the L2).  Every product is a bf16
+// One workgroup of 4 waves owns one (batch, head, 32 head channels) and walks
+// that head's chunks in order; the two channel halves of a head run as two
+// workgroups (they share B and C through the L2).  Every product is a bf16
 // MFMA with fp32 accumulation (16x16x32; 16x16x16 for the sums over the
 // state entries when N = 16).  Wave w owns the 16 steps
 // t in [16 w, 16 w + 16) of each chunk for the outputs and the state entries
@@ -37,10 +37,8 @@
 // significant bits, where a single bf16 rounding (8 bits) would leave errors
 // of order 1% in sums that cancel (C.h is a sum of N terms of either sign).
 // The chunk's inputs for the next chunk are loaded into registers while this
-// one is computed.  LDS per workgroup at N = 128: 41 KB with 16 channels
-// (three workgroups per CU), 60 KB with 32 (two).  16 channels where the
-// launch fills the GPU with them; 32, and sequence segments, where it would
-// not.
+// one is computed.  About 60 KB of LDS per workgroup (N = 128): two
+// workgroups share a CU.
 #include "ssm_device.h"
 #include "ssm_internal.h"
 
@@ -52,8 +50,8 @@ namespace {
 
 constexpr int kQ = 64;     // chunk length (4 tiles of 16)
 constexpr int64_t kMaxHeadDim = 4096;
-// Head channels per workgroup (PT, a template parameter): 16 or 32; the head
-// dim P is a multiple of 32.
+constexpr int kPT = 32;    // head channels per workgroup (the head dim P is a multiple)
+constexpr int kPTL = kPT / 16;  // MFMA column tiles per workgroup
 constexpr int kPadE = 8;   // row padding, bf16 elements (16 bytes)
 constexpr int kThreads = 256;
 
@@ -61,10 +59,10 @@ typedef short ssd_s4 __attribute__((ext_vector_type(4)));
 typedef __bf16 ssd_b8 __attribute__((ext_vector_type(8)));
 typedef float ssd_f4 __attribute__((ext_vector_type(4)));
 
-template <int N, int PT>
+template <int N>
 struct SsdLds {
     static constexpr int nld = N + kPadE;    // rows of N entries: Bs, HT
-    static constexpr int tld = PT + kPadE;  // rows of PT entries: Xs, Zs (Ys)
+    static constexpr int tld = kPT + kPadE;  // rows of kPT entries: Xs, Zs (Ys)
     static constexpr int qld = kQ + kPadE;   // rows of kQ entries: XWT
     // XT is read 8 bytes at a time only: rows 136 bytes apart put the 16 rows
     // of one read in disjoint 8-byte bank slots (144, as XWT, pairs rows r, r + 8)
@@ -72,14 +70,14 @@ struct SsdLds {
     static constexpr size_t bs = 0;
     static constexpr size_t xs = bs + (size_t)kQ * nld * 2;
     static constexpr size_t zs = xs + (size_t)kQ * tld * 2;
-    // HT: [hi/lo plane][PT channels][nld]
+    // HT: [hi/lo plane][kPT channels][nld]
     static constexpr size_t ht = zs + (size_t)kQ * tld * 2;
-    static constexpr size_t ht_plane = (size_t)PT * nld;  // elements
-    // XWT: [hi/lo plane][PT channels][qld]; then XT: x transposed, [PT][xld]
+    static constexpr size_t ht_plane = (size_t)kPT * nld;  // elements
+    // XWT: [hi/lo plane][kPT channels][qld]; then XT: x transposed, [kPT][xld]
     static constexpr size_t xwt = ht + 2 * ht_plane * 2;
-    static constexpr size_t xwt_plane = (size_t)PT * qld;
+    static constexpr size_t xwt_plane = (size_t)kPT * qld;
     static constexpr size_t xt = xwt + 2 * xwt_plane * 2;
-    static constexpr size_t dts = xt + (size_t)PT * xld * 2;  // 16-byte aligned (rows of 136 bytes)
+    static constexpr size_t dts = xt + (size_t)kPT * xld * 2;  // 16-byte aligned (32 rows of 136 bytes)
     // per wave: the chunk's prefix sums of dt a (times log2 e), then its ZOH weights (lane = step)
     static constexpr size_t scal = dts + (size_t)kQ * sizeof(float);
     static constexpr size_t total = scal + (size_t)4 * 2 * kQ * sizeof(float);
@@ -88,7 +86,7 @@ struct SsdLds {
 
 struct SsdParams {
     int64_t B, L, H, G;
-    int64_t P;  // head dim, a multiple of 32
+    int64_t P;  // head dim, a multiple of kPT
     const uint16_t *x, *delta, *Bm, *Cm, *z;
     const float *A, *Dskip, *dbias, *h0;
     uint16_t *y;
@@ -101,7 +99,6 @@ struct SsdParams {
     int64_t nseg, seg_chunks;
     float *ws_state;  // (nseg, B, H, P, N): end states, then entering states
     float *ws_lsum;   // (nseg, B, H): sum of dt a over the segment
-    int pt;           // head channels per workgroup: 16 or 32
 };
 
 __device__ __forceinline__ float bf(uint16_t v) { return bf16_bits_to_f32(v); }
@@ -195,8 +192,8 @@ __device__ __forceinline__ float wave_prefix_sum(float v, int lane) {
 
 // The chunk's inputs in registers between their global load and their LDS
 // store, so that the next chunk's loads are in flight during this chunk's
-// products.  Each thread owns KB 16-byte pieces of B, and the first
-// kQ PT / 8 threads one 16-byte piece each of x and z.
+// products.  Each thread owns KB 16-byte pieces of B, and one 16-byte piece
+// each of x and z.
 template <int N>
 struct ChunkRegs {
     static constexpr int PR = N / 8;  // pieces per B row
@@ -230,7 +227,7 @@ __device__ __forceinline__ void fetch_c(const SsdParams &p, int64_t b, int64_t g
     }
 }
 
-template <int N, int PT>
+template <int N>
 __device__ __forceinline__ void fetch_chunk(const SsdParams &p, int64_t b, int64_t h, int64_t g, int pt,
                                             int64_t t0, bool outputs, int tid, ChunkRegs<N> &r) {
     using R = ChunkRegs<N>;
@@ -247,13 +244,13 @@ __device__ __forceinline__ void fetch_chunk(const SsdParams &p, int64_t b, int64
         }
     }
     {
-        static_assert(kQ * (PT / 8) <= kThreads, "at most one x and one z piece per thread");
-        const int s = tid / (PT / 8), c8 = (tid % (PT / 8)) * 8;
+        static_assert(kQ * (kPT / 8) == kThreads, "one x and one z piece per thread");
+        const int s = tid / (kPT / 8), c8 = (tid % (kPT / 8)) * 8;
         const int64_t t = t0 + s;
         r.x = make_uint4(0, 0, 0, 0);
         r.z = r.x;
-        if (tid < kQ * (PT / 8) && t < L) {
-            const int64_t off = ((b * L + t) * p.H + h) * p.P + PT * pt + c8;
+        if (t < L) {
+            const int64_t off = ((b * L + t) * p.H + h) * p.P + kPT * pt + c8;
             r.x = *reinterpret_cast<const uint4 *>(p.x + off);
             if (p.z && outputs) r.z = *reinterpret_cast<const uint4 *>(p.z + off);
         }
@@ -262,12 +259,12 @@ __device__ __forceinline__ void fetch_chunk(const SsdParams &p, int64_t b, int64
     if (tid < kQ && t0 + tid < L) r.dt = p.delta[(b * L + t0 + tid) * p.H + h];
 }
 
-template <int N, int PT>
+template <int N>
 __device__ __forceinline__ void store_chunk(const ChunkRegs<N> &r, uint16_t *Bs, uint16_t *Xs, uint16_t *XT,
                                             uint16_t *Zs, float *dts, int tid, bool row_live, int softplus,
                                             float dbias) {
     using R = ChunkRegs<N>;
-    using Lay = SsdLds<N, PT>;
+    using Lay = SsdLds<N>;
 #pragma unroll
     for (int k = 0; k < R::KB; ++k) {
         const int id = tid + k * kThreads;
@@ -276,8 +273,8 @@ __device__ __forceinline__ void store_chunk(const ChunkRegs<N> &r, uint16_t *Bs,
             *reinterpret_cast<uint4 *>(Bs + s * Lay::nld + c8) = r.b[k];
         }
     }
-    if (tid < kQ * (PT / 8)) {
-        const int s = tid / (PT / 8), c8 = (tid % (PT / 8)) * 8;
+    {
+        const int s = tid / (kPT / 8), c8 = (tid % (kPT / 8)) * 8;
         *reinterpret_cast<uint4 *>(Xs + s * Lay::tld + c8) = r.x;
         *reinterpret_cast<uint4 *>(Zs + s * Lay::tld + c8) = r.z;
         // x transposed (channel-major), the k-contiguous operand of M X
@@ -293,10 +290,9 @@ __device__ __forceinline__ void store_chunk(const ChunkRegs<N> &r, uint16_t *Bs,
     }
 }
 
-template <int N, int MODE, int PT>
-__global__ __launch_bounds__(kThreads, PT == 16 ? 3 : 2) void ssd_chunk_kernel(SsdParams p) {
-    using Lay = SsdLds<N, PT>;
-    constexpr int kPTL = PT / 16;    // MFMA column tiles per workgroup
+template <int N, int MODE>
+__global__ __launch_bounds__(kThreads, 2) void ssd_chunk_kernel(SsdParams p) {
+    using Lay = SsdLds<N>;
     constexpr int NT = N / 16;       // state tiles of the head
     constexpr int NW = NT / 4;       // state tiles per wave (N >= 64); see below for N < 64
     constexpr int NWT = NW > 0 ? NW : 1;
@@ -320,8 +316,8 @@ __global__ __launch_bounds__(kThreads, PT == 16 ? 3 : 2) void ssd_chunk_kernel(S
     ssd_slot_rows(lane >> 4, nld, brow);
     const int64_t seg = (int64_t)blockIdx.x % p.nseg;
     const int64_t bhp = (int64_t)blockIdx.x / p.nseg;
-    const int pt = (int)(bhp % (p.P / PT));
-    const int64_t bh = bhp / (p.P / PT);
+    const int pt = (int)(bhp % (p.P / kPT));
+    const int64_t bh = bhp / (p.P / kPT);
     const int64_t b = bh / p.H, h = bh % p.H;
     const int64_t g = h / (p.H / p.G);
     const int64_t L = p.L;
@@ -329,7 +325,7 @@ __global__ __launch_bounds__(kThreads, PT == 16 ? 3 : 2) void ssd_chunk_kernel(S
     const float dsk = p.Dskip ? p.Dskip[h] : 0.0f;
     const float dbias = p.dbias ? p.dbias[h] : 0.0f;
     const int tb = w;  // this wave's 16-step row tile
-    // column tile j: this lane's head channel PT pt + 16 j + r16 (local 16 j + r16)
+    // column tile j: this lane's head channel kPT pt + 16 j + r16 (local 16 j + r16)
 
     // State tiles of this wave: st[i][j][v] is entry n = 16 nt + q4 + v of
     // local channel 16 j + r16, nt = NW w + i.  (N < 64: waves beyond NT hold
@@ -350,7 +346,7 @@ __global__ __launch_bounds__(kThreads, PT == 16 ? 3 : 2) void ssd_chunk_kernel(S
             float v4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
             if (owns_state && hin_bh) {
 #pragma unroll
-                for (int v = 0; v < 4; ++v) v4[v] = hin_bh[(PT * pt + pl) * N + 16 * nt + q4 + v];
+                for (int v = 0; v < 4; ++v) v4[v] = hin_bh[(kPT * pt + pl) * N + 16 * nt + q4 + v];
             }
             st[i][j] = ssd_f4{v4[0], v4[1], v4[2], v4[3]};
             if (owns_state) store_split4(HT + pl * nld + 16 * nt + q4, Lay::ht_plane, v4);
@@ -363,15 +359,15 @@ __global__ __launch_bounds__(kThreads, PT == 16 ? 3 : 2) void ssd_chunk_kernel(S
     ChunkRegs<N> regs;
     CRows<N> crow;
     if (c_begin < c_end) {
-        fetch_chunk<N, PT>(p, b, h, g, pt, c_begin * kQ, outputs, tid, regs);
+        fetch_chunk<N>(p, b, h, g, pt, c_begin * kQ, outputs, tid, regs);
         if constexpr (outputs) fetch_c<N>(p, b, g, c_begin * kQ, w, lane, crow);
     }
     for (int64_t c = c_begin; c < c_end; ++c) {
         const int64_t t0 = c * kQ;
-        store_chunk<N, PT>(regs, Bs, Xs, XT, Zs, dts, tid, t0 + tid < L, p.softplus, dbias);
+        store_chunk<N>(regs, Bs, Xs, XT, Zs, dts, tid, t0 + tid < L, p.softplus, dbias);
         __syncthreads();
         // the next chunk's loads fly while this chunk is computed
-        if (c + 1 < c_end) fetch_chunk<N, PT>(p, b, h, g, pt, t0 + kQ, outputs, tid, regs);
+        if (c + 1 < c_end) fetch_chunk<N>(p, b, h, g, pt, t0 + kQ, outputs, tid, regs);
 
         // ---- chunk scalars, one copy per wave (lane = step s) ----------------
         const float dtl = dts[lane];
@@ -384,23 +380,15 @@ __global__ __launch_bounds__(kThreads, PT == 16 ? 3 : 2) void ssd_chunk_kernel(S
         acum_s[lane] = acum * kLog2e;  // kept in log2 units: the readers exponentiate base 2
         wl_s[lane] = wl;
 
-        // ---- X' = f x -> XWT[p][slot of s] (hi, lo): wave w takes channels
-        // XC w .. XC w + XC - 1 of step s = lane, one row read of 2 XC bytes
-        // (read after the middle barrier)
+        // ---- X' = f x -> XWT[p][slot of s] (hi, lo): wave w takes channels 8w .. 8w+7
+        // of step s = lane, one 16-byte row read (read after the middle barrier)
         {
-            constexpr int XC = PT / 4;
-            uint32_t wv[XC / 2];
-            if constexpr (XC == 8) {
-                const uint4 q = *reinterpret_cast<const uint4 *>(Xs + lane * tld + XC * w);
-                wv[0] = q.x, wv[1] = q.y, wv[2] = q.z, wv[3] = q.w;
-            } else {
-                static_assert(XC == 4, "16 or 32 channels per workgroup");
-                const uint2 q = *reinterpret_cast<const uint2 *>(Xs + lane * tld + XC * w);
-                wv[0] = q.x, wv[1] = q.y;
-            }
+            static_assert(kPT / 4 == 8, "one 16-byte piece of x per lane");
+            const uint4 q = *reinterpret_cast<const uint4 *>(Xs + lane * tld + 8 * w);
+            const uint32_t wv[4] = {q.x, q.y, q.z, q.w};
 #pragma unroll
-            for (int i = 0; i < XC; ++i) {
-                const int pp = XC * w + i;
+            for (int i = 0; i < 8; ++i) {
+                const int pp = 8 * w + i;
                 const uint16_t xb = (uint16_t)(i % 2 ? wv[i / 2] >> 16 : wv[i / 2] & 0xffffu);
                 const float v = bf(xb) * fl;
                 const uint16_t hi = f32_to_bf16_bits(v);
@@ -541,11 +529,11 @@ __global__ __launch_bounds__(kThreads, PT == 16 ? 3 : 2) void ssd_chunk_kernel(S
 
         if constexpr (outputs) {
             // ---- outputs leave as 16-byte pieces, one per thread --------------------
-            if (tid < kQ * (PT / 8)) {
-                const int t = tid / (PT / 8), c8 = (tid % (PT / 8)) * 8;
+            {
+                const int t = tid / (kPT / 8), c8 = (tid % (kPT / 8)) * 8;
                 const int64_t tt = t0 + t;
                 if (tt < L)
-                    *reinterpret_cast<uint4 *>(p.y + ((b * L + tt) * p.H + h) * p.P + PT * pt + c8) =
+                    *reinterpret_cast<uint4 *>(p.y + ((b * L + tt) * p.H + h) * p.P + kPT * pt + c8) =
                         *reinterpret_cast<const uint4 *>(Zs + t * tld + c8);
             }
         }
@@ -595,7 +583,7 @@ __global__ __launch_bounds__(kThreads, PT == 16 ? 3 : 2) void ssd_chunk_kernel(S
             for (int j = 0; j < kPTL; ++j)
 #pragma unroll
                 for (int v = 0; v < 4; ++v)
-                    hout[(bh * p.P + PT * pt + 16 * j + r16) * N + 16 * my_nt(i) + q4 + v] = st[i][j][v];
+                    hout[(bh * p.P + kPT * pt + 16 * j + r16) * N + 16 * my_nt(i) + q4 + v] = st[i][j][v];
     }
     if (MODE == 1 && pt == 0 && tid == 0) p.ws_lsum[seg * p.B * p.H + bh] = lsum;
 }
@@ -619,22 +607,17 @@ __global__ __launch_bounds__(256) void ssd_seg_combine_kernel(float *ws_state, c
     if (h_final) h_final[i] = hs;
 }
 
-template <int N, int PT>
-hipError_t launch_npt(const SsdParams &p, hipStream_t stream) {
-    const unsigned grid = (unsigned)(p.B * p.H * (p.P / PT) * p.nseg);
-    const size_t lds = SsdLds<N, PT>::total;
-    if (p.mode == 1)
-        ssd_chunk_kernel<N, 1, PT><<<grid, kThreads, lds, stream>>>(p);
-    else if (p.mode == 2)
-        ssd_chunk_kernel<N, 2, PT><<<grid, kThreads, lds, stream>>>(p);
-    else
-        ssd_chunk_kernel<N, 0, PT><<<grid, kThreads, lds, stream>>>(p);
-    return hipGetLastError();
-}
-
 template <int N>
 hipError_t launch_n(const SsdParams &p, hipStream_t stream) {
-    return p.pt == 16 ? launch_npt<N, 16>(p, stream) : launch_npt<N, 32>(p, stream);
+    const unsigned grid = (unsigned)(p.B * p.H * (p.P / kPT) * p.nseg);
+    const size_t lds = SsdLds<N>::total;
+    if (p.mode == 1)
+        ssd_chunk_kernel<N, 1><<<grid, kThreads, lds, stream>>>(p);
+    else if (p.mode == 2)
+        ssd_chunk_kernel<N, 2><<<grid, kThreads, lds, stream>>>(p);
+    else
+        ssd_chunk_kernel<N, 0><<<grid, kThreads, lds, stream>>>(p);
+    return hipGetLastError();
 }
 
 hipError_t launch_dstate(const SsdParams &p, int64_t N, hipStream_t stream) {
@@ -651,31 +634,20 @@ hipError_t launch_dstate(const SsdParams &p, int64_t N, hipStream_t stream) {
 // segments of at least kMinSegChunks chunks, as many as still run in one
 // round (up to kMaxSeg).  The end-state pass and the combine cost about half
 // a pass, so fuller launches are left whole.
-constexpr int64_t kSlots16 = 3 * 256;  // resident workgroups of 16 channels (41 KB of LDS at N = 128)
-constexpr int64_t kSlotsWanted = 2 * 256;  // of 32 channels (60 KB)
+constexpr int64_t kSlotsWanted = 2 * 256;
 constexpr int64_t kMinSegChunks = 4;
 constexpr int64_t kMaxSeg = 64;
 
 struct SsdPlan {
     int64_t nseg, seg_chunks;
     size_t ws_state, ws_lsum;
-    int pt;
 };
 
 SsdPlan ssd_plan(const ssm_ssd_args_t &a) {
-    SsdPlan q{1, 0, 0, 0, 32};
+    SsdPlan q{1, 0, 0, 0};
     const int64_t nchunks = (a.seqlen + kQ - 1) / kQ;
     q.seg_chunks = nchunks;
-    // Workgroups of 16 channels where they fill more than half of their
-    // resident slots whole: more, shorter per-chunk chains in flight.
-    // Otherwise 32 channels, and segments when those fill at most half of
-    // theirs: a segment's chain is then shorter for the same number of
-    // resident workgroups.
-    if (2 * a.batch * a.nheads * (a.headdim / 16) > kSlots16) {
-        q.pt = 16;
-        return q;
-    }
-    const int64_t wgs = a.batch * a.nheads * (a.headdim / 32);
+    const int64_t wgs = a.batch * a.nheads * (a.headdim / kPT);
     if (wgs > 0 && 2 * wgs <= kSlotsWanted) {
         int64_t s = std::min<int64_t>({kMaxSeg, kSlotsWanted / wgs, nchunks / kMinSegChunks});
         if (s > 1) {
@@ -1064,7 +1036,7 @@ hipError_t launch_ssd_step(const ssm_ssd_step_args_t &a, hipStream_t stream) {
 }
 
 bool ssd_supported(int64_t headdim, int64_t dstate) {
-    return headdim >= 32 && headdim <= kMaxHeadDim && headdim % 32 == 0 &&
+    return headdim >= kPT && headdim <= kMaxHeadDim && headdim % kPT == 0 &&
            (dstate == 16 || dstate == 32 || dstate == 64 || dstate == 128);
 }
 
@@ -1095,7 +1067,6 @@ hipError_t launch_ssd_fwd(const ssm_ssd_args_t &a, hipStream_t stream) {
     p.h_final = a.h_final;
     p.softplus = a.delta_softplus;
     const SsdPlan q = ssd_plan(a);
-    p.pt = q.pt;
     p.nseg = q.nseg;
     p.seg_chunks = q.seg_chunks;
     p.ws_state = nullptr;

@@ -528,7 +528,7 @@ ssm_status_t check_ssd_sizes(const ssm_ssd_args_t *a) {
     const int64_t B = a->batch, L = a->seqlen, H = a->nheads, P = a->headdim, G = a->ngroups, N = a->dstate;
     if (!mul_ok(B, L, H * P) || !mul_ok(B, L, G * N) || !mul_ok(B, H, P * N))
         return fail(SSM_ERR_BAD_SHAPE, "sizes overflow");
-    // one workgroup of 256 threads per (batch, head, 16 channels): the launch holds < 2^32 threads
+    // one workgroup of 256 threads per (batch, head, 32 channels): the launch holds < 2^32 threads
     if (B * H * (P / 32) > ((int64_t)1 << 23))
         return fail(SSM_ERR_UNSUPPORTED, "batch * nheads * headdim / 32 (%lld) exceeds 2^23",
                     (long long)(B * H * (P / 32)));

@@ -84,7 +84,7 @@ HEADDIM_CASES = [
     ("p128_groups", 1, 200, 4, 128, 2, 32, dict(h0=True)),
     ("p32_segments", 1, 2600, 2, 32, 1, 16, dict(h0=True)),
     ("p256_segments_n128", 1, 1500, 1, 256, 1, 128, {}),
-    # wide launches (B H P / 16 > 384 workgroups of 16 channels): 16 channels per workgroup
+    # wide launches: hundreds of workgroups, a few chunks each
     ("wide_p32_n16_h0", 8, 70, 25, 32, 1, 16, dict(h0=True)),
     ("wide_p64_n128_groups", 4, 150, 26, 64, 2, 128, {}),
     ("wide_p96_n64_h0", 3, 100, 22, 96, 1, 64, dict(h0=True)),
@@ -95,8 +95,7 @@ HEADDIM_CASES = [
 @pytest.mark.parametrize("name,B,L,H,P,G,N,extra", HEADDIM_CASES, ids=[c[0] for c in HEADDIM_CASES])
 def test_ssd_head_dims(name, B, L, H, P, G, N, extra):
     """Head dims other than 64 (any multiple of 32: one workgroup per 32 channels of a
-    head, or per 16 when that many workgroups fill the GPU), whole sequences and
-    segmented ones, against the oracle."""
+    head), whole sequences and segmented ones, against the oracle."""
     print("case", name, flush=True)
     inp = W.make_ssd_inputs(B, L, H, P, G, N, seed=820 + L + P, device=DEV, **extra)
     y, hf = _run(inp)
