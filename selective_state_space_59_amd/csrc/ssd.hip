@@ -399,28 +399,39 @@ __global__ __launch_bounds__(kThreads, 2) void ssd_chunk_kernel(SsdParams p) {
 
         if constexpr (outputs) {
             // ---- this wave's G^T tiles, masked and decayed in place ---------------------
-            // All four s tiles are formed (those above the diagonal are masked to 0
-            // below): straight-line code lets the operand loads run ahead of the
-            // MFMAs, and every wave does the same work.
+            // Only the s tiles on or below the diagonal are formed (the rest stay 0).
+            // The count is a compile-time constant in one copy of the loop per wave
+            // index, so the operand loads still run ahead of the MFMAs in
+            // straight-line code.
             ssd_f4 gacc[kQ / 16];
     #pragma unroll
             for (int sb = 0; sb < kQ / 16; ++sb) gacc[sb] = ssd_f4{0.0f, 0.0f, 0.0f, 0.0f};
-            if constexpr (N >= 32) {
+            auto gt_tiles = [&](auto TBc) {
+                constexpr int TB = decltype(TBc)::value;
+                if constexpr (N >= 32) {
     #pragma unroll
-                for (int kk = 0; kk < N / 32; ++kk) {
-                    const ssd_b8 cop = __builtin_bit_cast(ssd_b8, crow.v[kk]);
+                    for (int kk = 0; kk < N / 32; ++kk) {
+                        const ssd_b8 cop = __builtin_bit_cast(ssd_b8, crow.v[kk]);
     #pragma unroll
-                    for (int sb = 0; sb < kQ / 16; ++sb)
-                        gacc[sb] = SSD_MFMA32(lds8(Bs + (16 * sb + r16) * nld + 32 * kk + 2 * q4), cop, gacc[sb]);
+                        for (int sb = 0; sb <= TB; ++sb)
+                            gacc[sb] = SSD_MFMA32(lds8(Bs + (16 * sb + r16) * nld + 32 * kk + 2 * q4), cop, gacc[sb]);
+                    }
+                } else {
+    #pragma unroll
+                    for (int kk = 0; kk < NT; ++kk) {
+                        const ssd_s4 cop = __builtin_bit_cast(ssd_s4, crow.v[kk]);
+    #pragma unroll
+                        for (int sb = 0; sb <= TB; ++sb)
+                            gacc[sb] = SSD_MFMA(lds4(Bs + (16 * sb + r16) * nld + 16 * kk + q4), cop, gacc[sb]);
+                    }
                 }
-            } else {
-    #pragma unroll
-                for (int kk = 0; kk < NT; ++kk) {
-                    const ssd_s4 cop = __builtin_bit_cast(ssd_s4, crow.v[kk]);
-    #pragma unroll
-                    for (int sb = 0; sb < kQ / 16; ++sb)
-                        gacc[sb] = SSD_MFMA(lds4(Bs + (16 * sb + r16) * nld + 16 * kk + q4), cop, gacc[sb]);
-                }
+            };
+            static_assert(kQ / 16 == 4, "four row tiles per chunk");
+            switch (__builtin_amdgcn_readfirstlane(tb)) {
+                case 0: gt_tiles(std::integral_constant<int, 0>()); break;
+                case 1: gt_tiles(std::integral_constant<int, 1>()); break;
+                case 2: gt_tiles(std::integral_constant<int, 2>()); break;
+                default: gt_tiles(std::integral_constant<int, 3>()); break;
             }
             // lane holds s = 16 sb + q4 + v, t = 16 tb + r16: M[t][s], the A operand
             // (row t, k = s) of M X as it stands
