@@ -139,3 +139,98 @@ def test_random_state_update_config(i):
             yr, ref = out
         assert_close(to64(y), yr, TOL[dt], "y step %d" % t)
     assert_close(to64(st), ref, TOL[dt], "state")
+
+
+# ---- backward -----------------------------------------------------------------
+# Per-element gradients at the forward's bound; the sums over batch, time or
+# channels (dA, dB, dC, dDskip, the Delta bias, the conv taps and bias) at the
+# same tol scaled by 1 + |ref| + mean|ref| (the scale of the backward's own
+# tests: a sum with cancellation can be far smaller than its terms).
+BWD_PER_ELEM = ("dx", "ddelta", "dz", "dh0", "dconv_state_in")
+
+
+def _check_grads(g, ref, dt):
+    for k, r in ref.items():
+        got = to64(g[k])
+        assert got.shape == r.shape, (k, got.shape, r.shape)
+        assert np.all(np.isfinite(got)), k
+        scale = 0.0 if k in BWD_PER_ELEM else float(np.mean(np.abs(r)))
+        err = np.abs(got - r) / (1.0 + np.abs(r) + scale)
+        worst = float(err.max()) if err.size else 0.0
+        assert worst <= TOL[dt], (k, worst)
+
+
+@pytest.mark.parametrize("i", list(range(16)))
+def test_random_backward_config(i):
+    rng = np.random.default_rng(6000 + i)
+    B, L, D = int(rng.integers(1, 4)), int(rng.integers(1, 300)), int(rng.integers(1, 200))
+    N = int(rng.choice([16, 16, int(rng.integers(1, 17))]))
+    dt = torch.bfloat16 if rng.random() < 0.5 else torch.float32
+    K = int(rng.choice([0, 0, 4, int(rng.integers(1, 5))]))
+    softplus = bool(rng.random() < 0.4)
+    h0, dhf_on = bool(rng.random() < 0.5), bool(rng.random() < 0.5)
+    print("case", i, B, L, D, N, dt, K, softplus, h0, dhf_on, flush=True)
+    inp = W.make_scan_inputs(B, L, D, N, io_dtype=dt, seed=200 + i, device=DEV, h0=h0, conv_k=K,
+                             gate=bool(rng.random() < 0.8), skip=bool(rng.random() < 0.8))
+    inp["A"] = _random_A(rng, D, N, L, f32=dt == torch.float32)
+    bias = None
+    if softplus:
+        raw = torch.tensor(rng.normal(-1.0, 1.5, size=(B, L, D)), dtype=torch.float32, device=DEV)
+        inp["delta"] = raw.to(dt).contiguous()
+        bias = torch.tensor(rng.normal(0.0, 0.4, size=D), dtype=torch.float32, device=DEV)
+    conv_b = (torch.tensor(rng.normal(0.0, 0.5, size=D), dtype=torch.float32, device=DEV)
+              if K and rng.random() < 0.5 else None)
+    dy = torch.tensor(rng.normal(size=(B, L, D)), dtype=torch.float32, device=DEV).to(dt)
+    dhf = (torch.tensor(rng.normal(size=(B, D, N)), dtype=torch.float32, device=DEV)
+           if dhf_on else None)
+    g = ssm.selective_scan_bwd(inp["x"], inp["delta"], inp["A"], inp["Bm"], inp["Cm"], dy,
+                               Dskip=inp["Dskip"], z=inp["z"], delta_bias=bias,
+                               delta_softplus=softplus, h0=inp["h0"], dh_final=dhf,
+                               conv_w=inp["conv_w"], conv_b=conv_b)
+    torch.cuda.synchronize()
+    ref = oracle.selective_scan_bwd(to64(inp["x"]), to64(inp["delta"]), to64(inp["A"]),
+                                    to64(inp["Bm"]), to64(inp["Cm"]), to64(dy),
+                                    Dskip=to64(inp["Dskip"]), z=to64(inp["z"]),
+                                    delta_bias=to64(bias), delta_softplus=softplus,
+                                    h0=to64(inp["h0"]), dh_final=to64(dhf),
+                                    conv_w=to64(inp["conv_w"]), conv_b=to64(conv_b))
+    _check_grads(g, ref, dt)
+
+
+# ---- SSD (Mamba-2) layer --------------------------------------------------------
+@pytest.mark.parametrize("i", list(range(16)))
+def test_random_ssd_config(i):
+    rng = np.random.default_rng(5000 + i)
+    N = int(rng.choice([16, 32, 64, 128]))
+    P = int(rng.choice([32, 64, 64, 96, 128]))
+    G = int(rng.choice([1, 1, 2]))
+    H = G * int(rng.integers(1, 5))
+    if i % 4 == 3:   # few (batch, head) pairs on a long row: segmented
+        B, L = 1, int(rng.integers(1500, 4000))
+    else:
+        B, L = int(rng.integers(1, 4)), int(rng.integers(1, 400))
+    dt = torch.float32 if rng.random() < 0.3 else torch.bfloat16
+    softplus = bool(rng.random() < 0.3)
+    print("case", i, B, L, H, P, G, N, dt, softplus, flush=True)
+    inp = W.make_ssd_inputs(B, L, H, P, G, N, seed=400 + i, device=DEV, io_dtype=dt,
+                            h0=bool(rng.random() < 0.5), gate=bool(rng.random() < 0.8),
+                            skip=bool(rng.random() < 0.8),
+                            delta_shift=float(rng.uniform(0.5, 3.0)))
+    A = -rng.uniform(0.05, 6.0, size=H)
+    if rng.random() < 0.3:
+        A[rng.integers(0, H)] = 0.0 if L <= 800 else -0.01
+    inp["A"] = torch.tensor(A, dtype=torch.float32, device=DEV)
+    bias = None
+    if softplus:
+        raw = torch.tensor(rng.normal(-1.0, 1.0, size=(B, L, H)), dtype=torch.float32, device=DEV)
+        inp["delta"] = raw.to(dt).contiguous()
+        bias = torch.tensor(rng.normal(0.0, 0.4, size=H), dtype=torch.float32, device=DEV)
+    y, hf = ssm.ssd_fwd(inp["x"], inp["delta"], inp["A"], inp["Bm"], inp["Cm"], Dskip=inp["Dskip"],
+                        z=inp["z"], delta_bias=bias, delta_softplus=softplus, h0=inp["h0"],
+                        return_final_state=True)
+    torch.cuda.synchronize()
+    yr, hr = oracle.ssd(to64(inp["x"]), to64(inp["delta"]), to64(inp["A"]), to64(inp["Bm"]),
+                        to64(inp["Cm"]), Dskip=to64(inp["Dskip"]), z=to64(inp["z"]),
+                        delta_bias=to64(bias), delta_softplus=softplus, h0=to64(inp["h0"]))
+    assert_close(to64(y), yr, TOL[dt], "y")
+    assert_close(to64(hf), hr, TOL[dt], "h_final")
