@@ -866,6 +866,12 @@ __device__ __forceinline__ void block_iter(const ScanKernelParams &p, const Span
         if (k.dvalid)
             (p.ckpt + (sp.t0 / kTB + j) * (p.B * p.D * kRow) + k.ckpt_wg)[k.ckpt_lane] = FAST ? cy.h * k.ia : cy.h;
     }
+    // Wave priority (wide path): the recurrence steps run at a raised priority,
+    // the LDS and memory phases around them at the base one, so a SIMD's
+    // waves drift apart in phase and one wave's step loop issues while the
+    // others wait on LDS.  Measured in one process against the same kernel
+    // without it: 1-5% faster, outputs bit-identical.
+    if constexpr (VEC && !CKPT) __builtin_amdgcn_s_setprio(0);
     // -- LDS reads of later blocks first ------------------------------------------
     float own_next[3];
     read_own<IO>(T, lds, s_next, n, ci, own_next);
@@ -925,6 +931,7 @@ __device__ __forceinline__ void block_iter(const ScanKernelParams &p, const Span
         if constexpr (MF) return bu_group<g>(ud, bop.g[g]);
         else return bcast<IO>(bop.v, ops.sel, g);
     };
+    if constexpr (VEC && !CKPT) __builtin_amdgcn_s_setprio(2);
     mfma_f32x4 Bn = bu_of(ic<0>{});
     static_for<kTB / 4>([&](auto G) {
         constexpr int gi = decltype(G)::value;
@@ -959,6 +966,7 @@ __device__ __forceinline__ void block_iter(const ScanKernelParams &p, const Span
     // writes, so that the reads may still be in flight at the next barrier
     // (wide path; see wave_barrier).  The element path reads C after
     // staging (its fetch registers are live until then).
+    if constexpr (VEC && !CKPT) __builtin_amdgcn_s_setprio(0);
     float part[kRow];
     COp<IO> cop;
     if constexpr (CKPT) {
@@ -988,6 +996,7 @@ __device__ __forceinline__ void block_iter(const ScanKernelParams &p, const Span
         // same registers.
         fetch_block<IO, VEC>(geo, du, j + 4, tid, nthreads, f);
     }
+    if constexpr (VEC && !CKPT) __builtin_amdgcn_s_setprio(0);  // the read-out sums too
     if constexpr (!CKPT) {
         if constexpr (!VEC) cop = load_cop<IO>(lds + T.bc + s_cur * T.bc_slot + kBTile<IO>, lane);
         const mfma_f32x4 w[4] = {weight_group<IO, 0>(ops.ws, cop), weight_group<IO, 1>(ops.ws, cop),
